@@ -1,0 +1,222 @@
+"""CPU oracle for hybrid compressed attention (CSA + HCA).
+
+TEST INFRASTRUCTURE ONLY: the slow, plain, double-precision definition that
+the GPU library is checked against.  It lives in ``lac_oracle.c`` (plain C,
+OpenMP over independent rows) and is reached through ctypes here.  Only the
+tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py``
+may import this package; the GPU library never does, and the two share no
+code.
+
+Inputs are the exact stored bytes (numpy arrays of float32, uint16 bfloat16
+bit patterns, uint8 mixed FP8/bf16 rows, or float64), decoded by the oracle's
+own decoders.  Storage codes: F32=0, BF16=1, MIXED=2 (E4M3 for the first D-r
+dims, bf16 for the last r), F64=3.
+
+Parity status of each function (what pins it is in ``tests/test_oracle_*.py``):
+all functions here are pinned; see the module docstrings of those tests.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+F32, BF16, MIXED, F64 = 0, 1, 2, 3
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lac_oracle.c")
+_LIB = os.path.join(_HERE, "liblac_oracle.so")
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle with gcc (IEEE double, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-std=c11", "-Wall", "-shared", "-fPIC",
+           "-o", _LIB + ".tmp", _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    lib.lo_bf16_decode.argtypes = [ctypes.c_uint16]
+    lib.lo_bf16_decode.restype = dbl
+    lib.lo_bf16_encode.argtypes = [dbl]
+    lib.lo_bf16_encode.restype = ctypes.c_uint16
+    lib.lo_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.lo_e4m3_decode.restype = dbl
+    lib.lo_e4m3_encode.argtypes = [dbl]
+    lib.lo_e4m3_encode.restype = ctypes.c_uint8
+    lib.lo_row_bytes.argtypes = [i32, i32, i32]
+    lib.lo_row_bytes.restype = i64
+    lib.lo_decode_rows.argtypes = [vp, i32, i64, i32, i32, vp]
+    lib.lo_decode_rows.restype = None
+    lib.lo_encode_rows.argtypes = [vp, i32, i64, i32, i32, vp]
+    lib.lo_encode_rows.restype = None
+    lib.lo_rope.argtypes = [vp, i32, i32, dbl, dbl]
+    lib.lo_rope.restype = None
+    lib.lo_compress.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, dbl, vp, i64, i64, vp, vp]
+    lib.lo_compress.restype = i32
+    lib.lo_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, i32,
+                                    vp, vp]
+    lib.lo_index_scores.restype = i32
+    lib.lo_topk.argtypes = [vp, i32, i32, vp, i32, vp]
+    lib.lo_topk.restype = i32
+    lib.lo_attend.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, vp,
+                              dbl, i32, i32, i32, i32, i32, dbl, vp, vp, i32, vp]
+    lib.lo_attend.restype = i32
+    lib.lo_num_threads.argtypes = []
+    lib.lo_num_threads.restype = i32
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("oracle inputs must be C-contiguous")
+    return a.ctypes.data
+
+
+def _i64(v, n):
+    if v is None:
+        return np.zeros(n, np.int64)
+    return np.ascontiguousarray(np.broadcast_to(np.asarray(v, np.int64), (n,)))
+
+
+def num_threads() -> int:
+    return _load().lo_num_threads()
+
+
+# ---------------------------------------------------------------- formats
+def bf16_decode(bits) -> np.ndarray:
+    lib = _load()
+    bits = np.asarray(bits, np.uint16)
+    return np.array([lib.lo_bf16_decode(int(b)) for b in bits.ravel()]).reshape(bits.shape)
+
+
+def bf16_encode(v) -> np.ndarray:
+    lib = _load()
+    v = np.asarray(v, np.float64)
+    return np.array([lib.lo_bf16_encode(float(x)) for x in v.ravel()],
+                    np.uint16).reshape(v.shape)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    lib = _load()
+    codes = np.asarray(codes, np.uint8)
+    return np.array([lib.lo_e4m3_decode(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e4m3_encode(v) -> np.ndarray:
+    lib = _load()
+    v = np.asarray(v, np.float64)
+    return np.array([lib.lo_e4m3_encode(float(x)) for x in v.ravel()],
+                    np.uint8).reshape(v.shape)
+
+
+def row_bytes(dtype: int, D: int, r: int) -> int:
+    return int(_load().lo_row_bytes(dtype, D, r))
+
+
+def decode_rows(src: np.ndarray, dtype: int, D: int, r: int) -> np.ndarray:
+    """Stored rows (any numpy dtype holding the bytes) -> float64 [..., D]."""
+    rb = row_bytes(dtype, D, r)
+    src = np.ascontiguousarray(src)
+    n = src.nbytes // rb
+    out = np.empty((n, D), np.float64)
+    _load().lo_decode_rows(_p(src), dtype, n, D, r, _p(out))
+    return out
+
+
+def encode_rows(v: np.ndarray, dtype: int, r: int) -> np.ndarray:
+    """float64 [n, D] -> stored bytes, uint8 [n, row_bytes]."""
+    v = np.ascontiguousarray(v, np.float64)
+    D = v.shape[-1]
+    n = v.size // D
+    rb = row_bytes(dtype, D, r)
+    out = np.empty((n, rb), np.uint8)
+    _load().lo_encode_rows(_p(v), dtype, n, D, r, _p(out))
+    return out
+
+
+def rope(v: np.ndarray, r: int, theta: float, pos: float) -> np.ndarray:
+    """Rotate the last r dims of one float64 vector at position pos (copy)."""
+    v = np.array(v, np.float64, copy=True)
+    _load().lo_rope(_p(v), v.shape[-1], r, float(theta), float(pos))
+    return v
+
+
+# ---------------------------------------------------------------- method
+def compress(x, z, in_dtype, B, T, D, m, r=0, theta=10000.0, pos0=None,
+             x_bstride=None, z_bstride=None, want_weights=False):
+    """Block-softmax pooling + rotation at the block start.  -> float64 [B, T//m, D]
+    (and the weights [B, T//m, m, D] when want_weights)."""
+    N = T // m
+    out = np.empty((B, N, D), np.float64)
+    alpha = np.empty((B, N, m, D), np.float64) if want_weights else None
+    rc = _load().lo_compress(_p(x), _p(z), in_dtype, B, T, D, m, r, float(theta),
+                             _p(_i64(pos0, B)), T if x_bstride is None else x_bstride,
+                             T if z_bstride is None else z_bstride, _p(out), _p(alpha))
+    if rc:
+        raise ValueError(f"lo_compress rejected its arguments ({rc})")
+    return (out, alpha) if want_weights else out
+
+
+def _rows(rows, B, Tq):
+    if rows is None:
+        rows = [(b, i) for b in range(B) for i in range(Tq)]
+    return np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
+
+
+def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None):
+    """-> (scores float64 [n_rows, N] with -inf where not visible, nvis int32 [n_rows])."""
+    rows = _rows(rows, B, Tq)
+    n = rows.shape[0]
+    scores = np.empty((n, N), np.float64)
+    nvis = np.empty(n, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    rc = _load().lo_index_scores(_p(q), _p(w), _p(K), dtype, B, Tq, HI, dI, N,
+                                 _p(_i64(qpos0, B)), m, _p(rows), n, _p(scores), _p(nvis))
+    if rc:
+        raise ValueError(f"lo_index_scores rejected its arguments ({rc})")
+    return scores, nvis
+
+
+def topk(scores, nvis, k):
+    """-> int32 [n_rows, k] (selection order, -1 padded)."""
+    scores = np.ascontiguousarray(scores, np.float64)
+    n, N = scores.shape
+    nvis = np.ascontiguousarray(nvis, np.int32)
+    idx = np.empty((n, k), np.int32)
+    _load().lo_topk(_p(scores), n, N, _p(nvis), k, _p(idx))
+    return idx
+
+
+def attend(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W, sink,
+           scale, B, Tq, H, D, r, theta, qpos0, rows=None):
+    """Core attention.  mode 0 = CSA (idx [n_rows, k]), mode 1 = HCA (m = m').
+    -> float64 [n_rows, H, D]."""
+    rows = _rows(rows, B, Tq)
+    n = rows.shape[0]
+    out = np.empty((n, H, D), np.float64)
+    if idx is not None:
+        idx = np.ascontiguousarray(idx, np.int32)
+    if sink is not None:
+        sink = np.ascontiguousarray(sink, np.float64)
+    rc = _load().lo_attend(_p(q), q_dtype, _p(kv), kv_dtype, N, mode, _p(idx), k, m, _p(raw),
+                           T_raw, _p(_i64(raw_pos0, B)), W, _p(sink), float(scale), B, Tq, H, D,
+                           r, float(theta), _p(_i64(qpos0, B)), _p(rows), n, _p(out))
+    if rc:
+        raise ValueError(f"lo_attend rejected its arguments ({rc})")
+    return out

@@ -1,0 +1,443 @@
+/*
+ * lac_oracle.c -- plain CPU oracle for hybrid compressed attention (CSA + HCA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the slow, obviously-correct
+ * definition that the GPU library is checked against.  It shares no code,
+ * header, table or constant with the GPU library, and the GPU library never
+ * calls it.  Only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark load it.
+ *
+ * Every quantity is computed in double precision straight from the stored
+ * input bytes (decoded here by this file's own decoders), in the order the
+ * pages describe the method.  Sources, by page title and section:
+ *
+ *   [P2] "深度解析 DeepSeek-V4：百万级长文本的低成本突破" (learnblockchain.cn),
+ *        section "CSA：Compressed Sparse Attention" (Step 1 Compress,
+ *        Step 2 Select, and its ASCII diagram), section "HCA：Heavily
+ *        Compressed Attention", section "Sliding Window Branch", section
+ *        "Attention Sink".
+ *   [P3] "DeepSeek-V4" rewrite of the QbitAI article (futuo-fx-trading.com):
+ *        the passages on partial RoPE over the last 64 dims with the
+ *        position -i rotation on the output, strict causality of the
+ *        compressed blocks, the lightning indexer + top-k step, and MQA over
+ *        the selected blocks.
+ *   [P4] "DeepSeek V4 技术架构深度解析" (aicoding.csdn.net), section
+ *        "KV Cache优化细节" (FP8 storage with BF16 RoPE dims) and the FP4/FP8/
+ *        BF16 bit-layout table in section "三、FP4量化".
+ *   [P1] "DeepSeek V4的4个技巧" (hubwiz.com), section "技巧1：混合注意力"
+ *        (top 2048 of the summary blocks).
+ *
+ * Where the pages leave a step open, the plainest reading is taken; each is
+ * named where it is used (and listed in the design notes of the repository).
+ *
+ * Storage codes (argument `dtype`):
+ *   0  float32 rows of D values
+ *   1  bfloat16 rows of D values
+ *   2  mixed rows: D-r bytes of FP8 E4M3 (the non-rotated dims) followed by
+ *      r bfloat16 values (the rotated dims), (D-r) + 2r bytes per row
+ *   3  float64 rows of D values (used only by the self-tests)
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define LO_F32 0
+#define LO_BF16 1
+#define LO_MIXED 2
+#define LO_F64 3
+
+/* ------------------------------------------------------------------------ */
+/* Number formats ([P4] bit-layout table: BF16 = 8 exponent + 7 mantissa     */
+/* bits, E4M3 = 4 exponent + 3 mantissa bits).                               */
+/* ------------------------------------------------------------------------ */
+
+double lo_bf16_decode(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16 (ties to even), directly from the
+ * exact value (no intermediate float rounding).  Overflow goes to infinity. */
+uint16_t lo_bf16_encode(double v) {
+    if (isnan(v)) return 0x7FC0;
+    double a = fabs(v);
+    double q;
+    if (a == 0.0) {
+        q = 0.0;
+    } else {
+        int e;
+        (void)frexp(a, &e);          /* a = f * 2^e, 0.5 <= f < 1 */
+        int unbiased = e - 1;        /* a = 1.xxx * 2^unbiased */
+        if (unbiased < -126) unbiased = -126; /* subnormal spacing 2^-133 */
+        double step = ldexp(1.0, unbiased - 7);
+        q = nearbyint(a / step) * step; /* default rounding mode: ties to even */
+        if (q > 3.3895313892515355e38) q = INFINITY; /* beyond the largest bf16 */
+    }
+    float f = (float)(signbit(v) ? -q : q); /* exact: q is a bf16 value */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(u >> 16);
+}
+
+/* E4M3 "fn" variant: bias 7, no infinities, only S.1111.111 is NaN,
+ * largest finite 448, subnormal step 2^-9. */
+double lo_e4m3_decode(uint8_t b) {
+    int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Round to nearest E4M3 (ties to even), saturating to +-448; NaN -> 0x7F.
+ * Reading: the pages give the format only, not a scale, so the store is
+ * unscaled and saturating. */
+uint8_t lo_e4m3_encode(double v) {
+    if (isnan(v)) return 0x7F;
+    uint8_t s = signbit(v) ? 0x80 : 0;
+    double a = fabs(v);
+    if (a >= 448.0) return s | 0x7E;
+    if (a < ldexp(1.0, -6)) {                  /* subnormal range */
+        double q = nearbyint(a * 512.0);       /* multiples of 2^-9 */
+        if (q >= 8.0) return s | 0x08;         /* rounds up to 2^-6 */
+        return s | (uint8_t)q;
+    }
+    int e;
+    double f = frexp(a, &e);                   /* a = f * 2^e, 0.5 <= f < 1 */
+    int E = e - 1;                             /* a = (2f) * 2^E */
+    double q = nearbyint(2.0 * f * 8.0);       /* 8..16 eighths */
+    if (q >= 16.0) { q = 8.0; E += 1; }
+    return s | (uint8_t)(((E + 7) << 3) | ((int)q - 8));
+}
+
+static int64_t row_bytes(int dtype, int D, int r) {
+    switch (dtype) {
+    case LO_F32: return 4LL * D;
+    case LO_BF16: return 2LL * D;
+    case LO_MIXED: return (int64_t)(D - r) + 2LL * r;
+    case LO_F64: return 8LL * D;
+    }
+    return -1;
+}
+
+/* Decode one stored row into D doubles. */
+static void decode_row(const uint8_t* p, int dtype, int D, int r, double* out) {
+    int c;
+    switch (dtype) {
+    case LO_F32:
+        for (c = 0; c < D; ++c) { float f; memcpy(&f, p + 4 * c, 4); out[c] = f; }
+        break;
+    case LO_BF16:
+        for (c = 0; c < D; ++c) { uint16_t h; memcpy(&h, p + 2 * c, 2); out[c] = lo_bf16_decode(h); }
+        break;
+    case LO_MIXED:
+        for (c = 0; c < D - r; ++c) out[c] = lo_e4m3_decode(p[c]);
+        for (c = 0; c < r; ++c) {
+            uint16_t h;
+            memcpy(&h, p + (D - r) + 2 * c, 2);
+            out[D - r + c] = lo_bf16_decode(h);
+        }
+        break;
+    case LO_F64:
+        memcpy(out, p, 8 * (size_t)D);
+        break;
+    }
+}
+
+/* Encode one row of D doubles into the storage format. */
+static void encode_row(const double* v, int dtype, int D, int r, uint8_t* p) {
+    int c;
+    switch (dtype) {
+    case LO_F32:
+        for (c = 0; c < D; ++c) { float f = (float)v[c]; memcpy(p + 4 * c, &f, 4); }
+        break;
+    case LO_BF16:
+        for (c = 0; c < D; ++c) { uint16_t h = lo_bf16_encode(v[c]); memcpy(p + 2 * c, &h, 2); }
+        break;
+    case LO_MIXED:
+        for (c = 0; c < D - r; ++c) p[c] = lo_e4m3_encode(v[c]);
+        for (c = 0; c < r; ++c) {
+            uint16_t h = lo_bf16_encode(v[D - r + c]);
+            memcpy(p + (D - r) + 2 * c, &h, 2);
+        }
+        break;
+    case LO_F64:
+        memcpy(p, v, 8 * (size_t)D);
+        break;
+    }
+}
+
+int64_t lo_row_bytes(int dtype, int D, int r) { return row_bytes(dtype, D, r); }
+
+void lo_decode_rows(const void* src, int dtype, int64_t n_rows, int D, int r, double* out) {
+    int64_t rb = row_bytes(dtype, D, r), i;
+    for (i = 0; i < n_rows; ++i) decode_row((const uint8_t*)src + i * rb, dtype, D, r, out + i * D);
+}
+
+void lo_encode_rows(const double* v, int dtype, int64_t n_rows, int D, int r, void* dst) {
+    int64_t rb = row_bytes(dtype, D, r), i;
+    for (i = 0; i < n_rows; ++i) encode_row(v + i * D, dtype, D, r, (uint8_t*)dst + i * rb);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Partial RoPE ([P3]: rotary position encoding on the last 64 dims of the   */
+/* query and the KV entries only; the output is rotated at position -i).     */
+/* Reading: pairs (D-r+2i, D-r+2i+1), frequency theta^(-2i/r), all in double. */
+/* ------------------------------------------------------------------------ */
+void lo_rope(double* v, int D, int r, double theta, double pos) {
+    int i;
+    for (i = 0; i < r / 2; ++i) {
+        double freq = pow(theta, -2.0 * i / (double)r);
+        double ang = pos * freq;
+        double c = cos(ang), s = sin(ang);
+        double a = v[D - r + 2 * i], b = v[D - r + 2 * i + 1];
+        v[D - r + 2 * i] = a * c - b * s;
+        v[D - r + 2 * i + 1] = a * s + b * c;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Compression ([P2] CSA Step 1; HCA uses the same pooling with m' tokens).   */
+/* Every m consecutive KV entries merge into one with learned softmax        */
+/* weights; reading: one softmax over the m tokens per channel, fed by a      */
+/* logit tensor of the same shape as the KV; no entry for a partial block.   */
+/* The entry is then rotated at the position of its first token.             */
+/* ------------------------------------------------------------------------ */
+
+/* alpha (optional, [B, T/m, m, D]) receives the per-channel weights. */
+int lo_compress(const void* x, const void* z, int in_dtype, int B, int T, int D, int m,
+                int r, double theta, const int64_t* pos0, int64_t x_bstride,
+                int64_t z_bstride, double* out, double* alpha) {
+    if (m < 1 || D < 1 || r < 0 || r > D || (r & 1)) return 1;
+    int N = T / m;
+    int64_t rb = row_bytes(in_dtype, D, 0);
+    int64_t bj;
+#pragma omp parallel for schedule(static)
+    for (bj = 0; bj < (int64_t)B * N; ++bj) {
+        int b = (int)(bj / N), j = (int)(bj % N);
+        double* xs = malloc(sizeof(double) * (size_t)m * D);
+        double* zs = malloc(sizeof(double) * (size_t)m * D);
+        int i, c;
+        for (i = 0; i < m; ++i) {
+            int64_t row = (int64_t)j * m + i;
+            decode_row((const uint8_t*)x + (b * x_bstride + row) * rb, in_dtype, D, 0, xs + i * D);
+            decode_row((const uint8_t*)z + (b * z_bstride + row) * rb, in_dtype, D, 0, zs + i * D);
+        }
+        double* o = out + bj * D;
+        for (c = 0; c < D; ++c) {
+            double mu = -INFINITY, den = 0.0, acc = 0.0;
+            for (i = 0; i < m; ++i) mu = fmax(mu, zs[i * D + c]);
+            for (i = 0; i < m; ++i) den += exp(zs[i * D + c] - mu);
+            for (i = 0; i < m; ++i) {
+                double a = exp(zs[i * D + c] - mu) / den;
+                if (alpha) alpha[(bj * m + i) * D + c] = a;
+                acc += a * xs[i * D + c];
+            }
+            o[c] = acc;
+        }
+        lo_rope(o, D, r, theta, (double)(pos0 ? pos0[b] : 0) + (double)j * m);
+        free(xs);
+        free(zs);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Lightning indexer ([P3] "对每名query token，用一名轻量之indexer计算它与每  */
+/* 名压缩KV块之相关性分数"; the score s = sum_h w_h * ReLU(q_h . k) is the      */
+/* indexer of DeepSeek-V3.2 that the pages say V4 keeps).  Strict causality   */
+/* ([P3]): query t sees compressed entry j only when j < floor(t/m).         */
+/* ------------------------------------------------------------------------ */
+
+static int64_t n_visible(int64_t t, int N, int m) {
+    int64_t n = t >= 0 ? t / m : 0;
+    return n < N ? n : N;
+}
+
+/* rows: n_rows pairs (b, i).  scores: [n_rows, N]; entries not visible are
+ * set to -inf.  nvis (optional): [n_rows]. */
+int lo_index_scores(const void* q, const float* w, const void* K, int dtype, int B, int Tq,
+                    int HI, int dI, int N, const int64_t* qpos0, int m,
+                    const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {
+    (void)B;
+    if (dtype != LO_F32 && dtype != LO_BF16 && dtype != LO_F64) return 2;
+    if (dI < 1 || dI > 1024) return 3;
+    int64_t rb = row_bytes(dtype, dI, 0);
+    double* qd = malloc(sizeof(double) * (size_t)n_rows * HI * dI);
+    int rr, h;
+    for (rr = 0; rr < n_rows; ++rr) {
+        int b = rows[2 * rr], i = rows[2 * rr + 1];
+        for (h = 0; h < HI; ++h)
+            decode_row((const uint8_t*)q + (((int64_t)b * Tq + i) * HI + h) * rb, dtype, dI, 0,
+                       qd + ((int64_t)rr * HI + h) * dI);
+        if (nvis) nvis[rr] = (int32_t)n_visible(qpos0[b] + i, N, m);
+    }
+    int64_t task;
+#pragma omp parallel for schedule(static)
+    for (task = 0; task < (int64_t)n_rows * N; ++task) {
+        int r2 = (int)(task / N);
+        int64_t j = task % N;
+        int b = rows[2 * r2], i = rows[2 * r2 + 1];
+        if (j >= n_visible(qpos0[b] + i, N, m)) { scores[task] = -INFINITY; continue; }
+        double kd[1024];
+        int c, hh;
+        decode_row((const uint8_t*)K + ((int64_t)b * N + j) * rb, dtype, dI, 0, kd);
+        double s = 0.0;
+        for (hh = 0; hh < HI; ++hh) {
+            const double* qh = qd + ((int64_t)r2 * HI + hh) * dI;
+            double dot = 0.0;
+            for (c = 0; c < dI; ++c) dot += qh[c] * kd[c];
+            s += (double)w[((int64_t)b * Tq + i) * HI + hh] * (dot > 0.0 ? dot : 0.0);
+        }
+        scores[task] = s;
+    }
+    free(qd);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Top-k ([P2] Step 2 Select and its diagram; [P1] top 2048).  Order:        */
+/* higher score first, lower index first among equal scores (reading); the   */
+/* first min(k, n_vis) are kept and the rest of the k slots hold -1.          */
+/* ------------------------------------------------------------------------ */
+typedef struct { double s; int32_t j; } lo_pair;
+
+static int pair_cmp(const void* a, const void* b) {
+    const lo_pair* x = (const lo_pair*)a;
+    const lo_pair* y = (const lo_pair*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+int lo_topk(const double* scores, int n_rows, int N, const int32_t* nvis, int k, int32_t* idx) {
+    int rr;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (rr = 0; rr < n_rows; ++rr) {
+        int nv = nvis[rr], j;
+        lo_pair* p = malloc(sizeof(lo_pair) * (size_t)(nv > 0 ? nv : 1));
+        for (j = 0; j < nv; ++j) { p[j].s = scores[(int64_t)rr * N + j]; p[j].j = j; }
+        qsort(p, (size_t)nv, sizeof(lo_pair), pair_cmp);
+        for (j = 0; j < k; ++j) idx[(int64_t)rr * k + j] = j < nv ? p[j].j : -1;
+        free(p);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Core attention ([P3] MQA over the selected compressed blocks; [P2] HCA    */
+/* dense over all compressed entries; [P2] sliding window of recent raw      */
+/* entries; [P2] attention sink in the denominator; [P3] KV entry = key =    */
+/* value, q rotated at t, raw entries at their position s, output at -t).     */
+/* Readings: one softmax over compressed entries, window entries and the    */
+/* optional sink; the window is raw positions [max(0, t-W+1), t]; entries   */
+/* are not de-duplicated between the two sets.                               */
+/* mode 0 = CSA (entries from idx, -1 skipped), mode 1 = HCA (entries        */
+/* j < min(N, floor(t/m))).                                                  */
+/* out: [n_rows, H, D].                                                      */
+/* ------------------------------------------------------------------------ */
+int lo_attend(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, int mode,
+              const int32_t* idx, int k, int m, const void* raw, int T_raw,
+              const int64_t* raw_pos0, int W, const double* sink, double scale, int B, int Tq,
+              int H, int D, int r, double theta, const int64_t* qpos0, const int32_t* rows,
+              int n_rows, double* out) {
+    (void)B;
+    int64_t qrb = row_bytes(q_dtype, D, 0);
+    int64_t krb = row_bytes(kv_dtype, D, r);
+    int64_t task;
+    int rr0;
+    if (scale == 0.0) scale = 1.0 / sqrt((double)D);
+    /* The raw buffer must hold every window position; CSA indices must name
+     * existing entries.  Anything else is rejected, never read. */
+    for (rr0 = 0; rr0 < n_rows; ++rr0) {
+        int b = rows[2 * rr0], i = rows[2 * rr0 + 1], e;
+        int64_t t = qpos0[b] + i;
+        int64_t s_lo = t - W + 1 < 0 ? 0 : t - W + 1;
+        if (W > 0 && (s_lo < raw_pos0[b] || t >= raw_pos0[b] + T_raw)) return 4;
+        if (mode == 0)
+            for (e = 0; e < k; ++e)
+                if (idx[(int64_t)rr0 * k + e] >= N) return 5;
+    }
+#pragma omp parallel for schedule(dynamic, 1)
+    for (task = 0; task < (int64_t)n_rows * H; ++task) {
+        int rr = (int)(task / H), h = (int)(task % H);
+        int b = rows[2 * rr], i = rows[2 * rr + 1];
+        int64_t t = qpos0[b] + i;
+        double* qv = malloc(sizeof(double) * (size_t)D);
+        double* ev = malloc(sizeof(double) * (size_t)D);
+        double* acc = calloc((size_t)D, sizeof(double));
+        double* y = out + ((int64_t)rr * H + h) * D;
+        int c;
+        decode_row((const uint8_t*)q + (((int64_t)b * Tq + i) * H + h) * qrb, q_dtype, D, 0, qv);
+        lo_rope(qv, D, r, theta, (double)t);
+
+        /* Collect the logits first (to take their maximum), then weights. */
+        int64_t n_comp = 0, n_win = 0, e;
+        int64_t s_lo = t - W + 1 < 0 ? 0 : t - W + 1;
+        if (W > 0 && t >= 0) n_win = t - s_lo + 1;
+        int64_t hca_n = mode == 1 ? n_visible(t, N, m) : 0;
+        n_comp = mode == 0 ? k : hca_n;
+        double* logit = malloc(sizeof(double) * (size_t)(n_comp + n_win + 1));
+        int* valid = malloc(sizeof(int) * (size_t)(n_comp + n_win + 1));
+        double mx = sink ? sink[h] : -INFINITY;
+        for (e = 0; e < n_comp + n_win; ++e) {
+            valid[e] = 0;
+            if (e < n_comp) {
+                int64_t j = mode == 0 ? idx[(int64_t)rr * k + e] : e;
+                if (j < 0) continue;
+                decode_row((const uint8_t*)kv + ((int64_t)b * N + j) * krb, kv_dtype, D, r, ev);
+            } else {
+                int64_t s = s_lo + (e - n_comp);
+                decode_row((const uint8_t*)raw + ((int64_t)b * T_raw + (s - raw_pos0[b])) * krb,
+                           kv_dtype, D, r, ev);
+                lo_rope(ev, D, r, theta, (double)s);
+            }
+            double dot = 0.0;
+            for (c = 0; c < D; ++c) dot += qv[c] * ev[c];
+            logit[e] = scale * dot;
+            valid[e] = 1;
+            if (logit[e] > mx) mx = logit[e];
+        }
+        double den = sink ? exp(sink[h] - mx) : 0.0;
+        for (e = 0; e < n_comp + n_win; ++e) {
+            if (!valid[e]) continue;
+            double p = exp(logit[e] - mx);
+            den += p;
+            if (e < n_comp) {
+                int64_t j = mode == 0 ? idx[(int64_t)rr * k + e] : e;
+                decode_row((const uint8_t*)kv + ((int64_t)b * N + j) * krb, kv_dtype, D, r, ev);
+            } else {
+                int64_t s = s_lo + (e - n_comp);
+                decode_row((const uint8_t*)raw + ((int64_t)b * T_raw + (s - raw_pos0[b])) * krb,
+                           kv_dtype, D, r, ev);
+                lo_rope(ev, D, r, theta, (double)s);
+            }
+            for (c = 0; c < D; ++c) acc[c] += p * ev[c];
+        }
+        for (c = 0; c < D; ++c) y[c] = den > 0.0 ? acc[c] / den : 0.0;
+        lo_rope(y, D, r, theta, -(double)t);
+        free(qv);
+        free(ev);
+        free(acc);
+        free(logit);
+        free(valid);
+    }
+    return 0;
+}
+
+int lo_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
