@@ -1,0 +1,227 @@
+/*
+ * lac.h -- C ABI of the MI355X (gfx950) hybrid compressed attention library.
+ *
+ * Five operations, one per step of the method as the pages state it:
+ *   csa_compress / hca_compress   pool m (CSA) or m' (HCA) raw KV entries
+ *   indexer_topk                  Lightning-Indexer scores + top-k selection
+ *   csa_attend                    MQA over the selected compressed entries
+ *   hca_attend                    MQA over all visible compressed entries
+ * Both attend calls also take the raw sliding window, the optional sink, the
+ * partial RoPE and its inverse on the output.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Memory.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *   The library never allocates, frees or copies between host and device,
+ *   and never synchronises.  Scratch memory is passed in as `workspace`
+ *   (device, 256-byte aligned), sized by the *_workspace_size() queries,
+ *   which are pure host arithmetic.  Tensors are dense row-major; base
+ *   pointers must be 16-byte aligned.
+ * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *   enqueued asynchronously; the calls are thread-safe (no global state
+ *   except the thread-local error string and the thread-local launch timer).
+ * Positions.  Host arrays of B int64 (NULL = all zero).  Query i of sequence
+ *   b sits at absolute position q_pos0[b] + i; raw row i at raw_pos0[b] + i.
+ *   Compressed entry j covers positions [j*m, j*m + m - 1] and is rotated at
+ *   position j*m.  Positions must be below 2^31.
+ * Storage formats (lac_dtype):
+ *   LAC_F32   float32 values
+ *   LAC_BF16  bfloat16 values
+ *   LAC_KV_E4M3_ROPE_BF16  KV rows of (D - r) FP8 E4M3 bytes ("fn" variant:
+ *             bias 7, max 448, no infinities) for the non-rotated dims,
+ *             followed by r bfloat16 values for the rotated dims; a row is
+ *             (D - r) + 2r bytes (576 B at D = 512, r = 64).  Stores round to
+ *             nearest even and saturate to +-448, unscaled.
+ *   The mixed format follows the KV-cache storage of "DeepSeek V4 技术架构深度
+ *   解析" (aicoding.csdn.net), section "KV Cache优化细节", and its bit-layout
+ *   table in section "三、FP4量化".
+ * Errors.  Every argument is validated before anything is enqueued.  On an
+ *   invalid argument a call returns a non-zero lac_status, enqueues nothing,
+ *   leaves outputs untouched and sets lac_last_error().  A failed kernel
+ *   launch returns LAC_ERR_DEVICE.  Device-side faults surface at the
+ *   caller's next synchronisation.  No C++ exception crosses the ABI.
+ *
+ * Page references are by title and section:
+ *   [P1] "DeepSeek V4的4个技巧" (hubwiz.com), section "技巧1：混合注意力".
+ *   [P2] "深度解析 DeepSeek-V4：百万级长文本的低成本突破" (learnblockchain.cn),
+ *        sections "CSA：Compressed Sparse Attention", "HCA：Heavily Compressed
+ *        Attention", "Sliding Window Branch", "Attention Sink".
+ *   [P3] the QbitAI article as rewritten on futuo-fx-trading.com: partial RoPE
+ *        passage, strict-causality passage, the lightning indexer + top-k step,
+ *        core attention (MQA) step.
+ */
+#ifndef LAC_H
+#define LAC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LAC_OK = 0,
+    LAC_ERR_INVALID = 1,     /* a pointer, size, position or combination is invalid */
+    LAC_ERR_UNSUPPORTED = 2, /* valid but not implemented (dtype/dim combination)   */
+    LAC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small          */
+    LAC_ERR_DEVICE = 4       /* the HIP runtime refused a launch                    */
+} lac_status;
+
+typedef enum {
+    LAC_F32 = 0,
+    LAC_BF16 = 1,
+    LAC_KV_E4M3_ROPE_BF16 = 2
+} lac_dtype;
+
+/* Largest batch the position arrays may describe. */
+#define LAC_MAX_BATCH 128
+
+/*
+ * csa_compress -- [P2] CSA Step 1 "Compress": every m consecutive KV entries
+ * are merged into one entry with learned softmax weights.  Reading of the
+ * weights: for entry j and channel c, alpha_i = softmax over the block's m
+ * tokens of logits[j*m + i, c]; out[j, c] = sum_i alpha_i * raw_kv[j*m + i, c].
+ * The entry is then rotated on its last `rope_dims` dims at position
+ * pos0[b] + j*m ([P3] partial RoPE; interleaved pairs (D-r+2i, D-r+2i+1),
+ * frequency rope_theta^(-2i/r)).  Indexer keys use the same call with
+ * rope_dims = 0.  Only complete blocks are emitted: floor(T/m) entries.
+ *
+ *   raw_kv   [B, kv_batch_stride rows, D] in in_dtype (LAC_F32 | LAC_BF16);
+ *            rows 0..T-1 of each batch are read
+ *   logits   [B, logit_batch_stride rows, D] in in_dtype
+ *   out      [B, out_batch_stride rows, row] in out_dtype (any lac_dtype);
+ *            rows 0..T/m-1 of each batch are written
+ *   m        block size, 1..256 (4 for CSA)
+ *   pos0     host [B], position of raw row 0; a multiple of m
+ * D must be a multiple of 8, rope_dims a multiple of 8 with rope_dims <= D.
+ * Streams raw KV and logits once from HBM; fp32 arithmetic.
+ */
+int32_t csa_compress(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                     int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                     int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                     int64_t kv_batch_stride, int64_t logit_batch_stride,
+                     int64_t out_batch_stride, void* stream);
+
+/*
+ * hca_compress -- [P2] HCA: the same pooling with the much larger block m'
+ * (128 in the pages), without overlap between blocks.  Arguments and
+ * behaviour are those of csa_compress.
+ */
+int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                     int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                     int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                     int64_t kv_batch_stride, int64_t logit_batch_stride,
+                     int64_t out_batch_stride, void* stream);
+
+/*
+ * indexer_topk -- [P3] lightning indexer + top-k; [P2] CSA Step 2 "Select";
+ * [P1] top 2048.  For query t = q_pos0[b] + i, the visible entries are
+ * j < n_vis(t) = min(N, floor(t/m)) ([P3] strict causality: a query never
+ * sees its own compressed block).  Score (reading of the indexer):
+ *     s[j] = sum_h w[b,i,h] * max(0, q_idx[b,i,h,:] . k_idx[b,j,:])
+ * with no scale and no rotation, accumulated in fp32.  The selection keeps
+ * the first min(k, n_vis) entries in the order (score descending, index
+ * ascending); the chosen indices are written in ascending index order and
+ * the remaining slots hold -1.
+ *
+ *   q_idx       [B, Tq, H_I, d_I] in dtype (LAC_F32 | LAC_BF16)
+ *   w           [B, Tq, H_I] float32
+ *   k_idx       [B, N, d_I] in dtype
+ *   topk_idx    [B, Tq, k] int32, output
+ *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
+ *               -inf in padded slots); may be NULL
+ *   workspace   >= indexer_topk_workspace_size(B, Tq, N, k) bytes
+ * LAC_BF16 needs H_I in {32, 64, 128} and d_I in {64, 128} (bf16 MFMA);
+ * LAC_F32 needs H_I * d_I <= 8192.  1 <= k <= 8192.
+ */
+size_t indexer_topk_workspace_size(int32_t B, int32_t Tq, int32_t N, int32_t k);
+int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32_t dtype,
+                     int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
+                     const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
+                     float* topk_score, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attend_workspace_size -- scratch for csa_attend / hca_attend: the rotated
+ * copy of the raw window and split-K partial results.  n_entries is the
+ * number of compressed entries one query may attend: k for csa_attend, N for
+ * hca_attend; the same values must be passed to the attend call.
+ */
+size_t attend_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t D, int32_t rope_dims,
+                             int32_t kv_dtype, int32_t n_entries, int32_t window);
+
+/*
+ * csa_attend -- [P3] core attention: Multi-Query Attention over the selected
+ * compressed entries; [P2] plus the sliding window of the most recent raw
+ * entries and the attention sink.  For query t and head h:
+ *     q~   = R(t) q[b,i,h]                       (rotation of the last r dims)
+ *     E    = { ckv[b,j] : j in topk_idx[b,i,:], j >= 0 }
+ *            U { R(s) raw_kv[b, s - raw_pos0[b]] : max(0, t-W+1) <= s <= t }
+ *     l_e  = scale * (q~ . e)                    (each entry is key and value)
+ *     o    = sum_e exp(l_e) e / (exp(sink[h]) + sum_e exp(l_e))
+ *     out  = R(-t) o                             ([P3] output rotation at -i)
+ * Readings: one softmax over both sets and the sink; no de-duplication; an
+ * empty set with no sink gives 0.
+ *
+ *   q         [B, Tq, H, D] in q_dtype (LAC_F32 | LAC_BF16), not rotated
+ *   ckv       [B, N, row] in kv_dtype, rotated at the block start
+ *   topk_idx  [B, Tq, k] int32; -1 entries are skipped; values >= N are
+ *             skipped as well (they name no entry)
+ *   raw_kv    [B, T_raw, row] in kv_dtype, not rotated; must hold every
+ *             window position of every query (else LAC_ERR_INVALID); may be
+ *             NULL when window == 0
+ *   sink      [H] float32 logits, or NULL for none
+ *   softmax_scale  0 selects 1/sqrt(D)
+ *   out       [B, Tq, H, D] in q_dtype
+ *   workspace >= attend_workspace_size(B, Tq, H, D, rope_dims, kv_dtype, k, window)
+ * q_dtype LAC_F32 needs kv_dtype LAC_F32, D <= 256 and H*D <= 8192;
+ * q_dtype LAC_BF16 needs kv_dtype LAC_BF16 or LAC_KV_E4M3_ROPE_BF16,
+ * D in {128, 256, 512} and H dividing 64 or a multiple of 64.
+ * rope_dims: a multiple of 8, <= D.
+ */
+int32_t csa_attend(const void* q, int32_t q_dtype, const void* ckv, int32_t kv_dtype, int32_t N,
+                   const int32_t* topk_idx, int32_t k, const void* raw_kv, int32_t T_raw,
+                   const int64_t* raw_pos0, int32_t window, const float* sink,
+                   float softmax_scale, int32_t B, int32_t Tq, int32_t H, int32_t D,
+                   int32_t rope_dims, float rope_theta, const int64_t* q_pos0, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * hca_attend -- [P2] HCA: dense attention over all compressed entries,
+ * here all j < n_vis(t) = min(N, floor(t/m)) ([P3] strict causality), plus
+ * the raw window and sink exactly as csa_attend.  m is the HCA block m'.
+ *   hkv       [B, N, row] in kv_dtype
+ *   workspace >= attend_workspace_size(B, Tq, H, D, rope_dims, kv_dtype, N, window)
+ * Other arguments as csa_attend.
+ */
+int32_t hca_attend(const void* q, int32_t q_dtype, const void* hkv, int32_t kv_dtype, int32_t N,
+                   int32_t m, const void* raw_kv, int32_t T_raw, const int64_t* raw_pos0,
+                   int32_t window, const float* sink, float softmax_scale, int32_t B, int32_t Tq,
+                   int32_t H, int32_t D, int32_t rope_dims, float rope_theta,
+                   const int64_t* q_pos0, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next call on this thread. */
+const char* lac_last_error(void);
+
+/*
+ * Launch timer, for measurement.  Arms a one-shot request on this thread:
+ * the next launch of kernel `kernel` (LAC_KERNEL_*) enqueued by this thread
+ * records hipEvent_t `start` just before it and `stop` just after it, on the
+ * stream of the launch.  Passing NULL events disarms.
+ */
+enum {
+    LAC_KERNEL_COMPRESS = 0,
+    LAC_KERNEL_INDEXER_SCORE = 1,
+    LAC_KERNEL_TOPK = 2,
+    LAC_KERNEL_ATTEND = 3,
+    LAC_KERNEL_COMBINE = 4
+};
+int32_t lac_time_next_launch(int32_t kernel, void* start, void* stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LAC_H */

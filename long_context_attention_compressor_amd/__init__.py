@@ -1,0 +1,220 @@
+"""Hybrid compressed attention (CSA + HCA) on MI355X: Python binding.
+
+This module only marshals arguments to the C ABI of ``liblac.so``
+(``include/lac.h``): tensor pointers, sizes, host position arrays and the
+current HIP stream.  Every step of the computation runs in the library's
+gfx950 kernels; if the library is missing, importing this module fails.
+
+Tensors are PyTorch tensors on the GPU, row-major.  Storage formats follow
+the tensor dtype: ``torch.float32`` -> LAC_F32, ``torch.bfloat16`` ->
+LAC_BF16, ``torch.uint8`` rows of ``(D - r) + 2r`` bytes -> the mixed FP8
+E4M3 / bf16 KV format.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Union
+
+import torch
+
+__all__ = [
+    "LacError", "csa_compress", "hca_compress", "indexer_topk", "indexer_topk_workspace_size",
+    "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
+    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "KERNELS",
+]
+
+LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 = 0, 1, 2
+KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4}
+STATUS = {0: "LAC_OK", 1: "LAC_ERR_INVALID", 2: "LAC_ERR_UNSUPPORTED", 3: "LAC_ERR_WORKSPACE",
+          4: "LAC_ERR_DEVICE"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblac.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_COMPRESS_ARGS = [_vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _i64, _i64,
+                  _i64, _vp]
+lib.csa_compress.argtypes = _COMPRESS_ARGS
+lib.csa_compress.restype = _i32
+lib.hca_compress.argtypes = _COMPRESS_ARGS
+lib.hca_compress.restype = _i32
+lib.indexer_topk_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
+lib.indexer_topk_workspace_size.restype = _sz
+lib.indexer_topk.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _i32,
+                             _vp, _vp, _vp, _sz, _vp]
+lib.indexer_topk.restype = _i32
+lib.attend_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
+lib.attend_workspace_size.restype = _sz
+lib.csa_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _f32,
+                           _i32, _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+lib.csa_attend.restype = _i32
+lib.hca_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _f32, _i32,
+                           _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
+lib.hca_attend.restype = _i32
+lib.lac_last_error.argtypes = []
+lib.lac_last_error.restype = ctypes.c_char_p
+lib.lac_time_next_launch.argtypes = [_i32, _vp, _vp]
+lib.lac_time_next_launch.restype = _i32
+
+
+class LacError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+def _check(status: int):
+    if status != 0:
+        raise LacError(status, lib.lac_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _positions(p: Union[None, int, Sequence[int], torch.Tensor], B: int):
+    if p is None:
+        return None
+    if isinstance(p, torch.Tensor):
+        p = p.tolist()
+    if isinstance(p, int):
+        p = [p] * B
+    if len(p) != B:
+        raise ValueError(f"expected {B} positions, got {len(p)}")
+    return (ctypes.c_int64 * B)(*[int(v) for v in p])
+
+
+def _fmt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LAC_F32
+    if t.dtype == torch.bfloat16:
+        return LAC_BF16
+    if t.dtype == torch.uint8:
+        return LAC_KV_E4M3_ROPE_BF16
+    raise TypeError(f"unsupported tensor dtype {t.dtype}")
+
+
+def _rows(t: torch.Tensor, what: str):
+    """Batch stride in rows of a [B, rows, width] tensor whose rows are dense."""
+    if t.dim() != 3 or t.stride(2) != 1 or t.stride(1) != t.shape[2]:
+        raise ValueError(f"{what} must be [B, rows, width] with dense rows")
+    return t.stride(0) // t.shape[2]
+
+
+def _need_dense(t: Optional[torch.Tensor], what: str):
+    if t is not None and not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return ws
+
+
+# ---------------------------------------------------------------- compress
+def _compress(fn, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T, stream):
+    B, _, D = raw_kv.shape
+    T = raw_kv.shape[1] if T is None else T
+    if logits.dtype != raw_kv.dtype:
+        raise TypeError("raw_kv and logits must share a dtype")
+    _check(fn(_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _fmt(out), B, T, D, m,
+              rope_dims, rope_theta, _positions(pos0, B), _rows(raw_kv, "raw_kv"),
+              _rows(logits, "logits"), _rows(out, "out"), _stream(stream)))
+    return out
+
+
+def csa_compress(raw_kv, logits, out, m=4, rope_dims=64, rope_theta=10000.0, pos0=None, T=None,
+                 stream=None):
+    """Pool every m raw KV rows into one entry (see include/lac.h)."""
+    return _compress(lib.csa_compress, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T,
+                     stream)
+
+
+def hca_compress(raw_kv, logits, out, m=128, rope_dims=64, rope_theta=10000.0, pos0=None, T=None,
+                 stream=None):
+    """Pool every m' raw KV rows into one entry (see include/lac.h)."""
+    return _compress(lib.hca_compress, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T,
+                     stream)
+
+
+# ---------------------------------------------------------------- indexer + top-k
+def indexer_topk_workspace_size(B, Tq, N, k) -> int:
+    return int(lib.indexer_topk_workspace_size(B, Tq, N, k))
+
+
+def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
+                 workspace=None, stream=None):
+    """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I].
+    Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""
+    B, Tq, HI, dI = q_idx.shape
+    N = k_idx.shape[1]
+    for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
+        _need_dense(t, nm)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+    workspace = _workspace(workspace, indexer_topk_workspace_size(B, Tq, N, k), q_idx.device)
+    _check(lib.indexer_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _fmt(q_idx), B, Tq, HI, dI, N,
+                            _positions(q_pos0, B), m, k, _ptr(topk_idx), _ptr(topk_score),
+                            _ptr(workspace), workspace.numel(), _stream(stream)))
+    return topk_idx
+
+
+# ---------------------------------------------------------------- attention
+def attend_workspace_size(B, Tq, H, D, rope_dims, kv_dtype, n_entries, window) -> int:
+    return int(lib.attend_workspace_size(B, Tq, H, D, rope_dims, kv_dtype, n_entries, window))
+
+
+def _attend_common(q, kv, raw_kv, out, raw_pos0, q_pos0):
+    B, Tq, H, D = q.shape
+    for t, nm in ((q, "q"), (kv, "kv"), (raw_kv, "raw_kv")):
+        _need_dense(t, nm)
+    if out is None:
+        out = torch.empty_like(q)
+    T_raw = 0 if raw_kv is None else raw_kv.shape[1]
+    return B, Tq, H, D, out, T_raw, _positions(raw_pos0, B), _positions(q_pos0, B)
+
+
+def csa_attend(q, ckv, topk_idx, raw_kv, window, q_pos0=None, raw_pos0=None, rope_dims=64,
+               rope_theta=10000.0, sink=None, softmax_scale=0.0, out=None, workspace=None,
+               stream=None):
+    """Sparse MQA over the selected compressed entries + raw window (include/lac.h)."""
+    B, Tq, H, D, out, T_raw, rp, qp = _attend_common(q, ckv, raw_kv, out, raw_pos0, q_pos0)
+    k = topk_idx.shape[-1]
+    kvf = _fmt(ckv)
+    workspace = _workspace(workspace, attend_workspace_size(B, Tq, H, D, rope_dims, kvf, k, window),
+                           q.device)
+    _check(lib.csa_attend(_ptr(q), _fmt(q), _ptr(ckv), kvf, ckv.shape[1], _ptr(topk_idx), k,
+                          _ptr(raw_kv), T_raw, rp, window, _ptr(sink), softmax_scale, B, Tq, H, D,
+                          rope_dims, rope_theta, qp, _ptr(out), _ptr(workspace),
+                          workspace.numel(), _stream(stream)))
+    return out
+
+
+def hca_attend(q, hkv, raw_kv, window, m=128, q_pos0=None, raw_pos0=None, rope_dims=64,
+               rope_theta=10000.0, sink=None, softmax_scale=0.0, out=None, workspace=None,
+               stream=None):
+    """Dense MQA over all visible compressed entries + raw window (include/lac.h)."""
+    B, Tq, H, D, out, T_raw, rp, qp = _attend_common(q, hkv, raw_kv, out, raw_pos0, q_pos0)
+    N = hkv.shape[1]
+    kvf = _fmt(hkv)
+    workspace = _workspace(workspace, attend_workspace_size(B, Tq, H, D, rope_dims, kvf, N, window),
+                           q.device)
+    _check(lib.hca_attend(_ptr(q), _fmt(q), _ptr(hkv), kvf, N, m, _ptr(raw_kv), T_raw, rp, window,
+                          _ptr(sink), softmax_scale, B, Tq, H, D, rope_dims, rope_theta, qp,
+                          _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def time_next_launch(kernel: str, start: "torch.cuda.Event", stop: "torch.cuda.Event"):
+    """Arm the library's one-shot launch timer (lac_time_next_launch)."""
+    _check(lib.lac_time_next_launch(KERNELS[kernel], start.cuda_event, stop.cuda_event))

@@ -1,0 +1,311 @@
+// abi.cpp -- the C ABI declared in include/lac.h: argument validation (pure
+// host code, nothing is enqueued on error), workspace sizing, the thread-local
+// error string and launch timer, and dispatch to the kernel launchers.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <exception>
+
+#include "lac.h"
+#include "lac_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+thread_local int g_timer_kernel = -1;
+thread_local hipEvent_t g_timer_start = nullptr;
+thread_local hipEvent_t g_timer_stop = nullptr;
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kPosLimit = (int64_t)1 << 31;
+
+// Copies host positions into the by-value struct, checking range and the
+// block alignment `mult` (1 = none).
+int32_t take_positions(const char* fn, const char* what, const int64_t* src, int B, int64_t span,
+                       int mult, lac::Positions* dst) {
+  for (int b = 0; b < B; ++b) {
+    const int64_t p = src ? src[b] : 0;
+    if (p < 0 || p + span >= kPosLimit)
+      return fail(LAC_ERR_INVALID, "%s: %s[%d] = %lld is outside [0, 2^31 - %lld)", fn, what, b,
+                  (long long)p, (long long)span);
+    if (mult > 1 && p % mult != 0)
+      return fail(LAC_ERR_INVALID, "%s: %s[%d] = %lld is not a multiple of m = %d", fn, what, b,
+                  (long long)p, mult);
+    dst->v[b] = (int32_t)p;
+  }
+  return LAC_OK;
+}
+
+int32_t launch_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(LAC_ERR_DEVICE, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  g_err[0] = 0;
+  return LAC_OK;
+}
+
+int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, int32_t in_dtype,
+                      void* out, int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                      int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                      int64_t kv_bstride, int64_t z_bstride, int64_t out_bstride, void* stream) {
+  if (in_dtype != LAC_F32 && in_dtype != LAC_BF16)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: in_dtype must be LAC_F32 or LAC_BF16", fn);
+  if (out_dtype < LAC_F32 || out_dtype > LAC_KV_E4M3_ROPE_BF16)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
+  if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
+  if (T < 0) return fail(LAC_ERR_INVALID, "%s: T = %d < 0", fn, T);
+  if (m < 1 || m > 256) return fail(LAC_ERR_INVALID, "%s: m = %d outside [1, 256]", fn, m);
+  if (D < 8 || D > 2048 || D % 8) return fail(LAC_ERR_INVALID, "%s: D = %d must be a multiple of 8 in [8, 2048]", fn, D);
+  if (rope_dims < 0 || rope_dims > D || rope_dims % 8)
+    return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, D]", fn, rope_dims);
+  if (rope_dims > 0 && !(rope_theta > 0.f && isfinite(rope_theta)))
+    return fail(LAC_ERR_INVALID, "%s: rope_theta must be positive and finite", fn);
+  const int N = T / m;
+  if (B > 1 && (kv_bstride < T || z_bstride < T || out_bstride < N))
+    return fail(LAC_ERR_INVALID, "%s: batch strides must cover T rows (in) and T/m rows (out)", fn);
+  lac::CompressArgs a{};
+  int32_t st = take_positions(fn, "pos0", pos0, B, T, m, &a.pos0);
+  if (st) return st;
+  if ((int64_t)B * N == 0) { g_err[0] = 0; return LAC_OK; }
+  if (!raw_kv || !logits || !out) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned(raw_kv, 16) || !aligned(logits, 16) || !aligned(out, 16))
+    return fail(LAC_ERR_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  if (out_dtype == LAC_KV_E4M3_ROPE_BF16 && (out_bstride * (int64_t)(D + rope_dims)) % 8)
+    return fail(LAC_ERR_INVALID, "%s: mixed-format batch stride must keep rows 8-byte aligned", fn);
+  a.kv = raw_kv; a.logits = logits; a.out = out;
+  a.in_fmt = in_dtype; a.out_fmt = out_dtype;
+  a.B = B; a.T = T; a.D = D; a.m = m; a.r = rope_dims; a.theta = rope_theta;
+  a.kv_bstride = kv_bstride; a.z_bstride = z_bstride; a.out_bstride = out_bstride;
+  return launch_status(fn, lac::launch_compress(a, static_cast<hipStream_t>(stream)));
+}
+
+struct AttendCommon {
+  const void* q; int32_t q_dtype; const void* kv; int32_t kv_dtype; int32_t N;
+  const void* raw; int32_t T_raw; const int64_t* raw_pos0; int32_t W; const float* sink;
+  float scale; int32_t B, Tq, H, D, r; float theta; const int64_t* q_pos0; void* out;
+  void* ws; size_t ws_bytes; void* stream;
+};
+
+int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32_t* idx, int32_t k,
+                    int32_t m) {
+  if (c.q_dtype != LAC_F32 && c.q_dtype != LAC_BF16)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: q_dtype must be LAC_F32 or LAC_BF16", fn);
+  if (c.kv_dtype < LAC_F32 || c.kv_dtype > LAC_KV_E4M3_ROPE_BF16)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: unknown kv_dtype %d", fn, c.kv_dtype);
+  if ((c.q_dtype == LAC_F32) != (c.kv_dtype == LAC_F32))
+    return fail(LAC_ERR_UNSUPPORTED, "%s: float32 queries need a float32 KV and vice versa", fn);
+  if (c.B < 0 || c.B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, c.B, LAC_MAX_BATCH);
+  if (c.Tq < 0 || c.N < 0 || c.T_raw < 0 || c.W < 0 || c.H < 1)
+    return fail(LAC_ERR_INVALID, "%s: negative size or H < 1", fn);
+  if (c.r < 0 || c.r > c.D || c.r % 8)
+    return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, D]", fn, c.r);
+  if (c.r > 0 && !(c.theta > 0.f && isfinite(c.theta)))
+    return fail(LAC_ERR_INVALID, "%s: rope_theta must be positive and finite", fn);
+  if (!isfinite(c.scale) || c.scale < 0.f) return fail(LAC_ERR_INVALID, "%s: softmax_scale must be finite and >= 0", fn);
+  if (c.q_dtype == LAC_F32) {
+    if (c.D < 8 || c.D > 256 || c.D % 8 || c.H * c.D > 8192)
+      return fail(LAC_ERR_UNSUPPORTED, "%s: float32 path needs D in [8, 256] (multiple of 8) and H*D <= 8192", fn);
+  } else {
+    if (c.D != 128 && c.D != 256 && c.D != 512)
+      return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs D in {128, 256, 512}", fn);
+    if (!((c.H <= 64 && 64 % c.H == 0) || c.H % 64 == 0))
+      return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H dividing 64 or a multiple of 64", fn);
+  }
+  if (mode == 0 && k < 0) return fail(LAC_ERR_INVALID, "%s: k = %d < 0", fn, k);
+  if (mode == 1 && m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
+  lac::AttendArgs a{};
+  int32_t st = take_positions(fn, "q_pos0", c.q_pos0, c.B, c.Tq, 1, &a.qpos);
+  if (st) return st;
+  st = take_positions(fn, "raw_pos0", c.raw_pos0, c.B, c.T_raw, 1, &a.rawpos);
+  if (st) return st;
+  if (c.W > 0) {
+    for (int b = 0; b < c.B; ++b) {
+      const int64_t qp = c.q_pos0 ? c.q_pos0[b] : 0, rp = c.raw_pos0 ? c.raw_pos0[b] : 0;
+      const int64_t lo = qp - c.W + 1 > 0 ? qp - c.W + 1 : 0, hi = qp + c.Tq - 1;
+      if (c.Tq > 0 && (lo < rp || hi >= rp + c.T_raw))
+        return fail(LAC_ERR_INVALID,
+                    "%s: raw window of batch %d needs positions [%lld, %lld] but raw_kv holds [%lld, %lld)",
+                    fn, b, (long long)lo, (long long)hi, (long long)rp, (long long)(rp + c.T_raw));
+    }
+  }
+  const int n_entries = mode == 0 ? k : c.N;
+  const size_t need = lac::attend_workspace_bytes(c.B, c.Tq, c.H, c.D, c.r, c.kv_dtype, n_entries, c.W);
+  if ((int64_t)c.B * c.Tq == 0) { g_err[0] = 0; return LAC_OK; }
+  if (!c.q || !c.out) return fail(LAC_ERR_INVALID, "%s: null q or out", fn);
+  if (c.N > 0 && !c.kv) return fail(LAC_ERR_INVALID, "%s: null compressed cache", fn);
+  if (c.W > 0 && !c.raw) return fail(LAC_ERR_INVALID, "%s: null raw_kv with window > 0", fn);
+  if (mode == 0 && k > 0 && !idx) return fail(LAC_ERR_INVALID, "%s: null topk_idx", fn);
+  if (!aligned(c.q, 16) || !aligned(c.out, 16) || (c.kv && !aligned(c.kv, 16)) ||
+      (c.raw && !aligned(c.raw, 16)) || (idx && !aligned(idx, 4)) || (c.sink && !aligned(c.sink, 4)))
+    return fail(LAC_ERR_INVALID, "%s: misaligned tensor pointer", fn);
+  if (need > 0 && (!c.ws || !aligned(c.ws, 256)))
+    return fail(LAC_ERR_WORKSPACE, "%s: workspace must be non-null and 256-byte aligned", fn);
+  if (c.ws_bytes < need)
+    return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, c.ws_bytes, need);
+  a.q = c.q; a.kv = c.kv; a.idx = idx; a.raw = c.raw; a.sink = c.sink; a.out = c.out;
+  a.q_fmt = c.q_dtype; a.kv_fmt = c.kv_dtype; a.mode = mode;
+  a.N = c.N; a.k = mode == 0 ? k : 0; a.m = mode == 1 ? m : 1; a.T_raw = c.T_raw; a.W = c.W;
+  a.B = c.B; a.Tq = c.Tq; a.H = c.H; a.D = c.D; a.r = c.r; a.theta = c.theta;
+  a.scale = c.scale == 0.f ? 1.0f / sqrtf((float)c.D) : c.scale;
+  a.n_entries = n_entries;
+  return launch_status(fn, lac::launch_attend(a, c.ws, static_cast<hipStream_t>(c.stream)));
+}
+
+}  // namespace
+
+namespace lac {
+
+void arm_timer(int kernel, hipEvent_t start, hipEvent_t stop) {
+  g_timer_kernel = (start && stop) ? kernel : -1;
+  g_timer_start = start;
+  g_timer_stop = stop;
+}
+
+TimedLaunch::TimedLaunch(int kernel, hipStream_t st) {
+  if (kernel == g_timer_kernel && g_timer_start) {
+    (void)hipEventRecord(g_timer_start, st);
+    stop_ = g_timer_stop;
+    st_ = st;
+    g_timer_kernel = -1;
+  }
+}
+
+TimedLaunch::~TimedLaunch() {
+  if (stop_) (void)hipEventRecord(stop_, st_);
+}
+
+}  // namespace lac
+
+extern "C" {
+
+int32_t csa_compress(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                     int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                     int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                     int64_t kv_batch_stride, int64_t logit_batch_stride,
+                     int64_t out_batch_stride, void* stream) {
+  try {
+    return compress_impl("csa_compress", raw_kv, logits, in_dtype, out, out_dtype, B, T, D, m,
+                         rope_dims, rope_theta, pos0, kv_batch_stride, logit_batch_stride,
+                         out_batch_stride, stream);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "csa_compress: internal error");
+  }
+}
+
+int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                     int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                     int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                     int64_t kv_batch_stride, int64_t logit_batch_stride,
+                     int64_t out_batch_stride, void* stream) {
+  try {
+    return compress_impl("hca_compress", raw_kv, logits, in_dtype, out, out_dtype, B, T, D, m,
+                         rope_dims, rope_theta, pos0, kv_batch_stride, logit_batch_stride,
+                         out_batch_stride, stream);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "hca_compress: internal error");
+  }
+}
+
+size_t indexer_topk_workspace_size(int32_t B, int32_t Tq, int32_t N, int32_t k) {
+  if (B < 0 || Tq < 0 || N < 0 || k < 1) return 0;
+  return lac::indexer_workspace_bytes(B, Tq, N, k);
+}
+
+int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32_t dtype,
+                     int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
+                     const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
+                     float* topk_score, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* fn = "indexer_topk";
+  try {
+    if (dtype != LAC_F32 && dtype != LAC_BF16)
+      return fail(LAC_ERR_UNSUPPORTED, "%s: dtype must be LAC_F32 or LAC_BF16", fn);
+    if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
+    if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
+    if (m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
+    if (k < 1 || k > 8192) return fail(LAC_ERR_INVALID, "%s: k = %d outside [1, 8192]", fn, k);
+    if (H_I < 1 || d_I < 1) return fail(LAC_ERR_INVALID, "%s: H_I and d_I must be >= 1", fn);
+    if (dtype == LAC_BF16) {
+      if ((H_I != 32 && H_I != 64 && H_I != 128) || (d_I != 64 && d_I != 128))
+        return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H_I in {32, 64, 128} and d_I in {64, 128}", fn);
+    } else if ((int64_t)H_I * d_I > 8192) {
+      return fail(LAC_ERR_UNSUPPORTED, "%s: float32 path needs H_I * d_I <= 8192", fn);
+    }
+    lac::IndexerArgs a{};
+    int32_t st = take_positions(fn, "q_pos0", q_pos0, B, Tq, 1, &a.qpos);
+    if (st) return st;
+    if ((int64_t)B * Tq == 0) { g_err[0] = 0; return LAC_OK; }
+    if (!q_idx || !w || !topk_idx || (N > 0 && !k_idx)) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
+    if (!aligned(q_idx, 16) || !aligned(w, 4) || (k_idx && !aligned(k_idx, 16)) ||
+        !aligned(topk_idx, 4) || (topk_score && !aligned(topk_score, 4)))
+      return fail(LAC_ERR_INVALID, "%s: misaligned tensor pointer", fn);
+    const size_t need = lac::indexer_workspace_bytes(B, Tq, N, k);
+    if (!workspace || !aligned(workspace, 256))
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace must be non-null and 256-byte aligned", fn);
+    if (workspace_bytes < need)
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
+    a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype;
+    a.B = B; a.Tq = Tq; a.HI = H_I; a.dI = d_I; a.N = N; a.m = m; a.k = k;
+    a.topk_idx = topk_idx; a.topk_score = topk_score;
+    return launch_status(fn, lac::launch_indexer_topk(a, workspace, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "%s: internal error", fn);
+  }
+}
+
+size_t attend_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t D, int32_t rope_dims,
+                             int32_t kv_dtype, int32_t n_entries, int32_t window) {
+  if (B < 0 || Tq < 0 || H < 1 || D < 8 || rope_dims < 0 || n_entries < 0 || window < 0) return 0;
+  if (kv_dtype < LAC_F32 || kv_dtype > LAC_KV_E4M3_ROPE_BF16) return 0;
+  return lac::attend_workspace_bytes(B, Tq, H, D, rope_dims, kv_dtype, n_entries, window);
+}
+
+int32_t csa_attend(const void* q, int32_t q_dtype, const void* ckv, int32_t kv_dtype, int32_t N,
+                   const int32_t* topk_idx, int32_t k, const void* raw_kv, int32_t T_raw,
+                   const int64_t* raw_pos0, int32_t window, const float* sink,
+                   float softmax_scale, int32_t B, int32_t Tq, int32_t H, int32_t D,
+                   int32_t rope_dims, float rope_theta, const int64_t* q_pos0, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  try {
+    AttendCommon c{q, q_dtype, ckv, kv_dtype, N, raw_kv, T_raw, raw_pos0, window, sink,
+                   softmax_scale, B, Tq, H, D, rope_dims, rope_theta, q_pos0, out, workspace,
+                   workspace_bytes, stream};
+    return attend_impl("csa_attend", c, 0, topk_idx, k, 1);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "csa_attend: internal error");
+  }
+}
+
+int32_t hca_attend(const void* q, int32_t q_dtype, const void* hkv, int32_t kv_dtype, int32_t N,
+                   int32_t m, const void* raw_kv, int32_t T_raw, const int64_t* raw_pos0,
+                   int32_t window, const float* sink, float softmax_scale, int32_t B, int32_t Tq,
+                   int32_t H, int32_t D, int32_t rope_dims, float rope_theta,
+                   const int64_t* q_pos0, void* out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  try {
+    AttendCommon c{q, q_dtype, hkv, kv_dtype, N, raw_kv, T_raw, raw_pos0, window, sink,
+                   softmax_scale, B, Tq, H, D, rope_dims, rope_theta, q_pos0, out, workspace,
+                   workspace_bytes, stream};
+    return attend_impl("hca_attend", c, 1, nullptr, 0, m);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "hca_attend: internal error");
+  }
+}
+
+const char* lac_last_error(void) { return g_err; }
+
+int32_t lac_time_next_launch(int32_t kernel, void* start, void* stop) {
+  if (kernel < 0 || kernel >= lac::kKernelCount)
+    return fail(LAC_ERR_INVALID, "lac_time_next_launch: unknown kernel %d", kernel);
+  lac::arm_timer(kernel, static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  return LAC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,182 @@
+// compress.hip -- block-softmax KV compression (CSA m = 4, HCA m' = 128).
+//
+// "深度解析 DeepSeek-V4" (learnblockchain.cn), section "CSA：Compressed Sparse
+// Attention", Step 1 Compress: every m consecutive KV entries merge into one
+// entry with learned softmax weights; section "HCA：Heavily Compressed
+// Attention": the same with m' = 128.  Per channel c of entry j:
+//   out[j, c] = sum_i softmax_i(logits[j*m + i, c]) * kv[j*m + i, c],
+// then the last r dims are rotated at the block start j*m (partial RoPE of the
+// QbitAI rewrite).
+//
+// The kernel is a pure HBM stream: each thread owns 8 consecutive channels
+// (one 16-byte bf16 load per token row, coalesced across the row) of one
+// entry and walks its share of the block's tokens with an online softmax
+// (running max, denominator and weighted sum in fp32).  When a block has
+// many tokens (HCA), S threads split the tokens and merge their partial
+// states through LDS, so short sequences still spread over many lanes.
+#include "lac_internal.h"
+
+namespace lac {
+
+namespace {
+
+template <int IN>
+__device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) {
+  if constexpr (IN == kF32) {
+    const float* p = static_cast<const float*>(base) + elem;
+    const uint4 a = ld_stream16(p), b = ld_stream16(p + 4);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  } else {
+    const uint4 a = ld_stream16(static_cast<const uint16_t*>(base) + elem);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+}
+
+template <int IN, int OUT>
+__global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
+  __shared__ float part[256][25];
+  const int G = a.D >> 3;            // channel groups of 8
+  const int per_entry = G * a.S;     // threads per entry
+  const int epb = 256 / per_entry;   // entries per block
+  const int t = threadIdx.x;
+  const int le = t / per_entry;
+  const int within = t - le * per_entry;
+  const int g = within % G;
+  const int s = within / G;
+  const int N = a.T / a.m;
+  const int64_t e = (int64_t)blockIdx.x * epb + le;
+  const bool live = le < epb && e < (int64_t)a.B * N;
+  const int b = live ? (int)(e / N) : 0;
+  const int j = live ? (int)(e - (int64_t)b * N) : 0;
+
+  float mx[8], den[8], acc[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
+
+  if (live) {
+    const int per = a.m / a.S;
+    const int64_t row0 = (int64_t)j * a.m + (int64_t)s * per;
+    for (int i = 0; i < per; ++i) {
+      float xv[8], zv[8];
+      load8<IN>(a.kv, (b * a.kv_bstride + row0 + i) * a.D + g * 8, xv);
+      load8<IN>(a.logits, (b * a.z_bstride + row0 + i) * a.D + g * 8, zv);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float nm = fmaxf(mx[c], zv[c]);
+        const float sc = __expf(mx[c] - nm);          // 0 on the first token
+        const float p = __expf(zv[c] - nm);
+        den[c] = den[c] * sc + p;
+        acc[c] = acc[c] * sc + p * xv[c];
+        mx[c] = nm;
+      }
+    }
+  }
+
+  if (a.S > 1) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      part[t][c] = mx[c];
+      part[t][8 + c] = den[c];
+      part[t][16 + c] = acc[c];
+    }
+    __syncthreads();
+    if (s != 0) return;
+    for (int o = 1; o < a.S; ++o) {
+      const int u = t + o * G;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float om = part[u][c];
+        const float nm = fmaxf(mx[c], om);
+        const float s0 = __expf(mx[c] - nm), s1 = __expf(om - nm);
+        den[c] = den[c] * s0 + part[u][8 + c] * s1;
+        acc[c] = acc[c] * s0 + part[u][16 + c] * s1;
+        mx[c] = nm;
+      }
+    }
+  }
+  if (!live) return;
+
+  float o[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o[c] = acc[c] / den[c];
+
+  const int c0 = g * 8;
+  const int nope = a.D - a.r;
+  if (c0 >= nope) {
+    const double pos = (double)a.pos0.v[b] + (double)j * a.m;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pair = (c0 - nope) / 2 + q;
+      float cs, sn;
+      rope_cos_sin(pos, rope_inv_freq(pair, a.r, a.theta), &cs, &sn);
+      const float x0 = o[2 * q], x1 = o[2 * q + 1];
+      o[2 * q] = x0 * cs - x1 * sn;
+      o[2 * q + 1] = x0 * sn + x1 * cs;
+    }
+  }
+
+  const int64_t orow = (int64_t)b * a.out_bstride + j;
+  uint8_t* out = static_cast<uint8_t*>(a.out);
+  if constexpr (OUT == kF32) {
+    float4* p = reinterpret_cast<float4*>(out + (orow * a.D + c0) * 4);
+    p[0] = make_float4(o[0], o[1], o[2], o[3]);
+    p[1] = make_float4(o[4], o[5], o[6], o[7]);
+  } else if constexpr (OUT == kBF16) {
+    uint4* p = reinterpret_cast<uint4*>(out + (orow * a.D + c0) * 2);
+    *p = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                    pack_bf16x2(o[6], o[7]));
+  } else {
+    const int64_t rowb = (int64_t)a.D + a.r;
+    uint8_t* rp = out + orow * rowb;
+    if (c0 < nope) {
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        lo |= f32_to_e4m3(o[c]) << (8 * c);
+        hi |= f32_to_e4m3(o[4 + c]) << (8 * c);
+      }
+      *reinterpret_cast<uint2*>(rp + c0) = make_uint2(lo, hi);
+    } else {
+      uint2* p = reinterpret_cast<uint2*>(rp + nope + 2 * (c0 - nope));
+      p[0] = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      p[1] = make_uint2(pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7]));
+    }
+  }
+}
+
+template <int IN, int OUT>
+hipError_t launch(const CompressArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((compress_kernel<IN, OUT>), dim3(grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(CompressArgs a, hipStream_t st) {
+  const int G = a.D / 8;
+  int S = 1;
+  while (a.m / S > 8 && G * S * 2 <= 256 && a.m % (2 * S) == 0) S *= 2;
+  a.S = S;
+  const int epb = 256 / (G * S);
+  const int64_t entries = (int64_t)a.B * (a.T / a.m);
+  if (entries == 0) return hipSuccess;
+  const int grid = (int)((entries + epb - 1) / epb);
+  TimedLaunch tl(kKernelCompress, st);
+  if (a.in_fmt == kF32) {
+    if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, st);
+    if (a.out_fmt == kBF16) return launch<kF32, kBF16>(a, grid, st);
+    return launch<kF32, kMixed>(a, grid, st);
+  }
+  if (a.out_fmt == kF32) return launch<kBF16, kF32>(a, grid, st);
+  if (a.out_fmt == kBF16) return launch<kBF16, kBF16>(a, grid, st);
+  return launch<kBF16, kMixed>(a, grid, st);
+}
+
+}  // namespace lac

@@ -1,0 +1,110 @@
+// lac_device.h -- device helpers shared by the gfx950 kernels of the library:
+// number formats, rotary angles, MFMA operand types and small reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lac {
+
+constexpr int kWave = 64;
+constexpr int kMaxBatch = 128;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Streaming loads (read-once data): non-temporal hint, 16 or 8 bytes.
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld_stream8(const void* p) {
+  const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+  return make_uint2(v.x, v.y);
+}
+
+enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2 };
+
+// Per-batch positions passed by value (the library keeps nothing on the device).
+struct Positions {
+  int32_t v[kMaxBatch];
+};
+
+// ---------------------------------------------------------------- bfloat16
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------- FP8 E4M3 ("fn")
+// Exponent bias 7, largest finite 448, subnormal step 2^-9, 0x7f/0xff NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t em = b & 0x7fu;
+  float v = em >= 8u ? __uint_as_float((em << 20) + (120u << 23))   // normal: rebias 7 -> 127
+                     : (float)em * 0.001953125f;                    // subnormal: em * 2^-9
+  if (em == 0x7fu) v = __uint_as_float(0x7fc00000u);
+  return (b & 0x80u) ? -v : v;
+}
+
+// Round to nearest even, saturate to +-448, NaN -> 0x7f.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  const float af = __uint_as_float(a);
+  if (af >= 448.0f) return s | 0x7eu;
+  if (af < 0.015625f) {                              // below 2^-6: multiples of 2^-9
+    return s | (uint32_t)__builtin_rintf(af * 512.0f);  // 8 encodes 2^-6 exactly
+  }
+  const uint32_t r = (a + 0x7ffffu + ((a >> 20) & 1u)) & 0xfff00000u;  // keep 3 mantissa bits
+  return s | ((((r >> 23) - 120u) << 3) | ((r >> 20) & 7u));
+}
+
+// ---------------------------------------------------------------- rotary angles
+// Rotation of pair i (of r/2) at integer position p by angle p * theta^(-2i/r).
+// The product and its reduction modulo 2*pi are taken in double, so the angle
+// stays exact to float precision at positions in the millions.
+__device__ __forceinline__ double rope_inv_freq(int i, int r, float theta) {
+  return exp2(-2.0 * (double)i / (double)r * log2((double)theta));
+}
+
+__device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float* c, float* s) {
+  const double a = pos * inv_freq;
+  const double k = rint(a * 0.15915494309189535);          // a / (2 pi)
+  double red = fma(-k, 6.283185307179586, a);              // 2 pi, high part
+  red = fma(-k, 2.4492935982947064e-16, red);              // 2 pi, low part
+  sincosf((float)red, s, c);
+}
+
+// ---------------------------------------------------------------- selection keys
+// Order-preserving map of a float score to uint32 (larger score -> larger key).
+// -0 is folded onto +0 so that equal scores compare equal.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// ---------------------------------------------------------------- positions
+__device__ __forceinline__ int64_t n_visible(int64_t t, int64_t N, int m) {
+  const int64_t n = t >= 0 ? t / m : 0;
+  return n < N ? n : N;
+}
+
+}  // namespace lac

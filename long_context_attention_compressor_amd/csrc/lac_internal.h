@@ -1,0 +1,81 @@
+// lac_internal.h -- launch interfaces between the C ABI (abi.cpp) and the
+// kernel files.  Everything here is host-visible and takes plain values.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lac_device.h"
+
+namespace lac {
+
+enum KernelId {
+  kKernelCompress = 0,
+  kKernelIndexerScore = 1,
+  kKernelTopk = 2,
+  kKernelAttend = 3,
+  kKernelCombine = 4,
+  kKernelCount = 5
+};
+
+// One-shot, thread-local launch timer (see lac_time_next_launch).  Records the
+// armed start event on construction and the stop event on destruction when
+// this launch is of the armed kernel.
+struct TimedLaunch {
+  TimedLaunch(int kernel, hipStream_t st);
+  ~TimedLaunch();
+  hipEvent_t stop_ = nullptr;
+  hipStream_t st_ = nullptr;
+};
+void arm_timer(int kernel, hipEvent_t start, hipEvent_t stop);
+
+// ---------------------------------------------------------------- compress
+struct CompressArgs {
+  const void* kv;
+  const void* logits;
+  void* out;
+  int in_fmt, out_fmt;
+  int B, T, D, m, r;
+  float theta;
+  int64_t kv_bstride, z_bstride, out_bstride;  // rows
+  int S;                                       // token splits (set by the launcher)
+  Positions pos0;
+};
+hipError_t launch_compress(CompressArgs a, hipStream_t st);
+
+// ---------------------------------------------------------------- indexer + top-k
+struct IndexerArgs {
+  const void* q;         // [B, Tq, HI, dI]
+  const float* w;        // [B, Tq, HI]
+  const void* K;         // [B, N, dI]
+  int fmt;               // kF32 | kBF16
+  int B, Tq, HI, dI, N, m, k;
+  int32_t* topk_idx;     // [B, Tq, k]
+  float* topk_score;     // [B, Tq, k] or null
+  Positions qpos;
+};
+size_t indexer_workspace_bytes(int B, int Tq, int N, int k);
+hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- attention
+struct AttendArgs {
+  const void* q;          // [B, Tq, H, D]
+  const void* kv;         // [B, N, row]
+  const int32_t* idx;     // [B, Tq, k] (CSA) or null (HCA)
+  const void* raw;        // [B, T_raw, row]
+  const float* sink;      // [H] or null
+  void* out;              // [B, Tq, H, D]
+  int q_fmt, kv_fmt;
+  int mode;               // 0 = CSA, 1 = HCA
+  int N, k, m, T_raw, W;
+  int B, Tq, H, D, r;
+  float theta, scale;
+  int n_entries;          // k (CSA) or N (HCA): sizes the split plan
+  Positions qpos, rawpos;
+};
+size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries,
+                              int W);
+hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st);
+
+}  // namespace lac

@@ -1,0 +1,91 @@
+"""Shared checks for the GPU-vs-oracle parity tests (test infrastructure).
+
+Tolerances (written here once, used by every parity test):
+  * compressed entries: |g - r| <= 2^-8 |r| + 1e-6 in bf16 dims,
+    1e-5 |r| + 1e-6 in float32, and within one E4M3 code (value step) in FP8
+    dims -- the storage rounding of the GPU's fp32 result may land on the
+    other side of a rounding boundary from the oracle's double result;
+  * top-k: identical sets except entries whose oracle score lies within
+    1e-3 |s_k| + 1e-6 of the oracle's k-th score (near-ties);
+  * attention outputs: per (b, t, h) row, max_c |g - r| / max_c |r| <= 1e-2
+    (bf16 operands, fp32 accumulation), r the oracle's double result.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+ATTN_TOL = 1e-2
+TIE_REL, TIE_ABS = 1e-3, 1e-6
+
+
+def host(t: torch.Tensor):
+    return synth.host_bytes(t)
+
+
+def as_f64(t: torch.Tensor) -> np.ndarray:
+    """GPU result -> float64 (through PyTorch's own conversion)."""
+    return t.detach().float().cpu().double().numpy()
+
+
+def check_compressed(gpu: torch.Tensor, ref: np.ndarray, fmt: str, D: int, r: int):
+    """gpu: stored entries [..., row]; ref: oracle doubles [..., D]."""
+    ref = ref.reshape(-1, D)
+    if fmt == "f32":
+        g = as_f64(gpu).reshape(-1, D)
+        bad = np.abs(g - ref) > 1e-5 * np.abs(ref) + 1e-6
+    elif fmt == "bf16":
+        g = as_f64(gpu).reshape(-1, D)
+        bad = np.abs(g - ref) > 2.0 ** -8 * np.abs(ref) + 1e-6
+    else:
+        rowb = (D - r) + 2 * r
+        raw = gpu.detach().cpu().numpy().reshape(-1, rowb)
+        g = oracle.decode_rows(np.ascontiguousarray(raw), oracle.MIXED, D, r)
+        fp8 = g[:, : D - r]
+        ref8 = ref[:, : D - r]
+        # one E4M3 step at the value's binade (2^-9 below 2^-6)
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref8), 2.0 ** -6))) - 3),
+                          2.0 ** -9)
+        bad8 = np.abs(fp8 - np.clip(ref8, -448, 448)) > step * (1 + 1e-9)
+        badb = np.abs(g[:, D - r:] - ref[:, D - r:]) > 2.0 ** -8 * np.abs(ref[:, D - r:]) + 1e-6
+        bad = np.concatenate([bad8, badb], axis=1)
+    assert not bad.any(), f"{int(bad.sum())} of {bad.size} compressed values out of tolerance"
+
+
+def check_topk(gpu_idx: np.ndarray, o_idx: np.ndarray, o_scores: np.ndarray, nvis: np.ndarray,
+               k: int):
+    """Rows of GPU indices vs oracle indices under the near-tie rule.
+    Returns the rows whose sets are identical."""
+    same_rows = []
+    for rr in range(gpu_idx.shape[0]):
+        nv = int(nvis[rr])
+        keff = min(k, nv)
+        g = gpu_idx[rr]
+        assert (g[keff:] == -1).all(), f"row {rr}: padding"
+        gs = g[:keff]
+        assert len(set(gs.tolist())) == keff, f"row {rr}: duplicates"
+        assert ((gs >= 0) & (gs < nv)).all(), f"row {rr}: invisible index"
+        osel = set(o_idx[rr, :keff].tolist())
+        diff = set(gs.tolist()) ^ osel
+        if diff:
+            s = o_scores[rr, :nv]
+            sk = np.sort(s)[::-1][keff - 1]
+            for j in diff:
+                assert abs(s[j] - sk) <= TIE_REL * abs(sk) + TIE_ABS, \
+                    f"row {rr}: index {j} score {s[j]} vs k-th {sk}"
+        else:
+            same_rows.append(rr)
+    return same_rows
+
+
+def check_attention(gpu: np.ndarray, ref: np.ndarray, what=""):
+    """gpu, ref: [rows, H, D] float64."""
+    num = np.abs(gpu - ref).max(axis=-1)
+    den = np.abs(ref).max(axis=-1)
+    rel = np.where(den > 0, num / np.maximum(den, 1e-300), num)
+    worst = float(rel.max()) if rel.size else 0.0
+    assert worst <= ATTN_TOL, f"{what}: worst row relative error {worst:.3e}"
+    return worst

@@ -1,0 +1,138 @@
+"""GPU parity of csa_attend / hca_attend against the oracle's core attention
+(QbitAI rewrite: MQA over the selected compressed blocks, KV = key = value,
+output rotated at -i, strict causality; 深度解析 DeepSeek-V4: HCA dense
+attention, Sliding Window Branch, Attention Sink).  Selected indices are
+seeded random subsets of the visible entries, shared by both sides."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_compressor_amd as lac
+import oracle
+import synth
+from parity import as_f64, check_attention, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMT_T = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _indices(seed, B, Tq, q_pos0, N, m, k, holes=True):
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, Tq, k), -1, np.int32)
+    for b in range(B):
+        for i in range(Tq):
+            nv = min(N, (q_pos0[b] + i) // m)
+            n = min(k, nv)
+            sel = np.sort(rng.choice(nv, n, replace=False)) if n else np.zeros(0, int)
+            if holes and n > 2:
+                sel[rng.integers(0, n)] = -1          # a skipped slot inside the list
+            idx[b, i, :n] = sel
+    return idx
+
+
+def _case(mode, B, Tq, H, D, r, N, k, m, W, q_pos0, fmt, seed, sink=False, rows=None):
+    print(f"attend mode={mode} B={B} Tq={Tq} H={H} D={D} N={N} k={k} m={m} W={W} {fmt} "
+          f"sink={sink}", flush=True)
+    q_fmt = "f32" if fmt == "f32" else "bf16"
+    q = synth.store(synth.normal(seed, "q", (B, Tq, H, D)), q_fmt)
+    kv = synth.store(synth.normal(seed, "kv", (B, N, D)), fmt, r)
+    raw_pos0 = [max(0, p - W + 1) for p in q_pos0]
+    T_raw = max(q_pos0[b] + Tq - raw_pos0[b] for b in range(B)) if W > 0 else 0
+    raw = synth.store(synth.normal(seed, "raw", (B, max(T_raw, 1), D)), fmt, r)
+    sk = synth.normal(seed, "sink", (H,)) * 2.0 if sink else None
+    out = torch.empty((B, Tq, H, D), dtype=FMT_T[q_fmt], device=DEV)
+    if mode == 0:
+        idx = _indices(seed, B, Tq, q_pos0, N, m, k)
+        lac.csa_attend(q.to(DEV), kv.to(DEV), torch.from_numpy(idx).to(DEV), raw.to(DEV), W,
+                       q_pos0=q_pos0, raw_pos0=raw_pos0, rope_dims=r,
+                       sink=None if sk is None else sk.to(DEV), out=out)
+    else:
+        idx = None
+        lac.hca_attend(q.to(DEV), kv.to(DEV), raw.to(DEV), W, m=m, q_pos0=q_pos0,
+                       raw_pos0=raw_pos0, rope_dims=r, sink=None if sk is None else sk.to(DEV),
+                       out=out)
+    torch.cuda.synchronize()
+    rr = [(b, i) for b in range(B) for i in range(Tq)] if rows is None else rows
+    o_idx = None if idx is None else np.ascontiguousarray(
+        np.stack([idx[b, i] for b, i in rr]))
+    code = synth.DTYPE_CODES[fmt]
+    ref = oracle.attend(host(q), synth.DTYPE_CODES[q_fmt], host(kv), code, N, mode, o_idx, k, m,
+                        host(raw), raw.shape[1], raw_pos0, W,
+                        None if sk is None else host(sk).astype(np.float64), 0.0, B, Tq, H, D, r,
+                        10000.0, q_pos0, rr)
+    g = as_f64(out)
+    g = np.stack([g[b, i] for b, i in rr])
+    return check_attention(g, ref, f"mode {mode} {fmt}")
+
+
+def test_csa_f32_tiny_prefill():
+    _case(0, 1, 256, 8, 128, 64, 64, 16, 4, 8, [0], "f32", 0)
+
+
+def test_csa_f32_with_sink():
+    _case(0, 2, 9, 8, 128, 64, 30, 5, 4, 3, [100, 7], "f32", 1, sink=True)
+
+
+def test_csa_bf16_decode_split():
+    _case(0, 3, 1, 64, 512, 64, 3000, 256, 4, 128, [12000, 12003, 8000], "bf16", 2)
+
+
+def test_csa_mixed_decode_split():
+    _case(0, 2, 1, 64, 512, 64, 2000, 512, 4, 128, [8000, 1 << 20], "mixed", 3)
+
+
+def test_csa_bf16_decode_with_sink():
+    _case(0, 2, 1, 64, 512, 64, 1000, 128, 4, 128, [4000, 4001], "bf16", 4, sink=True)
+
+
+def test_csa_bf16_prefill_rows():
+    _case(0, 1, 20, 64, 512, 64, 1300, 64, 4, 128, [5000], "bf16", 5)
+
+
+def test_csa_bf16_grouped_queries_h16():
+    _case(0, 1, 13, 16, 128, 64, 500, 32, 4, 128, [1990], "bf16", 6)
+
+
+def test_csa_bf16_two_head_tiles_d256():
+    _case(0, 2, 2, 128, 256, 64, 700, 40, 4, 64, [2790, 300], "bf16", 7)
+
+
+def test_csa_window_clipped_and_nothing_compressed():
+    _case(0, 1, 10, 64, 128, 64, 4, 4, 4, 4, [0], "bf16", 8)
+
+
+def test_csa_no_window():
+    _case(0, 2, 1, 64, 512, 64, 900, 100, 4, 0, [3600, 3000], "bf16", 9)
+
+
+def test_hca_bf16_prefill():
+    _case(1, 1, 1024, 16, 128, 64, 8, 0, 128, 128, [0], "bf16", 10)
+
+
+def test_hca_mixed_decode_split():
+    _case(1, 2, 1, 64, 512, 64, 600, 0, 128, 128, [600 * 128, 599 * 128 + 5], "mixed", 11)
+
+
+def test_hca_bf16_decode_sink_d256():
+    _case(1, 2, 1, 64, 256, 64, 200, 0, 128, 128, [200 * 128, 50 * 128], "bf16", 12, sink=True)
+
+
+def test_hca_f32_prefill():
+    _case(1, 1, 300, 8, 128, 64, 8, 0, 32, 16, [0], "f32", 13)
+
+
+def test_hca_blocks_of_one_window_one_rows():
+    _case(1, 1, 70, 16, 128, 64, 70, 0, 1, 1, [0], "bf16", 14)
+
+
+def test_attend_determinism():
+    B, N, k, H, D = 2, 1500, 300, 64, 512
+    q = synth.store(synth.normal(20, "q", (B, 1, H, D)), "bf16").to(DEV)
+    kv = synth.store(synth.normal(20, "kv", (B, N, D)), "bf16").to(DEV)
+    raw = synth.store(synth.normal(20, "raw", (B, 128, D)), "bf16").to(DEV)
+    idx = torch.from_numpy(_indices(20, B, 1, [6000, 6000], N, 4, k)).to(DEV)
+    outs = [lac.csa_attend(q, kv, idx, raw, 128, q_pos0=[6000] * B, raw_pos0=[5873] * B)
+            for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])

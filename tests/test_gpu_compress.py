@@ -1,0 +1,93 @@
+"""GPU parity of csa_compress / hca_compress against the oracle's compressor
+(深度解析 DeepSeek-V4, CSA Step 1 Compress and the HCA section), on seeded
+inputs, with ragged block counts, batch strides and every storage format."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_compressor_amd as lac
+import oracle
+import synth
+from parity import check_compressed, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMTS = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _run(B, T, D, m, r, in_fmt, out_fmt, pos0, seed, z_std=1.0, hca=False):
+    print(f"compress B={B} T={T} D={D} m={m} r={r} {in_fmt}->{out_fmt}", flush=True)
+    x = synth.store(synth.normal(seed, "x", (B, T, D)), in_fmt)
+    z = synth.store(synth.normal(seed, "z", (B, T, D), std=z_std), in_fmt)
+    N = T // m
+    if out_fmt == "mixed":
+        out = torch.full((B, N, D + r), 0x55, dtype=torch.uint8, device=DEV)
+    else:
+        out = torch.full((B, N, D), 7.0, dtype=FMTS[out_fmt], device=DEV)
+    fn = lac.hca_compress if hca else lac.csa_compress
+    fn(x.to(DEV), z.to(DEV), out, m=m, rope_dims=r, pos0=pos0)
+    torch.cuda.synchronize()
+    ref = oracle.compress(host(x), host(z), synth.DTYPE_CODES[in_fmt], B, T, D, m, r, 10000.0,
+                          pos0)
+    check_compressed(out, ref, out_fmt, D, r)
+
+
+def test_csa_f32_tiny_prefill():
+    _run(1, 256, 128, 4, 64, "f32", "f32", [0], 0)
+
+
+def test_hca_bf16_prefill():
+    _run(1, 8192, 128, 128, 64, "bf16", "bf16", [0], 1, z_std=0.5, hca=True)
+
+
+def test_csa_bf16_to_mixed_ragged_at_1m_positions():
+    _run(2, 4 * 37 + 3, 512, 4, 64, "bf16", "mixed", [0, (1 << 20) - 4 * 40], 2)
+
+
+def test_hca_bf16_to_mixed_at_1m_positions():
+    _run(2, 128 * 3 + 17, 512, 128, 64, "bf16", "mixed", [1 << 20, 4096], 3, hca=True)
+
+
+@pytest.mark.parametrize("m", [1, 2, 8, 16, 32, 64, 256])
+def test_block_sizes_and_no_rope(m):
+    _run(2, m * 5 + (m // 2), 256, m, 0, "bf16", "bf16", [0, 4096 * m], 4 + m)
+
+
+def test_indexer_keys_f32_no_rope():
+    _run(3, 64, 32, 4, 0, "f32", "f32", None, 5)
+
+
+def test_batch_strides_write_into_a_cache_slice():
+    B, T, D, m, r = 2, 64, 128, 4, 64
+    x = synth.store(synth.normal(9, "x", (B, T + 8, D)), "bf16").to(DEV)
+    z = synth.store(synth.normal(9, "z", (B, T, D)), "bf16").to(DEV)
+    cache = torch.zeros((B, 100, D), dtype=torch.bfloat16, device=DEV)
+    view_in = x[:, 8:]                      # rows 8.. of a larger raw buffer
+    view_out = cache[:, 40:]                # rows 40.. of a larger cache
+    lac.csa_compress(view_in, z, view_out, m=m, rope_dims=r, pos0=[160, 160], T=T)
+    torch.cuda.synchronize()
+    ref = oracle.compress(host(x[:, 8:].contiguous()), host(z), synth.BF16, B, T, D, m, r,
+                          10000.0, 160)
+    check_compressed(cache[:, 40:40 + T // m].contiguous(), ref, "bf16", D, r)
+    assert (cache[:, :40] == 0).all() and (cache[:, 40 + T // m:] == 0).all()
+
+
+def test_fewer_tokens_than_a_block_writes_nothing():
+    x = torch.ones((1, 3, 128), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((1, 1, 128), 5.0, dtype=torch.bfloat16, device=DEV)
+    lac.csa_compress(x, x, out, m=4)
+    torch.cuda.synchronize()
+    assert (out == 5.0).all()
+
+
+def test_constant_kv_and_determinism():
+    B, T, D = 1, 512, 512
+    x = torch.full((B, T, D), 0.375, dtype=torch.bfloat16, device=DEV)
+    z = synth.store(synth.normal(11, "z", (B, T, D)), "bf16").to(DEV)
+    o1 = torch.empty((B, T // 128, D), dtype=torch.bfloat16, device=DEV)
+    o2 = torch.empty_like(o1)
+    lac.hca_compress(x, z, o1, m=128, rope_dims=0)
+    lac.hca_compress(x, z, o2, m=128, rope_dims=0)
+    torch.cuda.synchronize()
+    assert (o1.float() == 0.375).all()
+    assert torch.equal(o1, o2)
