@@ -165,8 +165,9 @@ def compress(x, z, in_dtype, B, T, D, m, r=0, theta=10000.0, pos0=None,
     N = T // m
     out = np.empty((B, N, D), np.float64)
     alpha = np.empty((B, N, m, D), np.float64) if want_weights else None
+    pos = _i64(pos0, B)        # held until the call returns
     rc = _load().lo_compress(_p(x), _p(z), in_dtype, B, T, D, m, r, float(theta),
-                             _p(_i64(pos0, B)), T if x_bstride is None else x_bstride,
+                             _p(pos), T if x_bstride is None else x_bstride,
                              T if z_bstride is None else z_bstride, _p(out), _p(alpha))
     if rc:
         raise ValueError(f"lo_compress rejected its arguments ({rc})")
@@ -186,8 +187,9 @@ def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None):
     scores = np.empty((n, N), np.float64)
     nvis = np.empty(n, np.int32)
     w = np.ascontiguousarray(w, np.float32)
+    qpos = _i64(qpos0, B)      # held until the call returns
     rc = _load().lo_index_scores(_p(q), _p(w), _p(K), dtype, B, Tq, HI, dI, N,
-                                 _p(_i64(qpos0, B)), m, _p(rows), n, _p(scores), _p(nvis))
+                                 _p(qpos), m, _p(rows), n, _p(scores), _p(nvis))
     if rc:
         raise ValueError(f"lo_index_scores rejected its arguments ({rc})")
     return scores, nvis
@@ -214,9 +216,10 @@ def attend(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W
         idx = np.ascontiguousarray(idx, np.int32)
     if sink is not None:
         sink = np.ascontiguousarray(sink, np.float64)
+    rpos, qpos = _i64(raw_pos0, B), _i64(qpos0, B)   # held until the call returns
     rc = _load().lo_attend(_p(q), q_dtype, _p(kv), kv_dtype, N, mode, _p(idx), k, m, _p(raw),
-                           T_raw, _p(_i64(raw_pos0, B)), W, _p(sink), float(scale), B, Tq, H, D,
-                           r, float(theta), _p(_i64(qpos0, B)), _p(rows), n, _p(out))
+                           T_raw, _p(rpos), W, _p(sink), float(scale), B, Tq, H, D,
+                           r, float(theta), _p(qpos), _p(rows), n, _p(out))
     if rc:
         raise ValueError(f"lo_attend rejected its arguments ({rc})")
     return out
