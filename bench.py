@@ -1,0 +1,419 @@
+"""Throughput of the hybrid compressed attention path on one MI355X.
+
+Default workload (pair_decode_1m): one decode step of a CSA + HCA layer pair
+for 4 sequences at position 2^20 -- compress the newest complete blocks (CSA
+entry, indexer key, HCA entry), index 262144 compressed entries per sequence
+and keep the top 2048, sparse CSA attention and dense HCA attention over
+8192 entries, each with a 128-token raw window; 64 query heads, 512-dim KV
+stored as FP8 E4M3 with the 64 rotated dims in bf16.  The metric is decode
+tokens/s (4 per step) with the algorithmic HBM GB/s beside it.  Three
+independent cache sets rotate so that a step never finds its 294 MB working
+set in the 256 MB Infinity Cache.
+
+Other workloads (--workload): csa_decode_128k (32 sequences at 131072),
+csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
+hca_prefill_8k (8192 tokens; TFLOP/s).
+
+Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import torch  # noqa: E402
+
+METRIC = "CSA+HCA decode tokens/s and HBM GB/s at 128K-1M ctx; prefill TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def _rows(t, r0, r1):
+    return t[:, r0:r1]
+
+
+# ---------------------------------------------------------------- workloads
+class PairDecode:
+    name = "pair_decode_1m"
+    unit = "tokens/s"
+
+    def __init__(self, lac, synth, dev, sets, seed=4, B=4, ctx=1 << 20):
+        self.lac, self.B, self.ctx = lac, B, ctx
+        self.sets = [synth.pair_decode(seed=seed + 1000 * s, B=B, ctx=ctx, device=dev)
+                     for s in range(sets)]
+        c = self.sets[0]
+        self.c = c
+        self.idx = torch.empty((B, 1, c["k"]), dtype=torch.int32, device=dev)
+        self.out_csa = torch.empty_like(c["q_csa"])
+        self.out_hca = torch.empty_like(c["q_hca"])
+        self.ws_idx = torch.empty(lac.indexer_topk_workspace_size(B, 1, c["N"], c["k"]),
+                                  dtype=torch.uint8, device=dev)
+        self.ws_csa = torch.empty(lac.attend_workspace_size(B, 1, c["H"], c["D"], c["r"], 2, c["k"],
+                                                            c["W"]), dtype=torch.uint8, device=dev)
+        self.ws_hca = torch.empty(lac.attend_workspace_size(B, 1, c["H"], c["D"], c["r"], 2,
+                                                            c["Nh"], c["W"]),
+                                  dtype=torch.uint8, device=dev)
+
+    def step(self, i, timer=None):
+        lac, c, s = self.lac, self.c, self.sets[i % len(self.sets)]
+        N, Nh, m, mh, ctx = c["N"], c["Nh"], c["m"], c["m_hca"], self.ctx
+        lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
+                         rope_dims=c["r"], pos0=ctx - m)
+        lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m, rope_dims=0,
+                         pos0=ctx - m)
+        lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh), m=mh,
+                         rope_dims=c["r"], pos0=ctx - mh)
+        if timer is not None:
+            lac.time_next_launch("indexer_score", *timer)
+        lac.indexer_topk(s["qI"], s["w"], s["KI"], m=m, k=c["k"], q_pos0=ctx, topk_idx=self.idx,
+                         workspace=self.ws_idx)
+        lac.csa_attend(s["q_csa"], s["ckv"], self.idx, s["raw_csa"], c["W"], q_pos0=ctx,
+                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_csa,
+                       workspace=self.ws_csa)
+        lac.hca_attend(s["q_hca"], s["hkv"], s["raw_hca"], c["W"], m=mh, q_pos0=ctx,
+                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_hca,
+                       workspace=self.ws_hca)
+
+    def tokens_per_step(self):
+        return self.B
+
+    def bytes_per_step(self):
+        c = self.c
+        row = c["D"] - c["r"] + 2 * c["r"]
+        per_seq = (c["N"] * c["dI"] * 2 + c["HI"] * c["dI"] * 2 + c["HI"] * 4   # indexer
+                   + c["k"] * row + c["Nh"] * row + 2 * c["W"] * row               # gathers
+                   + 2 * c["H"] * c["D"] * 2 * 2)                                   # q, out
+        compress = ((c["m"] * c["D"] + c["m"] * c["dI"] + c["m_hca"] * c["D"]) * 2 * 2
+                    + 2 * row + c["dI"] * 2)
+        return self.B * (per_seq + compress)
+
+    def indexer_bytes_per_launch(self):
+        c = self.c
+        return self.B * (c["N"] * c["dI"] * 2 + c["HI"] * c["dI"] * 2 + c["HI"] * 4)
+
+    def config(self):
+        c = self.c
+        return {"workload": self.name, "batch": self.B, "ctx": self.ctx, "topk": c["k"],
+                "window": c["W"], "heads": c["H"], "kv_dim": c["D"], "rope_dims": c["r"],
+                "indexer": f"{c['HI']}x{c['dI']} bf16", "csa_entries": c["N"],
+                "hca_entries": c["Nh"], "kv_format": "e4m3 + bf16 rope dims (576 B/entry)",
+                "cache_sets": len(self.sets)}
+
+    def cpu_sample(self):
+        """The oracle's whole decode step for sequence 0 of cache set 0."""
+        import numpy as np
+
+        import oracle
+        from oracle import chain
+        import synth
+
+        c, s, ctx = self.c, self.sets[0], self.ctx
+        h = {k_: synth.host_bytes(v[:1]) for k_, v in s.items() if isinstance(v, torch.Tensor)}
+        N, Nh = c["N"], c["Nh"]
+        t0 = time.perf_counter()
+        ckv = h["ckv"].reshape(1, N, -1).copy()
+        KI = h["KI"].reshape(1, N, -1).copy()
+        hkv = h["hkv"].reshape(1, Nh, -1).copy()
+        ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16", "mixed", 1,
+                                              c["m"], c["D"], c["m"], c["r"], 1e4, ctx - c["m"])
+        KI.view(np.uint8)[:, N - 1:] = chain.compress_store(
+            h["new_kI"], h["new_zI"], "bf16", "bf16", 1, c["m"], c["dI"], c["m"], 0, 1e4,
+            ctx - c["m"])
+        hkv[:, Nh - 1:] = chain.compress_store(h["new_kv_hca"], h["new_z_hca"], "bf16", "mixed",
+                                               1, c["m_hca"], c["D"], c["m_hca"], c["r"], 1e4,
+                                               ctx - c["m_hca"])
+        idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, "bf16", 1, 1, c["HI"], c["dI"], N, ctx,
+                                     c["m"], c["k"])
+        oracle.attend(h["q_csa"], oracle.BF16, ckv, oracle.MIXED, N, 0, idx, c["k"], c["m"],
+                      h["raw_csa"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
+                      c["r"], 1e4, ctx)
+        oracle.attend(h["q_hca"], oracle.BF16, hkv, oracle.MIXED, Nh, 1, None, 0, c["m_hca"],
+                      h["raw_hca"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
+                      c["r"], 1e4, ctx)
+        el = time.perf_counter() - t0
+        return {"value": 1.0 / el, "unit": self.unit, "seconds": el,
+                "sample": "the full decode step (compress newest blocks, index 262144 entries, "
+                          "top-2048, CSA + HCA attention, 64 heads) of 1 of the 4 sequences, "
+                          "cache set 0"}
+
+
+class CsaDecode(PairDecode):
+    name = "csa_decode_128k"
+
+    def __init__(self, lac, synth, dev, sets, seed=2, B=32, ctx=131072):
+        self.lac, self.B, self.ctx = lac, B, ctx
+        self.sets = [synth.csa_decode(seed=seed + 1000 * s, B=B, ctx=ctx, device=dev)
+                     for s in range(sets)]
+        c = self.c = self.sets[0]
+        self.idx = torch.empty((B, 1, c["k"]), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(c["q"])
+        self.ws_idx = torch.empty(lac.indexer_topk_workspace_size(B, 1, c["N"], c["k"]),
+                                  dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(lac.attend_workspace_size(B, 1, c["H"], c["D"], c["r"], 1, c["k"],
+                                                        c["W"]), dtype=torch.uint8, device=dev)
+
+    def step(self, i, timer=None):
+        lac, c, s = self.lac, self.c, self.sets[i % len(self.sets)]
+        if timer is not None:
+            lac.time_next_launch("indexer_score", *timer)
+        lac.indexer_topk(s["qI"], s["w"], s["KI"], m=c["m"], k=c["k"], q_pos0=self.ctx,
+                         topk_idx=self.idx, workspace=self.ws_idx)
+        lac.csa_attend(s["q"], s["ckv"], self.idx, s["raw"], c["W"], q_pos0=self.ctx,
+                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out, workspace=self.ws)
+
+    def bytes_per_step(self):
+        c = self.c
+        return self.B * (c["N"] * c["dI"] * 2 + c["HI"] * c["dI"] * 2 + c["HI"] * 4
+                         + (c["k"] + c["W"]) * c["D"] * 2 + 2 * c["H"] * c["D"] * 2)
+
+    def config(self):
+        c = self.c
+        return {"workload": self.name, "batch": self.B, "ctx": self.ctx, "topk": c["k"],
+                "window": c["W"], "heads": c["H"], "kv_dim": c["D"],
+                "indexer": f"{c['HI']}x{c['dI']} bf16", "csa_entries": c["N"], "kv_format": "bf16",
+                "cache_sets": len(self.sets)}
+
+    def cpu_sample(self):
+        import oracle
+        from oracle import chain
+        import synth
+
+        c, s = self.c, self.sets[0]
+        h = {k_: synth.host_bytes(v[:1]) for k_, v in s.items() if isinstance(v, torch.Tensor)}
+        t0 = time.perf_counter()
+        idx, _, _ = chain.csa_select(h["qI"], h["w"], h["KI"], "bf16", 1, 1, c["HI"], c["dI"],
+                                     c["N"], self.ctx, c["m"], c["k"])
+        oracle.attend(h["q"], oracle.BF16, h["ckv"], oracle.BF16, c["N"], 0, idx, c["k"], c["m"],
+                      h["raw"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
+                      c["r"], 1e4, self.ctx)
+        el = time.perf_counter() - t0
+        return {"value": 1.0 / el, "unit": self.unit, "seconds": el,
+                "sample": "the decode step of 1 of the 32 sequences, cache set 0"}
+
+
+class ChunkPrefill:
+    name = "csa_chunk_prefill"
+    unit = "TFLOP/s"
+
+    def __init__(self, lac, synth, dev, sets, seed=3):
+        self.lac = lac
+        c = self.c = synth.csa_chunk_prefill(seed=seed, device=dev)
+        T = c["chunk"]
+        self.idx = torch.empty((1, T, c["k"]), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(c["q"])
+        self.ws_idx = torch.empty(lac.indexer_topk_workspace_size(1, T, c["N"], c["k"]),
+                                  dtype=torch.uint8, device=dev)
+        self.ws = torch.empty(lac.attend_workspace_size(1, T, c["H"], c["D"], c["r"], 1, c["k"],
+                                                        c["W"]), dtype=torch.uint8, device=dev)
+        self.sets = [c]
+
+    def step(self, i, timer=None):
+        lac, c = self.lac, self.c
+        n0, n1 = c["N_ctx"], c["N"]
+        lac.csa_compress(c["raw"][:, c["W"] - 1:], c["z"], c["ckv"][:, n0:n1], m=c["m"],
+                         rope_dims=c["r"], pos0=c["pos0"], T=c["chunk"])
+        lac.csa_compress(c["kI_raw"], c["zI"], c["KI"][:, n0:n1], m=c["m"], rope_dims=0,
+                         pos0=c["pos0"])
+        if timer is not None:
+            lac.time_next_launch("indexer_score", *timer)
+        lac.indexer_topk(c["qI"], c["w"], c["KI"], m=c["m"], k=c["k"], q_pos0=c["q_pos0"],
+                         topk_idx=self.idx, workspace=self.ws_idx)
+        lac.csa_attend(c["q"], c["ckv"], self.idx, c["raw"], c["W"], q_pos0=c["q_pos0"],
+                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out, workspace=self.ws)
+
+    def indexer_flops(self):
+        c = self.c
+        nv = sum(min(c["N"], (c["q_pos0"] + i) // c["m"]) for i in range(c["chunk"]))
+        return nv * c["HI"] * c["dI"] * 2
+
+    def flops_per_step(self):
+        c = self.c
+        att = 0
+        for i in range(c["chunk"]):
+            t = c["q_pos0"] + i
+            nv = min(c["N"], t // c["m"])
+            att += (min(c["k"], nv) + min(c["W"], t + 1)) * c["H"] * c["D"] * 4
+        return self.indexer_flops() + att
+
+    def tokens_per_step(self):
+        return self.c["chunk"]
+
+    def config(self):
+        c = self.c
+        return {"workload": self.name, "batch": 1, "ctx": c["q_pos0"], "chunk": c["chunk"],
+                "topk": c["k"], "window": c["W"], "heads": c["H"], "kv_dim": c["D"],
+                "indexer": f"{c['HI']}x{c['dI']} bf16", "csa_entries": c["N"], "kv_format": "bf16"}
+
+    def cpu_sample(self):
+        import oracle
+        from oracle import chain
+        import synth
+
+        c = self.c
+        h = {k_: synth.host_bytes(v) for k_, v in c.items() if isinstance(v, torch.Tensor)}
+        rows = [(0, i) for i in range(0, c["chunk"], 1024)]       # 4 of 4096 queries
+        t0 = time.perf_counter()
+        idx, _, _ = chain.csa_select(h["qI"], h["w"], h["KI"], "bf16", 1, c["chunk"], c["HI"],
+                                     c["dI"], c["N"], c["q_pos0"], c["m"], c["k"], rows)
+        oracle.attend(h["q"], oracle.BF16, h["ckv"], oracle.BF16, c["N"], 0, idx, c["k"], c["m"],
+                      h["raw"], c["T_raw"], c["raw_pos0"], c["W"], None, 0.0, 1, c["chunk"],
+                      c["H"], c["D"], c["r"], 1e4, c["q_pos0"], rows)
+        el = time.perf_counter() - t0
+        fl = self.flops_per_step() * len(rows) / c["chunk"]
+        return {"value": fl / el / 1e12, "unit": self.unit, "seconds": el,
+                "sample": "indexer + top-k + attention for 4 of the 4096 queries (the chunk's "
+                          "compression excluded), FLOPs scaled by 4/4096"}
+
+
+class HcaPrefill(ChunkPrefill):
+    name = "hca_prefill_8k"
+
+    def __init__(self, lac, synth, dev, sets, seed=1):
+        self.lac = lac
+        c = self.c = synth.hca_prefill(seed=seed, device=dev)
+        self.hkv = torch.empty((1, c["T"] // c["m"], c["D"]), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty_like(c["q"])
+        self.ws = torch.empty(lac.attend_workspace_size(1, c["T"], c["H"], c["D"], c["r"], 1,
+                                                        c["T"] // c["m"], c["W"]),
+                              dtype=torch.uint8, device=dev)
+        self.sets = [c]
+
+    def step(self, i, timer=None):
+        lac, c = self.lac, self.c
+        lac.hca_compress(c["kv"], c["z"], self.hkv, m=c["m"], rope_dims=c["r"], pos0=0)
+        if timer is not None:
+            lac.time_next_launch("attend", *timer)
+        lac.hca_attend(c["q"], self.hkv, c["kv"], c["W"], m=c["m"], q_pos0=0, raw_pos0=0,
+                       rope_dims=c["r"], out=self.out, workspace=self.ws)
+
+    def flops_per_step(self):
+        c = self.c
+        tot = 0
+        for t in range(c["T"]):
+            tot += (min(c["T"] // c["m"], t // c["m"]) + min(c["W"], t + 1)) * c["H"] * c["D"] * 4
+        return tot
+
+    def tokens_per_step(self):
+        return self.c["T"]
+
+    def config(self):
+        c = self.c
+        return {"workload": self.name, "batch": 1, "tokens": c["T"], "m_hca": c["m"],
+                "window": c["W"], "heads": c["H"], "kv_dim": c["D"], "kv_format": "bf16"}
+
+    def cpu_sample(self):
+        import oracle
+        from oracle import chain
+        import synth
+
+        c = self.c
+        h = {k_: synth.host_bytes(v) for k_, v in c.items() if isinstance(v, torch.Tensor)}
+        rows = [(0, t) for t in range(0, c["T"], 64)]
+        t0 = time.perf_counter()
+        hkv = chain.compress_store(h["kv"], h["z"], "bf16", "bf16", 1, c["T"], c["D"], c["m"],
+                                   c["r"], 1e4, 0)
+        oracle.attend(h["q"], oracle.BF16, hkv, oracle.BF16, c["T"] // c["m"], 1, None, 0,
+                      c["m"], h["kv"], c["T"], 0, c["W"], None, 0.0, 1, c["T"], c["H"], c["D"],
+                      c["r"], 1e4, 0, rows)
+        el = time.perf_counter() - t0
+        fl = self.flops_per_step() * len(rows) / c["T"]
+        return {"value": fl / el / 1e12, "unit": self.unit, "seconds": el,
+                "sample": "compression of all 8192 tokens + attention of 128 of the 8192 "
+                          "queries, FLOPs scaled by 128/8192"}
+
+
+WORKLOADS = {w.name: w for w in (PairDecode, CsaDecode, ChunkPrefill, HcaPrefill)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="pair_decode_1m", choices=sorted(WORKLOADS))
+    ap.add_argument("--sets", type=int, default=3, help="rotating cache sets (decode)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus 1 only)",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 1 << 30, "launches": 5}))
+        return
+
+    import long_context_attention_compressor_amd as lac
+    import synth
+
+    wl = WORKLOADS[args.workload](lac, synth, dev, args.sets)
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        wl.step(i)
+    torch.cuda.synchronize()
+    timers = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    for a, b in timers:          # PyTorch creates the HIP events on their first record
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        wl.step(args.warmup + i, timer=timers[i])
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = el * 1e3 / args.steps
+    kern_ms = sum(a.elapsed_time(b) for a, b in timers) / args.steps
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": wl.config()}
+    if wl.unit == "tokens/s":
+        res["value"] = wl.tokens_per_step() / (ms / 1e3)
+        res["unit"] = "tokens/s"
+        res["hbm_gbps"] = wl.bytes_per_step() / (ms / 1e3) / 1e9
+        ach = wl.indexer_bytes_per_launch() / (kern_ms / 1e3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": "score_bf16_kernel (indexer scores)",
+                           "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                           "launch_ms": round(kern_ms, 5)}
+    else:
+        fl = wl.flops_per_step()
+        res["value"] = fl / (ms / 1e3) / 1e12
+        res["unit"] = "TFLOP/s"
+        if isinstance(wl, HcaPrefill):
+            kfl, kname = fl, "attend_mfma_kernel (HCA attention)"
+        else:
+            kfl, kname = wl.indexer_flops(), "score_bf16_kernel (indexer scores)"
+        ach = kfl / (kern_ms / 1e3) / 1e12
+        res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
+                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                           "launch_ms": round(kern_ms, 5)}
+    if not args.no_cpu:
+        import oracle
+        cb = wl.cpu_sample()
+        res["cpu_baseline"] = {"value": cb["value"], "unit": cb["unit"],
+                               "cores": oracle.num_threads(), "kind": "oracle",
+                               "sample": cb["sample"], "seconds": round(cb["seconds"], 2)}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
