@@ -94,7 +94,7 @@ typedef enum {
  *            rows 0..T/m-1 of each batch are written
  *   m        block size, 1..256 (4 for CSA)
  *   pos0     host [B], position of raw row 0; a multiple of m
- * D must be a multiple of 8, rope_dims a multiple of 8 with rope_dims <= D.
+ * D must be a multiple of 8, rope_dims a multiple of 8 with rope_dims <= min(D, 128).
  * Streams raw KV and logits once from HBM; fp32 arithmetic.
  */
 int32_t csa_compress(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
@@ -177,7 +177,7 @@ size_t attend_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t D, int32_
  * q_dtype LAC_F32 needs kv_dtype LAC_F32, D <= 256 and H*D <= 8192;
  * q_dtype LAC_BF16 needs kv_dtype LAC_BF16 or LAC_KV_E4M3_ROPE_BF16,
  * D in {128, 256, 512} and H dividing 64 or a multiple of 64.
- * rope_dims: a multiple of 8, <= D.
+ * rope_dims: a multiple of 8, <= min(D, 128).
  */
 int32_t csa_attend(const void* q, int32_t q_dtype, const void* ckv, int32_t kv_dtype, int32_t N,
                    const int32_t* topk_idx, int32_t k, const void* raw_kv, int32_t T_raw,

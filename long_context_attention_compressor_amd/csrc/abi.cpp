@@ -64,8 +64,8 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
   if (T < 0) return fail(LAC_ERR_INVALID, "%s: T = %d < 0", fn, T);
   if (m < 1 || m > 256) return fail(LAC_ERR_INVALID, "%s: m = %d outside [1, 256]", fn, m);
   if (D < 8 || D > 2048 || D % 8) return fail(LAC_ERR_INVALID, "%s: D = %d must be a multiple of 8 in [8, 2048]", fn, D);
-  if (rope_dims < 0 || rope_dims > D || rope_dims % 8)
-    return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, D]", fn, rope_dims);
+  if (rope_dims < 0 || rope_dims > D || rope_dims > 128 || rope_dims % 8)
+    return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, min(D, 128)]", fn, rope_dims);
   if (rope_dims > 0 && !(rope_theta > 0.f && isfinite(rope_theta)))
     return fail(LAC_ERR_INVALID, "%s: rope_theta must be positive and finite", fn);
   const int N = T / m;
@@ -105,8 +105,8 @@ int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32
   if (c.B < 0 || c.B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, c.B, LAC_MAX_BATCH);
   if (c.Tq < 0 || c.N < 0 || c.T_raw < 0 || c.W < 0 || c.H < 1)
     return fail(LAC_ERR_INVALID, "%s: negative size or H < 1", fn);
-  if (c.r < 0 || c.r > c.D || c.r % 8)
-    return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, D]", fn, c.r);
+  if (c.r < 0 || c.r > c.D || c.r > 128 || c.r % 8)
+    return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, min(D, 128)]", fn, c.r);
   if (c.r > 0 && !(c.theta > 0.f && isfinite(c.theta)))
     return fail(LAC_ERR_INVALID, "%s: rope_theta must be positive and finite", fn);
   if (!isfinite(c.scale) || c.scale < 0.f) return fail(LAC_ERR_INVALID, "%s: softmax_scale must be finite and >= 0", fn);

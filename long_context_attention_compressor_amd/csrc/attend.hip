@@ -95,6 +95,9 @@ struct WinArgs {
 };
 
 __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
+  __shared__ double freq[kMaxRopePairs];
+  rope_freq_table(freq, a.r, a.theta);
+  __syncthreads();
   const int G8 = a.D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_b = a.win_rows * G8;
@@ -136,7 +139,7 @@ __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     float cs, sn;
-    rope_cos_sin((double)s, rope_inv_freq((c0 - nope) / 2 + q, a.r, a.theta), &cs, &sn);
+    rope_cos_sin((double)s, freq[(c0 - nope) / 2 + q], &cs, &sn);
     const float x0 = v[2 * q], x1 = v[2 * q + 1];
     v[2 * q] = x0 * cs - x1 * sn;
     v[2 * q + 1] = x0 * sn + x1 * cs;
@@ -303,6 +306,9 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   float* rowl = rowm + 64;                                              // [64]
   int* tags = reinterpret_cast<int*>(rowl + 64);                        // [32]
 
+  __shared__ double freq[kMaxRopePairs];
+  __shared__ float2 qcs[4][kMaxRopePairs];     // (cos, sin) of t_g * freq_p, g < G
+
   const int tid = threadIdx.x;
   const int wave = tid >> 6, l = tid & 63, hf = l >> 5, ln = l & 31;
   const Work w = make_work(a, blockIdx.y);
@@ -310,6 +316,17 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   const int64_t e_lo = (int64_t)split * a.chunk;
   const int64_t e_hi = min(w.n_tot, e_lo + a.chunk);
   const int nope = a.D - a.r;
+  const int npair = a.r / 2;
+
+  rope_freq_table(freq, a.r, a.theta);
+  __syncthreads();
+  for (int e = tid; e < a.G * npair; e += blockDim.x) {
+    const int g = e / npair, p = e - g * npair;
+    float cs, sn;
+    rope_cos_sin((double)(w.t_first + g), freq[p], &cs, &sn);
+    qcs[g][p] = make_float2(cs, sn);
+  }
+  __syncthreads();
 
   // ---- query fragments (rotated at t), rows rt*32 + ln, dims wave*DW + s*16 + hf*8
   bf16x8 qf[2][Gm::KQ];
@@ -318,7 +335,6 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     const int row = rt * 32 + ln;
     const int g = row / a.Hs, h = w.h0 + row % a.Hs;
     const bool live = g < w.n_q;
-    const int64_t t = w.t_first + g;
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
                        (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D;
 #pragma unroll
@@ -330,8 +346,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
         uint32_t o[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          float cs, sn;
-          rope_cos_sin((double)t, rope_inv_freq((c0 - nope) / 2 + p, a.r, a.theta), &cs, &sn);
+          const float2 cv = qcs[g][(c0 - nope) / 2 + p];
+          const float cs = cv.x, sn = cv.y;
           const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
           o[p] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
         }
@@ -504,15 +520,14 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
       float den = rowl[row];
       if (a.sink) den += exp2f(a.sink[h] * 1.4426950408889634f - (mr == -INFINITY ? 0.f : mr));
       const float inv = den > 0.f ? 1.f / den : 0.f;
-      const int64_t t = w.t_first + g;
 #pragma unroll
       for (int dt = 0; dt < Gm::DT; ++dt) {
         const int col = wave * Gm::DW + dt * 32 + ln;
         float o = oacc[rt][dt][v] * inv;
         const float partner = __shfl_xor(o, 1);
-        if (col >= nope) {
-          float cs, sn;
-          rope_cos_sin(-(double)t, rope_inv_freq((col - nope) >> 1, a.r, a.theta), &cs, &sn);
+        if (col >= nope) {            // rotation at -t: (cos, -sin) of the query's angle
+          const float2 cv = qcs[g < 4 ? g : 0][(col - nope) >> 1];
+          const float cs = cv.x, sn = -cv.y;
           o = (col & 1) ? partner * sn + o * cs : o * cs - partner * sn;
         }
         if (live) {
@@ -528,6 +543,9 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
 __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   __shared__ float wgt[1024];
   __shared__ float red[2];
+  __shared__ double freq[kMaxRopePairs];
+  rope_freq_table(freq, a.r, a.theta);
+  __syncthreads();
   const int work = blockIdx.x / 64, row = blockIdx.x % 64;
   const Work w = make_work(a, work);
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
@@ -572,7 +590,7 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
     o1 *= inv;
     if (c >= nope) {
       float cs, sn;
-      rope_cos_sin(-(double)t, rope_inv_freq((c - nope) >> 1, a.r, a.theta), &cs, &sn);
+      rope_cos_sin(-(double)t, freq[(c - nope) >> 1], &cs, &sn);
       const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
       o0 = r0;
       o1 = r1;
@@ -585,6 +603,8 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
 // One workgroup per query; H*D <= 8192, D <= 256.
 __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   extern __shared__ float fsm[];
+  __shared__ double freq[kMaxRopePairs];
+  rope_freq_table(freq, a.r, a.theta);
   const int H = a.H, D = a.D;
   float* qs = fsm;                    // [H][D]
   float* es = qs + H * D;             // [32][D]
@@ -604,7 +624,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   for (int e = tid; e < H * (a.r / 2); e += blockDim.x) {
     const int h = e / (a.r / 2), p = e % (a.r / 2);
     float cs, sn;
-    rope_cos_sin((double)t, rope_inv_freq(p, a.r, a.theta), &cs, &sn);
+    rope_cos_sin((double)t, freq[p], &cs, &sn);
     float* v = qs + h * D + nope + 2 * p;
     const float x0 = v[0], x1 = v[1];
     v[0] = x0 * cs - x1 * sn;
@@ -673,7 +693,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   for (int e = tid; e < H * (a.r / 2); e += blockDim.x) {
     const int h = e / (a.r / 2), p = e % (a.r / 2);
     float cs, sn;
-    rope_cos_sin(-(double)t, rope_inv_freq(p, a.r, a.theta), &cs, &sn);
+    rope_cos_sin(-(double)t, freq[p], &cs, &sn);
     float* v = qs + h * D + nope + 2 * p;
     const float x0 = v[0], x1 = v[1];
     v[0] = x0 * cs - x1 * sn;

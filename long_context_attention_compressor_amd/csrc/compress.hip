@@ -39,12 +39,31 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) 
   }
 }
 
+template <int IN>
+__device__ __forceinline__ void softmax_step(const float* xv, const float* zv, float* mx, float* den,
+                                             float* acc) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float nm = fmaxf(mx[c], zv[c]);
+    const float sc = __expf(mx[c] - nm);          // 0 on the first token
+    const float p = __expf(zv[c] - nm);
+    den[c] = den[c] * sc + p;
+    acc[c] = acc[c] * sc + p * xv[c];
+    mx[c] = nm;
+  }
+}
+
+// Block of blockDim.x threads: S threads per (entry, 8-channel group) split the
+// block's tokens; several entries per block when D/8 * S < blockDim.x.
 template <int IN, int OUT>
-__global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
-  __shared__ float part[256][25];
+__global__ void __launch_bounds__(1024) compress_kernel(CompressArgs a) {
+  extern __shared__ float part[];                  // [blockDim.x][25] when S > 1
+  __shared__ double freq[kMaxRopePairs];
+  rope_freq_table(freq, a.r, a.theta);
+  __syncthreads();
   const int G = a.D >> 3;            // channel groups of 8
   const int per_entry = G * a.S;     // threads per entry
-  const int epb = 256 / per_entry;   // entries per block
+  const int epb = blockDim.x / per_entry;   // entries per block
   const int t = threadIdx.x;
   const int le = t / per_entry;
   const int within = t - le * per_entry;
@@ -63,40 +82,47 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
   if (live) {
     const int per = a.m / a.S;
     const int64_t row0 = (int64_t)j * a.m + (int64_t)s * per;
-    for (int i = 0; i < per; ++i) {
-      float xv[8], zv[8];
-      load8<IN>(a.kv, (b * a.kv_bstride + row0 + i) * a.D + g * 8, xv);
-      load8<IN>(a.logits, (b * a.z_bstride + row0 + i) * a.D + g * 8, zv);
+    const int64_t xb = (b * a.kv_bstride + row0) * a.D + g * 8;
+    const int64_t zb = (b * a.z_bstride + row0) * a.D + g * 8;
+    int i = 0;
+    // Four tokens' loads in flight before any of them is used.
+    for (; i + 4 <= per; i += 4) {
+      float xv[4][8], zv[4][8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float nm = fmaxf(mx[c], zv[c]);
-        const float sc = __expf(mx[c] - nm);          // 0 on the first token
-        const float p = __expf(zv[c] - nm);
-        den[c] = den[c] * sc + p;
-        acc[c] = acc[c] * sc + p * xv[c];
-        mx[c] = nm;
+      for (int u = 0; u < 4; ++u) {
+        load8<IN>(a.kv, xb + (int64_t)(i + u) * a.D, xv[u]);
+        load8<IN>(a.logits, zb + (int64_t)(i + u) * a.D, zv[u]);
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) softmax_step<IN>(xv[u], zv[u], mx, den, acc);
+    }
+    for (; i < per; ++i) {
+      float xv[8], zv[8];
+      load8<IN>(a.kv, xb + (int64_t)i * a.D, xv);
+      load8<IN>(a.logits, zb + (int64_t)i * a.D, zv);
+      softmax_step<IN>(xv, zv, mx, den, acc);
     }
   }
 
   if (a.S > 1) {
+    float* mine = part + t * 25;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      part[t][c] = mx[c];
-      part[t][8 + c] = den[c];
-      part[t][16 + c] = acc[c];
+      mine[c] = mx[c];
+      mine[8 + c] = den[c];
+      mine[16 + c] = acc[c];
     }
     __syncthreads();
     if (s != 0) return;
     for (int o = 1; o < a.S; ++o) {
-      const int u = t + o * G;
+      const float* other = part + (t + o * G) * 25;
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float om = part[u][c];
+        const float om = other[c];
         const float nm = fmaxf(mx[c], om);
         const float s0 = __expf(mx[c] - nm), s1 = __expf(om - nm);
-        den[c] = den[c] * s0 + part[u][8 + c] * s1;
-        acc[c] = acc[c] * s0 + part[u][16 + c] * s1;
+        den[c] = den[c] * s0 + other[8 + c] * s1;
+        acc[c] = acc[c] * s0 + other[16 + c] * s1;
         mx[c] = nm;
       }
     }
@@ -115,7 +141,7 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int pair = (c0 - nope) / 2 + q;
       float cs, sn;
-      rope_cos_sin(pos, rope_inv_freq(pair, a.r, a.theta), &cs, &sn);
+      rope_cos_sin(pos, freq[pair], &cs, &sn);
       const float x0 = o[2 * q], x1 = o[2 * q + 1];
       o[2 * q] = x0 * cs - x1 * sn;
       o[2 * q + 1] = x0 * sn + x1 * cs;
@@ -152,8 +178,12 @@ __global__ void __launch_bounds__(256) compress_kernel(CompressArgs a) {
 }
 
 template <int IN, int OUT>
-hipError_t launch(const CompressArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((compress_kernel<IN, OUT>), dim3(grid), dim3(256), 0, st, a);
+hipError_t launch(const CompressArgs& a, int grid, int threads, size_t lds, hipStream_t st) {
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&compress_kernel<IN, OUT>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, 1024 * 25 * (int)sizeof(float));
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((compress_kernel<IN, OUT>), dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -161,22 +191,25 @@ hipError_t launch(const CompressArgs& a, int grid, hipStream_t st) {
 
 hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   const int G = a.D / 8;
+  // Split a block's tokens over S threads until each thread has at most 4.
   int S = 1;
-  while (a.m / S > 8 && G * S * 2 <= 256 && a.m % (2 * S) == 0) S *= 2;
+  while (a.m / S > 4 && G * S * 2 <= 1024 && a.m % (2 * S) == 0) S *= 2;
   a.S = S;
-  const int epb = 256 / (G * S);
+  const int threads = G * S <= 256 ? 256 : G * S;
+  const int epb = threads / (G * S);
+  const size_t lds = S > 1 ? (size_t)threads * 25 * sizeof(float) : 0;
   const int64_t entries = (int64_t)a.B * (a.T / a.m);
   if (entries == 0) return hipSuccess;
   const int grid = (int)((entries + epb - 1) / epb);
   TimedLaunch tl(kKernelCompress, st);
   if (a.in_fmt == kF32) {
-    if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, st);
-    if (a.out_fmt == kBF16) return launch<kF32, kBF16>(a, grid, st);
-    return launch<kF32, kMixed>(a, grid, st);
+    if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, threads, lds, st);
+    if (a.out_fmt == kBF16) return launch<kF32, kBF16>(a, grid, threads, lds, st);
+    return launch<kF32, kMixed>(a, grid, threads, lds, st);
   }
-  if (a.out_fmt == kF32) return launch<kBF16, kF32>(a, grid, st);
-  if (a.out_fmt == kBF16) return launch<kBF16, kBF16>(a, grid, st);
-  return launch<kBF16, kMixed>(a, grid, st);
+  if (a.out_fmt == kF32) return launch<kBF16, kF32>(a, grid, threads, lds, st);
+  if (a.out_fmt == kBF16) return launch<kBF16, kBF16>(a, grid, threads, lds, st);
+  return launch<kBF16, kMixed>(a, grid, threads, lds, st);
 }
 
 }  // namespace lac

@@ -53,8 +53,21 @@ struct ScoreArgs {
   int B, Tq, HI, dI, N, m;
   int64_t Np;
   int tiles_per_wave;     // 32-key tiles per wave
+  uint32_t* hist;         // [R, kHistBins] 12-bit key histogram (split path) or null
   Positions qpos;
 };
+
+// Wave-aggregated LDS histogram add: lanes with equal digits add once.
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool on, uint32_t d) {
+  uint64_t active = __ballot(on);
+  while (active) {
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    const uint32_t dl = __shfl(d, leader);
+    const uint64_t same = __ballot(on && d == dl) & active;
+    if (lane_id() == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+    active &= ~same;
+  }
+}
 
 // ---------------------------------------------------------------- fp32 scores (VALU)
 __global__ void __launch_bounds__(256) score_f32_kernel(ScoreArgs a) {
@@ -77,23 +90,37 @@ __global__ void __launch_bounds__(256) score_f32_kernel(ScoreArgs a) {
     s = fmaf(sq[a.HI * a.dI + h], fmaxf(dot, 0.f), s);
   }
   a.scores[row * a.Np + j] = s;
+  if (a.hist) atomicAdd(&a.hist[(int64_t)row * kHistBins + (score_key(s) >> 20)], 1u);
 }
 
 // ---------------------------------------------------------------- bf16 scores (MFMA)
 // Block = 4 waves.  RW waves along rows (each with QPW consecutive queries of
 // one sequence), 4/RW waves along keys.  Grid: x = key chunks, y = row groups.
+//
+// Keys reach the MFMA through a per-wave LDS tile: every global load
+// instruction reads 1 KB of consecutive key rows (fully used 128-byte lines),
+// written to LDS with the 16-byte chunks of each row XOR-swizzled by the row
+// index, so the MFMA-layout reads (one chunk of 32 different rows per half
+// wave) are free of bank conflicts.  The next tile is loaded into VGPRs while
+// the current one is consumed from LDS.
 template <int HT, int KS, int QPW, int RW>
 __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
-  constexpr int KW = 4 / RW;
   constexpr int kRowsPerBlock = RW * QPW;
-  __shared__ float sw[kRowsPerBlock][HT * 32];
+  constexpr int KW = 4 / RW;
+  constexpr int dI = KS * 16;
+  constexpr int HI = HT * 32;
+  constexpr int CH = dI / 8;                 // 16-byte chunks per key row
+  constexpr int ROWB = dI * 2;               // bytes per key row
+  constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
+  constexpr int NLD = TILEB / 1024;          // 1 KB load instructions per tile
+  __shared__ float sw[kRowsPerBlock][HI];
+  __shared__ __align__(16) uint8_t ktile[4][TILEB];
+  __shared__ uint32_t lhist[kHistBins];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int hf = l >> 5, ln = l & 31;
   const int wr = wave % RW, wk = wave / RW;
-  const int R = a.B * a.Tq;
-  const int dI = KS * 16;
-  const int HI = HT * 32;
+  const bool do_hist = a.hist != nullptr;
 
   // Rows of this block: consecutive queries of one sequence.
   const int groups_per_seq = (a.Tq + kRowsPerBlock - 1) / kRowsPerBlock;
@@ -108,86 +135,102 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     const int i = min(i0 + rr, a.Tq - 1);
     sw[rr][h] = a.w[((int64_t)b * a.Tq + i) * HI + h];
   }
+  if (do_hist)
+    for (int e = threadIdx.x; e < kHistBins; e += 256) lhist[e] = 0u;
   __syncthreads();
-  (void)R;
 
   const int64_t tile_lo = ((int64_t)blockIdx.x * KW + wk) * a.tiles_per_wave;
   int64_t tile_hi = tile_lo + a.tiles_per_wave;
   const int64_t n_tiles = (nv_max + 31) / 32;
   if (tile_hi > n_tiles) tile_hi = n_tiles;
-  if (tile_lo >= tile_hi) return;
 
-  // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
-  bf16x8 qf[QPW][HT][KS];
-  int64_t nv_row[QPW];
-#pragma unroll
-  for (int qi = 0; qi < QPW; ++qi) {
-    const int rr = wr * QPW + qi;
-    const int i = min(i0 + rr, a.Tq - 1);
-    nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                         ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
-#pragma unroll
-      for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
-    }
-  }
-
-  const __bf16* Kb = static_cast<const __bf16*>(a.K) + (int64_t)b * a.N * dI + hf * (dI / 2);
-  auto load_tile = [&](int64_t tile, bf16x8* kf) {
-    int64_t j = tile * 32 + ln;
-    if (j > a.N - 1) j = a.N - 1;
-    const __bf16* kp = Kb + j * dI;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const uint4 u = ld_stream16(kp + 8 * s);
-      kf[s] = *reinterpret_cast<const bf16x8*>(&u);
-    }
-  };
-
-  bf16x8 kcur[KS], knext[KS];
-  load_tile(tile_lo, kcur);
-  for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
-    if (tile + 1 < tile_hi) load_tile(tile + 1, knext);
-    const int64_t j = tile * 32 + ln;
+  if (tile_lo < tile_hi) {
+    // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
+    bf16x8 qf[QPW][HT][KS];
+    int64_t nv_row[QPW];
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
       const int rr = wr * QPW + qi;
-      float part = 0.f;
+      const int i = min(i0 + rr, a.Tq - 1);
+      nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        f32x16 acc = {};
+        const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                           ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kcur[s], acc, 0, 0, 0);
-        // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], fmaxf(acc[v], 0.f), part);
+        for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
       }
-      part += __shfl_xor(part, 32);
-      if (hf == 0 && j < nv_row[qi])
-        a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
     }
+
+    const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
+    uint8_t* kt = ktile[wave];
+    // Load instruction u of a tile: lane l takes 16 bytes at u*1024 + l*16 of
+    // the tile in LDS order, i.e. row kk, swizzled chunk slot cs, which holds
+    // the row's chunk cs ^ (kk % CH).
+    auto load_tile = [&](int64_t tile, uint4* st) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) kcur[s] = knext[s];
+      for (int u = 0; u < NLD; ++u) {
+        const int o = u * 1024 + l * 16;
+        const int kk = o / ROWB, cs = (o % ROWB) / 16;
+        int64_t j = tile * 32 + kk;
+        if (j > a.N - 1) j = a.N - 1;
+        st[u] = ld_stream16(Kb + j * ROWB + ((cs ^ (kk % CH)) * 16));
+      }
+    };
+    auto store_tile = [&](const uint4* st) {
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
+    };
+
+    uint4 stage[NLD];
+    load_tile(tile_lo, stage);
+    for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
+      store_tile(stage);
+      __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): LDS writes done
+      __builtin_amdgcn_wave_barrier();
+      if (tile + 1 < tile_hi) load_tile(tile + 1, stage);
+      bf16x8 kf[KS];
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const int c = hf * (CH / 2) + s;
+        kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+      }
+      const int64_t j = tile * 32 + ln;
+#pragma unroll
+      for (int qi = 0; qi < QPW; ++qi) {
+        const int rr = wr * QPW + qi;
+        float part = 0.f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) {
+          f32x16 acc = {};
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+          // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], fmaxf(acc[v], 0.f), part);
+        }
+        part += __shfl_xor(part, 32);
+        const bool live = hf == 0 && j < nv_row[qi];
+        if (live) a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
+        if (do_hist) hist_add(lhist, live, score_key(part) >> 20);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);      // LDS reads of this tile done
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+
+  if (do_hist) {
+    __syncthreads();
+    // Only the decode shape (one row per block) keeps a histogram.
+    uint32_t* gh = a.hist + ((int64_t)b * a.Tq + i0) * kHistBins;
+    for (int e = threadIdx.x; e < kHistBins; e += 256)
+      if (lhist[e]) atomicAdd(&gh[e], lhist[e]);
   }
 }
 
 // ---------------------------------------------------------------- radix select
-// Wave-aggregated LDS histogram add: lanes with equal digits add once.
-__device__ __forceinline__ void hist_add(uint32_t* hist, bool on, uint32_t d) {
-  uint64_t active = __ballot(on);
-  while (active) {
-    const int leader = __ffsll((unsigned long long)active) - 1;
-    const uint32_t dl = __shfl(d, leader);
-    const uint64_t same = __ballot(on && d == dl) & active;
-    if (lane_id() == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
-    active &= ~same;
-  }
-}
-
 // Finds, from the top digit down, the digit where the running count reaches
 // `need`.  Run by wave 0 only, over a 256-bin histogram.  Writes
 // out[0] = digit, out[1] = count of all digits above it, out[2] = its count.
@@ -340,30 +383,6 @@ __global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, int64_t n) {
   if (i < n) p[i] = 0u;
 }
 
-__global__ void __launch_bounds__(256) topk_hist_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[kHistBins];
-  const int row = blockIdx.y;
-  const int nv = (int)row_nvis(a, row);
-  const int keff = min(a.k, nv);
-  if (keff == nv) return;
-  const int lo = blockIdx.x * kSplitChunk;
-  if (lo >= nv) return;
-  const int hi = min(nv, lo + kSplitChunk);
-  for (int e = threadIdx.x; e < kHistBins; e += 256) hist[e] = 0;
-  __syncthreads();
-  const float* s = a.scores + (int64_t)row * a.Np;
-  for (int base = lo; base < hi; base += 256) {
-    const int e = base + threadIdx.x;
-    const bool on = e < hi;
-    const uint32_t u = on ? score_key(s[e]) : 0u;
-    hist_add(hist, on, u >> 20);
-  }
-  __syncthreads();
-  uint32_t* gh = a.hist + (int64_t)row * kHistBins;
-  for (int e = threadIdx.x; e < kHistBins; e += 256)
-    if (hist[e]) atomicAdd(&gh[e], hist[e]);
-}
-
 // The 12-bit bucket holding the keff-th largest key, and the count above it.
 __device__ void split_threshold(const uint32_t* gh, uint32_t need, uint32_t* lds,
                                 uint32_t* bucket, uint32_t* above) {
@@ -402,8 +421,32 @@ __device__ void split_threshold(const uint32_t* gh, uint32_t need, uint32_t* lds
   __syncthreads();
 }
 
+// Block-wide exclusive prefix sums of two per-thread counts (256 threads).
+__device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* lds, uint32_t& ex0,
+                                            uint32_t& ex1, uint32_t& tot0, uint32_t& tot1) {
+  const int l = lane_id(), wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t i0 = v0, i1 = v1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t a0 = __shfl_up(i0, o), a1 = __shfl_up(i1, o);
+    if (l >= o) { i0 += a0; i1 += a1; }
+  }
+  if (l == 63) { lds[wv] = i0; lds[16 + wv] = i1; }
+  __syncthreads();
+  uint32_t p0 = 0, p1 = 0, s0 = 0, s1 = 0;
+  for (int w = 0; w < nw; ++w) {
+    if (w < wv) { p0 += lds[w]; p1 += lds[16 + w]; }
+    s0 += lds[w]; s1 += lds[16 + w];
+  }
+  ex0 = p0 + i0 - v0;
+  ex1 = p1 + i1 - v1;
+  tot0 = s0; tot1 = s1;
+  __syncthreads();
+}
+
 __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
-  __shared__ uint32_t lds[16];
+  constexpr int kPer = kSplitChunk / 256;
+  __shared__ uint32_t lds[40];
   const int row = blockIdx.y;
   const int nv = (int)row_nvis(a, row);
   const int keff = min(a.k, nv);
@@ -414,24 +457,31 @@ __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
   uint32_t bucket, above;
   split_threshold(a.hist + (int64_t)row * kHistBins, (uint32_t)keff, lds, &bucket, &above);
   const float* s = a.scores + (int64_t)row * a.Np;
+  uint32_t key[kPer];
+  uint32_t n_up = 0, n_in = 0;
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int e = lo + it * 256 + threadIdx.x;
+    key[it] = e < hi ? score_key(s[e]) : 0u;
+    n_up += (e < hi && (key[it] >> 20) > bucket);
+    n_in += (e < hi && (key[it] >> 20) == bucket);
+  }
+  uint32_t ex_up, ex_in, tot_up, tot_in;
+  block_scan2(n_up, n_in, lds, ex_up, ex_in, tot_up, tot_in);
   uint32_t* cnt = a.cnt + (int64_t)row * 4;
-  const int l = lane_id();
-  const uint64_t below = (l == 0) ? 0ull : (~0ull >> (64 - l));
-  for (int base = lo; base < hi; base += 256) {
-    const int e = base + threadIdx.x;
-    const uint32_t u = e < hi ? score_key(s[e]) : 0u;
-    const bool up = e < hi && (u >> 20) > bucket;
-    const bool in = e < hi && (u >> 20) == bucket;
-    const uint64_t bu = __ballot(up), bi = __ballot(in);
-    uint32_t base_u = 0, base_i = 0;
-    if (l == 0) {
-      if (bu) base_u = atomicAdd(&cnt[0], (uint32_t)__popcll(bu));
-      if (bi) base_i = atomicAdd(&cnt[1], (uint32_t)__popcll(bi));
-    }
-    base_u = __shfl(base_u, 0);
-    base_i = __shfl(base_i, 0);
-    if (up) a.sel[(int64_t)row * a.k + base_u + __popcll(bu & below)] = e;
-    if (in) a.cand[(int64_t)row * a.Np + base_i + __popcll(bi & below)] = make_uint2(u, (uint32_t)e);
+  if (threadIdx.x == 0) {
+    lds[32] = tot_up ? atomicAdd(&cnt[0], tot_up) : 0u;
+    lds[33] = tot_in ? atomicAdd(&cnt[1], tot_in) : 0u;
+  }
+  __syncthreads();
+  uint32_t pu = lds[32] + ex_up, pi = lds[33] + ex_in;
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {
+    const int e = lo + it * 256 + threadIdx.x;
+    if (e >= hi) continue;
+    const uint32_t bk = key[it] >> 20;
+    if (bk > bucket) a.sel[(int64_t)row * a.k + pu++] = e;
+    else if (bk == bucket) a.cand[(int64_t)row * a.Np + pi++] = make_uint2(key[it], (uint32_t)e);
   }
 }
 
@@ -451,8 +501,12 @@ __device__ void bitonic_sort(int32_t* v, int n) {
   }
 }
 
+constexpr int kCandLds = 6144;         // candidates staged in LDS by the resolve step
+
 __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
-  extern __shared__ int32_t list[];     // next_pow2(k) entries
+  extern __shared__ __align__(16) uint8_t rsm[];
+  uint2* lcand = reinterpret_cast<uint2*>(rsm);                 // [kCandLds]
+  int32_t* list = reinterpret_cast<int32_t*>(lcand + kCandLds);  // [next_pow2(k)]
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[4];
   __shared__ uint32_t n_list;
@@ -462,13 +516,17 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
   if (keff == nv) { write_all_visible(a, row, nv); return; }
   const uint32_t* cnt = a.cnt + (int64_t)row * 4;
   const uint32_t n_sel = cnt[0], n_cand = cnt[1];
-  const uint2* cand = a.cand + (int64_t)row * a.Np;
+  const uint2* gcand = a.cand + (int64_t)row * a.Np;
+  const bool in_lds = n_cand <= (uint32_t)kCandLds;
   int pow2 = 1;
   while (pow2 < keff) pow2 <<= 1;
   for (int e = threadIdx.x; e < pow2; e += blockDim.x)
     list[e] = e < (int)n_sel ? a.sel[(int64_t)row * a.k + e] : INT32_MAX;
+  if (in_lds)
+    for (int e = threadIdx.x; e < (int)n_cand; e += blockDim.x) lcand[e] = gcand[e];
   if (threadIdx.x == 0) n_list = n_sel;
   __syncthreads();
+  const uint2* cand = in_lds ? lcand : gcand;
   const uint32_t need = (uint32_t)keff - n_sel;
   uint32_t thr, need_eq, cnt_eq;
   radix_select((int)n_cand, need,
@@ -551,6 +609,23 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
   if (R == 0) return hipSuccess;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   float* scores = reinterpret_cast<float*>(w8 + p.off_scores);
+  hipError_t err = hipSuccess;
+
+  TopkArgs ta{};
+  ta.scores = scores; ta.Np = p.Np; ta.B = a.B; ta.Tq = a.Tq; ta.N = a.N; ta.m = a.m; ta.k = a.k;
+  ta.idx = a.topk_idx; ta.score_out = a.topk_score; ta.qpos = a.qpos; ta.chunks = p.chunks;
+  if (p.split) {
+    ta.hist = reinterpret_cast<uint32_t*>(w8 + p.off_hist);
+    ta.cnt = reinterpret_cast<uint32_t*>(w8 + p.off_cnt);
+    ta.sel = reinterpret_cast<int32_t*>(w8 + p.off_sel);
+    ta.cand = reinterpret_cast<uint2*>(w8 + p.off_cand);
+    // The score kernel accumulates into the histogram: clear it (and the
+    // adjacent counters) first, with a kernel rather than a memset.
+    const int64_t n_clear = (int64_t)(p.off_sel - p.off_hist) / 4;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_clear + 255) / 256)), dim3(256), 0, st,
+                       ta.hist, n_clear);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
 
   // Largest visible count over all rows sizes the key sweep.
   int64_t nv_max = 0;
@@ -564,8 +639,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
   ScoreArgs sa{};
   sa.q = a.q; sa.w = a.w; sa.K = a.K; sa.scores = scores;
   sa.B = a.B; sa.Tq = a.Tq; sa.HI = a.HI; sa.dI = a.dI; sa.N = a.N; sa.m = a.m;
-  sa.Np = p.Np; sa.qpos = a.qpos;
-  hipError_t err = hipSuccess;
+  sa.Np = p.Np; sa.qpos = a.qpos; sa.hist = ta.hist;
   if (nv_max > 0) {
     TimedLaunch tl(kKernelIndexerScore, st);
     if (a.fmt == kF32) {
@@ -576,7 +650,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
     } else {
       const int64_t n_tiles = (nv_max + 31) / 32;
       const int HT = a.HI / 32, KS = a.dI / 16;
-      if (a.Tq >= 8) {
+      if (a.Tq >= 8 && !p.split) {
         // Prefill: 4 waves x 2 queries share each key sweep.
         sa.tiles_per_wave = 64;
         const int64_t chunks = (n_tiles + sa.tiles_per_wave - 1) / sa.tiles_per_wave;
@@ -587,7 +661,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
         LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
 #undef LAC_SCORE_CASE
       } else {
-        // Decode: one query per wave, 4 waves split the keys.
+        // Decode: one query per block, 4 waves split the keys.
         sa.tiles_per_wave = 8;
         const int64_t chunks = (n_tiles + 4 * sa.tiles_per_wave - 1) / (4 * sa.tiles_per_wave);
         const int groups = a.B * a.Tq;
@@ -601,33 +675,24 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
     if (err != hipSuccess) return err;
   }
 
-  TopkArgs ta{};
-  ta.scores = scores; ta.Np = p.Np; ta.B = a.B; ta.Tq = a.Tq; ta.N = a.N; ta.m = a.m; ta.k = a.k;
-  ta.idx = a.topk_idx; ta.score_out = a.topk_score; ta.qpos = a.qpos; ta.chunks = p.chunks;
   if (!p.split) {
     TimedLaunch tl(kKernelTopk, st);
     hipLaunchKernelGGL(topk_rowwise_kernel, dim3(R), dim3(kTopkThreads), 0, st, ta);
     return hipGetLastError();
   }
-  ta.hist = reinterpret_cast<uint32_t*>(w8 + p.off_hist);
-  ta.cnt = reinterpret_cast<uint32_t*>(w8 + p.off_cnt);
-  ta.sel = reinterpret_cast<int32_t*>(w8 + p.off_sel);
-  ta.cand = reinterpret_cast<uint2*>(w8 + p.off_cand);
-  // hist and counters are adjacent: clear both with one fill.
-  const int64_t n_clear = (int64_t)(p.off_sel - p.off_hist) / 4;
-  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_clear + 255) / 256)), dim3(256), 0, st,
-                     ta.hist, n_clear);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     TimedLaunch tl(kKernelTopk, st);
-    hipLaunchKernelGGL(topk_hist_kernel, dim3(p.chunks, R), dim3(256), 0, st, ta);
+    hipLaunchKernelGGL(topk_filter_kernel, dim3(p.chunks, R), dim3(256), 0, st, ta);
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(topk_filter_kernel, dim3(p.chunks, R), dim3(256), 0, st, ta);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   int pow2 = 1;
   while (pow2 < a.k) pow2 <<= 1;
-  hipLaunchKernelGGL(topk_resolve_kernel, dim3(R), dim3(1024), (size_t)pow2 * 4, st, ta);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&topk_resolve_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kCandLds * 8 + 8192 * 4);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(topk_resolve_kernel, dim3(R), dim3(1024),
+                     (size_t)kCandLds * 8 + (size_t)pow2 * 4, st, ta);
   return hipGetLastError();
 }
 

@@ -75,10 +75,16 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 
 // ---------------------------------------------------------------- rotary angles
 // Rotation of pair i (of r/2) at integer position p by angle p * theta^(-2i/r).
-// The product and its reduction modulo 2*pi are taken in double, so the angle
-// stays exact to float precision at positions in the millions.
-__device__ __forceinline__ double rope_inv_freq(int i, int r, float theta) {
-  return exp2(-2.0 * (double)i / (double)r * log2((double)theta));
+// The inverse frequencies are computed once per workgroup (one double pow per
+// pair) into LDS; the product with the position and its reduction modulo
+// 2*pi are taken in double, so the angle stays exact to float precision at
+// positions in the millions.
+constexpr int kMaxRopePairs = 64;   // rope_dims <= 128
+
+// Block-wide: tab[i] = theta^(-2i/r), i < r/2.  The caller synchronises.
+__device__ __forceinline__ void rope_freq_table(double* tab, int r, float theta) {
+  for (int i = threadIdx.x; i < r / 2; i += blockDim.x)
+    tab[i] = pow((double)theta, -2.0 * (double)i / (double)r);
 }
 
 __device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float* c, float* s) {
