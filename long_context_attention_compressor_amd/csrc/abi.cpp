@@ -119,6 +119,8 @@ int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32
     if (!((c.H <= 64 && 64 % c.H == 0) || c.H % 64 == 0))
       return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H dividing 64 or a multiple of 64", fn);
   }
+  if (c.kv_dtype == LAC_KV_E4M3_ROPE_BF16 && (c.r % 32 || (c.D - c.r) % 32))
+    return fail(LAC_ERR_UNSUPPORTED, "%s: the mixed KV format needs rope_dims and D - rope_dims multiples of 32", fn);
   if (mode == 0 && k < 0) return fail(LAC_ERR_INVALID, "%s: k = %d < 0", fn, k);
   if (mode == 1 && m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
   lac::AttendArgs a{};

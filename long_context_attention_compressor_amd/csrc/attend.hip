@@ -29,6 +29,9 @@
 //  * combine: merges split partials (max, sum, unnormalised output) with the
 //    sink, divides, applies the output rotation and stores.
 //  * attend_f32: a plain VALU kernel for float32 inputs (small shapes).
+#include <algorithm>
+#include <type_traits>
+
 #include "lac_internal.h"
 
 namespace lac {
@@ -36,6 +39,8 @@ namespace lac {
 namespace {
 
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+constexpr int kIdxLds = 2304;   // CSA indices of a split staged in LDS
 
 __host__ __device__ inline int64_t kv_row_bytes(int fmt, int D, int r) {
   return fmt == kF32 ? 4LL * D : fmt == kBF16 ? 2LL * D : (int64_t)D + r;
@@ -45,7 +50,7 @@ __host__ __device__ inline int64_t kv_row_bytes(int fmt, int D, int r) {
 struct AttnPlan {
   int G, Hs, n_htiles, n_qgroups, n_work, nsplit, chunk, max_entries;
   int64_t win_rows, row_bytes;
-  size_t off_win, off_po, off_pml, total;
+  size_t off_zero, off_win, off_po, off_pml, total;
 };
 
 AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries, int W,
@@ -54,6 +59,8 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.row_bytes = kv_row_bytes(kv_fmt, D, r);
   p.win_rows = W > 0 ? (int64_t)Tq + W - 1 : 0;
   size_t off = 0;
+  p.off_zero = off;
+  off += 256;
   p.off_win = off;
   off += round_up((int64_t)B * p.win_rows * p.row_bytes, 256);
   if (f32_path) {
@@ -73,6 +80,7 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   p.chunk = (int)round_up((p.max_entries + ns - 1) / ns, 32);
+  if (p.chunk > kIdxLds) p.chunk = kIdxLds;    // a split's CSA indices fit in LDS
   p.nsplit = (p.max_entries + p.chunk - 1) / p.chunk;
   if (p.nsplit > 1) {
     p.off_po = off;
@@ -88,6 +96,7 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
 struct WinArgs {
   const uint8_t* raw;
   uint8_t* win;
+  uint8_t* zero_row;
   int fmt, B, D, r, Tq, W;
   int64_t T_raw, win_rows, row_bytes;
   float theta;
@@ -98,6 +107,7 @@ __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
   __shared__ double freq[kMaxRopePairs];
   rope_freq_table(freq, a.r, a.theta);
   __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x < 4) reinterpret_cast<uint32_t*>(a.zero_row)[threadIdx.x] = 0u;
   const int G8 = a.D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_b = a.win_rows * G8;
@@ -163,6 +173,7 @@ struct KArgs {
   void* out;
   float* part_o;
   float* part_ml;
+  const uint8_t* zero_row;   // 16 zero bytes in workspace (source of empty slots)
   int mode, N, k, m, W, B, Tq, H, D, r;
   float theta, scale_log2;
   int G, Hs, n_htiles, n_qgroups, nsplit, chunk;
@@ -173,8 +184,10 @@ struct KArgs {
 // Work item decomposition: blockIdx.x = split (fastest), blockIdx.y = work.
 struct Work {
   int b, i0, h0, n_q;       // queries i0 .. i0+n_q-1, heads h0 ..
-  int64_t t_first, t_last;
-  int64_t n_comp, lo_w, n_tot;
+  int64_t t_first;
+  int n_comp, n_tot;        // compressed entries, all entries of the list
+  int64_t lo_w;             // first window position of the list
+  int64_t win_row0;         // its row in the rotated-window buffer
 };
 
 __device__ __forceinline__ Work make_work(const KArgs& a, int work) {
@@ -187,179 +200,246 @@ __device__ __forceinline__ Work make_work(const KArgs& a, int work) {
   w.h0 = ht * 64;
   w.n_q = min(a.G, a.Tq - w.i0);
   w.t_first = (int64_t)a.qpos.v[w.b] + w.i0;
-  w.t_last = w.t_first + w.n_q - 1;
-  w.n_comp = a.mode == 0 ? (int64_t)w.n_q * a.k : n_visible(w.t_last, a.N, a.m);
+  const int64_t t_last = w.t_first + w.n_q - 1;
+  w.n_comp = a.mode == 0 ? w.n_q * a.k : (int)n_visible(t_last, a.N, a.m);
   w.lo_w = max((int64_t)0, w.t_first - a.W + 1);
-  const int64_t n_win = a.W > 0 ? w.t_last - w.lo_w + 1 : 0;
+  w.win_row0 = w.lo_w - max((int64_t)0, (int64_t)a.qpos.v[w.b] - a.W + 1);
+  const int n_win = a.W > 0 ? (int)(t_last - w.lo_w + 1) : 0;
   w.n_tot = w.n_comp + n_win;
   return w;
 }
 
-// Entry e of the work list -> source row pointer (null if it names nothing)
-// and its tag: CSA compressed: query g (0..G-1); HCA compressed: -1 - j;
-// window: 1 << 30 | (s - lo_w).
-__device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& w, int64_t e,
+// Entry tags: CSA compressed entry selected by query g -> g; HCA compressed
+// entry j -> -1 - j; window entry at position lo_w + off -> 1 << 30 | off;
+// an empty slot -> kNoEntry.
+constexpr int kNoEntry = INT32_MIN;
+constexpr int kWinTag = 1 << 30;
+
+// Per-query visibility of the work item, from which every (query, entry)
+// test is a pair of int32 compares.
+struct Vis {
+  int nv;          // HCA: compressed entries visible to the query
+  int wlo, whi;    // window offsets (relative to lo_w) visible to the query
+};
+
+__device__ __forceinline__ Vis make_vis(const KArgs& a, const Work& w, int g) {
+  Vis v;
+  if (g >= w.n_q) { v.nv = 0; v.wlo = 1; v.whi = 0; return v; }
+  const int64_t t = w.t_first + g;
+  v.nv = a.mode == 1 ? (int)n_visible(t, a.N, a.m) : 0;
+  v.wlo = (int)max((int64_t)0, t - a.W + 1 - w.lo_w);
+  v.whi = (int)(t - w.lo_w);
+  if (a.W == 0) { v.wlo = 1; v.whi = 0; }
+  return v;
+}
+
+__device__ __forceinline__ bool visible(int tag, int g, const Vis& v) {
+  const int off = tag - kWinTag;
+  const bool win = tag >= kWinTag && off >= v.wlo && off <= v.whi;
+  const bool sel = tag >= 0 && tag < kWinTag && tag == g;
+  const bool dense = tag < 0 && tag != kNoEntry && -1 - tag < v.nv;
+  return win | sel | dense;
+}
+
+// Entry e of the work list -> source row (null if it names nothing) and tag.
+// With from_lds, the CSA index of entry e is lidx[e - e_lo] (LDS).
+__device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& w, int e,
+                                                    bool from_lds, const int32_t* lidx, int e_lo,
                                                     int* tag) {
-  if (e >= w.n_tot) { *tag = -0x7fffffff; return nullptr; }
+  if (e >= w.n_tot) { *tag = kNoEntry; return nullptr; }
   if (e < w.n_comp) {
-    int64_t j;
+    int j;
     if (a.mode == 0) {
-      const int g = (int)(e / a.k);
-      j = a.idx[((int64_t)w.b * a.Tq + w.i0 + g) * a.k + (e - (int64_t)g * a.k)];
-      if (j < 0 || j >= a.N) { *tag = -0x7fffffff; return nullptr; }
+      const int g = a.G == 1 ? 0 : e / a.k;
+      if (from_lds)
+        j = lidx[e - e_lo];
+      else
+        j = *(const __attribute__((address_space(1))) int32_t*)(
+            a.idx + ((int64_t)w.b * a.Tq + w.i0 + g) * a.k + (e - g * a.k));
+      if (j < 0 || j >= a.N) { *tag = kNoEntry; return nullptr; }
       *tag = g;
     } else {
       j = e;
-      *tag = -1 - (int)j;
+      *tag = -1 - j;
     }
     return a.kv + ((int64_t)w.b * a.N + j) * a.row_bytes;
   }
-  const int64_t off = e - w.n_comp;
-  *tag = (1 << 30) | (int)off;
-  return a.win + ((int64_t)w.b * a.win_rows + (w.lo_w - max((int64_t)0, (int64_t)a.qpos.v[w.b] - a.W + 1)) + off) * a.row_bytes;
-}
-
-// Whether entry with `tag` is visible to query g of the work item.
-__device__ __forceinline__ bool entry_visible(const KArgs& a, const Work& w, int tag, int g) {
-  if (tag == -0x7fffffff || g >= w.n_q) return false;
-  const int64_t t = w.t_first + g;
-  if (tag >= (1 << 30)) {
-    const int64_t s = w.lo_w + (tag - (1 << 30));
-    return s <= t && s >= t - a.W + 1;
-  }
-  if (a.mode == 0) return tag == g;
-  return (int64_t)(-1 - tag) < n_visible(t, a.N, a.m);
+  const int off = e - w.n_comp;
+  *tag = kWinTag | off;
+  return a.win + ((int64_t)w.b * a.win_rows + w.win_row0 + off) * a.row_bytes;
 }
 
 // ---------------------------------------------------------------- MFMA attention
+
+// ---- staging of 32-entry tiles
+// A tile's rows are gathered with 16-byte loads into VGPRs (8 threads per row,
+// chunks p, p + 8, ...; every lane issues the same loads, empty slots read a
+// zero row) one tile ahead, then written to LDS as bf16 rows (FP8 converted)
+// at a padded stride when the tile is consumed.  The rotated query tile also
+// lives in LDS, which keeps the per-wave registers for the output
+// accumulators and the prefetch.  Barriers inside the loop only wait for LDS
+// traffic, never for the prefetch in flight.
+constexpr int kTile = 32;
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D>
 struct Geo {
   static constexpr int DW = D / 4;          // columns per wave
   static constexpr int KQ = DW / 16;        // QK k-steps per wave
   static constexpr int DT = DW / 32;        // PV column tiles per wave
-  static constexpr int GPT = D / 64;        // 8-dim groups staged per thread
-  static constexpr int EROW = 2 * D + 16;   // LDS bytes per staged entry
+  static constexpr int EROW = 2 * D + 16;   // LDS bytes per staged entry / query row
   static constexpr int SROW = 68;           // floats per (wave, rt, v) logit row
   static constexpr int PROW = 40;           // bf16 per row of P
+  static constexpr int NCH = D / 64;        // 16-byte chunks per staging thread, bf16 rows
+  static constexpr int NCHM = D / 128 + 1;  // same for mixed rows (at most D/16 + 8 chunks)
 };
-
-template <int D, int KV>
-struct Stage {
-  uint4 raw[Geo<D>::GPT];
-};
-
-template <int D, int KV>
-__device__ __forceinline__ void stage_load(const uint8_t* src, int part, int nope, Stage<D, KV>& st) {
-  constexpr int GPT = Geo<D>::GPT;
-#pragma unroll
-  for (int q = 0; q < GPT; ++q) {
-    const int c0 = (part * GPT + q) * 8;
-    if (src == nullptr) { st.raw[q] = make_uint4(0, 0, 0, 0); continue; }
-    if constexpr (KV == kBF16) {
-      st.raw[q] = ld_stream16(src + 2 * c0);
-    } else {
-      if (c0 < nope) {
-        const uint2 x = ld_stream8(src + c0);
-        st.raw[q] = make_uint4(x.x, x.y, 0, 0);
-      } else {
-        const uint8_t* p = src + nope + 2 * (c0 - nope);
-        const uint2 x = ld_stream8(p), y = ld_stream8(p + 8);
-        st.raw[q] = make_uint4(x.x, x.y, y.x, y.y);
-      }
-    }
-  }
-}
-
-template <int D, int KV>
-__device__ __forceinline__ void stage_store(uint8_t* lds_row, int part, int nope, const Stage<D, KV>& st) {
-  constexpr int GPT = Geo<D>::GPT;
-#pragma unroll
-  for (int q = 0; q < GPT; ++q) {
-    const int c0 = (part * GPT + q) * 8;
-    uint4 v = st.raw[q];
-    if constexpr (KV == kMixed) {
-      if (c0 < nope) {
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[i] = e4m3_to_f32((v.x >> (8 * i)) & 0xffu);
-          f[4 + i] = e4m3_to_f32((v.y >> (8 * i)) & 0xffu);
-        }
-        // E4M3 values are exact in bf16.
-        v = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
-                       pack_bf16x2(f[6], f[7]));
-      }
-    }
-    *reinterpret_cast<uint4*>(lds_row + 2 * c0) = v;
-  }
-}
 
 template <int D, int KV>
 __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   using Gm = Geo<D>;
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint8_t* Et = smem;                                                   // [32][EROW]
-  float* Sp = reinterpret_cast<float*>(Et + 32 * Gm::EROW);             // [4][2][16][SROW]
-  uint16_t* Pl = reinterpret_cast<uint16_t*>(Sp + 4 * 2 * 16 * Gm::SROW);  // [64][PROW]
-  float* alpha = reinterpret_cast<float*>(Pl + 64 * Gm::PROW);         // [64]
-  float* rowm = alpha + 64;                                             // [64]
-  float* rowl = rowm + 64;                                              // [64]
-  int* tags = reinterpret_cast<int*>(rowl + 64);                        // [32]
-
+  __shared__ __align__(16) uint8_t Et[kTile * Gm::EROW];        // entry tile, bf16 rows
+  __shared__ __align__(16) uint8_t Qs[64 * Gm::EROW];           // rotated queries, bf16
+  __shared__ __align__(16) float Sp[4 * 2 * 16 * Gm::SROW];    // partial logits [wave][rt][v][lane]
+  __shared__ __align__(16) uint16_t Pl[64 * Gm::PROW];         // probabilities [row][entry]
+  __shared__ float alpha[64], rowm[64], rowl[64];
+  __shared__ __align__(16) int tags[kTile];
+  __shared__ int32_t lidx[kIdxLds];
   __shared__ double freq[kMaxRopePairs];
   __shared__ float2 qcs[4][kMaxRopePairs];     // (cos, sin) of t_g * freq_p, g < G
+  __shared__ Vis vis[4];
+  __shared__ int any_rescale;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, l = tid & 63, hf = l >> 5, ln = l & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, hf = l >> 5, ln = l & 31;
   const Work w = make_work(a, blockIdx.y);
   const int split = blockIdx.x;
-  const int64_t e_lo = (int64_t)split * a.chunk;
-  const int64_t e_hi = min(w.n_tot, e_lo + a.chunk);
+  const int e_lo = split * a.chunk;
+  const int e_hi = min(w.n_tot, e_lo + a.chunk);
   const int nope = a.D - a.r;
   const int npair = a.r / 2;
+  const int row_bytes = (int)a.row_bytes;
 
+  // CSA indices of this split to LDS (the plan keeps them within kIdxLds).
+  const int n_idx = a.mode == 0 ? max(0, min(e_hi, w.n_comp) - e_lo) : 0;
+  if (n_idx > 0) {
+    const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * a.k + e_lo;
+    for (int e = tid; e < n_idx; e += 256) lidx[e] = src[e];
+  }
+  if (tid < 4) vis[tid] = make_vis(a, w, tid);
   rope_freq_table(freq, a.r, a.theta);
   __syncthreads();
+
+  // Entry sources: fields hoisted out of the argument struct.
+  const int mode = a.mode, G = a.G, kk = a.k, NN = a.N;
+  const int n_comp = w.n_comp, n_tot = w.n_tot;
+  const uint8_t* kvb = a.kv + (int64_t)w.b * NN * row_bytes;
+  const uint8_t* winb = a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * row_bytes;
+  const uint8_t* zero_row = a.zero_row;
+  const int n_fp8 = KV == kMixed ? nope / 16 : 0;
+  const int n_chunks = KV == kMixed ? n_fp8 + a.r / 8 : D / 8;
+  const int st_e = tid >> 3, st_part = tid & 7;
+
+  constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
+  uint4 stage[NST];
+  int st_tag = kNoEntry;
+  auto load_tile = [&](int base) {
+    const int e = base + st_e;
+    const uint8_t* rs = nullptr;
+    int tag = kNoEntry;
+    if (e < e_hi) {
+      if (e < n_comp) {
+        if (mode == 0) {
+          const int j = lidx[e - e_lo];
+          if (j >= 0 && j < NN) { rs = kvb + (int64_t)j * row_bytes; tag = G == 1 ? 0 : e / kk; }
+        } else {
+          rs = kvb + (int64_t)e * row_bytes;
+          tag = -1 - e;
+        }
+      } else {
+        rs = winb + (int64_t)(e - n_comp) * row_bytes;
+        tag = kWinTag | (e - n_comp);
+      }
+    }
+    st_tag = tag;
+    // Every lane issues all NST loads (no divergent branches around them);
+    // chunks past the row and empty slots read the 16-byte zero row.
+#pragma unroll
+    for (int q = 0; q < NST; ++q) {
+      const int ch = st_part + 8 * q;
+      const uint8_t* src = (rs != nullptr && ch < n_chunks) ? rs + 16 * ch : zero_row;
+      stage[q] = ld_stream16(src);
+    }
+  };
+  auto store_tile = [&]() {
+    uint8_t* row = Et + st_e * Gm::EROW;
+#pragma unroll
+    for (int q = 0; q < NST; ++q) {
+      const int ch = st_part + 8 * q;
+      if (ch >= n_chunks) continue;
+      const uint4 v = stage[q];
+      if constexpr (KV == kMixed) {
+        if (ch < n_fp8) {    // 16 E4M3 codes -> 16 bf16 (exact)
+          uint4* dst = reinterpret_cast<uint4*>(row + 32 * ch);
+          dst[0] = e4m3x8_to_bf16x8(v.x, v.y);
+          dst[1] = e4m3x8_to_bf16x8(v.z, v.w);
+        } else {
+          *reinterpret_cast<uint4*>(row + 32 * n_fp8 + 16 * (ch - n_fp8)) = v;
+        }
+      } else {
+        *reinterpret_cast<uint4*>(row + 16 * ch) = v;
+      }
+    }
+    if (st_part == 0) tags[st_e] = st_tag;
+  };
+
+  const int n_tiles = e_hi > e_lo ? (e_hi - e_lo + kTile - 1) / kTile : 0;
+  if (n_tiles > 0) load_tile(e_lo);
+
+  // ---- prologue: rotated query tile into LDS (row = tid / 4, a quarter of D each)
   for (int e = tid; e < a.G * npair; e += blockDim.x) {
     const int g = e / npair, p = e - g * npair;
     float cs, sn;
     rope_cos_sin((double)(w.t_first + g), freq[p], &cs, &sn);
     qcs[g][p] = make_float2(cs, sn);
   }
-  __syncthreads();
-
-  // ---- query fragments (rotated at t), rows rt*32 + ln, dims wave*DW + s*16 + hf*8
-  bf16x8 qf[2][Gm::KQ];
-#pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const int row = rt * 32 + ln;
+  lds_barrier();
+  {
+    const int row = tid >> 2, qq = tid & 3;
     const int g = row / a.Hs, h = w.h0 + row % a.Hs;
     const bool live = g < w.n_q;
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                       (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D;
+                       (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D + qq * (D / 4);
+    uint4 qraw[D / 32];
 #pragma unroll
-    for (int s = 0; s < Gm::KQ; ++s) {
-      const int c0 = wave * Gm::DW + s * 16 + hf * 8;
-      uint4 raw = live ? *reinterpret_cast<const uint4*>(qp + c0) : make_uint4(0, 0, 0, 0);
+    for (int c = 0; c < D / 32; ++c)
+      qraw[c] = live ? *reinterpret_cast<const uint4*>(qp + c * 8) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      const int c0 = qq * (D / 4) + c * 8;
+      uint4 raw = qraw[c];
       if (c0 >= nope && live) {
         const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
         uint32_t o[4];
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
           const float2 cv = qcs[g][(c0 - nope) / 2 + p];
-          const float cs = cv.x, sn = cv.y;
           const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
-          o[p] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+          o[p] = pack_bf16x2(x0 * cv.x - x1 * cv.y, x0 * cv.y + x1 * cv.x);
         }
         raw = make_uint4(o[0], o[1], o[2], o[3]);
       }
-      qf[rt][s] = *reinterpret_cast<bf16x8*>(&raw);
+      *reinterpret_cast<uint4*>(Qs + row * Gm::EROW + 2 * c0) = raw;
     }
   }
 
   // ---- running softmax state: thread (row = tid/4, part = tid%4)
   const int srow = tid >> 2, spart = tid & 3;
   const int sg = srow / a.Hs;
+  const Vis myvis = vis[sg < 4 ? sg : 0];
   float m_run = -INFINITY, l_run = 0.f;
 
   f32x16 oacc[2][Gm::DT];
@@ -368,27 +448,12 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
 #pragma unroll
     for (int dt = 0; dt < Gm::DT; ++dt) oacc[rt][dt] = f32x16{};
 
-  const int st_e = tid >> 3, st_part = tid & 7;
-  Stage<D, KV> stage;
-  int st_tag = 0;
-  {
-    const uint8_t* src = e_lo + st_e < e_hi ? entry_src(a, w, e_lo + st_e, &st_tag) : nullptr;
-    if (e_lo + st_e >= e_hi) st_tag = -0x7fffffff;
-    stage_load<D, KV>(src, st_part, nope, stage);
-  }
-
-  for (int64_t base = e_lo; base < e_hi; base += 32) {
-    __syncthreads();   // previous tile fully consumed
-    stage_store<D, KV>(Et + st_e * Gm::EROW, st_part, nope, stage);
-    if (st_part == 0) tags[st_e] = st_tag;
-    __syncthreads();
-    // prefetch the next tile while this one is used
-    if (base + 32 < e_hi) {
-      const int64_t e = base + 32 + st_e;
-      const uint8_t* src = e < e_hi ? entry_src(a, w, e, &st_tag) : nullptr;
-      if (e >= e_hi) st_tag = -0x7fffffff;
-      stage_load<D, KV>(src, st_part, nope, stage);
-    }
+  for (int t = 0; t < n_tiles; ++t) {
+    lds_barrier();            // tile t-1 fully consumed (and the query tile written)
+    store_tile();             // waits for this thread's prefetched rows
+    if (tid == 0) any_rescale = 0;
+    lds_barrier();
+    if (t + 1 < n_tiles) load_tile(e_lo + (t + 1) * kTile);
 
     // ---- QK on this wave's quarter of D
 #pragma unroll
@@ -396,14 +461,15 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
       f32x16 sacc = {};
 #pragma unroll
       for (int s = 0; s < Gm::KQ; ++s) {
-        const bf16x8 ef = *reinterpret_cast<const bf16x8*>(
-            Et + ln * Gm::EROW + 2 * (wave * Gm::DW + s * 16 + hf * 8));
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[rt][s], ef, sacc, 0, 0, 0);
+        const int d0 = wave * Gm::DW + s * 16 + hf * 8;
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (rt * 32 + ln) * Gm::EROW + 2 * d0);
+        const bf16x8 ef = *reinterpret_cast<const bf16x8*>(Et + ln * Gm::EROW + 2 * d0);
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, ef, sacc, 0, 0, 0);
       }
 #pragma unroll
       for (int v = 0; v < 16; ++v) Sp[((wave * 2 + rt) * 16 + v) * Gm::SROW + l] = sacc[v];
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- online softmax: thread owns row srow, entries spart*8 .. +8
     {
@@ -414,15 +480,19 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
       for (int e = 0; e < 8; ++e) sv[e] = 0.f;
 #pragma unroll
       for (int wv = 0; wv < 4; ++wv) {
-        const float* src = Sp + ((wv * 2 + rt) * 16 + v) * Gm::SROW + shf * 32 + spart * 8;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sv[e] += src[e];
+        const float4* src = reinterpret_cast<const float4*>(
+            Sp + ((wv * 2 + rt) * 16 + v) * Gm::SROW + shf * 32 + spart * 8);
+        const float4 x = src[0], y = src[1];
+        sv[0] += x.x; sv[1] += x.y; sv[2] += x.z; sv[3] += x.w;
+        sv[4] += y.x; sv[5] += y.y; sv[6] += y.z; sv[7] += y.w;
       }
+      const int4 tg0 = *reinterpret_cast<const int4*>(tags + spart * 8);
+      const int4 tg1 = *reinterpret_cast<const int4*>(tags + spart * 8 + 4);
+      const int tg[8] = {tg0.x, tg0.y, tg0.z, tg0.w, tg1.x, tg1.y, tg1.z, tg1.w};
       float tmax = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const bool vis = entry_visible(a, w, tags[spart * 8 + e], sg);
-        sv[e] = vis ? sv[e] * a.scale_log2 : -INFINITY;
+        sv[e] = visible(tg[e], sg, myvis) ? sv[e] * a.scale_log2 : -INFINITY;
         tmax = fmaxf(tmax, sv[e]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
@@ -443,20 +513,26 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
       l_run = l_run * al + psum;
       m_run = m_new;
       *reinterpret_cast<uint4*>(Pl + srow * Gm::PROW + spart * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      if (spart == 0) alpha[srow] = al;
+      if (spart == 0) {
+        alpha[srow] = al;
+        if (al != 1.f) any_rescale = 1;
+      }
     }
-    __syncthreads();
+    lds_barrier();
 
-    // ---- rescale and PV on this wave's quarter of the output columns
+    // ---- rescale (only when some row's maximum moved) and PV on this wave's
+    // quarter of the output columns
+    if (any_rescale) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float al[16];
+      for (int rt = 0; rt < 2; ++rt) {
+        float al[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) al[v] = alpha[rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)];
+        for (int v = 0; v < 16; ++v) al[v] = alpha[rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)];
 #pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt)
+        for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) oacc[rt][dt][v] *= al[v];
+          for (int v = 0; v < 16; ++v) oacc[rt][dt][v] *= al[v];
+      }
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -476,18 +552,18 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
           u[i] = lo | (hi << 16);
         }
         uint4 uv = make_uint4(u[0], u[1], u[2], u[3]);
-        const bf16x8 ef = *reinterpret_cast<bf16x8*>(&uv);
+        const bf16x8 eb = *reinterpret_cast<bf16x8*>(&uv);
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt)
-          oacc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rt], ef, oacc[rt][dt], 0, 0, 0);
+          oacc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rt], eb, oacc[rt][dt], 0, 0, 0);
       }
     }
   }
 
   // ---- row statistics to LDS for the epilogue
-  __syncthreads();
+  lds_barrier();
   if (spart == 0) { rowm[srow] = m_run; rowl[srow] = l_run; }
-  __syncthreads();
+  lds_barrier();
 
   if (a.nsplit > 1) {
     const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
@@ -579,12 +655,13 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * a.D;
   for (int c = 2 * threadIdx.x; c < a.D; c += 2 * blockDim.x) {
     float o0 = 0.f, o1 = 0.f;
+    const float* pp = a.part_o + (slot0 * 64 + row) * a.D + c;
+    const int64_t stride = 64LL * a.D;
+#pragma unroll 8
     for (int s = 0; s < a.nsplit; ++s) {
-      const float f = wgt[s];
-      if (f == 0.f) continue;
-      const float2 x = *reinterpret_cast<const float2*>(a.part_o + ((slot0 + s) * 64 + row) * a.D + c);
-      o0 += f * x.x;
-      o1 += f * x.y;
+      const float2 x = *reinterpret_cast<const float2*>(pp + s * stride);
+      o0 = fmaf(wgt[s], x.x, o0);
+      o1 = fmaf(wgt[s], x.y, o1);
     }
     o0 *= inv;
     o1 *= inv;
@@ -615,6 +692,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   int* tags = reinterpret_cast<int*>(al + H);   // [32]
   const int tid = threadIdx.x;
   const Work w = make_work(a, blockIdx.x);      // G = 1, one query
+  const Vis vis0 = make_vis(a, w, 0);
   const int64_t t = w.t_first;
   const int nope = D - a.r;
   const float* q = static_cast<const float*>(a.q) + ((int64_t)w.b * a.Tq + w.i0) * H * D;
@@ -638,7 +716,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
     for (int e = tid; e < 32 * D; e += blockDim.x) {
       const int ei = e / D, c = e % D;
       int tag;
-      const uint8_t* src = entry_src(a, w, base + ei, &tag);
+      const uint8_t* src = entry_src(a, w, (int)(base + ei), false, nullptr, 0, &tag);
       es[e] = src ? reinterpret_cast<const float*>(src)[c] : 0.f;
       if (c == 0) tags[ei] = tag;
     }
@@ -647,7 +725,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
       const int h = e / 32, ei = e % 32;
       float dot = 0.f;
       for (int c = 0; c < D; ++c) dot = fmaf(qs[h * D + c], es[ei * D + c], dot);
-      lg[e] = entry_visible(a, w, tags[ei], 0) ? dot * a.scale_log2 : -INFINITY;
+      lg[e] = visible(tags[ei], 0, vis0) ? dot * a.scale_log2 : -INFINITY;
     }
     __syncthreads();
     for (int h = tid; h < H; h += blockDim.x) {
@@ -706,12 +784,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
 
 template <int D, int KV>
 hipError_t launch_mfma(const KArgs& k, const AttnPlan& p, hipStream_t st) {
-  using Gm = Geo<D>;
-  const size_t lds = 32 * Gm::EROW + 4 * 2 * 16 * Gm::SROW * 4 + 64 * Gm::PROW * 2 + 3 * 64 * 4 + 32 * 4;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&attend_mfma_kernel<D, KV>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
+  const size_t lds = 0;    // all LDS of the kernel is static
   {
     TimedLaunch tl(kKernelAttend, st);
     hipLaunchKernelGGL((attend_mfma_kernel<D, KV>), dim3(p.nsplit, p.n_work), dim3(256), lds, st, k);
@@ -735,20 +808,23 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   hipError_t e;
-  if (a.W > 0) {
+  {
+    // Rotated window rows, and the zero row that empty tile slots read.
     WinArgs wa{};
     wa.raw = static_cast<const uint8_t*>(a.raw);
     wa.win = w8 + p.off_win;
+    wa.zero_row = w8 + p.off_zero;
     wa.fmt = a.kv_fmt; wa.B = a.B; wa.D = a.D; wa.r = a.r; wa.Tq = a.Tq; wa.W = a.W;
     wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes; wa.theta = a.theta;
     wa.qpos = a.qpos; wa.rawpos = a.rawpos;
     const int64_t n = (int64_t)a.B * p.win_rows * (a.D / 8);
-    hipLaunchKernelGGL(rope_window_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, wa);
+    const unsigned blocks = (unsigned)std::max<int64_t>(1, (n + 255) / 256);
+    hipLaunchKernelGGL(rope_window_kernel, dim3(blocks), dim3(256), 0, st, wa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   KArgs k{};
   k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
-  k.sink = a.sink; k.out = a.out;
+  k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
   k.part_o = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_po) : nullptr;
   k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
   k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;
