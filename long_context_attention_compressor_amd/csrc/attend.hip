@@ -41,6 +41,7 @@ namespace {
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kIdxLds = 2304;   // CSA indices of a split staged in LDS
+constexpr int kGridTarget = 256;   // blocks per launch the split count aims at
 
 __host__ __device__ inline int64_t kv_row_bytes(int fmt, int D, int r) {
   return fmt == kF32 ? 4LL * D : fmt == kBF16 ? 2LL * D : (int64_t)D + r;
@@ -75,8 +76,10 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.n_work = B * p.n_qgroups * p.n_htiles;
   p.max_entries = p.G * n_entries + (W > 0 ? W + p.G - 1 : 0);
   if (p.max_entries < 1) p.max_entries = 1;
+  // One 152-KB block fits a compute unit, so the grid is sized to one wave of
+  // blocks over the 256 compute units; a split holds at least 4 tiles.
   const int max_split = (int)((p.max_entries + 127) / 128);
-  int ns = p.n_work >= 512 ? 1 : (512 + p.n_work - 1) / p.n_work;
+  int ns = p.n_work >= kGridTarget ? 1 : kGridTarget / p.n_work;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   p.chunk = (int)round_up((p.max_entries + ns - 1) / ns, 32);

@@ -1,0 +1,192 @@
+"""GPU parity at the full sizes of the measured workloads, in the launch
+configurations the benchmark times, checked on sampled outputs that the
+oracle computes row by row:
+
+  * 1M-token decode of a CSA + HCA layer pair (4 sequences, 262144 CSA and
+    8192 HCA entries, FP8 E4M3 + bf16 RoPE dims, top-2048, window 128);
+  * CSA decode at 131072 tokens (32 sequences, bf16, top-2048);
+  * CSA chunked prefill (4096 queries after 262144 tokens, top-2048);
+  * HCA prefill of 8192 tokens (bf16, m' = 128, window 128).
+
+The oracle never reads a value the GPU produced: it compresses the newest
+blocks itself, selects with its own scores, and its selection is uploaded to
+re-run the GPU attention on exactly that entry set.  Tolerances are those of
+tests/parity.py."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_compressor_amd as lac
+import oracle
+import synth
+from oracle import chain
+from parity import as_f64, check_attention, check_compressed, check_topk, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TH = 10000.0
+
+
+def _h(t):
+    return host(t.contiguous())
+
+
+def _check_select(g_idx, qI, w, KI_h, fmt, B, Tq, HI, dI, N, qpos, m, k, rows):
+    s, nv = oracle.index_scores(qI, w, KI_h, synth.DTYPE_CODES[fmt], B, Tq, HI, dI, N, qpos, m,
+                                rows)
+    o_idx = oracle.topk(s, nv, k)
+    sel = np.stack([g_idx[b, i] for b, i in rows])
+    same = check_topk(sel, o_idx, s, nv, k)
+    return o_idx, same
+
+
+def test_pair_decode_1m():
+    print("full size: pair decode, B=4 at 2^20", flush=True)
+    c = synth.pair_decode(device=DEV)
+    B, N, Nh, m, mh, D, r, k, W = (c[x] for x in ("B", "N", "Nh", "m", "m_hca", "D", "r", "k", "W"))
+    HI, dI, H, ctx = c["HI"], c["dI"], c["H"], c["q_pos0"]
+    # the benchmarked step
+    lac.csa_compress(c["new_kv_csa"], c["new_z_csa"], c["ckv"][:, N - 1:N], m=m, rope_dims=r,
+                     pos0=ctx - m)
+    lac.csa_compress(c["new_kI"], c["new_zI"], c["KI"][:, N - 1:N], m=m, rope_dims=0,
+                     pos0=ctx - m)
+    lac.hca_compress(c["new_kv_hca"], c["new_z_hca"], c["hkv"][:, Nh - 1:Nh], m=mh, rope_dims=r,
+                     pos0=ctx - mh)
+    idx = lac.indexer_topk(c["qI"], c["w"], c["KI"], m=m, k=k, q_pos0=ctx)
+    y_csa = lac.csa_attend(c["q_csa"], c["ckv"], idx, c["raw_csa"], W, q_pos0=ctx,
+                           raw_pos0=c["raw_pos0"], rope_dims=r)
+    y_hca = lac.hca_attend(c["q_hca"], c["hkv"], c["raw_hca"], W, m=mh, q_pos0=ctx,
+                           raw_pos0=c["raw_pos0"], rope_dims=r)
+    torch.cuda.synchronize()
+
+    # newest compressed entries
+    ref = oracle.compress(_h(c["new_kv_csa"]), _h(c["new_z_csa"]), oracle.BF16, B, m, D, m, r,
+                          TH, ctx - m)
+    check_compressed(c["ckv"][:, N - 1:N], ref, "mixed", D, r)
+    refI = oracle.compress(_h(c["new_kI"]), _h(c["new_zI"]), oracle.BF16, B, m, dI, m, 0, TH,
+                           ctx - m)
+    check_compressed(c["KI"][:, N - 1:N], refI, "bf16", dI, 0)
+    refH = oracle.compress(_h(c["new_kv_hca"]), _h(c["new_z_hca"]), oracle.BF16, B, mh, D, mh,
+                           r, TH, ctx - mh)
+    check_compressed(c["hkv"][:, Nh - 1:Nh], refH, "mixed", D, r)
+
+    # the oracle's caches: synthetic rows plus its own newest entries
+    ckv_h = _h(c["ckv"]).copy()
+    ckv_h[:, N - 1:] = oracle.encode_rows(ref.reshape(B, D), oracle.MIXED, r).reshape(B, 1, -1)
+    KI_h = _h(c["KI"]).copy()
+    KI_h[:, N - 1:] = oracle.encode_rows(refI.reshape(B, dI), oracle.BF16, 0).view(
+        np.uint16).reshape(B, 1, dI)
+    hkv_h = _h(c["hkv"]).copy()
+    hkv_h[:, Nh - 1:] = oracle.encode_rows(refH.reshape(B, D), oracle.MIXED, r).reshape(B, 1, -1)
+
+    rows = [(b, 0) for b in range(B)]
+    g_idx = idx.cpu().numpy()
+    o_idx, _ = _check_select(g_idx, _h(c["qI"]), _h(c["w"]), KI_h, "bf16", B, 1, HI, dI, N,
+                             ctx, m, k, rows)
+
+    # CSA attention on the oracle's selection, same launch configuration
+    y_sel = lac.csa_attend(c["q_csa"], c["ckv"],
+                           torch.from_numpy(o_idx.reshape(B, 1, k)).to(DEV), c["raw_csa"], W,
+                           q_pos0=ctx, raw_pos0=c["raw_pos0"], rope_dims=r)
+    torch.cuda.synchronize()
+    ref_csa = oracle.attend(_h(c["q_csa"]), oracle.BF16, ckv_h, oracle.MIXED, N, 0, o_idx, k, m,
+                            _h(c["raw_csa"]), W, c["raw_pos0"], W, None, 0.0, B, 1, H, D, r, TH,
+                            ctx, rows)
+    check_attention(as_f64(y_sel)[:, 0], ref_csa, "pair decode CSA")
+    ref_hca = oracle.attend(_h(c["q_hca"]), oracle.BF16, hkv_h, oracle.MIXED, Nh, 1, None, 0, mh,
+                            _h(c["raw_hca"]), W, c["raw_pos0"], W, None, 0.0, B, 1, H, D, r, TH,
+                            ctx, rows)
+    check_attention(as_f64(y_hca)[:, 0], ref_hca, "pair decode HCA")
+    assert torch.isfinite(y_csa.float()).all()
+
+
+def test_csa_decode_128k():
+    print("full size: CSA decode, B=32 at 131072", flush=True)
+    c = synth.csa_decode(device=DEV)
+    B, N, m, D, r, k, W = (c[x] for x in ("B", "N", "m", "D", "r", "k", "W"))
+    HI, dI, H, ctx = c["HI"], c["dI"], c["H"], c["q_pos0"]
+    idx = lac.indexer_topk(c["qI"], c["w"], c["KI"], m=m, k=k, q_pos0=ctx)
+    y = lac.csa_attend(c["q"], c["ckv"], idx, c["raw"], W, q_pos0=ctx, raw_pos0=c["raw_pos0"],
+                       rope_dims=r)
+    torch.cuda.synchronize()
+    seqs = [0, 7, 19, 31]
+    sub = lambda t: _h(t[seqs])
+    rows = [(b, 0) for b in range(len(seqs))]
+    g_idx = idx.cpu().numpy()[seqs]
+    o_idx, same = _check_select(g_idx, sub(c["qI"]), sub(c["w"]), sub(c["KI"]), "bf16",
+                                len(seqs), 1, HI, dI, N, ctx, m, k, rows)
+    full = np.full((B, 1, k), -1, np.int32)
+    full[:] = idx.cpu().numpy()
+    for j, b in enumerate(seqs):
+        full[b, 0] = o_idx[j]
+    y_sel = lac.csa_attend(c["q"], c["ckv"], torch.from_numpy(full).to(DEV), c["raw"], W,
+                           q_pos0=ctx, raw_pos0=c["raw_pos0"], rope_dims=r)
+    torch.cuda.synchronize()
+    ref = oracle.attend(sub(c["q"]), oracle.BF16, sub(c["ckv"]), oracle.BF16, N, 0, o_idx, k, m,
+                        sub(c["raw"]), W, c["raw_pos0"], W, None, 0.0, len(seqs), 1, H, D, r,
+                        TH, ctx, rows)
+    check_attention(as_f64(y_sel)[seqs, 0], ref, "CSA decode 128K")
+    # where the two selections agree the benchmarked output is checked as well
+    for j in same:
+        check_attention(as_f64(y)[seqs[j], 0][None], ref[j][None], "CSA decode 128K chain")
+
+
+def test_csa_chunk_prefill():
+    print("full size: CSA chunked prefill, 4096 queries after 262144", flush=True)
+    c = synth.csa_chunk_prefill(device=DEV)
+    N, N_ctx, chunk, m, D, r, k, W = (c[x] for x in ("N", "N_ctx", "chunk", "m", "D", "r", "k",
+                                                      "W"))
+    HI, dI, H, ctx = c["HI"], c["dI"], c["H"], c["q_pos0"]
+    raw_chunk = c["raw"][:, W - 1:]
+    lac.csa_compress(raw_chunk, c["z"], c["ckv"][:, N_ctx:], m=m, rope_dims=r, pos0=ctx)
+    lac.csa_compress(c["kI_raw"], c["zI"], c["KI"][:, N_ctx:], m=m, rope_dims=0, pos0=ctx)
+    idx = lac.indexer_topk(c["qI"], c["w"], c["KI"], m=m, k=k, q_pos0=ctx)
+    torch.cuda.synchronize()
+
+    ref = oracle.compress(_h(raw_chunk), _h(c["z"]), oracle.BF16, 1, chunk, D, m, r, TH, ctx)
+    check_compressed(c["ckv"][:, N_ctx:], ref, "bf16", D, r)
+    refI = oracle.compress(_h(c["kI_raw"]), _h(c["zI"]), oracle.BF16, 1, chunk, dI, m, 0, TH,
+                           ctx)
+    check_compressed(c["KI"][:, N_ctx:], refI, "bf16", dI, 0)
+    ckv_h = _h(c["ckv"]).copy()
+    ckv_h[:, N_ctx:] = oracle.encode_rows(ref.reshape(-1, D), oracle.BF16, r).view(
+        np.uint16).reshape(1, -1, D)
+    KI_h = _h(c["KI"]).copy()
+    KI_h[:, N_ctx:] = oracle.encode_rows(refI.reshape(-1, dI), oracle.BF16, 0).view(
+        np.uint16).reshape(1, -1, dI)
+
+    qi = [0, 1, 2, 3, 4, 5, 517, 1023, 2048, 3001, 4093, 4094, 4095]
+    rows = [(0, i) for i in qi]
+    g_idx = idx.cpu().numpy()
+    o_idx, _ = _check_select(g_idx, _h(c["qI"]), _h(c["w"]), KI_h, "bf16", 1, chunk, HI, dI, N,
+                             ctx, m, k, rows)
+    full = g_idx.copy()
+    for j, i in enumerate(qi):
+        full[0, i] = o_idx[j]
+    y = lac.csa_attend(c["q"], c["ckv"], torch.from_numpy(full).to(DEV), c["raw"], W,
+                       q_pos0=ctx, raw_pos0=c["raw_pos0"], rope_dims=r)
+    torch.cuda.synchronize()
+    ref_y = oracle.attend(_h(c["q"]), oracle.BF16, ckv_h, oracle.BF16, N, 0, o_idx, k, m,
+                          _h(c["raw"]), c["T_raw"], c["raw_pos0"], W, None, 0.0, 1, chunk, H, D,
+                          r, TH, ctx, rows)
+    check_attention(as_f64(y)[0, qi], ref_y, "CSA chunked prefill")
+
+
+def test_hca_prefill_8k():
+    print("full size: HCA prefill, T=8192", flush=True)
+    c = synth.hca_prefill(device=DEV)
+    T, D, m, r, H, W = (c[x] for x in ("T", "D", "m", "r", "H", "W"))
+    N = T // m
+    hkv = torch.empty((1, N, D), dtype=torch.bfloat16, device=DEV)
+    lac.hca_compress(c["kv"], c["z"], hkv, m=m, rope_dims=r, pos0=0)
+    y = lac.hca_attend(c["q"], hkv, c["kv"], W, m=m, q_pos0=0, raw_pos0=0, rope_dims=r)
+    torch.cuda.synchronize()
+    ref = oracle.compress(_h(c["kv"]), _h(c["z"]), oracle.BF16, 1, T, D, m, r, TH, 0)
+    check_compressed(hkv, ref, "bf16", D, r)
+    hkv_h = oracle.encode_rows(ref.reshape(N, D), oracle.BF16, r).view(np.uint16).reshape(1, N, D)
+    qi = sorted(set([0, 1, 126, 127, 128, 129, 255, 256, 1000, 4095, 4096, 8190, 8191]
+                    + list(range(3, 8192, 97))))
+    rows = [(0, i) for i in qi]
+    ref_y = oracle.attend(_h(c["q"]), oracle.BF16, hkv_h, oracle.BF16, N, 1, None, 0, m,
+                          _h(c["kv"]), T, 0, W, None, 0.0, 1, T, H, D, r, TH, 0, rows)
+    check_attention(as_f64(y)[0, qi], ref_y, "HCA prefill 8K")
