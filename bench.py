@@ -33,6 +33,24 @@ METRIC = "CSA+HCA decode tokens/s and HBM GB/s at 128K-1M ctx; prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
+# HBM bytes per launch of the indexer score kernel, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE (one pass each), scaled by what the same counters read for a 1 GiB
+# device copy (FETCH x2.000, WRITE x1.000).  They hold only for the kernel source
+# they were taken on, identified by its SHA-256; after any change to it the
+# roofline reports traffic as null until the counters are taken again.
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273368953, "csa_decode_128k": 277088924,
+                       "csa_chunk_prefill": 13659428059}
+SCORE_TRAFFIC_SOURCE_SHA256 = "cced70b5afdaa854c7e3475e9c1c06588e91bf4c33090c7ee3e0b0406b66c882"
+
+
+def _score_traffic(workload):
+    import hashlib
+    src = os.path.join(ROOT, "long_context_attention_compressor_amd", "csrc", "indexer.hip")
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != SCORE_TRAFFIC_SOURCE_SHA256:
+            return None
+    return SCORE_TRAFFIC_BYTES.get(workload)
+
 
 def _rows(t, r0, r1):
     return t[:, r0:r1]
@@ -391,20 +409,23 @@ def main():
         ach = wl.indexer_bytes_per_launch() / (kern_ms / 1e3) / 1e9
         res["roofline"] = {"bound": "hbm", "kernel": "score_bf16_kernel (indexer scores)",
                            "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                           "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": _score_traffic(wl.name), "traffic_unit": "B/launch",
                            "launch_ms": round(kern_ms, 5)}
     else:
         fl = wl.flops_per_step()
         res["value"] = fl / (ms / 1e3) / 1e12
         res["unit"] = "TFLOP/s"
         if isinstance(wl, HcaPrefill):
-            kfl, kname = fl, "attend_mfma_kernel (HCA attention)"
+            kfl, kname, traffic = fl, "attend_mfma_kernel (HCA attention)", None
         else:
             kfl, kname = wl.indexer_flops(), "score_bf16_kernel (indexer scores)"
+            traffic = _score_traffic(wl.name)
         ach = kfl / (kern_ms / 1e3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                           "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                           "traffic_unit": "B/launch",
                            "launch_ms": round(kern_ms, 5)}
     if not args.no_cpu:
         import oracle
