@@ -23,12 +23,15 @@
 //    aggregation of equal digits), then one ordered pass that keeps every key
 //    above the threshold and the lowest-index keys equal to it, written in
 //    ascending index order through a block-wide prefix count.
-//  * Split path (few long rows, e.g. decode at 1M tokens): many workgroups
-//    per row build a 12-bit histogram, then filter their chunks (keys above
-//    the threshold bucket go straight to the selection, keys in it become
-//    candidates), and one workgroup per row resolves the candidates with the
-//    same radix select, breaks ties by index and sorts the final set
-//    (bitonic, in LDS) into ascending index order.
+//  * Split path (few long rows, e.g. decode at 1M tokens): the score kernel
+//    builds a histogram of the keys' top 12 bits.  Many workgroups per row
+//    then filter their chunks into chunk-private lists (no atomics): keys
+//    above the threshold bucket are selected, keys in it become candidates
+//    and feed a second histogram of the next 12 bits.  One workgroup per row
+//    finds the threshold in that histogram, keeps the candidates above it,
+//    resolves the few keys that share its 24-bit prefix (by rank when few,
+//    else radix select on the full key, then the lowest indices), and writes
+//    the set in ascending index order from an LDS bitmap of the row.
 // Both paths give the same set: first min(k, n_vis) under (score desc, index
 // asc).  Deterministic: no floating-point atomics, ordered output.
 #include "lac_internal.h"
@@ -39,7 +42,9 @@ namespace {
 
 constexpr int kTopkThreads = 512;
 constexpr int kSplitChunk = 4096;      // scores per workgroup in the split path
-constexpr int kHistBins = 4096;        // 12-bit first digit of the split path
+constexpr int kHistBins = 4096;        // 12-bit digits of the split path
+constexpr int kTieLds = 2048;          // keys sharing the threshold's 24-bit prefix, in LDS
+constexpr int kBitmapMaxN = 1 << 20;   // longest row the LDS bitmap covers (128 KB)
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
@@ -319,10 +324,11 @@ struct TopkArgs {
   int B, Tq, N, m, k;
   int32_t* idx;           // [R, k]
   float* score_out;       // [R, k] or null
-  uint32_t* hist;         // split path: [R, kHistBins]
-  uint32_t* cnt;          // split path: [R, 4] (selected, candidates)
-  int32_t* sel;           // split path: [R, k]
-  uint2* cand;            // split path: [R, Np] (key, index)
+  uint32_t* hist;         // split path: [R, kHistBins] top-12-bit key histogram
+  uint32_t* hist2;        // split path: [R, kHistBins] next 12 bits, candidates only
+  uint32_t* cnt;          // split path: [R, chunks, 2] (selected, candidates) per chunk
+  int32_t* sel;           // split path: [R, Np] chunk-private selection lists
+  uint2* cand;            // split path: [R, Np] chunk-private (key, index) candidates
   int chunks;             // split path: workgroups per row
   Positions qpos;
 };
@@ -444,9 +450,13 @@ __device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* 
   __syncthreads();
 }
 
+// Chunk c of a row owns slots [c * kSplitChunk, (c + 1) * kSplitChunk) of the
+// row's selection and candidate lists, and writes its two counts to
+// cnt[row][c]: no atomics, no ordering between workgroups.
 __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
   constexpr int kPer = kSplitChunk / 256;
   __shared__ uint32_t lds[40];
+  __shared__ uint32_t h2[kHistBins];
   const int row = blockIdx.y;
   const int nv = (int)row_nvis(a, row);
   const int keff = min(a.k, nv);
@@ -454,126 +464,237 @@ __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
   const int lo = blockIdx.x * kSplitChunk;
   if (lo >= nv) return;
   const int hi = min(nv, lo + kSplitChunk);
+  const float* s = a.scores + (int64_t)row * a.Np;
+  float sc[kPer];
+#pragma unroll
+  for (int it = 0; it < kPer; ++it) {     // all loads first: one round trip
+    const int e = lo + it * 256 + threadIdx.x;
+    sc[it] = s[e < hi ? e : lo];
+  }
+  for (int e = threadIdx.x; e < kHistBins; e += 256) h2[e] = 0u;
   uint32_t bucket, above;
   split_threshold(a.hist + (int64_t)row * kHistBins, (uint32_t)keff, lds, &bucket, &above);
-  const float* s = a.scores + (int64_t)row * a.Np;
   uint32_t key[kPer];
   uint32_t n_up = 0, n_in = 0;
 #pragma unroll
   for (int it = 0; it < kPer; ++it) {
     const int e = lo + it * 256 + threadIdx.x;
-    key[it] = e < hi ? score_key(s[e]) : 0u;
+    key[it] = score_key(sc[it]);
     n_up += (e < hi && (key[it] >> 20) > bucket);
-    n_in += (e < hi && (key[it] >> 20) == bucket);
+    const bool in = e < hi && (key[it] >> 20) == bucket;
+    n_in += in;
+    hist_add(h2, in, (key[it] >> 8) & (kHistBins - 1));
   }
   uint32_t ex_up, ex_in, tot_up, tot_in;
   block_scan2(n_up, n_in, lds, ex_up, ex_in, tot_up, tot_in);
-  uint32_t* cnt = a.cnt + (int64_t)row * 4;
   if (threadIdx.x == 0) {
-    lds[32] = tot_up ? atomicAdd(&cnt[0], tot_up) : 0u;
-    lds[33] = tot_in ? atomicAdd(&cnt[1], tot_in) : 0u;
+    a.cnt[((int64_t)row * a.chunks + blockIdx.x) * 2] = tot_up;
+    a.cnt[((int64_t)row * a.chunks + blockIdx.x) * 2 + 1] = tot_in;
   }
-  __syncthreads();
-  uint32_t pu = lds[32] + ex_up, pi = lds[33] + ex_in;
+  int32_t* sel = a.sel + (int64_t)row * a.Np + lo;
+  uint2* cand = a.cand + (int64_t)row * a.Np + lo;
+  uint32_t pu = ex_up, pi = ex_in;
 #pragma unroll
   for (int it = 0; it < kPer; ++it) {
     const int e = lo + it * 256 + threadIdx.x;
     if (e >= hi) continue;
     const uint32_t bk = key[it] >> 20;
-    if (bk > bucket) a.sel[(int64_t)row * a.k + pu++] = e;
-    else if (bk == bucket) a.cand[(int64_t)row * a.Np + pi++] = make_uint2(key[it], (uint32_t)e);
+    if (bk > bucket) sel[pu++] = e;
+    else if (bk == bucket) cand[pi++] = make_uint2(key[it], (uint32_t)e);
+  }
+  uint32_t* g2 = a.hist2 + (int64_t)row * kHistBins;
+  for (int e = threadIdx.x; e < kHistBins; e += 256) {
+    const uint32_t c = h2[e];
+    if (c) atomicAdd(&g2[e], c);
   }
 }
 
-// Bitonic sort of n (power of two) int32 in LDS, ascending.
-__device__ void bitonic_sort(int32_t* v, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < n / 2; i += blockDim.x) {
-        const int lo = 2 * i - (i & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const int32_t x = v[lo], y = v[hi];
-        if ((x > y) == up) { v[lo] = y; v[hi] = x; }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-constexpr int kCandLds = 6144;         // candidates staged in LDS by the resolve step
-
+// Resolve one row (n_vis up to kBitmapMaxN) from the chunk lists, the second
+// histogram and an LDS bitmap of the row.
 __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
-  extern __shared__ __align__(16) uint8_t rsm[];
-  uint2* lcand = reinterpret_cast<uint2*>(rsm);                 // [kCandLds]
-  int32_t* list = reinterpret_cast<int32_t*>(lcand + kCandLds);  // [next_pow2(k)]
+  extern __shared__ __align__(16) uint32_t bits[];              // [ceil(nv / 32)]
+  __shared__ uint2 ties[kTieLds];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[4];
-  __shared__ uint32_t n_list;
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t ccnt[2 * (kBitmapMaxN / kSplitChunk)];
+  __shared__ uint32_t n_tie, t_b1, t_b2, t_above, t_sel;
   const int row = blockIdx.x;
   const int nv = (int)row_nvis(a, row);
   const int keff = min(a.k, nv);
   if (keff == nv) { write_all_visible(a, row, nv); return; }
-  const uint32_t* cnt = a.cnt + (int64_t)row * 4;
-  const uint32_t n_sel = cnt[0], n_cand = cnt[1];
-  const uint2* gcand = a.cand + (int64_t)row * a.Np;
-  const bool in_lds = n_cand <= (uint32_t)kCandLds;
-  int pow2 = 1;
-  while (pow2 < keff) pow2 <<= 1;
-  for (int e = threadIdx.x; e < pow2; e += blockDim.x)
-    list[e] = e < (int)n_sel ? a.sel[(int64_t)row * a.k + e] : INT32_MAX;
-  if (in_lds)
-    for (int e = threadIdx.x; e < (int)n_cand; e += blockDim.x) lcand[e] = gcand[e];
-  if (threadIdx.x == 0) n_list = n_sel;
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
+  const int nwords = (nv + 31) >> 5;
+  const int nchunks = (nv + kSplitChunk - 1) / kSplitChunk;
+  const uint32_t* g2 = a.hist2 + (int64_t)row * kHistBins;
+  uint32_t c[4], sum = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) { c[q] = g2[kHistBins - 1 - 4 * tid - q]; sum += c[q]; }
+  for (int e = tid; e < 2 * nchunks; e += 1024) ccnt[e] = a.cnt[(int64_t)row * a.chunks * 2 + e];
+  for (int e = tid; e < nwords; e += 1024) bits[e] = 0u;
+  if (tid == 0) { n_tie = 0; t_sel = 0; }
   __syncthreads();
-  const uint2* cand = in_lds ? lcand : gcand;
-  const uint32_t need = (uint32_t)keff - n_sel;
-  uint32_t thr, need_eq, cnt_eq;
-  radix_select((int)n_cand, need,
-               [&](int e, uint32_t* u) { *u = cand[e].x; return true; }, hist, bc, thr, need_eq,
-               cnt_eq);
-  // Ties at the threshold: keep the need_eq lowest indices (largest ~index).
-  uint32_t thr2 = 0;
-  if (cnt_eq > need_eq) {
-    uint32_t ne2, ce2;
-    radix_select((int)n_cand, need_eq,
-                 [&](int e, uint32_t* u) {
-                   const uint2 c = cand[e];
-                   *u = ~c.y;
-                   return c.x == thr;
-                 },
-                 hist, bc, thr2, ne2, ce2);
+  // Selected count (sum over chunks), then the threshold sub-bucket: thread t
+  // covers bins 4095-4t .. 4092-4t (descending).
+  if (tid < 64) {
+    uint32_t v = 0;
+    for (int ch = tid; ch < nchunks; ch += 64) v += ccnt[2 * ch];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if (tid == 0) t_sel = v;
   }
-  for (int e = threadIdx.x; e < (int)n_cand; e += blockDim.x) {
-    const uint2 c = cand[e];
-    if (c.x > thr || (c.x == thr && ~c.y >= thr2)) {
-      const uint32_t pos = atomicAdd(&n_list, 1u);
-      if (pos < (uint32_t)pow2) list[pos] = (int32_t)c.y;
+  __syncthreads();
+  const uint32_t need = (uint32_t)keff - t_sel;     // >= 1: the bucket holds the keff-th key
+  {
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_up(incl, o);
+      if (l >= o) incl += v;
+    }
+    if (l == 63) wsum[wv] = incl;
+    __syncthreads();
+    for (int w = 0; w < wv; ++w) incl += wsum[w];
+    const uint32_t excl = incl - sum;
+    if (excl < need && incl >= need) {
+      uint32_t cum = excl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cum + c[q] >= need) { t_b2 = kHistBins - 1 - 4 * tid - q; t_above = cum; break; }
+        cum += c[q];
+      }
     }
   }
   __syncthreads();
-  bitonic_sort(list, pow2);
+  const uint32_t b2 = t_b2, need_t = need - t_above;
+
+  // Chunk lists: wave w takes chunks w, w + 16, ...
+  const int32_t* sel = a.sel + (int64_t)row * a.Np;
+  const uint2* cand = a.cand + (int64_t)row * a.Np;
+  for (int ch = wv; ch < nchunks; ch += 16) {
+    const int n_up = (int)ccnt[2 * ch], n_in = (int)ccnt[2 * ch + 1];
+    const int64_t base = (int64_t)ch * kSplitChunk;
+    for (int i = l; i < n_up; i += 64) {
+      const int32_t j = sel[base + i];
+      atomicOr(&bits[j >> 5], 1u << (j & 31));
+    }
+    for (int i = l; i < n_in; i += 64) {
+      const uint2 cv = cand[base + i];
+      const uint32_t d2 = (cv.x >> 8) & (kHistBins - 1);
+      if (d2 > b2) {
+        atomicOr(&bits[cv.y >> 5], 1u << (cv.y & 31));
+      } else if (d2 == b2) {
+        const uint32_t pos = atomicAdd(&n_tie, 1u);
+        if (pos < (uint32_t)kTieLds) ties[pos] = cv;
+      }
+    }
+  }
+  __syncthreads();
+
+  // need_t of the keys sharing the threshold's 24-bit prefix, by (key desc,
+  // index asc).
+  const int nt = (int)n_tie;
+  if (nt <= 1024) {
+    // by rank: the number of ties ordered before this one
+    if (tid < nt) {
+      const uint2 me = ties[tid];
+      uint32_t rank = 0;
+      for (int j = 0; j < nt; ++j) {
+        const uint2 o = ties[j];
+        rank += (o.x > me.x) || (o.x == me.x && o.y < me.y);
+      }
+      if (rank < need_t) atomicOr(&bits[me.y >> 5], 1u << (me.y & 31));
+    }
+  } else if (nt <= kTieLds) {
+    uint32_t thr, need_eq, cnt_eq, thr2 = 0;
+    radix_select(nt, need_t, [&](int e, uint32_t* u) { *u = ties[e].x; return true; }, hist, bc,
+                 thr, need_eq, cnt_eq);
+    if (cnt_eq > need_eq) {
+      uint32_t ne2, ce2;
+      radix_select(nt, need_eq,
+                   [&](int e, uint32_t* u) { *u = ~ties[e].y; return ties[e].x == thr; }, hist,
+                   bc, thr2, ne2, ce2);
+    }
+    for (int e = tid; e < nt; e += 1024) {
+      const uint2 cv = ties[e];
+      if (cv.x > thr || (cv.x == thr && ~cv.y >= thr2))
+        atomicOr(&bits[cv.y >> 5], 1u << (cv.y & 31));
+    }
+  } else {
+    // More ties than LDS holds (e.g. many equal scores): radix select over the
+    // row's scores that carry the threshold's 24-bit prefix.
+    if (tid == 0) {
+      t_b1 = 0;
+      for (int ch = 0; ch < nchunks; ++ch)
+        if (ccnt[2 * ch + 1]) { t_b1 = cand[(int64_t)ch * kSplitChunk].x >> 20; break; }
+    }
+    __syncthreads();
+    const uint32_t prefix = (t_b1 << 12) | b2;
+    const float* s = a.scores + (int64_t)row * a.Np;
+    uint32_t thr, need_eq, cnt_eq, thr2 = 0;
+    radix_select(nv, need_t,
+                 [&](int e, uint32_t* u) { *u = score_key(s[e]); return (*u >> 8) == prefix; },
+                 hist, bc, thr, need_eq, cnt_eq);
+    if (cnt_eq > need_eq) {
+      uint32_t ne2, ce2;
+      radix_select(nv, need_eq,
+                   [&](int e, uint32_t* u) { *u = ~(uint32_t)e; return score_key(s[e]) == thr; },
+                   hist, bc, thr2, ne2, ce2);
+    }
+    for (int e = tid; e < nv; e += 1024) {
+      const uint32_t u = score_key(s[e]);
+      if ((u >> 8) == prefix && (u > thr || (u == thr && ~(uint32_t)e >= thr2)))
+        atomicOr(&bits[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+
+  // Emit the set in ascending index order: thread t owns a run of words.
+  const int per = (nwords + 1023) / 1024;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+  uint32_t mine = 0;
+  for (int w = w0; w < w1; ++w) mine += (uint32_t)__popc(bits[w]);
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o);
+    if (l >= o) incl += v;
+  }
+  if (l == 63) wsum[wv] = incl;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) incl += wsum[w];
+  uint32_t pos = incl - mine;
   const float* s = a.scores + (int64_t)row * a.Np;
-  for (int e = threadIdx.x; e < a.k; e += blockDim.x) {
-    const int32_t j = e < keff ? list[e] : -1;
-    a.idx[(int64_t)row * a.k + e] = j;
-    if (a.score_out) a.score_out[(int64_t)row * a.k + e] = j >= 0 ? s[j] : -INFINITY;
+  int32_t* out = a.idx + (int64_t)row * a.k;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t b = bits[w];
+    while (b) {
+      const int j = (w << 5) + __ffs(b) - 1;
+      b &= b - 1;
+      if (pos < (uint32_t)keff) {
+        out[pos] = j;
+        if (a.score_out) a.score_out[(int64_t)row * a.k + pos] = s[j];
+      }
+      ++pos;
+    }
+  }
+  for (int e = keff + tid; e < a.k; e += 1024) {
+    out[e] = -1;
+    if (a.score_out) a.score_out[(int64_t)row * a.k + e] = -INFINITY;
   }
 }
 
-// ---------------------------------------------------------------- plan
 struct Plan {
   int64_t Np;
   bool split;
   int chunks;
-  size_t off_scores, off_hist, off_cnt, off_sel, off_cand, total;
+  size_t off_scores, off_hist, off_hist2, off_cnt, off_sel, off_cand, total;
 };
 
 Plan make_plan(int B, int Tq, int N, int k) {
   Plan p{};
   const int64_t R = (int64_t)B * Tq;
   p.Np = round_up(N > 0 ? N : 1, 64);
-  p.split = R <= 64 && N > 16384;
+  p.split = R <= 64 && N > 16384 && N <= kBitmapMaxN;
   p.chunks = (int)((N + kSplitChunk - 1) / kSplitChunk);
   size_t off = 0;
   p.off_scores = off;
@@ -581,10 +702,12 @@ Plan make_plan(int B, int Tq, int N, int k) {
   if (p.split) {
     p.off_hist = off;
     off += round_up(R * kHistBins * 4, 256);
+    p.off_hist2 = off;
+    off += round_up(R * kHistBins * 4, 256);
     p.off_cnt = off;
-    off += round_up(R * 16, 256);
+    off += round_up(R * (int64_t)p.chunks * 8, 256);
     p.off_sel = off;
-    off += round_up(R * (int64_t)k * 4, 256);
+    off += round_up(R * p.Np * 4, 256);
     p.off_cand = off;
     off += round_up(R * p.Np * 8, 256);
   }
@@ -616,12 +739,13 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
   ta.idx = a.topk_idx; ta.score_out = a.topk_score; ta.qpos = a.qpos; ta.chunks = p.chunks;
   if (p.split) {
     ta.hist = reinterpret_cast<uint32_t*>(w8 + p.off_hist);
+    ta.hist2 = reinterpret_cast<uint32_t*>(w8 + p.off_hist2);
     ta.cnt = reinterpret_cast<uint32_t*>(w8 + p.off_cnt);
     ta.sel = reinterpret_cast<int32_t*>(w8 + p.off_sel);
     ta.cand = reinterpret_cast<uint2*>(w8 + p.off_cand);
-    // The score kernel accumulates into the histogram: clear it (and the
-    // adjacent counters) first, with a kernel rather than a memset.
-    const int64_t n_clear = (int64_t)(p.off_sel - p.off_hist) / 4;
+    // The score and filter kernels accumulate into the histograms: clear them
+    // (and the adjacent counters) first, with a kernel rather than a memset.
+    const int64_t n_clear = (int64_t)(p.off_cnt - p.off_hist) / 4;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_clear + 255) / 256)), dim3(256), 0, st,
                        ta.hist, n_clear);
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -685,14 +809,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
     hipLaunchKernelGGL(topk_filter_kernel, dim3(p.chunks, R), dim3(256), 0, st, ta);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  int pow2 = 1;
-  while (pow2 < a.k) pow2 <<= 1;
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&topk_resolve_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kCandLds * 8 + 8192 * 4);
+      hipFuncAttributeMaxDynamicSharedMemorySize, kBitmapMaxN / 8);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(topk_resolve_kernel, dim3(R), dim3(1024),
-                     (size_t)kCandLds * 8 + (size_t)pow2 * 4, st, ta);
+                     (size_t)((nv_max + 31) / 32) * 4, st, ta);
   return hipGetLastError();
 }
 
