@@ -51,7 +51,7 @@ __host__ __device__ inline int64_t kv_row_bytes(int fmt, int D, int r) {
 struct AttnPlan {
   int G, Hs, n_htiles, n_qgroups, n_work, nsplit, chunk, max_entries;
   int64_t win_rows, row_bytes;
-  size_t off_zero, off_win, off_po, off_pml, total;
+  size_t off_zero, off_win, off_ang, off_po, off_pml, total;
 };
 
 AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries, int W,
@@ -64,6 +64,8 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   off += 256;
   p.off_win = off;
   off += round_up((int64_t)B * p.win_rows * p.row_bytes, 256);
+  p.off_ang = off;
+  off += round_up((int64_t)B * Tq * (r / 2) * 8, 256);
   if (f32_path) {
     p.G = 1; p.Hs = H; p.n_htiles = 1; p.n_qgroups = Tq; p.n_work = B * Tq; p.nsplit = 1;
     p.total = off;
@@ -100,6 +102,8 @@ struct WinArgs {
   const uint8_t* raw;
   uint8_t* win;
   uint8_t* zero_row;
+  float2* ang;               // [B, Tq, r/2] (cos, sin) of each query position's angles
+  int64_t n_win_items;       // window work items (D/8 per row); angle items follow
   int fmt, B, D, r, Tq, W;
   int64_t T_raw, win_rows, row_bytes;
   float theta;
@@ -113,6 +117,18 @@ __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
   if (blockIdx.x == 0 && threadIdx.x < 4) reinterpret_cast<uint32_t*>(a.zero_row)[threadIdx.x] = 0u;
   const int G8 = a.D / 8;
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= a.n_win_items) {            // angle table of the query positions
+    const int np = a.r / 2;
+    const int64_t j = gid - a.n_win_items;
+    if (np == 0 || j >= (int64_t)a.B * a.Tq * np) return;
+    const int64_t qrow = j / np;
+    const int p = (int)(j - qrow * np);
+    const int b = (int)(qrow / a.Tq);
+    float cs, sn;
+    rope_cos_sin((double)((int64_t)a.qpos.v[b] + (qrow - (int64_t)b * a.Tq)), freq[p], &cs, &sn);
+    a.ang[j] = make_float2(cs, sn);
+    return;
+  }
   const int64_t per_b = a.win_rows * G8;
   if (gid >= (int64_t)a.B * per_b) return;
   const int b = (int)(gid / per_b);
@@ -177,6 +193,7 @@ struct KArgs {
   float* part_o;
   float* part_ml;
   const uint8_t* zero_row;   // 16 zero bytes in workspace (source of empty slots)
+  const float2* ang;         // [B, Tq, r/2] (cos, sin) of the query positions' angles
   int mode, N, k, m, W, B, Tq, H, D, r;
   float theta, scale_log2;
   int G, Hs, n_htiles, n_qgroups, nsplit, chunk;
@@ -274,28 +291,40 @@ __device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& 
 
 // ---------------------------------------------------------------- MFMA attention
 
-// ---- staging of 32-entry tiles
-// A tile's rows are gathered with 16-byte loads into VGPRs (8 threads per row,
-// chunks p, p + 8, ...; every lane issues the same loads, empty slots read a
-// zero row) one tile ahead, then written to LDS as bf16 rows (FP8 converted)
-// at a padded stride when the tile is consumed.  The rotated query tile also
-// lives in LDS, which keeps the per-wave registers for the output
-// accumulators and the prefetch.  Barriers inside the loop only wait for LDS
-// traffic, never for the prefetch in flight.
+// ---- tile loop
+// A block holds 64 query rows (G tokens x Hs heads) and four waves; wave w
+// owns rows 16w .. 16w+15 with the whole of D, so QK, the online softmax and
+// PV of a tile need no exchange between waves.  The product runs transposed,
+// on v_mfma_f32_16x16x32_bf16:
+//   S^T[e][r] = sum_d E[e][d] Q[r][d]: A = entry rows read from LDS, B = the
+//     wave's rotated query rows kept in VGPRs for the whole loop;
+//   O^T[d][r] += sum_e E^T[d][e] P^T[e][r]: B = the S^T accumulators
+//     themselves (exp'd, packed to bf16 -- a lane holds row r = lane % 16 and
+//     entries {4q..4q+3, 16+4q..16+4q+3}, q = lane / 16, which is a valid
+//     K order because the A side uses the same order), A = E^T read with
+//     ds_read_b64_tr_b16 (a 16-lane group's transposed 4 x 16 block).
+// A lane therefore keeps one row's running max (shared by its four lanes)
+// and a partial row sum.  Tiles of 32 entries are gathered into VGPRs one
+// tile ahead (8 threads per row, uniform 16-byte loads, empty slots read a
+// zero row), written to one of two LDS buffers as bf16 rows (E4M3 widened by
+// the hardware converter), and one barrier per tile publishes them.
 constexpr int kTile = 32;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x4 ds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
+}
+
 template <int D>
 struct Geo {
-  static constexpr int DW = D / 4;          // columns per wave
-  static constexpr int KQ = DW / 16;        // QK k-steps per wave
-  static constexpr int DT = DW / 32;        // PV column tiles per wave
-  static constexpr int EROW = 2 * D + 16;   // LDS bytes per staged entry / query row
-  static constexpr int SROW = 68;           // floats per (wave, rt, v) logit row
-  static constexpr int PROW = 40;           // bf16 per row of P
+  static constexpr int EROW = 2 * D + 16;   // LDS bytes per staged entry
+  static constexpr int KS = D / 32;         // QK k-steps
+  static constexpr int DT = D / 16;         // PV output tiles
   static constexpr int NCH = D / 64;        // 16-byte chunks per staging thread, bf16 rows
   static constexpr int NCHM = D / 128 + 1;  // same for mixed rows (at most D/16 + 8 chunks)
 };
@@ -303,21 +332,13 @@ struct Geo {
 template <int D, int KV>
 __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   using Gm = Geo<D>;
-  __shared__ __align__(16) uint8_t Et[kTile * Gm::EROW];        // entry tile, bf16 rows
-  __shared__ __align__(16) uint8_t Qs[64 * Gm::EROW];           // rotated queries, bf16
-  __shared__ __align__(16) float Sp[4 * 2 * 16 * Gm::SROW];    // partial logits [wave][rt][v][lane]
-  __shared__ __align__(16) uint16_t Pl[64 * Gm::PROW];         // probabilities [row][entry]
-  __shared__ float alpha[64], rowm[64], rowl[64];
-  __shared__ __align__(16) int tags[kTile];
+  __shared__ __align__(16) uint8_t Et[2][kTile * Gm::EROW];     // entry tiles, bf16 rows
+  __shared__ __align__(16) int tags[2][kTile];
   __shared__ int32_t lidx[kIdxLds];
-  __shared__ double freq[kMaxRopePairs];
-  __shared__ float2 qcs[4][kMaxRopePairs];     // (cos, sin) of t_g * freq_p, g < G
-  __shared__ Vis vis[4];
-  __shared__ int any_rescale;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l = tid & 63, hf = l >> 5, ln = l & 31;
+  const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const Work w = make_work(a, blockIdx.y);
   const int split = blockIdx.x;
   const int e_lo = split * a.chunk;
@@ -325,26 +346,37 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   const int nope = a.D - a.r;
   const int npair = a.r / 2;
   const int row_bytes = (int)a.row_bytes;
-
-  // CSA indices of this split to LDS (the plan keeps them within kIdxLds).
-  const int n_idx = a.mode == 0 ? max(0, min(e_hi, w.n_comp) - e_lo) : 0;
-  if (n_idx > 0) {
-    const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * a.k + e_lo;
-    for (int e = tid; e < n_idx; e += 256) lidx[e] = src[e];
-  }
-  if (tid < 4) vis[tid] = make_vis(a, w, tid);
-  rope_freq_table(freq, a.r, a.theta);
-  __syncthreads();
-
-  // Entry sources: fields hoisted out of the argument struct.
   const int mode = a.mode, G = a.G, kk = a.k, NN = a.N;
-  const int n_comp = w.n_comp, n_tot = w.n_tot;
+  const int n_comp = w.n_comp;
   const uint8_t* kvb = a.kv + (int64_t)w.b * NN * row_bytes;
   const uint8_t* winb = a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * row_bytes;
   const uint8_t* zero_row = a.zero_row;
   const int n_fp8 = KV == kMixed ? nope / 16 : 0;
   const int n_chunks = KV == kMixed ? n_fp8 + a.r / 8 : D / 8;
   const int st_e = tid >> 3, st_part = tid & 7;
+  const int n_tiles = e_hi > e_lo ? (e_hi - e_lo + kTile - 1) / kTile : 0;
+
+  // this lane's query row
+  const int row = wave * 16 + lr;
+  const int g = row / a.Hs, h = w.h0 + row % a.Hs;
+  const bool live = g < w.n_q;
+
+  // query row slices into registers first (one round trip with the tile-0 gather)
+  bf16x8 qreg[Gm::KS];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                       (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D + 8 * lq;
+#pragma unroll
+    for (int s = 0; s < Gm::KS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+  }
+
+  // CSA indices of this split to LDS (the plan keeps them within kIdxLds).
+  const int n_idx = mode == 0 ? max(0, min(e_hi, n_comp) - e_lo) : 0;
+  if (n_idx > 0) {
+    const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * kk + e_lo;
+    for (int e = tid; e < n_idx; e += 256) lidx[e] = src[e];
+  }
+  __syncthreads();
 
   constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
   uint4 stage[NST];
@@ -377,8 +409,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
       stage[q] = ld_stream16(src);
     }
   };
-  auto store_tile = [&]() {
-    uint8_t* row = Et + st_e * Gm::EROW;
+  auto store_tile = [&](int buf) {
+    uint8_t* dst_row = Et[buf] + st_e * Gm::EROW;
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
       const int ch = st_part + 8 * q;
@@ -386,235 +418,159 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
       const uint4 v = stage[q];
       if constexpr (KV == kMixed) {
         if (ch < n_fp8) {    // 16 E4M3 codes -> 16 bf16 (exact)
-          uint4* dst = reinterpret_cast<uint4*>(row + 32 * ch);
+          uint4* dst = reinterpret_cast<uint4*>(dst_row + 32 * ch);
           dst[0] = e4m3x8_to_bf16x8(v.x, v.y);
           dst[1] = e4m3x8_to_bf16x8(v.z, v.w);
         } else {
-          *reinterpret_cast<uint4*>(row + 32 * n_fp8 + 16 * (ch - n_fp8)) = v;
+          *reinterpret_cast<uint4*>(dst_row + 32 * n_fp8 + 16 * (ch - n_fp8)) = v;
         }
       } else {
-        *reinterpret_cast<uint4*>(row + 16 * ch) = v;
+        *reinterpret_cast<uint4*>(dst_row + 16 * ch) = v;
       }
     }
-    if (st_part == 0) tags[st_e] = st_tag;
+    if (st_part == 0) tags[buf][st_e] = st_tag;
   };
 
-  const int n_tiles = e_hi > e_lo ? (e_hi - e_lo + kTile - 1) / kTile : 0;
   if (n_tiles > 0) load_tile(e_lo);
 
-  // ---- prologue: rotated query tile into LDS (row = tid / 4, a quarter of D each)
-  for (int e = tid; e < a.G * npair; e += blockDim.x) {
-    const int g = e / npair, p = e - g * npair;
-    float cs, sn;
-    rope_cos_sin((double)(w.t_first + g), freq[p], &cs, &sn);
-    qcs[g][p] = make_float2(cs, sn);
-  }
-  lds_barrier();
-  {
-    const int row = tid >> 2, qq = tid & 3;
-    const int g = row / a.Hs, h = w.h0 + row % a.Hs;
-    const bool live = g < w.n_q;
-    const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                       (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D + qq * (D / 4);
-    uint4 qraw[D / 32];
+  // the lane's query slices rotated at t (angles from the table the window
+  // kernel wrote)
+  const float2* ang = a.ang + ((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * npair;
+  auto angle = [&](int p) { return ang[p]; };
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c)
-      qraw[c] = live ? *reinterpret_cast<const uint4*>(qp + c * 8) : make_uint4(0, 0, 0, 0);
+  for (int s = 0; s < Gm::KS; ++s) {
+    const int d0 = 32 * s + 8 * lq;
+    if (d0 >= nope) {
+      uint32_t wd[4];
+      __builtin_memcpy(wd, &qreg[s], 16);
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      const int c0 = qq * (D / 4) + c * 8;
-      uint4 raw = qraw[c];
-      if (c0 >= nope && live) {
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-        uint32_t o[4];
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float2 cv = qcs[g][(c0 - nope) / 2 + p];
-          const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
-          o[p] = pack_bf16x2(x0 * cv.x - x1 * cv.y, x0 * cv.y + x1 * cv.x);
-        }
-        raw = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int p = 0; p < 4; ++p) {
+        const float2 cv = angle((d0 - nope) / 2 + p);
+        const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
+        wd[p] = pack_bf16x2(x0 * cv.x - x1 * cv.y, x0 * cv.y + x1 * cv.x);
       }
-      *reinterpret_cast<uint4*>(Qs + row * Gm::EROW + 2 * c0) = raw;
+      __builtin_memcpy(&qreg[s], wd, 16);
     }
   }
 
-  // ---- running softmax state: thread (row = tid/4, part = tid%4)
-  const int srow = tid >> 2, spart = tid & 3;
-  const int sg = srow / a.Hs;
-  const Vis myvis = vis[sg < 4 ? sg : 0];
-  float m_run = -INFINITY, l_run = 0.f;
-
-  f32x16 oacc[2][Gm::DT];
+  const Vis myvis = make_vis(a, w, g);
+  const float scale_log2 = a.scale_log2;
+  float m_run = -INFINITY, l_part = 0.f;
+  f32x4 oacc[Gm::DT];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-    for (int dt = 0; dt < Gm::DT; ++dt) oacc[rt][dt] = f32x16{};
+  for (int dt = 0; dt < Gm::DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0; t < n_tiles; ++t) {
-    lds_barrier();            // tile t-1 fully consumed (and the query tile written)
-    store_tile();             // waits for this thread's prefetched rows
-    if (tid == 0) any_rescale = 0;
-    lds_barrier();
+    const int buf = t & 1;
+    store_tile(buf);          // waits for this thread's prefetched rows
+    lds_barrier();            // tile t visible; every wave is done with tile t-1
     if (t + 1 < n_tiles) load_tile(e_lo + (t + 1) * kTile);
+    const uint8_t* E = Et[buf];
 
-    // ---- QK on this wave's quarter of D
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      f32x16 sacc = {};
-#pragma unroll
-      for (int s = 0; s < Gm::KQ; ++s) {
-        const int d0 = wave * Gm::DW + s * 16 + hf * 8;
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(Qs + (rt * 32 + ln) * Gm::EROW + 2 * d0);
-        const bf16x8 ef = *reinterpret_cast<const bf16x8*>(Et + ln * Gm::EROW + 2 * d0);
-        sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, ef, sacc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) Sp[((wave * 2 + rt) * 16 + v) * Gm::SROW + l] = sacc[v];
-    }
-    lds_barrier();
-
-    // ---- online softmax: thread owns row srow, entries spart*8 .. +8
+    // ---- S^T for entries 0-15 (s0) and 16-31 (s1) of the tile
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     {
-      const int rt = srow >> 5, rem = srow & 31;
-      const int v = 4 * (rem >> 3) + (rem & 3), shf = (rem >> 2) & 1;
-      float sv[8];
+      const uint8_t* eb = E + lr * Gm::EROW + 16 * lq;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sv[e] = 0.f;
-#pragma unroll
-      for (int wv = 0; wv < 4; ++wv) {
-        const float4* src = reinterpret_cast<const float4*>(
-            Sp + ((wv * 2 + rt) * 16 + v) * Gm::SROW + shf * 32 + spart * 8);
-        const float4 x = src[0], y = src[1];
-        sv[0] += x.x; sv[1] += x.y; sv[2] += x.z; sv[3] += x.w;
-        sv[4] += y.x; sv[5] += y.y; sv[6] += y.z; sv[7] += y.w;
-      }
-      const int4 tg0 = *reinterpret_cast<const int4*>(tags + spart * 8);
-      const int4 tg1 = *reinterpret_cast<const int4*>(tags + spart * 8 + 4);
-      const int tg[8] = {tg0.x, tg0.y, tg0.z, tg0.w, tg1.x, tg1.y, tg1.z, tg1.w};
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = visible(tg[e], sg, myvis) ? sv[e] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[e]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 1));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 2));
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float al = exp2f(m_run - m_use);
-      float psum = 0.f;
-      uint32_t pk[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = exp2f(sv[e] - m_use), p1 = exp2f(sv[e + 1] - m_use);
-        psum += p0 + p1;
-        pk[e / 2] = pack_bf16x2(p0, p1);
-      }
-      psum += __shfl_xor(psum, 1);
-      psum += __shfl_xor(psum, 2);
-      l_run = l_run * al + psum;
-      m_run = m_new;
-      *reinterpret_cast<uint4*>(Pl + srow * Gm::PROW + spart * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      if (spart == 0) {
-        alpha[srow] = al;
-        if (al != 1.f) any_rescale = 1;
+      for (int s = 0; s < Gm::KS; ++s) {
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(eb + 64 * s);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * s);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[s], s1, 0, 0, 0);
       }
     }
-    lds_barrier();
 
-    // ---- rescale (only when some row's maximum moved) and PV on this wave's
-    // quarter of the output columns
-    if (any_rescale) {
+    // ---- online softmax of row `row` over the lane's 8 entries
+    const int4 tg0 = *reinterpret_cast<const int4*>(&tags[buf][4 * lq]);
+    const int4 tg1 = *reinterpret_cast<const int4*>(&tags[buf][16 + 4 * lq]);
+    const int tg[8] = {tg0.x, tg0.y, tg0.z, tg0.w, tg1.x, tg1.y, tg1.z, tg1.w};
+    float x[8];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        float al[16];
+    for (int i = 0; i < 4; ++i) { x[i] = s0[i]; x[4 + i] = s1[i]; }
+    float tmax = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) al[v] = alpha[rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)];
-#pragma unroll
-        for (int dt = 0; dt < Gm::DT; ++dt)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) oacc[rt][dt][v] *= al[v];
-      }
+    for (int i = 0; i < 8; ++i) {
+      x[i] = visible(tg[i], g, myvis) ? x[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
     }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float m_new = fmaxf(m_run, tmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float al = exp2f(m_run - m_use);
+    float psum = 0.f;
+    uint32_t pk[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      bf16x8 pf[2];
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-        pf[rt] = *reinterpret_cast<const bf16x8*>(Pl + (rt * 32 + ln) * Gm::PROW + s * 16 + hf * 8);
-#pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt) {
-        const int col = wave * Gm::DW + dt * 32 + ln;
-        const uint8_t* ep = Et + (s * 16 + hf * 8) * Gm::EROW + 2 * col;
-        uint32_t u[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo = *reinterpret_cast<const uint16_t*>(ep + (2 * i) * Gm::EROW);
-          const uint32_t hi = *reinterpret_cast<const uint16_t*>(ep + (2 * i + 1) * Gm::EROW);
-          u[i] = lo | (hi << 16);
-        }
-        uint4 uv = make_uint4(u[0], u[1], u[2], u[3]);
-        const bf16x8 eb = *reinterpret_cast<bf16x8*>(&uv);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-          oacc[rt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pf[rt], eb, oacc[rt][dt], 0, 0, 0);
-      }
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = exp2f(x[i] - m_use), p1 = exp2f(x[i + 1] - m_use);
+      psum += p0 + p1;
+      pk[i / 2] = pack_bf16x2(p0, p1);
     }
-  }
-
-  // ---- row statistics to LDS for the epilogue
-  lds_barrier();
-  if (spart == 0) { rowm[srow] = m_run; rowl[srow] = l_run; }
-  lds_barrier();
-
-  if (a.nsplit > 1) {
-    const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
-    float* po = a.part_o + slot * 64 * D;
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    l_part = l_part * al + psum;
+    m_run = m_new;
+    bf16x8 pb;
+    __builtin_memcpy(&pb, pk, 16);
+    if (__ballot(al != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-          po[row * D + wave * Gm::DW + dt * 32 + ln] = oacc[rt][dt][v];
-        }
-    if (tid < 64) {
-      a.part_ml[(slot * 64 + tid) * 2] = rowm[tid];
-      a.part_ml[(slot * 64 + tid) * 2 + 1] = rowl[tid];
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= al;
+    }
+
+    // ---- O^T += E^T P^T, 16 output dims per MFMA
+    {
+      const uint8_t* tb = E + (4 * lq + (lr >> 2)) * Gm::EROW + 8 * (lr & 3);
+#pragma unroll
+      for (int dt = 0; dt < Gm::DT; ++dt) {
+        const bf16x4 lo = ds_read_tr(tb + 32 * dt);
+        const bf16x4 hi = ds_read_tr(tb + 16 * Gm::EROW + 32 * dt);
+        const bf16x8 ab = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, pb, oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- row sum over the row's four lanes
+  float l_row = l_part;
+  l_row += __shfl_xor(l_row, 16);
+  l_row += __shfl_xor(l_row, 32);
+
+  if (a.nsplit > 1) {
+    const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
+    float* po = a.part_o + (slot * 64 + row) * D + 4 * lq;
+#pragma unroll
+    for (int dt = 0; dt < Gm::DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt) =
+          make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
+    if (lq == 0) {
+      a.part_ml[(slot * 64 + row) * 2] = m_run;
+      a.part_ml[(slot * 64 + row) * 2 + 1] = l_row;
     }
     return;
   }
 
   // ---- single split: normalise, rotate back at -t, store bf16
+  if (!live) return;
+  float den = l_row;
+  if (a.sink) den += exp2f(a.sink[h] * 1.4426950408889634f - (m_run == -INFINITY ? 0.f : m_run));
+  const float inv = den > 0.f ? 1.f / den : 0.f;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * D + 4 * lq;
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int dt = 0; dt < Gm::DT; ++dt) {
+    const int d0 = 16 * dt + 4 * lq;
+    float o[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int row = rt * 32 + 8 * (v >> 2) + 4 * hf + (v & 3);
-      const int g = row / a.Hs, h = w.h0 + row % a.Hs;
-      const bool live = g < w.n_q;
-      const float mr = rowm[row];
-      float den = rowl[row];
-      if (a.sink) den += exp2f(a.sink[h] * 1.4426950408889634f - (mr == -INFINITY ? 0.f : mr));
-      const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int i = 0; i < 4; ++i) o[i] = oacc[dt][i] * inv;
+    if (d0 >= nope) {             // rotation at -t: (cos, -sin) of the query's angle
 #pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt) {
-        const int col = wave * Gm::DW + dt * 32 + ln;
-        float o = oacc[rt][dt][v] * inv;
-        const float partner = __shfl_xor(o, 1);
-        if (col >= nope) {            // rotation at -t: (cos, -sin) of the query's angle
-          const float2 cv = qcs[g < 4 ? g : 0][(col - nope) >> 1];
-          const float cs = cv.x, sn = -cv.y;
-          o = (col & 1) ? partner * sn + o * cs : o * cs - partner * sn;
-        }
-        if (live) {
-          uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * D + col;
-          *op = (uint16_t)f32_to_bf16(o);
-        }
+      for (int p = 0; p < 2; ++p) {
+        const float2 cv = angle((d0 - nope) / 2 + p);
+        const float x0 = o[2 * p], x1 = o[2 * p + 1];
+        o[2 * p] = x0 * cv.x + x1 * cv.y;
+        o[2 * p + 1] = -x0 * cv.y + x1 * cv.x;
       }
     }
+    *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
   }
 }
 
@@ -622,9 +578,6 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
 __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   __shared__ float wgt[1024];
   __shared__ float red[2];
-  __shared__ double freq[kMaxRopePairs];
-  rope_freq_table(freq, a.r, a.theta);
-  __syncthreads();
   const int work = blockIdx.x / 64, row = blockIdx.x % 64;
   const Work w = make_work(a, work);
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
@@ -653,8 +606,8 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   }
   __syncthreads();
   const float inv = red[0];
-  const int64_t t = w.t_first + g;
   const int nope = a.D - a.r;
+  const float2* ang = a.ang + ((int64_t)w.b * a.Tq + w.i0 + g) * (a.r / 2);
   uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * a.D;
   for (int c = 2 * threadIdx.x; c < a.D; c += 2 * blockDim.x) {
     float o0 = 0.f, o1 = 0.f;
@@ -668,10 +621,9 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
     }
     o0 *= inv;
     o1 *= inv;
-    if (c >= nope) {
-      float cs, sn;
-      rope_cos_sin(-(double)t, freq[(c - nope) >> 1], &cs, &sn);
-      const float r0 = o0 * cs - o1 * sn, r1 = o0 * sn + o1 * cs;
+    if (c >= nope) {             // rotation at -t
+      const float2 cv = ang[(c - nope) >> 1];
+      const float r0 = o0 * cv.x + o1 * cv.y, r1 = -o0 * cv.y + o1 * cv.x;
       o0 = r0;
       o1 = r1;
     }
@@ -820,7 +772,9 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
     wa.fmt = a.kv_fmt; wa.B = a.B; wa.D = a.D; wa.r = a.r; wa.Tq = a.Tq; wa.W = a.W;
     wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes; wa.theta = a.theta;
     wa.qpos = a.qpos; wa.rawpos = a.rawpos;
-    const int64_t n = (int64_t)a.B * p.win_rows * (a.D / 8);
+    wa.ang = reinterpret_cast<float2*>(w8 + p.off_ang);
+    wa.n_win_items = (int64_t)a.B * p.win_rows * (a.D / 8);
+    const int64_t n = wa.n_win_items + (int64_t)a.B * a.Tq * (a.r / 2);
     const unsigned blocks = (unsigned)std::max<int64_t>(1, (n + 255) / 256);
     hipLaunchKernelGGL(rope_window_kernel, dim3(blocks), dim3(256), 0, st, wa);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -828,6 +782,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   KArgs k{};
   k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
   k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
+  k.ang = reinterpret_cast<const float2*>(w8 + p.off_ang);
   k.part_o = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_po) : nullptr;
   k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
   k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;

@@ -136,3 +136,12 @@ def test_attend_determinism():
             for _ in range(2)]
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
+
+
+def test_csa_bf16_h8_eight_tokens_per_block():
+    # H = 8: a block holds 8 query tokens, two per wave
+    _case(0, 1, 19, 8, 128, 64, 600, 24, 4, 16, [2400], "bf16", 13)
+
+
+def test_hca_bf16_h2_thirty_two_tokens_per_block():
+    _case(1, 1, 70, 2, 256, 64, 40, 0, 128, 64, [4800], "bf16", 14)
