@@ -34,6 +34,8 @@
 //    the set in ascending index order from an LDS bitmap of the row.
 // Both paths give the same set: first min(k, n_vis) under (score desc, index
 // asc).  Deterministic: no floating-point atomics, ordered output.
+#include <algorithm>
+
 #include "lac_internal.h"
 
 namespace lac {
@@ -67,7 +69,7 @@ __device__ __forceinline__ void hist_add(uint32_t* hist, bool on, uint32_t d) {
   uint64_t active = __ballot(on);
   while (active) {
     const int leader = __ffsll((unsigned long long)active) - 1;
-    const uint32_t dl = __shfl(d, leader);
+    const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
     const uint64_t same = __ballot(on && d == dl) & active;
     if (lane_id() == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
     active &= ~same;
@@ -135,24 +137,46 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   const int64_t t_last = (int64_t)a.qpos.v[b] + i0 + n_rows_blk - 1;
   const int64_t nv_max = n_visible(t_last, a.N, a.m);
 
-  for (int e = threadIdx.x; e < kRowsPerBlock * HI; e += 256) {
-    const int rr = e / HI, h = e - rr * HI;
-    const int i = min(i0 + rr, a.Tq - 1);
-    sw[rr][h] = a.w[((int64_t)b * a.Tq + i) * HI + h];
-  }
-  if (do_hist)
-    for (int e = threadIdx.x; e < kHistBins; e += 256) lhist[e] = 0u;
-  __syncthreads();
-
-  const int64_t tile_lo = ((int64_t)blockIdx.x * KW + wk) * a.tiles_per_wave;
-  int64_t tile_hi = tile_lo + a.tiles_per_wave;
+  // Wave gw of the row's nw key waves takes tiles gw, gw + nw, gw + 2nw, ...:
+  // at any moment the waves of a row stream one contiguous stretch of keys,
+  // which spreads their loads over all memory channels.
+  const int64_t gw = (int64_t)blockIdx.x * KW + wk, nw = (int64_t)gridDim.x * KW;
   const int64_t n_tiles = (nv_max + 31) / 32;
-  if (tile_hi > n_tiles) tile_hi = n_tiles;
+  const int64_t n_mine = gw < n_tiles ? std::min<int64_t>(a.tiles_per_wave, (n_tiles - gw + nw - 1) / nw) : 0;
 
-  if (tile_lo < tile_hi) {
-    // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
-    bf16x8 qf[QPW][HT][KS];
-    int64_t nv_row[QPW];
+  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
+  uint8_t* kt = ktile[wave];
+  // Load instruction u of a tile: lane l takes 16 bytes at u*1024 + l*16 of
+  // the tile in LDS order, i.e. row kk, swizzled chunk slot cs, which holds
+  // the row's chunk cs ^ (kk % CH).
+  auto load_tile = [&](int64_t tile, uint4* st) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int o = u * 1024 + l * 16;
+      const int kk = o / ROWB, cs = (o % ROWB) / 16;
+      int64_t j = tile * 32 + kk;
+      if (j > a.N - 1) j = a.N - 1;
+      st[u] = ld_stream16(Kb + j * ROWB + ((cs ^ (kk % CH)) * 16));
+    }
+  };
+  auto store_tile = [&](const uint4* st) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
+  };
+
+  // The first tiles and the query fragments are requested before anything
+  // else, so their latency overlaps the set-up below.  PF tiles are in
+  // flight per wave (two for the one-query decode shape, whose registers
+  // allow it); the stages alternate.
+  constexpr int PF = QPW == 1 ? 2 : 1;
+  uint4 stage[PF][NLD];
+#pragma unroll
+  for (int f = 0; f < PF; ++f)
+    if (f < n_mine) load_tile(gw + f * nw, stage[f]);
+  // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
+  bf16x8 qf[QPW][HT][KS];
+  int64_t nv_row[QPW];
+  if (n_mine > 0) {
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
       const int rr = wr * QPW + qi;
@@ -166,34 +190,24 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
         for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
       }
     }
+  }
 
-    const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
-    uint8_t* kt = ktile[wave];
-    // Load instruction u of a tile: lane l takes 16 bytes at u*1024 + l*16 of
-    // the tile in LDS order, i.e. row kk, swizzled chunk slot cs, which holds
-    // the row's chunk cs ^ (kk % CH).
-    auto load_tile = [&](int64_t tile, uint4* st) {
-#pragma unroll
-      for (int u = 0; u < NLD; ++u) {
-        const int o = u * 1024 + l * 16;
-        const int kk = o / ROWB, cs = (o % ROWB) / 16;
-        int64_t j = tile * 32 + kk;
-        if (j > a.N - 1) j = a.N - 1;
-        st[u] = ld_stream16(Kb + j * ROWB + ((cs ^ (kk % CH)) * 16));
-      }
-    };
-    auto store_tile = [&](const uint4* st) {
-#pragma unroll
-      for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
-    };
+  for (int e = threadIdx.x; e < kRowsPerBlock * HI; e += 256) {
+    const int rr = e / HI, h = e - rr * HI;
+    const int i = min(i0 + rr, a.Tq - 1);
+    sw[rr][h] = a.w[((int64_t)b * a.Tq + i) * HI + h];
+  }
+  if (do_hist)
+    for (int e = threadIdx.x; e < kHistBins; e += 256) lhist[e] = 0u;
+  __syncthreads();
 
-    uint4 stage[NLD];
-    load_tile(tile_lo, stage);
-    for (int64_t tile = tile_lo; tile < tile_hi; ++tile) {
-      store_tile(stage);
+  if (n_mine > 0) {
+    auto consume = [&](int64_t it, uint4* st) {
+      const int64_t tile = gw + it * nw;
+      store_tile(st);
       __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): LDS writes done
       __builtin_amdgcn_wave_barrier();
-      if (tile + 1 < tile_hi) load_tile(tile + 1, stage);
+      if (it + PF < n_mine) load_tile(tile + PF * nw, st);
       bf16x8 kf[KS];
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
@@ -223,6 +237,11 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);      // LDS reads of this tile done
       __builtin_amdgcn_wave_barrier();
+    };
+    for (int64_t it = 0; it < n_mine; it += PF) {
+#pragma unroll
+      for (int f = 0; f < PF; ++f)
+        if (it + f < n_mine) consume(it + f, stage[f]);
     }
   }
 
@@ -785,8 +804,12 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
         LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
 #undef LAC_SCORE_CASE
       } else {
-        // Decode: one query per block, 4 waves split the keys.
-        sa.tiles_per_wave = 8;
+        // Decode: one query per block, 4 waves split the keys.  The grid is
+        // one round of the 512 resident blocks (two blocks of 4 waves per
+        // compute unit at this kernel's register use), so no partial second
+        // round trails the sweep.
+        const int64_t per_row = std::max<int64_t>(1, 512 / R);
+        sa.tiles_per_wave = (int)std::max<int64_t>(2, (n_tiles + 4 * per_row - 1) / (4 * per_row));
         const int64_t chunks = (n_tiles + 4 * sa.tiles_per_wave - 1) / (4 * sa.tiles_per_wave);
         const int groups = a.B * a.Tq;
 #define LAC_SCORE_CASE(ht, ks) \
