@@ -11,14 +11,51 @@
 // The kernel is a pure HBM stream: each thread owns 8 consecutive channels
 // (one 16-byte bf16 load per token row, coalesced across the row) of one
 // entry and walks its share of the block's tokens with an online softmax
-// (running max, denominator and weighted sum in fp32).  When a block has
-// many tokens (HCA), S threads split the tokens and merge their partial
-// states through LDS, so short sequences still spread over many lanes.
+// (running max, denominator and weighted sum in fp32), with up to eight
+// tokens' loads in flight before any is used.  When a block has many tokens
+// (HCA), S threads split the tokens and merge their partial states through
+// LDS in a log2(S)-level tree, so short sequences still spread over many
+// lanes.  The rotation table is built while the first loads are in flight.
 #include "lac_internal.h"
 
 namespace lac {
 
 namespace {
+
+// Raw 8-channel slice of one token row: bf16 in one 16-byte word, f32 in two.
+template <int IN>
+struct Raw8 {
+  uint4 w[IN == kF32 ? 2 : 1];
+};
+
+template <int IN>
+__device__ __forceinline__ Raw8<IN> load_raw8(const void* base, int64_t elem) {
+  Raw8<IN> r;
+  if constexpr (IN == kF32) {
+    const float* p = static_cast<const float*>(base) + elem;
+    r.w[0] = ld_stream16(p);
+    r.w[1] = ld_stream16(p + 4);
+  } else {
+    r.w[0] = ld_stream16(static_cast<const uint16_t*>(base) + elem);
+  }
+  return r;
+}
+
+template <int IN>
+__device__ __forceinline__ void unpack8(const Raw8<IN>& r, float* v) {
+  if constexpr (IN == kF32) {
+    const uint32_t w[8] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w, r.w[1].x, r.w[1].y, r.w[1].z, r.w[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+  } else {
+    const uint32_t w[4] = {r.w[0].x, r.w[0].y, r.w[0].z, r.w[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+}
 
 template <int IN>
 __device__ __forceinline__ void load8(const void* base, int64_t elem, float* v) {
@@ -56,21 +93,23 @@ __device__ __forceinline__ void softmax_step(const float* xv, const float* zv, f
 // Block of blockDim.x threads: S threads per (entry, 8-channel group) split the
 // block's tokens; several entries per block when D/8 * S < blockDim.x.
 template <int IN, int OUT>
-__global__ void __launch_bounds__(1024) compress_kernel(CompressArgs a) {
+__global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
   extern __shared__ float part[];                  // [blockDim.x][25] when S > 1
   __shared__ double freq[kMaxRopePairs];
-  rope_freq_table(freq, a.r, a.theta);
-  __syncthreads();
-  const int G = a.D >> 3;            // channel groups of 8
-  const int per_entry = G * a.S;     // threads per entry
+  // A block covers GB of the entry's G groups of 8 channels (G / GB blocks
+  // per entry), or several whole entries when GB = G.
+  const int G = a.D >> 3;
+  const int GB = a.GB;
+  const int per_entry = GB * a.S;    // threads per (entry, channel slice)
   const int epb = blockDim.x / per_entry;   // entries per block
+  const int slices = G / GB;
   const int t = threadIdx.x;
   const int le = t / per_entry;
   const int within = t - le * per_entry;
-  const int g = within % G;
-  const int s = within / G;
+  const int s = within / GB;
+  const int g = (blockIdx.x % slices) * GB + (within - s * GB);
   const int N = a.T / a.m;
-  const int64_t e = (int64_t)blockIdx.x * epb + le;
+  const int64_t e = (int64_t)(blockIdx.x / slices) * epb + le;
   const bool live = le < epb && e < (int64_t)a.B * N;
   const int b = live ? (int)(e / N) : 0;
   const int j = live ? (int)(e - (int64_t)b * N) : 0;
@@ -84,48 +123,65 @@ __global__ void __launch_bounds__(1024) compress_kernel(CompressArgs a) {
     const int64_t row0 = (int64_t)j * a.m + (int64_t)s * per;
     const int64_t xb = (b * a.kv_bstride + row0) * a.D + g * 8;
     const int64_t zb = (b * a.z_bstride + row0) * a.D + g * 8;
-    int i = 0;
-    // Four tokens' loads in flight before any of them is used.
-    for (; i + 4 <= per; i += 4) {
-      float xv[4][8], zv[4][8];
+    // TOK tokens' loads in flight before any of them is used, kept packed
+    // until used (rows past the thread's share re-read its last row and are
+    // not used).
+    constexpr int TOK = IN == kF32 ? 4 : 8;
+    for (int i = 0; i < per; i += TOK) {
+      Raw8<IN> xr[TOK], zr[TOK];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        load8<IN>(a.kv, xb + (int64_t)(i + u) * a.D, xv[u]);
-        load8<IN>(a.logits, zb + (int64_t)(i + u) * a.D, zv[u]);
+      for (int u = 0; u < TOK; ++u) {
+        const int64_t row = min(i + u, per - 1);
+        xr[u] = load_raw8<IN>(a.kv, xb + row * a.D);
+        zr[u] = load_raw8<IN>(a.logits, zb + row * a.D);
+      }
+      if (i == 0) {
+        rope_freq_table(freq, a.r, a.theta);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) softmax_step<IN>(xv[u], zv[u], mx, den, acc);
+      for (int u = 0; u < TOK; ++u) {
+        if (i + u < per) {
+          float xv[8], zv[8];
+          unpack8<IN>(xr[u], xv);
+          unpack8<IN>(zr[u], zv);
+          softmax_step<IN>(xv, zv, mx, den, acc);
+        }
+      }
     }
-    for (; i < per; ++i) {
-      float xv[8], zv[8];
-      load8<IN>(a.kv, xb + (int64_t)i * a.D, xv);
-      load8<IN>(a.logits, zb + (int64_t)i * a.D, zv);
-      softmax_step<IN>(xv, zv, mx, den, acc);
-    }
+  } else {
+    rope_freq_table(freq, a.r, a.theta);
   }
+  __syncthreads();                   // rotation table complete
 
   if (a.S > 1) {
+    // Tree merge: at level o, thread s < o absorbs thread s + o.
     float* mine = part + t * 25;
+    for (int o = a.S >> 1; o >= 1; o >>= 1) {
+      if (s < 2 * o) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      mine[c] = mx[c];
-      mine[8 + c] = den[c];
-      mine[16 + c] = acc[c];
-    }
-    __syncthreads();
-    if (s != 0) return;
-    for (int o = 1; o < a.S; ++o) {
-      const float* other = part + (t + o * G) * 25;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float om = other[c];
-        const float nm = fmaxf(mx[c], om);
-        const float s0 = __expf(mx[c] - nm), s1 = __expf(om - nm);
-        den[c] = den[c] * s0 + other[8 + c] * s1;
-        acc[c] = acc[c] * s0 + other[16 + c] * s1;
-        mx[c] = nm;
+        for (int c = 0; c < 8; ++c) {
+          mine[c] = mx[c];
+          mine[8 + c] = den[c];
+          mine[16 + c] = acc[c];
+        }
       }
+      __syncthreads();
+      if (s < o) {
+        const float* other = part + (t + o * GB) * 25;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const float om = other[c];
+          const float nm = fmaxf(mx[c], om);
+          const float s0 = nm == -INFINITY ? 0.f : __expf(mx[c] - nm);
+          const float s1 = nm == -INFINITY ? 0.f : __expf(om - nm);
+          den[c] = den[c] * s0 + other[8 + c] * s1;
+          acc[c] = acc[c] * s0 + other[16 + c] * s1;
+          mx[c] = nm;
+        }
+      }
+      __syncthreads();
     }
+    if (s != 0) return;
   }
   if (!live) return;
 
@@ -181,7 +237,7 @@ template <int IN, int OUT>
 hipError_t launch(const CompressArgs& a, int grid, int threads, size_t lds, hipStream_t st) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&compress_kernel<IN, OUT>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, 1024 * 25 * (int)sizeof(float));
+      hipFuncAttributeMaxDynamicSharedMemorySize, 512 * 25 * (int)sizeof(float));
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((compress_kernel<IN, OUT>), dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
@@ -191,16 +247,25 @@ hipError_t launch(const CompressArgs& a, int grid, int threads, size_t lds, hipS
 
 hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   const int G = a.D / 8;
-  // Split a block's tokens over S threads until each thread has at most 4.
+  // Split a block's tokens over S threads until each thread has at most 8
+  // (a bf16 thread's loads are then all in flight at once), then give a
+  // block at most 256 threads: GB channel groups of one entry, or whole
+  // entries when an entry needs fewer threads.
   int S = 1;
-  while (a.m / S > 4 && G * S * 2 <= 1024 && a.m % (2 * S) == 0) S *= 2;
+  while (a.m / S > 8 && S < 256 && a.m % (2 * S) == 0) S *= 2;
+  int GB = G;
+  while (GB * S > 256 && GB % 2 == 0) GB /= 2;
+  if (GB * S > 512) {           // few channel groups and a long block: fewer splits
+    while (GB * S > 512) S /= 2;
+  }
   a.S = S;
-  const int threads = G * S <= 256 ? 256 : G * S;
-  const int epb = threads / (G * S);
+  a.GB = GB;
+  const int threads = GB * S <= 256 ? (GB == G ? 256 : GB * S) : GB * S;
+  const int epb = threads / (GB * S);
   const size_t lds = S > 1 ? (size_t)threads * 25 * sizeof(float) : 0;
   const int64_t entries = (int64_t)a.B * (a.T / a.m);
   if (entries == 0) return hipSuccess;
-  const int grid = (int)((entries + epb - 1) / epb);
+  const int grid = (int)(((entries + epb - 1) / epb) * (G / GB));
   TimedLaunch tl(kKernelCompress, st);
   if (a.in_fmt == kF32) {
     if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, threads, lds, st);

@@ -40,6 +40,7 @@ struct CompressArgs {
   float theta;
   int64_t kv_bstride, z_bstride, out_bstride;  // rows
   int S;                                       // token splits (set by the launcher)
+  int GB;                                      // 8-channel groups per block (launcher)
   Positions pos0;
 };
 hipError_t launch_compress(CompressArgs a, hipStream_t st);
