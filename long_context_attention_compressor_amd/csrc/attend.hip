@@ -192,8 +192,12 @@ struct KArgs {
   void* out;
   float* part_o;
   float* part_ml;
-  const uint8_t* zero_row;   // 16 zero bytes in workspace (source of empty slots)
-  const float2* ang;         // [B, Tq, r/2] (cos, sin) of the query positions' angles
+  const uint8_t* zero_row;   // 16 zero bytes in workspace (f32 path)
+  const float2* ang;         // [B, Tq, r/2] (cos, sin) of the query angles (f32 path)
+  const uint8_t* raw;        // [B, T_raw, row] raw window rows, not rotated
+  int64_t T_raw;
+  int win_rotated;           // window rows come pre-rotated from `win` (prefill)
+  Positions rawpos;
   int mode, N, k, m, W, B, Tq, H, D, r;
   float theta, scale_log2;
   int G, Hs, n_htiles, n_qgroups, nsplit, chunk;
@@ -304,7 +308,10 @@ __device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& 
 //     K order because the A side uses the same order), A = E^T read with
 //     ds_read_b64_tr_b16 (a 16-lane group's transposed 4 x 16 block).
 // A lane therefore keeps one row's running max (shared by its four lanes)
-// and a partial row sum.  Tiles of 32 entries are gathered into VGPRs one
+// and a partial row sum.  The max used for the exponentials moves only when
+// a logit exceeds it by more than 2^8 (log2 domain), so the accumulators are
+// rescaled rarely; probabilities up to 2^8 are exact enough in bf16 and the
+// final division by the row sum (taken with the same max) is unchanged.  Tiles of 32 entries are gathered into VGPRs one
 // tile ahead (8 threads per row, uniform 16-byte loads, empty slots read a
 // zero row), written to one of two LDS buffers as bf16 rows (E4M3 widened by
 // the hardware converter), and one barrier per tile publishes them.
@@ -335,6 +342,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   __shared__ __align__(16) uint8_t Et[2][kTile * Gm::EROW];     // entry tiles, bf16 rows
   __shared__ __align__(16) int tags[2][kTile];
   __shared__ int32_t lidx[kIdxLds];
+  __shared__ double freq[kMaxRopePairs];
+  extern __shared__ float2 qang[];            // [G][r/2] (cos, sin) of t_g * freq_p
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -349,8 +358,12 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   const int mode = a.mode, G = a.G, kk = a.k, NN = a.N;
   const int n_comp = w.n_comp;
   const uint8_t* kvb = a.kv + (int64_t)w.b * NN * row_bytes;
-  const uint8_t* winb = a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * row_bytes;
-  const uint8_t* zero_row = a.zero_row;
+  // window row of position lo_w + off: pre-rotated, or raw and rotated here
+  const bool rot_here = !a.win_rotated;
+  const uint8_t* winb = rot_here
+      ? a.raw + ((int64_t)w.b * a.T_raw + (w.lo_w - a.rawpos.v[w.b])) * row_bytes
+      : a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * row_bytes;
+  const uint8_t* any_row = static_cast<const uint8_t*>(a.q);   // valid address for empty slots
   const int n_fp8 = KV == kMixed ? nope / 16 : 0;
   const int n_chunks = KV == kMixed ? n_fp8 + a.r / 8 : D / 8;
   const int st_e = tid >> 3, st_part = tid & 7;
@@ -376,6 +389,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * kk + e_lo;
     for (int e = tid; e < n_idx; e += 256) lidx[e] = src[e];
   }
+  rope_freq_table(freq, a.r, a.theta);
   __syncthreads();
 
   constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
@@ -401,30 +415,49 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     }
     st_tag = tag;
     // Every lane issues all NST loads (no divergent branches around them);
-    // chunks past the row and empty slots read the 16-byte zero row.
+    // chunks past the row and empty slots read a valid address and are not
+    // used (an empty slot is staged as zeros).
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
       const int ch = st_part + 8 * q;
-      const uint8_t* src = (rs != nullptr && ch < n_chunks) ? rs + 16 * ch : zero_row;
+      const uint8_t* src = (rs != nullptr && ch < n_chunks) ? rs + 16 * ch : any_row;
       stage[q] = ld_stream16(src);
     }
   };
+  // A window row is rotated here at its position s: the 16-byte chunk of
+  // bf16 rope dims it holds is 4 pairs starting at pair p0.
+  auto rotate_chunk = [&](uint4 v, int p0, int64_t pos) {
+    uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      float cs, sn;
+      rope_cos_sin((double)pos, freq[p0 + p], &cs, &sn);
+      const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
+      wd[p] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+    }
+    return make_uint4(wd[0], wd[1], wd[2], wd[3]);
+  };
   auto store_tile = [&](int buf) {
     uint8_t* dst_row = Et[buf] + st_e * Gm::EROW;
+    const bool empty = st_tag == kNoEntry;
+    const bool win = rot_here && st_tag >= kWinTag;
+    const int64_t wpos = w.lo_w + (st_tag - kWinTag);
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
       const int ch = st_part + 8 * q;
       if (ch >= n_chunks) continue;
-      const uint4 v = stage[q];
+      uint4 v = empty ? make_uint4(0u, 0u, 0u, 0u) : stage[q];
       if constexpr (KV == kMixed) {
         if (ch < n_fp8) {    // 16 E4M3 codes -> 16 bf16 (exact)
           uint4* dst = reinterpret_cast<uint4*>(dst_row + 32 * ch);
           dst[0] = e4m3x8_to_bf16x8(v.x, v.y);
           dst[1] = e4m3x8_to_bf16x8(v.z, v.w);
         } else {
+          if (win) v = rotate_chunk(v, 4 * (ch - n_fp8), wpos);
           *reinterpret_cast<uint4*>(dst_row + 32 * n_fp8 + 16 * (ch - n_fp8)) = v;
         }
       } else {
+        if (win && 8 * ch >= nope) v = rotate_chunk(v, (8 * ch - nope) / 2, wpos);
         *reinterpret_cast<uint4*>(dst_row + 16 * ch) = v;
       }
     }
@@ -433,9 +466,15 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
 
   if (n_tiles > 0) load_tile(e_lo);
 
-  // the lane's query slices rotated at t (angles from the table the window
-  // kernel wrote)
-  const float2* ang = a.ang + ((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * npair;
+  // the block's query angles, then the lane's query slices rotated at t
+  for (int e = tid; e < G * npair; e += 256) {
+    const int gg = e / npair, p = e - gg * npair;
+    float cs, sn;
+    rope_cos_sin((double)(w.t_first + gg), freq[p], &cs, &sn);
+    qang[e] = make_float2(cs, sn);
+  }
+  __syncthreads();
+  const float2* ang = qang + (live ? g : 0) * npair;
   auto angle = [&](int p) { return ang[p]; };
 #pragma unroll
   for (int s = 0; s < Gm::KS; ++s) {
@@ -495,9 +534,11 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     }
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
+    const bool moved = tmax > m_run + 8.f;          // also true for the first visible entry
+    const bool rescale = moved && m_run != -INFINITY;   // the row's O holds earlier entries
+    const float m_new = moved ? tmax : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float al = exp2f(m_run - m_use);
+    const float al = moved ? exp2f(m_run - m_use) : 1.f;
     float psum = 0.f;
     uint32_t pk[4];
 #pragma unroll
@@ -510,7 +551,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     m_run = m_new;
     bf16x8 pb;
     __builtin_memcpy(&pb, pk, 16);
-    if (__ballot(al != 1.f)) {
+    if (__ballot(rescale)) {
 #pragma unroll
       for (int dt = 0; dt < Gm::DT; ++dt)
 #pragma unroll
@@ -578,6 +619,8 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
 __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   __shared__ float wgt[1024];
   __shared__ float red[2];
+  __shared__ double freq[kMaxRopePairs];
+  rope_freq_table(freq, a.r, a.theta);
   const int work = blockIdx.x / 64, row = blockIdx.x % 64;
   const Work w = make_work(a, work);
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
@@ -607,7 +650,7 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   __syncthreads();
   const float inv = red[0];
   const int nope = a.D - a.r;
-  const float2* ang = a.ang + ((int64_t)w.b * a.Tq + w.i0 + g) * (a.r / 2);
+  const int64_t t = w.t_first + g;
   uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * a.D;
   for (int c = 2 * threadIdx.x; c < a.D; c += 2 * blockDim.x) {
     float o0 = 0.f, o1 = 0.f;
@@ -622,8 +665,9 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
     o0 *= inv;
     o1 *= inv;
     if (c >= nope) {             // rotation at -t
-      const float2 cv = ang[(c - nope) >> 1];
-      const float r0 = o0 * cv.x + o1 * cv.y, r1 = -o0 * cv.y + o1 * cv.x;
+      float cs, sn;
+      rope_cos_sin((double)t, freq[(c - nope) >> 1], &cs, &sn);
+      const float r0 = o0 * cs + o1 * sn, r1 = -o0 * sn + o1 * cs;
       o0 = r0;
       o1 = r1;
     }
@@ -739,7 +783,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
 
 template <int D, int KV>
 hipError_t launch_mfma(const KArgs& k, const AttnPlan& p, hipStream_t st) {
-  const size_t lds = 0;    // all LDS of the kernel is static
+  const size_t lds = (size_t)p.G * (k.r / 2) * sizeof(float2);   // the block's query angles
   {
     TimedLaunch tl(kKernelAttend, st);
     hipLaunchKernelGGL((attend_mfma_kernel<D, KV>), dim3(p.nsplit, p.n_work), dim3(256), lds, st, k);
@@ -763,8 +807,11 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   hipError_t e;
-  {
-    // Rotated window rows, and the zero row that empty tile slots read.
+  // With many queries per sequence the window rows are shared by many blocks:
+  // rotate them once up front.  In decode each block rotates its own.
+  const bool win_rotated = f32 || a.Tq > 8;
+  if (win_rotated && a.W > 0) {
+    // Rotated window rows (and the query angles of the float32 path).
     WinArgs wa{};
     wa.raw = static_cast<const uint8_t*>(a.raw);
     wa.win = w8 + p.off_win;
@@ -791,6 +838,8 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   k.G = p.G; k.Hs = p.Hs; k.n_htiles = p.n_htiles; k.n_qgroups = p.n_qgroups;
   k.nsplit = p.nsplit; k.chunk = p.chunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;
   k.qpos = a.qpos;
+  k.raw = static_cast<const uint8_t*>(a.raw); k.T_raw = a.T_raw; k.rawpos = a.rawpos;
+  k.win_rotated = win_rotated;
   if (f32) {
     const size_t lds = ((size_t)a.H * a.D + 32 * a.D + a.H * 32 + 3 * a.H) * 4 + 32 * 4;
     TimedLaunch tl(kKernelAttend, st);
