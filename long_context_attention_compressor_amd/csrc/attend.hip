@@ -89,7 +89,7 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.nsplit = (p.max_entries + p.chunk - 1) / p.chunk;
   if (p.nsplit > 1) {
     p.off_po = off;
-    off += round_up((int64_t)p.n_work * p.nsplit * 64 * D * 4, 256);
+    off += round_up((int64_t)p.n_work * p.nsplit * 64 * D * 2, 256);
     p.off_pml = off;
     off += round_up((int64_t)p.n_work * p.nsplit * 64 * 2 * 4, 256);
   }
@@ -190,7 +190,7 @@ struct KArgs {
   const uint8_t* win;
   const float* sink;
   void* out;
-  float* part_o;
+  _Float16* part_o;         // [work, split, 64, D] partial outputs / their row sums
   float* part_ml;
   const uint8_t* zero_row;   // 16 zero bytes in workspace (f32 path)
   const float2* ang;         // [B, Tq, r/2] (cos, sin) of the query angles (f32 path)
@@ -296,25 +296,30 @@ __device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& 
 // ---------------------------------------------------------------- MFMA attention
 
 // ---- tile loop
-// A block holds 64 query rows (G tokens x Hs heads) and four waves; wave w
-// owns rows 16w .. 16w+15 with the whole of D, so QK, the online softmax and
-// PV of a tile need no exchange between waves.  The product runs transposed,
-// on v_mfma_f32_16x16x32_bf16:
+// A block holds 64 query rows (G tokens x Hs heads) and eight waves: wave w
+// owns rows 16 (w % 4) .. +15 and half of D (w / 4), so two waves share each
+// row group.  The products run transposed, on v_mfma_f32_16x16x32_bf16:
 //   S^T[e][r] = sum_d E[e][d] Q[r][d]: A = entry rows read from LDS, B = the
-//     wave's rotated query rows kept in VGPRs for the whole loop;
-//   O^T[d][r] += sum_e E^T[d][e] P^T[e][r]: B = the S^T accumulators
-//     themselves (exp'd, packed to bf16 -- a lane holds row r = lane % 16 and
-//     entries {4q..4q+3, 16+4q..16+4q+3}, q = lane / 16, which is a valid
-//     K order because the A side uses the same order), A = E^T read with
-//     ds_read_b64_tr_b16 (a 16-lane group's transposed 4 x 16 block).
-// A lane therefore keeps one row's running max (shared by its four lanes)
-// and a partial row sum.  The max used for the exponentials moves only when
-// a logit exceeds it by more than 2^8 (log2 domain), so the accumulators are
-// rescaled rarely; probabilities up to 2^8 are exact enough in bf16 and the
-// final division by the row sum (taken with the same max) is unchanged.  Tiles of 32 entries are gathered into VGPRs one
-// tile ahead (8 threads per row, uniform 16-byte loads, empty slots read a
-// zero row), written to one of two LDS buffers as bf16 rows (E4M3 widened by
-// the hardware converter), and one barrier per tile publishes them.
+//     wave's rotated query slices (its half of D) kept in VGPRs; the two
+//     halves' partial logits are summed through LDS, after which both waves
+//     of a row group run the same online softmax;
+//   O^T[d][r] += sum_e E^T[d][e] P^T[e][r] over the wave's half of D: B = the
+//     S^T accumulators themselves (exp'd, packed to bf16 -- a lane holds row
+//     r = lane % 16 and entries {4q..4q+3, 16+4q..16+4q+3}, q = lane / 16,
+//     which is a valid K order because the A side uses the same order),
+//     A = E^T read with ds_read_b64_tr_b16 (a 16-lane group's transposed
+//     4 x 16 block).
+// Splitting D halves each wave's query and output registers, so two waves
+// run per SIMD and hide each other's LDS and MFMA latency.  A lane keeps one
+// row's running max (shared by its four lanes) and a partial row sum.  The
+// max used for the exponentials moves only when a logit exceeds it by more
+// than 2^8 (log2 domain), so the accumulators are rescaled rarely;
+// probabilities up to 2^8 are exact enough in bf16 and the final division
+// by the row sum (taken with the same max) is unchanged.  Tiles of 32
+// entries are gathered into VGPRs one tile ahead (16 threads per row,
+// uniform 16-byte loads), written to one of two LDS buffers as bf16 rows
+// (E4M3 widened by the hardware converter; window rows rotated here in
+// decode), and a barrier publishes them.
 constexpr int kTile = 32;
 
 __device__ __forceinline__ void lds_barrier() {
@@ -329,24 +334,31 @@ __device__ __forceinline__ bf16x4 ds_read_tr(const uint8_t* p) {
 
 template <int D>
 struct Geo {
-  static constexpr int EROW = 2 * D + 16;   // LDS bytes per staged entry
-  static constexpr int KS = D / 32;         // QK k-steps
-  static constexpr int DT = D / 16;         // PV output tiles
-  static constexpr int NCH = D / 64;        // 16-byte chunks per staging thread, bf16 rows
-  static constexpr int NCHM = D / 128 + 1;  // same for mixed rows (at most D/16 + 8 chunks)
+  static constexpr int DS = D >= 256 ? 2 : 1;   // waves sharing a row group (D split)
+  static constexpr int NT = 256 * DS;            // threads per block
+  static constexpr int DW = D / DS;              // dims per wave
+  static constexpr int EROW = 2 * D + 16;        // LDS bytes per staged entry
+  static constexpr int KH = DW / 32;             // QK k-steps per wave
+  static constexpr int DH = DW / 16;             // PV output tiles per wave
+  static constexpr int TPR = 8 * DS;             // staging threads per entry row
+  static constexpr int NCH = D / 8 / TPR;        // 16-byte chunks per staging thread, bf16 rows
+  static constexpr int NCHM = (D / 16 + 8 + TPR - 1) / TPR;   // mixed rows (<= D/16 + 8 chunks)
 };
 
 template <int D, int KV>
-__global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
+__global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   using Gm = Geo<D>;
+  constexpr int DS = Gm::DS, NT = Gm::NT, TPR = Gm::TPR;
   __shared__ __align__(16) uint8_t Et[2][kTile * Gm::EROW];     // entry tiles, bf16 rows
   __shared__ __align__(16) int tags[2][kTile];
+  __shared__ __align__(16) float Sx[DS][4][64][8];             // partial logits [half][group][lane]
   __shared__ int32_t lidx[kIdxLds];
   __shared__ double freq[kMaxRopePairs];
   extern __shared__ float2 qang[];            // [G][r/2] (cos, sin) of t_g * freq_p
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = wave & 3, dh = DS == 2 ? wave >> 2 : 0;
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const Work w = make_work(a, blockIdx.y);
   const int split = blockIdx.x;
@@ -366,28 +378,29 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   const uint8_t* any_row = static_cast<const uint8_t*>(a.q);   // valid address for empty slots
   const int n_fp8 = KV == kMixed ? nope / 16 : 0;
   const int n_chunks = KV == kMixed ? n_fp8 + a.r / 8 : D / 8;
-  const int st_e = tid >> 3, st_part = tid & 7;
+  const int st_e = tid / TPR, st_part = tid % TPR;
   const int n_tiles = e_hi > e_lo ? (e_hi - e_lo + kTile - 1) / kTile : 0;
 
   // this lane's query row
-  const int row = wave * 16 + lr;
+  const int row = rg * 16 + lr;
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
   const bool live = g < w.n_q;
 
-  // query row slices into registers first (one round trip with the tile-0 gather)
-  bf16x8 qreg[Gm::KS];
+  // query slices of the wave's part of D into registers first
+  bf16x8 qreg[Gm::KH];
   {
     const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                       (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D + 8 * lq;
+                       (((int64_t)w.b * a.Tq + w.i0 + (live ? g : 0)) * a.H + h) * D +
+                       dh * Gm::DW + 8 * lq;
 #pragma unroll
-    for (int s = 0; s < Gm::KS; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+    for (int s = 0; s < Gm::KH; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
   }
 
   // CSA indices of this split to LDS (the plan keeps them within kIdxLds).
   const int n_idx = mode == 0 ? max(0, min(e_hi, n_comp) - e_lo) : 0;
   if (n_idx > 0) {
     const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * kk + e_lo;
-    for (int e = tid; e < n_idx; e += 256) lidx[e] = src[e];
+    for (int e = tid; e < n_idx; e += NT) lidx[e] = src[e];
   }
   rope_freq_table(freq, a.r, a.theta);
   __syncthreads();
@@ -419,7 +432,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     // used (an empty slot is staged as zeros).
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
-      const int ch = st_part + 8 * q;
+      const int ch = st_part + TPR * q;
       const uint8_t* src = (rs != nullptr && ch < n_chunks) ? rs + 16 * ch : any_row;
       stage[q] = ld_stream16(src);
     }
@@ -444,7 +457,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     const int64_t wpos = w.lo_w + (st_tag - kWinTag);
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
-      const int ch = st_part + 8 * q;
+      const int ch = st_part + TPR * q;
       if (ch >= n_chunks) continue;
       uint4 v = empty ? make_uint4(0u, 0u, 0u, 0u) : stage[q];
       if constexpr (KV == kMixed) {
@@ -467,7 +480,7 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   if (n_tiles > 0) load_tile(e_lo);
 
   // the block's query angles, then the lane's query slices rotated at t
-  for (int e = tid; e < G * npair; e += 256) {
+  for (int e = tid; e < G * npair; e += NT) {
     const int gg = e / npair, p = e - gg * npair;
     float cs, sn;
     rope_cos_sin((double)(w.t_first + gg), freq[p], &cs, &sn);
@@ -475,16 +488,15 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   }
   __syncthreads();
   const float2* ang = qang + (live ? g : 0) * npair;
-  auto angle = [&](int p) { return ang[p]; };
 #pragma unroll
-  for (int s = 0; s < Gm::KS; ++s) {
-    const int d0 = 32 * s + 8 * lq;
+  for (int s = 0; s < Gm::KH; ++s) {
+    const int d0 = dh * Gm::DW + 32 * s + 8 * lq;
     if (d0 >= nope) {
       uint32_t wd[4];
       __builtin_memcpy(wd, &qreg[s], 16);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float2 cv = angle((d0 - nope) / 2 + p);
+        const float2 cv = ang[(d0 - nope) / 2 + p];
         const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
         wd[p] = pack_bf16x2(x0 * cv.x - x1 * cv.y, x0 * cv.y + x1 * cv.x);
       }
@@ -492,12 +504,18 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     }
   }
 
+  // Every prologue load (query slices, first tile) completes here, so that
+  // inside the tile loop only the prefetch of the next tile is outstanding
+  // and no wait for it is placed before the compute of the current tile.
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   const Vis myvis = make_vis(a, w, g);
   const float scale_log2 = a.scale_log2;
   float m_run = -INFINITY, l_part = 0.f;
-  f32x4 oacc[Gm::DT];
+  f32x4 oacc[Gm::DH];
 #pragma unroll
-  for (int dt = 0; dt < Gm::DT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < Gm::DH; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float* sx_mine = &Sx[dh][rg][l][0];
+  const float* sx_other = &Sx[DS - 1 - dh][rg][l][0];
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
@@ -506,26 +524,53 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     if (t + 1 < n_tiles) load_tile(e_lo + (t + 1) * kTile);
     const uint8_t* E = Et[buf];
 
-    // ---- S^T for entries 0-15 (s0) and 16-31 (s1) of the tile
+    // ---- partial S^T over this wave's half of D, entries 0-15 (s0) and
+    // 16-31 (s1); the entry fragments are read one group of k-steps ahead.
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
     {
-      const uint8_t* eb = E + lr * Gm::EROW + 16 * lq;
+      constexpr int QG = Gm::KH >= 4 ? 4 : Gm::KH;
+      const uint8_t* eb = E + lr * Gm::EROW + 16 * lq + 2 * dh * Gm::DW;
+      bf16x8 fa[2][QG], fb[2][QG];
 #pragma unroll
-      for (int s = 0; s < Gm::KS; ++s) {
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(eb + 64 * s);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * s);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[s], s1, 0, 0, 0);
+      for (int u = 0; u < QG; ++u) {
+        fa[0][u] = *reinterpret_cast<const bf16x8*>(eb + 64 * u);
+        fb[0][u] = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * u);
+      }
+#pragma unroll
+      for (int gi = 0; gi < Gm::KH / QG; ++gi) {
+        const int cur = gi & 1;
+        if (gi + 1 < Gm::KH / QG) {
+#pragma unroll
+          for (int u = 0; u < QG; ++u) {
+            const int st = (gi + 1) * QG + u;
+            fa[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(eb + 64 * st);
+            fb[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * st);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < QG; ++u) {
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][u], qreg[gi * QG + u], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[cur][u], qreg[gi * QG + u], s1, 0, 0, 0);
+        }
       }
     }
-
-    // ---- online softmax of row `row` over the lane's 8 entries
+    // ---- sum the two halves' partial logits (D split over two waves)
     const int4 tg0 = *reinterpret_cast<const int4*>(&tags[buf][4 * lq]);
     const int4 tg1 = *reinterpret_cast<const int4*>(&tags[buf][16 + 4 * lq]);
+    float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+    if constexpr (DS == 2) {
+      *reinterpret_cast<float4*>(sx_mine) = make_float4(s0[0], s0[1], s0[2], s0[3]);
+      *reinterpret_cast<float4*>(sx_mine + 4) = make_float4(s1[0], s1[1], s1[2], s1[3]);
+      lds_barrier();
+      o0 = *reinterpret_cast<const float4*>(sx_other);
+      o1 = *reinterpret_cast<const float4*>(sx_other + 4);
+    }
+
+    // ---- online softmax of row `row` over the lane's 8 entries (the same in
+    // both waves of the row group)
     const int tg[8] = {tg0.x, tg0.y, tg0.z, tg0.w, tg1.x, tg1.y, tg1.z, tg1.w};
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { x[i] = s0[i]; x[4 + i] = s1[i]; }
+    float x[8] = {s0[0] + o0.x, s0[1] + o0.y, s0[2] + o0.z, s0[3] + o0.w,
+                  s1[0] + o1.x, s1[1] + o1.y, s1[2] + o1.z, s1[3] + o1.w};
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -553,20 +598,38 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
     __builtin_memcpy(&pb, pk, 16);
     if (__ballot(rescale)) {
 #pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt)
+      for (int dt = 0; dt < Gm::DH; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) oacc[dt][i] *= al;
     }
 
-    // ---- O^T += E^T P^T, 16 output dims per MFMA
+    // ---- O^T += E^T P^T over the wave's half of D, 16 output dims per MFMA;
+    // the transposed entry fragments are read PG output tiles ahead.
     {
-      const uint8_t* tb = E + (4 * lq + (lr >> 2)) * Gm::EROW + 8 * (lr & 3);
+      constexpr int PG = Gm::DH >= 8 ? 8 : Gm::DH;
+      const uint8_t* tb = E + (4 * lq + (lr >> 2)) * Gm::EROW + 8 * (lr & 3) + 2 * dh * Gm::DW;
+      bf16x4 lo[2][PG], hi[2][PG];
 #pragma unroll
-      for (int dt = 0; dt < Gm::DT; ++dt) {
-        const bf16x4 lo = ds_read_tr(tb + 32 * dt);
-        const bf16x4 hi = ds_read_tr(tb + 16 * Gm::EROW + 32 * dt);
-        const bf16x8 ab = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, pb, oacc[dt], 0, 0, 0);
+      for (int u = 0; u < PG; ++u) {
+        lo[0][u] = ds_read_tr(tb + 32 * u);
+        hi[0][u] = ds_read_tr(tb + 16 * Gm::EROW + 32 * u);
+      }
+#pragma unroll
+      for (int gi = 0; gi < Gm::DH / PG; ++gi) {
+        const int cur = gi & 1;
+        if (gi + 1 < Gm::DH / PG) {
+#pragma unroll
+          for (int u = 0; u < PG; ++u) {
+            const int dt = (gi + 1) * PG + u;
+            lo[cur ^ 1][u] = ds_read_tr(tb + 32 * dt);
+            hi[cur ^ 1][u] = ds_read_tr(tb + 16 * Gm::EROW + 32 * dt);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < PG; ++u) {
+          const bf16x8 ab = __builtin_shufflevector(lo[cur][u], hi[cur][u], 0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[gi * PG + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, pb, oacc[gi * PG + u], 0, 0, 0);
+        }
       }
     }
   }
@@ -577,13 +640,18 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   l_row += __shfl_xor(l_row, 32);
 
   if (a.nsplit > 1) {
+    // partial output normalised by its own row sum, in fp16 (|o| <= max |v|)
     const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
-    float* po = a.part_o + (slot * 64 + row) * D + 4 * lq;
+    _Float16* po = a.part_o + (slot * 64 + row) * D + dh * Gm::DW + 4 * lq;
+    const float rl = l_row > 0.f ? 1.f / l_row : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < Gm::DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt) =
-          make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]);
-    if (lq == 0) {
+    for (int dt = 0; dt < Gm::DH; ++dt) {
+      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+      const f16x4 hv = {(_Float16)(oacc[dt][0] * rl), (_Float16)(oacc[dt][1] * rl),
+                        (_Float16)(oacc[dt][2] * rl), (_Float16)(oacc[dt][3] * rl)};
+      *reinterpret_cast<f16x4*>(po + 16 * dt) = hv;
+    }
+    if (lq == 0 && dh == 0) {
       a.part_ml[(slot * 64 + row) * 2] = m_run;
       a.part_ml[(slot * 64 + row) * 2 + 1] = l_row;
     }
@@ -595,17 +663,18 @@ __global__ void __launch_bounds__(256) attend_mfma_kernel(KArgs a) {
   float den = l_row;
   if (a.sink) den += exp2f(a.sink[h] * 1.4426950408889634f - (m_run == -INFINITY ? 0.f : m_run));
   const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * D + 4 * lq;
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * D +
+                 dh * Gm::DW + 4 * lq;
 #pragma unroll
-  for (int dt = 0; dt < Gm::DT; ++dt) {
-    const int d0 = 16 * dt + 4 * lq;
+  for (int dt = 0; dt < Gm::DH; ++dt) {
+    const int d0 = dh * Gm::DW + 16 * dt + 4 * lq;
     float o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = oacc[dt][i] * inv;
     if (d0 >= nope) {             // rotation at -t: (cos, -sin) of the query's angle
 #pragma unroll
       for (int p = 0; p < 2; ++p) {
-        const float2 cv = angle((d0 - nope) / 2 + p);
+        const float2 cv = ang[(d0 - nope) / 2 + p];
         const float x0 = o[2 * p], x1 = o[2 * p + 1];
         o[2 * p] = x0 * cv.x + x1 * cv.y;
         o[2 * p + 1] = -x0 * cv.y + x1 * cv.x;
@@ -637,9 +706,9 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
     for (int s = threadIdx.x; s < a.nsplit; s += 64) {
       const float ms = a.part_ml[((slot0 + s) * 64 + row) * 2];
       const float ls = a.part_ml[((slot0 + s) * 64 + row) * 2 + 1];
-      const float f = exp2f(ms - Mu);
+      const float f = exp2f(ms - Mu) * ls;
       wgt[s] = f;
-      L += ls * f;
+      L += f;
     }
     for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
     if (threadIdx.x == 0) {
@@ -654,13 +723,14 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * a.D;
   for (int c = 2 * threadIdx.x; c < a.D; c += 2 * blockDim.x) {
     float o0 = 0.f, o1 = 0.f;
-    const float* pp = a.part_o + (slot0 * 64 + row) * a.D + c;
+    const _Float16* pp = a.part_o + (slot0 * 64 + row) * a.D + c;
     const int64_t stride = 64LL * a.D;
 #pragma unroll 8
     for (int s = 0; s < a.nsplit; ++s) {
-      const float2 x = *reinterpret_cast<const float2*>(pp + s * stride);
-      o0 = fmaf(wgt[s], x.x, o0);
-      o1 = fmaf(wgt[s], x.y, o1);
+      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+      const f16x2 x = *reinterpret_cast<const f16x2*>(pp + s * stride);
+      o0 = fmaf(wgt[s], (float)x[0], o0);
+      o1 = fmaf(wgt[s], (float)x[1], o1);
     }
     o0 *= inv;
     o1 *= inv;
@@ -786,7 +856,7 @@ hipError_t launch_mfma(const KArgs& k, const AttnPlan& p, hipStream_t st) {
   const size_t lds = (size_t)p.G * (k.r / 2) * sizeof(float2);   // the block's query angles
   {
     TimedLaunch tl(kKernelAttend, st);
-    hipLaunchKernelGGL((attend_mfma_kernel<D, KV>), dim3(p.nsplit, p.n_work), dim3(256), lds, st, k);
+    hipLaunchKernelGGL((attend_mfma_kernel<D, KV>), dim3(p.nsplit, p.n_work), dim3(Geo<D>::NT), lds, st, k);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
@@ -830,7 +900,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
   k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
   k.ang = reinterpret_cast<const float2*>(w8 + p.off_ang);
-  k.part_o = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_po) : nullptr;
+  k.part_o = p.nsplit > 1 ? reinterpret_cast<_Float16*>(w8 + p.off_po) : nullptr;
   k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
   k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;
   k.H = a.H; k.D = a.D; k.r = a.r; k.theta = a.theta;
