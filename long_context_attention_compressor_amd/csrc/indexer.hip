@@ -734,6 +734,123 @@ Plan make_plan(int B, int Tq, int N, int k) {
   return p;
 }
 
+// Prefill score kernel.  A block of eight waves holds 8 * QPW consecutive
+// queries of one sequence (QPW per wave, fragments in VGPRs) and sweeps all
+// keys the block can see, one 32-key tile at a time: the 512 threads load a
+// tile cooperatively (one 16-byte load each, XOR-swizzled into LDS, two
+// tiles ahead in registers) and every wave reads it from LDS, so each key
+// tile crosses HBM once per 8 * QPW queries and all waves of a compute unit
+// share it.
+template <int HT, int KS, int QPW>
+__global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
+  constexpr int QB = 8 * QPW;                // queries per block
+  constexpr int dI = KS * 16;
+  constexpr int HI = HT * 32;
+  constexpr int CH = dI / 8;                 // 16-byte chunks per key row
+  constexpr int ROWB = dI * 2;               // bytes per key row
+  constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
+  constexpr int LOADERS = TILEB / 16;        // threads that load one chunk each
+  __shared__ float sw[QB][HI];
+  __shared__ __align__(16) uint8_t ktile[2][TILEB];
+  const int wave = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int hf = l >> 5, ln = l & 31;
+  const int blocks_per_seq = (a.Tq + QB - 1) / QB;
+  const int b = blockIdx.x / blocks_per_seq;
+  const int i0 = (blockIdx.x - b * blocks_per_seq) * QB;
+  const int n_rows_blk = min(QB, a.Tq - i0);
+  const int64_t t_last = (int64_t)a.qpos.v[b] + i0 + n_rows_blk - 1;
+  const int64_t nv_max = n_visible(t_last, a.N, a.m);
+  const int64_t n_tiles = (nv_max + 31) / 32;
+
+  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
+  // Loader thread t takes 16 bytes at t*16 of the tile in LDS order: row kk,
+  // swizzled slot cs, which holds the row's chunk cs ^ (kk % CH).
+  const bool loader = (int)threadIdx.x < LOADERS;
+  const int lo_off = threadIdx.x * 16;
+  const int lo_kk = lo_off / ROWB, lo_cs = (lo_off % ROWB) / 16;
+  auto load_tile = [&](int64_t tile) {
+    int64_t j = tile * 32 + lo_kk;
+    if (j > a.N - 1) j = a.N - 1;
+    return ld_stream16(Kb + j * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16));
+  };
+  uint4 stage[2];
+  if (loader) {
+    if (n_tiles > 0) stage[0] = load_tile(0);
+    if (n_tiles > 1) stage[1] = load_tile(1);
+  }
+
+  // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
+  // Scores are written through a buffer resource per query row: a masked
+  // lane (hidden key, second half-wave, row past Tq) stores out of range and
+  // the store is dropped, so every store instruction is issued unconditionally
+  // and the memory counter stays exact for the prefetch waits.
+  bf16x8 qf[QPW][HT][KS];
+  int64_t nv_row[QPW];
+  __amdgpu_buffer_rsrc_t srow[QPW];
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) {
+    const int rr = wave * QPW + qi;
+    const int i = min(i0 + rr, a.Tq - 1);
+    nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
+    srow[qi] = __builtin_amdgcn_make_buffer_rsrc(a.scores + ((int64_t)b * a.Tq + i) * a.Np, 0,
+                                                 (int)(nv_row[qi] * 4), 0x00020000);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                         ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+    }
+  }
+  for (int e = threadIdx.x; e < QB * HI; e += 512) {
+    const int rr = e / HI, h = e - rr * HI;
+    const int i = min(i0 + rr, a.Tq - 1);
+    sw[rr][h] = a.w[((int64_t)b * a.Tq + i) * HI + h];
+  }
+
+  // One step per tile; the loop is unrolled by two so that the staging
+  // registers and LDS buffers are indexed statically (a runtime index would
+  // force the prefetch to complete when it is issued).
+  auto step = [&](int64_t tile, uint4& st, uint8_t* kt) {
+    if (loader) {
+      *reinterpret_cast<uint4*>(kt + lo_off) = st;
+      if (tile + 2 < n_tiles) st = load_tile(tile + 2);
+    }
+    __syncthreads();             // tile visible; every wave is done with tile - 1
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = hf * (CH / 2) + s;
+      kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+    }
+    const int64_t j = tile * 32 + ln;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      const int rr = wave * QPW + qi;
+      float part = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], fmaxf(acc[v], 0.f), part);
+      }
+      part += __shfl_xor(part, 32);
+      const int off = hf == 0 ? (int)j * 4 : 0x7fffffff;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[qi], off, 0, 0);
+    }
+  };
+  for (int64_t tile = 0; tile < n_tiles; tile += 2) {
+    step(tile, stage[0], ktile[0]);
+    if (tile + 1 < n_tiles) step(tile + 1, stage[1], ktile[1]);
+  }
+}
+
 template <int HT, int KS, int QPW, int RW>
 hipError_t launch_score(const ScoreArgs& sa, int64_t key_chunks, int row_groups, hipStream_t st) {
   hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW>), dim3((unsigned)key_chunks, row_groups),
@@ -794,14 +911,16 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
       const int64_t n_tiles = (nv_max + 31) / 32;
       const int HT = a.HI / 32, KS = a.dI / 16;
       if (a.Tq >= 8 && !p.split) {
-        // Prefill: 4 waves x 2 queries share each key sweep.
-        sa.tiles_per_wave = 64;
-        const int64_t chunks = (n_tiles + sa.tiles_per_wave - 1) / sa.tiles_per_wave;
-        const int groups = a.B * ((a.Tq + 7) / 8);
-#define LAC_SCORE_CASE(ht, ks) \
-  if (HT == ht && KS == ks) err = launch_score<ht, ks, 2, 4>(sa, chunks, groups, st);
-        LAC_SCORE_CASE(1, 4) LAC_SCORE_CASE(1, 8) LAC_SCORE_CASE(2, 4) LAC_SCORE_CASE(2, 8)
-        LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
+        // Prefill: a block of eight waves shares each key tile among 8 * QPW
+        // queries and sweeps all the keys they see.
+#define LAC_SCORE_CASE(ht, ks, qpw)                                                        \
+  if (HT == ht && KS == ks) {                                                              \
+    const int blocks = a.B * ((a.Tq + 8 * qpw - 1) / (8 * qpw));                           \
+    hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw>), dim3(blocks), dim3(512), 0, st, sa); \
+    err = hipGetLastError();                                                               \
+  }
+        LAC_SCORE_CASE(1, 4, 2) LAC_SCORE_CASE(1, 8, 2) LAC_SCORE_CASE(2, 4, 2)
+        LAC_SCORE_CASE(2, 8, 2) LAC_SCORE_CASE(4, 4, 2) LAC_SCORE_CASE(4, 8, 1)
 #undef LAC_SCORE_CASE
       } else {
         // Decode: one query per block, 4 waves split the keys.  The grid is
