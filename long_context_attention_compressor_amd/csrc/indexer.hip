@@ -64,15 +64,19 @@ struct ScoreArgs {
   Positions qpos;
 };
 
-// Wave-aggregated LDS histogram add: lanes with equal digits add once.
+// LDS histogram add for the wave's active lanes: one atomic when every
+// active lane holds the same digit (common in the high radix digits), else
+// one atomic per lane (cheaper than serialising over many distinct digits).
 __device__ __forceinline__ void hist_add(uint32_t* hist, bool on, uint32_t d) {
-  uint64_t active = __ballot(on);
-  while (active) {
-    const int leader = __ffsll((unsigned long long)active) - 1;
-    const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
-    const uint64_t same = __ballot(on && d == dl) & active;
+  const uint64_t active = __ballot(on);
+  if (!active) return;
+  const int leader = __ffsll((unsigned long long)active) - 1;
+  const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+  const uint64_t same = __ballot(on && d == dl);
+  if (same == active) {
     if (lane_id() == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
-    active &= ~same;
+  } else if (on) {
+    atomicAdd(&hist[d], 1u);
   }
 }
 
@@ -398,6 +402,192 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rowwise_kernel(TopkArgs a) 
   }
   for (int e = keff + threadIdx.x; e < a.k; e += blockDim.x) {
     a.idx[(int64_t)row * a.k + e] = -1;
+    if (a.score_out) a.score_out[(int64_t)row * a.k + e] = -INFINITY;
+  }
+}
+
+// Row-wise selection with the row's 16-bit key prefixes kept in LDS (rows of
+// up to kPrefixMax entries): one pass over the scores in HBM writes the
+// prefixes and a histogram of the top 12 key bits; the next 4 bits are
+// histogrammed from LDS, which fixes the 16-bit threshold prefix P.  Keys
+// above P are selected; the few keys that carry P are ranked by (full key
+// desc, index asc) after their full keys are read back (a radix select over
+// the row handles the rare case of more than kPrefCand of them).  Their
+// prefixes are then rewritten to 0xFFFF (chosen) or 0 (not), so "prefix > P
+// or prefix == 0xFFFF" is the selection, emitted in ascending index order by
+// one block-wide scan over per-thread runs of the row.
+constexpr int kPrefixMax = 67584;
+constexpr int kPrefCand = 1024;
+
+__global__ void __launch_bounds__(1024) topk_prefix_kernel(TopkArgs a) {
+  extern __shared__ __align__(16) uint16_t pre[];                // [round_up(nv, 4)]
+  __shared__ uint32_t hist[kHistBins];
+  __shared__ int32_t cidx[kPrefCand];
+  __shared__ uint32_t ckey[kPrefCand];
+  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t bc[4];
+  __shared__ uint32_t t_d, t_above, n_cand;
+  const int row = blockIdx.x;
+  const int nv = (int)row_nvis(a, row);
+  const int keff = min(a.k, nv);
+  if (keff == nv) { write_all_visible(a, row, nv); return; }
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
+  const float* s = a.scores + (int64_t)row * a.Np;
+
+  // ---- pass 1: scores -> 16-bit prefixes in LDS, histogram of key bits 31..20
+  constexpr int kU = (kPrefixMax + 4095) / 4096;           // float4 loads per thread
+  float4 v4[kU];
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int e = 4 * (tid + 1024 * u);
+    v4[u] = e < nv ? *reinterpret_cast<const float4*>(s + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int e = tid; e < kHistBins; e += 1024) hist[e] = 0u;
+  if (tid == 0) n_cand = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kU; ++u) {
+    const int e = 4 * (tid + 1024 * u);
+    const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
+    uint32_t key[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) key[c] = score_key(vv[c]);
+    if (e < nv)
+      *reinterpret_cast<uint2*>(pre + e) = make_uint2((key[0] >> 16) | (key[1] & 0xffff0000u),
+                                                      (key[2] >> 16) | (key[3] & 0xffff0000u));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) hist_add(hist, e + c < nv, key[c] >> 20);
+  }
+  __syncthreads();
+
+  // ---- threshold bucket of the top 12 bits: thread t covers bins 4095-4t .. 4092-4t
+  auto find_bucket = [&](uint32_t need) {
+    uint32_t c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { c[q] = hist[kHistBins - 1 - 4 * tid - q]; sum += c[q]; }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o);
+      if (l >= o) incl += x;
+    }
+    if (l == 63) wsum[wv] = incl;
+    __syncthreads();
+    for (int w = 0; w < wv; ++w) incl += wsum[w];
+    const uint32_t excl = incl - sum;
+    if (excl < need && incl >= need) {
+      uint32_t cum = excl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cum + c[q] >= need) { t_d = kHistBins - 1 - 4 * tid - q; t_above = cum; break; }
+        cum += c[q];
+      }
+    }
+    __syncthreads();
+  };
+  find_bucket((uint32_t)keff);
+  const uint32_t d1 = t_d, above1 = t_above;
+  __syncthreads();
+
+  // ---- pass 2 (LDS): key bits 19..16 of the bucket's keys
+  if (tid < 16) hist[tid] = 0u;
+  __syncthreads();
+  for (int e0 = 0; e0 < nv; e0 += 1024) {
+    const int e = e0 + tid;
+    const uint32_t pv = e < nv ? pre[e] : 0u;
+    hist_add(hist, e < nv && (pv >> 4) == d1, pv & 15u);
+  }
+  __syncthreads();
+  if (tid < 64) {
+    // 16 bins, descending: lane q covers bin 15 - q
+    const uint32_t need = (uint32_t)keff - above1;
+    const uint32_t cnt = l < 16 ? hist[15 - l] : 0u;
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o);
+      if (l >= o) incl += x;
+    }
+    if (l < 16 && incl - cnt < need && incl >= need) { t_d = (d1 << 4) | (15 - l); t_above = above1 + incl - cnt; }
+  }
+  __syncthreads();
+  const uint32_t P = t_d;
+  const uint32_t need_p = (uint32_t)keff - t_above;       // >= 1 keys carrying P
+
+  // ---- pass 3: the keys carrying P, with their full keys
+  for (int e0 = 0; e0 < nv; e0 += 1024) {
+    const int e = e0 + tid;
+    if (e < nv && pre[e] == P) {
+      const uint32_t pos = atomicAdd(&n_cand, 1u);
+      if (pos < (uint32_t)kPrefCand) { cidx[pos] = e; ckey[pos] = score_key(s[e]); }
+    }
+  }
+  __syncthreads();
+  const int nc = (int)n_cand;
+  if (nc <= kPrefCand) {
+    // by rank among the candidates
+    uint32_t chosen = 0;
+    int me = -1;
+    if (tid < nc) {
+      me = cidx[tid];
+      const uint32_t mk = ckey[tid];
+      uint32_t rank = 0;
+      for (int j = 0; j < nc; ++j) {
+        const uint32_t ok = ckey[j];
+        rank += (ok > mk) || (ok == mk && cidx[j] < me);
+      }
+      chosen = rank < need_p;
+    }
+    __syncthreads();
+    if (me >= 0) pre[me] = chosen ? (uint16_t)0xFFFF : (uint16_t)0;
+  } else {
+    // many keys share P: radix select over the row's keys carrying P
+    uint32_t thr, need_eq, cnt_eq, thr2 = 0;
+    radix_select(nv, need_p,
+                 [&](int e, uint32_t* u) { *u = score_key(s[e]); return (*u >> 16) == P; }, hist,
+                 bc, thr, need_eq, cnt_eq);
+    if (cnt_eq > need_eq) {
+      uint32_t ne2, ce2;
+      radix_select(nv, need_eq,
+                   [&](int e, uint32_t* u) { *u = ~(uint32_t)e; return score_key(s[e]) == thr; },
+                   hist, bc, thr2, ne2, ce2);
+    }
+    __syncthreads();
+    for (int e = tid; e < nv; e += 1024) {
+      if (pre[e] != P) continue;
+      const uint32_t u = score_key(s[e]);
+      pre[e] = (u > thr || (u == thr && ~(uint32_t)e >= thr2)) ? (uint16_t)0xFFFF : (uint16_t)0;
+    }
+  }
+  __syncthreads();
+
+  // ---- emit in ascending index order: thread t owns a run of the row
+  const int per = (nv + 1023) / 1024;
+  const int r0 = min(nv, tid * per), r1 = min(nv, r0 + per);
+  auto sel = [&](int e) { const uint32_t pv = pre[e]; return pv > P || pv == 0xFFFFu; };
+  uint32_t mine = 0;
+  for (int e = r0; e < r1; ++e) mine += sel(e);
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t x = __shfl_up(incl, o);
+    if (l >= o) incl += x;
+  }
+  if (l == 63) wsum[wv] = incl;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) incl += wsum[w];
+  uint32_t pos = incl - mine;
+  int32_t* out = a.idx + (int64_t)row * a.k;
+  for (int e = r0; e < r1; ++e) {
+    if (!sel(e)) continue;
+    if (pos < (uint32_t)keff) {
+      out[pos] = e;
+      if (a.score_out) a.score_out[(int64_t)row * a.k + pos] = s[e];
+    }
+    ++pos;
+  }
+  for (int e = keff + tid; e < a.k; e += 1024) {
+    out[e] = -1;
     if (a.score_out) a.score_out[(int64_t)row * a.k + e] = -INFINITY;
   }
 }
@@ -943,7 +1133,16 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
 
   if (!p.split) {
     TimedLaunch tl(kKernelTopk, st);
-    hipLaunchKernelGGL(topk_rowwise_kernel, dim3(R), dim3(kTopkThreads), 0, st, ta);
+    if (nv_max <= kPrefixMax) {
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&topk_prefix_kernel),
+          hipFuncAttributeMaxDynamicSharedMemorySize, kPrefixMax * 2);
+      if (attr != hipSuccess) return attr;
+      const size_t lds = (size_t)((nv_max + 3) / 4 * 4) * 2;
+      hipLaunchKernelGGL(topk_prefix_kernel, dim3(R), dim3(1024), lds, st, ta);
+    } else {
+      hipLaunchKernelGGL(topk_rowwise_kernel, dim3(R), dim3(kTopkThreads), 0, st, ta);
+    }
     return hipGetLastError();
   }
   {
