@@ -78,9 +78,9 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.n_work = B * p.n_qgroups * p.n_htiles;
   p.max_entries = p.G * n_entries + (W > 0 ? W + p.G - 1 : 0);
   if (p.max_entries < 1) p.max_entries = 1;
-  // One 152-KB block fits a compute unit, so the grid is sized to one wave of
-  // blocks over the 256 compute units; a split holds at least 4 tiles.
-  const int max_split = (int)((p.max_entries + 127) / 128);
+  // One block fills a compute unit's LDS, so the grid is sized to one wave of
+  // blocks over the 256 compute units; a split holds at least 2 tiles.
+  const int max_split = (int)((p.max_entries + 63) / 64);
   int ns = p.n_work >= kGridTarget ? 1 : kGridTarget / p.n_work;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
