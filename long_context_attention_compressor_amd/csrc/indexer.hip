@@ -141,6 +141,18 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   const int64_t t_last = (int64_t)a.qpos.v[b] + i0 + n_rows_blk - 1;
   const int64_t nv_max = n_visible(t_last, a.N, a.m);
 
+  // The head weights are requested first: loads complete in order, so the
+  // LDS store of w below does not wait for the key tiles requested after it.
+  constexpr int kWPer = (kRowsPerBlock * HI + 255) / 256;
+  float wreg[kWPer];
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int rr = e / HI, h = e - rr * HI;
+    const int i = min(i0 + rr, a.Tq - 1);
+    wreg[u] = e < kRowsPerBlock * HI ? a.w[((int64_t)b * a.Tq + i) * HI + h] : 0.f;
+  }
+
   // Wave gw of the row's nw key waves takes tiles gw, gw + nw, gw + 2nw, ...:
   // at any moment the waves of a row stream one contiguous stretch of keys,
   // which spreads their loads over all memory channels.
@@ -196,10 +208,10 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     }
   }
 
-  for (int e = threadIdx.x; e < kRowsPerBlock * HI; e += 256) {
-    const int rr = e / HI, h = e - rr * HI;
-    const int i = min(i0 + rr, a.Tq - 1);
-    sw[rr][h] = a.w[((int64_t)b * a.Tq + i) * HI + h];
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    if (e < kRowsPerBlock * HI) sw[e / HI][e % HI] = wreg[u];
   }
   if (do_hist)
     for (int e = threadIdx.x; e < kHistBins; e += 256) lhist[e] = 0u;
@@ -953,6 +965,17 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   const int64_t nv_max = n_visible(t_last, a.N, a.m);
   const int64_t n_tiles = (nv_max + 31) / 32;
 
+  // Head weights first (loads complete in order; see the decode kernel).
+  constexpr int kWPer = (QB * HI + 511) / 512;
+  float wreg[kWPer];
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 512 * u;
+    const int rr = e / HI, h = e - rr * HI;
+    const int i = min(i0 + rr, a.Tq - 1);
+    wreg[u] = e < QB * HI ? a.w[((int64_t)b * a.Tq + i) * HI + h] : 0.f;
+  }
+
   const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
   // Loader thread t takes 16 bytes at t*16 of the tile in LDS order: row kk,
   // swizzled slot cs, which holds the row's chunk cs ^ (kk % CH).
@@ -993,10 +1016,10 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
       for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
     }
   }
-  for (int e = threadIdx.x; e < QB * HI; e += 512) {
-    const int rr = e / HI, h = e - rr * HI;
-    const int i = min(i0 + rr, a.Tq - 1);
-    sw[rr][h] = a.w[((int64_t)b * a.Tq + i) * HI + h];
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 512 * u;
+    if (e < QB * HI) sw[e / HI][e % HI] = wreg[u];
   }
 
   // One step per tile; the loop is unrolled by two so that the staging
