@@ -81,12 +81,12 @@ class PairDecode:
     def step(self, i, timer=None):
         lac, c, s = self.lac, self.c, self.sets[i % len(self.sets)]
         N, Nh, m, mh, ctx = c["N"], c["Nh"], c["m"], c["m_hca"], self.ctx
+        # the CSA layer: compress its newest block (KV entry and indexer key),
+        # select, attend
         lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
                          rope_dims=c["r"], pos0=ctx - m)
         lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m, rope_dims=0,
                          pos0=ctx - m)
-        lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh), m=mh,
-                         rope_dims=c["r"], pos0=ctx - mh)
         if timer is not None:
             lac.time_next_launch("indexer_score", *timer)
         lac.indexer_topk(s["qI"], s["w"], s["KI"], m=m, k=c["k"], q_pos0=ctx, topk_idx=self.idx,
@@ -94,6 +94,9 @@ class PairDecode:
         lac.csa_attend(s["q_csa"], s["ckv"], self.idx, s["raw_csa"], c["W"], q_pos0=ctx,
                        raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_csa,
                        workspace=self.ws_csa)
+        # the HCA layer: compress its newest block, then attend
+        lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh), m=mh,
+                         rope_dims=c["r"], pos0=ctx - mh)
         lac.hca_attend(s["q_hca"], s["hkv"], s["raw_hca"], c["W"], m=mh, q_pos0=ctx,
                        raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_hca,
                        workspace=self.ws_hca)
