@@ -158,6 +158,9 @@ int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32
   a.B = c.B; a.Tq = c.Tq; a.H = c.H; a.D = c.D; a.r = c.r; a.theta = c.theta;
   a.scale = c.scale == 0.f ? 1.0f / sqrtf((float)c.D) : c.scale;
   a.n_entries = n_entries;
+  if (lac::attend_split_count(a) > lac::kMaxSplit)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: %s too long for one launch (it would take more than %d key splits)",
+                fn, mode == 0 ? "the selection" : "the compressed cache", lac::kMaxSplit);
   return launch_status(fn, lac::launch_attend(a, c.ws, static_cast<hipStream_t>(c.stream)));
 }
 

@@ -54,8 +54,10 @@ struct AttnPlan {
   size_t off_zero, off_win, off_ang, off_po, off_pml, total;
 };
 
+// shared_entries: the G queries of a work item see one common run of compressed
+// entries (HCA's causal prefix) rather than G separate selections (CSA).
 AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries, int W,
-                   bool f32_path) {
+                   bool f32_path, bool shared_entries) {
   AttnPlan p{};
   p.row_bytes = kv_row_bytes(kv_fmt, D, r);
   p.win_rows = W > 0 ? (int64_t)Tq + W - 1 : 0;
@@ -76,7 +78,7 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.n_htiles = H >= 64 ? H / 64 : 1;
   p.n_qgroups = (Tq + p.G - 1) / p.G;
   p.n_work = B * p.n_qgroups * p.n_htiles;
-  p.max_entries = p.G * n_entries + (W > 0 ? W + p.G - 1 : 0);
+  p.max_entries = (shared_entries ? n_entries : p.G * n_entries) + (W > 0 ? W + p.G - 1 : 0);
   if (p.max_entries < 1) p.max_entries = 1;
   // One block fills a compute unit's LDS, so the grid is sized to one wave of
   // blocks over the 256 compute units; a split holds at least 2 tiles.
@@ -639,79 +641,129 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   l_row += __shfl_xor(l_row, 16);
   l_row += __shfl_xor(l_row, 32);
 
-  if (a.nsplit > 1) {
-    // partial output normalised by its own row sum, in fp16 (|o| <= max |v|)
-    const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
-    _Float16* po = a.part_o + (slot * 64 + row) * D + dh * Gm::DW + 4 * lq;
-    const float rl = l_row > 0.f ? 1.f / l_row : 0.f;
+  // ---- output.  With several splits: the partial output normalised by its
+  // own row sum, in fp16 (|o| <= max |v|), plus (max, sum); with one: the
+  // output normalised (sink included), rotated back at -t, in bf16.  The
+  // block's 64 rows are staged in the tile buffers (free once every wave is
+  // done with the last tile) so that the global stores are whole rows.
+  const bool split_out = a.nsplit > 1;
+  float sc;
+  if (split_out) {
+    sc = l_row > 0.f ? 1.f / l_row : 0.f;
+  } else {
+    float den = l_row;
+    if (a.sink) den += exp2f(a.sink[h] * 1.4426950408889634f - (m_run == -INFINITY ? 0.f : m_run));
+    sc = den > 0.f ? 1.f / den : 0.f;
+  }
+  uint8_t* ob = &Et[0][0];                     // [64][EROW] bytes
+  __syncthreads();
+  {
+    uint8_t* orow = ob + row * Gm::EROW + 2 * (dh * Gm::DW + 4 * lq);
 #pragma unroll
     for (int dt = 0; dt < Gm::DH; ++dt) {
-      typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-      const f16x4 hv = {(_Float16)(oacc[dt][0] * rl), (_Float16)(oacc[dt][1] * rl),
-                        (_Float16)(oacc[dt][2] * rl), (_Float16)(oacc[dt][3] * rl)};
-      *reinterpret_cast<f16x4*>(po + 16 * dt) = hv;
-    }
-    if (lq == 0 && dh == 0) {
-      a.part_ml[(slot * 64 + row) * 2] = m_run;
-      a.part_ml[(slot * 64 + row) * 2 + 1] = l_row;
-    }
-    return;
-  }
-
-  // ---- single split: normalise, rotate back at -t, store bf16
-  if (!live) return;
-  float den = l_row;
-  if (a.sink) den += exp2f(a.sink[h] * 1.4426950408889634f - (m_run == -INFINITY ? 0.f : m_run));
-  const float inv = den > 0.f ? 1.f / den : 0.f;
-  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * D +
-                 dh * Gm::DW + 4 * lq;
+      const int d0 = dh * Gm::DW + 16 * dt + 4 * lq;
+      float o[4];
 #pragma unroll
-  for (int dt = 0; dt < Gm::DH; ++dt) {
-    const int d0 = dh * Gm::DW + 16 * dt + 4 * lq;
-    float o[4];
+      for (int i = 0; i < 4; ++i) o[i] = oacc[dt][i] * sc;
+      uint2 v;
+      if (split_out) {
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        const f16x4 hv = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
+        __builtin_memcpy(&v, &hv, 8);
+      } else {
+        if (d0 >= nope) {             // rotation at -t: (cos, -sin) of the query's angle
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = oacc[dt][i] * inv;
-    if (d0 >= nope) {             // rotation at -t: (cos, -sin) of the query's angle
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        const float2 cv = ang[(d0 - nope) / 2 + p];
-        const float x0 = o[2 * p], x1 = o[2 * p + 1];
-        o[2 * p] = x0 * cv.x + x1 * cv.y;
-        o[2 * p + 1] = -x0 * cv.y + x1 * cv.x;
+          for (int p = 0; p < 2; ++p) {
+            const float2 cv = ang[(d0 - nope) / 2 + p];
+            const float x0 = o[2 * p], x1 = o[2 * p + 1];
+            o[2 * p] = x0 * cv.x + x1 * cv.y;
+            o[2 * p + 1] = -x0 * cv.y + x1 * cv.x;
+          }
+        }
+        v = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
+      *reinterpret_cast<uint2*>(orow + 32 * dt) = v;
     }
-    *reinterpret_cast<uint2*>(op + 16 * dt) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+  }
+  const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
+  if (split_out && lq == 0 && dh == 0) {
+    a.part_ml[(slot * 64 + row) * 2] = m_run;
+    a.part_ml[(slot * 64 + row) * 2 + 1] = l_row;
+  }
+  __syncthreads();
+  // Row r of the block lands at row r of a contiguous run: the split's slot of
+  // the partials, or the output rows (b, i0 + r / Hs, h0 + r % Hs), which are
+  // consecutive because Hs == H whenever a block holds several tokens.
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  const int n_rows = split_out ? 64 : w.n_q * a.Hs;
+  uint8_t* dst = split_out
+      ? reinterpret_cast<uint8_t*>(a.part_o + slot * 64 * D)
+      : static_cast<uint8_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0) * a.H + w.h0) * D * 2;
+#pragma unroll
+  for (int k = 0; k < 64 * CPR / NT; ++k) {
+    const int c = tid + k * NT;
+    if (c < n_rows * CPR) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ob + (c / CPR) * Gm::EROW + 16 * (c % CPR));
+      *reinterpret_cast<uint4*>(dst + (int64_t)c * 16) = v;
+    }
   }
 }
 
 // ---------------------------------------------------------------- combine
 __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
-  __shared__ float wgt[1024];
-  __shared__ float red[2];
+  // wgt holds the split weights (nsplit <= kMaxSplit), then (reused) the split
+  // groups' partial sums: (256 / (D/8) - 1) * D floats <= 1920 for D >= 128.
+  __shared__ float wgt[kMaxSplit];
+  __shared__ float red[1];
   __shared__ double freq[kMaxRopePairs];
-  rope_freq_table(freq, a.r, a.theta);
   const int work = blockIdx.x / 64, row = blockIdx.x % 64;
   const Work w = make_work(a, work);
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
   if (g >= w.n_q) return;
   const int64_t slot0 = (int64_t)work * a.nsplit;
+  // Thread (split group sg, column group cg) sums splits sg, sg + n_sg, ... over
+  // 8 columns with 16-byte loads, eight splits' loads in flight at a time; the
+  // split groups then meet in LDS.  The first eight loads are issued before
+  // the split weights are formed.
+  const int n_cg = a.D / 8, n_sg = blockDim.x / n_cg;
+  const int cg = threadIdx.x % n_cg, sg = threadIdx.x / n_cg;
+  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+  const _Float16* pp = a.part_o + (slot0 * 64 + row) * a.D + 8 * cg;
+  const int64_t stride = 64LL * a.D;
+  f16x8 x[8];
+  auto issue = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * n_sg;
+      x[u] = *reinterpret_cast<const f16x8*>(pp + (int64_t)(s < a.nsplit ? s : 0) * stride);
+    }
+  };
+  issue(sg);
+  rope_freq_table(freq, a.r, a.theta);
   if (threadIdx.x < 64) {
-    float M = -INFINITY;
-    for (int s = threadIdx.x; s < a.nsplit; s += 64) M = fmaxf(M, a.part_ml[((slot0 + s) * 64 + row) * 2]);
+    const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * 64 + row;
+    const int tid = threadIdx.x;
+    const float2 v0 = tid < a.nsplit ? ml[(int64_t)tid * 64] : make_float2(-INFINITY, 0.f);
+    float M = v0.x;
+    for (int s = tid + 64; s < a.nsplit; s += 64) M = fmaxf(M, ml[(int64_t)s * 64].x);
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     const float sink2 = a.sink ? a.sink[h] * 1.4426950408889634f : -INFINITY;
     M = fmaxf(M, sink2);
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f;
-    for (int s = threadIdx.x; s < a.nsplit; s += 64) {
-      const float ms = a.part_ml[((slot0 + s) * 64 + row) * 2];
-      const float ls = a.part_ml[((slot0 + s) * 64 + row) * 2 + 1];
-      const float f = exp2f(ms - Mu) * ls;
+    if (tid < a.nsplit) {
+      const float f = exp2f(v0.x - Mu) * v0.y;
+      wgt[tid] = f;
+      L = f;
+    }
+    for (int s = tid + 64; s < a.nsplit; s += 64) {
+      const float2 v = ml[(int64_t)s * 64];
+      const float f = exp2f(v.x - Mu) * v.y;
       wgt[s] = f;
       L += f;
     }
     for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (threadIdx.x == 0) {
+    if (tid == 0) {
       if (a.sink) L += exp2f(sink2 - Mu);
       red[0] = L > 0.f ? 1.f / L : 0.f;
     }
@@ -720,29 +772,52 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   const float inv = red[0];
   const int nope = a.D - a.r;
   const int64_t t = w.t_first + g;
-  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * a.D;
-  for (int c = 2 * threadIdx.x; c < a.D; c += 2 * blockDim.x) {
-    float o0 = 0.f, o1 = 0.f;
-    const _Float16* pp = a.part_o + (slot0 * 64 + row) * a.D + c;
-    const int64_t stride = 64LL * a.D;
-#pragma unroll 8
-    for (int s = 0; s < a.nsplit; ++s) {
-      typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-      const f16x2 x = *reinterpret_cast<const f16x2*>(pp + s * stride);
-      o0 = fmaf(wgt[s], (float)x[0], o0);
-      o1 = fmaf(wgt[s], (float)x[1], o1);
+  // angles of the rotation at -t, formed while the loads are in flight
+  float2 cs[4];
+  const bool rot = sg == 0 && 8 * cg + 8 > nope;
+  if (rot) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = 8 * cg + 2 * q;
+      cs[q] = make_float2(1.f, 0.f);
+      if (c >= nope) rope_cos_sin((double)t, freq[(c - nope) >> 1], &cs[q].x, &cs[q].y);
     }
-    o0 *= inv;
-    o1 *= inv;
-    if (c >= nope) {             // rotation at -t
-      float cs, sn;
-      rope_cos_sin((double)t, freq[(c - nope) >> 1], &cs, &sn);
-      const float r0 = o0 * cs + o1 * sn, r1 = -o0 * sn + o1 * cs;
+  }
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < a.nsplit; s0 += 8 * n_sg) {
+    if (s0 != sg) issue(s0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u * n_sg;
+      const float wv = s < a.nsplit ? wgt[s] : 0.f;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(wv, (float)x[u][c], acc[c]);
+    }
+  }
+  float* part = reinterpret_cast<float*>(wgt + 0);   // the weights are no longer needed
+  __syncthreads();
+  if (sg > 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) part[(sg - 1) * a.D + 8 * cg + c] = acc[c];
+  }
+  __syncthreads();
+  if (sg != 0) return;
+  for (int o = 1; o < n_sg; ++o)
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] += part[(o - 1) * a.D + 8 * cg + c];
+  uint16_t* op = static_cast<uint16_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0 + g) * a.H + h) * a.D + 8 * cg;
+  uint32_t pk[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float o0 = acc[2 * q] * inv, o1 = acc[2 * q + 1] * inv;
+    if (rot) {
+      const float r0 = o0 * cs[q].x + o1 * cs[q].y, r1 = -o0 * cs[q].y + o1 * cs[q].x;
       o0 = r0;
       o1 = r1;
     }
-    *reinterpret_cast<uint32_t*>(op + c) = pack_bf16x2(o0, o1);
+    pk[q] = pack_bf16x2(o0, o1);
   }
+  *reinterpret_cast<uint4*>(op) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
 }
 
 // ---------------------------------------------------------------- float32 VALU path
@@ -867,13 +942,27 @@ hipError_t launch_mfma(const KArgs& k, const AttnPlan& p, hipStream_t st) {
 
 }  // namespace
 
+// The workspace is sized without knowing the mode (G * n_entries entries per
+// work item, enough for either); HCA launches with its tighter count unless
+// that would ask for more splits than the workspace holds.
 size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries, int W) {
-  return make_plan(B, Tq, H, D, r, kv_fmt, n_entries, W, kv_fmt == kF32).total;
+  return make_plan(B, Tq, H, D, r, kv_fmt, n_entries, W, kv_fmt == kF32, false).total;
 }
+
+static AttnPlan launch_plan(const AttendArgs& a) {
+  const bool f32 = a.kv_fmt == kF32;
+  const AttnPlan loose = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32, false);
+  if (a.mode != 1 || f32) return loose;
+  const AttnPlan tight = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32, true);
+  return tight.nsplit <= loose.nsplit ? tight : loose;
+}
+
+int attend_split_count(const AttendArgs& a) { return launch_plan(a).nsplit; }
 
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   const bool f32 = a.kv_fmt == kF32;
-  const AttnPlan p = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32);
+  const AttnPlan p = launch_plan(a);
+  if (p.nsplit > kMaxSplit) return hipErrorInvalidValue;
   if (a.B == 0 || a.Tq == 0) return hipSuccess;
   uint8_t* w8 = static_cast<uint8_t*>(ws);
   hipError_t e;

@@ -77,6 +77,10 @@ struct AttendArgs {
 };
 size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries,
                               int W);
+// Splits of the key range per work item that a launch would use; a launch
+// refuses more than kMaxSplit (the combine step keeps one weight per split in LDS).
+constexpr int kMaxSplit = 2048;
+int attend_split_count(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st);
 
 }  // namespace lac

@@ -145,3 +145,13 @@ def test_csa_bf16_h8_eight_tokens_per_block():
 
 def test_hca_bf16_h2_thirty_two_tokens_per_block():
     _case(1, 1, 70, 2, 256, 64, 40, 0, 128, 64, [4800], "bf16", 14)
+
+
+def test_hca_mixed_decode_over_64_splits_with_sink():
+    # one sequence over 8192 entries + window: more than 64 key splits to combine
+    _case(1, 1, 1, 64, 512, 64, 8192, 0, 128, 128, [8192 * 128 + 77], "mixed", 15, sink=True)
+
+
+def test_hca_bf16_h8_decode_group():
+    # H = 8, four tokens of one sequence: the block's queries share the entries
+    _case(1, 2, 4, 8, 128, 64, 900, 0, 128, 32, [900 * 128 - 2, 300 * 128], "bf16", 16)
