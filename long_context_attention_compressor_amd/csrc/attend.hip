@@ -715,7 +715,7 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   // groups' partial sums: (256 / (D/8) - 1) * D floats <= 1920 for D >= 128.
   __shared__ float wgt[kMaxSplit];
   __shared__ float red[1];
-  __shared__ double freq[kMaxRopePairs];
+  __shared__ float2 angle[kMaxRopePairs];
   const int work = blockIdx.x / 64, row = blockIdx.x % 64;
   const Work w = make_work(a, work);
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
@@ -739,10 +739,20 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
     }
   };
   issue(sg);
-  rope_freq_table(freq, a.r, a.theta);
-  if (threadIdx.x < 64) {
+  // While the loads are in flight, wave 1 forms the angles of the rotation
+  // at -t and the last wave the split weights.
+  const int nope = a.D - a.r;
+  const int64_t t = w.t_first + g;
+  if (threadIdx.x >= 64 && threadIdx.x < 64 + a.r / 2) {
+    const int p = threadIdx.x - 64;
+    float c, sn;
+    rope_cos_sin((double)t, rope_inv_freq(p, a.r, a.theta), &c, &sn);
+    angle[p] = make_float2(c, sn);
+  }
+  const int wlast = (int)(blockDim.x / 64) - 1;
+  if ((int)(threadIdx.x / 64) == wlast) {
     const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * 64 + row;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x - 64 * wlast;
     const float2 v0 = tid < a.nsplit ? ml[(int64_t)tid * 64] : make_float2(-INFINITY, 0.f);
     float M = v0.x;
     for (int s = tid + 64; s < a.nsplit; s += 64) M = fmaxf(M, ml[(int64_t)s * 64].x);
@@ -770,19 +780,6 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   }
   __syncthreads();
   const float inv = red[0];
-  const int nope = a.D - a.r;
-  const int64_t t = w.t_first + g;
-  // angles of the rotation at -t, formed while the loads are in flight
-  float2 cs[4];
-  const bool rot = sg == 0 && 8 * cg + 8 > nope;
-  if (rot) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = 8 * cg + 2 * q;
-      cs[q] = make_float2(1.f, 0.f);
-      if (c >= nope) rope_cos_sin((double)t, freq[(c - nope) >> 1], &cs[q].x, &cs[q].y);
-    }
-  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int s0 = sg; s0 < a.nsplit; s0 += 8 * n_sg) {
     if (s0 != sg) issue(s0);
@@ -809,9 +806,11 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   uint32_t pk[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
+    const int c = 8 * cg + 2 * q;
     float o0 = acc[2 * q] * inv, o1 = acc[2 * q + 1] * inv;
-    if (rot) {
-      const float r0 = o0 * cs[q].x + o1 * cs[q].y, r1 = -o0 * cs[q].y + o1 * cs[q].x;
+    if (c >= nope) {
+      const float2 cv = angle[(c - nope) >> 1];
+      const float r0 = o0 * cv.x + o1 * cv.y, r1 = -o0 * cv.y + o1 * cv.x;
       o0 = r0;
       o1 = r1;
     }

@@ -92,10 +92,14 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 // positions in the millions.
 constexpr int kMaxRopePairs = 64;   // rope_dims <= 128
 
+// theta^(-2i/r): the angular frequency of rotated pair i.
+__device__ __forceinline__ double rope_inv_freq(int i, int r, float theta) {
+  return pow((double)theta, -2.0 * (double)i / (double)r);
+}
+
 // Block-wide: tab[i] = theta^(-2i/r), i < r/2.  The caller synchronises.
 __device__ __forceinline__ void rope_freq_table(double* tab, int r, float theta) {
-  for (int i = threadIdx.x; i < r / 2; i += blockDim.x)
-    tab[i] = pow((double)theta, -2.0 * (double)i / (double)r);
+  for (int i = threadIdx.x; i < r / 2; i += blockDim.x) tab[i] = rope_inv_freq(i, r, theta);
 }
 
 __device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float* c, float* s) {
