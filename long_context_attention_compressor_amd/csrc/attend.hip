@@ -108,17 +108,17 @@ struct WinArgs {
   int64_t n_win_items;       // window work items (D/8 per row); angle items follow
   int fmt, B, D, r, Tq, W;
   int64_t T_raw, win_rows, row_bytes;
-  float theta;
+  RopeTable rope;
   Positions qpos, rawpos;
 };
 
 __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
   __shared__ double freq[kMaxRopePairs];
-  rope_freq_table(freq, a.r, a.theta);
+  rope_freq_table(freq, a.rope, a.r, threadIdx.x, 256);
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x < 4) reinterpret_cast<uint32_t*>(a.zero_row)[threadIdx.x] = 0u;
   const int G8 = a.D / 8;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= a.n_win_items) {            // angle table of the query positions
     const int np = a.r / 2;
     const int64_t j = gid - a.n_win_items;
@@ -205,6 +205,7 @@ struct KArgs {
   int G, Hs, n_htiles, n_qgroups, nsplit, chunk;
   int64_t win_rows, row_bytes;
   Positions qpos;
+  RopeTable rope;
 };
 
 // Work item decomposition: blockIdx.x = split (fastest), blockIdx.y = work.
@@ -404,7 +405,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
     const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * kk + e_lo;
     for (int e = tid; e < n_idx; e += NT) lidx[e] = src[e];
   }
-  rope_freq_table(freq, a.r, a.theta);
+  rope_freq_table(freq, a.rope, a.r, tid, NT);
   __syncthreads();
 
   constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
@@ -725,7 +726,7 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   // 8 columns with 16-byte loads, eight splits' loads in flight at a time; the
   // split groups then meet in LDS.  The first eight loads are issued before
   // the split weights are formed.
-  const int n_cg = a.D / 8, n_sg = blockDim.x / n_cg;
+  const int n_cg = a.D / 8, n_sg = 256 / n_cg;
   const int cg = threadIdx.x % n_cg, sg = threadIdx.x / n_cg;
   typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
   const _Float16* pp = a.part_o + (slot0 * 64 + row) * a.D + 8 * cg;
@@ -746,10 +747,10 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   if (threadIdx.x >= 64 && threadIdx.x < 64 + a.r / 2) {
     const int p = threadIdx.x - 64;
     float c, sn;
-    rope_cos_sin((double)t, rope_inv_freq(p, a.r, a.theta), &c, &sn);
+    rope_cos_sin((double)t, a.rope.inv_freq[p], &c, &sn);
     angle[p] = make_float2(c, sn);
   }
-  const int wlast = (int)(blockDim.x / 64) - 1;
+  const int wlast = 3;
   if ((int)(threadIdx.x / 64) == wlast) {
     const float2* ml = reinterpret_cast<const float2*>(a.part_ml) + slot0 * 64 + row;
     const int tid = threadIdx.x - 64 * wlast;
@@ -824,7 +825,7 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
 __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   extern __shared__ float fsm[];
   __shared__ double freq[kMaxRopePairs];
-  rope_freq_table(freq, a.r, a.theta);
+  rope_freq_table(freq, a.rope, a.r, threadIdx.x, 256);
   const int H = a.H, D = a.D;
   float* qs = fsm;                    // [H][D]
   float* es = qs + H * D;             // [32][D]
@@ -975,7 +976,8 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
     wa.win = w8 + p.off_win;
     wa.zero_row = w8 + p.off_zero;
     wa.fmt = a.kv_fmt; wa.B = a.B; wa.D = a.D; wa.r = a.r; wa.Tq = a.Tq; wa.W = a.W;
-    wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes; wa.theta = a.theta;
+    wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes;
+    make_rope_table(&wa.rope, a.r, a.theta);
     wa.qpos = a.qpos; wa.rawpos = a.rawpos;
     wa.ang = reinterpret_cast<float2*>(w8 + p.off_ang);
     wa.n_win_items = (int64_t)a.B * p.win_rows * (a.D / 8);
@@ -992,6 +994,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
   k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;
   k.H = a.H; k.D = a.D; k.r = a.r; k.theta = a.theta;
+  make_rope_table(&k.rope, a.r, a.theta);
   k.scale_log2 = a.scale * 1.4426950408889634f;
   k.G = p.G; k.Hs = p.Hs; k.n_htiles = p.n_htiles; k.n_qgroups = p.n_qgroups;
   k.nsplit = p.nsplit; k.chunk = p.chunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;

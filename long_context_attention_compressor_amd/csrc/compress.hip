@@ -90,36 +90,28 @@ __device__ __forceinline__ void softmax_step(const float* xv, const float* zv, f
   }
 }
 
-// Block of blockDim.x threads: S threads per (entry, 8-channel group) split the
-// block's tokens; several entries per block when D/8 * S < blockDim.x.
+// Block (GB, S, epb): thread (x, y, z) owns channel group slice * GB + x of
+// entry blockIdx.x * epb + z and token share y of its block; the grid is
+// (entry groups, channel slices, sequences), so no index needs a division.
 template <int IN, int OUT>
 __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
-  extern __shared__ float part[];                  // [blockDim.x][25] when S > 1
+  extern __shared__ float part[];                  // [blockDim][25] when S > 1
   __shared__ double freq[kMaxRopePairs];
-  // A block covers GB of the entry's G groups of 8 channels (G / GB blocks
-  // per entry), or several whole entries when GB = G.
-  const int G = a.D >> 3;
-  const int GB = a.GB;
-  const int per_entry = GB * a.S;    // threads per (entry, channel slice)
-  const int epb = blockDim.x / per_entry;   // entries per block
-  const int slices = G / GB;
-  const int t = threadIdx.x;
-  const int le = t / per_entry;
-  const int within = t - le * per_entry;
-  const int s = within / GB;
-  const int g = (blockIdx.x % slices) * GB + (within - s * GB);
-  const int N = a.T / a.m;
-  const int64_t e = (int64_t)(blockIdx.x / slices) * epb + le;
-  const bool live = le < epb && e < (int64_t)a.B * N;
-  const int b = live ? (int)(e / N) : 0;
-  const int j = live ? (int)(e - (int64_t)b * N) : 0;
+  const int GB = a.gb, S = a.s;
+  const int s = threadIdx.y;
+  const int g = blockIdx.y * GB + threadIdx.x;
+  const int b = blockIdx.z;
+  const int j = blockIdx.x * a.epb + threadIdx.z;
+  const bool live = j < a.N;
+  const int t = (threadIdx.z * S + s) * GB + threadIdx.x;
+  const int nthreads = GB * S * a.epb;
 
   float mx[8], den[8], acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
 
   if (live) {
-    const int per = a.m / a.S;
+    const int per = a.per;
     const int64_t row0 = (int64_t)j * a.m + (int64_t)s * per;
     const int64_t xb = (b * a.kv_bstride + row0) * a.D + g * 8;
     const int64_t zb = (b * a.z_bstride + row0) * a.D + g * 8;
@@ -136,7 +128,7 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
         zr[u] = load_raw8<IN>(a.logits, zb + row * a.D);
       }
       if (i == 0) {
-        rope_freq_table(freq, a.r, a.theta);
+        rope_freq_table(freq, a.rope, a.r, t, nthreads);
       }
 #pragma unroll
       for (int u = 0; u < TOK; ++u) {
@@ -149,14 +141,14 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
       }
     }
   } else {
-    rope_freq_table(freq, a.r, a.theta);
+    rope_freq_table(freq, a.rope, a.r, t, nthreads);
   }
   __syncthreads();                   // rotation table complete
 
-  if (a.S > 1) {
+  if (S > 1) {
     // Tree merge: at level o, thread s < o absorbs thread s + o.
     float* mine = part + t * 25;
-    for (int o = a.S >> 1; o >= 1; o >>= 1) {
+    for (int o = S >> 1; o >= 1; o >>= 1) {
       if (s < 2 * o) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -234,12 +226,12 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
 }
 
 template <int IN, int OUT>
-hipError_t launch(const CompressArgs& a, int grid, int threads, size_t lds, hipStream_t st) {
+hipError_t launch(const CompressArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&compress_kernel<IN, OUT>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 512 * 25 * (int)sizeof(float));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((compress_kernel<IN, OUT>), dim3(grid), dim3(threads), lds, st, a);
+  hipLaunchKernelGGL((compress_kernel<IN, OUT>), grid, block, lds, st, a);
   return hipGetLastError();
 }
 
@@ -258,23 +250,28 @@ hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   if (GB * S > 512) {           // few channel groups and a long block: fewer splits
     while (GB * S > 512) S /= 2;
   }
-  a.S = S;
-  a.GB = GB;
+  a.per = a.m / S;
+  a.gb = GB;
+  a.s = S;
   const int threads = GB * S <= 256 ? (GB == G ? 256 : GB * S) : GB * S;
   const int epb = threads / (GB * S);
+  a.epb = epb;
+  make_rope_table(&a.rope, a.r, a.theta);
   const size_t lds = S > 1 ? (size_t)threads * 25 * sizeof(float) : 0;
-  const int64_t entries = (int64_t)a.B * (a.T / a.m);
-  if (entries == 0) return hipSuccess;
-  const int grid = (int)(((entries + epb - 1) / epb) * (G / GB));
+  const int N = a.T / a.m;
+  a.N = N;
+  if ((int64_t)a.B * N == 0) return hipSuccess;
+  const dim3 grid((unsigned)((N + epb - 1) / epb), (unsigned)(G / GB), (unsigned)a.B);
+  const dim3 block((unsigned)GB, (unsigned)S, (unsigned)epb);
   TimedLaunch tl(kKernelCompress, st);
   if (a.in_fmt == kF32) {
-    if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, threads, lds, st);
-    if (a.out_fmt == kBF16) return launch<kF32, kBF16>(a, grid, threads, lds, st);
-    return launch<kF32, kMixed>(a, grid, threads, lds, st);
+    if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, block, lds, st);
+    if (a.out_fmt == kBF16) return launch<kF32, kBF16>(a, grid, block, lds, st);
+    return launch<kF32, kMixed>(a, grid, block, lds, st);
   }
-  if (a.out_fmt == kF32) return launch<kBF16, kF32>(a, grid, threads, lds, st);
-  if (a.out_fmt == kBF16) return launch<kBF16, kBF16>(a, grid, threads, lds, st);
-  return launch<kBF16, kMixed>(a, grid, threads, lds, st);
+  if (a.out_fmt == kF32) return launch<kBF16, kF32>(a, grid, block, lds, st);
+  if (a.out_fmt == kBF16) return launch<kBF16, kBF16>(a, grid, block, lds, st);
+  return launch<kBF16, kMixed>(a, grid, block, lds, st);
 }
 
 }  // namespace lac

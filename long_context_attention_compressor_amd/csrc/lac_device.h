@@ -1,6 +1,7 @@
 // lac_device.h -- device helpers shared by the gfx950 kernels of the library:
 // number formats, rotary angles, MFMA operand types and small reductions.
 #pragma once
+#include <cmath>
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -86,28 +87,47 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float f) {
 
 // ---------------------------------------------------------------- rotary angles
 // Rotation of pair i (of r/2) at integer position p by angle p * theta^(-2i/r).
-// The inverse frequencies are computed once per workgroup (one double pow per
-// pair) into LDS; the product with the position and its reduction modulo
-// 2*pi are taken in double, so the angle stays exact to float precision at
-// positions in the millions.
+// The inverse frequencies are computed on the host in double (one pow per
+// pair) and passed by value with the launch; a kernel copies them to LDS.
+// The product with the position and its reduction to a quarter turn are
+// taken in double, so the angle stays exact to float precision at positions
+// in the millions.
 constexpr int kMaxRopePairs = 64;   // rope_dims <= 128
 
-// theta^(-2i/r): the angular frequency of rotated pair i.
-__device__ __forceinline__ double rope_inv_freq(int i, int r, float theta) {
-  return pow((double)theta, -2.0 * (double)i / (double)r);
+struct RopeTable {
+  double inv_freq[kMaxRopePairs];
+};
+
+inline void make_rope_table(RopeTable* t, int r, float theta) {
+  for (int i = 0; i < kMaxRopePairs; ++i)
+    t->inv_freq[i] = i < r / 2 ? std::pow((double)theta, -2.0 * (double)i / (double)r) : 0.0;
 }
 
-// Block-wide: tab[i] = theta^(-2i/r), i < r/2.  The caller synchronises.
-__device__ __forceinline__ void rope_freq_table(double* tab, int r, float theta) {
-  for (int i = threadIdx.x; i < r / 2; i += blockDim.x) tab[i] = rope_inv_freq(i, r, theta);
+// tab[i] = inv_freq[i], i < r/2, by threads tid of nthreads; the caller
+// synchronises.
+__device__ __forceinline__ void rope_freq_table(double* tab, const RopeTable& t, int r, int tid,
+                                                int nthreads) {
+  for (int i = tid; i < r / 2; i += nthreads) tab[i] = t.inv_freq[i];
 }
 
+// cos and sin of pos * inv_freq.  The angle is reduced in double to
+// x in [-pi/4, pi/4] plus a quarter-turn count q; sin x and cos x are their
+// Taylor series through x^9 and x^10 in float (truncation below 2e-9 on
+// that interval), and q picks the signs and the swap.
 __device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float* c, float* s) {
   const double a = pos * inv_freq;
-  const double k = rint(a * 0.15915494309189535);          // a / (2 pi)
-  double red = fma(-k, 6.283185307179586, a);              // 2 pi, high part
-  red = fma(-k, 2.4492935982947064e-16, red);              // 2 pi, low part
-  sincosf((float)red, s, c);
+  const double k = rint(a * 0.63661977236758134);          // a / (pi/2)
+  double red = fma(-k, 1.5707963267948966, a);             // pi/2, high part
+  red = fma(-k, 6.123233995736766e-17, red);               // pi/2, low part
+  const float x = (float)red, x2 = x * x;
+  const float sx = x * fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, 1.f / 362880.f, -1.f / 5040.f), 1.f / 120.f),
+                                     -1.f / 6.f), 1.f);
+  const float cx = fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, fmaf(x2, -1.f / 3628800.f, 1.f / 40320.f),
+                                                   -1.f / 720.f), 1.f / 24.f), -0.5f), 1.f);
+  const int q = (int)((int64_t)k & 3);
+  const float sv = (q & 1) ? cx : sx, cv = (q & 1) ? sx : cx;
+  *s = (q & 2) ? -sv : sv;
+  *c = ((q + 1) & 2) ? -cv : cv;
 }
 
 // ---------------------------------------------------------------- selection keys

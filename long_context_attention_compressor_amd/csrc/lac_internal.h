@@ -39,8 +39,9 @@ struct CompressArgs {
   int B, T, D, m, r;
   float theta;
   int64_t kv_bstride, z_bstride, out_bstride;  // rows
-  int S;                                       // token splits (set by the launcher)
-  int GB;                                      // 8-channel groups per block (launcher)
+  // set by the launcher: tokens per thread, entries, block (gb, s, epb)
+  int per, N, gb, s, epb;
+  RopeTable rope;
   Positions pos0;
 };
 hipError_t launch_compress(CompressArgs a, hipStream_t st);
