@@ -788,25 +788,45 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
   __syncthreads();
   const uint32_t b2 = t_b2, need_t = need - t_above;
 
-  // Chunk lists: wave w takes chunks w, w + 16, ...
+  // Chunk lists: wave w takes chunks w, w + 16, ..., four at a time; the first
+  // 64 entries of each list of the four are loaded before any is used.
   const int32_t* sel = a.sel + (int64_t)row * a.Np;
   const uint2* cand = a.cand + (int64_t)row * a.Np;
-  for (int ch = wv; ch < nchunks; ch += 16) {
-    const int n_up = (int)ccnt[2 * ch], n_in = (int)ccnt[2 * ch + 1];
-    const int64_t base = (int64_t)ch * kSplitChunk;
-    for (int i = l; i < n_up; i += 64) {
-      const int32_t j = sel[base + i];
-      atomicOr(&bits[j >> 5], 1u << (j & 31));
+  auto take_cand = [&](uint2 cv) {
+    const uint32_t d2 = (cv.x >> 8) & (kHistBins - 1);
+    if (d2 > b2) {
+      atomicOr(&bits[cv.y >> 5], 1u << (cv.y & 31));
+    } else if (d2 == b2) {
+      const uint32_t pos = atomicAdd(&n_tie, 1u);
+      if (pos < (uint32_t)kTieLds) ties[pos] = cv;
     }
-    for (int i = l; i < n_in; i += 64) {
-      const uint2 cv = cand[base + i];
-      const uint32_t d2 = (cv.x >> 8) & (kHistBins - 1);
-      if (d2 > b2) {
-        atomicOr(&bits[cv.y >> 5], 1u << (cv.y & 31));
-      } else if (d2 == b2) {
-        const uint32_t pos = atomicAdd(&n_tie, 1u);
-        if (pos < (uint32_t)kTieLds) ties[pos] = cv;
+  };
+  for (int c0 = wv; c0 < nchunks; c0 += 64) {
+    int32_t jv[4];
+    uint2 cv[4];
+    int n_up[4], n_in[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int ch = c0 + 16 * u;
+      n_up[u] = ch < nchunks ? (int)ccnt[2 * ch] : 0;
+      n_in[u] = ch < nchunks ? (int)ccnt[2 * ch + 1] : 0;
+      const int64_t base = (int64_t)(ch < nchunks ? ch : 0) * kSplitChunk;
+      jv[u] = sel[base + (l < n_up[u] ? l : 0)];
+      cv[u] = cand[base + (l < n_in[u] ? l : 0)];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (l < n_up[u]) atomicOr(&bits[jv[u] >> 5], 1u << (jv[u] & 31));
+      if (l < n_in[u]) take_cand(cv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {     // lists longer than 64
+      const int64_t base = (int64_t)(c0 + 16 * u) * kSplitChunk;
+      for (int i = 64 + l; i < n_up[u]; i += 64) {
+        const int32_t j = sel[base + i];
+        atomicOr(&bits[j >> 5], 1u << (j & 31));
       }
+      for (int i = 64 + l; i < n_in[u]; i += 64) take_cand(cand[base + i]);
     }
   }
   __syncthreads();
