@@ -59,8 +59,11 @@ struct ScoreArgs {
   float* scores;          // [R, Np]
   int B, Tq, HI, dI, N, m;
   int64_t Np;
-  int tiles_per_wave;     // 32-key tiles per wave
+  int tiles_per_wave;     // 32-key tiles per wave (static schedule)
   uint32_t* hist;         // [R, kHistBins] 12-bit key histogram (split path) or null
+  uint32_t* tile_ctr;     // [R, 16 * 32] zeroed tile counters (dynamic schedule) or null
+  int n_static;           // dynamic schedule: strided tiles per wave before the counters
+  int n_groups;           // dynamic schedule: counters per row (<= 16)
   Positions qpos;
 };
 
@@ -114,7 +117,7 @@ __global__ void __launch_bounds__(256) score_f32_kernel(ScoreArgs a) {
 // index, so the MFMA-layout reads (one chunk of 32 different rows per half
 // wave) are free of bank conflicts.  The next tile is loaded into VGPRs while
 // the current one is consumed from LDS.
-template <int HT, int KS, int QPW, int RW>
+template <int HT, int KS, int QPW, int RW, bool DYN>
 __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   constexpr int kRowsPerBlock = RW * QPW;
   constexpr int KW = 4 / RW;
@@ -159,6 +162,10 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   const int64_t gw = (int64_t)blockIdx.x * KW + wk, nw = (int64_t)gridDim.x * KW;
   const int64_t n_tiles = (nv_max + 31) / 32;
   const int64_t n_mine = gw < n_tiles ? std::min<int64_t>(a.tiles_per_wave, (n_tiles - gw + nw - 1) / nw) : 0;
+  // Dynamic schedule: the one-query decode shape with tile counters (two
+  // stages per wave); otherwise each wave takes its n_mine strided tiles.
+  constexpr bool dynamic = DYN && QPW == 1;
+  uint32_t* ctr = dynamic ? a.tile_ctr + ((int64_t)b * a.Tq + i0) * (16 * 32) : nullptr;
 
   const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
   uint8_t* kt = ktile[wave];
@@ -186,13 +193,14 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   // allow it); the stages alternate.
   constexpr int PF = QPW == 1 ? 2 : 1;
   uint4 stage[PF][NLD];
+  // (Unconditional, so that the compiler can count them: a tile past the end
+  // reads clamped rows and is not used.)
 #pragma unroll
-  for (int f = 0; f < PF; ++f)
-    if (f < n_mine) load_tile(gw + f * nw, stage[f]);
+  for (int f = 0; f < PF; ++f) load_tile(gw + f * nw, stage[f]);
   // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
   bf16x8 qf[QPW][HT][KS];
   int64_t nv_row[QPW];
-  if (n_mine > 0) {
+  {
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
       const int rr = wr * QPW + qi;
@@ -217,47 +225,95 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     for (int e = threadIdx.x; e < kHistBins; e += 256) lhist[e] = 0u;
   __syncthreads();
 
-  if (n_mine > 0) {
-    auto consume = [&](int64_t it, uint4* st) {
-      const int64_t tile = gw + it * nw;
-      store_tile(st);
-      __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): LDS writes done
-      __builtin_amdgcn_wave_barrier();
-      if (it + PF < n_mine) load_tile(tile + PF * nw, st);
-      bf16x8 kf[KS];
+  // Work on one tile held in LDS: scores of the wave's query rows.
+  auto compute = [&](int64_t tile) {
+    bf16x8 kf[KS];
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const int c = hf * (CH / 2) + s;
-        kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+    for (int s = 0; s < KS; ++s) {
+      const int c = hf * (CH / 2) + s;
+      kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+    }
+    const int64_t j = tile * 32 + ln;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      const int rr = wr * QPW + qi;
+      float part = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], relu(acc[v]), part);
       }
-      const int64_t j = tile * 32 + ln;
-#pragma unroll
-      for (int qi = 0; qi < QPW; ++qi) {
-        const int rr = wr * QPW + qi;
-        float part = 0.f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) {
-          f32x16 acc = {};
-#pragma unroll
-          for (int s = 0; s < KS; ++s)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
-          // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
-#pragma unroll
-          for (int v = 0; v < 16; ++v)
-            part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], fmaxf(acc[v], 0.f), part);
-        }
-        part += __shfl_xor(part, 32);
-        const bool live = hf == 0 && j < nv_row[qi];
-        if (live) a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
-        if (do_hist) hist_add(lhist, live, score_key(part) >> 20);
-      }
-      __builtin_amdgcn_s_waitcnt(0xc07f);      // LDS reads of this tile done
-      __builtin_amdgcn_wave_barrier();
+      part += __shfl_xor(part, 32);
+      const bool live = hf == 0 && j < nv_row[qi];
+      if (live) a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
+      if (do_hist) hist_add(lhist, live, score_key(part) >> 20);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // LDS reads of this tile done
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto stage_in = [&](const uint4* st) {
+    store_tile(st);
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): LDS writes done
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  if constexpr (dynamic) {
+    // The first n_static tiles of a wave are its strided ones; the rest of
+    // the row's tiles are handed out by counters, so that waves that stream
+    // faster take more of them and all finish together.  Each of the row's
+    // n_groups counters (one per group of eight consecutive blocks, which
+    // spans every XCD) serves the tiles n_static * nw + c * n_groups + g:
+    // a device-scope atomic on one address costs tens of nanoseconds, so
+    // the load is spread over several addresses and only the tail of the
+    // sweep is dynamic.  Stage f holds tile t[f] (the wave's sequence
+    // number k[f]); its ticket r[f], drawn by lane 0 when stage f was last
+    // refilled, names the tile that refills it next, two tiles later, so the
+    // atomic's latency is hidden like a load's.
+    const int g = (int)((blockIdx.x >> 3) % (unsigned)a.n_groups);
+    uint32_t* gctr = ctr + 32 * g;
+    const int64_t ns = a.n_static, dyn0 = ns * nw;
+    auto tile_of = [&](int64_t k, uint32_t ticket) {
+      return k < ns ? gw + k * nw : dyn0 + (int64_t)ticket * a.n_groups + g;
     };
+    int64_t t[2] = {gw, gw + nw};
+    uint32_t r[2] = {0u, 0u};
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      if (l == 0 && t[f] < n_tiles && f + 2 >= ns) r[f] = atomicAdd(gctr, 1u);
+    int64_t k = 0;                 // sequence number of the tile in stage 0
+    for (;; k += 2) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (t[f] >= n_tiles) goto done;
+        stage_in(stage[f]);
+        const int64_t kn = k + f + 2;
+        const int64_t nt = tile_of(kn, kn >= ns ? __builtin_amdgcn_readfirstlane(r[f]) : 0u);
+        if (nt < n_tiles) {
+          load_tile(nt, stage[f]);
+          if (l == 0 && kn + 2 >= ns) r[f] = atomicAdd(gctr, 1u);
+        }
+        compute(t[f]);
+        t[f] = nt;
+      }
+    }
+  done:;
+  } else if (n_mine > 0) {
     for (int64_t it = 0; it < n_mine; it += PF) {
 #pragma unroll
-      for (int f = 0; f < PF; ++f)
-        if (it + f < n_mine) consume(it + f, stage[f]);
+      for (int f = 0; f < PF; ++f) {
+        if (it + f < n_mine) {
+          const int64_t tile = gw + (it + f) * nw;
+          stage_in(stage[f]);
+          if (it + f + PF < n_mine) load_tile(tile + PF * nw, stage[f]);
+          compute(tile);
+        }
+      }
     }
   }
 
@@ -928,7 +984,7 @@ struct Plan {
   int64_t Np;
   bool split;
   int chunks;
-  size_t off_scores, off_hist, off_hist2, off_cnt, off_sel, off_cand, total;
+  size_t off_scores, off_hist, off_hist2, off_ctr, off_cnt, off_sel, off_cand, total;
 };
 
 Plan make_plan(int B, int Tq, int N, int k) {
@@ -945,6 +1001,8 @@ Plan make_plan(int B, int Tq, int N, int k) {
     off += round_up(R * kHistBins * 4, 256);
     p.off_hist2 = off;
     off += round_up(R * kHistBins * 4, 256);
+    p.off_ctr = off;
+    off += round_up(R * 16 * 32 * 4, 256);
     p.off_cnt = off;
     off += round_up(R * (int64_t)p.chunks * 8, 256);
     p.off_sel = off;
@@ -1071,7 +1129,7 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
         // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], fmaxf(acc[v], 0.f), part);
+          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], relu(acc[v]), part);
       }
       part += __shfl_xor(part, 32);
       const int off = hf == 0 ? (int)j * 4 : 0x7fffffff;
@@ -1086,8 +1144,12 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
 
 template <int HT, int KS, int QPW, int RW>
 hipError_t launch_score(const ScoreArgs& sa, int64_t key_chunks, int row_groups, hipStream_t st) {
-  hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW>), dim3((unsigned)key_chunks, row_groups),
-                     dim3(256), 0, st, sa);
+  if (sa.tile_ctr != nullptr)
+    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, true>), dim3((unsigned)key_chunks, row_groups),
+                       dim3(256), 0, st, sa);
+  else
+    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, false>), dim3((unsigned)key_chunks, row_groups),
+                       dim3(256), 0, st, sa);
   return hipGetLastError();
 }
 
@@ -1112,8 +1174,9 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
     ta.cnt = reinterpret_cast<uint32_t*>(w8 + p.off_cnt);
     ta.sel = reinterpret_cast<int32_t*>(w8 + p.off_sel);
     ta.cand = reinterpret_cast<uint2*>(w8 + p.off_cand);
-    // The score and filter kernels accumulate into the histograms: clear them
-    // (and the adjacent counters) first, with a kernel rather than a memset.
+    // The score and filter kernels accumulate into the histograms and the
+    // score kernel draws tiles from counters: clear them (and the adjacent
+    // chunk counts) first, with a kernel rather than a memset.
     const int64_t n_clear = (int64_t)(p.off_cnt - p.off_hist) / 4;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_clear + 255) / 256)), dim3(256), 0, st,
                        ta.hist, n_clear);
@@ -1133,6 +1196,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
   sa.q = a.q; sa.w = a.w; sa.K = a.K; sa.scores = scores;
   sa.B = a.B; sa.Tq = a.Tq; sa.HI = a.HI; sa.dI = a.dI; sa.N = a.N; sa.m = a.m;
   sa.Np = p.Np; sa.qpos = a.qpos; sa.hist = ta.hist;
+  sa.tile_ctr = p.split ? reinterpret_cast<uint32_t*>(w8 + p.off_ctr) : nullptr;
   if (nv_max > 0) {
     TimedLaunch tl(kKernelIndexerScore, st);
     if (a.fmt == kF32) {
@@ -1163,6 +1227,9 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
         const int64_t per_row = std::max<int64_t>(1, 512 / R);
         sa.tiles_per_wave = (int)std::max<int64_t>(2, (n_tiles + 4 * per_row - 1) / (4 * per_row));
         const int64_t chunks = (n_tiles + 4 * sa.tiles_per_wave - 1) / (4 * sa.tiles_per_wave);
+        // dynamic schedule: about the last quarter of the sweep
+        sa.n_static = std::max(2, sa.tiles_per_wave * 3 / 4);
+        sa.n_groups = (int)std::min<int64_t>(16, std::max<int64_t>(1, chunks / 8));
         const int groups = a.B * a.Tq;
 #define LAC_SCORE_CASE(ht, ks) \
   if (HT == ht && KS == ks) err = launch_score<ht, ks, 1, 1>(sa, chunks, groups, st);

@@ -130,6 +130,13 @@ __device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float*
   *c = ((q + 1) & 2) ? -cv : cv;
 }
 
+// ---------------------------------------------------------------- ReLU
+// max(x, 0) as one integer max: a float with the sign bit set is a negative
+// int32 and maps to +0 (so does -0); a non-negative float is unchanged.
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 // ---------------------------------------------------------------- selection keys
 // Order-preserving map of a float score to uint32 (larger score -> larger key).
 // -0 is folded onto +0 so that equal scores compare equal.
