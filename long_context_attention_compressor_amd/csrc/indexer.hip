@@ -171,15 +171,24 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   uint8_t* kt = ktile[wave];
   // Load instruction u of a tile: lane l takes 16 bytes at u*1024 + l*16 of
   // the tile in LDS order, i.e. row kk, swizzled chunk slot cs, which holds
-  // the row's chunk cs ^ (kk % CH).
-  auto load_tile = [&](int64_t tile, uint4* st) {
+  // the row's chunk cs ^ (kk % CH).  The loads go through a buffer resource
+  // based at the tile and bounded by its rows below N, so rows past the end
+  // read as zeros and a lane's offsets are the same for every tile.
+  auto load_tile = [&](int64_t tile_any, uint4* st) {
+    // (the tile is the same in every lane: say so, so that the resource
+    // stays in scalar registers)
+    const int64_t tile = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tile_any >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)tile_any));
+    const int64_t rows = a.N - tile * 32;
+    const int nrec = rows >= 32 ? TILEB : rows > 0 ? (int)rows * ROWB : 0;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Kb + tile * TILEB), 0, nrec,
+                                                        0x00020000);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       const int o = u * 1024 + l * 16;
       const int kk = o / ROWB, cs = (o % ROWB) / 16;
-      int64_t j = tile * 32 + kk;
-      if (j > a.N - 1) j = a.N - 1;
-      st[u] = ld_stream16(Kb + j * ROWB + ((cs ^ (kk % CH)) * 16));
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, kk * ROWB + ((cs ^ (kk % CH)) * 16), 0, 2);
+      st[u] = make_uint4(v.x, v.y, v.z, v.w);
     }
   };
   auto store_tile = [&](const uint4* st) {
