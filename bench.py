@@ -35,20 +35,28 @@ BF16_PEAK_TFLOPS = 2500.0
 
 # HBM bytes per launch of the indexer score kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (one pass each), scaled by what the same counters read for a 1 GiB
-# device copy (FETCH x2.000, WRITE x1.000).  They hold only for the kernel source
-# they were taken on, identified by its SHA-256; after any change to it the
-# roofline reports traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273368953, "csa_decode_128k": 277088924,
-                       "csa_chunk_prefill": 13659428059}
-SCORE_TRAFFIC_SOURCE_SHA256 = "cced70b5afdaa854c7e3475e9c1c06588e91bf4c33090c7ee3e0b0406b66c882"
+# device copy (FETCH x2.000, WRITE x1.000).  They hold only for the kernel
+# sources they were taken on (score.hip and the device helpers it includes),
+# identified by their SHA-256; after any change to them the roofline reports
+# traffic as null until the counters are taken again.
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273734787, "csa_decode_128k": 277467942,
+                       "csa_chunk_prefill": 1338360086}
+SCORE_TRAFFIC_SOURCE_SHA256 = "d717940c93eca7522df44b3425fdadf63c3bc54251ac01cca416284426e6763e"
+SCORE_SOURCES = ("score.hip", "lac_device.h")
+
+
+def score_source_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for name in SCORE_SOURCES:
+        with open(os.path.join(ROOT, "long_context_attention_compressor_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def _score_traffic(workload):
-    import hashlib
-    src = os.path.join(ROOT, "long_context_attention_compressor_amd", "csrc", "indexer.hip")
-    with open(src, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != SCORE_TRAFFIC_SOURCE_SHA256:
-            return None
+    if score_source_sha256() != SCORE_TRAFFIC_SOURCE_SHA256:
+        return None
     return SCORE_TRAFFIC_BYTES.get(workload)
 
 

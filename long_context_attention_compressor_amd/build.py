@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblac.so")
-SOURCES = ["abi.cpp", "compress.hip", "indexer.hip", "attend.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "score.hip", "indexer.hip", "attend.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [
@@ -26,7 +26,7 @@ FLAGS = [
 # Per-source code generation options.  The score kernels read every MFMA
 # result with VALU work right away: accumulators in VGPRs save a copy out of
 # the accumulation registers per value.
-EXTRA = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"score.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str) -> str:

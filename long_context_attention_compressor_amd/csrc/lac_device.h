@@ -130,6 +130,25 @@ __device__ __forceinline__ void rope_cos_sin(double pos, double inv_freq, float*
   *c = ((q + 1) & 2) ? -cv : cv;
 }
 
+// ---------------------------------------------------------------- lanes, LDS histograms
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// LDS histogram add for the wave's active lanes: one atomic when every
+// active lane holds the same digit (common in the high radix digits), else
+// one atomic per lane (cheaper than serialising over many distinct digits).
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool on, uint32_t d) {
+  const uint64_t active = __ballot(on);
+  if (!active) return;
+  const int leader = __ffsll((unsigned long long)active) - 1;
+  const uint32_t dl = __builtin_amdgcn_readlane(d, leader);
+  const uint64_t same = __ballot(on && d == dl);
+  if (same == active) {
+    if (lane_id() == leader) atomicAdd(&hist[dl], (uint32_t)__popcll(same));
+  } else if (on) {
+    atomicAdd(&hist[d], 1u);
+  }
+}
+
 // ---------------------------------------------------------------- ReLU
 // max(x, 0) as one integer max: a float with the sign bit set is a negative
 // int32 and maps to +0 (so does -0); a non-negative float is unchanged.

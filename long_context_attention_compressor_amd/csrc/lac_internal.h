@@ -58,6 +58,19 @@ struct IndexerArgs {
   Positions qpos;
 };
 size_t indexer_workspace_bytes(int B, int Tq, int N, int k);
+// Lightning-Indexer scores (score.hip) into the top-k workspace: the score
+// rows, and on the split path the key histogram and the tile counters, both
+// cleared beforehand.  nv_max: largest visible count over the rows.
+constexpr int kScoreHistBins = 4096;   // top-12-bit key histogram bins
+struct ScoreBuffers {
+  float* scores;          // [R, Np]
+  int64_t Np;
+  uint32_t* hist;         // [R, kScoreHistBins] or null
+  uint32_t* tile_ctr;     // [R, 16 * 32] or null
+  bool split;
+};
+hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, int64_t nv_max,
+                                 hipStream_t st);
 hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st);
 
 // ---------------------------------------------------------------- attention

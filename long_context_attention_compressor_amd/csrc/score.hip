@@ -1,0 +1,494 @@
+// score.hip -- Lightning-Indexer scores.
+//
+// QbitAI rewrite (futuo-fx-trading.com), lightning indexer + top-k step: a
+// light indexer scores every compressed KV block against each query token;
+// "深度解析 DeepSeek-V4", CSA Step 2 Select.  Score of entry j for query t
+// (visible only when j < floor(t/m), strict causality):
+//     s[j] = sum_h w[h] * max(0, q[h] . K[j]).
+//
+// Score kernel (bf16).  One query's H_I x d_I block against 32 keys is one
+// tile of v_mfma_f32_32x32x16_bf16 per (32 heads, 16 dims): the heads are the
+// M side (A operand, kept in VGPRs for the whole sweep), the keys the N side
+// (B operand, streamed from HBM), the indexer dim the K side.  Because the
+// contraction order is free, each lane reads one contiguous half-row of its
+// key (d_I bytes), so a wave consumes whole 128-byte lines.  The ReLU and the
+// w-weighted head sum run on the accumulator in place: a lane holds one key
+// and 16 of the 32 heads, so one cross-half shuffle finishes the head sum.
+// Scores go to workspace as fp32.
+//
+#include <algorithm>
+
+#include "lac_internal.h"
+
+namespace lac {
+
+namespace {
+
+constexpr int kHistBins = kScoreHistBins;
+
+struct ScoreArgs {
+  const void* q;
+  const float* w;
+  const void* K;
+  float* scores;          // [R, Np]
+  int B, Tq, HI, dI, N, m;
+  int64_t Np;
+  int tiles_per_wave;     // 32-key tiles per wave (static schedule)
+  uint32_t* hist;         // [R, kHistBins] 12-bit key histogram (split path) or null
+  uint32_t* tile_ctr;     // [R, 16 * 32] zeroed tile counters (dynamic schedule) or null
+  int n_static;           // dynamic schedule: strided tiles per wave before the counters
+  int n_groups;           // dynamic schedule: counters per row (<= 16)
+  Positions qpos;
+};
+
+// ---------------------------------------------------------------- fp32 scores (VALU)
+__global__ void __launch_bounds__(256) score_f32_kernel(ScoreArgs a) {
+  extern __shared__ float sq[];   // [HI * dI] query + [HI] weights
+  const int row = blockIdx.y;
+  const int b = row / a.Tq, i = row - b * a.Tq;
+  const int64_t t = (int64_t)a.qpos.v[b] + i;
+  const int64_t nv = n_visible(t, a.N, a.m);
+  const float* q = static_cast<const float*>(a.q) + (int64_t)row * a.HI * a.dI;
+  for (int e = threadIdx.x; e < a.HI * a.dI; e += blockDim.x) sq[e] = q[e];
+  for (int e = threadIdx.x; e < a.HI; e += blockDim.x) sq[a.HI * a.dI + e] = a.w[(int64_t)row * a.HI + e];
+  __syncthreads();
+  const int64_t j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= nv) return;
+  const float* kr = static_cast<const float*>(a.K) + ((int64_t)b * a.N + j) * a.dI;
+  float s = 0.f;
+  for (int h = 0; h < a.HI; ++h) {
+    float dot = 0.f;
+    for (int c = 0; c < a.dI; ++c) dot = fmaf(sq[h * a.dI + c], kr[c], dot);
+    s = fmaf(sq[a.HI * a.dI + h], fmaxf(dot, 0.f), s);
+  }
+  a.scores[row * a.Np + j] = s;
+  if (a.hist) atomicAdd(&a.hist[(int64_t)row * kHistBins + (score_key(s) >> 20)], 1u);
+}
+
+// ---------------------------------------------------------------- bf16 scores (MFMA)
+// Block = 4 waves.  RW waves along rows (each with QPW consecutive queries of
+// one sequence), 4/RW waves along keys.  Grid: x = key chunks, y = row groups.
+//
+// Keys reach the MFMA through a per-wave LDS tile: every global load
+// instruction reads 1 KB of consecutive key rows (fully used 128-byte lines),
+// written to LDS with the 16-byte chunks of each row XOR-swizzled by the row
+// index, so the MFMA-layout reads (one chunk of 32 different rows per half
+// wave) are free of bank conflicts.  The next tile is loaded into VGPRs while
+// the current one is consumed from LDS.
+template <int HT, int KS, int QPW, int RW, bool DYN>
+__global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
+  constexpr int kRowsPerBlock = RW * QPW;
+  constexpr int KW = 4 / RW;
+  constexpr int dI = KS * 16;
+  constexpr int HI = HT * 32;
+  constexpr int CH = dI / 8;                 // 16-byte chunks per key row
+  constexpr int ROWB = dI * 2;               // bytes per key row
+  constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
+  constexpr int NLD = TILEB / 1024;          // 1 KB load instructions per tile
+  __shared__ float sw[kRowsPerBlock][HI];
+  __shared__ __align__(16) uint8_t ktile[4][TILEB];
+  __shared__ uint32_t lhist[kHistBins];
+  const int wave = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int hf = l >> 5, ln = l & 31;
+  const int wr = wave % RW, wk = wave / RW;
+  const bool do_hist = a.hist != nullptr;
+
+  // Rows of this block: consecutive queries of one sequence.
+  const int groups_per_seq = (a.Tq + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int b = blockIdx.y / groups_per_seq;
+  const int i0 = (blockIdx.y - b * groups_per_seq) * kRowsPerBlock;
+  const int n_rows_blk = min(kRowsPerBlock, a.Tq - i0);
+  const int64_t t_last = (int64_t)a.qpos.v[b] + i0 + n_rows_blk - 1;
+  const int64_t nv_max = n_visible(t_last, a.N, a.m);
+
+  // The head weights are requested first: loads complete in order, so the
+  // LDS store of w below does not wait for the key tiles requested after it.
+  constexpr int kWPer = (kRowsPerBlock * HI + 255) / 256;
+  float wreg[kWPer];
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    const int rr = e / HI, h = e - rr * HI;
+    const int i = min(i0 + rr, a.Tq - 1);
+    wreg[u] = e < kRowsPerBlock * HI ? a.w[((int64_t)b * a.Tq + i) * HI + h] : 0.f;
+  }
+
+  // Wave gw of the row's nw key waves takes tiles gw, gw + nw, gw + 2nw, ...:
+  // at any moment the waves of a row stream one contiguous stretch of keys,
+  // which spreads their loads over all memory channels.
+  const int64_t gw = (int64_t)blockIdx.x * KW + wk, nw = (int64_t)gridDim.x * KW;
+  const int64_t n_tiles = (nv_max + 31) / 32;
+  const int64_t n_mine = gw < n_tiles ? std::min<int64_t>(a.tiles_per_wave, (n_tiles - gw + nw - 1) / nw) : 0;
+  // Dynamic schedule: the one-query decode shape with tile counters (two
+  // stages per wave); otherwise each wave takes its n_mine strided tiles.
+  constexpr bool dynamic = DYN && QPW == 1;
+  uint32_t* ctr = dynamic ? a.tile_ctr + ((int64_t)b * a.Tq + i0) * (16 * 32) : nullptr;
+
+  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
+  uint8_t* kt = ktile[wave];
+  // Load instruction u of a tile: lane l takes 16 bytes at u*1024 + l*16 of
+  // the tile in LDS order, i.e. row kk, swizzled chunk slot cs, which holds
+  // the row's chunk cs ^ (kk % CH).  The loads go through a buffer resource
+  // based at the tile and bounded by its rows below N, so rows past the end
+  // read as zeros and a lane's offsets are the same for every tile.
+  auto load_tile = [&](int64_t tile_any, uint4* st) {
+    // (the tile is the same in every lane: say so, so that the resource
+    // stays in scalar registers)
+    const int64_t tile = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tile_any >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((int)tile_any));
+    const int64_t rows = a.N - tile * 32;
+    const int nrec = rows >= 32 ? TILEB : rows > 0 ? (int)rows * ROWB : 0;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Kb + tile * TILEB), 0, nrec,
+                                                        0x00020000);
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) {
+      const int o = u * 1024 + l * 16;
+      const int kk = o / ROWB, cs = (o % ROWB) / 16;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, kk * ROWB + ((cs ^ (kk % CH)) * 16), 0, 2);
+      st[u] = make_uint4(v.x, v.y, v.z, v.w);
+    }
+  };
+  auto store_tile = [&](const uint4* st) {
+#pragma unroll
+    for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
+  };
+
+  // The first tiles and the query fragments are requested before anything
+  // else, so their latency overlaps the set-up below.  PF tiles are in
+  // flight per wave (two for the one-query decode shape, whose registers
+  // allow it); the stages alternate.
+  constexpr int PF = QPW == 1 ? 2 : 1;
+  uint4 stage[PF][NLD];
+  // (Unconditional, so that the compiler can count them: a tile past the end
+  // reads clamped rows and is not used.)
+#pragma unroll
+  for (int f = 0; f < PF; ++f) load_tile(gw + f * nw, stage[f]);
+  // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
+  bf16x8 qf[QPW][HT][KS];
+  int64_t nv_row[QPW];
+  {
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      const int rr = wr * QPW + qi;
+      const int i = min(i0 + rr, a.Tq - 1);
+      nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                           ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 256 * u;
+    if (e < kRowsPerBlock * HI) sw[e / HI][e % HI] = wreg[u];
+  }
+  if (do_hist)
+    for (int e = threadIdx.x; e < kHistBins; e += 256) lhist[e] = 0u;
+  __syncthreads();
+
+  // Work on one tile held in LDS: scores of the wave's query rows.
+  auto compute = [&](int64_t tile) {
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = hf * (CH / 2) + s;
+      kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+    }
+    const int64_t j = tile * 32 + ln;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      const int rr = wr * QPW + qi;
+      float part = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], relu(acc[v]), part);
+      }
+      part += __shfl_xor(part, 32);
+      const bool live = hf == 0 && j < nv_row[qi];
+      if (live) a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
+      if (do_hist) hist_add(lhist, live, score_key(part) >> 20);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // LDS reads of this tile done
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto stage_in = [&](const uint4* st) {
+    store_tile(st);
+    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): LDS writes done
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  if constexpr (dynamic) {
+    // The first n_static tiles of a wave are its strided ones; the rest of
+    // the row's tiles are handed out by counters, so that waves that stream
+    // faster take more of them and all finish together.  Each of the row's
+    // n_groups counters (one per group of eight consecutive blocks, which
+    // spans every XCD) serves the tiles n_static * nw + c * n_groups + g:
+    // a device-scope atomic on one address costs tens of nanoseconds, so
+    // the load is spread over several addresses and only the tail of the
+    // sweep is dynamic.  Stage f holds tile t[f] (the wave's sequence
+    // number k[f]); its ticket r[f], drawn by lane 0 when stage f was last
+    // refilled, names the tile that refills it next, two tiles later, so the
+    // atomic's latency is hidden like a load's.
+    const int g = (int)((blockIdx.x >> 3) % (unsigned)a.n_groups);
+    uint32_t* gctr = ctr + 32 * g;
+    const int64_t ns = a.n_static, dyn0 = ns * nw;
+    auto tile_of = [&](int64_t k, uint32_t ticket) {
+      return k < ns ? gw + k * nw : dyn0 + (int64_t)ticket * a.n_groups + g;
+    };
+    int64_t t[2] = {gw, gw + nw};
+    uint32_t r[2] = {0u, 0u};
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      if (l == 0 && t[f] < n_tiles && f + 2 >= ns) r[f] = atomicAdd(gctr, 1u);
+    int64_t k = 0;                 // sequence number of the tile in stage 0
+    for (;; k += 2) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        if (t[f] >= n_tiles) goto done;
+        stage_in(stage[f]);
+        const int64_t kn = k + f + 2;
+        const int64_t nt = tile_of(kn, kn >= ns ? __builtin_amdgcn_readfirstlane(r[f]) : 0u);
+        if (nt < n_tiles) {
+          load_tile(nt, stage[f]);
+          if (l == 0 && kn + 2 >= ns) r[f] = atomicAdd(gctr, 1u);
+        }
+        compute(t[f]);
+        t[f] = nt;
+      }
+    }
+  done:;
+  } else if (n_mine > 0) {
+    for (int64_t it = 0; it < n_mine; it += PF) {
+#pragma unroll
+      for (int f = 0; f < PF; ++f) {
+        if (it + f < n_mine) {
+          const int64_t tile = gw + (it + f) * nw;
+          stage_in(stage[f]);
+          if (it + f + PF < n_mine) load_tile(tile + PF * nw, stage[f]);
+          compute(tile);
+        }
+      }
+    }
+  }
+
+  if (do_hist) {
+    __syncthreads();
+    // Only the decode shape (one row per block) keeps a histogram.
+    uint32_t* gh = a.hist + ((int64_t)b * a.Tq + i0) * kHistBins;
+    for (int e = threadIdx.x; e < kHistBins; e += 256)
+      if (lhist[e]) atomicAdd(&gh[e], lhist[e]);
+  }
+}
+
+// Prefill score kernel.  A block of eight waves holds 8 * QPW consecutive
+// queries of one sequence (QPW per wave, fragments in VGPRs) and sweeps all
+// keys the block can see, one 32-key tile at a time: the 512 threads load a
+// tile cooperatively (one 16-byte load each, XOR-swizzled into LDS, two
+// tiles ahead in registers) and every wave reads it from LDS, so each key
+// tile crosses HBM once per 8 * QPW queries and all waves of a compute unit
+// share it.
+template <int HT, int KS, int QPW>
+__global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
+  constexpr int QB = 8 * QPW;                // queries per block
+  constexpr int dI = KS * 16;
+  constexpr int HI = HT * 32;
+  constexpr int CH = dI / 8;                 // 16-byte chunks per key row
+  constexpr int ROWB = dI * 2;               // bytes per key row
+  constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
+  constexpr int LOADERS = TILEB / 16;        // threads that load one chunk each
+  __shared__ float sw[QB][HI];
+  __shared__ __align__(16) uint8_t ktile[2][TILEB];
+  const int wave = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int hf = l >> 5, ln = l & 31;
+  const int blocks_per_seq = (a.Tq + QB - 1) / QB;
+  const int b = blockIdx.x / blocks_per_seq;
+  const int i0 = (blockIdx.x - b * blocks_per_seq) * QB;
+  const int n_rows_blk = min(QB, a.Tq - i0);
+  const int64_t t_last = (int64_t)a.qpos.v[b] + i0 + n_rows_blk - 1;
+  const int64_t nv_max = n_visible(t_last, a.N, a.m);
+  const int64_t n_tiles = (nv_max + 31) / 32;
+
+  // Head weights first (loads complete in order; see the decode kernel).
+  constexpr int kWPer = (QB * HI + 511) / 512;
+  float wreg[kWPer];
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 512 * u;
+    const int rr = e / HI, h = e - rr * HI;
+    const int i = min(i0 + rr, a.Tq - 1);
+    wreg[u] = e < QB * HI ? a.w[((int64_t)b * a.Tq + i) * HI + h] : 0.f;
+  }
+
+  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
+  // Loader thread t takes 16 bytes at t*16 of the tile in LDS order: row kk,
+  // swizzled slot cs, which holds the row's chunk cs ^ (kk % CH).
+  const bool loader = (int)threadIdx.x < LOADERS;
+  const int lo_off = threadIdx.x * 16;
+  const int lo_kk = lo_off / ROWB, lo_cs = (lo_off % ROWB) / 16;
+  auto load_tile = [&](int64_t tile) {
+    int64_t j = tile * 32 + lo_kk;
+    if (j > a.N - 1) j = a.N - 1;
+    return ld_stream16(Kb + j * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16));
+  };
+  uint4 stage[2];
+  if (loader) {
+    if (n_tiles > 0) stage[0] = load_tile(0);
+    if (n_tiles > 1) stage[1] = load_tile(1);
+  }
+
+  // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
+  // Scores are written through a buffer resource per query row: a masked
+  // lane (hidden key, second half-wave, row past Tq) stores out of range and
+  // the store is dropped, so every store instruction is issued unconditionally
+  // and the memory counter stays exact for the prefetch waits.
+  bf16x8 qf[QPW][HT][KS];
+  int64_t nv_row[QPW];
+  __amdgpu_buffer_rsrc_t srow[QPW];
+#pragma unroll
+  for (int qi = 0; qi < QPW; ++qi) {
+    const int rr = wave * QPW + qi;
+    const int i = min(i0 + rr, a.Tq - 1);
+    nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
+    srow[qi] = __builtin_amdgcn_make_buffer_rsrc(a.scores + ((int64_t)b * a.Tq + i) * a.Np, 0,
+                                                 (int)(nv_row[qi] * 4), 0x00020000);
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const __bf16* qp = static_cast<const __bf16*>(a.q) +
+                         ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
+#pragma unroll
+      for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kWPer; ++u) {
+    const int e = threadIdx.x + 512 * u;
+    if (e < QB * HI) sw[e / HI][e % HI] = wreg[u];
+  }
+
+  // One step per tile; the loop is unrolled by two so that the staging
+  // registers and LDS buffers are indexed statically (a runtime index would
+  // force the prefetch to complete when it is issued).
+  auto step = [&](int64_t tile, uint4& st, uint8_t* kt) {
+    if (loader) {
+      *reinterpret_cast<uint4*>(kt + lo_off) = st;
+      if (tile + 2 < n_tiles) st = load_tile(tile + 2);
+    }
+    __syncthreads();             // tile visible; every wave is done with tile - 1
+    bf16x8 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int c = hf * (CH / 2) + s;
+      kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+    }
+    const int64_t j = tile * 32 + ln;
+#pragma unroll
+    for (int qi = 0; qi < QPW; ++qi) {
+      const int rr = wave * QPW + qi;
+      float part = 0.f;
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) {
+        f32x16 acc = {};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], relu(acc[v]), part);
+      }
+      part += __shfl_xor(part, 32);
+      const int off = hf == 0 ? (int)j * 4 : 0x7fffffff;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[qi], off, 0, 0);
+    }
+  };
+  for (int64_t tile = 0; tile < n_tiles; tile += 2) {
+    step(tile, stage[0], ktile[0]);
+    if (tile + 1 < n_tiles) step(tile + 1, stage[1], ktile[1]);
+  }
+}
+
+template <int HT, int KS, int QPW, int RW>
+hipError_t launch_score(const ScoreArgs& sa, int64_t key_chunks, int row_groups, hipStream_t st) {
+  if (sa.tile_ctr != nullptr)
+    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, true>), dim3((unsigned)key_chunks, row_groups),
+                       dim3(256), 0, st, sa);
+  else
+    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, false>), dim3((unsigned)key_chunks, row_groups),
+                       dim3(256), 0, st, sa);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, int64_t nv_max,
+                                 hipStream_t st) {
+  const int R = a.B * a.Tq;
+  if (R == 0 || nv_max <= 0) return hipSuccess;
+  hipError_t err = hipSuccess;
+  ScoreArgs sa{};
+  sa.q = a.q; sa.w = a.w; sa.K = a.K; sa.scores = sb.scores;
+  sa.B = a.B; sa.Tq = a.Tq; sa.HI = a.HI; sa.dI = a.dI; sa.N = a.N; sa.m = a.m;
+  sa.Np = sb.Np; sa.qpos = a.qpos; sa.hist = sb.hist;
+  sa.tile_ctr = sb.tile_ctr;
+  {
+    TimedLaunch tl(kKernelIndexerScore, st);
+    if (a.fmt == kF32) {
+      const size_t lds = (size_t)(a.HI * a.dI + a.HI) * 4;
+      hipLaunchKernelGGL(score_f32_kernel, dim3((unsigned)((nv_max + 255) / 256), R), dim3(256),
+                         lds, st, sa);
+      err = hipGetLastError();
+    } else {
+      const int64_t n_tiles = (nv_max + 31) / 32;
+      const int HT = a.HI / 32, KS = a.dI / 16;
+      if (a.Tq >= 8 && !sb.split) {
+        // Prefill: a block of eight waves shares each key tile among 8 * QPW
+        // queries and sweeps all the keys they see.
+#define LAC_SCORE_CASE(ht, ks, qpw)                                                        \
+  if (HT == ht && KS == ks) {                                                              \
+    const int blocks = a.B * ((a.Tq + 8 * qpw - 1) / (8 * qpw));                           \
+    hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw>), dim3(blocks), dim3(512), 0, st, sa); \
+    err = hipGetLastError();                                                               \
+  }
+        LAC_SCORE_CASE(1, 4, 2) LAC_SCORE_CASE(1, 8, 2) LAC_SCORE_CASE(2, 4, 2)
+        LAC_SCORE_CASE(2, 8, 2) LAC_SCORE_CASE(4, 4, 2) LAC_SCORE_CASE(4, 8, 1)
+#undef LAC_SCORE_CASE
+      } else {
+        // Decode: one query per block, 4 waves split the keys.  The grid is
+        // one round of the 512 resident blocks (two blocks of 4 waves per
+        // compute unit at this kernel's register use), so no partial second
+        // round trails the sweep.
+        const int64_t per_row = std::max<int64_t>(1, 512 / R);
+        sa.tiles_per_wave = (int)std::max<int64_t>(2, (n_tiles + 4 * per_row - 1) / (4 * per_row));
+        const int64_t chunks = (n_tiles + 4 * sa.tiles_per_wave - 1) / (4 * sa.tiles_per_wave);
+        // dynamic schedule: about the last quarter of the sweep
+        sa.n_static = std::max(2, sa.tiles_per_wave * 3 / 4);
+        sa.n_groups = (int)std::min<int64_t>(16, std::max<int64_t>(1, chunks / 8));
+        const int groups = a.B * a.Tq;
+#define LAC_SCORE_CASE(ht, ks) \
+  if (HT == ht && KS == ks) err = launch_score<ht, ks, 1, 1>(sa, chunks, groups, st);
+        LAC_SCORE_CASE(1, 4) LAC_SCORE_CASE(1, 8) LAC_SCORE_CASE(2, 4) LAC_SCORE_CASE(2, 8)
+        LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
+#undef LAC_SCORE_CASE
+      }
+    }
+    if (err != hipSuccess) return err;
+  }
+
+  return hipSuccess;
+}
+
+}  // namespace lac
