@@ -154,17 +154,15 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
   };
 
-  // The first tiles and the query fragments are requested before anything
+  // The query fragments and the first tiles are requested before anything
   // else, so their latency overlaps the set-up below.  PF tiles are in
   // flight per wave (two for the one-query decode shape, whose registers
   // allow it); the stages alternate.
   constexpr int PF = QPW == 1 ? 2 : 1;
   uint4 stage[PF][NLD];
-  // (Unconditional, so that the compiler can count them: a tile past the end
-  // reads clamped rows and is not used.)
-#pragma unroll
-  for (int f = 0; f < PF; ++f) load_tile(gw + f * nw, stage[f]);
-  // Query fragments: lane (ln, hf) holds head ht*32+ln, dims hf*dI/2 + s*8 .. +8.
+  // Query fragments first: lane (ln, hf) holds head ht*32+ln, dims
+  // hf*dI/2 + s*8 .. +8.  (They come from L2 for all but the first waves of
+  // a row, so the first tile's compute need not wait for the second tile.)
   bf16x8 qf[QPW][HT][KS];
   int64_t nv_row[QPW];
   {
@@ -182,6 +180,10 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
       }
     }
   }
+  // (Unconditional, so that the compiler can count them: a tile past the end
+  // reads zeros and is not used.)
+#pragma unroll
+  for (int f = 0; f < PF; ++f) load_tile(gw + f * nw, stage[f]);
 
 #pragma unroll
   for (int u = 0; u < kWPer; ++u) {
