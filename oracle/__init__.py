@@ -69,6 +69,9 @@ def _load():
     lib.lo_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, i32,
                                     vp, vp]
     lib.lo_index_scores.restype = i32
+    lib.lo_index_scores2.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp,
+                                     i32, vp, vp]
+    lib.lo_index_scores2.restype = i32
     lib.lo_topk.argtypes = [vp, i32, i32, vp, i32, vp]
     lib.lo_topk.restype = i32
     lib.lo_attend.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, vp,
@@ -180,16 +183,18 @@ def _rows(rows, B, Tq):
     return np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
 
 
-def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None):
-    """-> (scores float64 [n_rows, N] with -inf where not visible, nvis int32 [n_rows])."""
+def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None, k_dtype=None):
+    """-> (scores float64 [n_rows, N] with -inf where not visible, nvis int32 [n_rows]).
+    q is stored in dtype, K in k_dtype (default dtype; the mixed code with no
+    rotated dims means E4M3 keys)."""
     rows = _rows(rows, B, Tq)
     n = rows.shape[0]
     scores = np.empty((n, N), np.float64)
     nvis = np.empty(n, np.int32)
     w = np.ascontiguousarray(w, np.float32)
     qpos = _i64(qpos0, B)      # held until the call returns
-    rc = _load().lo_index_scores(_p(q), _p(w), _p(K), dtype, B, Tq, HI, dI, N,
-                                 _p(qpos), m, _p(rows), n, _p(scores), _p(nvis))
+    rc = _load().lo_index_scores2(_p(q), dtype, _p(w), _p(K), dtype if k_dtype is None else k_dtype,
+                                  B, Tq, HI, dI, N, _p(qpos), m, _p(rows), n, _p(scores), _p(nvis))
     if rc:
         raise ValueError(f"lo_index_scores rejected its arguments ({rc})")
     return scores, nvis

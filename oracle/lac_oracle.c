@@ -264,14 +264,17 @@ static int64_t n_visible(int64_t t, int N, int m) {
 }
 
 /* rows: n_rows pairs (b, i).  scores: [n_rows, N]; entries not visible are
- * set to -inf.  nvis (optional): [n_rows]. */
-int lo_index_scores(const void* q, const float* w, const void* K, int dtype, int B, int Tq,
-                    int HI, int dI, int N, const int64_t* qpos0, int m,
-                    const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {
+ * set to -inf.  nvis (optional): [n_rows].  q is stored in dtype, K in
+ * k_dtype (the same formats; LO_MIXED with no rotated dims is E4M3 keys). */
+int lo_index_scores2(const void* q, int dtype, const float* w, const void* K, int k_dtype,
+                     int B, int Tq, int HI, int dI, int N, const int64_t* qpos0, int m,
+                     const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {
     (void)B;
     if (dtype != LO_F32 && dtype != LO_BF16 && dtype != LO_F64) return 2;
+    if (k_dtype != LO_F32 && k_dtype != LO_BF16 && k_dtype != LO_F64 && k_dtype != LO_MIXED)
+        return 2;
     if (dI < 1 || dI > 1024) return 3;
-    int64_t rb = row_bytes(dtype, dI, 0);
+    int64_t rb = row_bytes(dtype, dI, 0), krb = row_bytes(k_dtype, dI, 0);
     double* qd = malloc(sizeof(double) * (size_t)n_rows * HI * dI);
     int rr, h;
     for (rr = 0; rr < n_rows; ++rr) {
@@ -290,7 +293,7 @@ int lo_index_scores(const void* q, const float* w, const void* K, int dtype, int
         if (j >= n_visible(qpos0[b] + i, N, m)) { scores[task] = -INFINITY; continue; }
         double kd[1024];
         int c, hh;
-        decode_row((const uint8_t*)K + ((int64_t)b * N + j) * rb, dtype, dI, 0, kd);
+        decode_row((const uint8_t*)K + ((int64_t)b * N + j) * krb, k_dtype, dI, 0, kd);
         double s = 0.0;
         for (hh = 0; hh < HI; ++hh) {
             const double* qh = qd + ((int64_t)r2 * HI + hh) * dI;
@@ -302,6 +305,13 @@ int lo_index_scores(const void* q, const float* w, const void* K, int dtype, int
     }
     free(qd);
     return 0;
+}
+
+int lo_index_scores(const void* q, const float* w, const void* K, int dtype, int B, int Tq,
+                    int HI, int dI, int N, const int64_t* qpos0, int m,
+                    const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {
+    return lo_index_scores2(q, dtype, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows, n_rows,
+                            scores, nvis);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -40,6 +40,30 @@ def test_scores_match_a_library_expression_and_causality():
             assert np.isneginf(s[rr, nv[rr]:]).all()
 
 
+def test_scores_with_e4m3_keys_use_the_decoded_key_values():
+    # Keys stored as E4M3 codes (the mixed row format with no rotated dims)
+    # score exactly as their decoded values would: checked against numpy's
+    # expression of the indexer over those values, queries in bf16.
+    B, Tq, HI, dI, N, m = 2, 5, 4, 32, 24, 4
+    qpos0 = (30, 99)
+    rng = np.random.default_rng(7)
+    q = oracle.bf16_encode(rng.standard_normal((B, Tq, HI, dI)))
+    codes = oracle.e4m3_encode(rng.standard_normal((B, N, dI)) * 2.0)
+    w = rng.uniform(0, 1, (B, Tq, HI)).astype(np.float32)
+    s, nv = oracle.index_scores(q, w, codes, oracle.BF16, B, Tq, HI, dI, N, np.array(qpos0), m,
+                                k_dtype=oracle.MIXED)
+    qd = oracle.bf16_decode(q)
+    kd = oracle.e4m3_decode(codes)
+    dots = np.einsum("bthc,bjc->btjh", qd, kd)
+    ref = (np.maximum(dots, 0.0) * w.astype(np.float64)[:, :, None, :]).sum(-1)
+    for b in range(B):
+        for i in range(Tq):
+            rr = b * Tq + i
+            assert nv[rr] == min(N, (qpos0[b] + i) // m)
+            assert np.allclose(s[rr, : nv[rr]], ref[b, i, : nv[rr]], rtol=1e-13, atol=1e-12)
+            assert np.isneginf(s[rr, nv[rr]:]).all()
+
+
 def test_worked_example_from_the_pages():
     g = json.load(open(os.path.join(GOLD, "worked_example_select.json")))
     s = np.array([g["scores"]], np.float64)
