@@ -10,7 +10,9 @@ tokens/s (4 per step) with the algorithmic HBM GB/s beside it.  Three
 independent cache sets rotate so that a step never finds its 294 MB working
 set in the 256 MB Infinity Cache.
 
-Other workloads (--workload): csa_decode_128k (32 sequences at 131072),
+Other workloads (--workload): pair_decode_1m_e4m3_indexer (the same step with
+the indexer keys stored as E4M3, one byte per dim), csa_decode_128k (32
+sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
 hca_prefill_8k (8192 tokens; TFLOP/s).
 
@@ -69,10 +71,12 @@ class PairDecode:
     name = "pair_decode_1m"
     unit = "tokens/s"
 
+    ki_fmt = "bf16"
+
     def __init__(self, lac, synth, dev, sets, seed=4, B=4, ctx=1 << 20):
         self.lac, self.B, self.ctx = lac, B, ctx
-        self.sets = [synth.pair_decode(seed=seed + 1000 * s, B=B, ctx=ctx, device=dev)
-                     for s in range(sets)]
+        self.sets = [synth.pair_decode(seed=seed + 1000 * s, B=B, ctx=ctx, ki_fmt=self.ki_fmt,
+                                       device=dev) for s in range(sets)]
         c = self.sets[0]
         self.c = c
         self.idx = torch.empty((B, 1, c["k"]), dtype=torch.int32, device=dev)
@@ -115,22 +119,26 @@ class PairDecode:
     def bytes_per_step(self):
         c = self.c
         row = c["D"] - c["r"] + 2 * c["r"]
-        per_seq = (c["N"] * c["dI"] * 2 + c["HI"] * c["dI"] * 2 + c["HI"] * 4   # indexer
+        kb = 1 if self.ki_fmt == "mixed" else 2                                   # key bytes/dim
+        per_seq = (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * 2 + c["HI"] * 4  # indexer
                    + c["k"] * row + c["Nh"] * row + 2 * c["W"] * row               # gathers
                    + 2 * c["H"] * c["D"] * 2 * 2)                                   # q, out
         compress = ((c["m"] * c["D"] + c["m"] * c["dI"] + c["m_hca"] * c["D"]) * 2 * 2
-                    + 2 * row + c["dI"] * 2)
+                    + 2 * row + c["dI"] * kb)
         return self.B * (per_seq + compress)
 
     def indexer_bytes_per_launch(self):
         c = self.c
-        return self.B * (c["N"] * c["dI"] * 2 + c["HI"] * c["dI"] * 2 + c["HI"] * 4)
+        kb = 1 if self.ki_fmt == "mixed" else 2
+        return self.B * (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * 2 + c["HI"] * 4)
 
     def config(self):
         c = self.c
         return {"workload": self.name, "batch": self.B, "ctx": self.ctx, "topk": c["k"],
                 "window": c["W"], "heads": c["H"], "kv_dim": c["D"], "rope_dims": c["r"],
-                "indexer": f"{c['HI']}x{c['dI']} bf16", "csa_entries": c["N"],
+                "indexer": (f"{c['HI']}x{c['dI']} bf16" if self.ki_fmt == "bf16" else
+                            f"{c['HI']}x{c['dI']}, bf16 queries, e4m3 keys"),
+                "csa_entries": c["N"],
                 "hca_entries": c["Nh"], "kv_format": "e4m3 + bf16 rope dims (576 B/entry)",
                 "cache_sets": len(self.sets)}
 
@@ -152,13 +160,13 @@ class PairDecode:
         ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16", "mixed", 1,
                                               c["m"], c["D"], c["m"], c["r"], 1e4, ctx - c["m"])
         KI.view(np.uint8)[:, N - 1:] = chain.compress_store(
-            h["new_kI"], h["new_zI"], "bf16", "bf16", 1, c["m"], c["dI"], c["m"], 0, 1e4,
+            h["new_kI"], h["new_zI"], "bf16", self.ki_fmt, 1, c["m"], c["dI"], c["m"], 0, 1e4,
             ctx - c["m"])
         hkv[:, Nh - 1:] = chain.compress_store(h["new_kv_hca"], h["new_z_hca"], "bf16", "mixed",
                                                1, c["m_hca"], c["D"], c["m_hca"], c["r"], 1e4,
                                                ctx - c["m_hca"])
         idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, "bf16", 1, 1, c["HI"], c["dI"], N, ctx,
-                                     c["m"], c["k"])
+                                     c["m"], c["k"], k_fmt=self.ki_fmt)
         oracle.attend(h["q_csa"], oracle.BF16, ckv, oracle.MIXED, N, 0, idx, c["k"], c["m"],
                       h["raw_csa"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
                       c["r"], 1e4, ctx)
@@ -170,6 +178,12 @@ class PairDecode:
                 "sample": "the full decode step (compress newest blocks, index 262144 entries, "
                           "top-2048, CSA + HCA attention, 64 heads) of 1 of the 4 sequences, "
                           "cache set 0"}
+
+
+class PairDecodeE4M3Indexer(PairDecode):
+    """pair_decode_1m with the indexer keys stored as E4M3 (d_I bytes per key)."""
+    name = "pair_decode_1m_e4m3_indexer"
+    ki_fmt = "mixed"
 
 
 class CsaDecode(PairDecode):
@@ -357,7 +371,8 @@ class HcaPrefill(ChunkPrefill):
                           "queries, FLOPs scaled by 128/8192"}
 
 
-WORKLOADS = {w.name: w for w in (PairDecode, CsaDecode, ChunkPrefill, HcaPrefill)}
+WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, CsaDecode, ChunkPrefill,
+                                   HcaPrefill)}
 
 
 def main():

@@ -125,15 +125,23 @@ int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, v
  * ascending); the chosen indices are written in ascending index order and
  * the remaining slots hold -1.
  *
- *   q_idx       [B, Tq, H_I, d_I] in dtype (LAC_F32 | LAC_BF16)
+ *   q_idx       [B, Tq, H_I, d_I] in dtype (LAC_F32 | LAC_BF16), or bf16 when
+ *               dtype is LAC_KV_E4M3_ROPE_BF16
  *   w           [B, Tq, H_I] float32
- *   k_idx       [B, N, d_I] in dtype
+ *   k_idx       [B, N, d_I] in dtype; with LAC_KV_E4M3_ROPE_BF16, E4M3 keys of
+ *               d_I bytes (the mixed row format with no rotated dims, as
+ *               csa_compress writes it with rope_dims = 0).  A low-precision
+ *               indexer key cache: [P2] runs the indexer's QK path in FP4
+ *               (CSA Step 2 Select; section "FP4 Quantization-Aware
+ *               Training", whose FP4 block scales dequantize losslessly into
+ *               FP8).  Here the keys are stored as unscaled E4M3, widened
+ *               exactly to bf16, and scored as above.
  *   topk_idx    [B, Tq, k] int32, output
  *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
  *               -inf in padded slots); may be NULL
  *   workspace   >= indexer_topk_workspace_size(B, Tq, N, k) bytes
- * LAC_BF16 needs H_I in {32, 64, 128} and d_I in {64, 128} (bf16 MFMA);
- * LAC_F32 needs H_I * d_I <= 8192.  1 <= k <= 8192.
+ * LAC_BF16 and LAC_KV_E4M3_ROPE_BF16 need H_I in {32, 64, 128} and d_I in
+ * {64, 128} (bf16 MFMA); LAC_F32 needs H_I * d_I <= 8192.  1 <= k <= 8192.
  */
 size_t indexer_topk_workspace_size(int32_t B, int32_t Tq, int32_t N, int32_t k);
 int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32_t dtype,

@@ -154,16 +154,18 @@ def indexer_topk_workspace_size(B, Tq, N, k) -> int:
 
 def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
                  workspace=None, stream=None):
-    """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I].
+    """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I]
+    (the dtype of q_idx, or uint8 E4M3 codes with bf16 q_idx).
     Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""
     B, Tq, HI, dI = q_idx.shape
     N = k_idx.shape[1]
+    dt = LAC_KV_E4M3_ROPE_BF16 if k_idx.dtype == torch.uint8 else _fmt(q_idx)
     for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
         _need_dense(t, nm)
     if topk_idx is None:
         topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
     workspace = _workspace(workspace, indexer_topk_workspace_size(B, Tq, N, k), q_idx.device)
-    _check(lib.indexer_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), _fmt(q_idx), B, Tq, HI, dI, N,
+    _check(lib.indexer_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
                             _positions(q_pos0, B), m, k, _ptr(topk_idx), _ptr(topk_score),
                             _ptr(workspace), workspace.numel(), _stream(stream)))
     return topk_idx

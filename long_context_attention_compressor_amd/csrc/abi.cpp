@@ -230,14 +230,15 @@ int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32
                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream) {
   const char* fn = "indexer_topk";
   try {
-    if (dtype != LAC_F32 && dtype != LAC_BF16)
-      return fail(LAC_ERR_UNSUPPORTED, "%s: dtype must be LAC_F32 or LAC_BF16", fn);
+    if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16)
+      return fail(LAC_ERR_UNSUPPORTED, "%s: dtype must be LAC_F32, LAC_BF16 or LAC_KV_E4M3_ROPE_BF16",
+                  fn);
     if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
     if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
     if (m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
     if (k < 1 || k > 8192) return fail(LAC_ERR_INVALID, "%s: k = %d outside [1, 8192]", fn, k);
     if (H_I < 1 || d_I < 1) return fail(LAC_ERR_INVALID, "%s: H_I and d_I must be >= 1", fn);
-    if (dtype == LAC_BF16) {
+    if (dtype != LAC_F32) {
       if ((H_I != 32 && H_I != 64 && H_I != 128) || (d_I != 64 && d_I != 128))
         return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H_I in {32, 64, 128} and d_I in {64, 128}", fn);
     } else if ((int64_t)H_I * d_I > 8192) {

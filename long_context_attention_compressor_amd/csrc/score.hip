@@ -75,7 +75,7 @@ __global__ void __launch_bounds__(256) score_f32_kernel(ScoreArgs a) {
 // index, so the MFMA-layout reads (one chunk of 32 different rows per half
 // wave) are free of bank conflicts.  The next tile is loaded into VGPRs while
 // the current one is consumed from LDS.
-template <int HT, int KS, int QPW, int RW, bool DYN>
+template <int HT, int KS, int QPW, int RW, bool DYN, int KF>
 __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   constexpr int kRowsPerBlock = RW * QPW;
   constexpr int KW = 4 / RW;
@@ -84,7 +84,13 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   constexpr int CH = dI / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = dI * 2;               // bytes per key row
   constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
-  constexpr int NLD = TILEB / 1024;          // 1 KB load instructions per tile
+  // Keys in HBM: bf16 rows (2 d_I bytes) or E4M3 rows (d_I bytes), widened
+  // to the same bf16 layout in LDS.
+  constexpr int KROWB = KF == kMixed ? dI : ROWB;
+  constexpr int KTILEB = 32 * KROWB;
+  constexpr int NLD = KTILEB / 1024;         // 16-byte registers per lane per tile
+  constexpr int kLPR = dI / 8;               // E4M3: lanes per key (8 codes each)
+  constexpr int kRPI = 64 / kLPR;            // E4M3: keys per 8-byte load
   __shared__ float sw[kRowsPerBlock][HI];
   __shared__ __align__(16) uint8_t ktile[4][TILEB];
   __shared__ uint32_t lhist[kHistBins];
@@ -125,7 +131,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   constexpr bool dynamic = DYN && QPW == 1;
   uint32_t* ctr = dynamic ? a.tile_ctr + ((int64_t)b * a.Tq + i0) * (16 * 32) : nullptr;
 
-  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
+  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * KROWB;
   uint8_t* kt = ktile[wave];
   // Load instruction u of a tile: lane l takes 16 bytes at u*1024 + l*16 of
   // the tile in LDS order, i.e. row kk, swizzled chunk slot cs, which holds
@@ -138,20 +144,44 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     const int64_t tile = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tile_any >> 32)) << 32) |
                                    (uint32_t)__builtin_amdgcn_readfirstlane((int)tile_any));
     const int64_t rows = a.N - tile * 32;
-    const int nrec = rows >= 32 ? TILEB : rows > 0 ? (int)rows * ROWB : 0;
-    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Kb + tile * TILEB), 0, nrec,
+    const int nrec = rows >= 32 ? KTILEB : rows > 0 ? (int)rows * KROWB : 0;
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(Kb + tile * KTILEB), 0, nrec,
                                                         0x00020000);
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
-      const int o = u * 1024 + l * 16;
-      const int kk = o / ROWB, cs = (o % ROWB) / 16;
-      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, kk * ROWB + ((cs ^ (kk % CH)) * 16), 0, 2);
-      st[u] = make_uint4(v.x, v.y, v.z, v.w);
+      if constexpr (KF == kMixed) {
+        // two 8-byte loads: 8 codes (one bf16 chunk) of key kk8(h) each
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int j = 2 * u + h;
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (kRPI * j + l / kLPR) * dI + (l % kLPR) * 8, 0, 2);
+          if (h == 0) { st[u].x = v[0]; st[u].y = v[1]; } else { st[u].z = v[0]; st[u].w = v[1]; }
+        }
+      } else {
+        const int o = u * 1024 + l * 16;
+        const int kk = o / ROWB, cs = (o % ROWB) / 16;
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, kk * ROWB + ((cs ^ (kk % CH)) * 16), 0, 2);
+        st[u] = make_uint4(v.x, v.y, v.z, v.w);
+      }
     }
   };
   auto store_tile = [&](const uint4* st) {
 #pragma unroll
-    for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
+    for (int u = 0; u < NLD; ++u) {
+      if constexpr (KF == kMixed) {
+        // 8 E4M3 codes of key kk -> bf16 chunk c of its swizzled LDS row
+        // (exact widening); the lanes of one load cover whole rows, so each
+        // store instruction writes whole rows of the tile.
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kk = kRPI * (2 * u + h) + l / kLPR, c = l % kLPR;
+          *reinterpret_cast<uint4*>(kt + kk * ROWB + ((c ^ (kk % CH)) * 16)) =
+              h == 0 ? e4m3x8_to_bf16x8(st[u].x, st[u].y) : e4m3x8_to_bf16x8(st[u].z, st[u].w);
+        }
+      } else {
+        *reinterpret_cast<uint4*>(kt + u * 1024 + l * 16) = st[u];
+      }
+    }
   };
 
   // The query fragments and the first tiles are requested before anything
@@ -241,8 +271,8 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     // a device-scope atomic on one address costs tens of nanoseconds, so
     // the load is spread over several addresses and only the tail of the
     // sweep is dynamic.  Stage f holds tile t[f] (the wave's sequence
-    // number k[f]); its ticket r[f], drawn by lane 0 when stage f was last
-    // refilled, names the tile that refills it next, two tiles later, so the
+    // number k + f); its ticket r[f], drawn by lane 0 when stage f was last
+    // refilled, names the tile that refills it next, PF tiles later, so the
     // atomic's latency is hidden like a load's.
     const int g = (int)((blockIdx.x >> 3) % (unsigned)a.n_groups);
     uint32_t* gctr = ctr + 32 * g;
@@ -250,22 +280,25 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     auto tile_of = [&](int64_t k, uint32_t ticket) {
       return k < ns ? gw + k * nw : dyn0 + (int64_t)ticket * a.n_groups + g;
     };
-    int64_t t[2] = {gw, gw + nw};
-    uint32_t r[2] = {0u, 0u};
+    int64_t t[PF];
+    uint32_t r[PF];
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
-      if (l == 0 && t[f] < n_tiles && f + 2 >= ns) r[f] = atomicAdd(gctr, 1u);
+    for (int f = 0; f < PF; ++f) {
+      t[f] = gw + f * nw;
+      r[f] = 0u;
+      if (l == 0 && t[f] < n_tiles && f + PF >= ns) r[f] = atomicAdd(gctr, 1u);
+    }
     int64_t k = 0;                 // sequence number of the tile in stage 0
-    for (;; k += 2) {
+    for (;; k += PF) {
 #pragma unroll
-      for (int f = 0; f < 2; ++f) {
+      for (int f = 0; f < PF; ++f) {
         if (t[f] >= n_tiles) goto done;
         stage_in(stage[f]);
-        const int64_t kn = k + f + 2;
+        const int64_t kn = k + f + PF;
         const int64_t nt = tile_of(kn, kn >= ns ? __builtin_amdgcn_readfirstlane(r[f]) : 0u);
         if (nt < n_tiles) {
           load_tile(nt, stage[f]);
-          if (l == 0 && kn + 2 >= ns) r[f] = atomicAdd(gctr, 1u);
+          if (l == 0 && kn + PF >= ns) r[f] = atomicAdd(gctr, 1u);
         }
         compute(t[f]);
         t[f] = nt;
@@ -302,7 +335,7 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
 // tiles ahead in registers) and every wave reads it from LDS, so each key
 // tile crosses HBM once per 8 * QPW queries and all waves of a compute unit
 // share it.
-template <int HT, int KS, int QPW>
+template <int HT, int KS, int QPW, int KF>
 __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   constexpr int QB = 8 * QPW;                // queries per block
   constexpr int dI = KS * 16;
@@ -310,7 +343,10 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   constexpr int CH = dI / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = dI * 2;               // bytes per key row
   constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
-  constexpr int LOADERS = TILEB / 16;        // threads that load one chunk each
+  // Keys in HBM: bf16 rows or E4M3 rows (widened to bf16 in LDS).
+  constexpr int KROWB = KF == kMixed ? dI : ROWB;
+  constexpr int LBYTES = KF == kMixed ? 8 : 16;    // bytes each loader reads
+  constexpr int LOADERS = 32 * KROWB / LBYTES;
   __shared__ float sw[QB][HI];
   __shared__ __align__(16) uint8_t ktile[2][TILEB];
   const int wave = threadIdx.x >> 6;
@@ -335,16 +371,31 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
     wreg[u] = e < QB * HI ? a.w[((int64_t)b * a.Tq + i) * HI + h] : 0.f;
   }
 
-  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * ROWB;
-  // Loader thread t takes 16 bytes at t*16 of the tile in LDS order: row kk,
-  // swizzled slot cs, which holds the row's chunk cs ^ (kk % CH).
+  const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * KROWB;
+  // bf16: loader thread t takes 16 bytes at t*16 of the tile in LDS order:
+  // row kk, swizzled slot cs, which holds the row's chunk cs ^ (kk % CH).
+  // E4M3: loader t takes the 8 codes of chunk cs of key kk (t*8 of the tile
+  // in HBM order) and writes them widened into that chunk's slot, so the
+  // loaders of one key fill its whole LDS row.
   const bool loader = (int)threadIdx.x < LOADERS;
-  const int lo_off = threadIdx.x * 16;
-  const int lo_kk = lo_off / ROWB, lo_cs = (lo_off % ROWB) / 16;
+  const int lo_off = threadIdx.x * LBYTES;
+  const int lo_kk = lo_off / KROWB, lo_cs = (lo_off % KROWB) / LBYTES;
   auto load_tile = [&](int64_t tile) {
     int64_t j = tile * 32 + lo_kk;
     if (j > a.N - 1) j = a.N - 1;
-    return ld_stream16(Kb + j * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16));
+    if constexpr (KF == kMixed) {
+      const uint2 v = ld_stream8(Kb + j * KROWB + lo_cs * 8);
+      return make_uint4(v.x, v.y, 0u, 0u);
+    } else {
+      return ld_stream16(Kb + j * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16));
+    }
+  };
+  auto put_tile = [&](uint8_t* kt, const uint4& st) {
+    if constexpr (KF == kMixed)
+      *reinterpret_cast<uint4*>(kt + lo_kk * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16)) =
+          e4m3x8_to_bf16x8(st.x, st.y);
+    else
+      *reinterpret_cast<uint4*>(kt + lo_off) = st;
   };
   uint4 stage[2];
   if (loader) {
@@ -386,7 +437,7 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   // force the prefetch to complete when it is issued).
   auto step = [&](int64_t tile, uint4& st, uint8_t* kt) {
     if (loader) {
-      *reinterpret_cast<uint4*>(kt + lo_off) = st;
+      put_tile(kt, st);
       if (tile + 2 < n_tiles) st = load_tile(tile + 2);
     }
     __syncthreads();             // tile visible; every wave is done with tile - 1
@@ -423,14 +474,14 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   }
 }
 
-template <int HT, int KS, int QPW, int RW>
+template <int HT, int KS, int QPW, int RW, int KF>
 hipError_t launch_score(const ScoreArgs& sa, int64_t key_chunks, int row_groups, hipStream_t st) {
   if (sa.tile_ctr != nullptr)
-    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, true>), dim3((unsigned)key_chunks, row_groups),
-                       dim3(256), 0, st, sa);
+    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, true, KF>),
+                       dim3((unsigned)key_chunks, row_groups), dim3(256), 0, st, sa);
   else
-    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, false>), dim3((unsigned)key_chunks, row_groups),
-                       dim3(256), 0, st, sa);
+    hipLaunchKernelGGL((score_bf16_kernel<HT, KS, QPW, RW, false, KF>),
+                       dim3((unsigned)key_chunks, row_groups), dim3(256), 0, st, sa);
   return hipGetLastError();
 }
 
@@ -456,13 +507,17 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
     } else {
       const int64_t n_tiles = (nv_max + 31) / 32;
       const int HT = a.HI / 32, KS = a.dI / 16;
+      const bool fp8 = a.fmt == kMixed;     // bf16 queries, E4M3 keys
       if (a.Tq >= 8 && !sb.split) {
         // Prefill: a block of eight waves shares each key tile among 8 * QPW
         // queries and sweeps all the keys they see.
 #define LAC_SCORE_CASE(ht, ks, qpw)                                                        \
   if (HT == ht && KS == ks) {                                                              \
     const int blocks = a.B * ((a.Tq + 8 * qpw - 1) / (8 * qpw));                           \
-    hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw>), dim3(blocks), dim3(512), 0, st, sa); \
+    if (fp8)                                                                               \
+      hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw, kMixed>), dim3(blocks), dim3(512), 0, st, sa); \
+    else                                                                                   \
+      hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw, kBF16>), dim3(blocks), dim3(512), 0, st, sa); \
     err = hipGetLastError();                                                               \
   }
         LAC_SCORE_CASE(1, 4, 2) LAC_SCORE_CASE(1, 8, 2) LAC_SCORE_CASE(2, 4, 2)
@@ -480,8 +535,10 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
         sa.n_static = std::max(2, sa.tiles_per_wave * 3 / 4);
         sa.n_groups = (int)std::min<int64_t>(16, std::max<int64_t>(1, chunks / 8));
         const int groups = a.B * a.Tq;
-#define LAC_SCORE_CASE(ht, ks) \
-  if (HT == ht && KS == ks) err = launch_score<ht, ks, 1, 1>(sa, chunks, groups, st);
+#define LAC_SCORE_CASE(ht, ks)                                                      \
+  if (HT == ht && KS == ks)                                                         \
+    err = fp8 ? launch_score<ht, ks, 1, 1, kMixed>(sa, chunks, groups, st)          \
+              : launch_score<ht, ks, 1, 1, kBF16>(sa, chunks, groups, st);
         LAC_SCORE_CASE(1, 4) LAC_SCORE_CASE(1, 8) LAC_SCORE_CASE(2, 4) LAC_SCORE_CASE(2, 8)
         LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
 #undef LAC_SCORE_CASE

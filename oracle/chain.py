@@ -23,9 +23,10 @@ def compress_store(x, z, in_fmt, out_fmt, B, T, D, m, r, theta, pos0):
     return encode_rows(vals.reshape(B * N, D), FMT[out_fmt], r).reshape(B, N, -1)
 
 
-def csa_select(qI, w, KI, fmt, B, Tq, HI, dI, N, q_pos0, m, k, rows=None):
+def csa_select(qI, w, KI, fmt, B, Tq, HI, dI, N, q_pos0, m, k, rows=None, k_fmt=None):
     """Index scores and top-k: (idx [n_rows, k], scores [n_rows, N], nvis)."""
-    s, nv = index_scores(qI, w, KI, FMT[fmt], B, Tq, HI, dI, N, q_pos0, m, rows)
+    s, nv = index_scores(qI, w, KI, FMT[fmt], B, Tq, HI, dI, N, q_pos0, m, rows,
+                         k_dtype=FMT[fmt if k_fmt is None else k_fmt])
     return topk(s, nv, k), s, nv
 
 

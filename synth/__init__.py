@@ -160,18 +160,19 @@ def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, d
 
 
 def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI=128, H=64,
-                k=2048, W=128, device="cpu"):
+                k=2048, W=128, ki_fmt="bf16", device="cpu"):
     """Decode of a CSA + HCA layer pair at position ctx with the KV stored as
     FP8 E4M3 plus bf16 rotated dims.  The step also compresses the newest
     complete block of each layer (CSA entry, indexer key, HCA entry) from
-    bf16 activations, so every stage of the path runs in one step."""
+    bf16 activations, so every stage of the path runs in one step.  The
+    indexer keys are bf16, or E4M3 with ki_fmt = "mixed" (no rotated dims)."""
     N = ctx // m
     Nh = ctx // m_hca
     return dict(
         kind="pair_decode", fmt="mixed", B=B, D=D, m=m, m_hca=m_hca, r=r, HI=HI, dI=dI, H=H,
         k=k, W=W, N=N, Nh=Nh, theta=10000.0, q_pos0=ctx, raw_pos0=ctx - W + 1, T_raw=W,
         ckv=store(normal(seed, "ckv", (B, N, D), device=device), "mixed", r),
-        KI=store(normal(seed, "KI", (B, N, dI), device=device), "bf16"),
+        KI=store(normal(seed, "KI", (B, N, dI), device=device), ki_fmt),
         hkv=store(normal(seed, "hkv", (B, Nh, D), device=device), "mixed", r),
         raw_csa=store(normal(seed, "raw_csa", (B, W, D), device=device), "mixed", r),
         raw_hca=store(normal(seed, "raw_hca", (B, W, D), device=device), "mixed", r),

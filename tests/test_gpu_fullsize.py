@@ -31,18 +31,20 @@ def _h(t):
     return host(t.contiguous())
 
 
-def _check_select(g_idx, qI, w, KI_h, fmt, B, Tq, HI, dI, N, qpos, m, k, rows):
+def _check_select(g_idx, qI, w, KI_h, fmt, B, Tq, HI, dI, N, qpos, m, k, rows, k_fmt=None):
     s, nv = oracle.index_scores(qI, w, KI_h, synth.DTYPE_CODES[fmt], B, Tq, HI, dI, N, qpos, m,
-                                rows)
+                                rows, k_dtype=synth.DTYPE_CODES[k_fmt or fmt])
     o_idx = oracle.topk(s, nv, k)
     sel = np.stack([g_idx[b, i] for b, i in rows])
     same = check_topk(sel, o_idx, s, nv, k)
     return o_idx, same
 
 
-def test_pair_decode_1m():
-    print("full size: pair decode, B=4 at 2^20", flush=True)
-    c = synth.pair_decode(device=DEV)
+@pytest.mark.parametrize("ki_fmt", ["bf16", "mixed"])
+def test_pair_decode_1m(ki_fmt):
+    # ki_fmt "mixed": the indexer keys are E4M3 (the mixed format, no rotated dims)
+    print(f"full size: pair decode, B=4 at 2^20, indexer keys {ki_fmt}", flush=True)
+    c = synth.pair_decode(ki_fmt=ki_fmt, device=DEV)
     B, N, Nh, m, mh, D, r, k, W = (c[x] for x in ("B", "N", "Nh", "m", "m_hca", "D", "r", "k", "W"))
     HI, dI, H, ctx = c["HI"], c["dI"], c["H"], c["q_pos0"]
     # the benchmarked step
@@ -65,7 +67,7 @@ def test_pair_decode_1m():
     check_compressed(c["ckv"][:, N - 1:N], ref, "mixed", D, r)
     refI = oracle.compress(_h(c["new_kI"]), _h(c["new_zI"]), oracle.BF16, B, m, dI, m, 0, TH,
                            ctx - m)
-    check_compressed(c["KI"][:, N - 1:N], refI, "bf16", dI, 0)
+    check_compressed(c["KI"][:, N - 1:N], refI, ki_fmt, dI, 0)
     refH = oracle.compress(_h(c["new_kv_hca"]), _h(c["new_z_hca"]), oracle.BF16, B, mh, D, mh,
                            r, TH, ctx - mh)
     check_compressed(c["hkv"][:, Nh - 1:Nh], refH, "mixed", D, r)
@@ -74,15 +76,15 @@ def test_pair_decode_1m():
     ckv_h = _h(c["ckv"]).copy()
     ckv_h[:, N - 1:] = oracle.encode_rows(ref.reshape(B, D), oracle.MIXED, r).reshape(B, 1, -1)
     KI_h = _h(c["KI"]).copy()
-    KI_h[:, N - 1:] = oracle.encode_rows(refI.reshape(B, dI), oracle.BF16, 0).view(
-        np.uint16).reshape(B, 1, dI)
+    newest = oracle.encode_rows(refI.reshape(B, dI), synth.DTYPE_CODES[ki_fmt], 0)
+    KI_h[:, N - 1:] = (newest.view(np.uint16) if ki_fmt == "bf16" else newest).reshape(B, 1, dI)
     hkv_h = _h(c["hkv"]).copy()
     hkv_h[:, Nh - 1:] = oracle.encode_rows(refH.reshape(B, D), oracle.MIXED, r).reshape(B, 1, -1)
 
     rows = [(b, 0) for b in range(B)]
     g_idx = idx.cpu().numpy()
     o_idx, _ = _check_select(g_idx, _h(c["qI"]), _h(c["w"]), KI_h, "bf16", B, 1, HI, dI, N,
-                             ctx, m, k, rows)
+                             ctx, m, k, rows, k_fmt=ki_fmt)
 
     # CSA attention on the oracle's selection, same launch configuration
     y_sel = lac.csa_attend(c["q_csa"], c["ckv"],

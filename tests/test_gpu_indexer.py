@@ -16,10 +16,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run(B, Tq, HI, dI, N, m, k, qpos, fmt, seed, w_zero=False, rows=None):
-    print(f"indexer B={B} Tq={Tq} HI={HI} dI={dI} N={N} m={m} k={k} {fmt}", flush=True)
+def _run(B, Tq, HI, dI, N, m, k, qpos, fmt, seed, w_zero=False, rows=None, kfmt=None):
+    kfmt = fmt if kfmt is None else kfmt
+    print(f"indexer B={B} Tq={Tq} HI={HI} dI={dI} N={N} m={m} k={k} {fmt} keys {kfmt}", flush=True)
     q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI)), fmt)
-    K = synth.store(synth.normal(seed, "KI", (B, N, dI)), fmt)
+    K = synth.store(synth.normal(seed, "KI", (B, N, dI)), kfmt)
     w = synth.uniform(seed, "w", (B, Tq, HI))
     if w_zero:
         w.zero_()
@@ -30,7 +31,8 @@ def _run(B, Tq, HI, dI, N, m, k, qpos, fmt, seed, w_zero=False, rows=None):
     g_idx = idx.cpu().numpy().reshape(B * Tq, k)
     g_sc = score.cpu().numpy().reshape(B * Tq, k)
     code = synth.DTYPE_CODES[fmt]
-    s, nv = oracle.index_scores(host(q), host(w), host(K), code, B, Tq, HI, dI, N, qpos, m, rows)
+    s, nv = oracle.index_scores(host(q), host(w), host(K), code, B, Tq, HI, dI, N, qpos, m, rows,
+                                k_dtype=synth.DTYPE_CODES[kfmt])
     o_idx = oracle.topk(s, nv, k)
     sel = np.arange(B * Tq) if rows is None else np.array([b * Tq + i for b, i in rows])
     g_idx, g_sc = g_idx[sel], g_sc[sel]
@@ -101,3 +103,25 @@ def test_determinism():
     b = lac.indexer_topk(q, w, K, m=4, k=2048, q_pos0=[4 * N] * B)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+# E4M3 keys (d_I bytes per key, the mixed row format with no rotated dims),
+# bf16 queries: the low-precision indexer key cache.
+def test_e4m3_keys_decode_split_path():
+    same = _run(2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], "bf16", 21, kfmt="mixed")
+    assert len(same) >= 1
+
+
+def test_e4m3_keys_decode_one_workgroup_per_row():
+    _run(4, 1, 64, 128, 5003, 4, 512, [4 * 5003 + 1, 4 * 5003, 4 * 3000 + 3, 40000], "bf16", 22,
+         kfmt="mixed")
+
+
+def test_e4m3_keys_chunked_prefill_causal_rows():
+    _run(1, 40, 64, 128, 5010, 4, 300, [20000], "bf16", 23, kfmt="mixed")
+
+
+@pytest.mark.parametrize("HI,dI", [(32, 64), (128, 128)])
+def test_e4m3_keys_head_and_dim_variants(HI, dI):
+    _run(2, 3, HI, dI, 2100, 4, 256, [8400, 9000], "bf16", 24 + HI + dI, kfmt="mixed")
+
