@@ -41,9 +41,9 @@ BF16_PEAK_TFLOPS = 2500.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273734787, "csa_decode_128k": 277467942,
-                       "csa_chunk_prefill": 1338360086}
-SCORE_TRAFFIC_SOURCE_SHA256 = "d717940c93eca7522df44b3425fdadf63c3bc54251ac01cca416284426e6763e"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273732313, "csa_decode_128k": 277460966,
+                       "csa_chunk_prefill": 1329887861, "pair_decode_1m_e4m3_indexer": 139524584}
+SCORE_TRAFFIC_SOURCE_SHA256 = "7d8bacd98d8f42092332a393d3c0d7fbad97b383836fc63359209f71601a81b6"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
