@@ -331,6 +331,15 @@ __device__ __forceinline__ void lds_barrier() {
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
+// Max over lanes l, l^16, l^32, l^48 (the four lanes that hold one row), by
+// the cross-lane swaps of 16-lane rows and 32-lane halves.
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 __device__ __forceinline__ bf16x4 ds_read_tr(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) bf16x4*)(p));
 }
@@ -353,7 +362,11 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   using Gm = Geo<D>;
   constexpr int DS = Gm::DS, NT = Gm::NT, TPR = Gm::TPR;
   __shared__ __align__(16) uint8_t Et[2][kTile * Gm::EROW];     // entry tiles, bf16 rows
-  __shared__ __align__(16) int tags[2][kTile];
+  // Per entry: the first query slot of the block that sees it and the span of
+  // slots after it that do (an empty slot has first = 64, which no slot
+  // reaches), so a (row, entry) visibility test is one unsigned compare.
+  __shared__ __align__(16) int vis_lo[2][kTile];
+  __shared__ __align__(16) int vis_span[2][kTile];
   __shared__ __align__(16) float Sx[DS][4][64][8];             // partial logits [half][group][lane]
   __shared__ int32_t lidx[kIdxLds];
   __shared__ double freq[kMaxRopePairs];
@@ -410,26 +423,41 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
 
   constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
   uint4 stage[NST];
-  int st_tag = kNoEntry;
+  int st_tag = kNoEntry, st_lo = 64, st_span = 0;
   auto load_tile = [&](int base) {
     const int e = base + st_e;
     const uint8_t* rs = nullptr;
     int tag = kNoEntry;
+    int64_t lo = 64, hi = -1;    // query slots g (0 .. n_q-1) that see the entry
     if (e < e_hi) {
       if (e < n_comp) {
         if (mode == 0) {
+          // CSA: the entry was selected by query e / k only
           const int j = lidx[e - e_lo];
-          if (j >= 0 && j < NN) { rs = kvb + (int64_t)j * row_bytes; tag = G == 1 ? 0 : e / kk; }
+          if (j >= 0 && j < NN) {
+            rs = kvb + (int64_t)j * row_bytes;
+            tag = G == 1 ? 0 : e / kk;
+            lo = hi = tag;
+          }
         } else {
+          // HCA entry e covers positions up to (e+1) m - 1: seen from t >= (e+1) m
           rs = kvb + (int64_t)e * row_bytes;
           tag = -1 - e;
+          lo = (int64_t)(e + 1) * a.m - w.t_first;
+          hi = w.n_q - 1;
         }
       } else {
+        // window row at position s = lo_w + off: seen from t in [s, s + W - 1]
         rs = winb + (int64_t)(e - n_comp) * row_bytes;
         tag = kWinTag | (e - n_comp);
+        lo = w.lo_w + (e - n_comp) - w.t_first;
+        hi = min((int64_t)w.n_q - 1, lo + a.W - 1);
       }
     }
+    lo = max(lo, (int64_t)0);
     st_tag = tag;
+    st_lo = lo <= hi ? (int)lo : 64;
+    st_span = lo <= hi ? (int)(hi - lo) : 0;
     // Every lane issues all NST loads (no divergent branches around them);
     // chunks past the row and empty slots read a valid address and are not
     // used (an empty slot is staged as zeros).
@@ -477,7 +505,10 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
         *reinterpret_cast<uint4*>(dst_row + 16 * ch) = v;
       }
     }
-    if (st_part == 0) tags[buf][st_e] = st_tag;
+    if (st_part == 0) {
+      vis_lo[buf][st_e] = st_lo;
+      vis_span[buf][st_e] = st_span;
+    }
   };
 
   if (n_tiles > 0) load_tile(e_lo);
@@ -511,7 +542,6 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   // inside the tile loop only the prefetch of the next tile is outstanding
   // and no wait for it is placed before the compute of the current tile.
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-  const Vis myvis = make_vis(a, w, g);
   const float scale_log2 = a.scale_log2;
   float m_run = -INFINITY, l_part = 0.f;
   f32x4 oacc[Gm::DH];
@@ -558,8 +588,10 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
       }
     }
     // ---- sum the two halves' partial logits (D split over two waves)
-    const int4 tg0 = *reinterpret_cast<const int4*>(&tags[buf][4 * lq]);
-    const int4 tg1 = *reinterpret_cast<const int4*>(&tags[buf][16 + 4 * lq]);
+    const int4 vl0 = *reinterpret_cast<const int4*>(&vis_lo[buf][4 * lq]);
+    const int4 vl1 = *reinterpret_cast<const int4*>(&vis_lo[buf][16 + 4 * lq]);
+    const int4 vs0 = *reinterpret_cast<const int4*>(&vis_span[buf][4 * lq]);
+    const int4 vs1 = *reinterpret_cast<const int4*>(&vis_span[buf][16 + 4 * lq]);
     float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
     if constexpr (DS == 2) {
       *reinterpret_cast<float4*>(sx_mine) = make_float4(s0[0], s0[1], s0[2], s0[3]);
@@ -571,27 +603,27 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
 
     // ---- online softmax of row `row` over the lane's 8 entries (the same in
     // both waves of the row group)
-    const int tg[8] = {tg0.x, tg0.y, tg0.z, tg0.w, tg1.x, tg1.y, tg1.z, tg1.w};
+    const int vlo[8] = {vl0.x, vl0.y, vl0.z, vl0.w, vl1.x, vl1.y, vl1.z, vl1.w};
+    const int vsp[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
     float x[8] = {s0[0] + o0.x, s0[1] + o0.y, s0[2] + o0.z, s0[3] + o0.w,
                   s1[0] + o1.x, s1[1] + o1.y, s1[2] + o1.z, s1[3] + o1.w};
     float tmax = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      x[i] = visible(tg[i], g, myvis) ? x[i] * scale_log2 : -INFINITY;
+      x[i] = (uint32_t)(g - vlo[i]) <= (uint32_t)vsp[i] ? x[i] * scale_log2 : -INFINITY;
       tmax = fmaxf(tmax, x[i]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    tmax = row_max4(tmax);
     const bool moved = tmax > m_run + 8.f;          // also true for the first visible entry
     const bool rescale = moved && m_run != -INFINITY;   // the row's O holds earlier entries
     const float m_new = moved ? tmax : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float al = moved ? exp2f(m_run - m_use) : 1.f;
+    const float al = moved ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
     float psum = 0.f;
     uint32_t pk[4];
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
-      const float p0 = exp2f(x[i] - m_use), p1 = exp2f(x[i + 1] - m_use);
+      const float p0 = __builtin_amdgcn_exp2f(x[i] - m_use), p1 = __builtin_amdgcn_exp2f(x[i + 1] - m_use);
       psum += p0 + p1;
       pk[i / 2] = pack_bf16x2(p0, p1);
     }

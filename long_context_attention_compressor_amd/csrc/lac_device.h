@@ -37,16 +37,15 @@ struct Positions {
 // ---------------------------------------------------------------- bfloat16
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// Round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// Two floats to two bf16 (lo in the low half), rounded to nearest even by the
+// hardware converter (v_cvt_pk_bf16_f32); NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t b = __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
 }
 
 // ---------------------------------------------------------------- FP8 E4M3 ("fn")
