@@ -11,8 +11,9 @@
 //
 // Top-k.  Keys are the order-preserving uint32 images of the fp32 scores.
 //  * Prefix path (many rows of up to 67584 entries, e.g. chunked prefill):
-//    one workgroup per row keeps the row's 16-bit key prefixes in LDS and
-//    finds the threshold from them with one pass over the scores in HBM.
+//    one workgroup per row keeps the row's keys in registers, fixes the
+//    threshold's 24-bit prefix from two LDS histograms, and writes the set
+//    through an LDS bitmap, reading the scores from HBM once.
 //  * Row-wise path (many longer rows): one workgroup per row runs a 4-pass
 //    MSD radix select (8-bit digits, LDS histograms with wave-level
 //    aggregation of equal digits), then one ordered pass that keeps every key
@@ -193,25 +194,41 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rowwise_kernel(TopkArgs a) 
   }
 }
 
-// Row-wise selection with the row's 16-bit key prefixes kept in LDS (rows of
-// up to kPrefixMax entries): one pass over the scores in HBM writes the
-// prefixes and a histogram of the top 12 key bits; the next 4 bits are
-// histogrammed from LDS, which fixes the 16-bit threshold prefix P.  Keys
-// above P are selected; the few keys that carry P are ranked by (full key
-// desc, index asc) after their full keys are read back (a radix select over
-// the row handles the rare case of more than kPrefCand of them).  Their
-// prefixes are then rewritten to 0xFFFF (chosen) or 0 (not), so "prefix > P
-// or prefix == 0xFFFF" is the selection, emitted in ascending index order by
-// one block-wide scan over per-thread runs of the row.
+// Row-wise selection for rows of up to kPrefixMax entries, one 512-thread
+// workgroup per row.  Each thread loads 4 consecutive scores out of every
+// 2048 (coalesced) and keeps their keys in registers for the whole selection:
+//  * a histogram of key bits 31..20 (four lane-interleaved copies, so the lanes
+//    of a wave whose keys share a bin mostly add to different words) fixes
+//    the threshold's 12-bit bucket; a histogram of bits 19..8 over the keys in
+//    that bucket fixes its 24-bit prefix P;
+//  * keys above P go into a bitmap of the row (eight lanes merge their 4-bit
+//    groups into a 32-bit word with DPP moves); the few keys that carry P,
+//    collected in the same pass, are ranked by (key desc, index asc) and
+//    added (a radix select over the row handles the rare case of more than
+//    kPrefCand of them);
+//  * the set is emitted in ascending index order by one block-wide scan over
+//    per-thread runs of bitmap words.
 constexpr int kPrefixMax = 67584;
 constexpr int kPrefCand = 1024;
+constexpr int kPT = 512;                           // threads per row
+constexpr int kPU = (kPrefixMax + 4 * kPT - 1) / (4 * kPT);   // float4 loads per thread
+constexpr int kPBins = kHistBins / kPT;            // histogram bins per thread
+constexpr int kPrefWords = kPrefixMax / 32;        // bitmap words of the longest row
 
-__global__ void __launch_bounds__(1024) topk_prefix_kernel(TopkArgs a) {
-  extern __shared__ __align__(16) uint16_t pre[];                // [round_up(nv, 4)]
-  __shared__ uint32_t hist[kHistBins];
+// OR of a value over each group of 8 consecutive lanes (all lanes active).
+__device__ __forceinline__ uint32_t or8(uint32_t v) {
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  return v;
+}
+
+__global__ void __launch_bounds__(kPT) topk_prefix_kernel(TopkArgs a) {
+  __shared__ __align__(16) uint32_t hist4[kHistBins * 4];   // 4 copies, then bits 19..8 (one copy)
+  __shared__ uint32_t bitmap[kPrefWords];
   __shared__ int32_t cidx[kPrefCand];
   __shared__ uint32_t ckey[kPrefCand];
-  __shared__ uint32_t wsum[16];
+  __shared__ uint32_t wsum[kPT / 64];
   __shared__ uint32_t bc[4];
   __shared__ uint32_t t_d, t_above, n_cand;
   const int row = blockIdx.x;
@@ -221,37 +238,50 @@ __global__ void __launch_bounds__(1024) topk_prefix_kernel(TopkArgs a) {
   const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
   const float* s = a.scores + (int64_t)row * a.Np;
 
-  // ---- pass 1: scores -> 16-bit prefixes in LDS, histogram of key bits 31..20
-  constexpr int kU = (kPrefixMax + 4095) / 4096;           // float4 loads per thread
-  float4 v4[kU];
+  // ---- the row's keys into registers: element 4 (tid + kPT u) + c.  Slots
+  // past the row hold key 0, which only a NaN with every bit set maps to; they
+  // are taken out of bin 0 of both histograms, and every later test on a key
+  // (above the threshold prefix, or equal to it) fails for them or checks the
+  // index.
+  uint32_t key[kPU][4];
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int e = 4 * (tid + 1024 * u);
-    v4[u] = e < nv ? *reinterpret_cast<const float4*>(s + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int u = 0; u < kPU; ++u) {
+    const int e = 4 * (tid + kPT * u);
+    const float4 v = e < nv ? *reinterpret_cast<const float4*>(s + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    key[u][0] = e < nv ? score_key(v.x) : 0u;
+    key[u][1] = e + 1 < nv ? score_key(v.y) : 0u;
+    key[u][2] = e + 2 < nv ? score_key(v.z) : 0u;
+    key[u][3] = e + 3 < nv ? score_key(v.w) : 0u;
   }
-  for (int e = tid; e < kHistBins; e += 1024) hist[e] = 0u;
+  const uint32_t n_pad = (uint32_t)(4 * kPT * kPU - nv);
+  for (int e = tid; e < kHistBins * 4; e += kPT) hist4[e] = 0u;
   if (tid == 0) n_cand = 0;
   __syncthreads();
+
+  // ---- histogram of key bits 31..20
 #pragma unroll
-  for (int u = 0; u < kU; ++u) {
-    const int e = 4 * (tid + 1024 * u);
-    const float vv[4] = {v4[u].x, v4[u].y, v4[u].z, v4[u].w};
-    uint32_t key[4];
+  for (int u = 0; u < kPU; ++u)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) key[c] = score_key(vv[c]);
-    if (e < nv)
-      *reinterpret_cast<uint2*>(pre + e) = make_uint2((key[0] >> 16) | (key[1] & 0xffff0000u),
-                                                      (key[2] >> 16) | (key[3] & 0xffff0000u));
-#pragma unroll
-    for (int c = 0; c < 4; ++c) hist_add(hist, e + c < nv, key[c] >> 20);
-  }
+    for (int c = 0; c < 4; ++c) atomicAdd(&hist4[4 * (key[u][c] >> 20) + (l & 3)], 1u);
+  __syncthreads();
+  if (tid == 0) hist4[0] -= n_pad;
   __syncthreads();
 
-  // ---- threshold bucket of the top 12 bits: thread t covers bins 4095-4t .. 4092-4t
-  auto find_bucket = [&](uint32_t need) {
-    uint32_t c[4], sum = 0;
+  // ---- the bin holding the need-th largest key: thread t covers bins
+  // 4095 - kPBins t downwards, summed over `copies` interleaved copies.
+  auto find_bucket = [&](uint32_t need, int copies) {
+    uint32_t c[kPBins], sum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) { c[q] = hist[kHistBins - 1 - 4 * tid - q]; sum += c[q]; }
+    for (int q = 0; q < kPBins; ++q) {
+      const int bin = kHistBins - 1 - kPBins * tid - q;
+      if (copies == 4) {
+        const uint4 h = *reinterpret_cast<const uint4*>(&hist4[4 * bin]);
+        c[q] = h.x + h.y + h.z + h.w;
+      } else {
+        c[q] = hist4[bin];
+      }
+      sum += c[q];
+    }
     uint32_t incl = sum;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
@@ -265,95 +295,106 @@ __global__ void __launch_bounds__(1024) topk_prefix_kernel(TopkArgs a) {
     if (excl < need && incl >= need) {
       uint32_t cum = excl;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (cum + c[q] >= need) { t_d = kHistBins - 1 - 4 * tid - q; t_above = cum; break; }
+      for (int q = 0; q < kPBins; ++q) {
+        if (cum + c[q] >= need) { t_d = kHistBins - 1 - kPBins * tid - q; t_above = cum; break; }
         cum += c[q];
       }
     }
     __syncthreads();
   };
-  find_bucket((uint32_t)keff);
+  find_bucket((uint32_t)keff, 4);
   const uint32_t d1 = t_d, above1 = t_above;
+  for (int e = tid; e < kHistBins; e += kPT) hist4[e] = 0u;
   __syncthreads();
 
-  // ---- pass 2 (LDS): key bits 19..16 of the bucket's keys
-  if (tid < 16) hist[tid] = 0u;
-  __syncthreads();
-  for (int e0 = 0; e0 < nv; e0 += 1024) {
-    const int e = e0 + tid;
-    const uint32_t pv = e < nv ? pre[e] : 0u;
-    hist_add(hist, e < nv && (pv >> 4) == d1, pv & 15u);
-  }
-  __syncthreads();
-  if (tid < 64) {
-    // 16 bins, descending: lane q covers bin 15 - q
-    const uint32_t need = (uint32_t)keff - above1;
-    const uint32_t cnt = l < 16 ? hist[15 - l] : 0u;
-    uint32_t incl = cnt;
+  // ---- bits 19..8 of the keys in bucket d1
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t x = __shfl_up(incl, o);
-      if (l >= o) incl += x;
+  for (int u = 0; u < kPU; ++u) {
+    bool in[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) in[c] = (key[u][c] >> 20) == d1;
+    if (__ballot(in[0] | in[1] | in[2] | in[3])) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (in[c]) atomicAdd(&hist4[(key[u][c] >> 8) & 4095u], 1u);
     }
-    if (l < 16 && incl - cnt < need && incl >= need) { t_d = (d1 << 4) | (15 - l); t_above = above1 + incl - cnt; }
   }
   __syncthreads();
-  const uint32_t P = t_d;
-  const uint32_t need_p = (uint32_t)keff - t_above;       // >= 1 keys carrying P
+  if (tid == 0 && d1 == 0) hist4[0] -= n_pad;
+  __syncthreads();
+  find_bucket((uint32_t)keff - above1, 1);
+  const uint32_t P = (d1 << 12) | t_d;                    // 24-bit threshold prefix
+  const uint32_t need_p = (uint32_t)keff - above1 - t_above;   // >= 1 keys carrying P
 
-  // ---- pass 3: the keys carrying P, with their full keys
-  for (int e0 = 0; e0 < nv; e0 += 1024) {
-    const int e = e0 + tid;
-    if (e < nv && pre[e] == P) {
-      const uint32_t pos = atomicAdd(&n_cand, 1u);
-      if (pos < (uint32_t)kPrefCand) { cidx[pos] = e; ckey[pos] = score_key(s[e]); }
+  // ---- bitmap of the keys above P; the keys carrying P (and their indices)
+  // are collected on the way
+#pragma unroll
+  for (int u = 0; u < kPU; ++u) {
+    uint32_t nib = 0, eq = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t k24 = key[u][c] >> 8;
+      nib |= (uint32_t)(k24 > P) << c;
+      eq |= (uint32_t)(k24 == P) << c;
+    }
+    const uint32_t word = or8(nib << (4 * (l & 7)));
+    const int wi = (tid + kPT * u) >> 3;
+    if ((l & 7) == 0 && wi < kPrefWords) bitmap[wi] = word;
+    if (__ballot(eq != 0)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * (tid + kPT * u) + c;
+        if (((eq >> c) & 1u) && e < nv) {
+          const uint32_t pos = atomicAdd(&n_cand, 1u);
+          if (pos < (uint32_t)kPrefCand) { cidx[pos] = e; ckey[pos] = key[u][c]; }
+        }
+      }
     }
   }
   __syncthreads();
   const int nc = (int)n_cand;
   if (nc <= kPrefCand) {
-    // by rank among the candidates
-    uint32_t chosen = 0;
-    int me = -1;
-    if (tid < nc) {
-      me = cidx[tid];
-      const uint32_t mk = ckey[tid];
+    // the need_p largest by (key desc, index asc), by rank among the candidates
+    for (int ci = tid; ci < nc; ci += kPT) {
+      const int me = cidx[ci];
+      const uint32_t mk = ckey[ci];
       uint32_t rank = 0;
       for (int j = 0; j < nc; ++j) {
         const uint32_t ok = ckey[j];
         rank += (ok > mk) || (ok == mk && cidx[j] < me);
       }
-      chosen = rank < need_p;
+      if (rank < need_p) atomicOr(&bitmap[me >> 5], 1u << (me & 31));
     }
-    __syncthreads();
-    if (me >= 0) pre[me] = chosen ? (uint16_t)0xFFFF : (uint16_t)0;
   } else {
-    // many keys share P: radix select over the row's keys carrying P
+    // many keys carry P: the (key, index) threshold of a radix select over them
     uint32_t thr, need_eq, cnt_eq, thr2 = 0;
     radix_select(nv, need_p,
-                 [&](int e, uint32_t* u) { *u = score_key(s[e]); return (*u >> 16) == P; }, hist,
+                 [&](int e, uint32_t* u) { *u = score_key(s[e]); return (*u >> 8) == P; }, hist4,
                  bc, thr, need_eq, cnt_eq);
     if (cnt_eq > need_eq) {
       uint32_t ne2, ce2;
       radix_select(nv, need_eq,
                    [&](int e, uint32_t* u) { *u = ~(uint32_t)e; return score_key(s[e]) == thr; },
-                   hist, bc, thr2, ne2, ce2);
+                   hist4, bc, thr2, ne2, ce2);
     }
-    __syncthreads();
-    for (int e = tid; e < nv; e += 1024) {
-      if (pre[e] != P) continue;
-      const uint32_t u = score_key(s[e]);
-      pre[e] = (u > thr || (u == thr && ~(uint32_t)e >= thr2)) ? (uint16_t)0xFFFF : (uint16_t)0;
-    }
+#pragma unroll
+    for (int u = 0; u < kPU; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * (tid + kPT * u) + c;
+        const uint32_t kk = key[u][c];
+        if ((kk >> 8) == P && e < nv && (kk > thr || (kk == thr && ~(uint32_t)e >= thr2)))
+          atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+      }
   }
   __syncthreads();
 
-  // ---- emit in ascending index order: thread t owns a run of the row
-  const int per = (nv + 1023) / 1024;
-  const int r0 = min(nv, tid * per), r1 = min(nv, r0 + per);
-  auto sel = [&](int e) { const uint32_t pv = pre[e]; return pv > P || pv == 0xFFFFu; };
+  // ---- emit in ascending index order: thread t owns a run of words
+  const int nwords = (nv + 31) / 32;
+  const int per = (nwords + kPT - 1) / kPT;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
   uint32_t mine = 0;
-  for (int e = r0; e < r1; ++e) mine += sel(e);
+  for (int w = w0; w < w1; ++w) mine += __popc(bitmap[w]);
   uint32_t incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -365,15 +406,19 @@ __global__ void __launch_bounds__(1024) topk_prefix_kernel(TopkArgs a) {
   for (int w = 0; w < wv; ++w) incl += wsum[w];
   uint32_t pos = incl - mine;
   int32_t* out = a.idx + (int64_t)row * a.k;
-  for (int e = r0; e < r1; ++e) {
-    if (!sel(e)) continue;
-    if (pos < (uint32_t)keff) {
-      out[pos] = e;
-      if (a.score_out) a.score_out[(int64_t)row * a.k + pos] = s[e];
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int e = 32 * w + __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < (uint32_t)keff) {
+        out[pos] = e;
+        if (a.score_out) a.score_out[(int64_t)row * a.k + pos] = s[e];
+      }
+      ++pos;
     }
-    ++pos;
   }
-  for (int e = keff + tid; e < a.k; e += 1024) {
+  for (int e = keff + tid; e < a.k; e += kPT) {
     out[e] = -1;
     if (a.score_out) a.score_out[(int64_t)row * a.k + e] = -INFINITY;
   }
@@ -779,12 +824,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
   if (!p.split) {
     TimedLaunch tl(kKernelTopk, st);
     if (nv_max <= kPrefixMax) {
-      static const hipError_t attr = hipFuncSetAttribute(
-          reinterpret_cast<const void*>(&topk_prefix_kernel),
-          hipFuncAttributeMaxDynamicSharedMemorySize, kPrefixMax * 2);
-      if (attr != hipSuccess) return attr;
-      const size_t lds = (size_t)((nv_max + 3) / 4 * 4) * 2;
-      hipLaunchKernelGGL(topk_prefix_kernel, dim3(R), dim3(1024), lds, st, ta);
+      hipLaunchKernelGGL(topk_prefix_kernel, dim3(R), dim3(kPT), 0, st, ta);
     } else {
       hipLaunchKernelGGL(topk_rowwise_kernel, dim3(R), dim3(kTopkThreads), 0, st, ta);
     }
