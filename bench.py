@@ -41,9 +41,9 @@ BF16_PEAK_TFLOPS = 2500.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273732313, "csa_decode_128k": 277460966,
-                       "csa_chunk_prefill": 1329887861, "pair_decode_1m_e4m3_indexer": 139524584}
-SCORE_TRAFFIC_SOURCE_SHA256 = "7d8bacd98d8f42092332a393d3c0d7fbad97b383836fc63359209f71601a81b6"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273731632, "csa_decode_128k": 277462983,
+                       "csa_chunk_prefill": 1332494273, "pair_decode_1m_e4m3_indexer": 139523310}
+SCORE_TRAFFIC_SOURCE_SHA256 = "00fcebfdb594ec465685d01b9fcdac003d938ef8d2b06275c755a06f178c0668"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
