@@ -497,7 +497,6 @@ __device__ __forceinline__ void block_scan2(uint32_t v0, uint32_t v1, uint32_t* 
 __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
   constexpr int kPer = kSplitChunk / 256;
   __shared__ uint32_t lds[40];
-  __shared__ uint32_t h2[kHistBins];
   const int row = blockIdx.y;
   const int nv = (int)row_nvis(a, row);
   const int keff = min(a.k, nv);
@@ -512,9 +511,11 @@ __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
     const int e = lo + it * 256 + threadIdx.x;
     sc[it] = s[e < hi ? e : lo];
   }
-  for (int e = threadIdx.x; e < kHistBins; e += 256) h2[e] = 0u;
   uint32_t bucket, above;
   split_threshold(a.hist + (int64_t)row * kHistBins, (uint32_t)keff, lds, &bucket, &above);
+  // Keys in the threshold bucket (a few per chunk) add their next 12 bits
+  // straight into the row's second histogram.
+  uint32_t* g2 = a.hist2 + (int64_t)row * kHistBins;
   uint32_t key[kPer];
   uint32_t n_up = 0, n_in = 0;
 #pragma unroll
@@ -524,7 +525,7 @@ __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
     n_up += (e < hi && (key[it] >> 20) > bucket);
     const bool in = e < hi && (key[it] >> 20) == bucket;
     n_in += in;
-    hist_add(h2, in, (key[it] >> 8) & (kHistBins - 1));
+    if (in) atomicAdd(&g2[(key[it] >> 8) & (kHistBins - 1)], 1u);
   }
   uint32_t ex_up, ex_in, tot_up, tot_in;
   block_scan2(n_up, n_in, lds, ex_up, ex_in, tot_up, tot_in);
@@ -543,17 +544,12 @@ __global__ void __launch_bounds__(256) topk_filter_kernel(TopkArgs a) {
     if (bk > bucket) sel[pu++] = e;
     else if (bk == bucket) cand[pi++] = make_uint2(key[it], (uint32_t)e);
   }
-  uint32_t* g2 = a.hist2 + (int64_t)row * kHistBins;
-  for (int e = threadIdx.x; e < kHistBins; e += 256) {
-    const uint32_t c = h2[e];
-    if (c) atomicAdd(&g2[e], c);
-  }
 }
 
 // Resolve one row (n_vis up to kBitmapMaxN) from the chunk lists, the second
 // histogram and an LDS bitmap of the row.
 __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
-  extern __shared__ __align__(16) uint32_t bits[];              // [ceil(nv / 32)]
+  extern __shared__ __align__(16) uint32_t bits[];              // [ceil(nv / 32) rounded up to 4]
   __shared__ uint2 ties[kTieLds];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bc[4];
@@ -572,7 +568,7 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) { c[q] = g2[kHistBins - 1 - 4 * tid - q]; sum += c[q]; }
   for (int e = tid; e < 2 * nchunks; e += 1024) ccnt[e] = a.cnt[(int64_t)row * a.chunks * 2 + e];
-  for (int e = tid; e < nwords; e += 1024) bits[e] = 0u;
+  for (int e = tid; e < ((nwords + 3) & ~3); e += 1024) bits[e] = 0u;
   if (tid == 0) { n_tie = 0; t_sel = 0; }
   __syncthreads();
   // Selected count (sum over chunks), then the threshold sub-bucket: thread t
@@ -709,11 +705,22 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
   }
   __syncthreads();
 
-  // Emit the set in ascending index order: thread t owns a run of words.
-  const int per = (nwords + 1023) / 1024;
+  // Emit the set in ascending index order: thread t owns a run of words (a
+  // multiple of 4, at most 32 for rows up to kBitmapMaxN), read as 16-byte
+  // groups; it counts their bits and notes which words are nonzero, then
+  // writes out only those words.
+  constexpr int kEmitG = kBitmapMaxN / 32 / 1024 / 4;
+  const int per = ((nwords + 1023) / 1024 + 3) & ~3;
   const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
-  uint32_t mine = 0;
-  for (int w = w0; w < w1; ++w) mine += (uint32_t)__popc(bits[w]);
+  uint32_t mine = 0, nz = 0;
+#pragma unroll
+  for (int g = 0; g < kEmitG; ++g) {
+    const int w = w0 + 4 * g;
+    const uint4 v = w < w1 ? *reinterpret_cast<const uint4*>(&bits[w]) : make_uint4(0u, 0u, 0u, 0u);
+    mine += (uint32_t)(__popc(v.x) + __popc(v.y) + __popc(v.z) + __popc(v.w));
+    nz |= ((uint32_t)(v.x != 0) | (uint32_t)(v.y != 0) << 1 | (uint32_t)(v.z != 0) << 2 |
+           (uint32_t)(v.w != 0) << 3) << (4 * g);
+  }
   uint32_t incl = mine;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -726,7 +733,9 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
   uint32_t pos = incl - mine;
   const float* s = a.scores + (int64_t)row * a.Np;
   int32_t* out = a.idx + (int64_t)row * a.k;
-  for (int w = w0; w < w1; ++w) {
+  while (nz) {
+    const int w = w0 + __ffs(nz) - 1;
+    nz &= nz - 1;
     uint32_t b = bits[w];
     while (b) {
       const int j = (w << 5) + __ffs(b) - 1;
@@ -840,7 +849,7 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
       hipFuncAttributeMaxDynamicSharedMemorySize, kBitmapMaxN / 8);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(topk_resolve_kernel, dim3(R), dim3(1024),
-                     (size_t)((nv_max + 31) / 32) * 4, st, ta);
+                     (size_t)(((nv_max + 31) / 32 + 3) & ~3) * 4, st, ta);
   return hipGetLastError();
 }
 
