@@ -732,12 +732,16 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   uint8_t* dst = split_out
       ? reinterpret_cast<uint8_t*>(a.part_o + slot * 64 * D)
       : static_cast<uint8_t*>(a.out) + (((int64_t)w.b * a.Tq + w.i0) * a.H + w.h0) * D * 2;
+  // Streaming stores: the rows are read once, by the next kernel, and leave
+  // no dirty L2 lines for the end-of-kernel write-back (which would delay
+  // that kernel's start on this XCD).
+  typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 #pragma unroll
   for (int k = 0; k < 64 * CPR / NT; ++k) {
     const int c = tid + k * NT;
     if (c < n_rows * CPR) {
       const uint4 v = *reinterpret_cast<const uint4*>(ob + (c / CPR) * Gm::EROW + 16 * (c % CPR));
-      *reinterpret_cast<uint4*>(dst + (int64_t)c * 16) = v;
+      __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16));
     }
   }
 }

@@ -465,7 +465,7 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
       }
       part += __shfl_xor(part, 32);
       const int off = hf == 0 ? (int)j * 4 : 0x7fffffff;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[qi], off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[qi], off, 0, 2);   // nt
     }
   };
   for (int64_t tile = 0; tile < n_tiles; tile += 2) {
