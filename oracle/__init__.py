@@ -66,6 +66,11 @@ def _load():
     lib.lo_rope.restype = None
     lib.lo_compress.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, dbl, vp, i64, i64, vp, vp]
     lib.lo_compress.restype = i32
+    lib.lo_compress2.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, dbl, vp, i64, i64, vp, dbl,
+                                 vp, vp]
+    lib.lo_compress2.restype = i32
+    lib.lo_rmsnorm.argtypes = [vp, i32, vp, dbl]
+    lib.lo_rmsnorm.restype = None
     lib.lo_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, i32,
                                     vp, vp]
     lib.lo_index_scores.restype = i32
@@ -77,6 +82,9 @@ def _load():
     lib.lo_attend.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, vp,
                               dbl, i32, i32, i32, i32, i32, dbl, vp, vp, i32, vp]
     lib.lo_attend.restype = i32
+    lib.lo_attend2.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, vp,
+                               dbl, i32, i32, i32, i32, i32, dbl, vp, vp, i32, vp, dbl, vp]
+    lib.lo_attend2.restype = i32
     lib.lo_num_threads.argtypes = []
     lib.lo_num_threads.restype = i32
     _lib = lib
@@ -161,17 +169,28 @@ def rope(v: np.ndarray, r: int, theta: float, pos: float) -> np.ndarray:
 
 
 # ---------------------------------------------------------------- method
+def rmsnorm(v, gain, eps):
+    """RMSNorm of one float64 vector over all its dims, times gain (copy)."""
+    v = np.array(v, np.float64, copy=True)
+    g = np.ascontiguousarray(gain, np.float32)
+    _load().lo_rmsnorm(_p(v), v.shape[-1], _p(g), float(eps))
+    return v
+
+
 def compress(x, z, in_dtype, B, T, D, m, r=0, theta=10000.0, pos0=None,
-             x_bstride=None, z_bstride=None, want_weights=False):
-    """Block-softmax pooling + rotation at the block start.  -> float64 [B, T//m, D]
-    (and the weights [B, T//m, m, D] when want_weights)."""
+             x_bstride=None, z_bstride=None, want_weights=False, norm_gain=None, norm_eps=1e-6):
+    """Block-softmax pooling (+ RMSNorm with norm_gain [D] when given) + rotation
+    at the block start.  -> float64 [B, T//m, D] (and the weights [B, T//m, m, D]
+    when want_weights)."""
     N = T // m
     out = np.empty((B, N, D), np.float64)
     alpha = np.empty((B, N, m, D), np.float64) if want_weights else None
     pos = _i64(pos0, B)        # held until the call returns
-    rc = _load().lo_compress(_p(x), _p(z), in_dtype, B, T, D, m, r, float(theta),
-                             _p(pos), T if x_bstride is None else x_bstride,
-                             T if z_bstride is None else z_bstride, _p(out), _p(alpha))
+    gain = None if norm_gain is None else np.ascontiguousarray(norm_gain, np.float32)
+    rc = _load().lo_compress2(_p(x), _p(z), in_dtype, B, T, D, m, r, float(theta),
+                              _p(pos), T if x_bstride is None else x_bstride,
+                              T if z_bstride is None else z_bstride, _p(gain), float(norm_eps),
+                              _p(out), _p(alpha))
     if rc:
         raise ValueError(f"lo_compress rejected its arguments ({rc})")
     return (out, alpha) if want_weights else out
@@ -211,8 +230,9 @@ def topk(scores, nvis, k):
 
 
 def attend(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W, sink,
-           scale, B, Tq, H, D, r, theta, qpos0, rows=None):
+           scale, B, Tq, H, D, r, theta, qpos0, rows=None, q_norm_gain=None, norm_eps=1e-6):
     """Core attention.  mode 0 = CSA (idx [n_rows, k]), mode 1 = HCA (m = m').
+    With q_norm_gain [D], each query head vector is RMSNorm'd first.
     -> float64 [n_rows, H, D]."""
     rows = _rows(rows, B, Tq)
     n = rows.shape[0]
@@ -222,9 +242,11 @@ def attend(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W
     if sink is not None:
         sink = np.ascontiguousarray(sink, np.float64)
     rpos, qpos = _i64(raw_pos0, B), _i64(qpos0, B)   # held until the call returns
-    rc = _load().lo_attend(_p(q), q_dtype, _p(kv), kv_dtype, N, mode, _p(idx), k, m, _p(raw),
-                           T_raw, _p(rpos), W, _p(sink), float(scale), B, Tq, H, D,
-                           r, float(theta), _p(qpos), _p(rows), n, _p(out))
+    gain = None if q_norm_gain is None else np.ascontiguousarray(q_norm_gain, np.float32)
+    rc = _load().lo_attend2(_p(q), q_dtype, _p(kv), kv_dtype, N, mode, _p(idx), k, m, _p(raw),
+                            T_raw, _p(rpos), W, _p(sink), float(scale), B, Tq, H, D,
+                            r, float(theta), _p(qpos), _p(rows), n, _p(gain), float(norm_eps),
+                            _p(out))
     if rc:
         raise ValueError(f"lo_attend rejected its arguments ({rc})")
     return out

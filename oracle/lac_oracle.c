@@ -206,6 +206,22 @@ void lo_rope(double* v, int D, int r, double theta, double pos) {
 }
 
 /* ------------------------------------------------------------------------ */
+/* RMSNorm ([P2] section "Attention Sink": V4 applies RMSNorm to the queries */
+/* and the compressed KV entries before core attention; [P3] the same for    */
+/* CSA and HCA, against exploding logits).  Reading: over all D dims of one  */
+/* vector, v <- v / sqrt(mean(v^2) + eps) * gain (gain per dim, fp32), taken */
+/* before the rotation.                                                     */
+/* ------------------------------------------------------------------------ */
+void lo_rmsnorm(double* v, int D, const float* gain, double eps) {
+    double ms = 0.0;
+    int c;
+    for (c = 0; c < D; ++c) ms += v[c] * v[c];
+    ms /= (double)D;
+    double inv = 1.0 / sqrt(ms + eps);
+    for (c = 0; c < D; ++c) v[c] = v[c] * inv * (double)gain[c];
+}
+
+/* ------------------------------------------------------------------------ */
 /* Compression ([P2] CSA Step 1; HCA uses the same pooling with m' tokens).   */
 /* Every m consecutive KV entries merge into one with learned softmax        */
 /* weights; reading: one softmax over the m tokens per channel, fed by a      */
@@ -213,10 +229,13 @@ void lo_rope(double* v, int D, int r, double theta, double pos) {
 /* The entry is then rotated at the position of its first token.             */
 /* ------------------------------------------------------------------------ */
 
-/* alpha (optional, [B, T/m, m, D]) receives the per-channel weights. */
-int lo_compress(const void* x, const void* z, int in_dtype, int B, int T, int D, int m,
-                int r, double theta, const int64_t* pos0, int64_t x_bstride,
-                int64_t z_bstride, double* out, double* alpha) {
+/* alpha (optional, [B, T/m, m, D]) receives the per-channel weights.       */
+/* norm_gain (optional, [D]): the entry is RMSNorm'd (eps norm_eps) before   */
+/* its rotation.                                                             */
+int lo_compress2(const void* x, const void* z, int in_dtype, int B, int T, int D, int m,
+                 int r, double theta, const int64_t* pos0, int64_t x_bstride,
+                 int64_t z_bstride, const float* norm_gain, double norm_eps, double* out,
+                 double* alpha) {
     if (m < 1 || D < 1 || r < 0 || r > D || (r & 1)) return 1;
     int N = T / m;
     int64_t rb = row_bytes(in_dtype, D, 0);
@@ -244,11 +263,19 @@ int lo_compress(const void* x, const void* z, int in_dtype, int B, int T, int D,
             }
             o[c] = acc;
         }
+        if (norm_gain) lo_rmsnorm(o, D, norm_gain, norm_eps);
         lo_rope(o, D, r, theta, (double)(pos0 ? pos0[b] : 0) + (double)j * m);
         free(xs);
         free(zs);
     }
     return 0;
+}
+
+int lo_compress(const void* x, const void* z, int in_dtype, int B, int T, int D, int m,
+                int r, double theta, const int64_t* pos0, int64_t x_bstride,
+                int64_t z_bstride, double* out, double* alpha) {
+    return lo_compress2(x, z, in_dtype, B, T, D, m, r, theta, pos0, x_bstride, z_bstride, NULL,
+                        0.0, out, alpha);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -355,11 +382,13 @@ int lo_topk(const double* scores, int n_rows, int N, const int32_t* nvis, int k,
 /* j < min(N, floor(t/m))).                                                  */
 /* out: [n_rows, H, D].                                                      */
 /* ------------------------------------------------------------------------ */
-int lo_attend(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, int mode,
-              const int32_t* idx, int k, int m, const void* raw, int T_raw,
-              const int64_t* raw_pos0, int W, const double* sink, double scale, int B, int Tq,
-              int H, int D, int r, double theta, const int64_t* qpos0, const int32_t* rows,
-              int n_rows, double* out) {
+/* q_norm_gain (optional, [D]): each query head vector is RMSNorm'd (eps    */
+/* norm_eps) before its rotation.                                           */
+int lo_attend2(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, int mode,
+               const int32_t* idx, int k, int m, const void* raw, int T_raw,
+               const int64_t* raw_pos0, int W, const double* sink, double scale, int B, int Tq,
+               int H, int D, int r, double theta, const int64_t* qpos0, const int32_t* rows,
+               int n_rows, const float* q_norm_gain, double norm_eps, double* out) {
     (void)B;
     int64_t qrb = row_bytes(q_dtype, D, 0);
     int64_t krb = row_bytes(kv_dtype, D, r);
@@ -388,6 +417,7 @@ int lo_attend(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, i
         double* y = out + ((int64_t)rr * H + h) * D;
         int c;
         decode_row((const uint8_t*)q + (((int64_t)b * Tq + i) * H + h) * qrb, q_dtype, D, 0, qv);
+        if (q_norm_gain) lo_rmsnorm(qv, D, q_norm_gain, norm_eps);
         lo_rope(qv, D, r, theta, (double)t);
 
         /* Collect the logits first (to take their maximum), then weights. */
@@ -442,6 +472,15 @@ int lo_attend(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, i
         free(valid);
     }
     return 0;
+}
+
+int lo_attend(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, int mode,
+              const int32_t* idx, int k, int m, const void* raw, int T_raw,
+              const int64_t* raw_pos0, int W, const double* sink, double scale, int B, int Tq,
+              int H, int D, int r, double theta, const int64_t* qpos0, const int32_t* rows,
+              int n_rows, double* out) {
+    return lo_attend2(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W,
+                      sink, scale, B, Tq, H, D, r, theta, qpos0, rows, n_rows, NULL, 0.0, out);
 }
 
 int lo_num_threads(void) {
