@@ -72,6 +72,8 @@ class PairDecode:
     unit = "tokens/s"
 
     ki_fmt = "bf16"
+    rmsnorm = False     # fused RMSNorm of the new compressed entries and the queries
+    gain = None
 
     def __init__(self, lac, synth, dev, sets, seed=4, B=4, ctx=1 << 20):
         self.lac, self.B, self.ctx = lac, B, ctx
@@ -79,6 +81,8 @@ class PairDecode:
                                        device=dev) for s in range(sets)]
         c = self.sets[0]
         self.c = c
+        # RMSNorm gains (synthetic: 1), used when rmsnorm is set
+        self.gain = torch.ones(c["D"], dtype=torch.float32, device=dev) if self.rmsnorm else None
         self.idx = torch.empty((B, 1, c["k"]), dtype=torch.int32, device=dev)
         self.out_csa = torch.empty_like(c["q_csa"])
         self.out_hca = torch.empty_like(c["q_hca"])
@@ -95,8 +99,9 @@ class PairDecode:
         N, Nh, m, mh, ctx = c["N"], c["Nh"], c["m"], c["m_hca"], self.ctx
         # the CSA layer: compress its newest block (KV entry and indexer key),
         # select, attend
+        g = self.gain
         lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
-                         rope_dims=c["r"], pos0=ctx - m)
+                         rope_dims=c["r"], pos0=ctx - m, norm_gain=g)
         lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m, rope_dims=0,
                          pos0=ctx - m)
         if timer is not None:
@@ -105,13 +110,13 @@ class PairDecode:
                          workspace=self.ws_idx)
         lac.csa_attend(s["q_csa"], s["ckv"], self.idx, s["raw_csa"], c["W"], q_pos0=ctx,
                        raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_csa,
-                       workspace=self.ws_csa)
+                       workspace=self.ws_csa, q_norm_gain=g)
         # the HCA layer: compress its newest block, then attend
         lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh), m=mh,
-                         rope_dims=c["r"], pos0=ctx - mh)
+                         rope_dims=c["r"], pos0=ctx - mh, norm_gain=g)
         lac.hca_attend(s["q_hca"], s["hkv"], s["raw_hca"], c["W"], m=mh, q_pos0=ctx,
                        raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_hca,
-                       workspace=self.ws_hca)
+                       workspace=self.ws_hca, q_norm_gain=g)
 
     def tokens_per_step(self):
         return self.B
@@ -140,6 +145,7 @@ class PairDecode:
                             f"{c['HI']}x{c['dI']}, bf16 queries, e4m3 keys"),
                 "csa_entries": c["N"],
                 "hca_entries": c["Nh"], "kv_format": "e4m3 + bf16 rope dims (576 B/entry)",
+                "rmsnorm": "q and new entries, fused" if self.rmsnorm else "none",
                 "cache_sets": len(self.sets)}
 
     def cpu_sample(self):
@@ -157,22 +163,24 @@ class PairDecode:
         ckv = h["ckv"].reshape(1, N, -1).copy()
         KI = h["KI"].reshape(1, N, -1).copy()
         hkv = h["hkv"].reshape(1, Nh, -1).copy()
+        g = None if self.gain is None else self.gain.cpu().numpy()
         ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16", "mixed", 1,
-                                              c["m"], c["D"], c["m"], c["r"], 1e4, ctx - c["m"])
+                                              c["m"], c["D"], c["m"], c["r"], 1e4, ctx - c["m"],
+                                              norm_gain=g)
         KI.view(np.uint8)[:, N - 1:] = chain.compress_store(
             h["new_kI"], h["new_zI"], "bf16", self.ki_fmt, 1, c["m"], c["dI"], c["m"], 0, 1e4,
             ctx - c["m"])
         hkv[:, Nh - 1:] = chain.compress_store(h["new_kv_hca"], h["new_z_hca"], "bf16", "mixed",
                                                1, c["m_hca"], c["D"], c["m_hca"], c["r"], 1e4,
-                                               ctx - c["m_hca"])
+                                               ctx - c["m_hca"], norm_gain=g)
         idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, "bf16", 1, 1, c["HI"], c["dI"], N, ctx,
                                      c["m"], c["k"], k_fmt=self.ki_fmt)
         oracle.attend(h["q_csa"], oracle.BF16, ckv, oracle.MIXED, N, 0, idx, c["k"], c["m"],
                       h["raw_csa"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
-                      c["r"], 1e4, ctx)
+                      c["r"], 1e4, ctx, q_norm_gain=g)
         oracle.attend(h["q_hca"], oracle.BF16, hkv, oracle.MIXED, Nh, 1, None, 0, c["m_hca"],
                       h["raw_hca"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
-                      c["r"], 1e4, ctx)
+                      c["r"], 1e4, ctx, q_norm_gain=g)
         el = time.perf_counter() - t0
         return {"value": 1.0 / el, "unit": self.unit, "seconds": el,
                 "sample": "the full decode step (compress newest blocks, index 262144 entries, "
@@ -184,6 +192,13 @@ class PairDecodeE4M3Indexer(PairDecode):
     """pair_decode_1m with the indexer keys stored as E4M3 (d_I bytes per key)."""
     name = "pair_decode_1m_e4m3_indexer"
     ki_fmt = "mixed"
+
+
+class PairDecodeRmsNorm(PairDecode):
+    """pair_decode_1m with RMSNorm of the new compressed entries (in the compress
+    epilogue) and of the queries (in the attention prologue)."""
+    name = "pair_decode_1m_rmsnorm"
+    rmsnorm = True
 
 
 class CsaDecode(PairDecode):
@@ -371,8 +386,8 @@ class HcaPrefill(ChunkPrefill):
                           "queries, FLOPs scaled by 128/8192"}
 
 
-WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, CsaDecode, ChunkPrefill,
-                                   HcaPrefill)}
+WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeRmsNorm, CsaDecode,
+                                  ChunkPrefill, HcaPrefill)}
 
 
 def main():

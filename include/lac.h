@@ -115,6 +115,32 @@ int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, v
                      int64_t out_batch_stride, void* stream);
 
 /*
+ * csa_compress_rmsnorm, hca_compress_rmsnorm -- csa_compress / hca_compress
+ * with the RMSNorm of each compressed entry fused into the epilogue.  [P2]
+ * (section "Attention Sink") and [P3] apply RMSNorm to the compressed KV
+ * entries before core attention.  Reading: after pooling and before the
+ * rotation, over all D dims of the entry,
+ *     e <- e / sqrt(mean_c(e[c]^2) + norm_eps) * norm_gain[c]
+ * in fp32; the rotation then follows as in csa_compress.
+ *   norm_gain  [D] float32 device array, 16-byte aligned (caller-owned)
+ *   norm_eps   >= 0 and finite
+ * Needs D/8 a power of two of at most 64 (D in {8, ..., 512}); else
+ * LAC_ERR_UNSUPPORTED.  Other arguments and errors as csa_compress.
+ */
+int32_t csa_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                             int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                             int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                             int64_t kv_batch_stride, int64_t logit_batch_stride,
+                             int64_t out_batch_stride, const float* norm_gain, float norm_eps,
+                             void* stream);
+int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                             int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                             int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                             int64_t kv_batch_stride, int64_t logit_batch_stride,
+                             int64_t out_batch_stride, const float* norm_gain, float norm_eps,
+                             void* stream);
+
+/*
  * indexer_topk -- [P3] lightning indexer + top-k; [P2] CSA Step 2 "Select";
  * [P1] top 2048.  For query t = q_pos0[b] + i, the visible entries are
  * j < n_vis(t) = min(N, floor(t/m)) ([P3] strict causality: a query never
@@ -208,6 +234,35 @@ int32_t hca_attend(const void* q, int32_t q_dtype, const void* hkv, int32_t kv_d
                    int32_t H, int32_t D, int32_t rope_dims, float rope_theta,
                    const int64_t* q_pos0, void* out, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * csa_attend_rmsnorm, hca_attend_rmsnorm -- csa_attend / hca_attend with the
+ * RMSNorm of each query head fused into the prologue ([P2] section
+ * "Attention Sink", [P3]: RMSNorm of the queries before core attention).
+ * Reading: before the rotation at t, over all D dims of q[b,i,h],
+ *     q <- q / sqrt(mean_c(q[c]^2) + norm_eps) * q_norm_gain[c]
+ * in fp32 (then rounded to bf16 once, with the rotation, on the bf16 path).
+ * The compressed entries are expected RMSNorm'd already (the *_compress_rmsnorm
+ * calls); raw window rows are used as given.
+ *   q_norm_gain  [D] float32 device array, 16-byte aligned (caller-owned)
+ *   norm_eps     >= 0 and finite
+ * Other arguments, limits and errors as csa_attend / hca_attend.
+ */
+int32_t csa_attend_rmsnorm(const void* q, int32_t q_dtype, const void* ckv, int32_t kv_dtype,
+                           int32_t N, const int32_t* topk_idx, int32_t k, const void* raw_kv,
+                           int32_t T_raw, const int64_t* raw_pos0, int32_t window,
+                           const float* sink, float softmax_scale, int32_t B, int32_t Tq,
+                           int32_t H, int32_t D, int32_t rope_dims, float rope_theta,
+                           const int64_t* q_pos0, void* out, void* workspace,
+                           size_t workspace_bytes, const float* q_norm_gain, float norm_eps,
+                           void* stream);
+int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int32_t kv_dtype,
+                           int32_t N, int32_t m, const void* raw_kv, int32_t T_raw,
+                           const int64_t* raw_pos0, int32_t window, const float* sink,
+                           float softmax_scale, int32_t B, int32_t Tq, int32_t H, int32_t D,
+                           int32_t rope_dims, float rope_theta, const int64_t* q_pos0, void* out,
+                           void* workspace, size_t workspace_bytes, const float* q_norm_gain,
+                           float norm_eps, void* stream);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call on this thread. */

@@ -42,6 +42,11 @@ lib.csa_compress.argtypes = _COMPRESS_ARGS
 lib.csa_compress.restype = _i32
 lib.hca_compress.argtypes = _COMPRESS_ARGS
 lib.hca_compress.restype = _i32
+_COMPRESS_NORM_ARGS = _COMPRESS_ARGS[:-1] + [_vp, _f32, _vp]
+lib.csa_compress_rmsnorm.argtypes = _COMPRESS_NORM_ARGS
+lib.csa_compress_rmsnorm.restype = _i32
+lib.hca_compress_rmsnorm.argtypes = _COMPRESS_NORM_ARGS
+lib.hca_compress_rmsnorm.restype = _i32
 lib.indexer_topk_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 lib.indexer_topk_workspace_size.restype = _sz
 lib.indexer_topk.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _i32,
@@ -55,6 +60,10 @@ lib.csa_attend.restype = _i32
 lib.hca_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _f32, _i32,
                            _i32, _i32, _i32, _i32, _f32, _vp, _vp, _vp, _sz, _vp]
 lib.hca_attend.restype = _i32
+lib.csa_attend_rmsnorm.argtypes = lib.csa_attend.argtypes[:-1] + [_vp, _f32, _vp]
+lib.csa_attend_rmsnorm.restype = _i32
+lib.hca_attend_rmsnorm.argtypes = lib.hca_attend.argtypes[:-1] + [_vp, _f32, _vp]
+lib.hca_attend_rmsnorm.restype = _i32
 lib.lac_last_error.argtypes = []
 lib.lac_last_error.restype = ctypes.c_char_p
 lib.lac_time_next_launch.argtypes = [_i32, _vp, _vp]
@@ -122,29 +131,46 @@ def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
 
 
 # ---------------------------------------------------------------- compress
-def _compress(fn, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T, stream):
+def _norm_gain(gain, D, device):
+    if gain is None:
+        return None
+    if gain.dtype != torch.float32 or gain.numel() != D or gain.device != device or not gain.is_contiguous():
+        raise TypeError(f"norm gain must be a contiguous float32 tensor of {D} values on {device}")
+    return gain
+
+
+def _compress(fn, fn_norm, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T, norm_gain,
+              norm_eps, stream):
     B, _, D = raw_kv.shape
     T = raw_kv.shape[1] if T is None else T
     if logits.dtype != raw_kv.dtype:
         raise TypeError("raw_kv and logits must share a dtype")
-    _check(fn(_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _fmt(out), B, T, D, m,
-              rope_dims, rope_theta, _positions(pos0, B), _rows(raw_kv, "raw_kv"),
-              _rows(logits, "logits"), _rows(out, "out"), _stream(stream)))
+    args = [_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _fmt(out), B, T, D, m,
+            rope_dims, rope_theta, _positions(pos0, B), _rows(raw_kv, "raw_kv"),
+            _rows(logits, "logits"), _rows(out, "out")]
+    gain = _norm_gain(norm_gain, D, raw_kv.device)
+    if gain is None:
+        _check(fn(*args, _stream(stream)))
+    else:
+        _check(fn_norm(*args, _ptr(gain), norm_eps, _stream(stream)))
     return out
 
 
 def csa_compress(raw_kv, logits, out, m=4, rope_dims=64, rope_theta=10000.0, pos0=None, T=None,
-                 stream=None):
-    """Pool every m raw KV rows into one entry (see include/lac.h)."""
-    return _compress(lib.csa_compress, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T,
-                     stream)
+                 stream=None, norm_gain=None, norm_eps=1e-6):
+    """Pool every m raw KV rows into one entry (see include/lac.h); with
+    norm_gain [D] float32, each entry is RMSNorm'd before its rotation
+    (csa_compress_rmsnorm)."""
+    return _compress(lib.csa_compress, lib.csa_compress_rmsnorm, raw_kv, logits, out, m,
+                     rope_dims, rope_theta, pos0, T, norm_gain, norm_eps, stream)
 
 
 def hca_compress(raw_kv, logits, out, m=128, rope_dims=64, rope_theta=10000.0, pos0=None, T=None,
-                 stream=None):
-    """Pool every m' raw KV rows into one entry (see include/lac.h)."""
-    return _compress(lib.hca_compress, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T,
-                     stream)
+                 stream=None, norm_gain=None, norm_eps=1e-6):
+    """Pool every m' raw KV rows into one entry (see include/lac.h); with
+    norm_gain, each entry is RMSNorm'd first (hca_compress_rmsnorm)."""
+    return _compress(lib.hca_compress, lib.hca_compress_rmsnorm, raw_kv, logits, out, m,
+                     rope_dims, rope_theta, pos0, T, norm_gain, norm_eps, stream)
 
 
 # ---------------------------------------------------------------- indexer + top-k
@@ -188,32 +214,44 @@ def _attend_common(q, kv, raw_kv, out, raw_pos0, q_pos0):
 
 def csa_attend(q, ckv, topk_idx, raw_kv, window, q_pos0=None, raw_pos0=None, rope_dims=64,
                rope_theta=10000.0, sink=None, softmax_scale=0.0, out=None, workspace=None,
-               stream=None):
-    """Sparse MQA over the selected compressed entries + raw window (include/lac.h)."""
+               stream=None, q_norm_gain=None, norm_eps=1e-6):
+    """Sparse MQA over the selected compressed entries + raw window (include/lac.h);
+    with q_norm_gain [D] float32, each query head is RMSNorm'd first
+    (csa_attend_rmsnorm)."""
     B, Tq, H, D, out, T_raw, rp, qp = _attend_common(q, ckv, raw_kv, out, raw_pos0, q_pos0)
     k = topk_idx.shape[-1]
     kvf = _fmt(ckv)
     workspace = _workspace(workspace, attend_workspace_size(B, Tq, H, D, rope_dims, kvf, k, window),
                            q.device)
-    _check(lib.csa_attend(_ptr(q), _fmt(q), _ptr(ckv), kvf, ckv.shape[1], _ptr(topk_idx), k,
-                          _ptr(raw_kv), T_raw, rp, window, _ptr(sink), softmax_scale, B, Tq, H, D,
-                          rope_dims, rope_theta, qp, _ptr(out), _ptr(workspace),
-                          workspace.numel(), _stream(stream)))
+    args = [_ptr(q), _fmt(q), _ptr(ckv), kvf, ckv.shape[1], _ptr(topk_idx), k, _ptr(raw_kv), T_raw,
+            rp, window, _ptr(sink), softmax_scale, B, Tq, H, D, rope_dims, rope_theta, qp,
+            _ptr(out), _ptr(workspace), workspace.numel()]
+    gain = _norm_gain(q_norm_gain, D, q.device)
+    if gain is None:
+        _check(lib.csa_attend(*args, _stream(stream)))
+    else:
+        _check(lib.csa_attend_rmsnorm(*args, _ptr(gain), norm_eps, _stream(stream)))
     return out
 
 
 def hca_attend(q, hkv, raw_kv, window, m=128, q_pos0=None, raw_pos0=None, rope_dims=64,
                rope_theta=10000.0, sink=None, softmax_scale=0.0, out=None, workspace=None,
-               stream=None):
-    """Dense MQA over all visible compressed entries + raw window (include/lac.h)."""
+               stream=None, q_norm_gain=None, norm_eps=1e-6):
+    """Dense MQA over all visible compressed entries + raw window (include/lac.h);
+    with q_norm_gain, each query head is RMSNorm'd first (hca_attend_rmsnorm)."""
     B, Tq, H, D, out, T_raw, rp, qp = _attend_common(q, hkv, raw_kv, out, raw_pos0, q_pos0)
     N = hkv.shape[1]
     kvf = _fmt(hkv)
     workspace = _workspace(workspace, attend_workspace_size(B, Tq, H, D, rope_dims, kvf, N, window),
                            q.device)
-    _check(lib.hca_attend(_ptr(q), _fmt(q), _ptr(hkv), kvf, N, m, _ptr(raw_kv), T_raw, rp, window,
-                          _ptr(sink), softmax_scale, B, Tq, H, D, rope_dims, rope_theta, qp,
-                          _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    args = [_ptr(q), _fmt(q), _ptr(hkv), kvf, N, m, _ptr(raw_kv), T_raw, rp, window, _ptr(sink),
+            softmax_scale, B, Tq, H, D, rope_dims, rope_theta, qp, _ptr(out), _ptr(workspace),
+            workspace.numel()]
+    gain = _norm_gain(q_norm_gain, D, q.device)
+    if gain is None:
+        _check(lib.hca_attend(*args, _stream(stream)))
+    else:
+        _check(lib.hca_attend_rmsnorm(*args, _ptr(gain), norm_eps, _stream(stream)))
     return out
 
 

@@ -52,10 +52,21 @@ int32_t launch_status(const char* fn, hipError_t e) {
   return LAC_OK;
 }
 
+// The optional RMSNorm of an entry (norm_gain [D] float32, 16-byte aligned,
+// eps >= 0) keeps all D/8 channel groups of an entry in one wave, so it needs
+// D/8 to be a power of two of at most 64.
+int32_t check_norm(const char* fn, const float* gain, float eps) {
+  if (!gain) return fail(LAC_ERR_INVALID, "%s: null norm gain", fn);
+  if (!aligned(gain, 16)) return fail(LAC_ERR_INVALID, "%s: norm gain must be 16-byte aligned", fn);
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(LAC_ERR_INVALID, "%s: norm eps must be finite and >= 0", fn);
+  return LAC_OK;
+}
+
 int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, int32_t in_dtype,
                       void* out, int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
                       int32_t rope_dims, float rope_theta, const int64_t* pos0,
-                      int64_t kv_bstride, int64_t z_bstride, int64_t out_bstride, void* stream) {
+                      int64_t kv_bstride, int64_t z_bstride, int64_t out_bstride, void* stream,
+                      const float* norm_gain = nullptr, float norm_eps = 0.f, bool norm = false) {
   if (in_dtype != LAC_F32 && in_dtype != LAC_BF16)
     return fail(LAC_ERR_UNSUPPORTED, "%s: in_dtype must be LAC_F32 or LAC_BF16", fn);
   if (out_dtype < LAC_F32 || out_dtype > LAC_KV_E4M3_ROPE_BF16)
@@ -71,7 +82,16 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
   const int N = T / m;
   if (B > 1 && (kv_bstride < T || z_bstride < T || out_bstride < N))
     return fail(LAC_ERR_INVALID, "%s: batch strides must cover T rows (in) and T/m rows (out)", fn);
+  if (norm) {
+    const int G = D / 8;
+    if (G > 64 || (G & (G - 1)))
+      return fail(LAC_ERR_UNSUPPORTED, "%s: RMSNorm needs D/8 a power of two of at most 64 (D = %d)", fn, D);
+    const int32_t st = check_norm(fn, norm_gain, norm_eps);
+    if (st) return st;
+  }
   lac::CompressArgs a{};
+  a.norm_gain = norm ? norm_gain : nullptr;
+  a.norm_eps = norm_eps;
   int32_t st = take_positions(fn, "pos0", pos0, B, T, m, &a.pos0);
   if (st) return st;
   if ((int64_t)B * N == 0) { g_err[0] = 0; return LAC_OK; }
@@ -92,6 +112,7 @@ struct AttendCommon {
   const void* raw; int32_t T_raw; const int64_t* raw_pos0; int32_t W; const float* sink;
   float scale; int32_t B, Tq, H, D, r; float theta; const int64_t* q_pos0; void* out;
   void* ws; size_t ws_bytes; void* stream;
+  const float* q_norm_gain = nullptr; float norm_eps = 0.f; bool norm = false;
 };
 
 int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32_t* idx, int32_t k,
@@ -123,7 +144,13 @@ int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32
     return fail(LAC_ERR_UNSUPPORTED, "%s: the mixed KV format needs rope_dims and D - rope_dims multiples of 32", fn);
   if (mode == 0 && k < 0) return fail(LAC_ERR_INVALID, "%s: k = %d < 0", fn, k);
   if (mode == 1 && m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
+  if (c.norm) {
+    const int32_t st = check_norm(fn, c.q_norm_gain, c.norm_eps);
+    if (st) return st;
+  }
   lac::AttendArgs a{};
+  a.q_norm_gain = c.norm ? c.q_norm_gain : nullptr;
+  a.norm_eps = c.norm_eps;
   int32_t st = take_positions(fn, "q_pos0", c.q_pos0, c.B, c.Tq, 1, &a.qpos);
   if (st) return st;
   st = take_positions(fn, "raw_pos0", c.raw_pos0, c.B, c.T_raw, 1, &a.rawpos);
@@ -219,6 +246,36 @@ int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, v
   }
 }
 
+int32_t csa_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                             int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                             int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                             int64_t kv_batch_stride, int64_t logit_batch_stride,
+                             int64_t out_batch_stride, const float* norm_gain, float norm_eps,
+                             void* stream) {
+  try {
+    return compress_impl("csa_compress_rmsnorm", raw_kv, logits, in_dtype, out, out_dtype, B, T, D,
+                         m, rope_dims, rope_theta, pos0, kv_batch_stride, logit_batch_stride,
+                         out_batch_stride, stream, norm_gain, norm_eps, true);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "csa_compress_rmsnorm: internal error");
+  }
+}
+
+int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                             int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                             int32_t rope_dims, float rope_theta, const int64_t* pos0,
+                             int64_t kv_batch_stride, int64_t logit_batch_stride,
+                             int64_t out_batch_stride, const float* norm_gain, float norm_eps,
+                             void* stream) {
+  try {
+    return compress_impl("hca_compress_rmsnorm", raw_kv, logits, in_dtype, out, out_dtype, B, T, D,
+                         m, rope_dims, rope_theta, pos0, kv_batch_stride, logit_batch_stride,
+                         out_batch_stride, stream, norm_gain, norm_eps, true);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "hca_compress_rmsnorm: internal error");
+  }
+}
+
 size_t indexer_topk_workspace_size(int32_t B, int32_t Tq, int32_t N, int32_t k) {
   if (B < 0 || Tq < 0 || N < 0 || k < 1) return 0;
   return lac::indexer_workspace_bytes(B, Tq, N, k);
@@ -302,6 +359,41 @@ int32_t hca_attend(const void* q, int32_t q_dtype, const void* hkv, int32_t kv_d
     return attend_impl("hca_attend", c, 1, nullptr, 0, m);
   } catch (...) {
     return fail(LAC_ERR_DEVICE, "hca_attend: internal error");
+  }
+}
+
+int32_t csa_attend_rmsnorm(const void* q, int32_t q_dtype, const void* ckv, int32_t kv_dtype,
+                           int32_t N, const int32_t* topk_idx, int32_t k, const void* raw_kv,
+                           int32_t T_raw, const int64_t* raw_pos0, int32_t window,
+                           const float* sink, float softmax_scale, int32_t B, int32_t Tq,
+                           int32_t H, int32_t D, int32_t rope_dims, float rope_theta,
+                           const int64_t* q_pos0, void* out, void* workspace,
+                           size_t workspace_bytes, const float* q_norm_gain, float norm_eps,
+                           void* stream) {
+  try {
+    AttendCommon c{q, q_dtype, ckv, kv_dtype, N, raw_kv, T_raw, raw_pos0, window, sink,
+                   softmax_scale, B, Tq, H, D, rope_dims, rope_theta, q_pos0, out, workspace,
+                   workspace_bytes, stream, q_norm_gain, norm_eps, true};
+    return attend_impl("csa_attend_rmsnorm", c, 0, topk_idx, k, 1);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "csa_attend_rmsnorm: internal error");
+  }
+}
+
+int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int32_t kv_dtype,
+                           int32_t N, int32_t m, const void* raw_kv, int32_t T_raw,
+                           const int64_t* raw_pos0, int32_t window, const float* sink,
+                           float softmax_scale, int32_t B, int32_t Tq, int32_t H, int32_t D,
+                           int32_t rope_dims, float rope_theta, const int64_t* q_pos0, void* out,
+                           void* workspace, size_t workspace_bytes, const float* q_norm_gain,
+                           float norm_eps, void* stream) {
+  try {
+    AttendCommon c{q, q_dtype, hkv, kv_dtype, N, raw_kv, T_raw, raw_pos0, window, sink,
+                   softmax_scale, B, Tq, H, D, rope_dims, rope_theta, q_pos0, out, workspace,
+                   workspace_bytes, stream, q_norm_gain, norm_eps, true};
+    return attend_impl("hca_attend_rmsnorm", c, 1, nullptr, 0, m);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "hca_attend_rmsnorm: internal error");
   }
 }
 

@@ -206,6 +206,8 @@ struct KArgs {
   int64_t win_rows, row_bytes;
   Positions qpos;
   RopeTable rope;
+  const float* q_norm_gain;  // [D] or null: RMSNorm of each query head before its rotation
+  float norm_eps;
 };
 
 // Work item decomposition: blockIdx.x = split (fastest), blockIdx.y = work.
@@ -368,6 +370,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   __shared__ __align__(16) int vis_lo[2][kTile];
   __shared__ __align__(16) int vis_span[2][kTile];
   __shared__ __align__(16) float Sx[DS][4][64][8];             // partial logits [half][group][lane]
+  __shared__ float qss[DS][64];              // query RMSNorm: each D part's sum of squares per row
   __shared__ int32_t lidx[kIdxLds];
   __shared__ double freq[kMaxRopePairs];
   extern __shared__ float2 qang[];            // [G][r/2] (cos, sin) of t_g * freq_p
@@ -401,6 +404,21 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   const int row = rg * 16 + lr;
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
   const bool live = g < w.n_q;
+
+  // Optional RMSNorm of the query heads (before the rotation): the gains of
+  // the lane's dims are requested first -- before the query slices, so that
+  // the waits for the slices and the first tile count their loads exactly.
+  const bool qnorm = a.q_norm_gain != nullptr;
+  float4 qg[Gm::KH][2];
+  float q_inv = 1.f;
+  if (qnorm) {
+#pragma unroll
+    for (int s = 0; s < Gm::KH; ++s) {
+      const float* gp = a.q_norm_gain + dh * Gm::DW + 32 * s + 8 * lq;
+      qg[s][0] = *reinterpret_cast<const float4*>(gp);
+      qg[s][1] = *reinterpret_cast<const float4*>(gp + 4);
+    }
+  }
 
   // query slices of the wave's part of D into registers first
   bf16x8 qreg[Gm::KH];
@@ -511,7 +529,10 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
     }
   };
 
-  if (n_tiles > 0) load_tile(e_lo);
+  // Unconditional (past the split's end the slots are empty and read a valid
+  // address), so the waits for the query slices below can count the three
+  // tile loads issued after them and leave those in flight.
+  load_tile(e_lo);
 
   // the block's query angles, then the lane's query slices rotated at t
   for (int e = tid; e < G * npair; e += NT) {
@@ -520,20 +541,58 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
     rope_cos_sin((double)(w.t_first + gg), freq[p], &cs, &sn);
     qang[e] = make_float2(cs, sn);
   }
-  __syncthreads();
-  const float2* ang = qang + (live ? g : 0) * npair;
+  float q_ss = 0.f;
+  if (qnorm) {
+    // the row's four lanes, then (D split over two waves) the other half
 #pragma unroll
-  for (int s = 0; s < Gm::KH; ++s) {
-    const int d0 = dh * Gm::DW + 32 * s + 8 * lq;
-    if (d0 >= nope) {
+    for (int s = 0; s < Gm::KH; ++s) {
       uint32_t wd[4];
       __builtin_memcpy(wd, &qreg[s], 16);
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        const float2 cv = ang[(d0 - nope) / 2 + p];
         const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
-        wd[p] = pack_bf16x2(x0 * cv.x - x1 * cv.y, x0 * cv.y + x1 * cv.x);
+        q_ss = fmaf(x0, x0, fmaf(x1, x1, q_ss));
       }
+    }
+    q_ss += __shfl_xor(q_ss, 16);
+    q_ss += __shfl_xor(q_ss, 32);
+    if (lq == 0) qss[dh][row] = q_ss;
+  }
+  __syncthreads();
+  if (qnorm) {
+    if constexpr (DS == 2) q_ss += qss[1 - dh][row];
+    q_inv = 1.0f / sqrtf(q_ss / (float)D + a.norm_eps);
+  }
+  const float2* ang = qang + (live ? g : 0) * npair;
+#pragma unroll
+  for (int s = 0; s < Gm::KH; ++s) {
+    const int d0 = dh * Gm::DW + 32 * s + 8 * lq;
+    if (qnorm || d0 >= nope) {
+      uint32_t wd[4];
+      __builtin_memcpy(wd, &qreg[s], 16);
+      float x[8];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        x[2 * p] = bf16_to_f32(wd[p] & 0xffffu);
+        x[2 * p + 1] = bf16_to_f32(wd[p] >> 16);
+      }
+      if (qnorm) {
+        const float gv[8] = {qg[s][0].x, qg[s][0].y, qg[s][0].z, qg[s][0].w,
+                             qg[s][1].x, qg[s][1].y, qg[s][1].z, qg[s][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] *= q_inv * gv[i];
+      }
+      if (d0 >= nope) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float2 cv = ang[(d0 - nope) / 2 + p];
+          const float x0 = x[2 * p], x1 = x[2 * p + 1];
+          x[2 * p] = x0 * cv.x - x1 * cv.y;
+          x[2 * p + 1] = x0 * cv.y + x1 * cv.x;
+        }
+      }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) wd[p] = pack_bf16x2(x[2 * p], x[2 * p + 1]);
       __builtin_memcpy(&qreg[s], wd, 16);
     }
   }
@@ -879,6 +938,15 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   for (int e = tid; e < H * D; e += blockDim.x) qs[e] = q[e];
   for (int h = tid; h < H; h += blockDim.x) { mrow[h] = -INFINITY; lrow[h] = 0.f; }
   __syncthreads();
+  if (a.q_norm_gain) {                // RMSNorm of each head, before the rotation
+    for (int h = tid; h < H; h += blockDim.x) {
+      float ss = 0.f;
+      for (int c = 0; c < D; ++c) ss = fmaf(qs[h * D + c], qs[h * D + c], ss);
+      const float inv = 1.0f / sqrtf(ss / (float)D + a.norm_eps);
+      for (int c = 0; c < D; ++c) qs[h * D + c] *= inv * a.q_norm_gain[c];
+    }
+    __syncthreads();
+  }
   for (int e = tid; e < H * (a.r / 2); e += blockDim.x) {
     const int h = e / (a.r / 2), p = e % (a.r / 2);
     float cs, sn;
@@ -1032,6 +1100,8 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   k.H = a.H; k.D = a.D; k.r = a.r; k.theta = a.theta;
   make_rope_table(&k.rope, a.r, a.theta);
   k.scale_log2 = a.scale * 1.4426950408889634f;
+  k.q_norm_gain = a.q_norm_gain;
+  k.norm_eps = a.norm_eps;
   k.G = p.G; k.Hs = p.Hs; k.n_htiles = p.n_htiles; k.n_qgroups = p.n_qgroups;
   k.nsplit = p.nsplit; k.chunk = p.chunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;
   k.qpos = a.qpos;

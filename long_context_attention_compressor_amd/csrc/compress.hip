@@ -16,6 +16,12 @@
 // (HCA), S threads split the tokens and merge their partial states through
 // LDS in a log2(S)-level tree, so short sequences still spread over many
 // lanes.  The rotation table is built while the first loads are in flight.
+//
+// Optional RMSNorm of each entry before its rotation ("深度解析 DeepSeek-V4",
+// section "Attention Sink": RMSNorm of the queries and compressed KV entries
+// before core attention): the block then holds all channel groups of an
+// entry, whose GB threads are consecutive lanes of one wave, and the entry's
+// sum of squares is reduced across them with lane shuffles.
 #include "lac_internal.h"
 
 namespace lac {
@@ -109,6 +115,12 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
   float mx[8], den[8], acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) { mx[c] = -INFINITY; den[c] = 0.f; acc[c] = 0.f; }
+  // the gains of this thread's 8 channels, requested first
+  float4 gain0 = make_float4(1.f, 1.f, 1.f, 1.f), gain1 = gain0;
+  if (a.norm_gain) {
+    gain0 = *reinterpret_cast<const float4*>(a.norm_gain + g * 8);
+    gain1 = *reinterpret_cast<const float4*>(a.norm_gain + g * 8 + 4);
+  }
 
   if (live) {
     const int per = a.per;
@@ -180,6 +192,18 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
   float o[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) o[c] = acc[c] / den[c];
+  if (a.norm_gain) {
+    // RMSNorm over the entry's D channels: its GB (a power of two, at most
+    // 64) threads are lanes t .. t + GB - 1 of one wave, aligned to GB.
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(o[c], o[c], ss);
+    for (int off = 1; off < GB; off <<= 1) ss += __shfl_xor(ss, off);
+    const float inv = 1.0f / sqrtf(ss / (float)a.D + a.norm_eps);
+    const float gv[8] = {gain0.x, gain0.y, gain0.z, gain0.w, gain1.x, gain1.y, gain1.z, gain1.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) o[c] = o[c] * inv * gv[c];
+  }
 
   const int c0 = g * 8;
   const int nope = a.D - a.r;
@@ -243,10 +267,14 @@ hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   // (a bf16 thread's loads are then all in flight at once), then give a
   // block at most 256 threads: GB channel groups of one entry, or whole
   // entries when an entry needs fewer threads.
+  // With RMSNorm the block keeps all G channel groups of an entry (G is a
+  // power of two, at most 64 with the norm), and the token split shrinks to
+  // fit: a long block (m' = 128) is then streamed by one compute unit.
   int S = 1;
   while (a.m / S > 8 && S < 256 && a.m % (2 * S) == 0) S *= 2;
   int GB = G;
-  while (GB * S > 256 && GB % 2 == 0) GB /= 2;
+  if (a.norm_gain == nullptr)
+    while (GB * S > 256 && GB % 2 == 0) GB /= 2;
   if (GB * S > 512) {           // few channel groups and a long block: fewer splits
     while (GB * S > 512) S /= 2;
   }

@@ -39,6 +39,8 @@ struct CompressArgs {
   int B, T, D, m, r;
   float theta;
   int64_t kv_bstride, z_bstride, out_bstride;  // rows
+  const float* norm_gain;   // [D] or null: RMSNorm of each entry before its rotation
+  float norm_eps;
   // set by the launcher: tokens per thread, entries, block (gb, s, epb)
   int per, N, gb, s, epb;
   RopeTable rope;
@@ -88,6 +90,8 @@ struct AttendArgs {
   float theta, scale;
   int n_entries;          // k (CSA) or N (HCA): sizes the split plan
   Positions qpos, rawpos;
+  const float* q_norm_gain;   // [D] or null: RMSNorm of each query head before its rotation
+  float norm_eps;
 };
 size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries,
                               int W);

@@ -16,9 +16,12 @@ from . import BF16, F32, MIXED, attend, compress, encode_rows, index_scores, top
 FMT = {"f32": F32, "bf16": BF16, "mixed": MIXED}
 
 
-def compress_store(x, z, in_fmt, out_fmt, B, T, D, m, r, theta, pos0):
-    """Compress and encode into the storage format: uint8 [B, T//m, row_bytes]."""
-    vals = compress(x, z, FMT[in_fmt], B, T, D, m, r, theta, pos0)
+def compress_store(x, z, in_fmt, out_fmt, B, T, D, m, r, theta, pos0, norm_gain=None,
+                   norm_eps=1e-6):
+    """Compress (RMSNorm'd with norm_gain when given) and encode into the
+    storage format: uint8 [B, T//m, row_bytes]."""
+    vals = compress(x, z, FMT[in_fmt], B, T, D, m, r, theta, pos0, norm_gain=norm_gain,
+                    norm_eps=norm_eps)
     N = T // m
     return encode_rows(vals.reshape(B * N, D), FMT[out_fmt], r).reshape(B, N, -1)
 
