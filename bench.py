@@ -41,9 +41,9 @@ BF16_PEAK_TFLOPS = 2500.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273731632, "csa_decode_128k": 277462983,
-                       "csa_chunk_prefill": 1332494273, "pair_decode_1m_e4m3_indexer": 139523310}
-SCORE_TRAFFIC_SOURCE_SHA256 = "00fcebfdb594ec465685d01b9fcdac003d938ef8d2b06275c755a06f178c0668"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273731094, "csa_decode_128k": 277462158,
+                       "csa_chunk_prefill": 1302840682, "pair_decode_1m_e4m3_indexer": 139523079}
+SCORE_TRAFFIC_SOURCE_SHA256 = "2752de378f707f48b2411f0971f74669c2da734ed1ba2269681b4b572e34f332"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
