@@ -85,6 +85,8 @@ def _load():
     lib.lo_attend2.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, vp,
                                dbl, i32, i32, i32, i32, i32, dbl, vp, vp, i32, vp, dbl, vp]
     lib.lo_attend2.restype = i32
+    lib.lo_grouped_projection.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp]
+    lib.lo_grouped_projection.restype = i32
     lib.lo_num_threads.argtypes = []
     lib.lo_num_threads.restype = i32
     _lib = lib
@@ -249,4 +251,18 @@ def attend(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W
                             _p(out))
     if rc:
         raise ValueError(f"lo_attend rejected its arguments ({rc})")
+    return out
+
+
+def grouped_projection(attn, w1, w2, dtype, T, H, D, G, d_g, d, y_dtype=F64):
+    """Grouped output projection (QbitAI rewrite, grouped output projection
+    step): heads split into G groups of H/G consecutive heads, group g's
+    concatenated outputs projected by W1[g] [d_g, (H/G)*D], the concatenation
+    of the G results by W2 [d, G*d_g].  y_dtype=BF16 rounds the intermediate
+    to bfloat16 between the products.  -> float64 [T, d]."""
+    out = np.empty((T, d), np.float64)
+    rc = _load().lo_grouped_projection(_p(attn), _p(w1), _p(w2), dtype, T, H, D, G, d_g, d,
+                                       y_dtype, _p(out))
+    if rc:
+        raise ValueError(f"lo_grouped_projection rejected its arguments ({rc})")
     return out

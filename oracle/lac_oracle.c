@@ -26,6 +26,9 @@
  *        BF16 bit-layout table in section "三、FP4量化".
  *   [P1] "DeepSeek V4的4个技巧" (hubwiz.com), section "技巧1：混合注意力"
  *        (top 2048 of the summary blocks).
+ *   [P3] also: the grouped output projection step (heads in g groups, each
+ *        projected to d_g, the concatenation projected back to d), which
+ *        follows core attention.
  *
  * Where the pages leave a step open, the plainest reading is taken; each is
  * named where it is used (and listed in the design notes of the repository).
@@ -481,6 +484,55 @@ int lo_attend(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, i
               int n_rows, double* out) {
     return lo_attend2(q, q_dtype, kv, kv_dtype, N, mode, idx, k, m, raw, T_raw, raw_pos0, W,
                       sink, scale, B, Tq, H, D, r, theta, qpos0, rows, n_rows, NULL, 0.0, out);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Grouped output projection ([P3]: with head dimension c = 512, projecting  */
+/* every head's output straight back to d would be costly, so the n_h heads  */
+/* are split into g groups, each group is projected to an intermediate      */
+/* width d_g, and the concatenation is projected back to d).  Reading: group */
+/* gi holds heads gi*H/G .. (gi+1)*H/G - 1, concatenated in head order;      */
+/*   y[gi] = W1[gi] x[gi]  (W1 [G, d_g, (H/G)*D]),                          */
+/*   out   = W2 [y[0]; ...; y[G-1]]  (W2 [d, G*d_g]).                        */
+/* attn [T, H, D] and the weights are stored in `dtype` (F32 | BF16);       */
+/* out [T, d] in double.  y_dtype is the format y is held in between the    */
+/* two products: F64 keeps it exact, BF16 rounds it to nearest even first   */
+/* (what a caller that stores y in bfloat16 computes).                       */
+/* ------------------------------------------------------------------------ */
+int lo_grouped_projection(const void* attn, const void* w1, const void* w2, int dtype, int T,
+                          int H, int D, int G, int d_g, int d, int y_dtype, double* out) {
+    if (G < 1 || H % G || T < 0 || D < 1 || d_g < 1 || d < 1) return 1;
+    if (y_dtype != 3 && y_dtype != 1) return 1;
+    int64_t K1 = (int64_t)(H / G) * D, Y = (int64_t)G * d_g;
+    int64_t t;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (t = 0; t < T; ++t) {
+        double* x = malloc(sizeof(double) * (size_t)H * D);
+        double* y = malloc(sizeof(double) * (size_t)Y);
+        double* row = malloc(sizeof(double) * (size_t)(K1 > Y ? K1 : Y));
+        int64_t gi, j, c;
+        decode_row((const uint8_t*)attn + t * row_bytes(dtype, H * D, 0), dtype, H * D, 0, x);
+        for (gi = 0; gi < G; ++gi)
+            for (j = 0; j < d_g; ++j) {
+                decode_row((const uint8_t*)w1 + (gi * d_g + j) * row_bytes(dtype, (int)K1, 0),
+                           dtype, (int)K1, 0, row);
+                double acc = 0.0;
+                for (c = 0; c < K1; ++c) acc += row[c] * x[gi * K1 + c];
+                y[gi * d_g + j] = acc;
+            }
+        if (y_dtype == 1)
+            for (c = 0; c < Y; ++c) y[c] = lo_bf16_decode(lo_bf16_encode(y[c]));
+        for (j = 0; j < d; ++j) {
+            decode_row((const uint8_t*)w2 + j * row_bytes(dtype, (int)Y, 0), dtype, (int)Y, 0, row);
+            double acc = 0.0;
+            for (c = 0; c < Y; ++c) acc += row[c] * y[c];
+            out[t * d + j] = acc;
+        }
+        free(x);
+        free(y);
+        free(row);
+    }
+    return 0;
 }
 
 int lo_num_threads(void) {
