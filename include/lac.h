@@ -264,6 +264,32 @@ int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int3
                            void* workspace, size_t workspace_bytes, const float* q_norm_gain,
                            float norm_eps, void* stream);
 
+/*
+ * grouped_output_projection -- the projection after core attention, in two
+ * dense products ([P3], grouped output projection step: with a head
+ * dimension of 512 the n_h heads are split into g groups, each group's output
+ * is projected to an intermediate width d_g, and the concatenated results
+ * are projected back to the model width d):
+ *     y[t, g*d_g + j] = sum_c w1[g, j, c] * attn[t, g*(H/G)*D + c]
+ *     out[t, j]       = sum_c w2[j, c]    * y[t, c]
+ *   Group g holds heads g*H/G .. (g+1)*H/G - 1, concatenated in head order.
+ *   attn  [T, H, D] bfloat16 (the attend output with T = B * Tq)
+ *   w1    [G, d_g, (H/G)*D] bfloat16
+ *   w2    [d, G*d_g] bfloat16
+ *   out   [T, d] bfloat16 (fp32 accumulation, rounded to nearest even)
+ *   workspace >= grouped_projection_workspace_size(T, G, d_g) bytes: holds
+ *         y [T, G*d_g] in bfloat16 between the products (rounded to nearest
+ *         even, as a caller storing y in bfloat16 would).
+ *   Supported: (H/G)*D and G*d_g multiples of 128, d_g and d multiples of 256,
+ *   H*D, G*d_g and d at most 2^22; others return LAC_ERR_UNSUPPORTED.  T = 0
+ *   is a no-op.  G must divide H (else LAC_ERR_INVALID).
+ */
+size_t grouped_projection_workspace_size(int32_t T, int32_t G, int32_t d_g);
+int32_t grouped_output_projection(const void* attn, const void* w1, const void* w2, int32_t T,
+                                  int32_t H, int32_t D, int32_t G, int32_t d_g, int32_t d,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call on this thread. */
 const char* lac_last_error(void);
@@ -272,14 +298,17 @@ const char* lac_last_error(void);
  * Launch timer, for measurement.  Arms a one-shot request on this thread:
  * the next launch of kernel `kernel` (LAC_KERNEL_*) enqueued by this thread
  * records hipEvent_t `start` just before it and `stop` just after it, on the
- * stream of the launch.  Passing NULL events disarms.
+ * stream of the launch.  Passing NULL events disarms.  LAC_KERNEL_PROJECT
+ * brackets both launches of one grouped_output_projection call (its two
+ * products run the same kernel).
  */
 enum {
     LAC_KERNEL_COMPRESS = 0,
     LAC_KERNEL_INDEXER_SCORE = 1,
     LAC_KERNEL_TOPK = 2,
     LAC_KERNEL_ATTEND = 3,
-    LAC_KERNEL_COMBINE = 4
+    LAC_KERNEL_COMBINE = 4,
+    LAC_KERNEL_PROJECT = 5
 };
 int32_t lac_time_next_launch(int32_t kernel, void* start, void* stop);
 

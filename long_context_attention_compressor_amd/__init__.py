@@ -21,11 +21,13 @@ import torch
 __all__ = [
     "LacError", "csa_compress", "hca_compress", "indexer_topk", "indexer_topk_workspace_size",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
+    "grouped_output_projection", "grouped_projection_workspace_size",
     "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "KERNELS",
 ]
 
 LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 = 0, 1, 2
-KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4}
+KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4,
+           "project": 5}
 STATUS = {0: "LAC_OK", 1: "LAC_ERR_INVALID", 2: "LAC_ERR_UNSUPPORTED", 3: "LAC_ERR_WORKSPACE",
           4: "LAC_ERR_DEVICE"}
 
@@ -64,6 +66,11 @@ lib.csa_attend_rmsnorm.argtypes = lib.csa_attend.argtypes[:-1] + [_vp, _f32, _vp
 lib.csa_attend_rmsnorm.restype = _i32
 lib.hca_attend_rmsnorm.argtypes = lib.hca_attend.argtypes[:-1] + [_vp, _f32, _vp]
 lib.hca_attend_rmsnorm.restype = _i32
+lib.grouped_projection_workspace_size.argtypes = [_i32, _i32, _i32]
+lib.grouped_projection_workspace_size.restype = _sz
+lib.grouped_output_projection.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
+                                          _vp, _sz, _vp]
+lib.grouped_output_projection.restype = _i32
 lib.lac_last_error.argtypes = []
 lib.lac_last_error.restype = ctypes.c_char_p
 lib.lac_time_next_launch.argtypes = [_i32, _vp, _vp]
@@ -252,6 +259,37 @@ def hca_attend(q, hkv, raw_kv, window, m=128, q_pos0=None, raw_pos0=None, rope_d
         _check(lib.hca_attend(*args, _stream(stream)))
     else:
         _check(lib.hca_attend_rmsnorm(*args, _ptr(gain), norm_eps, _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------- grouped output projection
+def grouped_projection_workspace_size(T, G, d_g) -> int:
+    return int(lib.grouped_projection_workspace_size(T, G, d_g))
+
+
+def grouped_output_projection(attn, w1, w2, out=None, workspace=None, stream=None):
+    """attn [..., H, D] bf16 (leading dims flattened to T tokens), w1 [G, d_g,
+    (H/G)*D] bf16, w2 [d, G*d_g] bf16 -> out [T, d] bf16."""
+    for t, what in ((attn, "attn"), (w1, "w1"), (w2, "w2")):
+        _need_dense(t, what)
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{what} must be bfloat16")
+    H, D = attn.shape[-2], attn.shape[-1]
+    T = attn.numel() // (H * D) if H * D else 0
+    G, d_g = w1.shape[0], w1.shape[1]
+    d = w2.shape[0]
+    if w1.dim() != 3 or w2.dim() != 2 or w2.shape[1] != G * d_g:
+        raise ValueError("w1 must be [G, d_g, (H/G)*D] and w2 [d, G*d_g]")
+    if H % G or w1.shape[2] != (H // G) * D:
+        raise ValueError("w1's last dim must be (H/G)*D")
+    if out is None:
+        out = torch.empty((T, d), dtype=torch.bfloat16, device=attn.device)
+    elif out.dtype != torch.bfloat16 or out.numel() != T * d or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bf16 tensor of T*d values")
+    workspace = _workspace(workspace, grouped_projection_workspace_size(T, G, d_g), attn.device)
+    _check(lib.grouped_output_projection(_ptr(attn), _ptr(w1), _ptr(w2), T, H, D, G, d_g, d,
+                                         _ptr(out), _ptr(workspace), workspace.numel(),
+                                         _stream(stream)))
     return out
 
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblac.so")
-SOURCES = ["abi.cpp", "compress.hip", "score.hip", "indexer.hip", "attend.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "score.hip", "indexer.hip", "attend.hip", "project.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -397,6 +397,43 @@ int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int3
   }
 }
 
+size_t grouped_projection_workspace_size(int32_t T, int32_t G, int32_t d_g) {
+  if (T < 0 || G < 1 || d_g < 1) return 0;
+  return (size_t)T * (size_t)G * (size_t)d_g * 2;
+}
+
+int32_t grouped_output_projection(const void* attn, const void* w1, const void* w2, int32_t T,
+                                  int32_t H, int32_t D, int32_t G, int32_t d_g, int32_t d,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  const char* fn = "grouped_output_projection";
+  try {
+    if (T < 0 || H < 1 || D < 1 || G < 1 || d_g < 1 || d < 1)
+      return fail(LAC_ERR_INVALID, "%s: negative T or a width < 1", fn);
+    if (H % G) return fail(LAC_ERR_INVALID, "%s: G = %d does not divide H = %d", fn, G, H);
+    const int64_t K1 = (int64_t)(H / G) * D, Y = (int64_t)G * d_g;
+    if ((int64_t)H * D > (1 << 22) || Y > (1 << 22) || d > (1 << 22))
+      return fail(LAC_ERR_UNSUPPORTED, "%s: H*D, G*d_g and d must be at most 2^22", fn);
+    if (!lac::projection_shape_ok(K1, d_g, Y, d))
+      return fail(LAC_ERR_UNSUPPORTED,
+                  "%s: needs (H/G)*D and G*d_g multiples of 128, d_g and d multiples of 256", fn);
+    if (T == 0) return LAC_OK;
+    if (!attn || !w1 || !w2 || !out) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
+    if (!aligned(attn, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16))
+      return fail(LAC_ERR_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+    const size_t need = grouped_projection_workspace_size(T, G, d_g);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned and hold %zu bytes",
+                  fn, need);
+    lac::ProjectArgs p{attn, w1, w2, workspace, out, T, H, D, G, d_g, d};
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    lac::TimedLaunch tl(lac::kKernelProject, st);
+    return launch_status(fn, lac::launch_projection(p, st));
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "%s: internal error", fn);
+  }
+}
+
 const char* lac_last_error(void) { return g_err; }
 
 int32_t lac_time_next_launch(int32_t kernel, void* start, void* stop) {

@@ -16,7 +16,8 @@ enum KernelId {
   kKernelTopk = 2,
   kKernelAttend = 3,
   kKernelCombine = 4,
-  kKernelCount = 5
+  kKernelProject = 5,
+  kKernelCount = 6
 };
 
 // One-shot, thread-local launch timer (see lac_time_next_launch).  Records the
@@ -100,5 +101,19 @@ size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, in
 constexpr int kMaxSplit = 2048;
 int attend_split_count(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st);
+
+// ---------------------------------------------------------------- grouped output projection
+struct ProjectArgs {
+  const void* attn;       // [T, H, D] bf16
+  const void* w1;         // [G, d_g, (H/G)*D] bf16
+  const void* w2;         // [d, G*d_g] bf16
+  void* y;                // [T, G*d_g] bf16 (workspace)
+  void* out;              // [T, d] bf16
+  int T, H, D, G, d_g, d;
+};
+// Contraction widths K1 = (H/G)*D and G*d_g, output widths d_g and d that the
+// product kernel tiles exactly.
+bool projection_shape_ok(int64_t K1, int64_t d_g, int64_t Kout, int64_t d);
+hipError_t launch_projection(const ProjectArgs& p, hipStream_t st);
 
 }  // namespace lac

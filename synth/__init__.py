@@ -187,3 +187,17 @@ def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI
         q_csa=store(normal(seed, "q_csa", (B, 1, H, D), device=device), "bf16"),
         q_hca=store(normal(seed, "q_hca", (B, 1, H, D), device=device), "bf16"),
     )
+
+
+def projection(seed=5, T=4096, H=64, D=512, G=8, d_g=1024, d=7168, device="cpu"):
+    """Inputs of the grouped output projection: attention outputs [T, H, D]
+    ~ N(0, 1) and weights scaled by 1/sqrt(fan-in) (W1 [G, d_g, (H/G)*D],
+    W2 [d, G*d_g]) so that the intermediate and the output stay near unit
+    scale; all bf16."""
+    K1 = (H // G) * D
+    return dict(
+        kind="projection", T=T, H=H, D=D, G=G, d_g=d_g, d=d,
+        attn=store(normal(seed, "attn", (T, H, D), device=device), "bf16"),
+        w1=store(normal(seed, "w1", (G, d_g, K1), std=K1 ** -0.5, device=device), "bf16"),
+        w2=store(normal(seed, "w2", (d, G * d_g), std=(G * d_g) ** -0.5, device=device), "bf16"),
+    )

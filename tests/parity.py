@@ -8,7 +8,17 @@ Tolerances (written here once, used by every parity test):
   * top-k: identical sets except entries whose oracle score lies within
     1e-3 |s_k| + 1e-6 of the oracle's k-th score (near-ties);
   * attention outputs: per (b, t, h) row, max_c |g - r| / max_c |r| <= 1e-2
-    (bf16 operands, fp32 accumulation), r the oracle's double result.
+    (bf16 operands, fp32 accumulation), r the oracle's double result;
+  * grouped projection outputs (bf16, against the oracle with the same
+    bfloat16 rounding of the intermediate y):
+        |g - r| <= 2^-8 |r| + (1 + 2^-8) F + A
+    2^-8 |r|: the output's own rounding (bf16 keeps 8 significant bits, so
+    rounding to nearest moves a value by at most 2^-8 of itself).  F: the
+    GPU sums y in fp32 before rounding it, so where the exact y lies within
+    that sum's error bound of a bf16 rounding midpoint it may round to the
+    neighbouring value; F adds |W2[j, c]| * ulp(y_c) over those c.  A: the
+    fp32 error bound of the second sum.  An fp32 sum of K exact bf16 products
+    in MFMA steps of 16 is within (K/16 + 1) 2^-24 sum|terms| of the exact sum.
 """
 from __future__ import annotations
 
@@ -89,3 +99,29 @@ def check_attention(gpu: np.ndarray, ref: np.ndarray, what=""):
     worst = float(rel.max()) if rel.size else 0.0
     assert worst <= ATTN_TOL, f"{what}: worst row relative error {worst:.3e}"
     return worst
+
+
+def _sum_bound(K, abs_sum):
+    return (K / 16 + 1) * 2.0 ** -24 * abs_sum
+
+
+def check_projection(gpu: np.ndarray, ref: np.ndarray, attn, w1, w2, what: str):
+    """gpu, ref: [rows, d] float64; attn [rows, H, D], w1 [G, d_g, K1], w2 [d, G*d_g]
+    as float64 arrays (the stored bf16 values)."""
+    rows = attn.shape[0]
+    G, d_g, K1 = w1.shape
+    x = attn.reshape(rows, G, K1)
+    y = np.einsum("tgk,gjk->tgj", x, w1).reshape(rows, G * d_g)
+    ya = np.einsum("tgk,gjk->tgj", np.abs(x), np.abs(w1)).reshape(rows, G * d_g)
+    rho = _sum_bound(K1, ya)
+    ay = np.maximum(np.abs(y), 2.0 ** -126)
+    ulp = 2.0 ** (np.floor(np.log2(ay)) - 7)
+    frac = np.abs(y) / ulp - np.floor(np.abs(y) / ulp)
+    near = np.abs(frac - 0.5) * ulp <= rho
+    F = (np.where(near, ulp, 0.0)) @ np.abs(w2).T
+    A = _sum_bound(G * d_g, (np.abs(y) + np.where(near, ulp, 0.0)) @ np.abs(w2).T)
+    bad = np.abs(gpu - ref) > 2.0 ** -8 * np.abs(ref) + (1 + 2.0 ** -8) * F + A
+    scale = np.max(np.abs(ref), axis=1, keepdims=True)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} projection outputs out of "
+                           f"tolerance, worst {np.max(np.abs(gpu - ref) / scale):.3g} of row max, "
+                           f"{int(near.sum())} intermediates near a rounding midpoint")
