@@ -62,6 +62,23 @@ def _score_traffic(workload):
     return SCORE_TRAFFIC_BYTES.get(workload)
 
 
+# The same for the product kernel of the grouped output projection: bytes per
+# launch averaged over its two launches (the per-group product and the output
+# product), for the kernel source identified by its SHA-256.
+PROJECT_TRAFFIC_BYTES = 755184243
+PROJECT_TRAFFIC_SOURCE_SHA256 = "a23af54f34706030dce69fa0edf628c91b5176cc7024d0a0df88fc528e3c5fd1"
+PROJECT_SOURCES = ("project.hip", "lac_device.h")
+
+
+def _project_traffic():
+    import hashlib
+    h = hashlib.sha256()
+    for name in PROJECT_SOURCES:
+        with open(os.path.join(ROOT, "long_context_attention_compressor_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return PROJECT_TRAFFIC_BYTES if h.hexdigest() == PROJECT_TRAFFIC_SOURCE_SHA256 else None
+
+
 def _rows(t, r0, r1):
     return t[:, r0:r1]
 
@@ -514,7 +531,7 @@ def main():
         launches = 1
         if isinstance(wl, ProjectionPrefill):
             # one timed span holds both products (the same kernel, launched twice)
-            kfl, kname, traffic, launches = fl, wl.kernel, None, 2
+            kfl, kname, traffic, launches = fl, wl.kernel, _project_traffic(), 2
         elif isinstance(wl, HcaPrefill):
             kfl, kname, traffic = fl, "attend_mfma_kernel (HCA attention)", None
         else:

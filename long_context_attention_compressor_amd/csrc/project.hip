@@ -18,9 +18,13 @@
 // steps of 32: per step the block stages a 256 x 32 slice of each operand in
 // LDS with loads that write LDS directly (no registers), four slots deep, so
 // a slice is requested three steps before it is read; the fragments of the
-// next slice are read from LDS while the current one's MFMAs run.  Rows are 64 bytes;
-// their four 16-byte chunks are XOR-swizzled by row pair so that eight
-// lanes reading one chunk column hit eight different bank groups.  Per
+// next slice are read from LDS while the current one's MFMAs run.  Rows are
+// 64 bytes; their four 16-byte chunks are XOR-swizzled by (row / 4) % 4.
+// A 16-byte LDS read is served 16 lanes at a time over 64 four-byte banks
+// (256 bytes): sixteen consecutive rows at one logical chunk then fill all
+// 16 slots of the bank window (the rocprofv3 counter SQ_LDS_BANK_CONFLICT
+// reads 0; keyed by row pair, which would suit 8 lanes over 32 banks, it
+// reads half the LDS busy cycles).  Per
 // 16-deep step a wave reads 4 A and 4 B fragments (8 KB from LDS) for 16
 // MFMAs.  The MFMA takes the weight fragment as its first operand, so a
 // lane's accumulator holds four runs of four consecutive output columns of
@@ -103,14 +107,14 @@ gemm_nt_bf16_kernel(GemmArgs a) {
 
   // Staging: a load instruction fills 1 KB of LDS, lane i the 16 bytes at
   // 16 i, i.e. rows of 64 bytes, lane i at row i / 4, slot i % 4.  Slot s of
-  // row r holds the row's chunk s ^ ((r / 2) % 4), so each lane fetches that
+  // row r holds the row's chunk s ^ ((r / 4) % 4), so each lane fetches that
   // chunk.  Wave w stages rows 64 w .. 64 w + 63 of both operands (4 loads
   // each).
   int aofs[4], bofs[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int row = wave * 64 + u * 16 + (l >> 2);
-    const int chunk = (l & 3) ^ ((row >> 1) & 3);
+    const int chunk = (l & 3) ^ ((row >> 2) & 3);
     aofs[u] = (int)((int64_t)row * a.lda * 2) + chunk * 16;
     bofs[u] = (int)((int64_t)row * a.ldb * 2) + chunk * 16;
   }
@@ -132,7 +136,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x16{};
 
   // Fragment rows: A row wm*128 + i*32 + ln, B row wn*128 + j*32 + ln; the
-  // row's swizzle key is (ln / 2) % 4 (the tile offsets are multiples of 8).
+  // row's swizzle key is (ln / 4) % 4 (the tile offsets are multiples of 32).
   // F[kk][0..3] are the A fragments of 16-deep step kk, F[kk][4..7] the B ones.
   const int arow = (wm * 128 + ln) * kRowB, brow = (wn * 128 + ln) * kRowB;
   typedef bf16x8 Frags[kBK / 16][8];
@@ -141,7 +145,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
     const uint8_t* lb = lds[slot][1];
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int cofs = ((kk * 2 + hf) ^ ((ln >> 1) & 3)) << 4;
+      const int cofs = ((kk * 2 + hf) ^ ((ln >> 2) & 3)) << 4;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         F[kk][i] = *reinterpret_cast<const bf16x8*>(la + arow + i * 32 * kRowB + cofs);
