@@ -7,7 +7,8 @@
  *   csa_attend                    MQA over the selected compressed entries
  *   hca_attend                    MQA over all visible compressed entries
  * Both attend calls also take the raw sliding window, the optional sink, the
- * partial RoPE and its inverse on the output.
+ * partial RoPE and its inverse on the output.  After core attention,
+ *   grouped_output_projection     heads in g groups -> d_g each -> d
  *
  * Conventions shared by every call
  * --------------------------------
@@ -48,7 +49,7 @@
  *        Attention", "Sliding Window Branch", "Attention Sink".
  *   [P3] the QbitAI article as rewritten on futuo-fx-trading.com: partial RoPE
  *        passage, strict-causality passage, the lightning indexer + top-k step,
- *        core attention (MQA) step.
+ *        core attention (MQA) step, grouped output projection step.
  */
 #ifndef LAC_H
 #define LAC_H
