@@ -415,7 +415,7 @@ class ProjectionPrefill:
         self.lac = lac
         c = self.c = synth.projection(seed=seed, device=dev)
         self.out = torch.empty((c["T"], c["d"]), dtype=torch.bfloat16, device=dev)
-        self.ws = torch.empty(lac.grouped_projection_workspace_size(c["T"], c["G"], c["d_g"]),
+        self.ws = torch.empty(lac.grouped_projection_workspace_size(c["T"], c["H"], c["D"], c["G"], c["d_g"], c["d"]),
                               dtype=torch.uint8, device=dev)
         self.sets = [c]
 

@@ -278,14 +278,17 @@ int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int3
  *   w1    [G, d_g, (H/G)*D] bfloat16
  *   w2    [d, G*d_g] bfloat16
  *   out   [T, d] bfloat16 (fp32 accumulation, rounded to nearest even)
- *   workspace >= grouped_projection_workspace_size(T, G, d_g) bytes: holds
- *         y [T, G*d_g] in bfloat16 between the products (rounded to nearest
- *         even, as a caller storing y in bfloat16 would).
- *   Supported: (H/G)*D and G*d_g multiples of 128, d_g and d multiples of 256,
+ *   workspace >= grouped_projection_workspace_size(T, H, D, G, d_g, d)
+ *         bytes: holds y [T, G*d_g] in bfloat16 between the products
+ *         (rounded to nearest even, as a caller storing y in bfloat16
+ *         would), and for T <= 64 the fp32 partial sums of the products'
+ *         contraction slices, which are added in a fixed order.
+ *   Supported: (H/G)*D and G*d_g multiples of 256, d_g and d multiples of 256,
  *   H*D, G*d_g and d at most 2^22; others return LAC_ERR_UNSUPPORTED.  T = 0
  *   is a no-op.  G must divide H (else LAC_ERR_INVALID).
  */
-size_t grouped_projection_workspace_size(int32_t T, int32_t G, int32_t d_g);
+size_t grouped_projection_workspace_size(int32_t T, int32_t H, int32_t D, int32_t G, int32_t d_g,
+                                         int32_t d);
 int32_t grouped_output_projection(const void* attn, const void* w1, const void* w2, int32_t T,
                                   int32_t H, int32_t D, int32_t G, int32_t d_g, int32_t d,
                                   void* out, void* workspace, size_t workspace_bytes,
@@ -300,8 +303,8 @@ const char* lac_last_error(void);
  * the next launch of kernel `kernel` (LAC_KERNEL_*) enqueued by this thread
  * records hipEvent_t `start` just before it and `stop` just after it, on the
  * stream of the launch.  Passing NULL events disarms.  LAC_KERNEL_PROJECT
- * brackets both launches of one grouped_output_projection call (its two
- * products run the same kernel).
+ * brackets all launches of one grouped_output_projection call (from 65
+ * tokens up, its two products run the same kernel).
  */
 enum {
     LAC_KERNEL_COMPRESS = 0,

@@ -66,7 +66,7 @@ lib.csa_attend_rmsnorm.argtypes = lib.csa_attend.argtypes[:-1] + [_vp, _f32, _vp
 lib.csa_attend_rmsnorm.restype = _i32
 lib.hca_attend_rmsnorm.argtypes = lib.hca_attend.argtypes[:-1] + [_vp, _f32, _vp]
 lib.hca_attend_rmsnorm.restype = _i32
-lib.grouped_projection_workspace_size.argtypes = [_i32, _i32, _i32]
+lib.grouped_projection_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
 lib.grouped_projection_workspace_size.restype = _sz
 lib.grouped_output_projection.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                                           _vp, _sz, _vp]
@@ -263,8 +263,8 @@ def hca_attend(q, hkv, raw_kv, window, m=128, q_pos0=None, raw_pos0=None, rope_d
 
 
 # ---------------------------------------------------------------- grouped output projection
-def grouped_projection_workspace_size(T, G, d_g) -> int:
-    return int(lib.grouped_projection_workspace_size(T, G, d_g))
+def grouped_projection_workspace_size(T, H, D, G, d_g, d) -> int:
+    return int(lib.grouped_projection_workspace_size(T, H, D, G, d_g, d))
 
 
 def grouped_output_projection(attn, w1, w2, out=None, workspace=None, stream=None):
@@ -286,7 +286,8 @@ def grouped_output_projection(attn, w1, w2, out=None, workspace=None, stream=Non
         out = torch.empty((T, d), dtype=torch.bfloat16, device=attn.device)
     elif out.dtype != torch.bfloat16 or out.numel() != T * d or not out.is_contiguous():
         raise ValueError("out must be a contiguous bf16 tensor of T*d values")
-    workspace = _workspace(workspace, grouped_projection_workspace_size(T, G, d_g), attn.device)
+    workspace = _workspace(workspace, grouped_projection_workspace_size(T, H, D, G, d_g, d),
+                           attn.device)
     _check(lib.grouped_output_projection(_ptr(attn), _ptr(w1), _ptr(w2), T, H, D, G, d_g, d,
                                          _ptr(out), _ptr(workspace), workspace.numel(),
                                          _stream(stream)))

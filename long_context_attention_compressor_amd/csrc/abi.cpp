@@ -397,9 +397,11 @@ int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int3
   }
 }
 
-size_t grouped_projection_workspace_size(int32_t T, int32_t G, int32_t d_g) {
-  if (T < 0 || G < 1 || d_g < 1) return 0;
-  return (size_t)T * (size_t)G * (size_t)d_g * 2;
+size_t grouped_projection_workspace_size(int32_t T, int32_t H, int32_t D, int32_t G, int32_t d_g,
+                                         int32_t d) {
+  if (T < 0 || H < 1 || D < 1 || G < 1 || H % G || d_g < 1 || d < 1) return 0;
+  if ((int64_t)H * D > (1 << 22) || (int64_t)G * d_g > (1 << 22) || d > (1 << 22)) return 0;
+  return lac::projection_workspace_bytes(T, H, D, G, d_g, d);
 }
 
 int32_t grouped_output_projection(const void* attn, const void* w1, const void* w2, int32_t T,
@@ -416,12 +418,12 @@ int32_t grouped_output_projection(const void* attn, const void* w1, const void* 
       return fail(LAC_ERR_UNSUPPORTED, "%s: H*D, G*d_g and d must be at most 2^22", fn);
     if (!lac::projection_shape_ok(K1, d_g, Y, d))
       return fail(LAC_ERR_UNSUPPORTED,
-                  "%s: needs (H/G)*D and G*d_g multiples of 128, d_g and d multiples of 256", fn);
+                  "%s: needs (H/G)*D and G*d_g multiples of 256, d_g and d multiples of 256", fn);
     if (T == 0) return LAC_OK;
     if (!attn || !w1 || !w2 || !out) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
     if (!aligned(attn, 16) || !aligned(w1, 16) || !aligned(w2, 16) || !aligned(out, 16))
       return fail(LAC_ERR_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
-    const size_t need = grouped_projection_workspace_size(T, G, d_g);
+    const size_t need = grouped_projection_workspace_size(T, H, D, G, d_g, d);
     if (!workspace || !aligned(workspace, 256) || workspace_bytes < need)
       return fail(LAC_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned and hold %zu bytes",
                   fn, need);

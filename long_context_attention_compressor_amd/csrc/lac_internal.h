@@ -107,13 +107,15 @@ struct ProjectArgs {
   const void* attn;       // [T, H, D] bf16
   const void* w1;         // [G, d_g, (H/G)*D] bf16
   const void* w2;         // [d, G*d_g] bf16
-  void* y;                // [T, G*d_g] bf16 (workspace)
+  void* y;                // workspace: y [T, G*d_g] bf16, then split partial sums
   void* out;              // [T, d] bf16
   int T, H, D, G, d_g, d;
 };
 // Contraction widths K1 = (H/G)*D and G*d_g, output widths d_g and d that the
 // product kernel tiles exactly.
 bool projection_shape_ok(int64_t K1, int64_t d_g, int64_t Kout, int64_t d);
+// Workspace: y [T, G*d_g] bf16, and for T <= 64 the split partial sums after it.
+size_t projection_workspace_bytes(int T, int H, int D, int G, int d_g, int d);
 hipError_t launch_projection(const ProjectArgs& p, hipStream_t st);
 
 }  // namespace lac

@@ -229,6 +229,154 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- few tokens
+// With a few tokens (decode) the products stream the weights once and do
+// little arithmetic, so the tiled kernel above would leave most of the chip
+// idle.  Here each wave owns 32 weight rows and one of S slices of the
+// contraction, and keeps all tokens (TT tiles of 32) in the MFMA's second
+// operand: a 128-deep step is eight MFMAs, each fed by one 16-byte load per
+// lane from its own row, two steps in flight.  Each load touches one line
+// per row, and the step's eight loads the same 32 lines, so the weights are
+// read with the default cache policy: with the streaming hint the lines left
+// the cache between the loads and every weight byte crossed HBM about eight
+// times.  The S partial sums go to workspace in fp32 and a second kernel
+// adds them in a fixed order and rounds to bf16, so results do not depend on
+// timing.
+constexpr int kSkinnyMaxT = 64;
+constexpr int kSkinnyStep = 128;                 // contraction per step
+constexpr int kSkinnyMinSteps = 4;               // steps per wave at least
+
+struct SkinnyArgs {
+  const __bf16* W;        // [batch][N, K] rows ldw apart, batch sW apart
+  const __bf16* X;        // [batch][T, K] rows ldx apart, batch sX apart
+  float* P;               // [S][T][ldp] partial sums; batch b at column b * N
+  int T, N, K, S, batches;
+  int64_t ldw, sW, ldx, sX, ldp;
+};
+
+template <int TT>
+__global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs a) {
+  const int l = lane_id(), ln = l & 31, hf = l >> 5;
+  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rtiles = a.N / 32;
+  const int per_batch = rtiles * a.S;
+  if (wid >= per_batch * a.batches) return;
+  const int batch = wid / per_batch;
+  const int r = wid - batch * per_batch;
+  const int split = r / rtiles, rt = r - split * rtiles;   // neighbouring waves: neighbouring rows
+  const int Ks = a.K / a.S;
+  const int k0 = split * Ks;
+  const __bf16* Wt = a.W + batch * a.sW + (int64_t)rt * 32 * a.ldw + k0;
+  const __bf16* Xt = a.X + batch * a.sX + k0;
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(Wt), 0, (int)min(((int64_t)31 * a.ldw + Ks) * 2, (int64_t)0x7fffffff),
+      0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(Xt), 0, (int)min(((int64_t)(a.T - 1) * a.ldx + Ks) * 2, (int64_t)0x7fffffff),
+      0x00020000);
+  // Load c of a step gives lane (ln, hf) the 16 bytes at 32 c + 16 hf of its
+  // row's 256-byte stretch, so one load touches one line per row.  Token
+  // lanes past T read row T - 1 again (same lines, results never stored).
+  const int wofs = (int)((int64_t)ln * a.ldw * 2) + hf * 16;
+  int xofs[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt)
+    xofs[tt] = (int)((int64_t)min(tt * 32 + ln, a.T - 1) * a.ldx * 2) + hf * 16;
+
+  typedef u32x4 Step[1 + TT][8];          // [weights | token tiles][chunk]
+  auto load = [&](Step& b, int kk) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      b[0][c] = __builtin_amdgcn_raw_buffer_load_b128(rw, wofs + c * 32, kk * 2, 0);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        b[1 + tt][c] = __builtin_amdgcn_raw_buffer_load_b128(rx, xofs[tt] + c * 32, kk * 2, 0);
+  };
+  f32x16 acc[TT];
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) acc[tt] = f32x16{};
+  auto mfmas = [&](const Step& b) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int tt = 0; tt < TT; ++tt)
+        acc[tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, b[0][c]), __builtin_bit_cast(bf16x8, b[1 + tt][c]),
+            acc[tt], 0, 0, 0);
+  };
+  // Steps past the end reload the last one (in bounds, unused): every load is
+  // unconditional, so the compiler's memory-counter waits stay exact.
+  const int ns = Ks / kSkinnyStep;        // even
+  Step b0, b1;
+  load(b0, 0);
+  load(b1, min(1, ns - 1) * kSkinnyStep);
+  for (int s = 0; s < ns; s += 2) {
+    mfmas(b0);
+    load(b0, min(s + 2, ns - 1) * kSkinnyStep);
+    mfmas(b1);
+    load(b1, min(s + 3, ns - 1) * kSkinnyStep);
+  }
+
+  // acc[tt][v]: weight row 32 rt + 8 (v / 4) + 4 hf + v % 4, token 32 tt + ln.
+#pragma unroll
+  for (int tt = 0; tt < TT; ++tt) {
+    const int t = tt * 32 + ln;
+    if (t < a.T) {
+      float* pr = a.P + ((int64_t)split * a.T + t) * a.ldp + batch * a.N + rt * 32 + 4 * hf;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *reinterpret_cast<f32x4*>(pr + 8 * g) =
+            f32x4{acc[tt][4 * g], acc[tt][4 * g + 1], acc[tt][4 * g + 2], acc[tt][4 * g + 3]};
+    }
+  }
+}
+
+// out[t, n] = bf16(sum over s of P[s][t][n]), s in order; four columns per thread.
+__global__ void __launch_bounds__(256) split_sum_kernel(const float* P, int S, int T, int64_t ldp,
+                                                        int ncols, __bf16* out, int64_t ldo) {
+  const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= (int64_t)T * ncols) return;
+  const int t = (int)(e / ncols), n = (int)(e - (int64_t)t * ncols);
+  f32x4 sum = *reinterpret_cast<const f32x4*>(P + (int64_t)t * ldp + n);
+  for (int s = 1; s < S; ++s)
+    sum += *reinterpret_cast<const f32x4*>(P + ((int64_t)s * T + t) * ldp + n);
+  *reinterpret_cast<uint2*>(out + (int64_t)t * ldo + n) =
+      make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
+}
+
+// Contraction slices for the few-token kernel: enough waves to keep HBM busy
+// (about 16 per compute unit), each at least kSkinnyMinSteps steps long, a
+// power of two that divides K / kSkinnyStep into an even count.
+int skinny_splits(int64_t rows, int64_t K) {
+  const int64_t steps = K / kSkinnyStep;
+  int S = 1;
+  while (rows / 32 * S < 4096 && steps % (2 * S * 2) == 0 && steps / (2 * S) >= kSkinnyMinSteps)
+    S *= 2;
+  return S;
+}
+
+hipError_t launch_skinny(const SkinnyArgs& s0, int S, hipStream_t st) {
+  SkinnyArgs s = s0;
+  s.S = S;
+  const int waves = s.N / 32 * S * s.batches;
+  const int blocks = (waves + 3) / 4;
+  if (s.T <= 32)
+    hipLaunchKernelGGL(gemm_skinny_kernel<1>, dim3(blocks), dim3(256), 0, st, s);
+  else
+    hipLaunchKernelGGL(gemm_skinny_kernel<2>, dim3(blocks), dim3(256), 0, st, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_sum(const float* P, int S, int T, int64_t ldp, int ncols, __bf16* out,
+                            int64_t ldo, hipStream_t st) {
+  const int64_t quads = (int64_t)T * ncols / 4;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, st,
+                     P, S, T, ldp, ncols, out, ldo);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& g0, int batches, hipStream_t st) {
   GemmArgs g = g0;
   g.mt = (g.M + kBM - 1) / kBM;
@@ -241,12 +389,62 @@ hipError_t launch_gemm(const GemmArgs& g0, int batches, hipStream_t st) {
 
 }  // namespace
 
+size_t projection_workspace_bytes(int T, int H, int D, int G, int d_g, int d) {
+  const int64_t K1 = (int64_t)(H / G) * D, Y = (int64_t)G * d_g;
+  size_t bytes = (((size_t)T * Y * 2) + 255) & ~(size_t)255;       // y
+  if (T <= kSkinnyMaxT) {
+    const size_t p1 = (size_t)skinny_splits(Y, K1) * T * Y * 4;
+    const size_t p2 = (size_t)skinny_splits(d, Y) * T * d * 4;
+    bytes += p1 > p2 ? p1 : p2;
+  }
+  return bytes;
+}
+
 bool projection_shape_ok(int64_t K1, int64_t d_g, int64_t Kout, int64_t d) {
-  return K1 % (2 * kBK) == 0 && Kout % (2 * kBK) == 0 && d_g % kBN == 0 && d % kBN == 0;
+  return K1 % (2 * kSkinnyStep) == 0 && Kout % (2 * kSkinnyStep) == 0 && d_g % kBN == 0 &&
+         d % kBN == 0;
 }
 
 hipError_t launch_projection(const ProjectArgs& p, hipStream_t st) {
   const int64_t K1 = (int64_t)(p.H / p.G) * p.D, Y = (int64_t)p.G * p.d_g;
+  if (p.T <= kSkinnyMaxT) {
+    __bf16* y = static_cast<__bf16*>(p.y);
+    float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(p.y) +
+                                        ((((size_t)p.T * Y * 2) + 255) & ~(size_t)255));
+    SkinnyArgs s1{};
+    s1.W = static_cast<const __bf16*>(p.w1);
+    s1.X = static_cast<const __bf16*>(p.attn);
+    s1.P = P;
+    s1.T = p.T;
+    s1.N = p.d_g;
+    s1.K = (int)K1;
+    s1.batches = p.G;
+    s1.ldw = K1;
+    s1.sW = (int64_t)p.d_g * K1;
+    s1.ldx = (int64_t)p.H * p.D;
+    s1.sX = K1;
+    s1.ldp = Y;
+    const int S1 = skinny_splits(Y, K1);
+    hipError_t e = launch_skinny(s1, S1, st);
+    if (e == hipSuccess) e = launch_split_sum(P, S1, p.T, Y, (int)Y, y, Y, st);
+    if (e != hipSuccess) return e;
+    SkinnyArgs s2{};
+    s2.W = static_cast<const __bf16*>(p.w2);
+    s2.X = y;
+    s2.P = P;
+    s2.T = p.T;
+    s2.N = p.d;
+    s2.K = (int)Y;
+    s2.batches = 1;
+    s2.ldw = Y;
+    s2.ldx = Y;
+    s2.ldp = p.d;
+    const int S2 = skinny_splits(p.d, Y);
+    e = launch_skinny(s2, S2, st);
+    if (e == hipSuccess)
+      e = launch_split_sum(P, S2, p.T, p.d, p.d, static_cast<__bf16*>(p.out), p.d, st);
+    return e;
+  }
   GemmArgs g1{};
   g1.A = static_cast<const __bf16*>(p.attn);
   g1.B = static_cast<const __bf16*>(p.w1);

@@ -2,7 +2,8 @@
 grouped output projection step: heads in g groups, each group projected to
 d_g, the concatenation projected back to d).  The oracle rounds the
 intermediate to bfloat16 as the library stores it.  Shapes span several
-256 x 256 output tiles with a ragged last row band; the full-size case (4096
+256 x 256 output tiles with a ragged last row band, and the few-token path
+(64 tokens or fewer: split contraction, fixed-order sums); the full-size case (4096
 tokens, 64 heads of 512, 8 groups of 1024, d = 7168) is checked on sampled
 tokens, which the oracle computes one by one (tokens are independent)."""
 import numpy as np
@@ -63,6 +64,21 @@ def test_ragged_full_width_on_sampled_tokens():
     _run(T, 64, 512, 8, 1024, 7168, 55, rows)
 
 
+@pytest.mark.parametrize("T", [1, 4, 32, 33, 64])
+def test_decode_token_counts_full_width(T):
+    # 64 tokens or fewer take the split-contraction path (one or two token
+    # tiles); every token is checked
+    _run(T, 64, 512, 8, 1024, 7168, 60 + T)
+
+
+def test_decode_path_small_groups():
+    _run(5, 8, 128, 2, 256, 512, 70)
+
+
+def test_first_token_count_on_the_tiled_path():
+    _run(65, 16, 128, 4, 256, 512, 71)
+
+
 def test_zero_tokens_is_a_no_op():
     attn = torch.zeros((0, 8, 64), dtype=torch.bfloat16, device=DEV)
     w1 = torch.zeros((2, 256, 256), dtype=torch.bfloat16, device=DEV)
@@ -84,8 +100,8 @@ def test_small_workspace_is_refused():
     w1 = torch.zeros((2, 256, 256), dtype=torch.bfloat16, device=DEV)
     w2 = torch.zeros((256, 512), dtype=torch.bfloat16, device=DEV)
     out = torch.zeros((4, 256), dtype=torch.bfloat16, device=DEV)
-    need = lac.grouped_projection_workspace_size(4, 2, 256)
-    assert need == 4 * 512 * 2
+    need = lac.grouped_projection_workspace_size(4, 8, 64, 2, 256, 256)
+    assert need >= 4 * 512 * 2
     ws = torch.empty(need, dtype=torch.uint8, device=DEV)
     st = lac.lib.grouped_output_projection(attn.data_ptr(), w1.data_ptr(), w2.data_ptr(), 4, 8,
                                            64, 2, 256, 256, out.data_ptr(), ws.data_ptr(),
