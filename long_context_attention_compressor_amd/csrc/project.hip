@@ -235,7 +235,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
 // idle.  Here each wave owns 32 weight rows and one of S slices of the
 // contraction, and keeps all tokens (TT tiles of 32) in the MFMA's second
 // operand: a 128-deep step is eight MFMAs, each fed by one 16-byte load per
-// lane from its own row, two steps in flight.  Each load touches one line
+// lane from its own row, two steps in flight (a whole slice, usually).  Each load touches one line
 // per row, and the step's eight loads the same 32 lines, so the weights are
 // read with the default cache policy: with the streaming hint the lines left
 // the cache between the loads and every weight byte crossed HBM about eight
@@ -244,7 +244,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
 // timing.
 constexpr int kSkinnyMaxT = 64;
 constexpr int kSkinnyStep = 128;                 // contraction per step
-constexpr int kSkinnyMinSteps = 4;               // steps per wave at least
+constexpr int kSkinnyMinSteps = 2;               // steps per wave at least
 
 struct SkinnyArgs {
   const __bf16* W;        // [batch][N, K] rows ldw apart, batch sW apart
@@ -306,17 +306,15 @@ __global__ void __launch_bounds__(256) gemm_skinny_kernel(SkinnyArgs a) {
             __builtin_bit_cast(bf16x8, b[0][c]), __builtin_bit_cast(bf16x8, b[1 + tt][c]),
             acc[tt], 0, 0, 0);
   };
-  // Steps past the end reload the last one (in bounds, unused): every load is
-  // unconditional, so the compiler's memory-counter waits stay exact.
+  // Two steps per round, both in flight at once (the usual slice is one
+  // round); the loads are unconditional, so the memory-counter waits are exact.
   const int ns = Ks / kSkinnyStep;        // even
-  Step b0, b1;
-  load(b0, 0);
-  load(b1, min(1, ns - 1) * kSkinnyStep);
   for (int s = 0; s < ns; s += 2) {
+    Step b0, b1;
+    load(b0, s * kSkinnyStep);
+    load(b1, (s + 1) * kSkinnyStep);
     mfmas(b0);
-    load(b0, min(s + 2, ns - 1) * kSkinnyStep);
     mfmas(b1);
-    load(b1, min(s + 3, ns - 1) * kSkinnyStep);
   }
 
   // acc[tt][v]: weight row 32 rt + 8 (v / 4) + 4 hf + v % 4, token 32 tt + ln.
@@ -339,20 +337,32 @@ __global__ void __launch_bounds__(256) split_sum_kernel(const float* P, int S, i
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= (int64_t)T * ncols) return;
   const int t = (int)(e / ncols), n = (int)(e - (int64_t)t * ncols);
-  f32x4 sum = *reinterpret_cast<const f32x4*>(P + (int64_t)t * ldp + n);
-  for (int s = 1; s < S; ++s)
-    sum += *reinterpret_cast<const f32x4*>(P + ((int64_t)s * T + t) * ldp + n);
+  // loads in groups of up to 16 (S is a power of two, at most 64), each
+  // group's loads issued together, then added in order
+  f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < S; s0 += 16) {
+    f32x4 part[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s0 + s < S)
+        part[s] = *reinterpret_cast<const f32x4*>(P + ((int64_t)(s0 + s) * T + t) * ldp + n);
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+      if (s0 + s < S) sum += part[s];
+  }
   *reinterpret_cast<uint2*>(out + (int64_t)t * ldo + n) =
       make_uint2(pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3]));
 }
 
 // Contraction slices for the few-token kernel: enough waves to keep HBM busy
-// (about 16 per compute unit), each at least kSkinnyMinSteps steps long, a
-// power of two that divides K / kSkinnyStep into an even count.
+// (about 16 per compute unit, all loads of a wave in flight at once when it
+// has two steps), each at least kSkinnyMinSteps steps long, a power of two
+// (at most 64) that divides K / kSkinnyStep into an even count.
 int skinny_splits(int64_t rows, int64_t K) {
   const int64_t steps = K / kSkinnyStep;
   int S = 1;
-  while (rows / 32 * S < 4096 && steps % (2 * S * 2) == 0 && steps / (2 * S) >= kSkinnyMinSteps)
+  while (S < 64 && rows / 32 * S < 4096 && steps % (2 * S * 2) == 0 &&
+         steps / (2 * S) >= kSkinnyMinSteps)
     S *= 2;
   return S;
 }
