@@ -457,8 +457,49 @@ class ProjectionPrefill:
                 "seconds": el, "sample": f"{n} of the {c['T']} tokens"}
 
 
+class ProjectionDecode(ProjectionPrefill):
+    """The grouped output projection of one decode step of 4 sequences (4
+    tokens): the weights (176 MB) stream from HBM once per call."""
+    name = "grouped_projection_decode"
+    unit = "tokens/s"
+    kernel = "grouped_output_projection call (2 product + 2 sum launches)"
+
+    def __init__(self, lac, synth, dev, sets, seed=6):
+        self.lac = lac
+        c = self.c = synth.projection(seed=seed, T=4, device=dev)
+        self.out = torch.empty((c["T"], c["d"]), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(lac.grouped_projection_workspace_size(c["T"], c["H"], c["D"], c["G"],
+                                                                    c["d_g"], c["d"]),
+                              dtype=torch.uint8, device=dev)
+        self.sets = [c]
+
+    def bytes_per_step(self):
+        c = self.c
+        K1 = c["H"] // c["G"] * c["D"]
+        weights = (c["G"] * c["d_g"] * K1 + c["d"] * c["G"] * c["d_g"]) * 2
+        acts = c["T"] * (c["H"] * c["D"] + c["G"] * c["d_g"] * 2 + c["d"]) * 2
+        return weights + acts
+
+    def cpu_sample(self):
+        import oracle
+        import synth
+
+        c = self.c
+        attn = synth.host_bytes(c["attn"])
+        w1, w2 = synth.host_bytes(c["w1"]), synth.host_bytes(c["w2"])
+        t0 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t0 < 10.0:
+            oracle.grouped_projection(attn, w1, w2, oracle.BF16, c["T"], c["H"], c["D"], c["G"],
+                                      c["d_g"], c["d"], y_dtype=oracle.BF16)
+            reps += 1
+        el = time.perf_counter() - t0
+        return {"value": reps * c["T"] / el, "unit": self.unit, "seconds": el,
+                "sample": f"{reps} whole calls of {c['T']} tokens"}
+
+
 WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeRmsNorm, CsaDecode,
-                                  ChunkPrefill, HcaPrefill, ProjectionPrefill)}
+                                  ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode)}
 
 
 def main():
@@ -514,7 +555,17 @@ def main():
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": wl.config()}
-    if wl.unit == "tokens/s":
+    if isinstance(wl, ProjectionDecode):
+        # HBM-bound: the timed span brackets the whole call (4 launches)
+        res["value"] = wl.tokens_per_step() / (ms / 1e3)
+        res["unit"] = "tokens/s"
+        ach = wl.bytes_per_step() / (kern_ms / 1e3) / 1e9
+        res["hbm_gbps"] = wl.bytes_per_step() / (ms / 1e3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": wl.kernel, "achieved": round(ach, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                           "traffic_unit": "B/call", "launch_ms": round(kern_ms, 5)}
+    elif wl.unit == "tokens/s":
         res["value"] = wl.tokens_per_step() / (ms / 1e3)
         res["unit"] = "tokens/s"
         res["hbm_gbps"] = wl.bytes_per_step() / (ms / 1e3) / 1e9
