@@ -65,8 +65,8 @@ def _score_traffic(workload):
 # The same for the product kernel of the grouped output projection: bytes per
 # launch averaged over its two launches (the per-group product and the output
 # product), for the kernel source identified by its SHA-256.
-PROJECT_TRAFFIC_BYTES = 763460658
-PROJECT_TRAFFIC_SOURCE_SHA256 = "1ff58a1eff7dc1354ea1d42968f7e0107a324933b76933a2d9d0cb736ee43b46"
+PROJECT_TRAFFIC_BYTES = 693250895
+PROJECT_TRAFFIC_SOURCE_SHA256 = "d37fefcaee7d088b2bf589edbc396fb10f11c4026dab0a343eb22c65ee488e30"
 PROJECT_SOURCES = ("project.hip", "lac_device.h")
 
 

@@ -12,9 +12,10 @@
 // contraction index (activations [M, K], weights [N, K]), so one kernel runs
 // both: the first batched over the groups, the second with one batch.
 //
-// Kernel.  A 256 x 256 output tile per block of four waves, each wave a
-// 128 x 128 quarter held as 4 x 4 v_mfma_f32_32x32x16_bf16 accumulators
-// (256 fp32 per lane, in the accumulator registers).  The contraction runs in
+// Kernel.  A 256 x 256 output tile per block of eight waves (two per SIMD,
+// so one wave's waits and barrier overlap the other's MFMAs), each wave a
+// 128 x 64 part held as 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators (128
+// fp32 per lane).  Four waves of 128 x 128 each did 10% less work per second.  The contraction runs in
 // steps of 32: per step the block stages a 256 x 32 slice of each operand in
 // LDS with loads that write LDS directly (no registers), four slots deep, so
 // a slice is requested three steps before it is read; the fragments of the
@@ -25,7 +26,7 @@
 // 16 slots of the bank window (the rocprofv3 counter SQ_LDS_BANK_CONFLICT
 // reads 0; keyed by row pair, which would suit 8 lanes over 32 banks, it
 // reads half the LDS busy cycles).  Per
-// 16-deep step a wave reads 4 A and 4 B fragments (8 KB from LDS) for 16
+// 16-deep step a wave reads 4 A and 2 B fragments (6 KB from LDS) for 8
 // MFMAs.  The MFMA takes the weight fragment as its first operand, so a
 // lane's accumulator holds four runs of four consecutive output columns of
 // one row and stores them as 8-byte pieces.
@@ -61,10 +62,12 @@ struct GemmArgs {
 // The staging loads write LDS directly and are tracked by hand: the waits and
 // barriers below are written out (asm with a memory clobber, so the compiler
 // neither moves LDS accesses across them nor adds waits of its own).
+constexpr int kWaves = 8;                        // 2 (rows) x 4 (columns) waves per block
+constexpr int kLoadsPerSlice = 2 * (256 / 16) / kWaves;   // staging loads per wave per slice
+
 __device__ __forceinline__ void wait_vm(void) {
-  // every wave has 8 staging loads per slice; wait until all but the
-  // kStages - 2 newest slices have landed
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (kStages - 2)) : "memory");
+  // wait until all but the kStages - 2 newest slices' staging loads have landed
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerSlice * (kStages - 2)) : "memory");
 }
 __device__ __forceinline__ void wait_lds_reads(void) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -73,11 +76,11 @@ __device__ __forceinline__ void block_barrier(void) {
   asm volatile("s_barrier" ::: "memory");
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(64 * kWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 gemm_nt_bf16_kernel(GemmArgs a) {
   __shared__ __align__(16) uint8_t lds[kStages][2][kSliceB];   // [stage][A | B]
   const int l = lane_id(), ln = l & 31, hf = l >> 5;
-  const int wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
+  const int wave = threadIdx.x >> 6, wm = wave >> 2, wn = wave & 3;
 
   // XCD-contiguous tile order (see the header); within a batch, bands of
   // kGroupM row tiles walked column by column.
@@ -108,12 +111,13 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   // Staging: a load instruction fills 1 KB of LDS, lane i the 16 bytes at
   // 16 i, i.e. rows of 64 bytes, lane i at row i / 4, slot i % 4.  Slot s of
   // row r holds the row's chunk s ^ ((r / 4) % 4), so each lane fetches that
-  // chunk.  Wave w stages rows 64 w .. 64 w + 63 of both operands (4 loads
+  // chunk.  Wave w stages rows 32 w .. 32 w + 31 of both operands (2 loads
   // each).
-  int aofs[4], bofs[4];
+  constexpr int kRowsPerWave = 256 / kWaves;
+  int aofs[kRowsPerWave / 16], bofs[kRowsPerWave / 16];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int row = wave * 64 + u * 16 + (l >> 2);
+  for (int u = 0; u < kRowsPerWave / 16; ++u) {
+    const int row = wave * kRowsPerWave + u * 16 + (l >> 2);
     const int chunk = (l & 3) ^ ((row >> 2) & 3);
     aofs[u] = (int)((int64_t)row * a.lda * 2) + chunk * 16;
     bofs[u] = (int)((int64_t)row * a.ldb * 2) + chunk * 16;
@@ -121,25 +125,28 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   typedef __attribute__((address_space(3))) void lds_void;
   auto stage = [&](int slot, int k0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kRowsPerWave / 16; ++u) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (lds_void*)&lds[slot][0][(wave * 64 + u * 16) * kRowB], 16, aofs[u], k0 * 2, 0, 0);
+          ra, (lds_void*)&lds[slot][0][(wave * kRowsPerWave + u * 16) * kRowB], 16, aofs[u],
+          k0 * 2, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rb, (lds_void*)&lds[slot][1][(wave * 64 + u * 16) * kRowB], 16, bofs[u], k0 * 2, 0, 0);
+          rb, (lds_void*)&lds[slot][1][(wave * kRowsPerWave + u * 16) * kRowB], 16, bofs[u],
+          k0 * 2, 0, 0);
     }
   };
 
-  f32x16 acc[4][4];
+  constexpr int NJ = 2;                   // 32-column tiles per wave
+  f32x16 acc[NJ][4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < NJ; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[j][i] = f32x16{};
 
-  // Fragment rows: A row wm*128 + i*32 + ln, B row wn*128 + j*32 + ln; the
+  // Fragment rows: A row wm*128 + i*32 + ln, B row wn*64 + j*32 + ln; the
   // row's swizzle key is (ln / 4) % 4 (the tile offsets are multiples of 32).
   // F[kk][0..3] are the A fragments of 16-deep step kk, F[kk][4..7] the B ones.
-  const int arow = (wm * 128 + ln) * kRowB, brow = (wn * 128 + ln) * kRowB;
-  typedef bf16x8 Frags[kBK / 16][8];
+  const int arow = (wm * 128 + ln) * kRowB, brow = (wn * 32 * NJ + ln) * kRowB;
+  typedef bf16x8 Frags[kBK / 16][4 + NJ];
   auto read_frags = [&](int slot, Frags& F) {
     const uint8_t* la = lds[slot][0];
     const uint8_t* lb = lds[slot][1];
@@ -150,7 +157,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
       for (int i = 0; i < 4; ++i)
         F[kk][i] = *reinterpret_cast<const bf16x8*>(la + arow + i * 32 * kRowB + cofs);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
         F[kk][4 + j] = *reinterpret_cast<const bf16x8*>(lb + brow + j * 32 * kRowB + cofs);
     }
   };
@@ -158,7 +165,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(F[kk][4 + j], F[kk][i], acc[j][i],
@@ -178,7 +185,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
 #pragma unroll
   for (int s = 0; s < kStages; ++s) stage(s, min(s, nk - 1) * kBK);
   Frags F0, F1;
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (kStages - 1)) : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsPerSlice * (kStages - 1)) : "memory");
   block_barrier();
   read_frags(0, F0);
   auto step = [&](int kt, const Frags& cur, Frags& next) {
@@ -194,12 +201,13 @@ gemm_nt_bf16_kernel(GemmArgs a) {
     mfmas(cur);
     // Order inside the step: the staging loads, then one fragment read per
     // two MFMAs, so the reads for the next step start early and spread out.
-    __builtin_amdgcn_sched_group_barrier(0x020, 8, 0);        // VMEM reads
+    __builtin_amdgcn_sched_group_barrier(0x020, kLoadsPerSlice, 0);   // VMEM reads
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < 2 * (4 + NJ); ++g) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
     }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * 4 * NJ - 2 * (4 + NJ), 0);
     __builtin_amdgcn_sched_barrier(0);
   };
   for (int kt = 0; kt < nk; kt += 2) {
@@ -208,16 +216,16 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write may outlive the block
 
-  // acc[j][i][v]: column n0 + wn*128 + j*32 + 8*(v/4) + 4*hf + v%4 of row
+  // acc[j][i][v]: column n0 + wn*64 + j*32 + 8*(v/4) + 4*hf + v%4 of row
   // m0 + wm*128 + i*32 + ln.
   __bf16* Cb = a.C + batch * a.sC;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + wm * 128 + i * 32 + ln;
     if (row < a.M) {
-      __bf16* cr = Cb + (int64_t)row * a.ldc + n0 + wn * 128 + 4 * hf;
+      __bf16* cr = Cb + (int64_t)row * a.ldc + n0 + wn * 32 * NJ + 4 * hf;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const f32x16& c = acc[j][i];
@@ -393,7 +401,7 @@ hipError_t launch_gemm(const GemmArgs& g0, int batches, hipStream_t st) {
   g.nt = g.N / kBN;
   g.tiles = g.mt * g.nt * batches;
   if (g.tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(g.tiles), dim3(256), 0, st, g);
+  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(g.tiles), dim3(64 * kWaves), 0, st, g);
   return hipGetLastError();
 }
 
