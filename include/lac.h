@@ -281,8 +281,9 @@ int32_t hca_attend_rmsnorm(const void* q, int32_t q_dtype, const void* hkv, int3
  *   workspace >= grouped_projection_workspace_size(T, H, D, G, d_g, d)
  *         bytes: holds y [T, G*d_g] in bfloat16 between the products
  *         (rounded to nearest even, as a caller storing y in bfloat16
- *         would), and for T <= 64 the fp32 partial sums of the products'
- *         contraction slices, which are added in a fixed order.
+ *         would), and where the products' contraction is split (T <= 64,
+ *         or too few output tiles to cover the chip) the fp32 partial sums
+ *         of the slices, which are added in a fixed order.
  *   Supported: (H/G)*D and G*d_g multiples of 256, d_g and d multiples of 256,
  *   H*D, G*d_g and d at most 2^22; others return LAC_ERR_UNSUPPORTED.  T = 0
  *   is a no-op.  G must divide H (else LAC_ERR_INVALID).

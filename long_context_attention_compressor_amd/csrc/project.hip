@@ -56,7 +56,10 @@ struct GemmArgs {
   __bf16* C;              // [batch][M, N] rows ldc apart, batch sC apart
   int M, N, K;
   int64_t lda, ldb, ldc, sA, sB, sC;
-  int mt, nt, tiles;      // tiles per batch (mt * nt) and in all
+  int mt, nt, tiles;      // tiles per batch (mt * nt) and in all batches
+  int S;                  // contraction slices (grid = tiles * S)
+  float* P;               // S > 1: fp32 partials [S][M][ldp], batch b at column b * N
+  int64_t ldp;
 };
 
 // The staging loads write LDS directly and are tracked by hand: the waits and
@@ -88,6 +91,9 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   const int per_xcd = nb >> 3;
   int tile = blockIdx.x;
   if ((nb & 7) == 0) tile = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  const int split = tile / a.tiles;
+  tile -= split * a.tiles;
+  const int Ks = a.K / a.S, k_begin = split * Ks;
   const int batch = tile / (a.mt * a.nt);
   const int rem = tile - batch * a.mt * a.nt;
   const int band = rem / (kGroupM * a.nt), in_band = rem - band * kGroupM * a.nt;
@@ -99,10 +105,10 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   // first row: the contraction offset goes in the scalar offset, and rows
   // past M fall outside the A resource, which returns zeros for them (their
   // results are never stored).
-  const __bf16* At = a.A + batch * a.sA + (int64_t)m0 * a.lda;
-  const __bf16* Bt = a.B + batch * a.sB + (int64_t)n0 * a.ldb;
-  const int64_t a_bytes = ((int64_t)(a.M - 1 - m0) * a.lda + a.K) * 2;
-  const int64_t b_bytes = ((int64_t)(kBN - 1) * a.ldb + a.K) * 2;
+  const __bf16* At = a.A + batch * a.sA + (int64_t)m0 * a.lda + k_begin;
+  const __bf16* Bt = a.B + batch * a.sB + (int64_t)n0 * a.ldb + k_begin;
+  const int64_t a_bytes = ((int64_t)(a.M - 1 - m0) * a.lda + Ks) * 2;
+  const int64_t b_bytes = ((int64_t)(kBN - 1) * a.ldb + Ks) * 2;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<__bf16*>(At), 0, (int)min(a_bytes, (int64_t)0x7fffffff), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -181,7 +187,7 @@ gemm_nt_bf16_kernel(GemmArgs a) {
   // MFMAs and a slice is requested kStages - 1 steps before it is read.
   // Slices past the last one reload it (in bounds, never used), so every wave
   // issues the same loads each step and the wait count is constant.
-  const int nk = a.K / kBK;              // even
+  const int nk = Ks / kBK;               // even
 #pragma unroll
   for (int s = 0; s < kStages; ++s) stage(s, min(s, nk - 1) * kBK);
   Frags F0, F1;
@@ -218,6 +224,25 @@ gemm_nt_bf16_kernel(GemmArgs a) {
 
   // acc[j][i][v]: column n0 + wn*64 + j*32 + 8*(v/4) + 4*hf + v%4 of row
   // m0 + wm*128 + i*32 + ln.
+  if (a.S > 1) {                         // fp32 partials of this slice
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + wm * 128 + i * 32 + ln;
+      if (row < a.M) {
+        float* pr = a.P + ((int64_t)split * a.M + row) * a.ldp + batch * a.N + n0 + wn * 32 * NJ +
+                    4 * hf;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x16& c = acc[j][i];
+            *reinterpret_cast<f32x4*>(pr + j * 32 + 8 * g) =
+                f32x4{c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]};
+          }
+      }
+    }
+    return;
+  }
   __bf16* Cb = a.C + batch * a.sC;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -395,13 +420,31 @@ hipError_t launch_split_sum(const float* P, int S, int T, int64_t ldp, int ncols
   return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& g0, int batches, hipStream_t st) {
+// Contraction slices for the tiled kernel: with fewer tiles than compute
+// units, split the contraction until the grid covers the chip, keeping at
+// least 8 (an even number of) 32-deep steps per slice.
+int tiled_splits(int64_t tiles, int64_t K) {
+  int S = 1;
+  while (tiles * S < 256 && (K / kBK) % (4 * S) == 0 && K / kBK / (2 * S) >= 8) S *= 2;
+  return S;
+}
+
+// With S > 1 the kernel writes fp32 partials to P and split_sum_kernel adds
+// them in order into C (the column offset of batch b is b * N in both).
+hipError_t launch_gemm(const GemmArgs& g0, int batches, float* P, hipStream_t st) {
   GemmArgs g = g0;
   g.mt = (g.M + kBM - 1) / kBM;
   g.nt = g.N / kBN;
   g.tiles = g.mt * g.nt * batches;
   if (g.tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(g.tiles), dim3(64 * kWaves), 0, st, g);
+  g.S = tiled_splits(g.tiles, g.K);
+  g.P = P;
+  g.ldp = (int64_t)g.N * batches;
+  hipLaunchKernelGGL(gemm_nt_bf16_kernel, dim3(g.tiles * g.S), dim3(64 * kWaves), 0, st, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || g.S == 1) return e;
+  hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)(((int64_t)g.M * g.ldp / 4 + 255) / 256)),
+                     dim3(256), 0, st, P, g.S, g.M, g.ldp, (int)g.ldp, g.C, g.ldc);
   return hipGetLastError();
 }
 
@@ -413,6 +456,12 @@ size_t projection_workspace_bytes(int T, int H, int D, int G, int d_g, int d) {
   if (T <= kSkinnyMaxT) {
     const size_t p1 = (size_t)skinny_splits(Y, K1) * T * Y * 4;
     const size_t p2 = (size_t)skinny_splits(d, Y) * T * d * 4;
+    bytes += p1 > p2 ? p1 : p2;
+  } else {
+    const int64_t mt = (T + kBM - 1) / kBM;
+    const int S1 = tiled_splits(mt * (d_g / kBN) * G, K1), S2 = tiled_splits(mt * (d / kBN), Y);
+    const size_t p1 = S1 > 1 ? (size_t)S1 * T * Y * 4 : 0;
+    const size_t p2 = S2 > 1 ? (size_t)S2 * T * d * 4 : 0;
     bytes += p1 > p2 ? p1 : p2;
   }
   return bytes;
@@ -476,7 +525,9 @@ hipError_t launch_projection(const ProjectArgs& p, hipStream_t st) {
   g1.sA = K1;
   g1.sB = (int64_t)p.d_g * K1;
   g1.sC = p.d_g;
-  hipError_t e = launch_gemm(g1, p.G, st);
+  float* P = reinterpret_cast<float*>(static_cast<uint8_t*>(p.y) +
+                                      ((((size_t)p.T * Y * 2) + 255) & ~(size_t)255));
+  hipError_t e = launch_gemm(g1, p.G, P, st);
   if (e != hipSuccess) return e;
   GemmArgs g2{};
   g2.A = static_cast<const __bf16*>(p.y);
@@ -488,7 +539,7 @@ hipError_t launch_projection(const ProjectArgs& p, hipStream_t st) {
   g2.lda = Y;
   g2.ldb = Y;
   g2.ldc = p.d;
-  return launch_gemm(g2, 1, st);
+  return launch_gemm(g2, 1, P, st);
 }
 
 }  // namespace lac
