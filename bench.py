@@ -65,8 +65,8 @@ def _score_traffic(workload):
 # The same for the product kernel of the grouped output projection: bytes per
 # launch averaged over its two launches (the per-group product and the output
 # product), for the kernel source identified by its SHA-256.
-PROJECT_TRAFFIC_BYTES = 693250895
-PROJECT_TRAFFIC_SOURCE_SHA256 = "d37fefcaee7d088b2bf589edbc396fb10f11c4026dab0a343eb22c65ee488e30"
+PROJECT_TRAFFIC_BYTES = 688514801
+PROJECT_TRAFFIC_SOURCE_SHA256 = "71f3771f1facab32cb70505661b95e4d60f0e51022455247a042c8dfb8bb7384"
 PROJECT_SOURCES = ("project.hip", "lac_device.h")
 
 
