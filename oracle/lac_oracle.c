@@ -398,16 +398,14 @@ int lo_attend2(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, 
     int64_t task;
     int rr0;
     if (scale == 0.0) scale = 1.0 / sqrt((double)D);
-    /* The raw buffer must hold every window position; CSA indices must name
-     * existing entries.  Anything else is rejected, never read. */
+    /* The raw buffer must hold every window position; anything else is
+     * rejected, never read.  A CSA index outside [0, N) names no entry: it is
+     * skipped like the -1 padding of a short selection. */
     for (rr0 = 0; rr0 < n_rows; ++rr0) {
-        int b = rows[2 * rr0], i = rows[2 * rr0 + 1], e;
+        int b = rows[2 * rr0], i = rows[2 * rr0 + 1];
         int64_t t = qpos0[b] + i;
         int64_t s_lo = t - W + 1 < 0 ? 0 : t - W + 1;
         if (W > 0 && (s_lo < raw_pos0[b] || t >= raw_pos0[b] + T_raw)) return 4;
-        if (mode == 0)
-            for (e = 0; e < k; ++e)
-                if (idx[(int64_t)rr0 * k + e] >= N) return 5;
     }
 #pragma omp parallel for schedule(dynamic, 1)
     for (task = 0; task < (int64_t)n_rows * H; ++task) {
@@ -436,7 +434,7 @@ int lo_attend2(const void* q, int q_dtype, const void* kv, int kv_dtype, int N, 
             valid[e] = 0;
             if (e < n_comp) {
                 int64_t j = mode == 0 ? idx[(int64_t)rr * k + e] : e;
-                if (j < 0) continue;
+                if (j < 0 || j >= N) continue;
                 decode_row((const uint8_t*)kv + ((int64_t)b * N + j) * krb, kv_dtype, D, r, ev);
             } else {
                 int64_t s = s_lo + (e - n_comp);

@@ -165,3 +165,19 @@ def test_no_information_leaks_from_the_future_or_the_own_block():
             y = chain.csa_prefill_tiny({**inp, **pert})["y"]
             assert np.array_equal(y[t], ref[t]), (t, name)
             assert not np.array_equal(y[T - 1], ref[T - 1])    # a later query does see it
+
+
+def test_csa_indices_past_the_cache_name_no_entry():
+    # An index >= N names no entry: it is skipped like the -1 padding, so a
+    # selection padded with such values is still ordinary causal attention.
+    rng = np.random.default_rng(7)
+    T, H, D, r = 10, 2, 16, 8
+    x = rng.standard_normal((1, T, D))
+    q = rng.standard_normal((1, T, H, D))
+    kv = oracle.compress(x, np.zeros((1, T, D)), oracle.F64, 1, T, D, 1, r, TH)
+    idx = np.full((T, T + 3), -1, np.int32)
+    for t in range(T):
+        idx[t, :t] = np.random.default_rng(t).permutation(t)
+        idx[t, t:] = [T, T + 5, 1 << 30][: T + 3 - t] + [-1] * max(0, T - t)
+    y = _att(q, kv, x, T, 0, idx=idx, k=T + 3, m=1, W=1, r=r)
+    assert np.allclose(y.reshape(T, H, D), _sdpa_causal(q[0], x[0], r), rtol=0, atol=1e-12)
