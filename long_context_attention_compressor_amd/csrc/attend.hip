@@ -192,7 +192,7 @@ struct KArgs {
   const uint8_t* win;
   const float* sink;
   void* out;
-  _Float16* part_o;         // [work, split, 64, D] partial outputs / their row sums
+  uint16_t* part_o;         // [work, split, 64, D] bf16 partial outputs / their row sums
   float* part_ml;
   const uint8_t* zero_row;   // 16 zero bytes in workspace (f32 path)
   const float2* ang;         // [B, Tq, r/2] (cos, sin) of the query angles (f32 path)
@@ -734,7 +734,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   l_row += __shfl_xor(l_row, 32);
 
   // ---- output.  With several splits: the partial output normalised by its
-  // own row sum, in fp16 (|o| <= max |v|), plus (max, sum); with one: the
+  // own row sum, in bf16 (the range of the values themselves), plus (max, sum); with one: the
   // output normalised (sink included), rotated back at -t, in bf16.  The
   // block's 64 rows are staged in the tile buffers (free once every wave is
   // done with the last tile) so that the global stores are whole rows.
@@ -759,9 +759,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
       for (int i = 0; i < 4; ++i) o[i] = oacc[dt][i] * sc;
       uint2 v;
       if (split_out) {
-        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-        const f16x4 hv = {(_Float16)o[0], (_Float16)o[1], (_Float16)o[2], (_Float16)o[3]};
-        __builtin_memcpy(&v, &hv, 8);
+        v = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       } else {
         if (d0 >= nope) {             // rotation at -t: (cos, -sin) of the query's angle
 #pragma unroll
@@ -823,15 +821,14 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   // the split weights are formed.
   const int n_cg = a.D / 8, n_sg = 256 / n_cg;
   const int cg = threadIdx.x % n_cg, sg = threadIdx.x / n_cg;
-  typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-  const _Float16* pp = a.part_o + (slot0 * 64 + row) * a.D + 8 * cg;
+  const uint16_t* pp = a.part_o + (slot0 * 64 + row) * a.D + 8 * cg;
   const int64_t stride = 64LL * a.D;
-  f16x8 x[8];
+  uint4 x[8];
   auto issue = [&](int s0) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int s = s0 + u * n_sg;
-      x[u] = *reinterpret_cast<const f16x8*>(pp + (int64_t)(s < a.nsplit ? s : 0) * stride);
+      x[u] = *reinterpret_cast<const uint4*>(pp + (int64_t)(s < a.nsplit ? s : 0) * stride);
     }
   };
   issue(sg);
@@ -883,8 +880,12 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
     for (int u = 0; u < 8; ++u) {
       const int s = s0 + u * n_sg;
       const float wv = s < a.nsplit ? wgt[s] : 0.f;
+      const uint32_t wd[4] = {x[u].x, x[u].y, x[u].z, x[u].w};
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = fmaf(wv, (float)x[u][c], acc[c]);
+      for (int c = 0; c < 4; ++c) {
+        acc[2 * c] = fmaf(wv, bf16_to_f32(wd[c] & 0xffffu), acc[2 * c]);
+        acc[2 * c + 1] = fmaf(wv, bf16_to_f32(wd[c] >> 16), acc[2 * c + 1]);
+      }
     }
   }
   float* part = reinterpret_cast<float*>(wgt + 0);   // the weights are no longer needed
@@ -1094,7 +1095,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
   k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
   k.ang = reinterpret_cast<const float2*>(w8 + p.off_ang);
-  k.part_o = p.nsplit > 1 ? reinterpret_cast<_Float16*>(w8 + p.off_po) : nullptr;
+  k.part_o = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(w8 + p.off_po) : nullptr;
   k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
   k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;
   k.H = a.H; k.D = a.D; k.r = a.r; k.theta = a.theta;

@@ -17,7 +17,7 @@ DEV = "cuda"
 FMT_T = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def _indices(seed, B, Tq, q_pos0, N, m, k, holes=True):
+def _indices(seed, B, Tq, q_pos0, N, m, k, holes=True, past_end=False):
     rng = np.random.default_rng(seed)
     idx = np.full((B, Tq, k), -1, np.int32)
     for b in range(B):
@@ -27,23 +27,28 @@ def _indices(seed, B, Tq, q_pos0, N, m, k, holes=True):
             sel = np.sort(rng.choice(nv, n, replace=False)) if n else np.zeros(0, int)
             if holes and n > 2:
                 sel[rng.integers(0, n)] = -1          # a skipped slot inside the list
+            if past_end and n > 4:                    # slots naming no entry (>= N)
+                sel[rng.integers(0, n, 3)] = [N, N + 7, 1 << 30]
             idx[b, i, :n] = sel
     return idx
 
 
-def _case(mode, B, Tq, H, D, r, N, k, m, W, q_pos0, fmt, seed, sink=False, rows=None):
+def _case(mode, B, Tq, H, D, r, N, k, m, W, q_pos0, fmt, seed, sink=False, rows=None,
+          past_end=False, kv_scale=1.0):
     print(f"attend mode={mode} B={B} Tq={Tq} H={H} D={D} N={N} k={k} m={m} W={W} {fmt} "
-          f"sink={sink}", flush=True)
+          f"sink={sink} past_end={past_end} kv_scale={kv_scale}", flush=True)
     q_fmt = "f32" if fmt == "f32" else "bf16"
-    q = synth.store(synth.normal(seed, "q", (B, Tq, H, D)), q_fmt)
-    kv = synth.store(synth.normal(seed, "kv", (B, N, D)), fmt, r)
+    # kv_scale scales the entries and divides the queries, so the logits keep
+    # their size while the values (and outputs) take the scale
+    q = synth.store(synth.normal(seed, "q", (B, Tq, H, D), std=1.0 / kv_scale), q_fmt)
+    kv = synth.store(synth.normal(seed, "kv", (B, N, D), std=kv_scale), fmt, r)
     raw_pos0 = [max(0, p - W + 1) for p in q_pos0]
     T_raw = max(q_pos0[b] + Tq - raw_pos0[b] for b in range(B)) if W > 0 else 0
-    raw = synth.store(synth.normal(seed, "raw", (B, max(T_raw, 1), D)), fmt, r)
+    raw = synth.store(synth.normal(seed, "raw", (B, max(T_raw, 1), D), std=kv_scale), fmt, r)
     sk = synth.normal(seed, "sink", (H,)) * 2.0 if sink else None
     out = torch.empty((B, Tq, H, D), dtype=FMT_T[q_fmt], device=DEV)
     if mode == 0:
-        idx = _indices(seed, B, Tq, q_pos0, N, m, k)
+        idx = _indices(seed, B, Tq, q_pos0, N, m, k, past_end=past_end)
         lac.csa_attend(q.to(DEV), kv.to(DEV), torch.from_numpy(idx).to(DEV), raw.to(DEV), W,
                        q_pos0=q_pos0, raw_pos0=raw_pos0, rope_dims=r,
                        sink=None if sk is None else sk.to(DEV), out=out)
@@ -155,3 +160,22 @@ def test_hca_mixed_decode_over_64_splits_with_sink():
 def test_hca_bf16_h8_decode_group():
     # H = 8, four tokens of one sequence: the block's queries share the entries
     _case(1, 2, 4, 8, 128, 64, 900, 0, 128, 32, [900 * 128 - 2, 300 * 128], "bf16", 16)
+
+
+def test_csa_indices_past_the_cache_are_skipped():
+    # slots holding N, N + 7 and 2^30 name no entry (include/lac.h): skipped
+    # like -1, on the split decode path and the float32 path
+    _case(0, 3, 1, 64, 512, 64, 3000, 256, 4, 128, [12000, 12003, 8000], "bf16", 51,
+          past_end=True)
+    _case(0, 2, 9, 8, 128, 64, 30, 5, 4, 3, [100, 7], "f32", 52, past_end=True)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_values_around_1e5_on_split_and_single_split_launches(mode):
+    # KV values of about 1e5 (above the float16 range) are valid bf16 input;
+    # decode shapes run several splits per query, the 300-query prefill one
+    N, k, m = (3000, 256, 4) if mode == 0 else (200, 0, 16)
+    _case(mode, 2, 1, 64, 512, 64, N, k, m, 128, [12000, 3200], "bf16", 53 + mode,
+          kv_scale=1e5)
+    _case(mode, 1, 300, 64, 128, 64, N, k, m, 16, [3000], "bf16", 55 + mode, kv_scale=1e5,
+          rows=[(0, i) for i in range(0, 300, 23)])

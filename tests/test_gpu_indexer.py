@@ -53,7 +53,8 @@ def test_f32_tiny_prefill_all_queries():
     _run(1, 256, 4, 32, 64, 4, 16, [0], "f32", 0)
 
 
-def test_bf16_decode_rowwise_ragged():
+def test_bf16_decode_prefix_path_ragged():
+    # n_vis up to 5003: one workgroup per row holding the row in registers
     _run(4, 1, 64, 128, 5003, 4, 512, [4 * 5003 + 1, 4 * 5003, 4 * 3000 + 3, 40000], "bf16", 1)
 
 
@@ -72,7 +73,7 @@ def test_bf16_decode_split_path_all_tied_takes_lowest_indices():
     assert torch.equal(idx[0, 0].cpu(), torch.arange(k, dtype=torch.int32))
 
 
-def test_bf16_rowwise_all_tied_takes_lowest_indices():
+def test_bf16_prefix_path_all_tied_takes_lowest_indices():
     _run(2, 1, 32, 64, 3000, 4, 100, [12000, 12000], "bf16", 4, w_zero=True)
 
 
@@ -125,3 +126,49 @@ def test_e4m3_keys_chunked_prefill_causal_rows():
 def test_e4m3_keys_head_and_dim_variants(HI, dI):
     _run(2, 3, HI, dI, 2100, 4, 256, [8400, 9000], "bf16", 24 + HI + dI, kfmt="mixed")
 
+
+
+# Rows longer than the register-resident kernel holds (67584 visible entries)
+# and too many of them for the split path (more than 64 rows): the 8-bit radix
+# select, one workgroup per row.  Drawn on the GPU; the oracle scores sampled
+# rows from a host copy of their sequences.
+def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zero=False):
+    print(f"indexer (row-wise radix path) B={B} Tq={Tq} N={N} k={k}", flush=True)
+    q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI), device=DEV), "bf16")
+    K = synth.store(synth.normal(seed, "KI", (B, N, dI), device=DEV), "bf16")
+    w = synth.uniform(seed, "w", (B, Tq, HI), device=DEV)
+    if w_zero:
+        w.zero_()
+    score = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    idx = lac.indexer_topk(q, w, K, m=m, k=k, q_pos0=qpos, topk_score=score)
+    torch.cuda.synchronize()
+    sub = lambda t: host(t[seqs].contiguous())
+    rows = [(j, i) for j in range(len(seqs)) for i in rows_per_seq]
+    s, nv = oracle.index_scores(sub(q), sub(w), sub(K), synth.BF16, len(seqs), Tq, HI, dI, N,
+                                [qpos[b] for b in seqs], m, rows)
+    assert (nv > 67584).all() and B * Tq > 64
+    o_idx = oracle.topk(s, nv, k)
+    g_idx = np.stack([idx[seqs[j], i].cpu().numpy() for j, i in rows])
+    g_sc = np.stack([score[seqs[j], i].cpu().numpy() for j, i in rows])
+    check_topk(g_idx, o_idx, s, nv, k)
+    for rr in range(len(rows)):
+        keff = min(k, int(nv[rr]))
+        gi = g_idx[rr, :keff]
+        assert (np.diff(gi) > 0).all(), "indices must be ascending"
+        assert np.allclose(g_sc[rr, :keff], s[rr, gi], rtol=1e-4, atol=1e-3)
+    return idx
+
+
+def test_bf16_rowwise_kernel_prefill_rows_past_67584():
+    # 80 queries at 280000..280079: n_vis 70000..70019 > 67584, 80 rows > 64
+    _run_gpu_drawn(1, 80, 32, 64, 70080, 4, 2048, [280000], 41, [0], [0, 1, 39, 40, 78, 79])
+
+
+def test_bf16_rowwise_kernel_decode_72_sequences():
+    qpos = [4 * 70080 - 8 * b for b in range(72)]
+    _run_gpu_drawn(72, 1, 32, 64, 70080, 4, 2048, qpos, 42, [0, 35, 71], [0])
+
+
+def test_bf16_rowwise_kernel_all_tied_takes_lowest_indices():
+    idx = _run_gpu_drawn(1, 80, 32, 64, 70080, 4, 2048, [280000], 43, [0], [0, 79], w_zero=True)
+    assert torch.equal(idx[0].cpu(), torch.arange(2048, dtype=torch.int32).expand(80, 2048))
