@@ -20,7 +20,9 @@
  *   pointers must be 16-byte aligned.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Work is
  *   enqueued asynchronously; the calls are thread-safe (no global state
- *   except the thread-local error string and the thread-local launch timer).
+ *   except the thread-local error string, the thread-local launch timer and
+ *   the fixed device scratch of indexer_topk_noalloc, whose overlapping calls
+ *   on one GPU race).
  * Positions.  Host arrays of B int64 (NULL = all zero).  Query i of sequence
  *   b sits at absolute position q_pos0[b] + i; raw row i at raw_pos0[b] + i.
  *   Compressed entry j covers positions [j*m, j*m + m - 1] and is rotated at
@@ -175,6 +177,26 @@ int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32
                      int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
                      const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * indexer_topk_noalloc -- indexer_topk for callers that cannot allocate
+ * device memory: code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as
+ * indexer_topk, without the workspace: the call uses a fixed scratch array
+ * that the library holds in device memory, 32 MiB on each GPU it runs on,
+ * from the first call on that GPU until the process ends.  The call itself
+ * allocates and frees nothing.  A call whose indexer_topk_workspace_size(B,
+ * Tq, N, k) exceeds 32 MiB returns LAC_ERR_WORKSPACE and enqueues nothing
+ * (32 MiB covers, e.g., B = 4 rows at N = 262144 and B = 32 at N = 32768).
+ * Every call on one GPU shares that GPU's array and the array keeps the last
+ * call's contents (each call clears what it needs cleared): calls that may
+ * overlap on one GPU (different streams, or host threads without ordering)
+ * race, and must be serialised by the caller.
+ */
+int32_t indexer_topk_noalloc(const void* q_idx, const float* w, const void* k_idx, int32_t dtype,
+                             int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
+                             const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
+                             float* topk_score, void* stream);
 
 /*
  * attend_workspace_size -- scratch for csa_attend / hca_attend: the rotated

@@ -20,6 +20,7 @@ import torch
 
 __all__ = [
     "LacError", "csa_compress", "hca_compress", "indexer_topk", "indexer_topk_workspace_size",
+    "indexer_topk_noalloc",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
     "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "KERNELS",
@@ -54,6 +55,8 @@ lib.indexer_topk_workspace_size.restype = _sz
 lib.indexer_topk.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _i32, _i32,
                              _vp, _vp, _vp, _sz, _vp]
 lib.indexer_topk.restype = _i32
+lib.indexer_topk_noalloc.argtypes = lib.indexer_topk.argtypes[:-3] + [_vp]
+lib.indexer_topk_noalloc.restype = _i32
 lib.attend_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
 lib.attend_workspace_size.restype = _sz
 lib.csa_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _f32,
@@ -201,6 +204,24 @@ def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=N
     _check(lib.indexer_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
                             _positions(q_pos0, B), m, k, _ptr(topk_idx), _ptr(topk_score),
                             _ptr(workspace), workspace.numel(), _stream(stream)))
+    return topk_idx
+
+
+def indexer_topk_noalloc(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
+                         stream=None):
+    """indexer_topk on the library's fixed per-device scratch (no workspace, no
+    allocation in the call; see include/lac.h).  topk_idx must be given when
+    the caller cannot allocate."""
+    B, Tq, HI, dI = q_idx.shape
+    N = k_idx.shape[1]
+    dt = LAC_KV_E4M3_ROPE_BF16 if k_idx.dtype == torch.uint8 else _fmt(q_idx)
+    for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
+        _need_dense(t, nm)
+    if topk_idx is None:
+        topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
+    _check(lib.indexer_topk_noalloc(_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
+                                    _positions(q_pos0, B), m, k, _ptr(topk_idx),
+                                    _ptr(topk_score), _stream(stream)))
     return topk_idx
 
 

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblac.so")
-SOURCES = ["abi.cpp", "compress.hip", "score.hip", "indexer.hip", "attend.hip", "project.hip"]
+SOURCES = ["abi.cpp", "compress.hip", "score.hip", "indexer.hip", "attend.hip", "project.hip",
+           "noalloc.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 FLAGS = [

@@ -107,6 +107,58 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
   return launch_status(fn, lac::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
+// indexer_topk and indexer_topk_noalloc.  With `fixed`, the workspace is the
+// library's per-device scratch array (looked up only after every argument
+// has been validated), and workspace_bytes is its size.
+int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const void* k_idx,
+                     int32_t dtype, int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
+                     const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
+                     float* topk_score, void* workspace, size_t workspace_bytes, bool fixed,
+                     void* stream) {
+  if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: dtype must be LAC_F32, LAC_BF16 or LAC_KV_E4M3_ROPE_BF16",
+                fn);
+  if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
+  if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
+  if (m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
+  if (k < 1 || k > 8192) return fail(LAC_ERR_INVALID, "%s: k = %d outside [1, 8192]", fn, k);
+  if (H_I < 1 || d_I < 1) return fail(LAC_ERR_INVALID, "%s: H_I and d_I must be >= 1", fn);
+  if (dtype != LAC_F32) {
+    if ((H_I != 32 && H_I != 64 && H_I != 128) || (d_I != 64 && d_I != 128))
+      return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H_I in {32, 64, 128} and d_I in {64, 128}", fn);
+  } else if ((int64_t)H_I * d_I > 8192) {
+    return fail(LAC_ERR_UNSUPPORTED, "%s: float32 path needs H_I * d_I <= 8192", fn);
+  }
+  lac::IndexerArgs a{};
+  int32_t st = take_positions(fn, "q_pos0", q_pos0, B, Tq, 1, &a.qpos);
+  if (st) return st;
+  if ((int64_t)B * Tq == 0) { g_err[0] = 0; return LAC_OK; }
+  if (!q_idx || !w || !topk_idx || (N > 0 && !k_idx)) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
+  if (!aligned(q_idx, 16) || !aligned(w, 4) || (k_idx && !aligned(k_idx, 16)) ||
+      !aligned(topk_idx, 4) || (topk_score && !aligned(topk_score, 4)))
+    return fail(LAC_ERR_INVALID, "%s: misaligned tensor pointer", fn);
+  const size_t need = lac::indexer_workspace_bytes(B, Tq, N, k);
+  if (fixed) {
+    if (need > workspace_bytes)
+      return fail(LAC_ERR_WORKSPACE,
+                  "%s: this call needs %zu bytes of scratch, above the fixed %zu (use indexer_topk "
+                  "with a workspace)", fn, need, workspace_bytes);
+    const hipError_t e = lac::noalloc_scratch(&workspace);
+    if (e != hipSuccess)
+      return fail(LAC_ERR_DEVICE, "%s: no scratch address on the current device: %s", fn,
+                  hipGetErrorString(e));
+  } else {
+    if (!workspace || !aligned(workspace, 256))
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace must be non-null and 256-byte aligned", fn);
+    if (workspace_bytes < need)
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
+  }
+  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype;
+  a.B = B; a.Tq = Tq; a.HI = H_I; a.dI = d_I; a.N = N; a.m = m; a.k = k;
+  a.topk_idx = topk_idx; a.topk_score = topk_score;
+  return launch_status(fn, lac::launch_indexer_topk(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
 struct AttendCommon {
   const void* q; int32_t q_dtype; const void* kv; int32_t kv_dtype; int32_t N;
   const void* raw; int32_t T_raw; const int64_t* raw_pos0; int32_t W; const float* sink;
@@ -285,41 +337,24 @@ int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32
                      int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
                      const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* fn = "indexer_topk";
   try {
-    if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16)
-      return fail(LAC_ERR_UNSUPPORTED, "%s: dtype must be LAC_F32, LAC_BF16 or LAC_KV_E4M3_ROPE_BF16",
-                  fn);
-    if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
-    if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
-    if (m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
-    if (k < 1 || k > 8192) return fail(LAC_ERR_INVALID, "%s: k = %d outside [1, 8192]", fn, k);
-    if (H_I < 1 || d_I < 1) return fail(LAC_ERR_INVALID, "%s: H_I and d_I must be >= 1", fn);
-    if (dtype != LAC_F32) {
-      if ((H_I != 32 && H_I != 64 && H_I != 128) || (d_I != 64 && d_I != 128))
-        return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H_I in {32, 64, 128} and d_I in {64, 128}", fn);
-    } else if ((int64_t)H_I * d_I > 8192) {
-      return fail(LAC_ERR_UNSUPPORTED, "%s: float32 path needs H_I * d_I <= 8192", fn);
-    }
-    lac::IndexerArgs a{};
-    int32_t st = take_positions(fn, "q_pos0", q_pos0, B, Tq, 1, &a.qpos);
-    if (st) return st;
-    if ((int64_t)B * Tq == 0) { g_err[0] = 0; return LAC_OK; }
-    if (!q_idx || !w || !topk_idx || (N > 0 && !k_idx)) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
-    if (!aligned(q_idx, 16) || !aligned(w, 4) || (k_idx && !aligned(k_idx, 16)) ||
-        !aligned(topk_idx, 4) || (topk_score && !aligned(topk_score, 4)))
-      return fail(LAC_ERR_INVALID, "%s: misaligned tensor pointer", fn);
-    const size_t need = lac::indexer_workspace_bytes(B, Tq, N, k);
-    if (!workspace || !aligned(workspace, 256))
-      return fail(LAC_ERR_WORKSPACE, "%s: workspace must be non-null and 256-byte aligned", fn);
-    if (workspace_bytes < need)
-      return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
-    a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype;
-    a.B = B; a.Tq = Tq; a.HI = H_I; a.dI = d_I; a.N = N; a.m = m; a.k = k;
-    a.topk_idx = topk_idx; a.topk_score = topk_score;
-    return launch_status(fn, lac::launch_indexer_topk(a, workspace, static_cast<hipStream_t>(stream)));
+    return indexer_impl("indexer_topk", q_idx, w, k_idx, dtype, B, Tq, H_I, d_I, N, q_pos0, m, k,
+                        topk_idx, topk_score, workspace, workspace_bytes, false, stream);
   } catch (...) {
-    return fail(LAC_ERR_DEVICE, "%s: internal error", fn);
+    return fail(LAC_ERR_DEVICE, "indexer_topk: internal error");
+  }
+}
+
+int32_t indexer_topk_noalloc(const void* q_idx, const float* w, const void* k_idx, int32_t dtype,
+                             int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
+                             const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
+                             float* topk_score, void* stream) {
+  try {
+    return indexer_impl("indexer_topk_noalloc", q_idx, w, k_idx, dtype, B, Tq, H_I, d_I, N,
+                        q_pos0, m, k, topk_idx, topk_score, nullptr, lac::kNoallocScratchBytes,
+                        true, stream);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "indexer_topk_noalloc: internal error");
   }
 }
 

@@ -76,6 +76,12 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
                                  hipStream_t st);
 hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st);
 
+// ---------------------------------------------------------------- fixed scratch
+// Size of the per-device scratch array of the allocation-free entry point, and
+// its device address on the current device (looked up once per device).
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(void** ptr);
+
 // ---------------------------------------------------------------- attention
 struct AttendArgs {
   const void* q;          // [B, Tq, H, D]
