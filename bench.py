@@ -14,7 +14,13 @@ Other workloads (--workload): pair_decode_1m_e4m3_indexer (the same step with
 the indexer keys stored as E4M3, one byte per dim), csa_decode_128k (32
 sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
-hca_prefill_8k (8192 tokens; TFLOP/s).
+hca_prefill_8k (8192 tokens; TFLOP/s), bulk_compress_1m and
+bulk_compress_128k (building the compressed caches of whole contexts from raw
+activations; GB/s), and the grouped output projection.
+
+Each step's library calls are marshalled once per cache set (lac.CallList)
+and replayed, so the host cost of a step is one ctypes call per entry point
+plus the library's own validation and launches.
 
 Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -111,7 +117,9 @@ class PairDecode:
                                                             c["Nh"], c["W"]),
                                   dtype=torch.uint8, device=dev)
 
-    def step(self, i, timer=None):
+    timer_kernel = "indexer_score"
+
+    def step(self, i):
         lac, c, s = self.lac, self.c, self.sets[i % len(self.sets)]
         N, Nh, m, mh, ctx = c["N"], c["Nh"], c["m"], c["m_hca"], self.ctx
         # the CSA layer: compress its newest block (KV entry and indexer key),
@@ -121,8 +129,6 @@ class PairDecode:
                          rope_dims=c["r"], pos0=ctx - m, norm_gain=g)
         lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m, rope_dims=0,
                          pos0=ctx - m)
-        if timer is not None:
-            lac.time_next_launch("indexer_score", *timer)
         lac.indexer_topk(s["qI"], s["w"], s["KI"], m=m, k=c["k"], q_pos0=ctx, topk_idx=self.idx,
                          workspace=self.ws_idx)
         lac.csa_attend(s["q_csa"], s["ckv"], self.idx, s["raw_csa"], c["W"], q_pos0=ctx,
@@ -233,10 +239,8 @@ class CsaDecode(PairDecode):
         self.ws = torch.empty(lac.attend_workspace_size(B, 1, c["H"], c["D"], c["r"], 1, c["k"],
                                                         c["W"]), dtype=torch.uint8, device=dev)
 
-    def step(self, i, timer=None):
+    def step(self, i):
         lac, c, s = self.lac, self.c, self.sets[i % len(self.sets)]
-        if timer is not None:
-            lac.time_next_launch("indexer_score", *timer)
         lac.indexer_topk(s["qI"], s["w"], s["KI"], m=c["m"], k=c["k"], q_pos0=self.ctx,
                          topk_idx=self.idx, workspace=self.ws_idx)
         lac.csa_attend(s["q"], s["ckv"], self.idx, s["raw"], c["W"], q_pos0=self.ctx,
@@ -275,6 +279,7 @@ class CsaDecode(PairDecode):
 class ChunkPrefill:
     name = "csa_chunk_prefill"
     unit = "TFLOP/s"
+    timer_kernel = "indexer_score"
 
     def __init__(self, lac, synth, dev, sets, seed=3):
         self.lac = lac
@@ -288,15 +293,13 @@ class ChunkPrefill:
                                                         c["W"]), dtype=torch.uint8, device=dev)
         self.sets = [c]
 
-    def step(self, i, timer=None):
+    def step(self, i):
         lac, c = self.lac, self.c
         n0, n1 = c["N_ctx"], c["N"]
         lac.csa_compress(c["raw"][:, c["W"] - 1:], c["z"], c["ckv"][:, n0:n1], m=c["m"],
                          rope_dims=c["r"], pos0=c["pos0"], T=c["chunk"])
         lac.csa_compress(c["kI_raw"], c["zI"], c["KI"][:, n0:n1], m=c["m"], rope_dims=0,
                          pos0=c["pos0"])
-        if timer is not None:
-            lac.time_next_launch("indexer_score", *timer)
         lac.indexer_topk(c["qI"], c["w"], c["KI"], m=c["m"], k=c["k"], q_pos0=c["q_pos0"],
                          topk_idx=self.idx, workspace=self.ws_idx)
         lac.csa_attend(c["q"], c["ckv"], self.idx, c["raw"], c["W"], q_pos0=c["q_pos0"],
@@ -348,6 +351,7 @@ class ChunkPrefill:
 
 class HcaPrefill(ChunkPrefill):
     name = "hca_prefill_8k"
+    timer_kernel = "attend"
 
     def __init__(self, lac, synth, dev, sets, seed=1):
         self.lac = lac
@@ -359,11 +363,9 @@ class HcaPrefill(ChunkPrefill):
                               dtype=torch.uint8, device=dev)
         self.sets = [c]
 
-    def step(self, i, timer=None):
+    def step(self, i):
         lac, c = self.lac, self.c
         lac.hca_compress(c["kv"], c["z"], self.hkv, m=c["m"], rope_dims=c["r"], pos0=0)
-        if timer is not None:
-            lac.time_next_launch("attend", *timer)
         lac.hca_attend(c["q"], self.hkv, c["kv"], c["W"], m=c["m"], q_pos0=0, raw_pos0=0,
                        rope_dims=c["r"], out=self.out, workspace=self.ws)
 
@@ -410,6 +412,7 @@ class ProjectionPrefill:
     name = "grouped_projection_prefill"
     unit = "TFLOP/s"
     kernel = "gemm_nt_bf16_kernel (both products)"
+    timer_kernel = "project"
 
     def __init__(self, lac, synth, dev, sets, seed=5):
         self.lac = lac
@@ -419,10 +422,8 @@ class ProjectionPrefill:
                               dtype=torch.uint8, device=dev)
         self.sets = [c]
 
-    def step(self, i, timer=None):
+    def step(self, i):
         c = self.c
-        if timer is not None:
-            self.lac.time_next_launch("project", *timer)
         self.lac.grouped_output_projection(c["attn"], c["w1"], c["w2"], out=self.out,
                                            workspace=self.ws)
 
@@ -498,8 +499,108 @@ class ProjectionDecode(ProjectionPrefill):
                 "sample": f"{reps} whole calls of {c['T']} tokens"}
 
 
+class BulkCompress1M:
+    """Building the compressed caches of a 1M-token CSA + HCA layer pair from
+    raw activations (4 sequences of 2^20 tokens): CSA entries (m = 4, E4M3 +
+    bf16 rotated dims), indexer keys (m = 4, bf16) and HCA entries (m' = 128,
+    E4M3 + bf16), each layer from its own raw KV and logits."""
+    name = "bulk_compress_1m"
+    unit = "GB/s"
+    timer_kernel = "compress"
+    kernel = "compress_kernel (CSA entries, m = 4)"
+
+    def __init__(self, lac, synth, dev, sets, seed=4, B=4, T=1 << 20):
+        self.lac = lac
+        c = self.c = synth.bulk_compress(seed=seed, B=B, T=T, device=dev)
+        self.r, self.m, self.mh = 64, 4, 128
+        D, dI = c["D"], c["dI"]
+        row = D - self.r + 2 * self.r
+        self.ckv = torch.empty((B, T // self.m, row), dtype=torch.uint8, device=dev)
+        self.KI = torch.empty((B, T // self.m, dI), dtype=torch.bfloat16, device=dev)
+        self.hkv = torch.empty((B, T // self.mh, row), dtype=torch.uint8, device=dev)
+        self.sets = [c]
+
+    def step(self, i):
+        lac, c = self.lac, self.c
+        lac.csa_compress(c["kv"], c["z"], self.ckv, m=self.m, rope_dims=self.r, pos0=0)
+        lac.csa_compress(c["kI_raw"], c["zI"], self.KI, m=self.m, rope_dims=0, pos0=0)
+        lac.hca_compress(c["kv_hca"], c["z_hca"], self.hkv, m=self.mh, rope_dims=self.r, pos0=0)
+
+    def tokens_per_step(self):
+        return self.c["B"] * self.c["T"]
+
+    def kernel_bytes(self):
+        """Bytes of the timed launch (the CSA entries): raw KV and logits read,
+        entries written."""
+        c = self.c
+        return c["B"] * c["T"] * c["D"] * 2 * 2 + self.ckv.numel()
+
+    def bytes_per_step(self):
+        c = self.c
+        rd = c["B"] * c["T"] * (2 * c["D"] + 2 * c["dI"] + (2 * c["D"] if "kv_hca" in c else 0)) * 2
+        wr = self.ckv.numel() + self.KI.numel() * 2 + (self.hkv.numel() if "kv_hca" in c else 0)
+        return rd + wr
+
+    def config(self):
+        c = self.c
+        return {"workload": self.name, "batch": c["B"], "tokens": c["T"], "kv_dim": c["D"],
+                "indexer_dim": c["dI"], "m": self.m, "m_hca": self.mh, "rope_dims": self.r,
+                "in_format": "bf16", "out_format": "csa/hca e4m3 + bf16 rope dims, keys bf16"}
+
+    def cpu_sample(self):
+        import oracle
+        import synth
+
+        c = self.c
+        n = 4096                      # raw tokens of sequence 0 per layer
+        h = {k_: synth.host_bytes(c[k_][0, :n]) for k_ in ("kv", "z", "kI_raw", "zI", "kv_hca",
+                                                            "z_hca") if k_ in c}
+        t0 = time.perf_counter()
+        oracle.compress(h["kv"], h["z"], oracle.BF16, 1, n, c["D"], self.m, self.r)
+        oracle.compress(h["kI_raw"], h["zI"], oracle.BF16, 1, n, c["dI"], self.m, 0)
+        if "kv_hca" in h:
+            oracle.compress(h["kv_hca"], h["z_hca"], oracle.BF16, 1, n, c["D"], self.mh, self.r)
+        el = time.perf_counter() - t0
+        frac = n / (c["B"] * c["T"])
+        return {"value": self.bytes_per_step() * frac / el / 1e9, "unit": self.unit,
+                "seconds": el, "sample": f"the first {n} tokens of sequence 0 (every cache), "
+                                         "bytes scaled by the same fraction"}
+
+
+class BulkCompress128K(BulkCompress1M):
+    """Building the CSA caches of 32 sequences of 131072 tokens (bf16 entries
+    and indexer keys) from raw activations."""
+    name = "bulk_compress_128k"
+    kernel = "compress_kernel (CSA entries, m = 4)"
+
+    def __init__(self, lac, synth, dev, sets, seed=2, B=32, T=131072):
+        self.lac = lac
+        c = self.c = synth.bulk_compress(seed=seed, B=B, T=T, hca=False, device=dev)
+        self.r, self.m, self.mh = 64, 4, 128
+        self.ckv = torch.empty((B, T // self.m, c["D"]), dtype=torch.bfloat16, device=dev)
+        self.KI = torch.empty((B, T // self.m, c["dI"]), dtype=torch.bfloat16, device=dev)
+        self.sets = [c]
+
+    def step(self, i):
+        lac, c = self.lac, self.c
+        lac.csa_compress(c["kv"], c["z"], self.ckv, m=self.m, rope_dims=self.r, pos0=0)
+        lac.csa_compress(c["kI_raw"], c["zI"], self.KI, m=self.m, rope_dims=0, pos0=0)
+
+    def kernel_bytes(self):
+        c = self.c
+        return c["B"] * c["T"] * c["D"] * 2 * 2 + self.ckv.numel() * 2
+
+    def config(self):
+        d = super().config()
+        d["out_format"] = "bf16"
+        d.pop("m_hca")
+        return d
+
+
 WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeRmsNorm, CsaDecode,
-                                  ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode)}
+                                  ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode,
+                                  BulkCompress1M, BulkCompress128K)}
+
 
 
 def main():
@@ -534,9 +635,15 @@ def main():
     import synth
 
     wl = WORKLOADS[args.workload](lac, synth, dev, args.sets)
+    # one marshalled call list per cache set (the binding records, not runs)
+    lists = []
+    for i in range(len(wl.sets)):
+        with lac.CallList() as cl:
+            wl.step(i)
+        lists.append(cl)
     torch.cuda.synchronize()
     for i in range(args.warmup):
-        wl.step(i)
+        lists[i % len(lists)].run()
     torch.cuda.synchronize()
     timers = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.steps)]
@@ -546,7 +653,9 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        wl.step(args.warmup + i, timer=timers[i])
+        lac.time_next_launch(wl.timer_kernel, *timers[i])
+        lists[(args.warmup + i) % len(lists)].run()
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el * 1e3 / args.steps
@@ -564,7 +673,18 @@ def main():
         res["roofline"] = {"bound": "hbm", "kernel": wl.kernel, "achieved": round(ach, 1),
                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                           "traffic_unit": "B/call", "launch_ms": round(kern_ms, 5)}
+                           "traffic_unit": "B/call", "launch_ms": round(kern_ms, 5),
+                           "step_frac": round(res["hbm_gbps"] / HBM_PEAK_GBS, 4)}
+    elif isinstance(wl, BulkCompress1M):
+        res["value"] = wl.bytes_per_step() / (ms / 1e3) / 1e9
+        res["unit"] = "GB/s"
+        res["tokens_per_s"] = wl.tokens_per_step() / (ms / 1e3)
+        ach = wl.kernel_bytes() / (kern_ms / 1e3) / 1e9
+        res["roofline"] = {"bound": "hbm", "kernel": wl.kernel, "achieved": round(ach, 1),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                           "traffic_unit": "B/launch", "launch_ms": round(kern_ms, 5),
+                           "step_frac": round(res["value"] / HBM_PEAK_GBS, 4)}
     elif wl.unit == "tokens/s":
         res["value"] = wl.tokens_per_step() / (ms / 1e3)
         res["unit"] = "tokens/s"
@@ -574,7 +694,8 @@ def main():
                            "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(ach / HBM_PEAK_GBS, 4),
                            "traffic": _score_traffic(wl.name), "traffic_unit": "B/launch",
-                           "launch_ms": round(kern_ms, 5)}
+                           "launch_ms": round(kern_ms, 5),
+                           "step_frac": round(res["hbm_gbps"] / HBM_PEAK_GBS, 4)}
     else:
         fl = wl.flops_per_step()
         res["value"] = fl / (ms / 1e3) / 1e12
@@ -586,14 +707,16 @@ def main():
         elif isinstance(wl, HcaPrefill):
             kfl, kname, traffic = fl, "attend_mfma_kernel (HCA attention)", None
         else:
-            kfl, kname = wl.indexer_flops(), "score_bf16_kernel (indexer scores)"
+            kfl, kname = wl.indexer_flops(), "score_prefill_kernel (indexer scores)"
             traffic = _score_traffic(wl.name)
         ach = kfl / (kern_ms / 1e3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                            "traffic_unit": "B/launch",
-                           "launch_ms": round(kern_ms / launches, 5)}
+                           "launch_ms": round(kern_ms / launches, 5),
+                           "step_frac": round(res["value"] / BF16_PEAK_TFLOPS, 4)}
+    res["host_enqueue_ms_per_step"] = round((t_enq - t0) * 1e3 / args.steps, 5)
     if not args.no_cpu:
         import oracle
         cb = wl.cpu_sample()

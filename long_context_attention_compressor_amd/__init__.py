@@ -23,7 +23,7 @@ __all__ = [
     "indexer_topk_noalloc",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
-    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "KERNELS",
+    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "KERNELS", "CallList",
 ]
 
 LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 = 0, 1, 2
@@ -89,6 +89,50 @@ class LacError(RuntimeError):
 def _check(status: int):
     if status != 0:
         raise LacError(status, lib.lac_last_error().decode())
+
+
+_recording = None
+
+
+def _call(fn, args):
+    """Calls an entry point, or (inside a CallList) records the call with its
+    arguments already converted to their ctypes types."""
+    if _recording is None:
+        _check(fn(*args))
+        return
+    conv = []
+    for t, a in zip(fn.argtypes, args):
+        conv.append(a if a is None or isinstance(a, (ctypes.Array, ctypes._SimpleCData)) else t(a))
+    _recording.append((fn, tuple(conv)))
+
+
+class CallList:
+    """A fixed sequence of library calls, marshalled once and replayed.
+
+    Inside ``with CallList() as cl:`` the entry points of this module record
+    their C call (tensor pointers, sizes, positions, the current stream)
+    instead of making it; ``cl.run()`` then makes the recorded calls in order,
+    one ctypes call each, with the same validation in the library.  The
+    tensors behind the recorded pointers must stay alive and in place."""
+
+    def __init__(self):
+        self.calls = []
+
+    def __enter__(self):
+        global _recording
+        _recording = self.calls
+        return self
+
+    def __exit__(self, *exc):
+        global _recording
+        _recording = None
+        return False
+
+    def run(self):
+        for fn, a in self.calls:
+            st = fn(*a)
+            if st:
+                raise LacError(st, lib.lac_last_error().decode())
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -160,9 +204,9 @@ def _compress(fn, fn_norm, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, 
             _rows(logits, "logits"), _rows(out, "out")]
     gain = _norm_gain(norm_gain, D, raw_kv.device)
     if gain is None:
-        _check(fn(*args, _stream(stream)))
+        _call(fn, (*args, _stream(stream)))
     else:
-        _check(fn_norm(*args, _ptr(gain), norm_eps, _stream(stream)))
+        _call(fn_norm, (*args, _ptr(gain), norm_eps, _stream(stream)))
     return out
 
 
@@ -201,9 +245,9 @@ def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=N
     if topk_idx is None:
         topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
     workspace = _workspace(workspace, indexer_topk_workspace_size(B, Tq, N, k), q_idx.device)
-    _check(lib.indexer_topk(_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
-                            _positions(q_pos0, B), m, k, _ptr(topk_idx), _ptr(topk_score),
-                            _ptr(workspace), workspace.numel(), _stream(stream)))
+    _call(lib.indexer_topk, (_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
+                             _positions(q_pos0, B), m, k, _ptr(topk_idx), _ptr(topk_score),
+                             _ptr(workspace), workspace.numel(), _stream(stream)))
     return topk_idx
 
 
@@ -219,9 +263,9 @@ def indexer_topk_noalloc(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk
         _need_dense(t, nm)
     if topk_idx is None:
         topk_idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q_idx.device)
-    _check(lib.indexer_topk_noalloc(_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
-                                    _positions(q_pos0, B), m, k, _ptr(topk_idx),
-                                    _ptr(topk_score), _stream(stream)))
+    _call(lib.indexer_topk_noalloc, (_ptr(q_idx), _ptr(w), _ptr(k_idx), dt, B, Tq, HI, dI, N,
+                                     _positions(q_pos0, B), m, k, _ptr(topk_idx),
+                                     _ptr(topk_score), _stream(stream)))
     return topk_idx
 
 
@@ -256,9 +300,9 @@ def csa_attend(q, ckv, topk_idx, raw_kv, window, q_pos0=None, raw_pos0=None, rop
             _ptr(out), _ptr(workspace), workspace.numel()]
     gain = _norm_gain(q_norm_gain, D, q.device)
     if gain is None:
-        _check(lib.csa_attend(*args, _stream(stream)))
+        _call(lib.csa_attend, (*args, _stream(stream)))
     else:
-        _check(lib.csa_attend_rmsnorm(*args, _ptr(gain), norm_eps, _stream(stream)))
+        _call(lib.csa_attend_rmsnorm, (*args, _ptr(gain), norm_eps, _stream(stream)))
     return out
 
 
@@ -277,9 +321,9 @@ def hca_attend(q, hkv, raw_kv, window, m=128, q_pos0=None, raw_pos0=None, rope_d
             workspace.numel()]
     gain = _norm_gain(q_norm_gain, D, q.device)
     if gain is None:
-        _check(lib.hca_attend(*args, _stream(stream)))
+        _call(lib.hca_attend, (*args, _stream(stream)))
     else:
-        _check(lib.hca_attend_rmsnorm(*args, _ptr(gain), norm_eps, _stream(stream)))
+        _call(lib.hca_attend_rmsnorm, (*args, _ptr(gain), norm_eps, _stream(stream)))
     return out
 
 
@@ -309,9 +353,9 @@ def grouped_output_projection(attn, w1, w2, out=None, workspace=None, stream=Non
         raise ValueError("out must be a contiguous bf16 tensor of T*d values")
     workspace = _workspace(workspace, grouped_projection_workspace_size(T, H, D, G, d_g, d),
                            attn.device)
-    _check(lib.grouped_output_projection(_ptr(attn), _ptr(w1), _ptr(w2), T, H, D, G, d_g, d,
-                                         _ptr(out), _ptr(workspace), workspace.numel(),
-                                         _stream(stream)))
+    _call(lib.grouped_output_projection, (_ptr(attn), _ptr(w1), _ptr(w2), T, H, D, G, d_g, d,
+                                          _ptr(out), _ptr(workspace), workspace.numel(),
+                                          _stream(stream)))
     return out
 
 

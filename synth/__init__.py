@@ -201,3 +201,21 @@ def projection(seed=5, T=4096, H=64, D=512, G=8, d_g=1024, d=7168, device="cpu")
         w1=store(normal(seed, "w1", (G, d_g, K1), std=K1 ** -0.5, device=device), "bf16"),
         w2=store(normal(seed, "w2", (d, G * d_g), std=(G * d_g) ** -0.5, device=device), "bf16"),
     )
+
+
+def bulk_compress(seed=4, B=4, T=1 << 20, D=512, dI=128, hca=True, device="cpu"):
+    """Raw activations of whole contexts for building the compressed caches in
+    bulk: the CSA layer's KV and logits [B, T, D] and raw indexer keys and
+    logits [B, T, dI], and with hca the HCA layer's KV and logits [B, T, D];
+    all N(0, 1) in bf16.  Drawn one sequence at a time (names carry the
+    sequence) to bound the float32 temporaries."""
+    names = [("kv", D), ("z", D), ("kI_raw", dI), ("zI", dI)]
+    if hca:
+        names += [("kv_hca", D), ("z_hca", D)]
+    out = dict(kind="bulk_compress", B=B, T=T, D=D, dI=dI, pos0=0)
+    for name, width in names:
+        t = torch.empty((B, T, width), dtype=torch.bfloat16, device=device)
+        for b in range(B):
+            t[b] = normal(seed, f"{name}/{b}", (T, width), device=device).to(torch.bfloat16)
+        out[name] = t
+    return out
