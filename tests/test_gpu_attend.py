@@ -179,3 +179,24 @@ def test_values_around_1e5_on_split_and_single_split_launches(mode):
           kv_scale=1e5)
     _case(mode, 1, 300, 64, 128, 64, N, k, m, 16, [3000], "bf16", 55 + mode, kv_scale=1e5,
           rows=[(0, i) for i in range(0, 300, 23)])
+
+
+# D = 512 with whole 64-head tiles: single-split launches (output
+# normalised, sink and rotation at -t in the kernel), two head tiles, mixed
+# prefill windows rotated up front, and no rotated dims.
+def test_d512_csa_bf16_prefill_single_split_with_sink():
+    _case(0, 1, 260, 64, 512, 64, 1500, 64, 4, 128, [5000], "bf16", 61, sink=True,
+          rows=[(0, i) for i in (0, 1, 63, 64, 65, 127, 128, 200, 258, 259)])
+
+
+def test_d512_hca_mixed_prefill_two_head_tiles():
+    _case(1, 1, 40, 128, 512, 64, 80, 0, 64, 32, [5000], "mixed", 62)
+
+
+def test_d512_csa_mixed_prefill_single_split_with_sink():
+    _case(0, 1, 270, 64, 512, 64, 2000, 130, 4, 128, [7000], "mixed", 63, sink=True,
+          rows=[(0, i) for i in (0, 5, 99, 100, 150, 268, 269)])
+
+
+def test_d512_csa_bf16_decode_without_rotated_dims():
+    _case(0, 2, 1, 64, 512, 0, 900, 100, 4, 16, [3600, 3000], "bf16", 64)
