@@ -69,6 +69,9 @@ def _load():
     lib.lo_compress2.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, dbl, vp, i64, i64, vp, dbl,
                                  vp, vp]
     lib.lo_compress2.restype = i32
+    lib.lo_compress_overlap.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl, vp, i64,
+                                        i64, vp, vp]
+    lib.lo_compress_overlap.restype = i32
     lib.lo_rmsnorm.argtypes = [vp, i32, vp, dbl]
     lib.lo_rmsnorm.restype = None
     lib.lo_index_scores.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp, i32,
@@ -195,6 +198,28 @@ def compress(x, z, in_dtype, B, T, D, m, r=0, theta=10000.0, pos0=None,
                               _p(out), _p(alpha))
     if rc:
         raise ValueError(f"lo_compress rejected its arguments ({rc})")
+    return (out, alpha) if want_weights else out
+
+
+def compress_overlap(x, z, in_dtype, B, T, D, m, o, r=0, theta=10000.0, pos0=None,
+                     x_bstride=None, z_bstride=None, want_weights=False):
+    """CSA compression with overlapping windows: entry j pools positions
+    [max(0, p_j - o), p_j + m) (p_j = pos0 + j*m), then is rotated at p_j.
+    Row 0 of sequence b is at position pos0[b] - min(o, pos0[b]); T rows
+    follow that lead.  -> float64 [B, T//m, D] (and the weights
+    [B, T//m, m + o, D] when want_weights)."""
+    N = T // m
+    out = np.empty((B, N, D), np.float64)
+    alpha = np.empty((B, N, m + o, D), np.float64) if want_weights else None
+    pos = _i64(pos0, B)        # held until the call returns
+    lead = np.minimum(pos, o)
+    rows = T + int(lead.max()) if B else T
+    rc = _load().lo_compress_overlap(_p(x), _p(z), in_dtype, B, T, D, m, o, r, float(theta),
+                                     _p(pos), rows if x_bstride is None else x_bstride,
+                                     rows if z_bstride is None else z_bstride, _p(out),
+                                     _p(alpha))
+    if rc:
+        raise ValueError(f"lo_compress_overlap rejected its arguments ({rc})")
     return (out, alpha) if want_weights else out
 
 

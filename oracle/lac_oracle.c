@@ -282,6 +282,68 @@ int lo_compress(const void* x, const void* z, int in_dtype, int B, int T, int D,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Overlapping compression windows for CSA.  [P3] says, of HCA, that its     */
+/* compression has none of the overlap CSA's has and pools each m' tokens as  */
+/* one group; the pages give no extent.  Reading: CSA entry j (block start    */
+/* p_j = pos0 + j*m) pools the m tokens of its own block and the o tokens     */
+/* before it, positions [max(0, p_j - o), p_j + m), with one softmax over      */
+/* those tokens per channel; o = 0 is the plain compression above.  The       */
+/* newest token of entry j is still p_j + m - 1, so the causality rule of the */
+/* indexer and the attention (query t sees entry j iff j < floor(t/m)) is     */
+/* unchanged: the overlap reaches only further back.  The entry is rotated at */
+/* p_j.  Input rows: row 0 of sequence b is at position pos0[b] - lead_b with */
+/* lead_b = min(o, pos0[b]), and T rows follow the lead (entries: T/m).      */
+/* alpha (optional, [B, T/m, m + o, D]): slot i holds the weight of position  */
+/* p_j - o + i (0 for positions before the sequence start).                   */
+/* ------------------------------------------------------------------------ */
+int lo_compress_overlap(const void* x, const void* z, int in_dtype, int B, int T, int D, int m,
+                        int o, int r, double theta, const int64_t* pos0, int64_t x_bstride,
+                        int64_t z_bstride, double* out, double* alpha) {
+    if (m < 1 || o < 0 || D < 1 || r < 0 || r > D || (r & 1)) return 1;
+    int N = T / m, L = m + o;
+    int64_t rb = row_bytes(in_dtype, D, 0);
+    int64_t bj;
+#pragma omp parallel for schedule(static)
+    for (bj = 0; bj < (int64_t)B * N; ++bj) {
+        int b = (int)(bj / N), j = (int)(bj % N);
+        int64_t p0 = pos0 ? pos0[b] : 0;
+        int64_t lead = o < p0 ? o : p0;
+        int64_t pj = p0 + (int64_t)j * m;
+        double* xs = malloc(sizeof(double) * (size_t)L * D);
+        double* zs = malloc(sizeof(double) * (size_t)L * D);
+        int* have = malloc(sizeof(int) * (size_t)L);
+        int i, c;
+        for (i = 0; i < L; ++i) {
+            int64_t pos = pj - o + i;
+            have[i] = pos >= 0;
+            if (!have[i]) continue;
+            int64_t row = pos - (p0 - lead);
+            decode_row((const uint8_t*)x + (b * x_bstride + row) * rb, in_dtype, D, 0, xs + (int64_t)i * D);
+            decode_row((const uint8_t*)z + (b * z_bstride + row) * rb, in_dtype, D, 0, zs + (int64_t)i * D);
+        }
+        double* ov = out + bj * D;
+        for (c = 0; c < D; ++c) {
+            double mu = -INFINITY, den = 0.0, acc = 0.0;
+            for (i = 0; i < L; ++i)
+                if (have[i]) mu = fmax(mu, zs[(int64_t)i * D + c]);
+            for (i = 0; i < L; ++i)
+                if (have[i]) den += exp(zs[(int64_t)i * D + c] - mu);
+            for (i = 0; i < L; ++i) {
+                double a = have[i] ? exp(zs[(int64_t)i * D + c] - mu) / den : 0.0;
+                if (alpha) alpha[(bj * L + i) * D + c] = a;
+                if (have[i]) acc += a * xs[(int64_t)i * D + c];
+            }
+            ov[c] = acc;
+        }
+        lo_rope(ov, D, r, theta, (double)pj);
+        free(xs);
+        free(zs);
+        free(have);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Lightning indexer ([P3] "对每名query token，用一名轻量之indexer计算它与每  */
 /* 名压缩KV块之相关性分数"; the score s = sum_h w_h * ReLU(q_h . k) is the      */
 /* indexer of DeepSeek-V3.2 that the pages say V4 keeps).  Strict causality   */
