@@ -97,11 +97,13 @@ class PairDecode:
     ki_fmt = "bf16"
     rmsnorm = False     # fused RMSNorm of the new compressed entries and the queries
     gain = None
+    overlap = 0         # CSA compression windows reaching this many tokens back
 
     def __init__(self, lac, synth, dev, sets, seed=4, B=4, ctx=1 << 20):
         self.lac, self.B, self.ctx = lac, B, ctx
         self.sets = [synth.pair_decode(seed=seed + 1000 * s, B=B, ctx=ctx, ki_fmt=self.ki_fmt,
-                                       device=dev) for s in range(sets)]
+                                       csa_overlap=self.overlap, device=dev)
+                     for s in range(sets)]
         c = self.sets[0]
         self.c = c
         # RMSNorm gains (synthetic: 1), used when rmsnorm is set
@@ -126,7 +128,7 @@ class PairDecode:
         # select, attend
         g = self.gain
         lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
-                         rope_dims=c["r"], pos0=ctx - m, norm_gain=g)
+                         rope_dims=c["r"], pos0=ctx - m, norm_gain=g, T=m, overlap=self.overlap)
         lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m, rope_dims=0,
                          pos0=ctx - m)
         lac.indexer_topk(s["qI"], s["w"], s["KI"], m=m, k=c["k"], q_pos0=ctx, topk_idx=self.idx,
@@ -151,8 +153,8 @@ class PairDecode:
         per_seq = (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * 2 + c["HI"] * 4  # indexer
                    + c["k"] * row + c["Nh"] * row + 2 * c["W"] * row               # gathers
                    + 2 * c["H"] * c["D"] * 2 * 2)                                   # q, out
-        compress = ((c["m"] * c["D"] + c["m"] * c["dI"] + c["m_hca"] * c["D"]) * 2 * 2
-                    + 2 * row + c["dI"] * kb)
+        compress = (((c["m"] + self.overlap) * c["D"] + c["m"] * c["dI"] + c["m_hca"] * c["D"])
+                    * 2 * 2 + 2 * row + c["dI"] * kb)
         return self.B * (per_seq + compress)
 
     def indexer_bytes_per_launch(self):
@@ -169,6 +171,7 @@ class PairDecode:
                 "csa_entries": c["N"],
                 "hca_entries": c["Nh"], "kv_format": "e4m3 + bf16 rope dims (576 B/entry)",
                 "rmsnorm": "q and new entries, fused" if self.rmsnorm else "none",
+                "csa_window_overlap": self.overlap,
                 "cache_sets": len(self.sets)}
 
     def cpu_sample(self):
@@ -187,9 +190,15 @@ class PairDecode:
         KI = h["KI"].reshape(1, N, -1).copy()
         hkv = h["hkv"].reshape(1, Nh, -1).copy()
         g = None if self.gain is None else self.gain.cpu().numpy()
-        ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16", "mixed", 1,
-                                              c["m"], c["D"], c["m"], c["r"], 1e4, ctx - c["m"],
-                                              norm_gain=g)
+        if self.overlap:
+            vals = oracle.compress_overlap(h["new_kv_csa"], h["new_z_csa"], oracle.BF16, 1, c["m"],
+                                           c["D"], c["m"], self.overlap, c["r"], 1e4, ctx - c["m"])
+            ckv[:, N - 1:] = oracle.encode_rows(vals.reshape(1, c["D"]), oracle.MIXED,
+                                                c["r"]).reshape(1, 1, -1)
+        else:
+            ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16", "mixed",
+                                                  1, c["m"], c["D"], c["m"], c["r"], 1e4,
+                                                  ctx - c["m"], norm_gain=g)
         KI.view(np.uint8)[:, N - 1:] = chain.compress_store(
             h["new_kI"], h["new_zI"], "bf16", self.ki_fmt, 1, c["m"], c["dI"], c["m"], 0, 1e4,
             ctx - c["m"])
@@ -222,6 +231,13 @@ class PairDecodeRmsNorm(PairDecode):
     epilogue) and of the queries (in the attention prologue)."""
     name = "pair_decode_1m_rmsnorm"
     rmsnorm = True
+
+
+class PairDecodeOverlap(PairDecode):
+    """pair_decode_1m with overlapping CSA compression windows: the new CSA
+    entry pools its block and the 4 tokens before it."""
+    name = "pair_decode_1m_overlap"
+    overlap = 4
 
 
 class CsaDecode(PairDecode):
@@ -597,7 +613,8 @@ class BulkCompress128K(BulkCompress1M):
         return d
 
 
-WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeRmsNorm, CsaDecode,
+WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeRmsNorm,
+                                  PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode,
                                   BulkCompress1M, BulkCompress128K)}
 

@@ -118,6 +118,29 @@ int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, v
                      int64_t out_batch_stride, void* stream);
 
 /*
+ * csa_compress_overlap -- csa_compress with overlapping windows.  The QbitAI
+ * rewrite says that HCA's compression has none of the overlap that CSA's
+ * has (each m' tokens pooled as one group); it gives no extent.  Reading:
+ * entry j, whose block starts at p_j = pos0[b] + j*m, pools the positions
+ * [max(0, p_j - overlap), p_j + m): its own m tokens and the `overlap`
+ * tokens before them, with one softmax per channel over all of them, and
+ * is rotated at p_j.  Its newest token is still p_j + m - 1, so a query at
+ * t sees it iff j < floor(t/m), as without overlap.  overlap = 0 is
+ * csa_compress.
+ *   raw_kv, logits  row 0 of sequence b holds position
+ *            pos0[b] - min(overlap, pos0[b]); T rows (floor(T/m) entries)
+ *            follow those leading rows, so a batch stride must cover
+ *            T + min(overlap, pos0[b]) rows
+ *   overlap  0 .. 256 - m tokens
+ * Other arguments, formats and errors as csa_compress.
+ */
+int32_t csa_compress_overlap(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                             int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                             int32_t overlap, int32_t rope_dims, float rope_theta,
+                             const int64_t* pos0, int64_t kv_batch_stride,
+                             int64_t logit_batch_stride, int64_t out_batch_stride, void* stream);
+
+/*
  * csa_compress_rmsnorm, hca_compress_rmsnorm -- csa_compress / hca_compress
  * with the RMSNorm of each compressed entry fused into the epilogue.  [P2]
  * (section "Attention Sink") and [P3] apply RMSNorm to the compressed KV

@@ -45,6 +45,8 @@ lib.csa_compress.argtypes = _COMPRESS_ARGS
 lib.csa_compress.restype = _i32
 lib.hca_compress.argtypes = _COMPRESS_ARGS
 lib.hca_compress.restype = _i32
+lib.csa_compress_overlap.argtypes = _COMPRESS_ARGS[:9] + [_i32] + _COMPRESS_ARGS[9:]
+lib.csa_compress_overlap.restype = _i32
 _COMPRESS_NORM_ARGS = _COMPRESS_ARGS[:-1] + [_vp, _f32, _vp]
 lib.csa_compress_rmsnorm.argtypes = _COMPRESS_NORM_ARGS
 lib.csa_compress_rmsnorm.restype = _i32
@@ -211,12 +213,31 @@ def _compress(fn, fn_norm, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, 
 
 
 def csa_compress(raw_kv, logits, out, m=4, rope_dims=64, rope_theta=10000.0, pos0=None, T=None,
-                 stream=None, norm_gain=None, norm_eps=1e-6):
+                 stream=None, norm_gain=None, norm_eps=1e-6, overlap=0):
     """Pool every m raw KV rows into one entry (see include/lac.h); with
     norm_gain [D] float32, each entry is RMSNorm'd before its rotation
-    (csa_compress_rmsnorm)."""
-    return _compress(lib.csa_compress, lib.csa_compress_rmsnorm, raw_kv, logits, out, m,
-                     rope_dims, rope_theta, pos0, T, norm_gain, norm_eps, stream)
+    (csa_compress_rmsnorm).  With overlap > 0 each entry also pools the
+    `overlap` tokens before its block (csa_compress_overlap): raw_kv and
+    logits then start min(overlap, pos0[b]) rows before the first block, and
+    T defaults to the rows after the largest such lead."""
+    if overlap == 0:
+        return _compress(lib.csa_compress, lib.csa_compress_rmsnorm, raw_kv, logits, out, m,
+                         rope_dims, rope_theta, pos0, T, norm_gain, norm_eps, stream)
+    if norm_gain is not None:
+        raise ValueError("overlapping windows take no fused RMSNorm")
+    B, rows, D = raw_kv.shape
+    if logits.dtype != raw_kv.dtype:
+        raise TypeError("raw_kv and logits must share a dtype")
+    pos = _positions(pos0, B)
+    if T is None:
+        lead = max((min(overlap, max(0, int(pos[b]) if pos is not None else 0)) for b in range(B)),
+                   default=0)
+        T = rows - lead
+    _call(lib.csa_compress_overlap, (_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _fmt(out),
+                                     B, T, D, m, overlap, rope_dims, rope_theta, pos,
+                                     _rows(raw_kv, "raw_kv"), _rows(logits, "logits"),
+                                     _rows(out, "out"), _stream(stream)))
+    return out
 
 
 def hca_compress(raw_kv, logits, out, m=128, rope_dims=64, rope_theta=10000.0, pos0=None, T=None,

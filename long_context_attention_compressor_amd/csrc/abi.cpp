@@ -66,7 +66,8 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
                       void* out, int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
                       int32_t rope_dims, float rope_theta, const int64_t* pos0,
                       int64_t kv_bstride, int64_t z_bstride, int64_t out_bstride, void* stream,
-                      const float* norm_gain = nullptr, float norm_eps = 0.f, bool norm = false) {
+                      const float* norm_gain = nullptr, float norm_eps = 0.f, bool norm = false,
+                      int32_t overlap = 0) {
   if (in_dtype != LAC_F32 && in_dtype != LAC_BF16)
     return fail(LAC_ERR_UNSUPPORTED, "%s: in_dtype must be LAC_F32 or LAC_BF16", fn);
   if (out_dtype < LAC_F32 || out_dtype > LAC_KV_E4M3_ROPE_BF16)
@@ -79,9 +80,18 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
     return fail(LAC_ERR_INVALID, "%s: rope_dims = %d must be a multiple of 8 in [0, min(D, 128)]", fn, rope_dims);
   if (rope_dims > 0 && !(rope_theta > 0.f && isfinite(rope_theta)))
     return fail(LAC_ERR_INVALID, "%s: rope_theta must be positive and finite", fn);
+  if (overlap < 0 || overlap > 256 - m)
+    return fail(LAC_ERR_INVALID, "%s: overlap = %d outside [0, 256 - m]", fn, overlap);
   const int N = T / m;
-  if (B > 1 && (kv_bstride < T || z_bstride < T || out_bstride < N))
-    return fail(LAC_ERR_INVALID, "%s: batch strides must cover T rows (in) and T/m rows (out)", fn);
+  int64_t lead_max = 0;        // rows before the first block (overlapping windows)
+  for (int b = 0; b < B && overlap > 0; ++b) {
+    const int64_t p = pos0 ? pos0[b] : 0;
+    const int64_t lead = p < overlap ? (p > 0 ? p : 0) : overlap;
+    if (lead > lead_max) lead_max = lead;
+  }
+  if (B > 1 && (kv_bstride < T + lead_max || z_bstride < T + lead_max || out_bstride < N))
+    return fail(LAC_ERR_INVALID, "%s: batch strides must cover T rows (in; plus the overlap's "
+                "leading rows) and T/m rows (out)", fn);
   if (norm) {
     const int G = D / 8;
     if (G > 64 || (G & (G - 1)))
@@ -102,7 +112,7 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
     return fail(LAC_ERR_INVALID, "%s: mixed-format batch stride must keep rows 8-byte aligned", fn);
   a.kv = raw_kv; a.logits = logits; a.out = out;
   a.in_fmt = in_dtype; a.out_fmt = out_dtype;
-  a.B = B; a.T = T; a.D = D; a.m = m; a.r = rope_dims; a.theta = rope_theta;
+  a.B = B; a.T = T; a.D = D; a.m = m; a.r = rope_dims; a.theta = rope_theta; a.overlap = overlap;
   a.kv_bstride = kv_bstride; a.z_bstride = z_bstride; a.out_bstride = out_bstride;
   return launch_status(fn, lac::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
@@ -295,6 +305,20 @@ int32_t hca_compress(const void* raw_kv, const void* logits, int32_t in_dtype, v
                          out_batch_stride, stream);
   } catch (...) {
     return fail(LAC_ERR_DEVICE, "hca_compress: internal error");
+  }
+}
+
+int32_t csa_compress_overlap(const void* raw_kv, const void* logits, int32_t in_dtype, void* out,
+                             int32_t out_dtype, int32_t B, int32_t T, int32_t D, int32_t m,
+                             int32_t overlap, int32_t rope_dims, float rope_theta,
+                             const int64_t* pos0, int64_t kv_batch_stride,
+                             int64_t logit_batch_stride, int64_t out_batch_stride, void* stream) {
+  try {
+    return compress_impl("csa_compress_overlap", raw_kv, logits, in_dtype, out, out_dtype, B, T, D,
+                         m, rope_dims, rope_theta, pos0, kv_batch_stride, logit_batch_stride,
+                         out_batch_stride, stream, nullptr, 0.f, false, overlap);
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "csa_compress_overlap: internal error");
   }
 }
 

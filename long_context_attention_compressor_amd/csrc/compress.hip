@@ -99,7 +99,7 @@ __device__ __forceinline__ void softmax_step(const float* xv, const float* zv, f
 // Block (GB, S, epb): thread (x, y, z) owns channel group slice * GB + x of
 // entry blockIdx.x * epb + z and token share y of its block; the grid is
 // (entry groups, channel slices, sequences), so no index needs a division.
-template <int IN, int OUT>
+template <int IN, int OUT, int TOKN>
 __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
   extern __shared__ float part[];                  // [blockDim][25] when S > 1
   __shared__ double freq[kMaxRopePairs];
@@ -123,19 +123,27 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
   }
 
   if (live) {
+    // The entry's window: with an overlap o, positions [max(0, p_j - o),
+    // p_j + m) of the rows that start min(o, pos0) before the first block;
+    // this thread takes tokens s * per .. of it.
     const int per = a.per;
-    const int64_t row0 = (int64_t)j * a.m + (int64_t)s * per;
+    const int64_t pj = (int64_t)a.pos0.v[b] + (int64_t)j * a.m;
+    const int64_t lead = min((int64_t)a.overlap, (int64_t)a.pos0.v[b]);
+    const int64_t back = min((int64_t)a.overlap, pj);
+    const int cnt = a.m + (int)back;                       // window tokens
+    const int mine = max(0, min(per, cnt - s * per));      // this thread's tokens
+    const int64_t row0 = lead + (int64_t)j * a.m - back + (int64_t)s * per;
     const int64_t xb = (b * a.kv_bstride + row0) * a.D + g * 8;
     const int64_t zb = (b * a.z_bstride + row0) * a.D + g * 8;
     // TOK tokens' loads in flight before any of them is used, kept packed
     // until used (rows past the thread's share re-read its last row and are
-    // not used).
-    constexpr int TOK = IN == kF32 ? 4 : 8;
-    for (int i = 0; i < per; i += TOK) {
+    // not used); TOKN = 4 when a thread's share is at most 4 tokens.
+    constexpr int TOK = IN == kF32 ? (TOKN < 4 ? TOKN : 4) : TOKN;
+    for (int i = 0; i < mine; i += TOK) {
       Raw8<IN> xr[TOK], zr[TOK];
 #pragma unroll
       for (int u = 0; u < TOK; ++u) {
-        const int64_t row = min(i + u, per - 1);
+        const int64_t row = min(i + u, mine - 1);
         xr[u] = load_raw8<IN>(a.kv, xb + row * a.D);
         zr[u] = load_raw8<IN>(a.logits, zb + row * a.D);
       }
@@ -144,7 +152,7 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
       }
 #pragma unroll
       for (int u = 0; u < TOK; ++u) {
-        if (i + u < per) {
+        if (i + u < mine) {
           float xv[8], zv[8];
           unpack8<IN>(xr[u], xv);
           unpack8<IN>(zr[u], zv);
@@ -152,6 +160,7 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
         }
       }
     }
+    if (mine == 0) rope_freq_table(freq, a.rope, a.r, t, nthreads);
   } else {
     rope_freq_table(freq, a.rope, a.r, t, nthreads);
   }
@@ -249,14 +258,20 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
   }
 }
 
-template <int IN, int OUT>
-hipError_t launch(const CompressArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+template <int IN, int OUT, int TOKN>
+hipError_t launch_tok(const CompressArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&compress_kernel<IN, OUT>),
+      reinterpret_cast<const void*>(&compress_kernel<IN, OUT, TOKN>),
       hipFuncAttributeMaxDynamicSharedMemorySize, 512 * 25 * (int)sizeof(float));
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((compress_kernel<IN, OUT>), grid, block, lds, st, a);
+  hipLaunchKernelGGL((compress_kernel<IN, OUT, TOKN>), grid, block, lds, st, a);
   return hipGetLastError();
+}
+
+template <int IN, int OUT>
+hipError_t launch(const CompressArgs& a, dim3 grid, dim3 block, size_t lds, hipStream_t st) {
+  return a.per <= 4 ? launch_tok<IN, OUT, 4>(a, grid, block, lds, st)
+                    : launch_tok<IN, OUT, 8>(a, grid, block, lds, st);
 }
 
 }  // namespace
@@ -271,14 +286,15 @@ hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   // power of two, at most 64 with the norm), and the token split shrinks to
   // fit: a long block (m' = 128) is then streamed by one compute unit.
   int S = 1;
-  while (a.m / S > 8 && S < 256 && a.m % (2 * S) == 0) S *= 2;
+  const int L = a.m + a.overlap;                 // tokens per window
+  while ((L + S - 1) / S > 8 && S < 256 && (a.overlap > 0 || a.m % (2 * S) == 0)) S *= 2;
   int GB = G;
   if (a.norm_gain == nullptr)
     while (GB * S > 256 && GB % 2 == 0) GB /= 2;
   if (GB * S > 512) {           // few channel groups and a long block: fewer splits
     while (GB * S > 512) S /= 2;
   }
-  a.per = a.m / S;
+  a.per = (L + S - 1) / S;
   a.gb = GB;
   a.s = S;
   const int threads = GB * S <= 256 ? (GB == G ? 256 : GB * S) : GB * S;

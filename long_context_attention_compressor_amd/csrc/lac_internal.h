@@ -38,6 +38,7 @@ struct CompressArgs {
   void* out;
   int in_fmt, out_fmt;
   int B, T, D, m, r;
+  int overlap;            // CSA window overlap o (tokens before the block), 0 = none
   float theta;
   int64_t kv_bstride, z_bstride, out_bstride;  // rows
   const float* norm_gain;   // [D] or null: RMSNorm of each entry before its rotation

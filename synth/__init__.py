@@ -160,12 +160,14 @@ def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, d
 
 
 def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI=128, H=64,
-                k=2048, W=128, ki_fmt="bf16", device="cpu"):
+                k=2048, W=128, ki_fmt="bf16", csa_overlap=0, device="cpu"):
     """Decode of a CSA + HCA layer pair at position ctx with the KV stored as
     FP8 E4M3 plus bf16 rotated dims.  The step also compresses the newest
     complete block of each layer (CSA entry, indexer key, HCA entry) from
     bf16 activations, so every stage of the path runs in one step.  The
-    indexer keys are bf16, or E4M3 with ki_fmt = "mixed" (no rotated dims)."""
+    indexer keys are bf16, or E4M3 with ki_fmt = "mixed" (no rotated dims).
+    With csa_overlap > 0 the newest CSA block comes with the csa_overlap raw
+    rows before it (overlapping compression windows)."""
     N = ctx // m
     Nh = ctx // m_hca
     return dict(
@@ -176,8 +178,9 @@ def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI
         hkv=store(normal(seed, "hkv", (B, Nh, D), device=device), "mixed", r),
         raw_csa=store(normal(seed, "raw_csa", (B, W, D), device=device), "mixed", r),
         raw_hca=store(normal(seed, "raw_hca", (B, W, D), device=device), "mixed", r),
-        new_kv_csa=store(normal(seed, "new_kv_csa", (B, m, D), device=device), "bf16"),
-        new_z_csa=store(normal(seed, "new_z_csa", (B, m, D), device=device), "bf16"),
+        csa_overlap=csa_overlap,
+        new_kv_csa=store(normal(seed, "new_kv_csa", (B, m + csa_overlap, D), device=device), "bf16"),
+        new_z_csa=store(normal(seed, "new_z_csa", (B, m + csa_overlap, D), device=device), "bf16"),
         new_kI=store(normal(seed, "new_kI", (B, m, dI), device=device), "bf16"),
         new_zI=store(normal(seed, "new_zI", (B, m, dI), device=device), "bf16"),
         new_kv_hca=store(normal(seed, "new_kv_hca", (B, m_hca, D), device=device), "bf16"),
