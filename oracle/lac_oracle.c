@@ -357,12 +357,13 @@ static int64_t n_visible(int64_t t, int N, int m) {
 
 /* rows: n_rows pairs (b, i).  scores: [n_rows, N]; entries not visible are
  * set to -inf.  nvis (optional): [n_rows].  q is stored in dtype, K in
- * k_dtype (the same formats; LO_MIXED with no rotated dims is E4M3 keys). */
+ * k_dtype (the same formats; LO_MIXED with no rotated dims is E4M3 codes,
+ * for queries as well as keys). */
 int lo_index_scores2(const void* q, int dtype, const float* w, const void* K, int k_dtype,
                      int B, int Tq, int HI, int dI, int N, const int64_t* qpos0, int m,
                      const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {
     (void)B;
-    if (dtype != LO_F32 && dtype != LO_BF16 && dtype != LO_F64) return 2;
+    if (dtype != LO_F32 && dtype != LO_BF16 && dtype != LO_F64 && dtype != LO_MIXED) return 2;
     if (k_dtype != LO_F32 && k_dtype != LO_BF16 && k_dtype != LO_F64 && k_dtype != LO_MIXED)
         return 2;
     if (dI < 1 || dI > 1024) return 3;

@@ -64,6 +64,35 @@ def test_scores_with_e4m3_keys_use_the_decoded_key_values():
             assert np.isneginf(s[rr, nv[rr]:]).all()
 
 
+def test_scores_with_e4m3_queries_and_keys_use_the_decoded_values():
+    # Queries and keys both stored as E4M3 codes (the low-precision indexer
+    # QK path, 深度解析 DeepSeek-V4, CSA Step 2 Select and section "FP4
+    # Quantization-Aware Training"): the codes come from PyTorch's float8
+    # conversion and are decoded by PyTorch, so the oracle's own E4M3 decoder
+    # is pinned against a library one here.
+    import torch
+    B, Tq, HI, dI, N, m = 2, 4, 8, 64, 30, 4
+    qpos0 = (60, 131)
+    rng = np.random.default_rng(11)
+    qv = torch.from_numpy(rng.standard_normal((B, Tq, HI, dI)) * 3.0).to(torch.float8_e4m3fn)
+    kv = torch.from_numpy(rng.standard_normal((B, N, dI)) * 0.5).to(torch.float8_e4m3fn)
+    w = rng.uniform(-0.2, 1, (B, Tq, HI)).astype(np.float32)
+    q8 = qv.view(torch.uint8).numpy().copy()
+    k8 = kv.view(torch.uint8).numpy().copy()
+    s, nv = oracle.index_scores(q8, w, k8, oracle.MIXED, B, Tq, HI, dI, N, np.array(qpos0), m,
+                                k_dtype=oracle.MIXED)
+    qd = qv.to(torch.float64).numpy()
+    kd = kv.to(torch.float64).numpy()
+    dots = np.einsum("bthc,bjc->btjh", qd, kd)
+    ref = (np.maximum(dots, 0.0) * w.astype(np.float64)[:, :, None, :]).sum(-1)
+    for b in range(B):
+        for i in range(Tq):
+            rr = b * Tq + i
+            assert nv[rr] == min(N, (qpos0[b] + i) // m)
+            assert np.allclose(s[rr, : nv[rr]], ref[b, i, : nv[rr]], rtol=1e-13, atol=1e-12)
+            assert np.isneginf(s[rr, nv[rr]:]).all()
+
+
 def test_worked_example_from_the_pages():
     g = json.load(open(os.path.join(GOLD, "worked_example_select.json")))
     s = np.array([g["scores"]], np.float64)
