@@ -11,7 +11,8 @@ independent cache sets rotate so that a step never finds its 294 MB working
 set in the 256 MB Infinity Cache.
 
 Other workloads (--workload): pair_decode_1m_e4m3_indexer (the same step with
-the indexer keys stored as E4M3, one byte per dim), csa_decode_128k (32
+the indexer keys stored as E4M3, one byte per dim), pair_decode_1m_fp8_indexer
+(E4M3 indexer queries and keys on the FP8 matrix cores), csa_decode_128k (32
 sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
 hca_prefill_8k (8192 tokens; TFLOP/s), bulk_compress_1m and
@@ -95,6 +96,7 @@ class PairDecode:
     unit = "tokens/s"
 
     ki_fmt = "bf16"
+    qi_fmt = "bf16"
     rmsnorm = False     # fused RMSNorm of the new compressed entries and the queries
     gain = None
     overlap = 0         # CSA compression windows reaching this many tokens back
@@ -102,7 +104,7 @@ class PairDecode:
     def __init__(self, lac, synth, dev, sets, seed=4, B=4, ctx=1 << 20):
         self.lac, self.B, self.ctx = lac, B, ctx
         self.sets = [synth.pair_decode(seed=seed + 1000 * s, B=B, ctx=ctx, ki_fmt=self.ki_fmt,
-                                       csa_overlap=self.overlap, device=dev)
+                                       qi_fmt=self.qi_fmt, csa_overlap=self.overlap, device=dev)
                      for s in range(sets)]
         c = self.sets[0]
         self.c = c
@@ -150,7 +152,8 @@ class PairDecode:
         c = self.c
         row = c["D"] - c["r"] + 2 * c["r"]
         kb = 1 if self.ki_fmt == "mixed" else 2                                   # key bytes/dim
-        per_seq = (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * 2 + c["HI"] * 4  # indexer
+        qb = 1 if self.qi_fmt == "mixed" else 2                                   # query bytes/dim
+        per_seq = (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * qb + c["HI"] * 4  # indexer
                    + c["k"] * row + c["Nh"] * row + 2 * c["W"] * row               # gathers
                    + 2 * c["H"] * c["D"] * 2 * 2)                                   # q, out
         compress = (((c["m"] + self.overlap) * c["D"] + c["m"] * c["dI"] + c["m_hca"] * c["D"])
@@ -160,14 +163,16 @@ class PairDecode:
     def indexer_bytes_per_launch(self):
         c = self.c
         kb = 1 if self.ki_fmt == "mixed" else 2
-        return self.B * (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * 2 + c["HI"] * 4)
+        qb = 1 if self.qi_fmt == "mixed" else 2
+        return self.B * (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * qb + c["HI"] * 4)
 
     def config(self):
         c = self.c
         return {"workload": self.name, "batch": self.B, "ctx": self.ctx, "topk": c["k"],
                 "window": c["W"], "heads": c["H"], "kv_dim": c["D"], "rope_dims": c["r"],
                 "indexer": (f"{c['HI']}x{c['dI']} bf16" if self.ki_fmt == "bf16" else
-                            f"{c['HI']}x{c['dI']}, bf16 queries, e4m3 keys"),
+                            f"{c['HI']}x{c['dI']}, bf16 queries, e4m3 keys" if self.qi_fmt == "bf16"
+                            else f"{c['HI']}x{c['dI']}, e4m3 queries and keys (fp8 mfma)"),
                 "csa_entries": c["N"],
                 "hca_entries": c["Nh"], "kv_format": "e4m3 + bf16 rope dims (576 B/entry)",
                 "rmsnorm": "q and new entries, fused" if self.rmsnorm else "none",
@@ -205,8 +210,8 @@ class PairDecode:
         hkv[:, Nh - 1:] = chain.compress_store(h["new_kv_hca"], h["new_z_hca"], "bf16", "mixed",
                                                1, c["m_hca"], c["D"], c["m_hca"], c["r"], 1e4,
                                                ctx - c["m_hca"], norm_gain=g)
-        idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, "bf16", 1, 1, c["HI"], c["dI"], N, ctx,
-                                     c["m"], c["k"], k_fmt=self.ki_fmt)
+        idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, self.qi_fmt, 1, 1, c["HI"], c["dI"], N,
+                                     ctx, c["m"], c["k"], k_fmt=self.ki_fmt)
         oracle.attend(h["q_csa"], oracle.BF16, ckv, oracle.MIXED, N, 0, idx, c["k"], c["m"],
                       h["raw_csa"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
                       c["r"], 1e4, ctx, q_norm_gain=g)
@@ -224,6 +229,14 @@ class PairDecodeE4M3Indexer(PairDecode):
     """pair_decode_1m with the indexer keys stored as E4M3 (d_I bytes per key)."""
     name = "pair_decode_1m_e4m3_indexer"
     ki_fmt = "mixed"
+
+
+class PairDecodeFp8Indexer(PairDecode):
+    """pair_decode_1m with E4M3 indexer queries and keys, scored on the FP8
+    matrix cores."""
+    name = "pair_decode_1m_fp8_indexer"
+    ki_fmt = "mixed"
+    qi_fmt = "mixed"
 
 
 class PairDecodeRmsNorm(PairDecode):
@@ -613,8 +626,8 @@ class BulkCompress128K(BulkCompress1M):
         return d
 
 
-WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeRmsNorm,
-                                  PairDecodeOverlap, CsaDecode,
+WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeFp8Indexer,
+                                  PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode,
                                   BulkCompress1M, BulkCompress128K)}
 

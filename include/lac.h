@@ -35,6 +35,8 @@
  *             followed by r bfloat16 values for the rotated dims; a row is
  *             (D - r) + 2r bytes (576 B at D = 512, r = 64).  Stores round to
  *             nearest even and saturate to +-448, unscaled.
+ *   LAC_E4M3  FP8 E4M3 codes ("fn" variant as above), one byte per value,
+ *             unscaled (indexer queries and keys only).
  *   The mixed format follows the KV-cache storage of "DeepSeek V4 技术架构深度
  *   解析" (aicoding.csdn.net), section "KV Cache优化细节", and its bit-layout
  *   table in section "三、FP4量化".
@@ -74,7 +76,8 @@ typedef enum {
 typedef enum {
     LAC_F32 = 0,
     LAC_BF16 = 1,
-    LAC_KV_E4M3_ROPE_BF16 = 2
+    LAC_KV_E4M3_ROPE_BF16 = 2,
+    LAC_E4M3 = 3
 } lac_dtype;
 
 /* Largest batch the position arrays may describe. */
@@ -177,8 +180,8 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  * ascending); the chosen indices are written in ascending index order and
  * the remaining slots hold -1.
  *
- *   q_idx       [B, Tq, H_I, d_I] in dtype (LAC_F32 | LAC_BF16), or bf16 when
- *               dtype is LAC_KV_E4M3_ROPE_BF16
+ *   q_idx       [B, Tq, H_I, d_I] in dtype (LAC_F32 | LAC_BF16 | LAC_E4M3),
+ *               or bf16 when dtype is LAC_KV_E4M3_ROPE_BF16
  *   w           [B, Tq, H_I] float32
  *   k_idx       [B, N, d_I] in dtype; with LAC_KV_E4M3_ROPE_BF16, E4M3 keys of
  *               d_I bytes (the mixed row format with no rotated dims, as
@@ -187,13 +190,17 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  *               (CSA Step 2 Select; section "FP4 Quantization-Aware
  *               Training", whose FP4 block scales dequantize losslessly into
  *               FP8).  Here the keys are stored as unscaled E4M3, widened
- *               exactly to bf16, and scored as above.
+ *               exactly to bf16, and scored as above.  With LAC_E4M3 both
+ *               q_idx and k_idx are E4M3 codes of d_I bytes per row and the
+ *               products run on the FP8 matrix cores (each product exact,
+ *               sums in fp32).
  *   topk_idx    [B, Tq, k] int32, output
  *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
  *               -inf in padded slots); may be NULL
  *   workspace   >= indexer_topk_workspace_size(B, Tq, N, k) bytes
- * LAC_BF16 and LAC_KV_E4M3_ROPE_BF16 need H_I in {32, 64, 128} and d_I in
- * {64, 128} (bf16 MFMA); LAC_F32 needs H_I * d_I <= 8192.  1 <= k <= 8192.
+ * LAC_BF16, LAC_KV_E4M3_ROPE_BF16 and LAC_E4M3 need H_I in {32, 64, 128} and
+ * d_I in {64, 128} (MFMA tiles); LAC_F32 needs H_I * d_I <= 8192.
+ * 1 <= k <= 8192.
  */
 size_t indexer_topk_workspace_size(int32_t B, int32_t Tq, int32_t N, int32_t k);
 int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32_t dtype,

@@ -23,10 +23,10 @@ __all__ = [
     "indexer_topk_noalloc",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
-    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "KERNELS", "CallList",
+    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "KERNELS", "CallList",
 ]
 
-LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 = 0, 1, 2
+LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3 = 0, 1, 2, 3
 KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4,
            "project": 5}
 STATUS = {0: "LAC_OK", 1: "LAC_ERR_INVALID", 2: "LAC_ERR_UNSUPPORTED", 3: "LAC_ERR_WORKSPACE",
@@ -253,14 +253,24 @@ def indexer_topk_workspace_size(B, Tq, N, k) -> int:
     return int(lib.indexer_topk_workspace_size(B, Tq, N, k))
 
 
+def _indexer_dtype(q_idx, k_idx):
+    if q_idx.dtype == torch.uint8:
+        if k_idx.dtype != torch.uint8:
+            raise TypeError("E4M3 (uint8) q_idx needs E4M3 (uint8) k_idx")
+        return LAC_E4M3
+    if k_idx.dtype == torch.uint8:
+        return LAC_KV_E4M3_ROPE_BF16
+    return _fmt(q_idx)
+
+
 def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
                  workspace=None, stream=None):
     """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I]
-    (the dtype of q_idx, or uint8 E4M3 codes with bf16 q_idx).
+    (the dtype of q_idx, or uint8 E4M3 codes with bf16 or uint8 E4M3 q_idx).
     Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""
     B, Tq, HI, dI = q_idx.shape
     N = k_idx.shape[1]
-    dt = LAC_KV_E4M3_ROPE_BF16 if k_idx.dtype == torch.uint8 else _fmt(q_idx)
+    dt = _indexer_dtype(q_idx, k_idx)
     for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
         _need_dense(t, nm)
     if topk_idx is None:
@@ -279,7 +289,7 @@ def indexer_topk_noalloc(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk
     the caller cannot allocate."""
     B, Tq, HI, dI = q_idx.shape
     N = k_idx.shape[1]
-    dt = LAC_KV_E4M3_ROPE_BF16 if k_idx.dtype == torch.uint8 else _fmt(q_idx)
+    dt = _indexer_dtype(q_idx, k_idx)
     for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
         _need_dense(t, nm)
     if topk_idx is None:

@@ -125,9 +125,9 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
                      const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                      float* topk_score, void* workspace, size_t workspace_bytes, bool fixed,
                      void* stream) {
-  if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16)
-    return fail(LAC_ERR_UNSUPPORTED, "%s: dtype must be LAC_F32, LAC_BF16 or LAC_KV_E4M3_ROPE_BF16",
-                fn);
+  if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16 && dtype != LAC_E4M3)
+    return fail(LAC_ERR_UNSUPPORTED,
+                "%s: dtype must be LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 or LAC_E4M3", fn);
   if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
   if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
   if (m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);
@@ -135,7 +135,7 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
   if (H_I < 1 || d_I < 1) return fail(LAC_ERR_INVALID, "%s: H_I and d_I must be >= 1", fn);
   if (dtype != LAC_F32) {
     if ((H_I != 32 && H_I != 64 && H_I != 128) || (d_I != 64 && d_I != 128))
-      return fail(LAC_ERR_UNSUPPORTED, "%s: bf16 path needs H_I in {32, 64, 128} and d_I in {64, 128}", fn);
+      return fail(LAC_ERR_UNSUPPORTED, "%s: MFMA path needs H_I in {32, 64, 128} and d_I in {64, 128}", fn);
   } else if ((int64_t)H_I * d_I > 8192) {
     return fail(LAC_ERR_UNSUPPORTED, "%s: float32 path needs H_I * d_I <= 8192", fn);
   }

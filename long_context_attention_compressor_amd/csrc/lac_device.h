@@ -27,7 +27,7 @@ __device__ __forceinline__ uint2 ld_stream8(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
-enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2 };
+enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2, kE4M3 = 3 };
 
 // Per-batch positions passed by value (the library keeps nothing on the device).
 struct Positions {

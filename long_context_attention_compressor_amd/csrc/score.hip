@@ -25,6 +25,34 @@ namespace lac {
 namespace {
 
 constexpr int kHistBins = kScoreHistBins;
+// Decode score launches: tile stages in flight per wave (bf16 keys, E4M3
+// keys) and the blocks the grid spreads over (bf16, E4M3 queries).
+constexpr int kStagesBF16 = 2, kStagesF8 = 2;
+constexpr int kDecodeBlocksBF16 = 512, kDecodeBlocksF8 = 512;
+
+// E4M3 key tiles in LDS (E4M3 queries): a row is d_I bytes, its 8-byte
+// chunks XOR-swizzled by f8_swz(row), chosen so that the MFMA-layout reads
+// (chunk c of 32 consecutive rows, 16 lanes per LDS cycle) hit distinct
+// banks: with d_I = 64 two rows share a 128-byte line, so the swizzle
+// follows the line index.
+template <int dI>
+__device__ __forceinline__ int f8_swz(int row) {
+  static_assert(dI == 64 || dI == 128, "E4M3 score tiles take d_I of 64 or 128");
+  return (row / (128 / dI)) % (dI / 8);
+}
+// The 16 bytes at LDS offset o of a swizzled E4M3 tile: physical chunks 2p,
+// 2p + 1 of row kk hold its chunks 2p ^ x and 2p ^ x ^ 1 (x = f8_swz(kk)),
+// i.e. its 16-byte chunk p ^ (x / 2), with the halves swapped when x is odd.
+// Returns the byte offset of that chunk in the HBM tile and the swap flag.
+template <int dI>
+__device__ __forceinline__ int f8_src(int o, bool& swap) {
+  const int kk = o / dI, p = (o % dI) / 16, x = f8_swz<dI>(kk);
+  swap = x & 1;
+  return kk * dI + ((p ^ (x >> 1)) * 16);
+}
+__device__ __forceinline__ uint4 swap_halves(const uint4& v, bool swap) {
+  return swap ? make_uint4(v.z, v.w, v.x, v.y) : v;
+}
 
 struct ScoreArgs {
   const void* q;
@@ -84,15 +112,19 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   constexpr int CH = dI / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = dI * 2;               // bytes per key row
   constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
-  // Keys in HBM: bf16 rows (2 d_I bytes) or E4M3 rows (d_I bytes), widened
-  // to the same bf16 layout in LDS.
-  constexpr int KROWB = KF == kMixed ? dI : ROWB;
+  // Keys in HBM: bf16 rows (2 d_I bytes) or E4M3 rows (d_I bytes).  With
+  // bf16 queries (kMixed) E4M3 keys are widened to the bf16 layout in LDS;
+  // with E4M3 queries (kE4M3) they stay E4M3 in LDS (f8_swz) and feed the
+  // FP8 MFMA.
+  constexpr bool F8 = KF == kE4M3;
+  constexpr int KROWB = KF == kMixed || F8 ? dI : ROWB;
+  constexpr int CH8 = dI / 8;                // 8-byte chunks per E4M3 key row
   constexpr int KTILEB = 32 * KROWB;
   constexpr int NLD = KTILEB / 1024;         // 16-byte registers per lane per tile
   constexpr int kLPR = dI / 8;               // E4M3: lanes per key (8 codes each)
   constexpr int kRPI = 64 / kLPR;            // E4M3: keys per 8-byte load
   __shared__ float sw[kRowsPerBlock][HI];
-  __shared__ __align__(16) uint8_t ktile[4][TILEB];
+  __shared__ __align__(16) uint8_t ktile[4][F8 ? KTILEB : TILEB];
   __shared__ uint32_t lhist[kHistBins];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
@@ -157,6 +189,11 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
           const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (kRPI * j + l / kLPR) * dI + (l % kLPR) * 8, 0, 2);
           if (h == 0) { st[u].x = v[0]; st[u].y = v[1]; } else { st[u].z = v[0]; st[u].w = v[1]; }
         }
+      } else if constexpr (F8) {
+        bool sw8;
+        const int src = f8_src<dI>(u * 1024 + l * 16, sw8);
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, src, 0, 2);
+        st[u] = swap_halves(make_uint4(v.x, v.y, v.z, v.w), sw8);
       } else {
         const int o = u * 1024 + l * 16;
         const int kk = o / ROWB, cs = (o % ROWB) / 16;
@@ -188,12 +225,13 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   // else, so their latency overlaps the set-up below.  PF tiles are in
   // flight per wave (two for the one-query decode shape, whose registers
   // allow it); the stages alternate.
-  constexpr int PF = QPW == 1 ? 2 : 1;
+  constexpr int PF = QPW == 1 ? (F8 ? kStagesF8 : kStagesBF16) : 1;
   uint4 stage[PF][NLD];
   // Query fragments first: lane (ln, hf) holds head ht*32+ln, dims
   // hf*dI/2 + s*8 .. +8.  (They come from L2 for all but the first waves of
   // a row, so the first tile's compute need not wait for the second tile.)
-  bf16x8 qf[QPW][HT][KS];
+  typedef typename std::conditional<F8, long, bf16x8>::type QFrag;
+  QFrag qf[QPW][HT][KS];
   int64_t nv_row[QPW];
   {
 #pragma unroll
@@ -203,10 +241,16 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
       nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
-        const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                           ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
+        const int64_t qrow = (((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln;
+        if constexpr (F8) {
+          const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * dI + hf * (dI / 2);
 #pragma unroll
-        for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+          for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const long*>(qp + s * 8);
+        } else {
+          const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow * dI + hf * (dI / 2);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+        }
       }
     }
   }
@@ -226,11 +270,16 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
 
   // Work on one tile held in LDS: scores of the wave's query rows.
   auto compute = [&](int64_t tile) {
-    bf16x8 kf[KS];
+    QFrag kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int c = hf * (CH / 2) + s;
-      kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+      if constexpr (F8) {
+        const int c = hf * (CH8 / 2) + s;
+        kf[s] = *reinterpret_cast<const long*>(kt + ln * dI + ((c ^ f8_swz<dI>(ln)) * 8));
+      } else {
+        const int c = hf * (CH / 2) + s;
+        kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+      }
     }
     const int64_t j = tile * 32 + ln;
 #pragma unroll
@@ -241,8 +290,12 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+          if constexpr (F8)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+          else
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        }
         // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
 #pragma unroll
         for (int v = 0; v < 16; ++v)
@@ -343,12 +396,15 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   constexpr int CH = dI / 8;                 // 16-byte chunks per key row
   constexpr int ROWB = dI * 2;               // bytes per key row
   constexpr int TILEB = 32 * ROWB;           // bytes per 32-key tile
-  // Keys in HBM: bf16 rows or E4M3 rows (widened to bf16 in LDS).
-  constexpr int KROWB = KF == kMixed ? dI : ROWB;
+  // Keys in HBM: bf16 rows or E4M3 rows (widened to bf16 in LDS for bf16
+  // queries, kept E4M3 in LDS for E4M3 queries).
+  constexpr bool F8 = KF == kE4M3;
+  constexpr int KROWB = KF == kMixed || F8 ? dI : ROWB;
+  constexpr int CH8 = dI / 8;
   constexpr int LBYTES = KF == kMixed ? 8 : 16;    // bytes each loader reads
   constexpr int LOADERS = 32 * KROWB / LBYTES;
   __shared__ float sw[QB][HI];
-  __shared__ __align__(16) uint8_t ktile[2][TILEB];
+  __shared__ __align__(16) uint8_t ktile[2][F8 ? 32 * dI : TILEB];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int hf = l >> 5, ln = l & 31;
@@ -374,18 +430,23 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   const uint8_t* Kb = static_cast<const uint8_t*>(a.K) + (int64_t)b * a.N * KROWB;
   // bf16: loader thread t takes 16 bytes at t*16 of the tile in LDS order:
   // row kk, swizzled slot cs, which holds the row's chunk cs ^ (kk % CH).
-  // E4M3: loader t takes the 8 codes of chunk cs of key kk (t*8 of the tile
-  // in HBM order) and writes them widened into that chunk's slot, so the
-  // loaders of one key fill its whole LDS row.
+  // E4M3 widened: loader t takes the 8 codes of chunk cs of key kk (t*8 of
+  // the tile in HBM order) and writes them widened into that chunk's slot, so
+  // the loaders of one key fill its whole LDS row.  E4M3 kept: loader t fills
+  // the 16 bytes at t*16 of the swizzled tile (f8_src).
   const bool loader = (int)threadIdx.x < LOADERS;
   const int lo_off = threadIdx.x * LBYTES;
   const int lo_kk = lo_off / KROWB, lo_cs = (lo_off % KROWB) / LBYTES;
+  bool lo_swap = false;
+  const int lo_src8 = F8 ? f8_src<dI>(lo_off, lo_swap) % dI : 0;   // byte in its row
   auto load_tile = [&](int64_t tile) {
     int64_t j = tile * 32 + lo_kk;
     if (j > a.N - 1) j = a.N - 1;
     if constexpr (KF == kMixed) {
       const uint2 v = ld_stream8(Kb + j * KROWB + lo_cs * 8);
       return make_uint4(v.x, v.y, 0u, 0u);
+    } else if constexpr (F8) {
+      return swap_halves(ld_stream16(Kb + j * dI + lo_src8), lo_swap);
     } else {
       return ld_stream16(Kb + j * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16));
     }
@@ -408,7 +469,8 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   // lane (hidden key, second half-wave, row past Tq) stores out of range and
   // the store is dropped, so every store instruction is issued unconditionally
   // and the memory counter stays exact for the prefetch waits.
-  bf16x8 qf[QPW][HT][KS];
+  typedef typename std::conditional<F8, long, bf16x8>::type QFrag;
+  QFrag qf[QPW][HT][KS];
   int64_t nv_row[QPW];
   __amdgpu_buffer_rsrc_t srow[QPW];
 #pragma unroll
@@ -420,10 +482,16 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
                                                  (int)(nv_row[qi] * 4), 0x00020000);
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
-      const __bf16* qp = static_cast<const __bf16*>(a.q) +
-                         ((((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln) * dI + hf * (dI / 2);
+      const int64_t qrow = (((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln;
+      if constexpr (F8) {
+        const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * dI + hf * (dI / 2);
 #pragma unroll
-      for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+        for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const long*>(qp + s * 8);
+      } else {
+        const __bf16* qp = static_cast<const __bf16*>(a.q) + qrow * dI + hf * (dI / 2);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const bf16x8*>(qp + s * 8);
+      }
     }
   }
 #pragma unroll
@@ -441,11 +509,16 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
       if (tile + 2 < n_tiles) st = load_tile(tile + 2);
     }
     __syncthreads();             // tile visible; every wave is done with tile - 1
-    bf16x8 kf[KS];
+    QFrag kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const int c = hf * (CH / 2) + s;
-      kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+      if constexpr (F8) {
+        const int c = hf * (CH8 / 2) + s;
+        kf[s] = *reinterpret_cast<const long*>(kt + ln * dI + ((c ^ f8_swz<dI>(ln)) * 8));
+      } else {
+        const int c = hf * (CH / 2) + s;
+        kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
+      }
     }
     const int64_t j = tile * 32 + ln;
 #pragma unroll
@@ -456,8 +529,12 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc = {};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        for (int s = 0; s < KS; ++s) {
+          if constexpr (F8)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+          else
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
+        }
         // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
 #pragma unroll
         for (int v = 0; v < 16; ++v)
@@ -507,14 +584,18 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
     } else {
       const int64_t n_tiles = (nv_max + 31) / 32;
       const int HT = a.HI / 32, KS = a.dI / 16;
-      const bool fp8 = a.fmt == kMixed;     // bf16 queries, E4M3 keys
+      // kBF16: bf16 queries and keys; kMixed: bf16 queries, E4M3 keys;
+      // kE4M3: E4M3 queries and keys (FP8 MFMA)
+      const int kf = a.fmt;
       if (a.Tq >= 8 && !sb.split) {
         // Prefill: a block of eight waves shares each key tile among 8 * QPW
         // queries and sweeps all the keys they see.
 #define LAC_SCORE_CASE(ht, ks, qpw)                                                        \
   if (HT == ht && KS == ks) {                                                              \
     const int blocks = a.B * ((a.Tq + 8 * qpw - 1) / (8 * qpw));                           \
-    if (fp8)                                                                               \
+    if (kf == kE4M3)                                                                       \
+      hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw, kE4M3>), dim3(blocks), dim3(512), 0, st, sa); \
+    else if (kf == kMixed)                                                                 \
       hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw, kMixed>), dim3(blocks), dim3(512), 0, st, sa); \
     else                                                                                   \
       hipLaunchKernelGGL((score_prefill_kernel<ht, ks, qpw, kBF16>), dim3(blocks), dim3(512), 0, st, sa); \
@@ -528,7 +609,7 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
         // one round of the 512 resident blocks (two blocks of 4 waves per
         // compute unit at this kernel's register use), so no partial second
         // round trails the sweep.
-        const int64_t per_row = std::max<int64_t>(1, 512 / R);
+        const int64_t per_row = std::max<int64_t>(1, (kf == kE4M3 ? kDecodeBlocksF8 : kDecodeBlocksBF16) / R);
         sa.tiles_per_wave = (int)std::max<int64_t>(2, (n_tiles + 4 * per_row - 1) / (4 * per_row));
         const int64_t chunks = (n_tiles + 4 * sa.tiles_per_wave - 1) / (4 * sa.tiles_per_wave);
         // dynamic schedule: about the last quarter of the sweep
@@ -537,8 +618,9 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
         const int groups = a.B * a.Tq;
 #define LAC_SCORE_CASE(ht, ks)                                                      \
   if (HT == ht && KS == ks)                                                         \
-    err = fp8 ? launch_score<ht, ks, 1, 1, kMixed>(sa, chunks, groups, st)          \
-              : launch_score<ht, ks, 1, 1, kBF16>(sa, chunks, groups, st);
+    err = kf == kE4M3    ? launch_score<ht, ks, 1, 1, kE4M3>(sa, chunks, groups, st)  \
+          : kf == kMixed ? launch_score<ht, ks, 1, 1, kMixed>(sa, chunks, groups, st) \
+                         : launch_score<ht, ks, 1, 1, kBF16>(sa, chunks, groups, st);
         LAC_SCORE_CASE(1, 4) LAC_SCORE_CASE(1, 8) LAC_SCORE_CASE(2, 4) LAC_SCORE_CASE(2, 8)
         LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
 #undef LAC_SCORE_CASE

@@ -125,7 +125,7 @@ def csa_decode(seed=2, B=32, ctx=131072, D=512, m=4, r=64, HI=64, dI=128, H=64, 
         ckv=store(normal(seed, "ckv", (B, N, D), device=device), fmt, r),
         KI=store(normal(seed, "KI", (B, N, dI), device=device), "bf16"),
         raw=store(normal(seed, "raw", (B, W, D), device=device), fmt, r),
-        qI=store(normal(seed, "qI", (B, 1, HI, dI), device=device), "bf16"),
+        qI=store(normal(seed, "qI", (B, 1, HI, dI), device=device), qi_fmt),
         w=uniform(seed, "w", (B, 1, HI), device=device),
         q=store(normal(seed, "q", (B, 1, H, D), device=device), "bf16"),
     )
@@ -160,12 +160,13 @@ def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, d
 
 
 def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI=128, H=64,
-                k=2048, W=128, ki_fmt="bf16", csa_overlap=0, device="cpu"):
+                k=2048, W=128, ki_fmt="bf16", csa_overlap=0, qi_fmt="bf16", device="cpu"):
     """Decode of a CSA + HCA layer pair at position ctx with the KV stored as
     FP8 E4M3 plus bf16 rotated dims.  The step also compresses the newest
     complete block of each layer (CSA entry, indexer key, HCA entry) from
     bf16 activations, so every stage of the path runs in one step.  The
-    indexer keys are bf16, or E4M3 with ki_fmt = "mixed" (no rotated dims).
+    indexer keys are bf16, or E4M3 with ki_fmt = "mixed" (no rotated dims);
+    indexer queries likewise with qi_fmt.
     With csa_overlap > 0 the newest CSA block comes with the csa_overlap raw
     rows before it (overlapping compression windows)."""
     N = ctx // m
@@ -185,7 +186,7 @@ def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI
         new_zI=store(normal(seed, "new_zI", (B, m, dI), device=device), "bf16"),
         new_kv_hca=store(normal(seed, "new_kv_hca", (B, m_hca, D), device=device), "bf16"),
         new_z_hca=store(normal(seed, "new_z_hca", (B, m_hca, D), device=device), "bf16"),
-        qI=store(normal(seed, "qI", (B, 1, HI, dI), device=device), "bf16"),
+        qI=store(normal(seed, "qI", (B, 1, HI, dI), device=device), qi_fmt),
         w=uniform(seed, "w", (B, 1, HI), device=device),
         q_csa=store(normal(seed, "q_csa", (B, 1, H, D), device=device), "bf16"),
         q_hca=store(normal(seed, "q_hca", (B, 1, H, D), device=device), "bf16"),

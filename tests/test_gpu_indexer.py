@@ -172,3 +172,34 @@ def test_bf16_rowwise_kernel_decode_72_sequences():
 def test_bf16_rowwise_kernel_all_tied_takes_lowest_indices():
     idx = _run_gpu_drawn(1, 80, 32, 64, 70080, 4, 2048, [280000], 43, [0], [0, 79], w_zero=True)
     assert torch.equal(idx[0].cpu(), torch.arange(2048, dtype=torch.int32).expand(80, 2048))
+
+
+# E4M3 queries and E4M3 keys (d_I bytes each): products on the FP8 matrix
+# cores, exact per product, summed in fp32.
+def test_e4m3_queries_decode_split_path():
+    same = _run(2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], "mixed", 31,
+                kfmt="mixed")
+    assert len(same) >= 1
+
+
+def test_e4m3_queries_decode_prefix_path_ragged():
+    _run(4, 1, 64, 128, 5003, 4, 512, [4 * 5003 + 1, 4 * 5003, 4 * 3000 + 3, 40000], "mixed", 32,
+         kfmt="mixed")
+
+
+def test_e4m3_queries_chunked_prefill_causal_rows():
+    _run(1, 40, 64, 128, 5010, 4, 300, [20000], "mixed", 33, kfmt="mixed")
+
+
+def test_e4m3_queries_prefill_with_rows_that_see_nothing():
+    _run(2, 24, 64, 128, 64, 4, 8, [0, 100], "mixed", 34, kfmt="mixed")
+
+
+@pytest.mark.parametrize("HI,dI", [(32, 64), (32, 128), (64, 64), (128, 128)])
+def test_e4m3_queries_head_and_dim_variants(HI, dI):
+    _run(2, 1, HI, dI, 2100, 4, 256, [8400, 9000], "mixed", 35 + HI + dI, kfmt="mixed")
+
+
+@pytest.mark.parametrize("HI,dI", [(32, 64), (128, 128)])
+def test_e4m3_queries_prefill_head_and_dim_variants(HI, dI):
+    _run(1, 17, HI, dI, 700, 4, 64, [2790], "mixed", 36 + HI + dI, kfmt="mixed")
