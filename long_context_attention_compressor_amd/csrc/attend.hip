@@ -41,6 +41,7 @@ namespace {
 inline int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kIdxLds = 2304;   // CSA indices of a split staged in LDS
+constexpr int kTile = 32;       // entries per attention tile
 constexpr int kGridTarget = 256;   // blocks per launch the split count aims at
 
 __host__ __device__ inline int64_t kv_row_bytes(int fmt, int D, int r) {
@@ -49,10 +50,18 @@ __host__ __device__ inline int64_t kv_row_bytes(int fmt, int D, int r) {
 
 // ---------------------------------------------------------------- plan
 struct AttnPlan {
-  int G, Hs, n_htiles, n_qgroups, n_work, nsplit, chunk, max_entries;
-  int64_t win_rows, row_bytes;
+  int G, Hs, n_htiles, n_qgroups, n_work, nsplit, chunk, wchunk, max_entries;
+  int64_t win_rows, row_bytes, win_row_bytes;
   size_t off_zero, off_win, off_ang, off_po, off_pml, total;
 };
+
+// Low parts of rotated window dims.  A window row rotated at its position is
+// rounded to bf16 for the matrix cores; its dims from lo_base = D - R32 on
+// (R32 = r rounded up to 32) also keep the residual x - bf16(x) as a second
+// bf16 value, and the tiles holding window rows add that part's products,
+// so the rotation adds no rounding beyond the bf16 storage of the raw row.
+__host__ __device__ inline int lo_dims(int r) { return (r + 31) / 32 * 32; }
+constexpr int kLoRow = 2 * 128 + 16;          // LDS bytes per staged low row (R32 <= 128)
 
 // shared_entries: the G queries of a work item see one common run of compressed
 // entries (HCA's causal prefix) rather than G separate selections (CSA).
@@ -64,8 +73,11 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   size_t off = 0;
   p.off_zero = off;
   off += 256;
+  // pre-rotated window rows (bf16 and mixed formats) carry their low parts
+  // after the row: R32 bf16 values for dims lo_base .. D-1
+  p.win_row_bytes = p.row_bytes + (f32_path ? 0 : 2 * lo_dims(r));
   p.off_win = off;
-  off += round_up((int64_t)B * p.win_rows * p.row_bytes, 256);
+  off += round_up((int64_t)B * p.win_rows * p.win_row_bytes, 256);
   p.off_ang = off;
   off += round_up((int64_t)B * Tq * (r / 2) * 8, 256);
   if (f32_path) {
@@ -89,6 +101,15 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.chunk = (int)round_up((p.max_entries + ns - 1) / ns, 32);
   if (p.chunk > kIdxLds) p.chunk = kIdxLds;    // a split's CSA indices fit in LDS
   p.nsplit = (p.max_entries + p.chunk - 1) / p.chunk;
+  if (p.nsplit > 1 && W > 0) {
+    // Split-K with a window: the window rows (rotated in the kernel, with
+    // low parts) get splits of one tile each after the compressed entries'
+    // splits, so that their extra work does not lengthen the longest split.
+    const int n_comp_max = p.max_entries - (W + p.G - 1);
+    const int n_win_max = W + p.G - 1;
+    p.wchunk = kTile;
+    p.nsplit = (n_comp_max + p.chunk - 1) / p.chunk + (n_win_max + kTile - 1) / kTile;
+  }
   if (p.nsplit > 1) {
     p.off_po = off;
     off += round_up((int64_t)p.n_work * p.nsplit * 64 * D * 2, 256);
@@ -102,12 +123,12 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
 // ---------------------------------------------------------------- window rotation
 struct WinArgs {
   const uint8_t* raw;
-  uint8_t* win;
+  uint8_t* win;              // [B, win_rows, win_row_bytes]
   uint8_t* zero_row;
   float2* ang;               // [B, Tq, r/2] (cos, sin) of each query position's angles
   int64_t n_win_items;       // window work items (D/8 per row); angle items follow
   int fmt, B, D, r, Tq, W;
-  int64_t T_raw, win_rows, row_bytes;
+  int64_t T_raw, win_rows, row_bytes, win_row_bytes;
   RopeTable rope;
   Positions qpos, rawpos;
 };
@@ -141,8 +162,12 @@ __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
   const int64_t s = lo + row;
   if (s > (int64_t)a.qpos.v[b] + a.Tq - 1) return;
   const uint8_t* src = a.raw + ((int64_t)b * a.T_raw + (s - a.rawpos.v[b])) * a.row_bytes;
-  uint8_t* dst = a.win + ((int64_t)b * a.win_rows + row) * a.row_bytes;
+  uint8_t* dst = a.win + ((int64_t)b * a.win_rows + row) * a.win_row_bytes;
   const int c0 = g * 8, nope = a.D - a.r;
+  const int lo_base = a.D - lo_dims(a.r);
+  uint16_t* lrow = reinterpret_cast<uint16_t*>(dst + a.row_bytes);    // the row's low parts
+  if (a.fmt != kF32 && c0 >= lo_base && c0 < nope)     // no low part below the rotated dims
+    *reinterpret_cast<uint4*>(lrow + (c0 - lo_base)) = make_uint4(0u, 0u, 0u, 0u);
   if (c0 < nope) {   // not rotated: copy
     if (a.fmt == kF32) {
       reinterpret_cast<float4*>(dst + c0 * 4)[0] = reinterpret_cast<const float4*>(src + c0 * 4)[0];
@@ -179,8 +204,12 @@ __global__ void __launch_bounds__(256) rope_window_kernel(WinArgs a) {
     reinterpret_cast<float4*>(dst + off)[0] = make_float4(v[0], v[1], v[2], v[3]);
     reinterpret_cast<float4*>(dst + off)[1] = make_float4(v[4], v[5], v[6], v[7]);
   } else {
-    reinterpret_cast<uint2*>(dst + off)[0] = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-    reinterpret_cast<uint2*>(dst + off)[1] = make_uint2(pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split_bf16x2(v[2 * q], v[2 * q + 1], &hw[q], &lw[q]);
+    reinterpret_cast<uint2*>(dst + off)[0] = make_uint2(hw[0], hw[1]);
+    reinterpret_cast<uint2*>(dst + off)[1] = make_uint2(hw[2], hw[3]);
+    *reinterpret_cast<uint4*>(lrow + (c0 - lo_base)) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
 }
 
@@ -189,7 +218,7 @@ struct KArgs {
   const void* q;
   const uint8_t* kv;
   const int32_t* idx;
-  const uint8_t* win;
+  const uint8_t* win;        // pre-rotated window rows, win_row_bytes each
   const float* sink;
   void* out;
   uint16_t* part_o;         // [work, split, 64, D] bf16 partial outputs / their row sums
@@ -202,8 +231,8 @@ struct KArgs {
   Positions rawpos;
   int mode, N, k, m, W, B, Tq, H, D, r;
   float theta, scale_log2;
-  int G, Hs, n_htiles, n_qgroups, nsplit, chunk;
-  int64_t win_rows, row_bytes;
+  int G, Hs, n_htiles, n_qgroups, nsplit, chunk, wchunk;
+  int64_t win_rows, row_bytes, win_row_bytes;
   Positions qpos;
   RopeTable rope;
   const float* q_norm_gain;  // [D] or null: RMSNorm of each query head before its rotation
@@ -295,7 +324,7 @@ __device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& 
   }
   const int off = e - w.n_comp;
   *tag = kWinTag | off;
-  return a.win + ((int64_t)w.b * a.win_rows + w.win_row0 + off) * a.row_bytes;
+  return a.win + ((int64_t)w.b * a.win_rows + w.win_row0 + off) * a.win_row_bytes;
 }
 
 // ---------------------------------------------------------------- MFMA attention
@@ -325,7 +354,6 @@ __device__ __forceinline__ const uint8_t* entry_src(const KArgs& a, const Work& 
 // uniform 16-byte loads), written to one of two LDS buffers as bf16 rows
 // (E4M3 widened by the hardware converter; window rows rotated here in
 // decode), and a barrier publishes them.
-constexpr int kTile = 32;
 
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -357,6 +385,7 @@ struct Geo {
   static constexpr int TPR = 8 * DS;             // staging threads per entry row
   static constexpr int NCH = D / 8 / TPR;        // 16-byte chunks per staging thread, bf16 rows
   static constexpr int NCHM = (D / 16 + 8 + TPR - 1) / TPR;   // mixed rows (<= D/16 + 8 chunks)
+  static constexpr int NLO = (16 + TPR - 1) / TPR;            // low-part chunks (<= 16 per row)
 };
 
 template <int D, int KV>
@@ -364,6 +393,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   using Gm = Geo<D>;
   constexpr int DS = Gm::DS, NT = Gm::NT, TPR = Gm::TPR;
   __shared__ __align__(16) uint8_t Et[2][kTile * Gm::EROW];     // entry tiles, bf16 rows
+  __shared__ __align__(16) uint8_t Elo[2][kTile * kLoRow];      // low parts, dims lo_base..D-1
   // Per entry: the first query slot of the block that sees it and the span of
   // slots after it that do (an empty slot has first = 64, which no slot
   // reaches), so a (row, entry) visibility test is one unsigned compare.
@@ -381,8 +411,20 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
   const Work w = make_work(a, blockIdx.y);
   const int split = blockIdx.x;
-  const int e_lo = split * a.chunk;
-  const int e_hi = min(w.n_tot, e_lo + a.chunk);
+  // Split -> entry range: chunk entries per split, or, with wchunk, chunk
+  // entries per split over the compressed entries and then wchunk per split
+  // over the window rows.
+  int e_lo, e_hi;
+  {
+    const int ns_c = a.wchunk > 0 ? (w.n_comp + a.chunk - 1) / a.chunk : 1 << 30;
+    if (split < ns_c) {
+      e_lo = split * a.chunk;
+      e_hi = min(a.wchunk > 0 ? w.n_comp : w.n_tot, e_lo + a.chunk);
+    } else {
+      e_lo = w.n_comp + (split - ns_c) * a.wchunk;
+      e_hi = min(w.n_tot, e_lo + a.wchunk);
+    }
+  }
   const int nope = a.D - a.r;
   const int npair = a.r / 2;
   const int row_bytes = (int)a.row_bytes;
@@ -393,7 +435,16 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   const bool rot_here = !a.win_rotated;
   const uint8_t* winb = rot_here
       ? a.raw + ((int64_t)w.b * a.T_raw + (w.lo_w - a.rawpos.v[w.b])) * row_bytes
-      : a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * row_bytes;
+      : a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * a.win_row_bytes;
+  // low parts of rotated window dims (dims lo_base .. D-1), added on the
+  // tiles that hold window rows
+  const int lo_base = D - lo_dims(a.r);
+  const int n_lo_ch = (D - lo_base) / 8;        // 16-byte chunks of a row's low parts
+  const bool has_lo = a.r > 0 && a.W > 0;
+  // 32-dim k-steps of this wave's part of D at or past lo_base (its last
+  // ones; lo_base is a multiple of 32 and at least D - 128)
+  const int nlo = __builtin_amdgcn_readfirstlane(
+      max(0, min(Gm::DW, (dh + 1) * Gm::DW - lo_base)) / 32);
   const uint8_t* any_row = static_cast<const uint8_t*>(a.q);   // valid address for empty slots
   const int n_fp8 = KV == kMixed ? nope / 16 : 0;
   const int n_chunks = KV == kMixed ? n_fp8 + a.r / 8 : D / 8;
@@ -440,9 +491,17 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   __syncthreads();
 
   constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
-  uint4 stage[NST];
+  uint4 stage[NST], stage_lo[Gm::NLO];
+  // first dim of 16-byte staging chunk ch (mixed rows: 16 E4M3 dims per chunk,
+  // then 8 bf16 rope dims per chunk)
+  auto chunk_dim = [&](int ch) {
+    if constexpr (KV == kMixed) return ch < n_fp8 ? 16 * ch : nope + 8 * (ch - n_fp8);
+    return 8 * ch;
+  };
   int st_tag = kNoEntry, st_lo = 64, st_span = 0;
-  auto load_tile = [&](int base) {
+  // lo_loads: the tile holds pre-rotated window rows, whose low parts are
+  // loaded too (a uniform branch; every lane then issues those loads).
+  auto load_tile = [&](int base, bool lo_loads) {
     const int e = base + st_e;
     const uint8_t* rs = nullptr;
     int tag = kNoEntry;
@@ -466,7 +525,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
         }
       } else {
         // window row at position s = lo_w + off: seen from t in [s, s + W - 1]
-        rs = winb + (int64_t)(e - n_comp) * row_bytes;
+        rs = winb + (int64_t)(e - n_comp) * (rot_here ? row_bytes : (int)a.win_row_bytes);
         tag = kWinTag | (e - n_comp);
         lo = w.lo_w + (e - n_comp) - w.t_first;
         hi = min((int64_t)w.n_q - 1, lo + a.W - 1);
@@ -485,42 +544,72 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
       const uint8_t* src = (rs != nullptr && ch < n_chunks) ? rs + 16 * ch : any_row;
       stage[q] = ld_stream16(src);
     }
+    // pre-rotated window rows carry their low parts after the row
+    if (lo_loads) {
+#pragma unroll
+      for (int q = 0; q < Gm::NLO; ++q) {
+        const int j = st_part + TPR * q;
+        const bool mine = rs != nullptr && tag >= kWinTag && j < n_lo_ch;
+        stage_lo[q] = ld_stream16(mine ? rs + 16 * (n_chunks + j) : any_row);
+      }
+    }
   };
   // A window row is rotated here at its position s: the 16-byte chunk of
-  // bf16 rope dims it holds is 4 pairs starting at pair p0.
-  auto rotate_chunk = [&](uint4 v, int p0, int64_t pos) {
-    uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+  // bf16 rope dims it holds is 4 pairs starting at pair p0; the rotated
+  // values leave as bf16 high parts (returned) and low parts (*lo).
+  auto rotate_chunk = [&](uint4 v, int p0, int64_t pos, uint4* lo) {
+    uint32_t wd[4] = {v.x, v.y, v.z, v.w}, lw[4];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       float cs, sn;
       rope_cos_sin((double)pos, freq[p0 + p], &cs, &sn);
       const float x0 = bf16_to_f32(wd[p] & 0xffffu), x1 = bf16_to_f32(wd[p] >> 16);
-      wd[p] = pack_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+      split_bf16x2(x0 * cs - x1 * sn, x0 * sn + x1 * cs, &wd[p], &lw[p]);
     }
+    *lo = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     return make_uint4(wd[0], wd[1], wd[2], wd[3]);
   };
-  auto store_tile = [&](int buf) {
+  // with_lo: the tile holds window rows, so every row of it writes its low
+  // parts (zero but for the rotated dims of window rows).
+  auto store_tile = [&](int buf, auto with_lo_c) {
+    constexpr bool with_lo = decltype(with_lo_c)::value;
     uint8_t* dst_row = Et[buf] + st_e * Gm::EROW;
+    uint8_t* lo_row = Elo[buf] + st_e * kLoRow;
     const bool empty = st_tag == kNoEntry;
-    const bool win = rot_here && st_tag >= kWinTag;
+    const bool is_win = st_tag >= kWinTag;
+    const bool win = rot_here && is_win;
     const int64_t wpos = w.lo_w + (st_tag - kWinTag);
 #pragma unroll
     for (int q = 0; q < NST; ++q) {
       const int ch = st_part + TPR * q;
       if (ch >= n_chunks) continue;
       uint4 v = empty ? make_uint4(0u, 0u, 0u, 0u) : stage[q];
+      uint4 lo = make_uint4(0u, 0u, 0u, 0u);
+      const int dc = chunk_dim(ch);
       if constexpr (KV == kMixed) {
         if (ch < n_fp8) {    // 16 E4M3 codes -> 16 bf16 (exact)
           uint4* dst = reinterpret_cast<uint4*>(dst_row + 32 * ch);
           dst[0] = e4m3x8_to_bf16x8(v.x, v.y);
           dst[1] = e4m3x8_to_bf16x8(v.z, v.w);
         } else {
-          if (win) v = rotate_chunk(v, 4 * (ch - n_fp8), wpos);
+          if (win) v = rotate_chunk(v, 4 * (ch - n_fp8), wpos, &lo);
           *reinterpret_cast<uint4*>(dst_row + 32 * n_fp8 + 16 * (ch - n_fp8)) = v;
         }
       } else {
-        if (win && 8 * ch >= nope) v = rotate_chunk(v, (8 * ch - nope) / 2, wpos);
+        if (win && dc >= nope) v = rotate_chunk(v, (dc - nope) / 2, wpos, &lo);
         *reinterpret_cast<uint4*>(dst_row + 16 * ch) = v;
+      }
+      if (with_lo && win && dc >= nope) *reinterpret_cast<uint4*>(lo_row + 2 * (dc - lo_base)) = lo;
+    }
+    if constexpr (with_lo) {
+      // low-part slot j: the loaded low parts of a pre-rotated window row,
+      // else zeros, except where a window row rotated here wrote its own
+#pragma unroll
+      for (int q = 0; q < Gm::NLO; ++q) {
+        const int j = st_part + TPR * q;
+        if (j < n_lo_ch && !(win && lo_base + 8 * j >= nope))
+          *reinterpret_cast<uint4*>(lo_row + 16 * j) =
+              (!rot_here && is_win) ? stage_lo[q] : make_uint4(0u, 0u, 0u, 0u);
       }
     }
     if (st_part == 0) {
@@ -532,7 +621,11 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   // Unconditional (past the split's end the slots are empty and read a valid
   // address), so the waits for the query slices below can count the three
   // tile loads issued after them and leave those in flight.
-  load_tile(e_lo);
+  // tiles from t_win on hold window rows (they sit at the end of the entry
+  // list, from n_comp on); pre-rotated ones bring their low parts
+  const int t_win = has_lo && e_hi > n_comp ? min(n_tiles, max(0, n_comp - e_lo) / kTile) : n_tiles;
+  const bool lo_loads = !rot_here && has_lo;
+  load_tile(e_lo, lo_loads && t_win == 0);
 
   // the block's query angles, then the lane's query slices rotated at t
   for (int e = tid; e < G * npair; e += NT) {
@@ -609,123 +702,15 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   float* sx_mine = &Sx[dh][rg][l][0];
   const float* sx_other = &Sx[DS - 1 - dh][rg][l][0];
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    store_tile(buf);          // waits for this thread's prefetched rows
-    lds_barrier();            // tile t visible; every wave is done with tile t-1
-    if (t + 1 < n_tiles) load_tile(e_lo + (t + 1) * kTile);
-    const uint8_t* E = Et[buf];
-
-    // ---- partial S^T over this wave's half of D, entries 0-15 (s0) and
-    // 16-31 (s1); the entry fragments are read one group of k-steps ahead.
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    {
-      constexpr int QG = Gm::KH >= 4 ? 4 : Gm::KH;
-      const uint8_t* eb = E + lr * Gm::EROW + 16 * lq + 2 * dh * Gm::DW;
-      bf16x8 fa[2][QG], fb[2][QG];
-#pragma unroll
-      for (int u = 0; u < QG; ++u) {
-        fa[0][u] = *reinterpret_cast<const bf16x8*>(eb + 64 * u);
-        fb[0][u] = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * u);
-      }
-#pragma unroll
-      for (int gi = 0; gi < Gm::KH / QG; ++gi) {
-        const int cur = gi & 1;
-        if (gi + 1 < Gm::KH / QG) {
-#pragma unroll
-          for (int u = 0; u < QG; ++u) {
-            const int st = (gi + 1) * QG + u;
-            fa[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(eb + 64 * st);
-            fb[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * st);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < QG; ++u) {
-          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][u], qreg[gi * QG + u], s0, 0, 0, 0);
-          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[cur][u], qreg[gi * QG + u], s1, 0, 0, 0);
-        }
-      }
-    }
-    // ---- sum the two halves' partial logits (D split over two waves)
-    const int4 vl0 = *reinterpret_cast<const int4*>(&vis_lo[buf][4 * lq]);
-    const int4 vl1 = *reinterpret_cast<const int4*>(&vis_lo[buf][16 + 4 * lq]);
-    const int4 vs0 = *reinterpret_cast<const int4*>(&vis_span[buf][4 * lq]);
-    const int4 vs1 = *reinterpret_cast<const int4*>(&vis_span[buf][16 + 4 * lq]);
-    float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
-    if constexpr (DS == 2) {
-      *reinterpret_cast<float4*>(sx_mine) = make_float4(s0[0], s0[1], s0[2], s0[3]);
-      *reinterpret_cast<float4*>(sx_mine + 4) = make_float4(s1[0], s1[1], s1[2], s1[3]);
-      lds_barrier();
-      o0 = *reinterpret_cast<const float4*>(sx_other);
-      o1 = *reinterpret_cast<const float4*>(sx_other + 4);
-    }
-
-    // ---- online softmax of row `row` over the lane's 8 entries (the same in
-    // both waves of the row group)
-    const int vlo[8] = {vl0.x, vl0.y, vl0.z, vl0.w, vl1.x, vl1.y, vl1.z, vl1.w};
-    const int vsp[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
-    float x[8] = {s0[0] + o0.x, s0[1] + o0.y, s0[2] + o0.z, s0[3] + o0.w,
-                  s1[0] + o1.x, s1[1] + o1.y, s1[2] + o1.z, s1[3] + o1.w};
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[i] = (uint32_t)(g - vlo[i]) <= (uint32_t)vsp[i] ? x[i] * scale_log2 : -INFINITY;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = row_max4(tmax);
-    const bool moved = tmax > m_run + 8.f;          // also true for the first visible entry
-    const bool rescale = moved && m_run != -INFINITY;   // the row's O holds earlier entries
-    const float m_new = moved ? tmax : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float al = moved ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-    float psum = 0.f;
-    uint32_t pk[4];
-#pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(x[i] - m_use), p1 = __builtin_amdgcn_exp2f(x[i + 1] - m_use);
-      psum += p0 + p1;
-      pk[i / 2] = pack_bf16x2(p0, p1);
-    }
-    l_part = l_part * al + psum;
-    m_run = m_new;
-    bf16x8 pb;
-    __builtin_memcpy(&pb, pk, 16);
-    if (__ballot(rescale)) {
-#pragma unroll
-      for (int dt = 0; dt < Gm::DH; ++dt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oacc[dt][i] *= al;
-    }
-
-    // ---- O^T += E^T P^T over the wave's half of D, 16 output dims per MFMA;
-    // the transposed entry fragments are read PG output tiles ahead.
-    {
-      constexpr int PG = Gm::DH >= 8 ? 8 : Gm::DH;
-      const uint8_t* tb = E + (4 * lq + (lr >> 2)) * Gm::EROW + 8 * (lr & 3) + 2 * dh * Gm::DW;
-      bf16x4 lo[2][PG], hi[2][PG];
-#pragma unroll
-      for (int u = 0; u < PG; ++u) {
-        lo[0][u] = ds_read_tr(tb + 32 * u);
-        hi[0][u] = ds_read_tr(tb + 16 * Gm::EROW + 32 * u);
-      }
-#pragma unroll
-      for (int gi = 0; gi < Gm::DH / PG; ++gi) {
-        const int cur = gi & 1;
-        if (gi + 1 < Gm::DH / PG) {
-#pragma unroll
-          for (int u = 0; u < PG; ++u) {
-            const int dt = (gi + 1) * PG + u;
-            lo[cur ^ 1][u] = ds_read_tr(tb + 32 * dt);
-            hi[cur ^ 1][u] = ds_read_tr(tb + 16 * Gm::EROW + 32 * dt);
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < PG; ++u) {
-          const bf16x8 ab = __builtin_shufflevector(lo[cur][u], hi[cur][u], 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[gi * PG + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, pb, oacc[gi * PG + u], 0, 0, 0);
-        }
-      }
-    }
+  for (int t = 0; t < t_win; ++t) {
+#define LAC_TILE_LO false
+#include "attend_tile.inc"
+#undef LAC_TILE_LO
+  }
+  for (int t = t_win; t < n_tiles; ++t) {
+#define LAC_TILE_LO true
+#include "attend_tile.inc"
+#undef LAC_TILE_LO
   }
 
   // ---- row sum over the row's four lanes
@@ -1079,6 +1064,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
     WinArgs wa{};
     wa.raw = static_cast<const uint8_t*>(a.raw);
     wa.win = w8 + p.off_win;
+    wa.win_row_bytes = p.win_row_bytes;
     wa.zero_row = w8 + p.off_zero;
     wa.fmt = a.kv_fmt; wa.B = a.B; wa.D = a.D; wa.r = a.r; wa.Tq = a.Tq; wa.W = a.W;
     wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes;
@@ -1093,6 +1079,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   }
   KArgs k{};
   k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
+  k.win_row_bytes = p.win_row_bytes;
   k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
   k.ang = reinterpret_cast<const float2*>(w8 + p.off_ang);
   k.part_o = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(w8 + p.off_po) : nullptr;
@@ -1104,7 +1091,7 @@ hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
   k.q_norm_gain = a.q_norm_gain;
   k.norm_eps = a.norm_eps;
   k.G = p.G; k.Hs = p.Hs; k.n_htiles = p.n_htiles; k.n_qgroups = p.n_qgroups;
-  k.nsplit = p.nsplit; k.chunk = p.chunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;
+  k.nsplit = p.nsplit; k.chunk = p.chunk; k.wchunk = p.wchunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;
   k.qpos = a.qpos;
   k.raw = static_cast<const uint8_t*>(a.raw); k.T_raw = a.T_raw; k.rawpos = a.rawpos;
   k.win_rotated = win_rotated;

@@ -48,6 +48,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return u;
 }
 
+// Two floats as bf16 high parts plus bf16 low parts: hi = bf16(x), lo =
+// bf16(x - hi) (the difference is exact in fp32), so hi + lo carries about 16
+// significant bits of x.
+__device__ __forceinline__ void split_bf16x2(float x0, float x1, uint32_t* hi, uint32_t* lo) {
+  const uint32_t h = pack_bf16x2(x0, x1);
+  *hi = h;
+  *lo = pack_bf16x2(x0 - bf16_to_f32(h & 0xffffu), x1 - bf16_to_f32(h >> 16));
+}
+
 // ---------------------------------------------------------------- FP8 E4M3 ("fn")
 // Exponent bias 7, largest finite 448, subnormal step 2^-9, 0x7f/0xff NaN.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {

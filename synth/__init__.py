@@ -125,7 +125,7 @@ def csa_decode(seed=2, B=32, ctx=131072, D=512, m=4, r=64, HI=64, dI=128, H=64, 
         ckv=store(normal(seed, "ckv", (B, N, D), device=device), fmt, r),
         KI=store(normal(seed, "KI", (B, N, dI), device=device), "bf16"),
         raw=store(normal(seed, "raw", (B, W, D), device=device), fmt, r),
-        qI=store(normal(seed, "qI", (B, 1, HI, dI), device=device), qi_fmt),
+        qI=store(normal(seed, "qI", (B, 1, HI, dI), device=device), "bf16"),
         w=uniform(seed, "w", (B, 1, HI), device=device),
         q=store(normal(seed, "q", (B, 1, H, D), device=device), "bf16"),
     )

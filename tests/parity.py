@@ -97,7 +97,14 @@ def check_attention(gpu: np.ndarray, ref: np.ndarray, what=""):
     den = np.abs(ref).max(axis=-1)
     rel = np.where(den > 0, num / np.maximum(den, 1e-300), num)
     worst = float(rel.max()) if rel.size else 0.0
-    assert worst <= ATTN_TOL, f"{what}: worst row relative error {worst:.3e}"
+    if worst > ATTN_TOL:
+        bad = np.argwhere(rel > ATTN_TOL)
+        r, h = (int(v) for v in np.unravel_index(int(np.argmax(rel)), rel.shape))
+        d = int(np.argmax(np.abs(gpu[r, h] - ref[r, h])))
+        raise AssertionError(
+            f"{what}: worst row relative error {worst:.3e} at (row {r}, head {h}, dim {d}): "
+            f"gpu {gpu[r, h, d]:.6g} ref {ref[r, h, d]:.6g}, row max |ref| {den[r, h]:.4g}; "
+            f"{len(bad)} (row, head) pairs over {ATTN_TOL}: first {bad[:12].tolist()}")
     return worst
 
 

@@ -4,9 +4,10 @@ oracle computes row by row:
 
   * 1M-token decode of a CSA + HCA layer pair (4 sequences, 262144 CSA and
     8192 HCA entries, FP8 E4M3 + bf16 RoPE dims, top-2048, window 128);
-  * CSA decode at 131072 tokens (32 sequences, bf16, top-2048);
+  * CSA decode at 131072 tokens (32 sequences, bf16, top-2048), every
+    sequence;
   * CSA chunked prefill (4096 queries after 262144 tokens, top-2048);
-  * HCA prefill of 8192 tokens (bf16, m' = 128, window 128).
+  * HCA prefill of 8192 tokens (bf16, m' = 128, window 128), every query.
 
 The oracle never reads a value the GPU produced: it compresses the newest
 blocks itself, selects with its own scores, and its selection is uploaded to
@@ -111,7 +112,7 @@ def test_csa_decode_128k():
     y = lac.csa_attend(c["q"], c["ckv"], idx, c["raw"], W, q_pos0=ctx, raw_pos0=c["raw_pos0"],
                        rope_dims=r)
     torch.cuda.synchronize()
-    seqs = [0, 7, 19, 31]
+    seqs = list(range(B))          # every sequence
     sub = lambda t: _h(t[seqs])
     rows = [(b, 0) for b in range(len(seqs))]
     g_idx = idx.cpu().numpy()[seqs]
@@ -128,7 +129,9 @@ def test_csa_decode_128k():
                         sub(c["raw"]), W, c["raw_pos0"], W, None, 0.0, len(seqs), 1, H, D, r,
                         TH, ctx, rows)
     check_attention(as_f64(y_sel)[seqs, 0], ref, "CSA decode 128K")
-    # where the two selections agree the benchmarked output is checked as well
+    # where the two selections agree the benchmarked output is checked as
+    # well; the other rows' selections differ only at near-ties (check_topk)
+    # and their attention was checked above on the oracle's selection
     for j in same:
         check_attention(as_f64(y)[seqs[j], 0][None], ref[j][None], "CSA decode 128K chain")
 
@@ -186,8 +189,7 @@ def test_hca_prefill_8k():
     ref = oracle.compress(_h(c["kv"]), _h(c["z"]), oracle.BF16, 1, T, D, m, r, TH, 0)
     check_compressed(hkv, ref, "bf16", D, r)
     hkv_h = oracle.encode_rows(ref.reshape(N, D), oracle.BF16, r).view(np.uint16).reshape(1, N, D)
-    qi = sorted(set([0, 1, 126, 127, 128, 129, 255, 256, 1000, 4095, 4096, 8190, 8191]
-                    + list(range(3, 8192, 97))))
+    qi = list(range(T))            # every query
     rows = [(0, i) for i in qi]
     ref_y = oracle.attend(_h(c["q"]), oracle.BF16, hkv_h, oracle.BF16, N, 1, None, 0, m,
                           _h(c["kv"]), T, 0, W, None, 0.0, 1, T, H, D, r, TH, 0, rows)
