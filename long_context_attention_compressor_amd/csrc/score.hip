@@ -28,7 +28,7 @@ constexpr int kHistBins = kScoreHistBins;
 // Decode score launches: tile stages in flight per wave (bf16 keys, E4M3
 // keys) and the blocks the grid spreads over (bf16, E4M3 queries).
 constexpr int kStagesBF16 = 2, kStagesF8 = 2;
-constexpr int kDecodeBlocksBF16 = 512, kDecodeBlocksF8 = 512;
+constexpr int kDecodeBlocksBF16 = 512, kDecodeBlocksF8 = 768;
 
 // E4M3 key tiles in LDS (E4M3 queries): a row is d_I bytes, its 8-byte
 // chunks XOR-swizzled by f8_swz(row), chosen so that the MFMA-layout reads
