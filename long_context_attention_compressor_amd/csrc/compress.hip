@@ -287,10 +287,16 @@ hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   // fit: a long block (m' = 128) is then streamed by one compute unit.
   int S = 1;
   const int L = a.m + a.overlap;                 // tokens per window
-  while ((L + S - 1) / S > 8 && S < 256 && (a.overlap > 0 || a.m % (2 * S) == 0)) S *= 2;
+  // Few entries (a decode step's newest block): up to kFewPer tokens per
+  // thread and kFewGB channel groups per block, so that a long block spreads
+  // over more workgroups.
+  constexpr int kFewPer = 4, kFewGB = 4;
+  const bool few = a.norm_gain == nullptr && (int64_t)a.B * (a.T / a.m) * G < 4096;
+  const int per_max = few ? kFewPer : 8;
+  while ((L + S - 1) / S > per_max && S < 256 && (a.overlap > 0 || a.m % (2 * S) == 0)) S *= 2;
   int GB = G;
   if (a.norm_gain == nullptr)
-    while (GB * S > 256 && GB % 2 == 0) GB /= 2;
+    while ((GB * S > 256 || (few && GB > kFewGB)) && GB % 2 == 0) GB /= 2;
   if (GB * S > 512) {           // few channel groups and a long block: fewer splits
     while (GB * S > 512) S /= 2;
   }
