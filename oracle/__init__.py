@@ -80,6 +80,8 @@ def _load():
     lib.lo_index_scores2.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp,
                                      i32, vp, vp]
     lib.lo_index_scores2.restype = i32
+    lib.lo_round_scores_bf16.argtypes = [vp, ctypes.c_int64]
+    lib.lo_round_scores_bf16.restype = i32
     lib.lo_topk.argtypes = [vp, i32, i32, vp, i32, vp]
     lib.lo_topk.restype = i32
     lib.lo_attend.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, vp, i32, vp, i32, vp,
@@ -229,10 +231,11 @@ def _rows(rows, B, Tq):
     return np.ascontiguousarray(np.asarray(rows, np.int32).reshape(-1, 2))
 
 
-def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None, k_dtype=None):
+def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None, k_dtype=None,
+                 score_bf16=False):
     """-> (scores float64 [n_rows, N] with -inf where not visible, nvis int32 [n_rows]).
     q is stored in dtype, K in k_dtype (default dtype; the mixed code with no
-    rotated dims means E4M3 keys)."""
+    rotated dims means E4M3 codes).  score_bf16: the scores rounded to bf16."""
     rows = _rows(rows, B, Tq)
     n = rows.shape[0]
     scores = np.empty((n, N), np.float64)
@@ -243,7 +246,16 @@ def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None, k_dtype=
                                   B, Tq, HI, dI, N, _p(qpos), m, _p(rows), n, _p(scores), _p(nvis))
     if rc:
         raise ValueError(f"lo_index_scores rejected its arguments ({rc})")
+    if score_bf16:
+        _load().lo_round_scores_bf16(_p(scores), scores.size)
     return scores, nvis
+
+
+def round_scores_bf16(scores):
+    """Index scores rounded to bf16 (ties to even), in a new float64 array."""
+    out = np.array(scores, np.float64, copy=True, order="C")
+    _load().lo_round_scores_bf16(_p(out), out.size)
+    return out
 
 
 def topk(scores, nvis, k):

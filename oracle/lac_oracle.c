@@ -400,6 +400,17 @@ int lo_index_scores2(const void* q, int dtype, const float* w, const void* K, in
     return 0;
 }
 
+/* Index scores kept in BF16 ("DeepSeek V4 技术架构深度解析", section "三、FP4量化",
+ * its table of the quantisation scheme: the index scores go from FP32 to
+ * BF16).  Rounds every finite score in place to the nearest bf16 value, ties
+ * to even; -inf (an entry not visible) stays. */
+int lo_round_scores_bf16(double* s, int64_t n) {
+    int64_t i;
+    for (i = 0; i < n; ++i)
+        if (isfinite(s[i])) s[i] = lo_bf16_decode(lo_bf16_encode(s[i]));
+    return 0;
+}
+
 int lo_index_scores(const void* q, const float* w, const void* K, int dtype, int B, int Tq,
                     int HI, int dI, int N, const int64_t* qpos0, int m,
                     const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {

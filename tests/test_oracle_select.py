@@ -93,6 +93,36 @@ def test_scores_with_e4m3_queries_and_keys_use_the_decoded_values():
             assert np.isneginf(s[rr, nv[rr]:]).all()
 
 
+def test_bf16_rounded_scores_match_torch_and_keep_the_lower_index_on_ties():
+    # Index scores kept in BF16 (DeepSeek V4 技术架构深度解析, 三、FP4量化): the
+    # oracle rounds its double scores to bf16, ties to even.  Checked against
+    # PyTorch's bfloat16 conversion (of the float32 value: for random scores
+    # the intermediate float rounding never lands on a bf16 midpoint), the
+    # half-ulp bound, and the selection's index rule on the ties it creates.
+    import torch
+    B, Tq, HI, dI, N, m = 1, 3, 4, 16, 300, 4
+    rng = np.random.default_rng(12)
+    q = rng.standard_normal((B, Tq, HI, dI))
+    K = rng.standard_normal((B, N, dI))
+    w = rng.uniform(0, 1, (B, Tq, HI)).astype(np.float32)
+    qpos0 = np.array([4 * N])
+    s, nv = oracle.index_scores(q, w, K, oracle.F64, B, Tq, HI, dI, N, qpos0, m)
+    r, nv2 = oracle.index_scores(q, w, K, oracle.F64, B, Tq, HI, dI, N, qpos0, m, score_bf16=True)
+    assert (nv == nv2).all()
+    fin = np.isfinite(s)
+    assert (np.isneginf(r) == ~fin).all()
+    ref = torch.from_numpy(s[fin].astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(r[fin], ref)
+    half_ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(r[fin]), 1e-300))) - 8)   # 8 bits
+    assert (np.abs(r[fin] - s[fin]) <= half_ulp).all()
+    # ties: a row whose scores share few bf16 values picks the lowest indices
+    t = np.array([[1.0, 1.0039, 1.0, 0.5, 1.0078125, 1.0, 1.0]])    # 1.0039 -> 1.0 in bf16
+    tr = oracle.round_scores_bf16(t)
+    assert tr[0, 1] == 1.0 and tr[0, 4] == 1.0078125
+    idx = oracle.topk(tr, np.array([7], np.int32), 3)
+    assert idx[0].tolist() == [4, 0, 1]
+
+
 def test_worked_example_from_the_pages():
     g = json.load(open(os.path.join(GOLD, "worked_example_select.json")))
     s = np.array([g["scores"]], np.float64)
