@@ -80,6 +80,10 @@ typedef enum {
     LAC_E4M3 = 3
 } lac_dtype;
 
+/* Flag for the dtype of indexer_topk: round every score to bf16 before the
+ * selection (see indexer_topk). */
+#define LAC_SCORE_BF16 0x100
+
 /* Largest batch the position arrays may describe. */
 #define LAC_MAX_BATCH 128
 
@@ -198,6 +202,12 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
  *               -inf in padded slots); may be NULL
  *   workspace   >= indexer_topk_workspace_size(B, Tq, N, k) bytes
+ * dtype | LAC_SCORE_BF16: every score is rounded to the nearest bf16 value
+ * (ties to even) once it is summed, and the selection runs on the rounded
+ * scores with the same order (score descending, index ascending), so equal
+ * rounded scores go to the lower index; topk_score returns the rounded
+ * scores.  "DeepSeek V4 技术架构深度解析" (section "三、FP4量化", its
+ * table of the quantisation scheme) keeps the index scores in BF16.
  * LAC_BF16, LAC_KV_E4M3_ROPE_BF16 and LAC_E4M3 need H_I in {32, 64, 128} and
  * d_I in {64, 128} (MFMA tiles); LAC_F32 needs H_I * d_I <= 8192.
  * 1 <= k <= 8192.

@@ -23,10 +23,12 @@ __all__ = [
     "indexer_topk_noalloc",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
-    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "KERNELS", "CallList",
+    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "LAC_SCORE_BF16", "KERNELS",
+    "CallList",
 ]
 
 LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3 = 0, 1, 2, 3
+LAC_SCORE_BF16 = 0x100      # dtype flag of indexer_topk: scores rounded to bf16
 KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4,
            "project": 5}
 STATUS = {0: "LAC_OK", 1: "LAC_ERR_INVALID", 2: "LAC_ERR_UNSUPPORTED", 3: "LAC_ERR_WORKSPACE",
@@ -264,13 +266,14 @@ def _indexer_dtype(q_idx, k_idx):
 
 
 def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
-                 workspace=None, stream=None):
+                 workspace=None, stream=None, score_bf16=False):
     """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I]
     (the dtype of q_idx, or uint8 E4M3 codes with bf16 or uint8 E4M3 q_idx).
+    score_bf16: select on scores rounded to bf16 (include/lac.h).
     Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""
     B, Tq, HI, dI = q_idx.shape
     N = k_idx.shape[1]
-    dt = _indexer_dtype(q_idx, k_idx)
+    dt = _indexer_dtype(q_idx, k_idx) | (LAC_SCORE_BF16 if score_bf16 else 0)
     for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
         _need_dense(t, nm)
     if topk_idx is None:
@@ -283,13 +286,13 @@ def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=N
 
 
 def indexer_topk_noalloc(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
-                         stream=None):
+                         stream=None, score_bf16=False):
     """indexer_topk on the library's fixed per-device scratch (no workspace, no
     allocation in the call; see include/lac.h).  topk_idx must be given when
     the caller cannot allocate."""
     B, Tq, HI, dI = q_idx.shape
     N = k_idx.shape[1]
-    dt = _indexer_dtype(q_idx, k_idx)
+    dt = _indexer_dtype(q_idx, k_idx) | (LAC_SCORE_BF16 if score_bf16 else 0)
     for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
         _need_dense(t, nm)
     if topk_idx is None:

@@ -125,6 +125,8 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
                      const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                      float* topk_score, void* workspace, size_t workspace_bytes, bool fixed,
                      void* stream) {
+  const int round_bf16 = (dtype & LAC_SCORE_BF16) != 0;
+  dtype &= ~LAC_SCORE_BF16;
   if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16 && dtype != LAC_E4M3)
     return fail(LAC_ERR_UNSUPPORTED,
                 "%s: dtype must be LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 or LAC_E4M3", fn);
@@ -163,7 +165,7 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
     if (workspace_bytes < need)
       return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
   }
-  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype;
+  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype; a.round_bf16 = round_bf16;
   a.B = B; a.Tq = Tq; a.HI = H_I; a.dI = d_I; a.N = N; a.m = m; a.k = k;
   a.topk_idx = topk_idx; a.topk_score = topk_score;
   return launch_status(fn, lac::launch_indexer_topk(a, workspace, static_cast<hipStream_t>(stream)));

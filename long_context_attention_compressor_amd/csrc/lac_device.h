@@ -48,6 +48,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return u;
 }
 
+// x rounded to the nearest bf16 value (ties to even), as a float.
+__device__ __forceinline__ float round_bf16(float x) { return bf16_to_f32(pack_bf16x2(x, 0.f) & 0xffffu); }
+
 // Two floats as bf16 high parts plus bf16 low parts: hi = bf16(x), lo =
 // bf16(x - hi) (the difference is exact in fp32), so hi + lo carries about 16
 // significant bits of x.

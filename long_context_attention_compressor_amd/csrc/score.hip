@@ -66,6 +66,7 @@ struct ScoreArgs {
   uint32_t* tile_ctr;     // [R, 16 * 32] zeroed tile counters (dynamic schedule) or null
   int n_static;           // dynamic schedule: strided tiles per wave before the counters
   int n_groups;           // dynamic schedule: counters per row (<= 16)
+  int round_bf16;         // scores rounded to bf16 (ties to even) before they are stored
   Positions qpos;
 };
 
@@ -89,6 +90,7 @@ __global__ void __launch_bounds__(256) score_f32_kernel(ScoreArgs a) {
     for (int c = 0; c < a.dI; ++c) dot = fmaf(sq[h * a.dI + c], kr[c], dot);
     s = fmaf(sq[a.HI * a.dI + h], fmaxf(dot, 0.f), s);
   }
+  if (a.round_bf16) s = round_bf16(s);
   a.scores[row * a.Np + j] = s;
   if (a.hist) atomicAdd(&a.hist[(int64_t)row * kHistBins + (score_key(s) >> 20)], 1u);
 }
@@ -302,6 +304,8 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
           part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], relu(acc[v]), part);
       }
       part += __shfl_xor(part, 32);
+      const float pr = round_bf16(part);
+      part = a.round_bf16 ? pr : part;
       const bool live = hf == 0 && j < nv_row[qi];
       if (live) a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
       if (do_hist) hist_add(lhist, live, score_key(part) >> 20);
@@ -541,6 +545,8 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
           part = fmaf(sw[rr][ht * 32 + 8 * (v >> 2) + 4 * hf + (v & 3)], relu(acc[v]), part);
       }
       part += __shfl_xor(part, 32);
+      const float pr = round_bf16(part);
+      part = a.round_bf16 ? pr : part;
       const int off = hf == 0 ? (int)j * 4 : 0x7fffffff;
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[qi], off, 0, 2);   // nt
     }
@@ -574,6 +580,7 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
   sa.B = a.B; sa.Tq = a.Tq; sa.HI = a.HI; sa.dI = a.dI; sa.N = a.N; sa.m = a.m;
   sa.Np = sb.Np; sa.qpos = a.qpos; sa.hist = sb.hist;
   sa.tile_ctr = sb.tile_ctr;
+  sa.round_bf16 = a.round_bf16;
   {
     TimedLaunch tl(kKernelIndexerScore, st);
     if (a.fmt == kF32) {

@@ -91,6 +91,40 @@ def check_topk(gpu_idx: np.ndarray, o_idx: np.ndarray, o_scores: np.ndarray, nvi
     return same_rows
 
 
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (the smallest normal spacing below 2^-126)."""
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def check_topk_bf16(gpu_idx, gpu_score, o_idx, o_rounded, nvis, k):
+    """Selection on bf16-rounded scores (LAC_SCORE_BF16).  The GPU rounds its
+    fp32 sum, the oracle its double score, so a score can land one bf16 step
+    apart; rows must then agree except for indices whose oracle score lies
+    within one step of the k-th, and every returned score within one step of
+    the oracle's rounded score.  Returns the rows whose sets are identical."""
+    same_rows = []
+    for rr in range(gpu_idx.shape[0]):
+        nv = int(nvis[rr])
+        keff = min(k, nv)
+        g = gpu_idx[rr]
+        assert (g[keff:] == -1).all(), f"row {rr}: padding"
+        gs = g[:keff]
+        assert len(set(gs.tolist())) == keff, f"row {rr}: duplicates"
+        assert ((gs >= 0) & (gs < nv)).all(), f"row {rr}: invisible index"
+        s = o_rounded[rr, :nv]
+        assert (np.abs(gpu_score[rr, :keff] - s[gs]) <= bf16_ulp(s[gs])).all(), \
+            f"row {rr}: returned scores off by more than one bf16 step"
+        diff = set(gs.tolist()) ^ set(o_idx[rr, :keff].tolist())
+        if diff:
+            sk = np.sort(s)[::-1][keff - 1]
+            for j in diff:
+                assert abs(s[j] - sk) <= bf16_ulp(sk), f"row {rr}: index {j} score {s[j]} vs k-th {sk}"
+        else:
+            same_rows.append(rr)
+    return same_rows
+
+
 def check_attention(gpu: np.ndarray, ref: np.ndarray, what=""):
     """gpu, ref: [rows, H, D] float64."""
     num = np.abs(gpu - ref).max(axis=-1)

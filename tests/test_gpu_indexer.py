@@ -10,7 +10,7 @@ import torch
 import long_context_attention_compressor_amd as lac
 import oracle
 import synth
-from parity import check_topk, host
+from parity import check_topk, check_topk_bf16, host
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -203,3 +203,49 @@ def test_e4m3_queries_head_and_dim_variants(HI, dI):
 @pytest.mark.parametrize("HI,dI", [(32, 64), (128, 128)])
 def test_e4m3_queries_prefill_head_and_dim_variants(HI, dI):
     _run(1, 17, HI, dI, 700, 4, 64, [2790], "mixed", 36 + HI + dI, kfmt="mixed")
+
+
+# Scores rounded to bf16 before the selection (LAC_SCORE_BF16): every path.
+def _run_bf16(B, Tq, HI, dI, N, m, k, qpos, fmt, seed, kfmt=None, w_zero=False):
+    kfmt = fmt if kfmt is None else kfmt
+    print(f"indexer bf16 scores B={B} Tq={Tq} HI={HI} dI={dI} N={N} k={k} {fmt}/{kfmt}", flush=True)
+    q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI)), fmt)
+    K = synth.store(synth.normal(seed, "KI", (B, N, dI)), kfmt)
+    w = synth.uniform(seed, "w", (B, Tq, HI))
+    if w_zero:
+        w.zero_()
+    score = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    idx = lac.indexer_topk(q.to(DEV), w.to(DEV), K.to(DEV), m=m, k=k, q_pos0=qpos,
+                           topk_score=score, score_bf16=True)
+    torch.cuda.synchronize()
+    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.DTYPE_CODES[fmt], B, Tq, HI, dI,
+                                N, qpos, m, k_dtype=synth.DTYPE_CODES[kfmt], score_bf16=True)
+    o_idx = oracle.topk(s, nv, k)
+    g_idx = idx.cpu().numpy().reshape(B * Tq, k)
+    g_sc = score.cpu().numpy().reshape(B * Tq, k).astype(np.float64)
+    return check_topk_bf16(g_idx, g_sc, o_idx, s, nv, k)
+
+
+def test_bf16_scores_decode_split_path():
+    _run_bf16(2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], "bf16", 41)
+
+
+def test_bf16_scores_decode_prefix_path():
+    _run_bf16(4, 1, 64, 128, 5003, 4, 512, [4 * 5003 + 1, 4 * 5003, 4 * 3000 + 3, 40000], "bf16", 42)
+
+
+def test_bf16_scores_chunked_prefill():
+    _run_bf16(1, 40, 64, 128, 5010, 4, 300, [20000], "bf16", 43)
+
+
+def test_bf16_scores_f32_inputs():
+    _run_bf16(1, 256, 4, 32, 64, 4, 16, [0], "f32", 44)
+
+
+def test_bf16_scores_e4m3_queries_split_path():
+    _run_bf16(2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], "mixed", 45,
+              kfmt="mixed")
+
+
+def test_bf16_scores_all_tied_take_the_lowest_indices():
+    _run_bf16(2, 1, 32, 64, 30000, 4, 100, [4 * 30000, 4 * 30000], "bf16", 46, w_zero=True)
