@@ -23,7 +23,7 @@ import subprocess
 
 import numpy as np
 
-F32, BF16, MIXED, F64 = 0, 1, 2, 3
+F32, BF16, MIXED, F64, MXFP4 = 0, 1, 2, 3, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lac_oracle.c")
@@ -80,6 +80,10 @@ def _load():
     lib.lo_index_scores2.argtypes = [vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, i32, vp,
                                      i32, vp, vp]
     lib.lo_index_scores2.restype = i32
+    lib.lo_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.lo_e2m1_decode.restype = dbl
+    lib.lo_e8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.lo_e8m0_decode.restype = dbl
     lib.lo_round_scores_bf16.argtypes = [vp, ctypes.c_int64]
     lib.lo_round_scores_bf16.restype = i32
     lib.lo_topk.argtypes = [vp, i32, i32, vp, i32, vp]
@@ -249,6 +253,18 @@ def index_scores(q, w, K, dtype, B, Tq, HI, dI, N, qpos0, m, rows=None, k_dtype=
     if score_bf16:
         _load().lo_round_scores_bf16(_p(scores), scores.size)
     return scores, nvis
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """E2M1 codes (0..15) -> float64."""
+    f = _load().lo_e2m1_decode
+    return np.array([f(int(c)) for c in np.ravel(codes)], np.float64).reshape(np.shape(codes))
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """E8M0 scale bytes -> float64 powers of two (255 -> NaN)."""
+    f = _load().lo_e8m0_decode
+    return np.array([f(int(c)) for c in np.ravel(codes)], np.float64).reshape(np.shape(codes))
 
 
 def round_scores_bf16(scores):

@@ -39,6 +39,9 @@
  *   2  mixed rows: D-r bytes of FP8 E4M3 (the non-rotated dims) followed by
  *      r bfloat16 values (the rotated dims), (D-r) + 2r bytes per row
  *   3  float64 rows of D values (used only by the self-tests)
+ *   4  MXFP4 rows (indexer keys): D/2 bytes of E2M1 codes, element 2i in the
+ *      low nibble of byte i and 2i+1 in the high nibble, then D/32 E8M0
+ *      scale bytes, one per block of 32 consecutive elements
  */
 #include <math.h>
 #include <stdint.h>
@@ -52,6 +55,7 @@
 #define LO_BF16 1
 #define LO_MIXED 2
 #define LO_F64 3
+#define LO_MXFP4 4
 
 /* ------------------------------------------------------------------------ */
 /* Number formats ([P4] bit-layout table: BF16 = 8 exponent + 7 mantissa     */
@@ -122,12 +126,30 @@ uint8_t lo_e4m3_encode(double v) {
     return s | (uint8_t)(((E + 7) << 3) | ((int)q - 8));
 }
 
+/* E2M1 ([P4] bit-layout table: FP4 = 2 exponent bits + 1 mantissa bit).
+ * Reading: exponent bias 1, E = 0 subnormal (m * 0.5), no infinities or NaN,
+ * so the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4 and 6. */
+double lo_e2m1_decode(uint8_t nibble) {
+    int s = (nibble >> 3) & 1, e = (nibble >> 1) & 3, m = nibble & 1;
+    double v = e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+    return s ? -v : v;
+}
+
+/* E8M0 block scale ([P2] "FP4 Quantization-Aware Training": FP4 block
+ * scales fold into FP8 on dequantisation).  Reading: a power of two
+ * 2^(b - 127), b = 255 NaN. */
+double lo_e8m0_decode(uint8_t b) {
+    if (b == 255) return NAN;
+    return ldexp(1.0, (int)b - 127);
+}
+
 static int64_t row_bytes(int dtype, int D, int r) {
     switch (dtype) {
     case LO_F32: return 4LL * D;
     case LO_BF16: return 2LL * D;
     case LO_MIXED: return (int64_t)(D - r) + 2LL * r;
     case LO_F64: return 8LL * D;
+    case LO_MXFP4: return (int64_t)D / 2 + D / 32;
     }
     return -1;
 }
@@ -152,6 +174,12 @@ static void decode_row(const uint8_t* p, int dtype, int D, int r, double* out) {
         break;
     case LO_F64:
         memcpy(out, p, 8 * (size_t)D);
+        break;
+    case LO_MXFP4:
+        for (c = 0; c < D; ++c) {
+            uint8_t code = (uint8_t)((p[c / 2] >> (4 * (c & 1))) & 15);
+            out[c] = lo_e2m1_decode(code) * lo_e8m0_decode(p[D / 2 + c / 32]);
+        }
         break;
     }
 }
@@ -358,14 +386,16 @@ static int64_t n_visible(int64_t t, int N, int m) {
 /* rows: n_rows pairs (b, i).  scores: [n_rows, N]; entries not visible are
  * set to -inf.  nvis (optional): [n_rows].  q is stored in dtype, K in
  * k_dtype (the same formats; LO_MIXED with no rotated dims is E4M3 codes,
- * for queries as well as keys). */
+ * for queries as well as keys; keys may also be LO_MXFP4). */
 int lo_index_scores2(const void* q, int dtype, const float* w, const void* K, int k_dtype,
                      int B, int Tq, int HI, int dI, int N, const int64_t* qpos0, int m,
                      const int32_t* rows, int n_rows, double* scores, int32_t* nvis) {
     (void)B;
     if (dtype != LO_F32 && dtype != LO_BF16 && dtype != LO_F64 && dtype != LO_MIXED) return 2;
-    if (k_dtype != LO_F32 && k_dtype != LO_BF16 && k_dtype != LO_F64 && k_dtype != LO_MIXED)
+    if (k_dtype != LO_F32 && k_dtype != LO_BF16 && k_dtype != LO_F64 && k_dtype != LO_MIXED &&
+        k_dtype != LO_MXFP4)
         return 2;
+    if (k_dtype == LO_MXFP4 && dI % 32) return 3;
     if (dI < 1 || dI > 1024) return 3;
     int64_t rb = row_bytes(dtype, dI, 0), krb = row_bytes(k_dtype, dI, 0);
     double* qd = malloc(sizeof(double) * (size_t)n_rows * HI * dI);

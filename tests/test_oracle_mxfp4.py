@@ -1,0 +1,94 @@
+"""Pins of the oracle's MXFP4 indexer keys: E2M1 codes with E8M0 block
+scales (DeepSeek V4 技术架构深度解析, 三、FP4量化, bit-layout table: FP4 is E2M1,
+2 exponent bits and 1 mantissa bit; 深度解析 DeepSeek-V4, section "FP4
+Quantization-Aware Training": the indexer's QK path runs in FP4 and FP4 block
+scales fold losslessly into FP8 on dequantisation)."""
+import numpy as np
+import torch
+
+import oracle
+
+
+def _minifloat(code, e_bits, m_bits):
+    """IEEE-style value of a sign / e_bits / m_bits code (bias 2^(e_bits-1) - 1,
+    exponent 0 subnormal); infinities and NaNs are not modelled."""
+    bias = 2 ** (e_bits - 1) - 1
+    s = (code >> (e_bits + m_bits)) & 1
+    e = (code >> m_bits) & (2 ** e_bits - 1)
+    m = code & (2 ** m_bits - 1)
+    if e == 0:
+        v = (m / 2 ** m_bits) * 2.0 ** (1 - bias)
+    else:
+        v = (1 + m / 2 ** m_bits) * 2.0 ** (e - bias)
+    return -v if s else v
+
+
+def test_generic_minifloat_formula_matches_library_formats():
+    # the formula the E2M1 pin uses reproduces PyTorch's E4M3 (all finite
+    # codes) and bf16 (normal and subnormal codes) decoders
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for c in range(256):
+        if c & 0x7F == 0x7F:
+            continue
+        assert _minifloat(c, 4, 3) == e4[c]
+    bf = torch.arange(0, 65536, 97, dtype=torch.int32).to(torch.int16).view(torch.bfloat16).double().numpy()
+    for c, v in zip(range(0, 65536, 97), bf):
+        if (c >> 7) & 0xFF == 0xFF:
+            continue
+        assert _minifloat(c, 8, 7) == v
+
+
+def test_e2m1_decode_follows_the_two_exponent_one_mantissa_layout():
+    got = oracle.e2m1_decode(np.arange(16))
+    want = np.array([_minifloat(c, 2, 1) for c in range(16)])
+    assert np.array_equal(got, want)
+    assert got[:8].tolist() == sorted(got[:8].tolist())           # magnitudes ascending
+    assert np.array_equal(got[8:], -got[:8])                       # sign bit
+
+
+def test_e8m0_decode_matches_torch():
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    o = oracle.e8m0_decode(np.arange(256))
+    assert np.array_equal(np.isnan(o), np.isnan(t))
+    assert np.array_equal(o[~np.isnan(o)], t[~np.isnan(t)])
+
+
+def test_scaled_e2m1_is_exact_in_e4m3_over_the_lossless_range():
+    # the pages' claim: FP4 values with their block scale are FP8 values.
+    # Every E2M1 value times 2^k, -8 <= k <= 6, survives PyTorch's E4M3
+    # conversion unchanged.
+    vals = oracle.e2m1_decode(np.arange(16))
+    for k in range(-8, 7):
+        x = vals * 2.0 ** k
+        back = torch.from_numpy(x).to(torch.float8_e4m3fn).double().numpy()
+        assert np.array_equal(back, x), k
+
+
+def _decode_rows(rows, d):
+    """Test-side MXFP4 row decode from the codes' definition (header layout)."""
+    n = rows.shape[0]
+    out = np.empty((n, d))
+    for i in range(n):
+        for c in range(d):
+            code = (rows[i, c // 2] >> (4 * (c & 1))) & 15
+            out[i, c] = _minifloat(int(code), 2, 1) * 2.0 ** (int(rows[i, d // 2 + c // 32]) - 127)
+    return out
+
+
+def test_scores_with_mxfp4_keys_use_the_decoded_key_values():
+    B, Tq, HI, dI, N, m = 1, 3, 4, 64, 20, 4
+    rng = np.random.default_rng(21)
+    keys = rng.integers(0, 256, (B, N, dI // 2 + dI // 32), dtype=np.uint8)
+    keys[..., dI // 2:] = rng.integers(122, 132, (B, N, dI // 32))
+    q = oracle.bf16_encode(rng.standard_normal((B, Tq, HI, dI)))
+    w = rng.uniform(0, 1, (B, Tq, HI)).astype(np.float32)
+    qpos0 = np.array([4 * N + 3])
+    s, nv = oracle.index_scores(q, w, keys, oracle.BF16, B, Tq, HI, dI, N, qpos0, m,
+                                k_dtype=oracle.MXFP4)
+    kd = _decode_rows(keys[0], dI)[None]
+    qd = oracle.bf16_decode(q)
+    dots = np.einsum("bthc,bjc->btjh", qd, kd)
+    ref = (np.maximum(dots, 0.0) * w.astype(np.float64)[:, :, None, :]).sum(-1)
+    for i in range(Tq):
+        assert nv[i] == min(N, (qpos0[0] + i) // m)
+        assert np.allclose(s[i, : nv[i]], ref[0, i, : nv[i]], rtol=1e-13, atol=1e-12)
