@@ -143,6 +143,51 @@ double lo_e8m0_decode(uint8_t b) {
     return ldexp(1.0, (int)b - 127);
 }
 
+/* Nearest E2M1 magnitude code of |x| (ties to the even code, i.e. mantissa
+ * bit 0), saturating at 6: the grid is 0, 0.5, 1, 1.5, 2, 3, 4, 6. */
+static uint8_t e2m1_code(double a) {
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    int c;
+    if (a >= 6.0) return 7;
+    for (c = 0; c < 7; ++c) {
+        double mid = 0.5 * (grid[c] + grid[c + 1]);
+        if (a < mid) return (uint8_t)c;
+        if (a == mid) return (uint8_t)((c & 1) ? c + 1 : c);   /* even code */
+    }
+    return 7;
+}
+
+/* One MXFP4 row from D values (D a multiple of 32).  Reading of the
+ * quantisation (the pages give the format, not the rule): each block of 32
+ * takes the shared exponent e = floor(log2(max |v|)) - 2 (2 is E2M1's largest
+ * exponent, so the block's largest value lands in [4, 8)), clamped to
+ * [-127, 127], stored as the E8M0 byte e + 127 (127 for an all-zero block);
+ * every value v becomes the nearest E2M1 code of v / 2^e (ties to even,
+ * saturating at 6), with the sign bit set for v < 0. */
+static void mxfp4_encode_row(const double* v, int D, uint8_t* p) {
+    int blk, c;
+    memset(p, 0, (size_t)D / 2);
+    for (blk = 0; blk < D / 32; ++blk) {
+        double amax = 0.0;
+        for (c = 0; c < 32; ++c) amax = fmax(amax, fabs(v[32 * blk + c]));
+        int e = 0;
+        if (amax > 0.0) {
+            int ex;
+            frexp(amax, &ex);                  /* amax = f * 2^ex, 0.5 <= f < 1 */
+            e = ex - 1 - 2;
+            if (e < -127) e = -127;
+            if (e > 127) e = 127;
+        }
+        p[D / 2 + blk] = (uint8_t)(e + 127);
+        for (c = 0; c < 32; ++c) {
+            double x = ldexp(v[32 * blk + c], -e);
+            uint8_t code = (uint8_t)(e2m1_code(fabs(x)) | (x < 0.0 ? 8 : 0));
+            int i = 32 * blk + c;
+            p[i / 2] |= (uint8_t)(code << (4 * (i & 1)));
+        }
+    }
+}
+
 static int64_t row_bytes(int dtype, int D, int r) {
     switch (dtype) {
     case LO_F32: return 4LL * D;
@@ -203,6 +248,9 @@ static void encode_row(const double* v, int dtype, int D, int r, uint8_t* p) {
         break;
     case LO_F64:
         memcpy(p, v, 8 * (size_t)D);
+        break;
+    case LO_MXFP4:
+        mxfp4_encode_row(v, D, p);
         break;
     }
 }

@@ -92,3 +92,51 @@ def test_scores_with_mxfp4_keys_use_the_decoded_key_values():
     for i in range(Tq):
         assert nv[i] == min(N, (qpos0[0] + i) // m)
         assert np.allclose(s[i, : nv[i]], ref[0, i, : nv[i]], rtol=1e-13, atol=1e-12)
+
+
+def test_mxfp4_encode_round_trips_rows_whose_blocks_reach_four():
+    # a block whose largest code is 4 or 6 times 2^k has shared exponent k,
+    # so encoding its decoded values gives the same bytes back
+    rng = np.random.default_rng(22)
+    d, n = 128, 40
+    codes = rng.integers(0, 16, (n, d))
+    codes[codes == 8] = 0                               # -0 decodes to 0.0
+    for i in range(n):
+        for blk in range(d // 32):
+            codes[i, 32 * blk + rng.integers(0, 32)] = rng.choice([6, 7, 14, 15])
+    rows = np.zeros((n, d // 2 + d // 32), np.uint8)
+    for c in range(d):
+        rows[:, c // 2] |= (codes[:, c] << (4 * (c & 1))).astype(np.uint8)
+    rows[:, d // 2:] = rng.integers(100, 150, (n, d // 32))
+    vals = oracle.decode_rows(rows, oracle.MXFP4, d, 0)
+    assert np.array_equal(oracle.encode_rows(vals, oracle.MXFP4, 0), rows)
+
+
+def test_mxfp4_encode_rounds_to_nearest_even_and_saturates():
+    # block maximum 7 -> shared exponent 0; the rest are ties of the E2M1
+    # grid (0, 0.5, 1, 1.5, 2, 3, 4, 6), which go to the even code
+    v = np.zeros((1, 32))
+    v[0, :10] = [7.0, 2.5, 0.25, 0.75, 5.0, -1.25, 1.75, 3.5, -0.1, 6.5]
+    dec = oracle.decode_rows(oracle.encode_rows(v, oracle.MXFP4, 0), oracle.MXFP4, 32, 0)
+    assert dec[0, :10].tolist() == [6.0, 2.0, 0.0, 1.0, 4.0, -1.0, 2.0, 4.0, -0.0, 6.0]
+    assert oracle.encode_rows(v, oracle.MXFP4, 0)[0, 16] == 127
+    # an all-zero block keeps scale byte 127; a block of 0.3 gets 2^-4 (0.3 = 4.8 x 2^-4)
+    z = np.zeros((1, 64))
+    z[0, 32:] = 0.3
+    b = oracle.encode_rows(z, oracle.MXFP4, 0)
+    assert b[0, 32:].tolist() == [127, 123]
+    assert np.allclose(oracle.decode_rows(b, oracle.MXFP4, 64, 0)[0, 32:], 0.25)
+
+
+def test_mxfp4_encode_error_is_within_half_a_grid_step():
+    rng = np.random.default_rng(23)
+    v = rng.standard_normal((50, 128)) * np.exp(rng.uniform(-4, 4, (50, 1)))
+    b = oracle.encode_rows(v, oracle.MXFP4, 0)
+    dec = oracle.decode_rows(b, oracle.MXFP4, 128, 0)
+    S = 2.0 ** (b[:, 64:].astype(np.int64) - 127)
+    S = np.repeat(S, 32, axis=1)
+    x = np.abs(v) / S
+    assert (x < 8).all() and (np.abs(v).reshape(50, 4, 32).max(-1) / S[:, ::32] >= 4).all()
+    gap = np.where(x < 2, 0.5, np.where(x < 4, 1.0, 2.0))
+    bound = np.where(x <= 6, 0.5 * gap * S, np.abs(v) - 6 * S)
+    assert (np.abs(dec - v) <= bound * (1 + 1e-12)).all()
