@@ -12,7 +12,8 @@ set in the 256 MB Infinity Cache.
 
 Other workloads (--workload): pair_decode_1m_e4m3_indexer (the same step with
 the indexer keys stored as E4M3, one byte per dim), pair_decode_1m_fp8_indexer
-(E4M3 indexer queries and keys on the FP8 matrix cores), csa_decode_128k (32
+(E4M3 indexer queries and keys on the FP8 matrix cores),
+pair_decode_1m_mxfp4_indexer (MXFP4 indexer keys), csa_decode_128k (32
 sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
 hca_prefill_8k (8192 tokens; TFLOP/s), bulk_compress_1m and
@@ -151,26 +152,32 @@ class PairDecode:
     def bytes_per_step(self):
         c = self.c
         row = c["D"] - c["r"] + 2 * c["r"]
-        kb = 1 if self.ki_fmt == "mixed" else 2                                   # key bytes/dim
+        kb = self.key_bytes_per_dim()
         qb = 1 if self.qi_fmt == "mixed" else 2                                   # query bytes/dim
         per_seq = (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * qb + c["HI"] * 4  # indexer
                    + c["k"] * row + c["Nh"] * row + 2 * c["W"] * row               # gathers
                    + 2 * c["H"] * c["D"] * 2 * 2)                                   # q, out
         compress = (((c["m"] + self.overlap) * c["D"] + c["m"] * c["dI"] + c["m_hca"] * c["D"])
-                    * 2 * 2 + 2 * row + c["dI"] * kb)
+                    * 2 * 2 + 2 * row + int(c["dI"] * kb))
         return self.B * (per_seq + compress)
+
+    def key_bytes_per_dim(self):
+        """Indexer key bytes per dim: bf16 2, E4M3 1, MXFP4 (codes + scales) 17/32."""
+        return {"bf16": 2, "mixed": 1, "mxfp4": 17 / 32}[self.ki_fmt]
 
     def indexer_bytes_per_launch(self):
         c = self.c
-        kb = 1 if self.ki_fmt == "mixed" else 2
+        kb = self.key_bytes_per_dim()
         qb = 1 if self.qi_fmt == "mixed" else 2
-        return self.B * (c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * qb + c["HI"] * 4)
+        return self.B * int(c["N"] * c["dI"] * kb + c["HI"] * c["dI"] * qb + c["HI"] * 4)
 
     def config(self):
         c = self.c
         return {"workload": self.name, "batch": self.B, "ctx": self.ctx, "topk": c["k"],
                 "window": c["W"], "heads": c["H"], "kv_dim": c["D"], "rope_dims": c["r"],
                 "indexer": (f"{c['HI']}x{c['dI']} bf16" if self.ki_fmt == "bf16" else
+                            f"{c['HI']}x{c['dI']}, bf16 queries, mxfp4 keys (e2m1 + e8m0 per 32)"
+                            if self.ki_fmt == "mxfp4" else
                             f"{c['HI']}x{c['dI']}, bf16 queries, e4m3 keys" if self.qi_fmt == "bf16"
                             else f"{c['HI']}x{c['dI']}, e4m3 queries and keys (fp8 mfma)"),
                 "csa_entries": c["N"],
@@ -237,6 +244,13 @@ class PairDecodeFp8Indexer(PairDecode):
     name = "pair_decode_1m_fp8_indexer"
     ki_fmt = "mixed"
     qi_fmt = "mixed"
+
+
+class PairDecodeMxfp4Indexer(PairDecode):
+    """pair_decode_1m with MXFP4 indexer keys (E2M1 codes and an E8M0 scale
+    per 32 dims, 68 bytes per key); the step quantises the newest key."""
+    name = "pair_decode_1m_mxfp4_indexer"
+    ki_fmt = "mxfp4"
 
 
 class PairDecodeRmsNorm(PairDecode):
@@ -627,6 +641,7 @@ class BulkCompress128K(BulkCompress1M):
 
 
 WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeFp8Indexer,
+                                  PairDecodeMxfp4Indexer,
                                   PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode,
                                   BulkCompress1M, BulkCompress128K)}

@@ -37,6 +37,13 @@
  *             nearest even and saturate to +-448, unscaled.
  *   LAC_E4M3  FP8 E4M3 codes ("fn" variant as above), one byte per value,
  *             unscaled (indexer queries and keys only).
+ *   LAC_MXFP4 indexer keys as FP4 E2M1 codes with block scales: a row of d
+ *             values is d/2 bytes of codes (value 2i in the low nibble of
+ *             byte i, 2i+1 in the high nibble; sign, 2 exponent bits with
+ *             bias 1, 1 mantissa bit, exponent 0 subnormal: magnitudes 0,
+ *             0.5, 1, 1.5, 2, 3, 4, 6) followed by d/32 E8M0 scale bytes,
+ *             byte b scaling its block of 32 values by 2^(b - 127) (255 is
+ *             NaN).  d/2 + d/32 bytes per row (68 at d = 128).
  *   The mixed format follows the KV-cache storage of "DeepSeek V4 技术架构深度
  *   解析" (aicoding.csdn.net), section "KV Cache优化细节", and its bit-layout
  *   table in section "三、FP4量化".
@@ -77,7 +84,8 @@ typedef enum {
     LAC_F32 = 0,
     LAC_BF16 = 1,
     LAC_KV_E4M3_ROPE_BF16 = 2,
-    LAC_E4M3 = 3
+    LAC_E4M3 = 3,
+    LAC_MXFP4 = 4
 } lac_dtype;
 
 /* Flag for the dtype of indexer_topk: round every score to bf16 before the
@@ -100,8 +108,17 @@ typedef enum {
  *   raw_kv   [B, kv_batch_stride rows, D] in in_dtype (LAC_F32 | LAC_BF16);
  *            rows 0..T-1 of each batch are read
  *   logits   [B, logit_batch_stride rows, D] in in_dtype
- *   out      [B, out_batch_stride rows, row] in out_dtype (any lac_dtype);
- *            rows 0..T/m-1 of each batch are written
+ *   out      [B, out_batch_stride rows, row] in out_dtype (LAC_F32,
+ *            LAC_BF16, LAC_KV_E4M3_ROPE_BF16 or, for indexer keys,
+ *            LAC_MXFP4); rows 0..T/m-1 of each batch are written.
+ *            LAC_MXFP4 (rope_dims = 0, D a multiple of 32): each block of 32
+ *            channels of an entry takes the shared exponent
+ *            e = floor(log2 max|v|) - 2 (clamped to [-127, 127]; 0 for an
+ *            all-zero block), stored as the scale byte e + 127, and each
+ *            value the nearest E2M1 code of v / 2^e, ties to even,
+ *            saturating at 6, sign bit for v < 0.  Reading: the pages give
+ *            the FP4 format and its block scales, not the rounding rule.
+ *            An MXFP4 out pointer needs only 4-byte alignment.
  *   m        block size, 1..256 (4 for CSA)
  *   pos0     host [B], position of raw row 0; a multiple of m
  * D must be a multiple of 8, rope_dims a multiple of 8 with rope_dims <= min(D, 128).
@@ -197,7 +214,12 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  *               exactly to bf16, and scored as above.  With LAC_E4M3 both
  *               q_idx and k_idx are E4M3 codes of d_I bytes per row and the
  *               products run on the FP8 matrix cores (each product exact,
- *               sums in fp32).
+ *               sums in fp32).  With LAC_MXFP4, q_idx is bf16 and k_idx
+ *               holds MXFP4 rows (d_I/2 + d_I/32 bytes each): the FP4 QK
+ *               path of [P2] (CSA Step 2 Select; "FP4 Quantization-Aware
+ *               Training": FP4 block scales fold losslessly into FP8).
+ *               Each key value E2M1 x 2^(b - 127) is formed exactly in bf16
+ *               (which holds every such FP8 value) and scored as above.
  *   topk_idx    [B, Tq, k] int32, output
  *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
  *               -inf in padded slots); may be NULL
@@ -208,7 +230,7 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  * rounded scores go to the lower index; topk_score returns the rounded
  * scores.  "DeepSeek V4 技术架构深度解析" (section "三、FP4量化", its
  * table of the quantisation scheme) keeps the index scores in BF16.
- * LAC_BF16, LAC_KV_E4M3_ROPE_BF16 and LAC_E4M3 need H_I in {32, 64, 128} and
+ * LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3 and LAC_MXFP4 need H_I in {32, 64, 128} and
  * d_I in {64, 128} (MFMA tiles); LAC_F32 needs H_I * d_I <= 8192.
  * 1 <= k <= 8192.
  */

@@ -23,11 +23,12 @@ __all__ = [
     "indexer_topk_noalloc",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
-    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "LAC_SCORE_BF16", "KERNELS",
+    "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "LAC_MXFP4", "LAC_SCORE_BF16",
+    "KERNELS",
     "CallList",
 ]
 
-LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3 = 0, 1, 2, 3
+LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3, LAC_MXFP4 = 0, 1, 2, 3, 4
 LAC_SCORE_BF16 = 0x100      # dtype flag of indexer_topk: scores rounded to bf16
 KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4,
            "project": 5}
@@ -197,13 +198,22 @@ def _norm_gain(gain, D, device):
     return gain
 
 
+def _out_fmt(out, D, rope_dims):
+    """Compressed-row format of `out`: uint8 rows of D/2 + D/32 bytes with no
+    rotated dims are MXFP4 (include/lac.h); other uint8 rows the mixed format."""
+    if out.dtype == torch.uint8 and rope_dims == 0 and D % 32 == 0 and \
+            out.shape[-1] == D // 2 + D // 32:
+        return LAC_MXFP4
+    return _fmt(out)
+
+
 def _compress(fn, fn_norm, raw_kv, logits, out, m, rope_dims, rope_theta, pos0, T, norm_gain,
               norm_eps, stream):
     B, _, D = raw_kv.shape
     T = raw_kv.shape[1] if T is None else T
     if logits.dtype != raw_kv.dtype:
         raise TypeError("raw_kv and logits must share a dtype")
-    args = [_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _fmt(out), B, T, D, m,
+    args = [_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _out_fmt(out, D, rope_dims), B, T, D, m,
             rope_dims, rope_theta, _positions(pos0, B), _rows(raw_kv, "raw_kv"),
             _rows(logits, "logits"), _rows(out, "out")]
     gain = _norm_gain(norm_gain, D, raw_kv.device)
@@ -235,7 +245,8 @@ def csa_compress(raw_kv, logits, out, m=4, rope_dims=64, rope_theta=10000.0, pos
         lead = max((min(overlap, max(0, int(pos[b]) if pos is not None else 0)) for b in range(B)),
                    default=0)
         T = rows - lead
-    _call(lib.csa_compress_overlap, (_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out), _fmt(out),
+    _call(lib.csa_compress_overlap, (_ptr(raw_kv), _ptr(logits), _fmt(raw_kv), _ptr(out),
+                                     _out_fmt(out, D, rope_dims),
                                      B, T, D, m, overlap, rope_dims, rope_theta, pos,
                                      _rows(raw_kv, "raw_kv"), _rows(logits, "logits"),
                                      _rows(out, "out"), _stream(stream)))
@@ -256,6 +267,10 @@ def indexer_topk_workspace_size(B, Tq, N, k) -> int:
 
 
 def _indexer_dtype(q_idx, k_idx):
+    dI = q_idx.shape[-1]
+    if k_idx.dtype == torch.uint8 and q_idx.dtype == torch.bfloat16 and \
+            k_idx.shape[-1] == dI // 2 + dI // 32 and dI % 32 == 0:
+        return LAC_MXFP4                       # MXFP4 key rows (include/lac.h)
     if q_idx.dtype == torch.uint8:
         if k_idx.dtype != torch.uint8:
             raise TypeError("E4M3 (uint8) q_idx needs E4M3 (uint8) k_idx")
@@ -268,7 +283,8 @@ def _indexer_dtype(q_idx, k_idx):
 def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
                  workspace=None, stream=None, score_bf16=False):
     """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I]
-    (the dtype of q_idx, or uint8 E4M3 codes with bf16 or uint8 E4M3 q_idx).
+    (the dtype of q_idx; uint8 E4M3 codes with bf16 or uint8 E4M3 q_idx; or
+    uint8 MXFP4 rows of d_I/2 + d_I/32 bytes with bf16 q_idx).
     score_bf16: select on scores rounded to bf16 (include/lac.h).
     Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""
     B, Tq, HI, dI = q_idx.shape

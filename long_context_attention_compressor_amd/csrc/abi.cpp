@@ -70,8 +70,10 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
                       int32_t overlap = 0) {
   if (in_dtype != LAC_F32 && in_dtype != LAC_BF16)
     return fail(LAC_ERR_UNSUPPORTED, "%s: in_dtype must be LAC_F32 or LAC_BF16", fn);
-  if (out_dtype < LAC_F32 || out_dtype > LAC_KV_E4M3_ROPE_BF16)
+  if ((out_dtype < LAC_F32 || out_dtype > LAC_KV_E4M3_ROPE_BF16) && out_dtype != LAC_MXFP4)
     return fail(LAC_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", fn, out_dtype);
+  if (out_dtype == LAC_MXFP4 && (rope_dims != 0 || D % 32))
+    return fail(LAC_ERR_UNSUPPORTED, "%s: MXFP4 output needs rope_dims = 0 and D a multiple of 32", fn);
   if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
   if (T < 0) return fail(LAC_ERR_INVALID, "%s: T = %d < 0", fn, T);
   if (m < 1 || m > 256) return fail(LAC_ERR_INVALID, "%s: m = %d outside [1, 256]", fn, m);
@@ -106,8 +108,11 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
   if (st) return st;
   if ((int64_t)B * N == 0) { g_err[0] = 0; return LAC_OK; }
   if (!raw_kv || !logits || !out) return fail(LAC_ERR_INVALID, "%s: null tensor pointer", fn);
-  if (!aligned(raw_kv, 16) || !aligned(logits, 16) || !aligned(out, 16))
-    return fail(LAC_ERR_INVALID, "%s: tensor pointers must be 16-byte aligned", fn);
+  // MXFP4 rows (D/2 + D/32 bytes, written as 4-byte code words and scale
+  // bytes) need only 4-byte alignment, so that a single row of a cache can
+  // be the output
+  if (!aligned(raw_kv, 16) || !aligned(logits, 16) || !aligned(out, out_dtype == LAC_MXFP4 ? 4 : 16))
+    return fail(LAC_ERR_INVALID, "%s: tensor pointers must be 16-byte aligned (4 for MXFP4 output)", fn);
   if (out_dtype == LAC_KV_E4M3_ROPE_BF16 && (out_bstride * (int64_t)(D + rope_dims)) % 8)
     return fail(LAC_ERR_INVALID, "%s: mixed-format batch stride must keep rows 8-byte aligned", fn);
   a.kv = raw_kv; a.logits = logits; a.out = out;
@@ -127,9 +132,10 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
                      void* stream) {
   const int round_bf16 = (dtype & LAC_SCORE_BF16) != 0;
   dtype &= ~LAC_SCORE_BF16;
-  if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16 && dtype != LAC_E4M3)
+  if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16 && dtype != LAC_E4M3 &&
+      dtype != LAC_MXFP4)
     return fail(LAC_ERR_UNSUPPORTED,
-                "%s: dtype must be LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16 or LAC_E4M3", fn);
+                "%s: dtype must be LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3 or LAC_MXFP4", fn);
   if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
   if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
   if (m < 1) return fail(LAC_ERR_INVALID, "%s: m = %d < 1", fn, m);

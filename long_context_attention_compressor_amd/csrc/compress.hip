@@ -239,6 +239,29 @@ __global__ void __launch_bounds__(512) compress_kernel(CompressArgs a) {
     uint4* p = reinterpret_cast<uint4*>(out + (orow * a.D + c0) * 2);
     *p = make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                     pack_bf16x2(o[6], o[7]));
+  } else if constexpr (OUT == kMXFP4) {
+    // MXFP4 (no rotated dims): the 4 threads of a 32-channel block are lanes
+    // 4k .. 4k+3 (GB is a multiple of 4), and share the block's exponent
+    // e = floor(log2 max|o|) - 2; each value becomes the nearest E2M1 code of
+    // o / 2^e (ties to even, saturating at 6), sign bit for o < 0.
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) amax = fmaxf(amax, fabsf(o[c]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int e = amax > 0.f ? min(127, max(-127, ilogbf(amax) - 2)) : 0;
+    uint32_t codes = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float x = ldexpf(o[c], -e);
+      const float ax = fabsf(x);
+      const uint32_t q = ax <= 0.25f ? 0u : ax < 0.75f ? 1u : ax <= 1.25f ? 2u : ax < 1.75f ? 3u
+                       : ax <= 2.5f ? 4u : ax < 3.5f ? 5u : ax <= 5.f ? 6u : 7u;
+      codes |= (q | (x < 0.f ? 8u : 0u)) << (4 * c);
+    }
+    uint8_t* rp = out + orow * (int64_t)(a.D / 2 + a.D / 32);
+    *reinterpret_cast<uint32_t*>(rp + c0 / 2) = codes;
+    if ((g & 3) == 0) rp[a.D / 2 + c0 / 32] = (uint8_t)(e + 127);
   } else {
     const int64_t rowb = (int64_t)a.D + a.r;
     uint8_t* rp = out + orow * rowb;
@@ -297,6 +320,7 @@ hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   int GB = G;
   if (a.norm_gain == nullptr)
     while ((GB * S > 256 || (few && GB > kFewGB)) && GB % 2 == 0) GB /= 2;
+  if (a.out_fmt == kMXFP4 && GB % 4) GB = 4;   // a 32-channel block's threads share one block
   if (GB * S > 512) {           // few channel groups and a long block: fewer splits
     while (GB * S > 512) S /= 2;
   }
@@ -317,10 +341,12 @@ hipError_t launch_compress(CompressArgs a, hipStream_t st) {
   if (a.in_fmt == kF32) {
     if (a.out_fmt == kF32) return launch<kF32, kF32>(a, grid, block, lds, st);
     if (a.out_fmt == kBF16) return launch<kF32, kBF16>(a, grid, block, lds, st);
+    if (a.out_fmt == kMXFP4) return launch<kF32, kMXFP4>(a, grid, block, lds, st);
     return launch<kF32, kMixed>(a, grid, block, lds, st);
   }
   if (a.out_fmt == kF32) return launch<kBF16, kF32>(a, grid, block, lds, st);
   if (a.out_fmt == kBF16) return launch<kBF16, kBF16>(a, grid, block, lds, st);
+  if (a.out_fmt == kMXFP4) return launch<kBF16, kMXFP4>(a, grid, block, lds, st);
   return launch<kBF16, kMixed>(a, grid, block, lds, st);
 }
 

@@ -27,7 +27,7 @@ __device__ __forceinline__ uint2 ld_stream8(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
-enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2, kE4M3 = 3 };
+enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2, kE4M3 = 3, kMXFP4 = 4 };
 
 // Per-batch positions passed by value (the library keeps nothing on the device).
 struct Positions {
@@ -46,6 +46,41 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   uint32_t u;
   __builtin_memcpy(&u, &b, 4);
   return u;
+}
+
+// Eight E2M1 codes (nibbles of `codes`, element j in bits 4j..4j+3) times
+// the E8M0 scale 2^(sc - 127) -> eight bf16, exact (E2M1: bias 1, exponent 0
+// subnormal; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6).  Scale bytes 1..254 go
+// through gfx950's scaled FP4 conversion (two codes of one byte per
+// instruction, the low nibble first; exact for these scales), the two
+// edge bytes (2^-127, NaN) through float arithmetic.
+__device__ __noinline__ uint4 e2m1x8_to_bf16x8_edge(uint32_t codes, uint32_t sc) {
+  const float scale = sc == 0u ? __uint_as_float(0x00400000u) : __uint_as_float(0x7fc00000u);
+  float v[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t c = (codes >> (4 * j)) & 7u;
+    const float mag = c == 0u ? 0.f : c == 1u ? 0.5f : __uint_as_float(((126u + (c >> 1)) << 23) | ((c & 1u) << 22));
+    v[j] = ((codes >> (4 * j + 3)) & 1u ? -mag : mag) * scale;
+  }
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
+}
+
+__device__ __forceinline__ uint4 e2m1x8_to_bf16x8(uint32_t codes, uint32_t sc) {
+  if (sc == 0u || sc == 255u) return e2m1x8_to_bf16x8_edge(codes, sc);
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const float scale = __uint_as_float(sc << 23);
+  const bf16x2_t r0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+  const bf16x2_t r1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+  const bf16x2_t r2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+  const bf16x2_t r3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+  uint4 out;
+  __builtin_memcpy(&out.x, &r0, 4);
+  __builtin_memcpy(&out.y, &r1, 4);
+  __builtin_memcpy(&out.z, &r2, 4);
+  __builtin_memcpy(&out.w, &r3, 4);
+  return out;
 }
 
 // x rounded to the nearest bf16 value (ties to even), as a float.

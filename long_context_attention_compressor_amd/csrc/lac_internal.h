@@ -55,7 +55,7 @@ struct IndexerArgs {
   const void* q;         // [B, Tq, HI, dI]
   const float* w;        // [B, Tq, HI]
   const void* K;         // [B, N, dI]
-  int fmt;               // kF32 | kBF16 | kMixed (E4M3 keys) | kE4M3 (E4M3 queries and keys)
+  int fmt;               // kF32 | kBF16 | kMixed (E4M3 keys) | kE4M3 (E4M3 queries and keys) | kMXFP4 (MXFP4 keys)
   int round_bf16;        // scores rounded to bf16 before selection
   int B, Tq, HI, dI, N, m, k;
   int32_t* topk_idx;     // [B, Tq, k]

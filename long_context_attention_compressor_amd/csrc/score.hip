@@ -119,14 +119,19 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   // with E4M3 queries (kE4M3) they stay E4M3 in LDS (f8_swz) and feed the
   // FP8 MFMA.
   constexpr bool F8 = KF == kE4M3;
-  constexpr int KROWB = KF == kMixed || F8 ? dI : ROWB;
+  // MXFP4 keys (kMXFP4): rows of d_I/2 bytes of E2M1 codes and d_I/32 scale
+  // bytes; a tile is copied as bytes to a per-wave LDS area and widened from
+  // there to the bf16 layout.
+  constexpr bool FP4 = KF == kMXFP4;
+  constexpr int KROWB = FP4 ? dI / 2 + dI / 32 : KF == kMixed || F8 ? dI : ROWB;
   constexpr int CH8 = dI / 8;                // 8-byte chunks per E4M3 key row
   constexpr int KTILEB = 32 * KROWB;
-  constexpr int NLD = KTILEB / 1024;         // 16-byte registers per lane per tile
+  constexpr int NLD = (KTILEB + 1023) / 1024;   // 16-byte registers per lane per tile
   constexpr int kLPR = dI / 8;               // E4M3: lanes per key (8 codes each)
   constexpr int kRPI = 64 / kLPR;            // E4M3: keys per 8-byte load
   __shared__ float sw[kRowsPerBlock][HI];
   __shared__ __align__(16) uint8_t ktile[4][F8 ? KTILEB : TILEB];
+  __shared__ __align__(16) uint8_t kraw[4][FP4 ? NLD * 1024 : 16];
   __shared__ uint32_t lhist[kHistBins];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
@@ -191,6 +196,9 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
           const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (kRPI * j + l / kLPR) * dI + (l % kLPR) * 8, 0, 2);
           if (h == 0) { st[u].x = v[0]; st[u].y = v[1]; } else { st[u].z = v[0]; st[u].w = v[1]; }
         }
+      } else if constexpr (FP4) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, u * 1024 + l * 16, 0, 2);
+        st[u] = make_uint4(v.x, v.y, v.z, v.w);
       } else if constexpr (F8) {
         bool sw8;
         const int src = f8_src<dI>(u * 1024 + l * 16, sw8);
@@ -205,6 +213,26 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     }
   };
   auto store_tile = [&](const uint4* st) {
+    if constexpr (FP4) {
+      // bytes of the tile to the wave's raw area, then lane l widens chunks
+      // l, l + 64, ... (key kk = o / CH, 8 dims c = o % CH): 4 code bytes and
+      // the scale byte of their 32-dim block, into the swizzled bf16 row
+      uint8_t* raw = kraw[wave];
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) *reinterpret_cast<uint4*>(raw + u * 1024 + l * 16) = st[u];
+      __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < 32 * CH / 64; ++i) {
+        const int o = l + 64 * i, kk = o / CH, c = o % CH;
+        const uint8_t* p = raw + kk * KROWB + 4 * c;   // 2-byte aligned (KROWB even)
+        const uint32_t codes = (uint32_t)*reinterpret_cast<const uint16_t*>(p) |
+                               ((uint32_t)*reinterpret_cast<const uint16_t*>(p + 2) << 16);
+        const uint32_t sc = raw[kk * KROWB + dI / 2 + c / 4];
+        *reinterpret_cast<uint4*>(kt + kk * ROWB + ((c ^ (kk % CH)) * 16)) = e2m1x8_to_bf16x8(codes, sc);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NLD; ++u) {
       if constexpr (KF == kMixed) {
@@ -592,9 +620,10 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
       const int64_t n_tiles = (nv_max + 31) / 32;
       const int HT = a.HI / 32, KS = a.dI / 16;
       // kBF16: bf16 queries and keys; kMixed: bf16 queries, E4M3 keys;
-      // kE4M3: E4M3 queries and keys (FP8 MFMA)
+      // kE4M3: E4M3 queries and keys (FP8 MFMA); kMXFP4: bf16 queries, MXFP4
+      // keys (the decode kernel for every shape)
       const int kf = a.fmt;
-      if (a.Tq >= 8 && !sb.split) {
+      if (a.Tq >= 8 && !sb.split && kf != kMXFP4) {
         // Prefill: a block of eight waves shares each key tile among 8 * QPW
         // queries and sweeps all the keys they see.
 #define LAC_SCORE_CASE(ht, ks, qpw)                                                        \
@@ -627,6 +656,7 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
   if (HT == ht && KS == ks)                                                         \
     err = kf == kE4M3    ? launch_score<ht, ks, 1, 1, kE4M3>(sa, chunks, groups, st)  \
           : kf == kMixed ? launch_score<ht, ks, 1, 1, kMixed>(sa, chunks, groups, st) \
+          : kf == kMXFP4 ? launch_score<ht, ks, 1, 1, kMXFP4>(sa, chunks, groups, st) \
                          : launch_score<ht, ks, 1, 1, kBF16>(sa, chunks, groups, st);
         LAC_SCORE_CASE(1, 4) LAC_SCORE_CASE(1, 8) LAC_SCORE_CASE(2, 4) LAC_SCORE_CASE(2, 8)
         LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)

@@ -11,9 +11,9 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import BF16, F32, MIXED, attend, compress, encode_rows, index_scores, topk
+from . import BF16, F32, MIXED, MXFP4, attend, compress, encode_rows, index_scores, topk
 
-FMT = {"f32": F32, "bf16": BF16, "mixed": MIXED}
+FMT = {"f32": F32, "bf16": BF16, "mixed": MIXED, "mxfp4": MXFP4}
 
 
 def compress_store(x, z, in_fmt, out_fmt, B, T, D, m, r, theta, pos0, norm_gain=None,

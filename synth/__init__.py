@@ -24,8 +24,8 @@ import zlib
 
 import torch
 
-F32, BF16, MIXED = 0, 1, 2
-DTYPE_CODES = {"f32": F32, "bf16": BF16, "mixed": MIXED}
+F32, BF16, MIXED, MXFP4 = 0, 1, 2, 4
+DTYPE_CODES = {"f32": F32, "bf16": BF16, "mixed": MIXED, "mxfp4": MXFP4}
 
 
 def _gen(seed: int, name: str, device) -> torch.Generator:
@@ -47,6 +47,17 @@ def uniform(seed: int, name: str, shape, device="cpu") -> torch.Tensor:
     """float32 draws from U(0, 1)."""
     return torch.rand(tuple(shape), generator=_gen(seed, name, device), device=device,
                       dtype=torch.float32)
+
+
+def mxfp4_rows(seed: int, name: str, shape, d: int, scale_lo: int = 124, scale_hi: int = 130,
+               device="cpu") -> torch.Tensor:
+    """Random MXFP4 rows [*shape, d/2 + d/32] uint8: uniform code bytes (two
+    E2M1 codes each), then scale bytes drawn from [scale_lo, scale_hi]."""
+    g = _gen(seed, name, device)
+    codes = torch.randint(0, 256, (*shape, d // 2), generator=g, device=device, dtype=torch.int32)
+    scales = torch.randint(scale_lo, scale_hi + 1, (*shape, d // 32), generator=g, device=device,
+                           dtype=torch.int32)
+    return torch.cat([codes, scales], dim=-1).to(torch.uint8).contiguous()
 
 
 def store(t: torch.Tensor, fmt: str, rope_dims: int = 0) -> torch.Tensor:
@@ -165,8 +176,9 @@ def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI
     FP8 E4M3 plus bf16 rotated dims.  The step also compresses the newest
     complete block of each layer (CSA entry, indexer key, HCA entry) from
     bf16 activations, so every stage of the path runs in one step.  The
-    indexer keys are bf16, or E4M3 with ki_fmt = "mixed" (no rotated dims);
-    indexer queries likewise with qi_fmt.
+    indexer keys are bf16, E4M3 with ki_fmt = "mixed" (no rotated dims), or
+    MXFP4 rows with ki_fmt = "mxfp4" (random codes, scales 2^-3..2^3);
+    indexer queries bf16 or E4M3 likewise with qi_fmt.
     With csa_overlap > 0 the newest CSA block comes with the csa_overlap raw
     rows before it (overlapping compression windows)."""
     N = ctx // m
@@ -175,7 +187,8 @@ def pair_decode(seed=4, B=4, ctx=1 << 20, D=512, m=4, m_hca=128, r=64, HI=64, dI
         kind="pair_decode", fmt="mixed", B=B, D=D, m=m, m_hca=m_hca, r=r, HI=HI, dI=dI, H=H,
         k=k, W=W, N=N, Nh=Nh, theta=10000.0, q_pos0=ctx, raw_pos0=ctx - W + 1, T_raw=W,
         ckv=store(normal(seed, "ckv", (B, N, D), device=device), "mixed", r),
-        KI=store(normal(seed, "KI", (B, N, dI), device=device), ki_fmt),
+        KI=(mxfp4_rows(seed, "KI", (B, N), dI, device=device) if ki_fmt == "mxfp4" else
+            store(normal(seed, "KI", (B, N, dI), device=device), ki_fmt)),
         hkv=store(normal(seed, "hkv", (B, Nh, D), device=device), "mixed", r),
         raw_csa=store(normal(seed, "raw_csa", (B, W, D), device=device), "mixed", r),
         raw_hca=store(normal(seed, "raw_hca", (B, W, D), device=device), "mixed", r),

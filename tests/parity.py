@@ -50,6 +50,21 @@ def check_compressed(gpu: torch.Tensor, ref: np.ndarray, fmt: str, D: int, r: in
     elif fmt == "bf16":
         g = as_f64(gpu).reshape(-1, D)
         bad = np.abs(g - ref) > 2.0 ** -8 * np.abs(ref) + 1e-6
+    elif fmt == "mxfp4":
+        # within one E2M1 grid step of the exact value at the coarser of the
+        # two blocks' scales (the GPU's fp32 pooled value can round to the
+        # neighbouring code, or cross a power of two and take the next scale)
+        rowb = D // 2 + D // 32
+        raw = np.ascontiguousarray(gpu.detach().cpu().numpy().reshape(-1, rowb))
+        g = oracle.decode_rows(raw, oracle.MXFP4, D, 0)
+        mine = oracle.encode_rows(ref, oracle.MXFP4, 0)
+        S = np.repeat(2.0 ** (np.maximum(raw[:, D // 2:], mine[:, D // 2:]).astype(np.int64) - 127),
+                      32, axis=1)
+        x = np.abs(ref) / S
+        gap = np.where(x < 2, 0.5, np.where(x < 4, 1.0, 2.0))
+        bad = np.abs(g - ref) > np.where(x <= 6, gap * S, np.abs(ref) - 6 * S + 2 * S) * (1 + 1e-9)
+        same = (raw == mine).mean()
+        assert same > 0.98, f"only {same:.3f} of the MXFP4 bytes equal the oracle's encoding"
     else:
         rowb = (D - r) + 2 * r
         raw = gpu.detach().cpu().numpy().reshape(-1, rowb)

@@ -22,6 +22,8 @@ def _run(B, T, D, m, r, in_fmt, out_fmt, pos0, seed, z_std=1.0, hca=False):
     N = T // m
     if out_fmt == "mixed":
         out = torch.full((B, N, D + r), 0x55, dtype=torch.uint8, device=DEV)
+    elif out_fmt == "mxfp4":
+        out = torch.full((B, N, D // 2 + D // 32), 0x55, dtype=torch.uint8, device=DEV)
     else:
         out = torch.full((B, N, D), 7.0, dtype=FMTS[out_fmt], device=DEV)
     fn = lac.hca_compress if hca else lac.csa_compress
@@ -91,3 +93,17 @@ def test_constant_kv_and_determinism():
     torch.cuda.synchronize()
     assert (o1.float() == 0.375).all()
     assert torch.equal(o1, o2)
+
+
+# MXFP4 indexer keys (no rotated dims): per 32 channels a shared exponent and
+# E2M1 codes; decode steps (one block per sequence) and bulk prefill.
+def test_mxfp4_keys_decode_blocks():
+    _run(4, 4, 128, 4, 0, "bf16", "mxfp4", [4 * 262143] * 4, 71)
+
+
+def test_mxfp4_keys_prefill_ragged():
+    _run(2, 4096 + 7, 128, 4, 0, "bf16", "mxfp4", [0, 100], 72)
+
+
+def test_mxfp4_keys_f32_input_d64_long_blocks():
+    _run(1, 1024, 64, 128, 0, "f32", "mxfp4", [128 * 7], 73, hca=True)

@@ -41,9 +41,10 @@ def _check_select(g_idx, qI, w, KI_h, fmt, B, Tq, HI, dI, N, qpos, m, k, rows, k
     return o_idx, same
 
 
-@pytest.mark.parametrize("ki_fmt", ["bf16", "mixed"])
+@pytest.mark.parametrize("ki_fmt", ["bf16", "mixed", "mxfp4"])
 def test_pair_decode_1m(ki_fmt):
-    # ki_fmt "mixed": the indexer keys are E4M3 (the mixed format, no rotated dims)
+    # ki_fmt "mixed": the indexer keys are E4M3 (the mixed format, no rotated
+    # dims); "mxfp4": E2M1 codes with a scale per 32 dims
     print(f"full size: pair decode, B=4 at 2^20, indexer keys {ki_fmt}", flush=True)
     c = synth.pair_decode(ki_fmt=ki_fmt, device=DEV)
     B, N, Nh, m, mh, D, r, k, W = (c[x] for x in ("B", "N", "Nh", "m", "m_hca", "D", "r", "k", "W"))
@@ -78,7 +79,7 @@ def test_pair_decode_1m(ki_fmt):
     ckv_h[:, N - 1:] = oracle.encode_rows(ref.reshape(B, D), oracle.MIXED, r).reshape(B, 1, -1)
     KI_h = _h(c["KI"]).copy()
     newest = oracle.encode_rows(refI.reshape(B, dI), synth.DTYPE_CODES[ki_fmt], 0)
-    KI_h[:, N - 1:] = (newest.view(np.uint16) if ki_fmt == "bf16" else newest).reshape(B, 1, dI)
+    KI_h[:, N - 1:] = (newest.view(np.uint16) if ki_fmt == "bf16" else newest).reshape(B, 1, -1)
     hkv_h = _h(c["hkv"]).copy()
     hkv_h[:, Nh - 1:] = oracle.encode_rows(refH.reshape(B, D), oracle.MIXED, r).reshape(B, 1, -1)
 

@@ -249,3 +249,45 @@ def test_bf16_scores_e4m3_queries_split_path():
 
 def test_bf16_scores_all_tied_take_the_lowest_indices():
     _run_bf16(2, 1, 32, 64, 30000, 4, 100, [4 * 30000, 4 * 30000], "bf16", 46, w_zero=True)
+
+
+# MXFP4 keys (E2M1 codes with E8M0 block scales) and bf16 queries: the keys
+# are widened exactly to bf16 in LDS.  Random code bytes; scales 2^-3..2^3.
+def _run_fp4(B, Tq, HI, dI, N, m, k, qpos, seed):
+    print(f"indexer mxfp4 keys B={B} Tq={Tq} HI={HI} dI={dI} N={N} k={k}", flush=True)
+    q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI)), "bf16")
+    K = synth.mxfp4_rows(seed, "KI", (B, N), dI)
+    w = synth.uniform(seed, "w", (B, Tq, HI))
+    score = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    idx = lac.indexer_topk(q.to(DEV), w.to(DEV), K.to(DEV), m=m, k=k, q_pos0=qpos,
+                           topk_score=score)
+    torch.cuda.synchronize()
+    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.DTYPE_CODES["bf16"], B, Tq, HI,
+                                dI, N, qpos, m, k_dtype=synth.DTYPE_CODES["mxfp4"])
+    o_idx = oracle.topk(s, nv, k)
+    g_idx = idx.cpu().numpy().reshape(B * Tq, k)
+    g_sc = score.cpu().numpy().reshape(B * Tq, k)
+    same = check_topk(g_idx, o_idx, s, nv, k)
+    for rr in range(B * Tq):
+        keff = min(k, int(nv[rr]))
+        gi = g_idx[rr, :keff]
+        assert (np.diff(gi) > 0).all()
+        assert np.allclose(g_sc[rr, :keff], s[rr, gi], rtol=1e-4, atol=1e-3)
+    return same
+
+
+def test_mxfp4_keys_decode_split_path():
+    _run_fp4(2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], 51)
+
+
+def test_mxfp4_keys_decode_prefix_path_ragged():
+    _run_fp4(4, 1, 64, 128, 5003, 4, 512, [4 * 5003 + 1, 4 * 5003, 4 * 3000 + 3, 40000], 52)
+
+
+def test_mxfp4_keys_prefill_rows():
+    _run_fp4(1, 20, 64, 128, 2010, 4, 300, [8000], 53)
+
+
+@pytest.mark.parametrize("HI,dI", [(32, 64), (128, 128)])
+def test_mxfp4_keys_head_and_dim_variants(HI, dI):
+    _run_fp4(2, 1, HI, dI, 2100, 4, 256, [8400, 9000], 54 + HI + dI)
