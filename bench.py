@@ -8,7 +8,9 @@ and keep the top 2048, sparse CSA attention and dense HCA attention over
 stored as FP8 E4M3 with the 64 rotated dims in bf16.  The metric is decode
 tokens/s (4 per step) with the algorithmic HBM GB/s beside it.  Three
 independent cache sets rotate so that a step never finds its 294 MB working
-set in the 256 MB Infinity Cache.
+set in the 256 MB Infinity Cache.  The step's three compress calls run as one
+launch group, and so do its two attention calls (lac.group);
+pair_decode_1m_ungrouped makes the same calls one launch each.
 
 Other workloads (--workload): pair_decode_1m_e4m3_indexer (the same step with
 the indexer keys stored as E4M3, one byte per dim), pair_decode_1m_fp8_indexer
@@ -29,6 +31,7 @@ Prints one JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -101,6 +104,7 @@ class PairDecode:
     rmsnorm = False     # fused RMSNorm of the new compressed entries and the queries
     gain = None
     overlap = 0         # CSA compression windows reaching this many tokens back
+    grouped = True      # the step's independent calls in launch groups (lac.group)
 
     def __init__(self, lac, synth, dev, sets, seed=4, B=4, ctx=1 << 20):
         self.lac, self.B, self.ctx = lac, B, ctx
@@ -127,24 +131,30 @@ class PairDecode:
     def step(self, i):
         lac, c, s = self.lac, self.c, self.sets[i % len(self.sets)]
         N, Nh, m, mh, ctx = c["N"], c["Nh"], c["m"], c["m_hca"], self.ctx
-        # the CSA layer: compress its newest block (KV entry and indexer key),
-        # select, attend
         g = self.gain
-        lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
-                         rope_dims=c["r"], pos0=ctx - m, norm_gain=g, T=m, overlap=self.overlap)
-        lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m, rope_dims=0,
-                         pos0=ctx - m)
+        grp = lac.group if self.grouped else contextlib.nullcontext
+        # compress the newest blocks: the CSA layer's KV entry and indexer key,
+        # the HCA layer's entry (independent calls: one launch when grouped)
+        with grp():
+            lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
+                             rope_dims=c["r"], pos0=ctx - m, norm_gain=g, T=m,
+                             overlap=self.overlap)
+            lac.csa_compress(s["new_kI"], s["new_zI"], _rows(s["KI"], N - 1, N), m=m,
+                             rope_dims=0, pos0=ctx - m)
+            lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh),
+                             m=mh, rope_dims=c["r"], pos0=ctx - mh, norm_gain=g)
+        # the CSA layer's selection
         lac.indexer_topk(s["qI"], s["w"], s["KI"], m=m, k=c["k"], q_pos0=ctx, topk_idx=self.idx,
                          workspace=self.ws_idx)
-        lac.csa_attend(s["q_csa"], s["ckv"], self.idx, s["raw_csa"], c["W"], q_pos0=ctx,
-                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_csa,
-                       workspace=self.ws_csa, q_norm_gain=g)
-        # the HCA layer: compress its newest block, then attend
-        lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh), m=mh,
-                         rope_dims=c["r"], pos0=ctx - mh, norm_gain=g)
-        lac.hca_attend(s["q_hca"], s["hkv"], s["raw_hca"], c["W"], m=mh, q_pos0=ctx,
-                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_hca,
-                       workspace=self.ws_hca, q_norm_gain=g)
+        # both layers' attention (independent: one attention and one combine
+        # launch when grouped)
+        with grp():
+            lac.csa_attend(s["q_csa"], s["ckv"], self.idx, s["raw_csa"], c["W"], q_pos0=ctx,
+                           raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_csa,
+                           workspace=self.ws_csa, q_norm_gain=g)
+            lac.hca_attend(s["q_hca"], s["hkv"], s["raw_hca"], c["W"], m=mh, q_pos0=ctx,
+                           raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=self.out_hca,
+                           workspace=self.ws_hca, q_norm_gain=g)
 
     def tokens_per_step(self):
         return self.B
@@ -230,6 +240,13 @@ class PairDecode:
                 "sample": "the full decode step (compress newest blocks, index 262144 entries, "
                           "top-2048, CSA + HCA attention, 64 heads) of 1 of the 4 sequences, "
                           "cache set 0"}
+
+
+class PairDecodeUngrouped(PairDecode):
+    """pair_decode_1m with every call launched on its own (no launch groups):
+    seven launches of compress, attention and combine instead of three."""
+    name = "pair_decode_1m_ungrouped"
+    grouped = False
 
 
 class PairDecodeE4M3Indexer(PairDecode):
@@ -640,7 +657,8 @@ class BulkCompress128K(BulkCompress1M):
         return d
 
 
-WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeE4M3Indexer, PairDecodeFp8Indexer,
+WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeUngrouped, PairDecodeE4M3Indexer,
+                                  PairDecodeFp8Indexer,
                                   PairDecodeMxfp4Indexer,
                                   PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode,

@@ -20,9 +20,9 @@
  *   pointers must be 16-byte aligned.
  * Streams.  `stream` is a hipStream_t (NULL = the default stream).  Work is
  *   enqueued asynchronously; the calls are thread-safe (no global state
- *   except the thread-local error string, the thread-local launch timer and
- *   the fixed device scratch of indexer_topk_noalloc, whose overlapping calls
- *   on one GPU race).
+ *   except the thread-local error string, the thread-local launch timer, the
+ *   thread-local launch group and the fixed device scratch of
+ *   indexer_topk_noalloc, whose overlapping calls on one GPU race).
  * Positions.  Host arrays of B int64 (NULL = all zero).  Query i of sequence
  *   b sits at absolute position q_pos0[b] + i; raw row i at raw_pos0[b] + i.
  *   Compressed entry j covers positions [j*m, j*m + m - 1] and is rotated at
@@ -378,6 +378,50 @@ int32_t grouped_output_projection(const void* attn, const void* w1, const void* 
                                   int32_t H, int32_t D, int32_t G, int32_t d_g, int32_t d,
                                   void* out, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/*
+ * Launch groups.  lac_group_begin(stream) opens a group on the calling host
+ * thread.  Until lac_group_end(stream), the compress calls (csa_compress,
+ * csa_compress_overlap, hca_compress and their _rmsnorm forms) and the
+ * attention calls (csa_attend, hca_attend and their _rmsnorm forms) made on
+ * this thread validate their arguments exactly as outside a group, return
+ * LAC_OK and enqueue nothing: they are recorded, with copies of their scalar
+ * and host-array arguments (not of the device memory their pointers name).
+ * lac_group_end enqueues every recorded call on `stream`:
+ *   - the compress calls as one kernel launch (per input dtype, at most four
+ *     calls and 384 batch positions per launch);
+ *   - the attention calls as one attention launch followed by one combine
+ *     launch (per D and KV dtype, at most four calls sharing one rope_theta
+ *     and rope_dims per launch; float32 calls run one by one; prefill shapes
+ *     add each call's window-rotation launch first), with the calls' key
+ *     splits planned together so that they share one wave of workgroups.
+ * Compress results are those of the same calls made outside the group; an
+ * attention call's key range may be split differently, so its output may
+ * differ from the ungrouped call's in the rounding of the split sums.  For a
+ * decode step this replaces up to seven launches by three: each launch has
+ * a fixed cost of several microseconds.
+ *
+ * The caller guarantees that the calls of one group are independent: no call
+ * reads device memory that another call of the group writes, and no two
+ * calls write the same memory (outputs, or workspaces: overlapping attention
+ * workspaces are detected and refused).  Memory named by a recorded call must
+ * stay valid until the enqueued work completes, as for any call.
+ *
+ * Inside a group, every call must pass the group's stream (else
+ * LAC_ERR_INVALID, nothing recorded), and indexer_topk, indexer_topk_noalloc
+ * and grouped_output_projection return LAC_ERR_INVALID.  lac_group_begin on a
+ * thread whose group is open returns LAC_ERR_INVALID; lac_group_end without
+ * an open group returns LAC_ERR_INVALID.  lac_group_end always closes the
+ * group: on an error (another stream, overlapping workspaces:
+ * LAC_ERR_WORKSPACE, a refused launch: LAC_ERR_DEVICE) it enqueues nothing
+ * further and drops what remains.  A group with no calls is a no-op.  The
+ * launch timer brackets a grouped launch like any other launch of its
+ * kernel.  lac_group_cancel closes the open group and drops its recorded
+ * calls without enqueuing any (LAC_ERR_INVALID when none is open).
+ */
+int32_t lac_group_begin(void* stream);
+int32_t lac_group_end(void* stream);
+int32_t lac_group_cancel(void);
 
 /* Message of the last failed call on this thread ("" if none).  Valid until
  * the next call on this thread. */

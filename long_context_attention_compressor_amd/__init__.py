@@ -25,7 +25,7 @@ __all__ = [
     "grouped_output_projection", "grouped_projection_workspace_size",
     "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "LAC_MXFP4", "LAC_SCORE_BF16",
     "KERNELS",
-    "CallList",
+    "CallList", "group",
 ]
 
 LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3, LAC_MXFP4 = 0, 1, 2, 3, 4
@@ -83,6 +83,12 @@ lib.lac_last_error.argtypes = []
 lib.lac_last_error.restype = ctypes.c_char_p
 lib.lac_time_next_launch.argtypes = [_i32, _vp, _vp]
 lib.lac_time_next_launch.restype = _i32
+lib.lac_group_begin.argtypes = [_vp]
+lib.lac_group_begin.restype = _i32
+lib.lac_group_end.argtypes = [_vp]
+lib.lac_group_end.restype = _i32
+lib.lac_group_cancel.argtypes = []
+lib.lac_group_cancel.restype = _i32
 
 
 class LacError(RuntimeError):
@@ -183,10 +189,49 @@ def _need_dense(t: Optional[torch.Tensor], what: str):
         raise ValueError(f"{what} must be contiguous")
 
 
+_group_keep = None
+
+
 def _workspace(ws: Optional[torch.Tensor], need: int, device) -> torch.Tensor:
     if ws is None or ws.numel() < need:
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        if _group_keep is not None:      # used only when the group is enqueued
+            _group_keep.append(ws)
     return ws
+
+
+class group:
+    """Launch group (lac_group_begin / lac_group_end in include/lac.h).
+
+    Inside ``with group():`` the compress and attention calls on the stream
+    are validated and recorded; leaving the block enqueues them together
+    (compress calls in one launch, attention calls in one attention launch
+    and one combine launch).  The calls must be independent: none reads what
+    another writes.  Workspaces the wrappers allocate are kept alive until
+    the group is enqueued.  An exception inside the block cancels the group
+    (nothing recorded is enqueued).  Inside a CallList the begin and end
+    calls are recorded like any other."""
+
+    def __init__(self, stream=None):
+        self.stream = stream
+
+    def __enter__(self):
+        global _group_keep
+        _call(lib.lac_group_begin, (_stream(self.stream),))
+        if _recording is None:
+            _group_keep = []
+        return self
+
+    def __exit__(self, exc_type, *rest):
+        global _group_keep
+        try:
+            if exc_type is None:
+                _call(lib.lac_group_end, (_stream(self.stream),))
+            elif _recording is None:
+                lib.lac_group_cancel()
+        finally:
+            _group_keep = None
+        return False
 
 
 # ---------------------------------------------------------------- compress

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <exception>
+#include <vector>
 
 #include "lac.h"
 #include "lac_internal.h"
@@ -16,6 +17,26 @@ thread_local char g_err[512] = "";
 thread_local int g_timer_kernel = -1;
 thread_local hipEvent_t g_timer_start = nullptr;
 thread_local hipEvent_t g_timer_stop = nullptr;
+
+// The launch group open on this thread (lac_group_begin .. lac_group_end):
+// the validated calls recorded for one grouped enqueue.
+struct Group {
+  bool open = false;
+  void* stream = nullptr;
+  std::vector<lac::CompressArgs> comp;
+  std::vector<lac::AttendArgs> att;
+  std::vector<void*> att_ws;
+  std::vector<size_t> att_need;
+  void close() {
+    open = false;
+    stream = nullptr;
+    comp.clear();
+    att.clear();
+    att_ws.clear();
+    att_need.clear();
+  }
+};
+thread_local Group g_group;
 
 int32_t fail(int32_t code, const char* fmt, ...) {
   va_list ap;
@@ -43,6 +64,17 @@ int32_t take_positions(const char* fn, const char* what, const int64_t* src, int
                   (long long)p, mult);
     dst->v[b] = (int32_t)p;
   }
+  return LAC_OK;
+}
+
+// Entry points that cannot be recorded refuse to run inside a group.
+int32_t refuse_in_group(const char* fn) {
+  return fail(LAC_ERR_INVALID, "%s: not allowed while a launch group is open on this thread", fn);
+}
+
+int32_t group_stream(const char* fn, void* stream) {
+  if (stream != g_group.stream)
+    return fail(LAC_ERR_INVALID, "%s: stream differs from the open launch group's", fn);
   return LAC_OK;
 }
 
@@ -94,6 +126,9 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
   if (B > 1 && (kv_bstride < T + lead_max || z_bstride < T + lead_max || out_bstride < N))
     return fail(LAC_ERR_INVALID, "%s: batch strides must cover T rows (in; plus the overlap's "
                 "leading rows) and T/m rows (out)", fn);
+  if ((int64_t)B * N * (D / 8) >= lac::kCompressMaxGroups)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: B * floor(T/m) * D/8 = %lld reaches 2^31 (one launch's limit)",
+                fn, (long long)B * N * (D / 8));
   if (norm) {
     const int G = D / 8;
     if (G > 64 || (G & (G - 1)))
@@ -119,6 +154,12 @@ int32_t compress_impl(const char* fn, const void* raw_kv, const void* logits, in
   a.in_fmt = in_dtype; a.out_fmt = out_dtype;
   a.B = B; a.T = T; a.D = D; a.m = m; a.r = rope_dims; a.theta = rope_theta; a.overlap = overlap;
   a.kv_bstride = kv_bstride; a.z_bstride = z_bstride; a.out_bstride = out_bstride;
+  if (g_group.open) {
+    if ((st = group_stream(fn, stream))) return st;
+    g_group.comp.push_back(a);
+    g_err[0] = 0;
+    return LAC_OK;
+  }
   return launch_status(fn, lac::launch_compress(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -258,6 +299,14 @@ int32_t attend_impl(const char* fn, const AttendCommon& c, int mode, const int32
   if (lac::attend_split_count(a) > lac::kMaxSplit)
     return fail(LAC_ERR_UNSUPPORTED, "%s: %s too long for one launch (it would take more than %d key splits)",
                 fn, mode == 0 ? "the selection" : "the compressed cache", lac::kMaxSplit);
+  if (g_group.open) {
+    if ((st = group_stream(fn, c.stream))) return st;
+    g_group.att.push_back(a);
+    g_group.att_ws.push_back(c.ws);
+    g_group.att_need.push_back(need);
+    g_err[0] = 0;
+    return LAC_OK;
+  }
   return launch_status(fn, lac::launch_attend(a, c.ws, static_cast<hipStream_t>(c.stream)));
 }
 
@@ -370,6 +419,7 @@ int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32
                      const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream) {
   try {
+    if (g_group.open) return refuse_in_group("indexer_topk");
     return indexer_impl("indexer_topk", q_idx, w, k_idx, dtype, B, Tq, H_I, d_I, N, q_pos0, m, k,
                         topk_idx, topk_score, workspace, workspace_bytes, false, stream);
   } catch (...) {
@@ -382,6 +432,7 @@ int32_t indexer_topk_noalloc(const void* q_idx, const float* w, const void* k_id
                              const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                              float* topk_score, void* stream) {
   try {
+    if (g_group.open) return refuse_in_group("indexer_topk_noalloc");
     return indexer_impl("indexer_topk_noalloc", q_idx, w, k_idx, dtype, B, Tq, H_I, d_I, N,
                         q_pos0, m, k, topk_idx, topk_score, nullptr, lac::kNoallocScratchBytes,
                         true, stream);
@@ -477,6 +528,7 @@ int32_t grouped_output_projection(const void* attn, const void* w1, const void* 
                                   void* stream) {
   const char* fn = "grouped_output_projection";
   try {
+    if (g_group.open) return refuse_in_group(fn);
     if (T < 0 || H < 1 || D < 1 || G < 1 || d_g < 1 || d < 1)
       return fail(LAC_ERR_INVALID, "%s: negative T or a width < 1", fn);
     if (H % G) return fail(LAC_ERR_INVALID, "%s: G = %d does not divide H = %d", fn, G, H);
@@ -504,6 +556,55 @@ int32_t grouped_output_projection(const void* attn, const void* w1, const void* 
 }
 
 const char* lac_last_error(void) { return g_err; }
+
+int32_t lac_group_begin(void* stream) {
+  if (g_group.open)
+    return fail(LAC_ERR_INVALID, "lac_group_begin: a launch group is already open on this thread");
+  g_group.close();
+  g_group.open = true;
+  g_group.stream = stream;
+  g_err[0] = 0;
+  return LAC_OK;
+}
+
+int32_t lac_group_end(void* stream) {
+  const char* fn = "lac_group_end";
+  if (!g_group.open) return fail(LAC_ERR_INVALID, "%s: no launch group is open on this thread", fn);
+  try {
+    int32_t st = group_stream(fn, stream);
+    // attention workspaces are written by the library: no two may overlap
+    const size_t na = g_group.att.size();
+    for (size_t i = 0; i < na && st == LAC_OK; ++i) {
+      const uintptr_t lo_i = reinterpret_cast<uintptr_t>(g_group.att_ws[i]);
+      for (size_t j = i + 1; j < na && st == LAC_OK; ++j) {
+        const uintptr_t lo_j = reinterpret_cast<uintptr_t>(g_group.att_ws[j]);
+        if (g_group.att_need[i] && g_group.att_need[j] && lo_i < lo_j + g_group.att_need[j] &&
+            lo_j < lo_i + g_group.att_need[i])
+          st = fail(LAC_ERR_WORKSPACE, "%s: attention calls %zu and %zu of the group share workspace memory",
+                    fn, i, j);
+      }
+    }
+    if (st) { g_group.close(); return st; }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (!g_group.comp.empty())
+      e = lac::launch_compress_group(g_group.comp.data(), (int)g_group.comp.size(), hs);
+    if (e == hipSuccess && na)
+      e = lac::launch_attend_group(g_group.att.data(), g_group.att_ws.data(), (int)na, hs);
+    g_group.close();
+    return launch_status(fn, e);
+  } catch (...) {
+    g_group.close();
+    return fail(LAC_ERR_DEVICE, "%s: internal error", fn);
+  }
+}
+
+int32_t lac_group_cancel(void) {
+  if (!g_group.open) return fail(LAC_ERR_INVALID, "lac_group_cancel: no launch group is open on this thread");
+  g_group.close();
+  g_err[0] = 0;
+  return LAC_OK;
+}
 
 int32_t lac_time_next_launch(int32_t kernel, void* start, void* stop) {
   if (kernel < 0 || kernel >= lac::kKernelCount)

@@ -32,6 +32,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <vector>
+
 #include "lac_internal.h"
 
 namespace lac {
@@ -66,7 +68,7 @@ constexpr int kLoRow = 2 * 128 + 16;          // LDS bytes per staged low row (R
 // shared_entries: the G queries of a work item see one common run of compressed
 // entries (HCA's causal prefix) rather than G separate selections (CSA).
 AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries, int W,
-                   bool f32_path, bool shared_entries) {
+                   bool f32_path, bool shared_entries, int grid_target = kGridTarget) {
   AttnPlan p{};
   p.row_bytes = kv_row_bytes(kv_fmt, D, r);
   p.win_rows = W > 0 ? (int64_t)Tq + W - 1 : 0;
@@ -95,7 +97,7 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   // One block fills a compute unit's LDS, so the grid is sized to one wave of
   // blocks over the 256 compute units; a split holds at least 2 tiles.
   const int max_split = (int)((p.max_entries + 63) / 64);
-  int ns = p.n_work >= kGridTarget ? 1 : kGridTarget / p.n_work;
+  int ns = p.n_work >= grid_target ? 1 : grid_target / p.n_work;
   if (ns > max_split) ns = max_split;
   if (ns < 1) ns = 1;
   p.chunk = (int)round_up((p.max_entries + ns - 1) / ns, 32);
@@ -228,16 +230,42 @@ struct KArgs {
   const uint8_t* raw;        // [B, T_raw, row] raw window rows, not rotated
   int64_t T_raw;
   int win_rotated;           // window rows come pre-rotated from `win` (prefill)
-  Positions rawpos;
   int mode, N, k, m, W, B, Tq, H, D, r;
   float theta, scale_log2;
-  int G, Hs, n_htiles, n_qgroups, nsplit, chunk, wchunk;
+  int G, Hs, n_htiles, n_qgroups, n_work, nsplit, chunk, wchunk;
   int64_t win_rows, row_bytes, win_row_bytes;
-  Positions qpos;
-  RopeTable rope;
+  int pos_q, pos_raw;        // q_pos0 and raw_pos0 in the launch's position pool
   const float* q_norm_gain;  // [D] or null: RMSNorm of each query head before its rotation
   float norm_eps;
 };
+
+// One launch: up to kAttendGroup independent calls whose workgroups follow
+// one another (a call's are work-major, split fastest), their positions in
+// one pool and one rotation table shared by all of them, so that the whole
+// launch fits one kernel argument.
+constexpr int kAttendGroup = 4;
+constexpr int kAttendPos = 384;
+
+struct KLaunch {
+  KArgs k[kAttendGroup];
+  uint32_t blk_end[kAttendGroup];   // workgroups of calls 0 .. i
+  int n;
+  int32_t pos[kAttendPos];
+  double freq[kMaxRopePairs];
+};
+
+// The call that workgroup wg belongs to, and wg's index within that call.
+__device__ __forceinline__ int launch_call(const KLaunch& L, uint32_t wg, uint32_t* local) {
+  int ci = 0;
+  while (ci + 1 < L.n && wg >= L.blk_end[ci]) ++ci;
+  *local = wg - (ci ? L.blk_end[ci - 1] : 0u);
+  return ci;
+}
+
+__device__ __forceinline__ void launch_freq_table(double* tab, const KLaunch& L, int r, int tid,
+                                                  int nthreads) {
+  for (int i = tid; i < r / 2; i += nthreads) tab[i] = L.freq[i];
+}
 
 // Work item decomposition: blockIdx.x = split (fastest), blockIdx.y = work.
 struct Work {
@@ -248,7 +276,9 @@ struct Work {
   int64_t win_row0;         // its row in the rotated-window buffer
 };
 
-__device__ __forceinline__ Work make_work(const KArgs& a, int work) {
+// (A launch of one call has its q_pos0 at the start of the position pool.)
+template <bool MULTI = true>
+__device__ __forceinline__ Work make_work(const KLaunch& L, const KArgs& a, int work) {
   Work w;
   const int ht = work % a.n_htiles;
   const int rest = work / a.n_htiles;
@@ -257,11 +287,12 @@ __device__ __forceinline__ Work make_work(const KArgs& a, int work) {
   w.i0 = qg * a.G;
   w.h0 = ht * 64;
   w.n_q = min(a.G, a.Tq - w.i0);
-  w.t_first = (int64_t)a.qpos.v[w.b] + w.i0;
+  const int64_t qpos = L.pos[(MULTI ? a.pos_q : 0) + w.b];
+  w.t_first = qpos + w.i0;
   const int64_t t_last = w.t_first + w.n_q - 1;
   w.n_comp = a.mode == 0 ? w.n_q * a.k : (int)n_visible(t_last, a.N, a.m);
   w.lo_w = max((int64_t)0, w.t_first - a.W + 1);
-  w.win_row0 = w.lo_w - max((int64_t)0, (int64_t)a.qpos.v[w.b] - a.W + 1);
+  w.win_row0 = w.lo_w - max((int64_t)0, qpos - a.W + 1);
   const int n_win = a.W > 0 ? (int)(t_last - w.lo_w + 1) : 0;
   w.n_tot = w.n_comp + n_win;
   return w;
@@ -388,8 +419,10 @@ struct Geo {
   static constexpr int NLO = (16 + TPR - 1) / TPR;            // low-part chunks (<= 16 per row)
 };
 
-template <int D, int KV>
-__global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
+// MULTI false: a launch of one call, grid (splits, work items).  MULTI true:
+// a flat grid of several calls' workgroups (KLaunch).
+template <int D, int KV, bool MULTI>
+__global__ void __launch_bounds__(512) attend_mfma_kernel(KLaunch L) {
   using Gm = Geo<D>;
   constexpr int DS = Gm::DS, NT = Gm::NT, TPR = Gm::TPR;
   __shared__ __align__(16) uint8_t Et[2][kTile * Gm::EROW];     // entry tiles, bf16 rows
@@ -409,8 +442,12 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave & 3, dh = DS == 2 ? wave >> 2 : 0;
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
-  const Work w = make_work(a, blockIdx.y);
-  const int split = blockIdx.x;
+  uint32_t lb = 0;
+  const int ci = MULTI ? launch_call(L, blockIdx.x, &lb) : 0;
+  const KArgs& a = L.k[ci];
+  const int work = MULTI ? (int)(lb / (uint32_t)a.nsplit) : (int)blockIdx.y;
+  const int split = MULTI ? (int)(lb % (uint32_t)a.nsplit) : (int)blockIdx.x;
+  const Work w = make_work<MULTI>(L, a, work);
   // Split -> entry range: chunk entries per split, or, with wchunk, chunk
   // entries per split over the compressed entries and then wchunk per split
   // over the window rows.
@@ -434,7 +471,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
   // window row of position lo_w + off: pre-rotated, or raw and rotated here
   const bool rot_here = !a.win_rotated;
   const uint8_t* winb = rot_here
-      ? a.raw + ((int64_t)w.b * a.T_raw + (w.lo_w - a.rawpos.v[w.b])) * row_bytes
+      ? a.raw + ((int64_t)w.b * a.T_raw + (w.lo_w - L.pos[(MULTI ? a.pos_raw : a.B) + w.b])) * row_bytes
       : a.win + ((int64_t)w.b * a.win_rows + w.win_row0) * a.win_row_bytes;
   // low parts of rotated window dims (dims lo_base .. D-1), added on the
   // tiles that hold window rows
@@ -487,7 +524,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
     const int32_t* src = a.idx + ((int64_t)w.b * a.Tq + w.i0) * kk + e_lo;
     for (int e = tid; e < n_idx; e += NT) lidx[e] = src[e];
   }
-  rope_freq_table(freq, a.rope, a.r, tid, NT);
+  launch_freq_table(freq, L, a.r, tid, NT);
   __syncthreads();
 
   constexpr int NST = KV == kMixed ? Gm::NCHM : Gm::NCH;
@@ -760,7 +797,7 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
       *reinterpret_cast<uint2*>(orow + 32 * dt) = v;
     }
   }
-  const int64_t slot = (int64_t)blockIdx.y * a.nsplit + split;
+  const int64_t slot = (int64_t)work * a.nsplit + split;
   if (split_out && lq == 0 && dh == 0) {
     a.part_ml[(slot * 64 + row) * 2] = m_run;
     a.part_ml[(slot * 64 + row) * 2 + 1] = l_row;
@@ -789,14 +826,18 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KArgs a) {
 }
 
 // ---------------------------------------------------------------- combine
-__global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
+template <bool MULTI>
+__global__ void __launch_bounds__(256) combine_kernel(KLaunch L) {
   // wgt holds the split weights (nsplit <= kMaxSplit), then (reused) the split
   // groups' partial sums: (256 / (D/8) - 1) * D floats <= 1920 for D >= 128.
   __shared__ float wgt[kMaxSplit];
   __shared__ float red[1];
   __shared__ float2 angle[kMaxRopePairs];
-  const int work = blockIdx.x / 64, row = blockIdx.x % 64;
-  const Work w = make_work(a, work);
+  uint32_t lb = blockIdx.x;
+  const int ci = MULTI ? launch_call(L, blockIdx.x, &lb) : 0;
+  const KArgs& a = L.k[ci];
+  const int work = (int)(lb / 64), row = (int)(lb % 64);
+  const Work w = make_work<MULTI>(L, a, work);
   const int g = row / a.Hs, h = w.h0 + row % a.Hs;
   if (g >= w.n_q) return;
   const int64_t slot0 = (int64_t)work * a.nsplit;
@@ -824,7 +865,7 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
   if (threadIdx.x >= 64 && threadIdx.x < 64 + a.r / 2) {
     const int p = threadIdx.x - 64;
     float c, sn;
-    rope_cos_sin((double)t, a.rope.inv_freq[p], &c, &sn);
+    rope_cos_sin((double)t, L.freq[p], &c, &sn);
     angle[p] = make_float2(c, sn);
   }
   const int wlast = 3;
@@ -903,10 +944,11 @@ __global__ void __launch_bounds__(256) combine_kernel(KArgs a) {
 
 // ---------------------------------------------------------------- float32 VALU path
 // One workgroup per query; H*D <= 8192, D <= 256.
-__global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
+__global__ void __launch_bounds__(256) attend_f32_kernel(KLaunch L) {
   extern __shared__ float fsm[];
   __shared__ double freq[kMaxRopePairs];
-  rope_freq_table(freq, a.rope, a.r, threadIdx.x, 256);
+  const KArgs& a = L.k[0];
+  launch_freq_table(freq, L, a.r, threadIdx.x, 256);
   const int H = a.H, D = a.D;
   float* qs = fsm;                    // [H][D]
   float* es = qs + H * D;             // [32][D]
@@ -916,7 +958,7 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
   float* al = lrow + H;               // [H]
   int* tags = reinterpret_cast<int*>(al + H);   // [32]
   const int tid = threadIdx.x;
-  const Work w = make_work(a, blockIdx.x);      // G = 1, one query
+  const Work w = make_work(L, a, blockIdx.x);   // G = 1, one query
   const Vis vis0 = make_vis(a, w, 0);
   const int64_t t = w.t_first;
   const int nope = D - a.r;
@@ -1017,17 +1059,136 @@ __global__ void __launch_bounds__(256) attend_f32_kernel(KArgs a) {
 }
 
 template <int D, int KV>
-hipError_t launch_mfma(const KArgs& k, const AttnPlan& p, hipStream_t st) {
-  const size_t lds = (size_t)p.G * (k.r / 2) * sizeof(float2);   // the block's query angles
+hipError_t launch_mfma(const KLaunch& L, size_t lds, hipStream_t st) {
   {
     TimedLaunch tl(kKernelAttend, st);
-    hipLaunchKernelGGL((attend_mfma_kernel<D, KV>), dim3(p.nsplit, p.n_work), dim3(Geo<D>::NT), lds, st, k);
+    if (L.n == 1)
+      hipLaunchKernelGGL((attend_mfma_kernel<D, KV, false>), dim3(L.k[0].nsplit, L.k[0].n_work),
+                         dim3(Geo<D>::NT), lds, st, L);
+    else
+      hipLaunchKernelGGL((attend_mfma_kernel<D, KV, true>), dim3(L.blk_end[L.n - 1]),
+                         dim3(Geo<D>::NT), lds, st, L);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.nsplit == 1) return e;
+  if (e != hipSuccess) return e;
+  // the calls with split partials, merged by one combine launch; their
+  // positions are packed again from the start of the pool (a launch of one
+  // call finds them there)
+  KLaunch C = L;
+  C.n = 0;
+  int n_pos = 0;
+  for (int i = 0; i < L.n; ++i) {
+    const KArgs& k = L.k[i];
+    if (k.nsplit == 1) continue;
+    C.k[C.n] = k;
+    for (int b = 0; b < k.B; ++b) {
+      C.pos[n_pos + b] = L.pos[k.pos_q + b];
+      C.pos[n_pos + k.B + b] = L.pos[k.pos_raw + b];
+    }
+    C.k[C.n].pos_q = n_pos;
+    C.k[C.n].pos_raw = n_pos + k.B;
+    n_pos += 2 * k.B;
+    C.blk_end[C.n] = (C.n ? C.blk_end[C.n - 1] : 0u) + (uint32_t)k.n_work * 64u;
+    ++C.n;
+  }
+  if (C.n == 0) return hipSuccess;
   TimedLaunch tl(kKernelCombine, st);
-  hipLaunchKernelGGL(combine_kernel, dim3(p.n_work * 64), dim3(256), 0, st, k);
+  if (C.n == 1)
+    hipLaunchKernelGGL(combine_kernel<false>, dim3(C.blk_end[0]), dim3(256), 0, st, C);
+  else
+    hipLaunchKernelGGL(combine_kernel<true>, dim3(C.blk_end[C.n - 1]), dim3(256), 0, st, C);
   return hipGetLastError();
+}
+
+// The kernel arguments of one call under plan p; positions go to the pool of L.
+KArgs make_kargs(const AttendArgs& a, const AttnPlan& p, void* ws, KLaunch* L, int* n_pos) {
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  KArgs k{};
+  k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
+  k.win_row_bytes = p.win_row_bytes;
+  k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
+  k.ang = reinterpret_cast<const float2*>(w8 + p.off_ang);
+  k.part_o = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(w8 + p.off_po) : nullptr;
+  k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
+  k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;
+  k.H = a.H; k.D = a.D; k.r = a.r; k.theta = a.theta;
+  k.scale_log2 = a.scale * 1.4426950408889634f;
+  k.q_norm_gain = a.q_norm_gain;
+  k.norm_eps = a.norm_eps;
+  k.G = p.G; k.Hs = p.Hs; k.n_htiles = p.n_htiles; k.n_qgroups = p.n_qgroups; k.n_work = p.n_work;
+  k.nsplit = p.nsplit; k.chunk = p.chunk; k.wchunk = p.wchunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;
+  k.raw = static_cast<const uint8_t*>(a.raw); k.T_raw = a.T_raw;
+  k.win_rotated = a.kv_fmt == kF32 || a.Tq > 8;
+  k.pos_q = *n_pos;
+  k.pos_raw = *n_pos + a.B;
+  for (int b = 0; b < a.B; ++b) {
+    L->pos[*n_pos + b] = a.qpos.v[b];
+    L->pos[*n_pos + a.B + b] = a.rawpos.v[b];
+  }
+  *n_pos += 2 * a.B;
+  return k;
+}
+
+// With many queries per sequence the window rows are shared by many blocks:
+// rotate them once up front (and, on the float32 path, the query angles).
+// In decode each block rotates its own.
+hipError_t rotate_window(const AttendArgs& a, const AttnPlan& p, void* ws, hipStream_t st) {
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  WinArgs wa{};
+  wa.raw = static_cast<const uint8_t*>(a.raw);
+  wa.win = w8 + p.off_win;
+  wa.win_row_bytes = p.win_row_bytes;
+  wa.zero_row = w8 + p.off_zero;
+  wa.fmt = a.kv_fmt; wa.B = a.B; wa.D = a.D; wa.r = a.r; wa.Tq = a.Tq; wa.W = a.W;
+  wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes;
+  make_rope_table(&wa.rope, a.r, a.theta);
+  wa.qpos = a.qpos; wa.rawpos = a.rawpos;
+  wa.ang = reinterpret_cast<float2*>(w8 + p.off_ang);
+  wa.n_win_items = (int64_t)a.B * p.win_rows * (a.D / 8);
+  const int64_t n = wa.n_win_items + (int64_t)a.B * a.Tq * (a.r / 2);
+  const unsigned blocks = (unsigned)std::max<int64_t>(1, (n + 255) / 256);
+  hipLaunchKernelGGL(rope_window_kernel, dim3(blocks), dim3(256), 0, st, wa);
+  return hipGetLastError();
+}
+
+AttnPlan launch_plan(const AttendArgs& a, int grid_target = kGridTarget) {
+  const bool f32 = a.kv_fmt == kF32;
+  const AttnPlan loose = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32, false, grid_target);
+  if (a.mode != 1 || f32) return loose;
+  const AttnPlan tight = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32, true, grid_target);
+  return tight.nsplit <= loose.nsplit ? tight : loose;
+}
+
+// Plans of n calls launched together: the one-wave grid (kGridTarget
+// workgroups) is shared in proportion to each call's tiles, and while the
+// calls' workgroups exceed it, the call with the most gives up one split per
+// work item.  A smaller target never adds splits, so every plan fits the
+// workspace its call was sized for.
+void plan_group(const AttendArgs* calls, const int* idx, int n, AttnPlan* plans) {
+  if (n == 1) { plans[0] = launch_plan(calls[idx[0]]); return; }
+  int target[kAttendGroup];
+  double cost[kAttendGroup], total = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const AttnPlan p = launch_plan(calls[idx[i]]);
+    cost[i] = (double)p.n_work * (double)((p.max_entries + kTile - 1) / kTile);
+    total += cost[i];
+  }
+  for (int i = 0; i < n; ++i) {
+    const AttnPlan p = launch_plan(calls[idx[i]]);
+    target[i] = std::max(p.n_work, (int)(kGridTarget * cost[i] / std::max(total, 1.0)));
+  }
+  for (;;) {
+    int64_t blocks = 0, worst_blocks = 0;
+    int worst = -1;
+    for (int i = 0; i < n; ++i) {
+      plans[i] = launch_plan(calls[idx[i]], target[i]);
+      const int64_t b = (int64_t)plans[i].nsplit * plans[i].n_work;
+      blocks += b;
+      if (target[i] > plans[i].n_work && b > worst_blocks) { worst = i; worst_blocks = b; }
+    }
+    if (blocks <= kGridTarget || worst < 0) return;
+    target[worst] = std::max(plans[worst].n_work, target[worst] - plans[worst].n_work);
+  }
 }
 
 }  // namespace
@@ -1039,76 +1200,86 @@ size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, in
   return make_plan(B, Tq, H, D, r, kv_fmt, n_entries, W, kv_fmt == kF32, false).total;
 }
 
-static AttnPlan launch_plan(const AttendArgs& a) {
-  const bool f32 = a.kv_fmt == kF32;
-  const AttnPlan loose = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32, false);
-  if (a.mode != 1 || f32) return loose;
-  const AttnPlan tight = make_plan(a.B, a.Tq, a.H, a.D, a.r, a.kv_fmt, a.n_entries, a.W, f32, true);
-  return tight.nsplit <= loose.nsplit ? tight : loose;
-}
-
 int attend_split_count(const AttendArgs& a) { return launch_plan(a).nsplit; }
 
-hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
-  const bool f32 = a.kv_fmt == kF32;
-  const AttnPlan p = launch_plan(a);
-  if (p.nsplit > kMaxSplit) return hipErrorInvalidValue;
-  if (a.B == 0 || a.Tq == 0) return hipSuccess;
-  uint8_t* w8 = static_cast<uint8_t*>(ws);
+// n independent calls: the float32 ones one by one; the others with plans
+// made together, their window rotations (prefill shapes) first, then one
+// attention launch per (D, KV format) and up to kAttendGroup calls sharing a
+// rotation table, each followed by the combine of its split calls.
+hipError_t launch_attend_group(const AttendArgs* calls, void* const* ws, int n, hipStream_t st) {
   hipError_t e;
-  // With many queries per sequence the window rows are shared by many blocks:
-  // rotate them once up front.  In decode each block rotates its own.
-  const bool win_rotated = f32 || a.Tq > 8;
-  if (win_rotated && a.W > 0) {
-    // Rotated window rows (and the query angles of the float32 path).
-    WinArgs wa{};
-    wa.raw = static_cast<const uint8_t*>(a.raw);
-    wa.win = w8 + p.off_win;
-    wa.win_row_bytes = p.win_row_bytes;
-    wa.zero_row = w8 + p.off_zero;
-    wa.fmt = a.kv_fmt; wa.B = a.B; wa.D = a.D; wa.r = a.r; wa.Tq = a.Tq; wa.W = a.W;
-    wa.T_raw = a.T_raw; wa.win_rows = p.win_rows; wa.row_bytes = p.row_bytes;
-    make_rope_table(&wa.rope, a.r, a.theta);
-    wa.qpos = a.qpos; wa.rawpos = a.rawpos;
-    wa.ang = reinterpret_cast<float2*>(w8 + p.off_ang);
-    wa.n_win_items = (int64_t)a.B * p.win_rows * (a.D / 8);
-    const int64_t n = wa.n_win_items + (int64_t)a.B * a.Tq * (a.r / 2);
-    const unsigned blocks = (unsigned)std::max<int64_t>(1, (n + 255) / 256);
-    hipLaunchKernelGGL(rope_window_kernel, dim3(blocks), dim3(256), 0, st, wa);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+  std::vector<int> idx;
+  for (int i = 0; i < n; ++i) {
+    const AttendArgs& a = calls[i];
+    if (a.B == 0 || a.Tq == 0) continue;
+    if (a.kv_fmt == kF32) {
+      const AttnPlan p = launch_plan(a);
+      if (a.W > 0 && (e = rotate_window(a, p, ws[i], st)) != hipSuccess) return e;
+      KLaunch L{};
+      int n_pos = 0;
+      L.k[0] = make_kargs(a, p, ws[i], &L, &n_pos);
+      L.n = 1;
+      RopeTable rt;
+      make_rope_table(&rt, a.r, a.theta);
+      for (int q = 0; q < kMaxRopePairs; ++q) L.freq[q] = rt.inv_freq[q];
+      const size_t lds = ((size_t)a.H * a.D + 32 * a.D + a.H * 32 + 3 * a.H) * 4 + 32 * 4;
+      TimedLaunch tl(kKernelAttend, st);
+      hipLaunchKernelGGL(attend_f32_kernel, dim3(p.n_work), dim3(256), lds, st, L);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      continue;
+    }
+    idx.push_back(i);
   }
-  KArgs k{};
-  k.q = a.q; k.kv = static_cast<const uint8_t*>(a.kv); k.idx = a.idx; k.win = w8 + p.off_win;
-  k.win_row_bytes = p.win_row_bytes;
-  k.sink = a.sink; k.out = a.out; k.zero_row = w8 + p.off_zero;
-  k.ang = reinterpret_cast<const float2*>(w8 + p.off_ang);
-  k.part_o = p.nsplit > 1 ? reinterpret_cast<uint16_t*>(w8 + p.off_po) : nullptr;
-  k.part_ml = p.nsplit > 1 ? reinterpret_cast<float*>(w8 + p.off_pml) : nullptr;
-  k.mode = a.mode; k.N = a.N; k.k = a.k; k.m = a.m; k.W = a.W; k.B = a.B; k.Tq = a.Tq;
-  k.H = a.H; k.D = a.D; k.r = a.r; k.theta = a.theta;
-  make_rope_table(&k.rope, a.r, a.theta);
-  k.scale_log2 = a.scale * 1.4426950408889634f;
-  k.q_norm_gain = a.q_norm_gain;
-  k.norm_eps = a.norm_eps;
-  k.G = p.G; k.Hs = p.Hs; k.n_htiles = p.n_htiles; k.n_qgroups = p.n_qgroups;
-  k.nsplit = p.nsplit; k.chunk = p.chunk; k.wchunk = p.wchunk; k.win_rows = p.win_rows; k.row_bytes = p.row_bytes;
-  k.qpos = a.qpos;
-  k.raw = static_cast<const uint8_t*>(a.raw); k.T_raw = a.T_raw; k.rawpos = a.rawpos;
-  k.win_rotated = win_rotated;
-  if (f32) {
-    const size_t lds = ((size_t)a.H * a.D + 32 * a.D + a.H * 32 + 3 * a.H) * 4 + 32 * 4;
-    TimedLaunch tl(kKernelAttend, st);
-    hipLaunchKernelGGL(attend_f32_kernel, dim3(p.n_work), dim3(256), lds, st, k);
-    return hipGetLastError();
+  const int m = (int)idx.size();
+  // plans: together for up to kAttendGroup calls at a time, in call order
+  for (int g0 = 0; g0 < m; g0 += kAttendGroup) {
+    const int gn = std::min(kAttendGroup, m - g0);
+    AttnPlan plans[kAttendGroup];
+    plan_group(calls, idx.data() + g0, gn, plans);
+    for (int i = 0; i < gn; ++i) {
+      const AttendArgs& a = calls[idx[g0 + i]];
+      if (plans[i].nsplit > kMaxSplit) return hipErrorInvalidValue;
+      if (a.W > 0 && a.Tq > 8 && (e = rotate_window(a, plans[i], ws[idx[g0 + i]], st)) != hipSuccess) return e;
+    }
+    // launches: calls of one (D, KV format) and one rotation table together
+    bool done[kAttendGroup] = {};
+    for (int i = 0; i < gn; ++i) {
+      if (done[i]) continue;
+      const AttendArgs& a0 = calls[idx[g0 + i]];
+      KLaunch L{};
+      int n_pos = 0;
+      size_t lds = 0;
+      for (int j = i; j < gn; ++j) {
+        const AttendArgs& a = calls[idx[g0 + j]];
+        const bool same_table = a.r == a0.r && (a.r == 0 || a.theta == a0.theta);
+        if (done[j] || a.D != a0.D || a.kv_fmt != a0.kv_fmt || !same_table ||
+            n_pos + 2 * a.B > kAttendPos)
+          continue;
+        const AttnPlan& p = plans[j];
+        L.k[L.n] = make_kargs(a, p, ws[idx[g0 + j]], &L, &n_pos);
+        L.blk_end[L.n] = (L.n ? L.blk_end[L.n - 1] : 0u) + (uint32_t)p.nsplit * (uint32_t)p.n_work;
+        ++L.n;
+        lds = std::max(lds, (size_t)p.G * (a.r / 2) * sizeof(float2));   // the block's query angles
+        done[j] = true;
+      }
+      RopeTable rt;
+      make_rope_table(&rt, a0.r, a0.theta);
+      for (int q = 0; q < kMaxRopePairs; ++q) L.freq[q] = rt.inv_freq[q];
+      if (a0.kv_fmt == kBF16) {
+        e = a0.D == 128 ? launch_mfma<128, kBF16>(L, lds, st)
+          : a0.D == 256 ? launch_mfma<256, kBF16>(L, lds, st) : launch_mfma<512, kBF16>(L, lds, st);
+      } else {
+        e = a0.D == 128 ? launch_mfma<128, kMixed>(L, lds, st)
+          : a0.D == 256 ? launch_mfma<256, kMixed>(L, lds, st) : launch_mfma<512, kMixed>(L, lds, st);
+      }
+      if (e != hipSuccess) return e;
+    }
   }
-  if (a.kv_fmt == kBF16) {
-    if (a.D == 128) return launch_mfma<128, kBF16>(k, p, st);
-    if (a.D == 256) return launch_mfma<256, kBF16>(k, p, st);
-    return launch_mfma<512, kBF16>(k, p, st);
-  }
-  if (a.D == 128) return launch_mfma<128, kMixed>(k, p, st);
-  if (a.D == 256) return launch_mfma<256, kMixed>(k, p, st);
-  return launch_mfma<512, kMixed>(k, p, st);
+  return hipSuccess;
+}
+
+hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st) {
+  return launch_attend_group(&a, &ws, 1, st);
 }
 
 }  // namespace lac

@@ -43,12 +43,14 @@ struct CompressArgs {
   int64_t kv_bstride, z_bstride, out_bstride;  // rows
   const float* norm_gain;   // [D] or null: RMSNorm of each entry before its rotation
   float norm_eps;
-  // set by the launcher: tokens per thread, entries, block (gb, s, epb)
-  int per, N, gb, s, epb;
-  RopeTable rope;
   Positions pos0;
 };
 hipError_t launch_compress(CompressArgs a, hipStream_t st);
+// n independent calls (none reads what another writes), in as few launches
+// as their input formats and the launch's argument pools allow.
+hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t st);
+// Launch limit: a call's workgroups, at most B * floor(T/m) * D/8, stay below 2^31.
+constexpr int64_t kCompressMaxGroups = (int64_t)1 << 31;
 
 // ---------------------------------------------------------------- indexer + top-k
 struct IndexerArgs {
@@ -109,6 +111,10 @@ size_t attend_workspace_bytes(int B, int Tq, int H, int D, int r, int kv_fmt, in
 constexpr int kMaxSplit = 2048;
 int attend_split_count(const AttendArgs& a);
 hipError_t launch_attend(const AttendArgs& a, void* ws, hipStream_t st);
+// n independent calls (none reads what another writes; workspaces disjoint),
+// their splits planned together so that they share one wave of workgroups,
+// in one attention launch (and one combine launch) per kernel instance.
+hipError_t launch_attend_group(const AttendArgs* calls, void* const* ws, int n, hipStream_t st);
 
 // ---------------------------------------------------------------- grouped output projection
 struct ProjectArgs {

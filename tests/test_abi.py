@@ -134,3 +134,64 @@ def test_attend_rejects_bad_arguments(L):
 def test_timer_rejects_unknown_kernel(L):
     assert L.lib.lac_time_next_launch(99, None, None) == 1
     assert L.lib.lac_time_next_launch(1, None, None) == 0    # disarm
+
+
+# ---------------------------------------------------------------- launch groups
+def _csa_compress_args(fake, stream=None):
+    # a valid call: bf16 in, bf16 out, B = 1, T = 16, D = 128, m = 4, r = 64
+    return (fake, fake, 1, fake, 1, 1, 16, 128, 4, 64, 1e4, None, 16, 16, 4, stream)
+
+
+def _hca_attend_args(fake, ws, stream=None):
+    # q, q_dtype, hkv, kv_dtype, N, m, raw, T_raw, raw_pos0, W, sink, scale, B, Tq, H, D, r,
+    # theta, q_pos0, out, ws, ws_bytes, stream
+    return (fake, 1, fake, 1, 8, 128, fake, 16, None, 16, None, 0.0, 1, 1, 64, 512, 64, 1e4,
+            (ctypes.c_int64 * 1)(15), fake, ws, 1 << 24, stream)
+
+
+def test_group_state_machine(L):
+    lib = L.lib
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.lac_group_end(None) == 1 and "no launch group" in _err(L)
+    assert lib.lac_group_cancel() == 1
+    assert lib.lac_group_begin(None) == 0
+    assert lib.lac_group_begin(None) == 1 and "already open" in _err(L)
+    # recorded, not launched: valid calls return OK without a device
+    assert lib.csa_compress(*_csa_compress_args(fake)) == 0
+    # validation is unchanged inside a group
+    bad = list(_csa_compress_args(fake))
+    bad[7] = 100
+    assert lib.csa_compress(*bad) == 1
+    # another stream than the group's
+    assert lib.csa_compress(*_csa_compress_args(fake, ctypes.c_void_p(0x20000))) == 1
+    assert "stream" in _err(L)
+    # entry points that cannot be recorded
+    assert lib.grouped_output_projection(fake, fake, fake, 1, 8, 128, 1, 256, 256, fake, fake,
+                                         1 << 20, None) == 1
+    assert "launch group" in _err(L)
+    assert lib.indexer_topk(fake, fake, fake, 1, 1, 1, 64, 128, 64, None, 4, 16, fake, None,
+                            fake, 1 << 20, None) == 1
+    assert lib.lac_group_cancel() == 0         # drops the recorded call
+    assert lib.lac_group_cancel() == 1
+    assert lib.lac_group_begin(None) == 0
+    assert lib.lac_group_end(None) == 0        # empty group: nothing to enqueue
+
+
+def test_group_refuses_shared_attention_workspace(L):
+    lib = L.lib
+    fake = ctypes.c_void_p(0x10000)
+    ws = ctypes.c_void_p(0x1000000)
+    assert lib.lac_group_begin(None) == 0
+    assert lib.hca_attend(*_hca_attend_args(fake, ws)) == 0
+    assert lib.hca_attend(*_hca_attend_args(fake, ws)) == 0
+    assert lib.lac_group_end(None) == 3 and "workspace" in _err(L)
+    assert lib.lac_group_end(None) == 1        # the failed end closed the group
+
+
+def test_group_end_on_another_stream_closes_the_group(L):
+    lib = L.lib
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.lac_group_begin(None) == 0
+    assert lib.csa_compress(*_csa_compress_args(fake)) == 0
+    assert lib.lac_group_end(ctypes.c_void_p(0x20000)) == 1
+    assert lib.lac_group_end(None) == 1

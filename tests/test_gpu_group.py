@@ -1,0 +1,186 @@
+"""GPU parity of launch groups (lac_group_begin / lac_group_end): calls
+recorded in a group and enqueued together give the oracle's results, as the
+same calls made one by one do.  Compress calls keep their own block
+decomposition in the grouped launch, so their outputs are bit-identical to
+the ungrouped calls'; grouped attention calls get their key splits planned
+together, so they are checked against the oracle (深度解析 DeepSeek-V4, CSA
+and HCA sections; QbitAI rewrite: core attention) at the attention
+tolerance, and against the ungrouped outputs at that tolerance too."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_compressor_amd as lac
+import oracle
+import synth
+from parity import as_f64, check_attention, check_compressed, host
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+FMT_T = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+# ---------------------------------------------------------------- compress
+def _compress_case(B, T, D, m, r, in_fmt, out_fmt, pos0, seed):
+    x = synth.store(synth.normal(seed, "x", (B, T, D)), in_fmt).to(DEV)
+    z = synth.store(synth.normal(seed, "z", (B, T, D)), in_fmt).to(DEV)
+    N = T // m
+    width = D + r if out_fmt == "mixed" else D // 2 + D // 32 if out_fmt == "mxfp4" else D
+
+    def new_out():
+        if out_fmt in ("mixed", "mxfp4"):
+            return torch.full((B, N, width), 0x55, dtype=torch.uint8, device=DEV)
+        return torch.full((B, N, D), 7.0, dtype=FMT_T[out_fmt], device=DEV)
+
+    return dict(x=x, z=z, B=B, T=T, D=D, m=m, r=r, in_fmt=in_fmt, out_fmt=out_fmt, pos0=pos0,
+                new_out=new_out)
+
+
+def _compress(c, out):
+    fn = lac.hca_compress if c["m"] >= 64 else lac.csa_compress
+    fn(c["x"], c["z"], out, m=c["m"], rope_dims=c["r"], pos0=c["pos0"])
+
+
+def _check_compress_group(cases):
+    singles = []
+    for c in cases:
+        out = c["new_out"]()
+        _compress(c, out)
+        singles.append(out)
+    grouped = [c["new_out"]() for c in cases]
+    with lac.group():
+        for c, out in zip(cases, grouped):
+            _compress(c, out)
+    torch.cuda.synchronize()
+    for c, g, s in zip(cases, grouped, singles):
+        print(f"group compress B={c['B']} T={c['T']} D={c['D']} m={c['m']} r={c['r']} "
+              f"{c['in_fmt']}->{c['out_fmt']}", flush=True)
+        assert torch.equal(g.view(torch.uint8), s.view(torch.uint8))
+        ref = oracle.compress(host(c["x"]), host(c["z"]), synth.DTYPE_CODES[c["in_fmt"]], c["B"],
+                              c["T"], c["D"], c["m"], c["r"], 10000.0, c["pos0"])
+        check_compressed(g, ref, c["out_fmt"], c["D"], c["r"])
+
+
+def test_decode_step_compress_group():
+    # a decode step's three calls: the newest HCA entry and CSA entry of four
+    # sequences at 1M positions (mixed rows), and the indexer keys (bf16, no rope)
+    pos = [(1 << 20) - 128, (1 << 20) - 256, 4096, 128 * 77]
+    _check_compress_group([
+        _compress_case(4, 128, 512, 128, 64, "bf16", "mixed", pos, 1),
+        _compress_case(4, 4, 512, 4, 64, "bf16", "mixed", [p + 124 for p in pos], 2),
+        _compress_case(4, 4, 128, 4, 0, "bf16", "bf16", [p + 124 for p in pos], 3),
+    ])
+
+
+def test_compress_group_mixed_shapes_formats_and_tables():
+    # block shapes of different sizes in one launch, MXFP4 keys, two rotation
+    # tables, f32 inputs in a launch of their own, more calls than one launch holds
+    _check_compress_group([
+        _compress_case(2, 4 * 37 + 3, 512, 4, 64, "bf16", "mixed", [0, 4096], 4),
+        _compress_case(1, 128 * 3 + 17, 256, 128, 32, "bf16", "bf16", [1 << 19], 5),
+        _compress_case(3, 64, 128, 4, 0, "bf16", "mxfp4", None, 6),
+        _compress_case(3, 64, 32, 4, 0, "f32", "f32", None, 7),
+        _compress_case(2, 16 * 9, 256, 16, 64, "bf16", "bf16", [0, 16 * 3], 8),
+        _compress_case(1, 40, 128, 8, 16, "f32", "bf16", [64], 9),
+    ])
+
+
+# ---------------------------------------------------------------- attention
+def _indices(seed, B, Tq, q_pos0, N, m, k):
+    rng = np.random.default_rng(seed)
+    idx = np.full((B, Tq, k), -1, np.int32)
+    for b in range(B):
+        for i in range(Tq):
+            nv = min(N, (q_pos0[b] + i) // m)
+            n = min(k, nv)
+            if n:
+                idx[b, i, :n] = np.sort(rng.choice(nv, n, replace=False))
+    return idx
+
+
+def _attend_case(mode, B, Tq, H, D, r, N, k, m, W, q_pos0, fmt, seed, sink=False):
+    q_fmt = "f32" if fmt == "f32" else "bf16"
+    q = synth.store(synth.normal(seed, "q", (B, Tq, H, D)), q_fmt)
+    kv = synth.store(synth.normal(seed, "kv", (B, N, D)), fmt, r)
+    raw_pos0 = [max(0, p - W + 1) for p in q_pos0]
+    T_raw = max(q_pos0[b] + Tq - raw_pos0[b] for b in range(B)) if W > 0 else 0
+    raw = synth.store(synth.normal(seed, "raw", (B, max(T_raw, 1), D)), fmt, r)
+    sk = synth.normal(seed, "sink", (H,)) * 2.0 if sink else None
+    idx = _indices(seed, B, Tq, q_pos0, N, m, k) if mode == 0 else None
+    ref = oracle.attend(host(q), synth.DTYPE_CODES[q_fmt], host(kv), synth.DTYPE_CODES[fmt], N,
+                        mode, None if idx is None else idx.reshape(B * Tq, k), k, m, host(raw),
+                        raw.shape[1], raw_pos0, W,
+                        None if sk is None else host(sk).astype(np.float64), 0.0, B, Tq, H, D,
+                        r, 10000.0, q_pos0, [(b, i) for b in range(B) for i in range(Tq)])
+    n_ent = k if mode == 0 else N
+    need = lac.attend_workspace_size(B, Tq, H, D, r, synth.DTYPE_CODES[fmt], n_ent, W)
+    return dict(mode=mode, q=q.to(DEV), kv=kv.to(DEV), raw=raw.to(DEV), W=W, m=m, r=r,
+                q_pos0=q_pos0, raw_pos0=raw_pos0, idx=None if idx is None else torch.from_numpy(idx).to(DEV),
+                sink=None if sk is None else sk.to(DEV), ref=ref, shape=(B, Tq, H, D),
+                need=need, tag=f"mode={mode} B={B} Tq={Tq} H={H} D={D} N={N} k={k} W={W} {fmt}")
+
+
+def _attend(c, out, ws):
+    if c["mode"] == 0:
+        lac.csa_attend(c["q"], c["kv"], c["idx"], c["raw"], c["W"], q_pos0=c["q_pos0"],
+                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], sink=c["sink"], out=out,
+                       workspace=ws)
+    else:
+        lac.hca_attend(c["q"], c["kv"], c["raw"], c["W"], m=c["m"], q_pos0=c["q_pos0"],
+                       raw_pos0=c["raw_pos0"], rope_dims=c["r"], sink=c["sink"], out=out,
+                       workspace=ws)
+
+
+def _check_attend_group(cases):
+    singles = []
+    for c in cases:
+        out = torch.empty_like(c["q"])
+        _attend(c, out, None)
+        singles.append(out)
+    # each call its own workspace, filled with garbage first
+    wss = [torch.full((max(c["need"], 256),), 0xA5, dtype=torch.uint8, device=DEV) for c in cases]
+    grouped = [torch.full_like(c["q"], 3.0) for c in cases]
+    with lac.group():
+        for c, out, ws in zip(cases, grouped, wss):
+            _attend(c, out, ws)
+    torch.cuda.synchronize()
+    for c, g, s in zip(cases, grouped, singles):
+        print(f"group attend {c['tag']}", flush=True)
+        B, Tq, H, D = c["shape"]
+        gf = as_f64(g).reshape(B * Tq, H, D)
+        check_attention(gf, c["ref"], "grouped " + c["tag"])
+        check_attention(gf, as_f64(s).reshape(B * Tq, H, D), "grouped vs single " + c["tag"])
+
+
+def test_decode_pair_attention_group():
+    # the layer pair's decode step: CSA over k selected entries and HCA over
+    # every visible entry, both with split-K, planned together
+    pos = [(1 << 20) - 1, 700_001, 300_003, 131_075]
+    _check_attend_group([
+        _attend_case(0, 4, 1, 64, 512, 64, 40000, 512, 4, 128, pos, "mixed", 11, sink=True),
+        _attend_case(1, 4, 1, 64, 512, 64, 8192, 0, 128, 128, pos, "mixed", 12, sink=True),
+    ])
+
+
+def test_attention_group_prefill_f32_and_several_launches():
+    # a prefill shape (window rotated up front), an f32 call (launched on its
+    # own), D = 128 and 512 (separate launches), and five bf16 calls (more
+    # than one launch holds)
+    _check_attend_group([
+        _attend_case(0, 1, 40, 64, 512, 64, 200, 16, 4, 24, [900], "mixed", 13),
+        _attend_case(1, 2, 1, 64, 512, 64, 300, 0, 128, 64, [40_000, 38_500], "bf16", 14),
+        _attend_case(0, 2, 9, 8, 128, 64, 30, 5, 4, 3, [100, 7], "f32", 15, sink=True),
+        _attend_case(1, 1, 3, 16, 128, 64, 90, 0, 16, 32, [1500], "bf16", 16),
+        _attend_case(0, 3, 1, 64, 512, 64, 5000, 256, 4, 128, [20_003, 19_999, 20_400], "mixed", 17),
+        _attend_case(1, 1, 1, 128, 512, 64, 2000, 0, 128, 0, [256_100], "mixed", 18),
+    ])
+
+
+def test_group_refuses_shared_workspace_on_the_gpu():
+    c = _attend_case(1, 1, 1, 64, 512, 64, 64, 0, 128, 16, [9000], "mixed", 19)
+    ws = torch.empty(max(c["need"], 256), dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(c["q"])
+    with pytest.raises(lac.LacError):
+        with lac.group():
+            _attend(c, out, ws)
+            _attend(c, out, ws)
