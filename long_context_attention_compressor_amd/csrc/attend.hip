@@ -442,6 +442,17 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KLaunch L) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = wave & 3, dh = DS == 2 ? wave >> 2 : 0;
   const int l = tid & 63, lr = l & 15, lq = l >> 4;
+  // Entry rows of each 16-row half of a tile are read in the order
+  // rho(v) = 2 (v mod 8) + v / 8: the QK operand lane lr reads row rho(lr)
+  // and the transposed PV read of lane (lr, lq) row rho(4 lq + lr / 4).  The
+  // 16 rows of a 16-lane 16-byte read still hit 16 different 16-byte bank
+  // groups (row stride = 16 mod 256 bytes), and the 8 rows of a 32-lane
+  // transposed read (32 bytes each) now lie 32 bytes apart, so neither
+  // conflicts.  The softmax lane then holds entries rho(4 lq + i) (+ 16):
+  // the staging writes each entry's visibility at position rho^-1(row).
+  const int q_row = ((lr & 7) << 1) | (lr >> 3);
+  const int pv_v = 4 * lq + (lr >> 2);
+  const int pv_row = ((pv_v & 7) << 1) | (pv_v >> 3);
   uint32_t lb = 0;
   const int ci = MULTI ? launch_call(L, blockIdx.x, &lb) : 0;
   const KArgs& a = L.k[ci];
@@ -650,8 +661,9 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KLaunch L) {
       }
     }
     if (st_part == 0) {
-      vis_lo[buf][st_e] = st_lo;
-      vis_span[buf][st_e] = st_span;
+      const int vpos = (((st_e & 1) << 3) | ((st_e & 15) >> 1)) | (st_e & 16);   // rho^-1
+      vis_lo[buf][vpos] = st_lo;
+      vis_span[buf][vpos] = st_span;
     }
   };
 
