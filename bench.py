@@ -52,9 +52,11 @@ BF16_PEAK_TFLOPS = 2500.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273731094, "csa_decode_128k": 277462158,
-                       "csa_chunk_prefill": 1302840682, "pair_decode_1m_e4m3_indexer": 139523079}
-SCORE_TRAFFIC_SOURCE_SHA256 = "2752de378f707f48b2411f0971f74669c2da734ed1ba2269681b4b572e34f332"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273731584, "pair_decode_1m_ungrouped": 273731584,
+                       "csa_decode_128k": 277464064, "csa_chunk_prefill": 1330352128,
+                       "pair_decode_1m_fp8_indexer": 139360256,
+                       "pair_decode_1m_mxfp4_indexer": 76702720}
+SCORE_TRAFFIC_SOURCE_SHA256 = "b4f7338e6bf5913564328b601bac09fc91ed627f9e88e56676fd6106312d4420"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
@@ -196,50 +198,59 @@ class PairDecode:
                 "csa_window_overlap": self.overlap,
                 "cache_sets": len(self.sets)}
 
-    def cpu_sample(self):
-        """The oracle's whole decode step for sequence 0 of cache set 0."""
+    def cpu_sample(self, min_seconds=10.0, max_steps=48):
+        """The oracle's whole decode step, one sequence at a time: sequences
+        0..B-1 of cache sets 0, 1, ... in turn until min_seconds of oracle
+        work (at most max_steps); only the oracle's calls are timed."""
         import numpy as np
 
         import oracle
         from oracle import chain
         import synth
 
-        c, s, ctx = self.c, self.sets[0], self.ctx
-        h = {k_: synth.host_bytes(v[:1]) for k_, v in s.items() if isinstance(v, torch.Tensor)}
+        c, ctx = self.c, self.ctx
         N, Nh = c["N"], c["Nh"]
-        t0 = time.perf_counter()
-        ckv = h["ckv"].reshape(1, N, -1).copy()
-        KI = h["KI"].reshape(1, N, -1).copy()
-        hkv = h["hkv"].reshape(1, Nh, -1).copy()
         g = None if self.gain is None else self.gain.cpu().numpy()
-        if self.overlap:
-            vals = oracle.compress_overlap(h["new_kv_csa"], h["new_z_csa"], oracle.BF16, 1, c["m"],
-                                           c["D"], c["m"], self.overlap, c["r"], 1e4, ctx - c["m"])
-            ckv[:, N - 1:] = oracle.encode_rows(vals.reshape(1, c["D"]), oracle.MIXED,
-                                                c["r"]).reshape(1, 1, -1)
-        else:
-            ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16", "mixed",
-                                                  1, c["m"], c["D"], c["m"], c["r"], 1e4,
-                                                  ctx - c["m"], norm_gain=g)
-        KI.view(np.uint8)[:, N - 1:] = chain.compress_store(
-            h["new_kI"], h["new_zI"], "bf16", self.ki_fmt, 1, c["m"], c["dI"], c["m"], 0, 1e4,
-            ctx - c["m"])
-        hkv[:, Nh - 1:] = chain.compress_store(h["new_kv_hca"], h["new_z_hca"], "bf16", "mixed",
-                                               1, c["m_hca"], c["D"], c["m_hca"], c["r"], 1e4,
-                                               ctx - c["m_hca"], norm_gain=g)
-        idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, self.qi_fmt, 1, 1, c["HI"], c["dI"], N,
-                                     ctx, c["m"], c["k"], k_fmt=self.ki_fmt)
-        oracle.attend(h["q_csa"], oracle.BF16, ckv, oracle.MIXED, N, 0, idx, c["k"], c["m"],
-                      h["raw_csa"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
-                      c["r"], 1e4, ctx, q_norm_gain=g)
-        oracle.attend(h["q_hca"], oracle.BF16, hkv, oracle.MIXED, Nh, 1, None, 0, c["m_hca"],
-                      h["raw_hca"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"], c["D"],
-                      c["r"], 1e4, ctx, q_norm_gain=g)
-        el = time.perf_counter() - t0
-        return {"value": 1.0 / el, "unit": self.unit, "seconds": el,
-                "sample": "the full decode step (compress newest blocks, index 262144 entries, "
-                          "top-2048, CSA + HCA attention, 64 heads) of 1 of the 4 sequences, "
-                          "cache set 0"}
+        el, steps = 0.0, 0
+        while steps < max_steps and (el < min_seconds or steps == 0):
+            s = self.sets[(steps // self.B) % len(self.sets)]
+            b = steps % self.B
+            h = {k_: synth.host_bytes(v[b:b + 1]) for k_, v in s.items()
+                 if isinstance(v, torch.Tensor)}
+            ckv = h["ckv"].reshape(1, N, -1).copy()
+            KI = h["KI"].reshape(1, N, -1).copy()
+            hkv = h["hkv"].reshape(1, Nh, -1).copy()
+            t0 = time.perf_counter()
+            if self.overlap:
+                vals = oracle.compress_overlap(h["new_kv_csa"], h["new_z_csa"], oracle.BF16, 1,
+                                               c["m"], c["D"], c["m"], self.overlap, c["r"], 1e4,
+                                               ctx - c["m"])
+                ckv[:, N - 1:] = oracle.encode_rows(vals.reshape(1, c["D"]), oracle.MIXED,
+                                                    c["r"]).reshape(1, 1, -1)
+            else:
+                ckv[:, N - 1:] = chain.compress_store(h["new_kv_csa"], h["new_z_csa"], "bf16",
+                                                      "mixed", 1, c["m"], c["D"], c["m"], c["r"],
+                                                      1e4, ctx - c["m"], norm_gain=g)
+            KI.view(np.uint8)[:, N - 1:] = chain.compress_store(
+                h["new_kI"], h["new_zI"], "bf16", self.ki_fmt, 1, c["m"], c["dI"], c["m"], 0, 1e4,
+                ctx - c["m"])
+            hkv[:, Nh - 1:] = chain.compress_store(h["new_kv_hca"], h["new_z_hca"], "bf16",
+                                                   "mixed", 1, c["m_hca"], c["D"], c["m_hca"],
+                                                   c["r"], 1e4, ctx - c["m_hca"], norm_gain=g)
+            idx, _, _ = chain.csa_select(h["qI"], h["w"], KI, self.qi_fmt, 1, 1, c["HI"], c["dI"],
+                                         N, ctx, c["m"], c["k"], k_fmt=self.ki_fmt)
+            oracle.attend(h["q_csa"], oracle.BF16, ckv, oracle.MIXED, N, 0, idx, c["k"], c["m"],
+                          h["raw_csa"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"],
+                          c["D"], c["r"], 1e4, ctx, q_norm_gain=g)
+            oracle.attend(h["q_hca"], oracle.BF16, hkv, oracle.MIXED, Nh, 1, None, 0, c["m_hca"],
+                          h["raw_hca"], c["W"], c["raw_pos0"], c["W"], None, 0.0, 1, 1, c["H"],
+                          c["D"], c["r"], 1e4, ctx, q_norm_gain=g)
+            el += time.perf_counter() - t0
+            steps += 1
+        return {"value": steps / el, "unit": self.unit, "seconds": el,
+                "sample": f"{steps} single-sequence decode steps (compress newest blocks, index "
+                          f"262144 entries, top-2048, CSA + HCA attention, 64 heads), sequences "
+                          f"0-{self.B - 1} of the cache sets in turn"}
 
 
 class PairDecodeUngrouped(PairDecode):

@@ -63,6 +63,13 @@ def test_bf16_decode_split_path():
     assert len(same) >= 1
 
 
+def test_bf16_decode_split_path_rows_of_different_lengths():
+    # one launch filters every row's chunks and the last chunk of each row to
+    # finish resolves it: a row keeping all its visible entries, rows with
+    # different chunk counts (ragged last chunks) and one seeing nothing
+    _run(4, 1, 64, 128, 20000, 4, 4096, [4 * 3000, 4 * 20000, 4 * 9000 + 1, 2], "bf16", 12)
+
+
 def test_bf16_decode_split_path_all_tied_takes_lowest_indices():
     B, N, k = 1, 20000, 700
     q = synth.store(synth.normal(3, "qI", (B, 1, 64, 128)), "bf16").to(DEV)
