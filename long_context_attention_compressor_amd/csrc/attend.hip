@@ -751,16 +751,210 @@ __global__ void __launch_bounds__(512) attend_mfma_kernel(KLaunch L) {
   float* sx_mine = &Sx[dh][rg][l][0];
   const float* sx_other = &Sx[DS - 1 - dh][rg][l][0];
 
-  for (int t = 0; t < t_win; ++t) {
-#define LAC_TILE_LO false
-#include "attend_tile.inc"
-#undef LAC_TILE_LO
+  // ---- the tile loop, software-pipelined by one tile: iteration t stages
+  // tile t and computes its logits (QK) while it runs the softmax and PV of
+  // tile t-1, so that the matrix cores work on one tile while the vector
+  // unit and LDS serve the other.  Each piece is inlined where it is used,
+  // once per combination of window-tile flags (wt: the tile holds window
+  // rows and adds their low parts), so that no runtime branch splits an
+  // iteration's instruction stream.
+#define LAC_INLINE __attribute__((always_inline))
+  // store tile t (waits for this thread's prefetched rows), publish it, and
+  // prefetch tile t+1
+  auto publish = [&](int t, auto wt_c) LAC_INLINE {
+    store_tile(t & 1, wt_c);
+    lds_barrier();            // tile t visible; every wave is done with tile t-2
+    if (t + 1 < n_tiles) load_tile(e_lo + (t + 1) * kTile, lo_loads && t + 1 >= t_win);
+  };
+  // partial S^T over this wave's half of D, entries 0-15 (s0) and 16-31 (s1);
+  // the entry fragments are read one group of k-steps ahead
+  auto qk = [&](int buf, auto wt_c, f32x4& s0, f32x4& s1) LAC_INLINE {
+    constexpr bool wt = decltype(wt_c)::value;
+    const uint8_t* E = Et[buf];
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int QG = Gm::KH >= 4 ? 4 : Gm::KH;
+    const uint8_t* eb = E + q_row * Gm::EROW + 16 * lq + 2 * dh * Gm::DW;
+    bf16x8 fa[2][QG], fb[2][QG];
+#pragma unroll
+    for (int u = 0; u < QG; ++u) {
+      fa[0][u] = *reinterpret_cast<const bf16x8*>(eb + 64 * u);
+      fb[0][u] = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * u);
+    }
+#pragma unroll
+    for (int gi = 0; gi < Gm::KH / QG; ++gi) {
+      const int cur = gi & 1;
+      if (gi + 1 < Gm::KH / QG) {
+#pragma unroll
+        for (int u = 0; u < QG; ++u) {
+          const int st = (gi + 1) * QG + u;
+          fa[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(eb + 64 * st);
+          fb[cur ^ 1][u] = *reinterpret_cast<const bf16x8*>(eb + 16 * Gm::EROW + 64 * st);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < QG; ++u) {
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[cur][u], qreg[gi * QG + u], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[cur][u], qreg[gi * QG + u], s1, 0, 0, 0);
+      }
+    }
+    if constexpr (wt) {
+      // the window rows' low parts over the wave's last nlo k-steps
+      auto lo_qk = [&](auto nk_c) LAC_INLINE {
+        constexpr int NK = decltype(nk_c)::value;
+#pragma unroll
+        for (int st = Gm::KH - NK; st < Gm::KH; ++st) {
+          const uint8_t* lb = Elo[buf] + q_row * kLoRow + 16 * lq + 2 * (dh * Gm::DW + 32 * st - lo_base);
+          const bf16x8 la = *reinterpret_cast<const bf16x8*>(lb);
+          const bf16x8 lc = *reinterpret_cast<const bf16x8*>(lb + 16 * kLoRow);
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(la, qreg[st], s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lc, qreg[st], s1, 0, 0, 0);
+        }
+      };
+      switch (nlo) {
+        case 1: lo_qk(std::integral_constant<int, 1>{}); break;
+        case 2: lo_qk(std::integral_constant<int, 2>{}); break;
+        case 3: lo_qk(std::integral_constant<int, Gm::KH >= 3 ? 3 : 1>{}); break;
+        case 4: lo_qk(std::integral_constant<int, Gm::KH >= 4 ? 4 : 1>{}); break;
+        default: break;
+      }
+    }
+  };
+  // the two halves' partial logits summed (D split over two waves): x = the
+  // lane's 8 raw logits of the tile
+  auto exchange = [&](const f32x4& s0, const f32x4& s1, float* x) LAC_INLINE {
+    float4 o0 = make_float4(0.f, 0.f, 0.f, 0.f), o1 = o0;
+    if constexpr (DS == 2) {
+      *reinterpret_cast<float4*>(sx_mine) = make_float4(s0[0], s0[1], s0[2], s0[3]);
+      *reinterpret_cast<float4*>(sx_mine + 4) = make_float4(s1[0], s1[1], s1[2], s1[3]);
+      lds_barrier();
+      o0 = *reinterpret_cast<const float4*>(sx_other);
+      o1 = *reinterpret_cast<const float4*>(sx_other + 4);
+    }
+    x[0] = s0[0] + o0.x; x[1] = s0[1] + o0.y; x[2] = s0[2] + o0.z; x[3] = s0[3] + o0.w;
+    x[4] = s1[0] + o1.x; x[5] = s1[1] + o1.y; x[6] = s1[2] + o1.z; x[7] = s1[3] + o1.w;
+  };
+  // online softmax of row `row` over the lane's 8 entries of the tile in
+  // buffer buf (the same in both waves of the row group), then
+  // O^T += E^T P^T over the wave's half of D, 16 output dims per MFMA; the
+  // transposed entry fragments are read PG output tiles ahead
+  auto softmax_pv = [&](int buf, auto wt_c, const float* xin) LAC_INLINE {
+    constexpr bool wt = decltype(wt_c)::value;
+    const uint8_t* E = Et[buf];
+    const int4 vl0 = *reinterpret_cast<const int4*>(&vis_lo[buf][4 * lq]);
+    const int4 vl1 = *reinterpret_cast<const int4*>(&vis_lo[buf][16 + 4 * lq]);
+    const int4 vs0 = *reinterpret_cast<const int4*>(&vis_span[buf][4 * lq]);
+    const int4 vs1 = *reinterpret_cast<const int4*>(&vis_span[buf][16 + 4 * lq]);
+    const int vlo[8] = {vl0.x, vl0.y, vl0.z, vl0.w, vl1.x, vl1.y, vl1.z, vl1.w};
+    const int vsp[8] = {vs0.x, vs0.y, vs0.z, vs0.w, vs1.x, vs1.y, vs1.z, vs1.w};
+    float x[8];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = (uint32_t)(g - vlo[i]) <= (uint32_t)vsp[i] ? xin[i] * scale_log2 : -INFINITY;
+      tmax = fmaxf(tmax, x[i]);
+    }
+    tmax = row_max4(tmax);
+    const bool moved = tmax > m_run + 8.f;          // also true for the first visible entry
+    const bool rescale = moved && m_run != -INFINITY;   // the row's O holds earlier entries
+    const float m_new = moved ? tmax : m_run;
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float al = moved ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+    float psum = 0.f;
+    uint32_t pk[4];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(x[i] - m_use), p1 = __builtin_amdgcn_exp2f(x[i + 1] - m_use);
+      psum += p0 + p1;
+      pk[i / 2] = pack_bf16x2(p0, p1);
+    }
+    l_part = l_part * al + psum;
+    m_run = m_new;
+    bf16x8 pb;
+    __builtin_memcpy(&pb, pk, 16);
+    if (__ballot(rescale)) {
+#pragma unroll
+      for (int dt = 0; dt < Gm::DH; ++dt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= al;
+    }
+    constexpr int PG = Gm::DH >= 8 ? 8 : Gm::DH;
+    const uint8_t* tb = E + pv_row * Gm::EROW + 8 * (lr & 3) + 2 * dh * Gm::DW;
+    bf16x4 lo[2][PG], hi[2][PG];
+#pragma unroll
+    for (int u = 0; u < PG; ++u) {
+      lo[0][u] = ds_read_tr(tb + 32 * u);
+      hi[0][u] = ds_read_tr(tb + 16 * Gm::EROW + 32 * u);
+    }
+#pragma unroll
+    for (int gi = 0; gi < Gm::DH / PG; ++gi) {
+      const int cur = gi & 1;
+      if (gi + 1 < Gm::DH / PG) {
+#pragma unroll
+        for (int u = 0; u < PG; ++u) {
+          const int dt = (gi + 1) * PG + u;
+          lo[cur ^ 1][u] = ds_read_tr(tb + 32 * dt);
+          hi[cur ^ 1][u] = ds_read_tr(tb + 16 * Gm::EROW + 32 * dt);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < PG; ++u) {
+        const bf16x8 ab = __builtin_shufflevector(lo[cur][u], hi[cur][u], 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[gi * PG + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, pb, oacc[gi * PG + u], 0, 0, 0);
+      }
+    }
+    if constexpr (wt) {
+      // the window rows' low parts of the wave's last 2 nlo output tiles
+      auto lo_pv = [&](auto nk_c) LAC_INLINE {
+        constexpr int NT2 = 2 * decltype(nk_c)::value;
+#pragma unroll
+        for (int dt = Gm::DH - NT2; dt < Gm::DH; ++dt) {
+          const uint8_t* tl = Elo[buf] + pv_row * kLoRow + 8 * (lr & 3) +
+                              2 * (dh * Gm::DW + 16 * dt - lo_base);
+          const bf16x8 ab = __builtin_shufflevector(ds_read_tr(tl), ds_read_tr(tl + 16 * kLoRow),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, pb, oacc[dt], 0, 0, 0);
+        }
+      };
+      switch (nlo) {
+        case 1: lo_pv(std::integral_constant<int, 1>{}); break;
+        case 2: lo_pv(std::integral_constant<int, 2>{}); break;
+        case 3: lo_pv(std::integral_constant<int, Gm::KH >= 3 ? 3 : 1>{}); break;
+        case 4: lo_pv(std::integral_constant<int, Gm::KH >= 4 ? 4 : 1>{}); break;
+        default: break;
+      }
+    }
+  };
+  // one iteration: tile t staged and its logits formed, tile t-1 consumed.
+  // The buffers of tile t-1 are staged over by tile t+1: the exchange's
+  // barrier (or, without a D split, one of its own) keeps that after every
+  // wave's PV of tile t-1.
+  auto iter = [&](int t, auto wq_c, auto wp_c, float* x) LAC_INLINE {
+    publish(t, wq_c);
+    f32x4 s0, s1;
+    qk(t & 1, wq_c, s0, s1);
+    softmax_pv((t - 1) & 1, wp_c, x);
+    if constexpr (DS == 1) lds_barrier();
+    exchange(s0, s1, x);
+  };
+  using F = std::integral_constant<bool, false>;
+  using T = std::integral_constant<bool, true>;
+  if (n_tiles > 0) {
+    float x[8];
+    {
+      f32x4 s0, s1;
+      if (t_win == 0) { publish(0, T{}); qk(0, T{}, s0, s1); }
+      else { publish(0, F{}); qk(0, F{}, s0, s1); }
+      exchange(s0, s1, x);
+    }
+    int t = 1;
+    for (; t < t_win; ++t) iter(t, F{}, F{}, x);            // both tiles before the window
+    if (t == t_win && t < n_tiles) { iter(t, T{}, F{}, x); ++t; }   // the first window tile
+    for (; t < n_tiles; ++t) iter(t, T{}, T{}, x);          // both tiles hold window rows
+    if (n_tiles - 1 >= t_win) softmax_pv((n_tiles - 1) & 1, T{}, x);
+    else softmax_pv((n_tiles - 1) & 1, F{}, x);
   }
-  for (int t = t_win; t < n_tiles; ++t) {
-#define LAC_TILE_LO true
-#include "attend_tile.inc"
-#undef LAC_TILE_LO
-  }
+#undef LAC_INLINE
 
   // ---- row sum over the row's four lanes
   float l_row = l_part;
