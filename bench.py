@@ -136,7 +136,8 @@ class PairDecode:
         g = self.gain
         grp = lac.group if self.grouped else contextlib.nullcontext
         # compress the newest blocks: the CSA layer's KV entry and indexer key,
-        # the HCA layer's entry (independent calls: one launch when grouped)
+        # the HCA layer's entry; grouped, the indexer's workspace zeroing joins
+        # their launch (independent calls: one launch)
         with grp():
             lac.csa_compress(s["new_kv_csa"], s["new_z_csa"], _rows(s["ckv"], N - 1, N), m=m,
                              rope_dims=c["r"], pos0=ctx - m, norm_gain=g, T=m,
@@ -145,9 +146,11 @@ class PairDecode:
                              rope_dims=0, pos0=ctx - m)
             lac.hca_compress(s["new_kv_hca"], s["new_z_hca"], _rows(s["hkv"], Nh - 1, Nh),
                              m=mh, rope_dims=c["r"], pos0=ctx - mh, norm_gain=g)
+            if self.grouped:
+                lac.indexer_topk_prepare(self.B, 1, N, c["k"], self.ws_idx)
         # the CSA layer's selection
         lac.indexer_topk(s["qI"], s["w"], s["KI"], m=m, k=c["k"], q_pos0=ctx, topk_idx=self.idx,
-                         workspace=self.ws_idx)
+                         workspace=self.ws_idx, prepared=self.grouped)
         # both layers' attention (independent: one attention and one combine
         # launch when grouped)
         with grp():
@@ -255,7 +258,8 @@ class PairDecode:
 
 class PairDecodeUngrouped(PairDecode):
     """pair_decode_1m with every call launched on its own (no launch groups):
-    seven launches of compress, attention and combine instead of three."""
+    seven launches of compress, attention and combine instead of three, and
+    the indexer zeroing its workspace in a launch of its own."""
     name = "pair_decode_1m_ungrouped"
     grouped = False
 

@@ -91,6 +91,9 @@ typedef enum {
 /* Flag for the dtype of indexer_topk: round every score to bf16 before the
  * selection (see indexer_topk). */
 #define LAC_SCORE_BF16 0x100
+/* Flag for the dtype of indexer_topk: the workspace was prepared by
+ * indexer_topk_prepare (see there). */
+#define LAC_TOPK_PREPARED 0x200
 
 /* Largest batch the position arrays may describe. */
 #define LAC_MAX_BATCH 128
@@ -224,6 +227,9 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
  *               -inf in padded slots); may be NULL
  *   workspace   >= indexer_topk_workspace_size(B, Tq, N, k) bytes
+ * dtype | LAC_TOPK_PREPARED: the workspace went through indexer_topk_prepare
+ * with the same B, Tq, N and k and nothing wrote it since; the call skips
+ * zeroing its counters.
  * dtype | LAC_SCORE_BF16: every score is rounded to the nearest bf16 value
  * (ties to even) once it is summed, and the selection runs on the rounded
  * scores with the same order (score descending, index ascending), so equal
@@ -239,6 +245,26 @@ int32_t indexer_topk(const void* q_idx, const float* w, const void* k_idx, int32
                      int32_t B, int32_t Tq, int32_t H_I, int32_t d_I, int32_t N,
                      const int64_t* q_pos0, int32_t m, int32_t k, int32_t* topk_idx,
                      float* topk_score, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * indexer_topk_prepare -- the part of indexer_topk that reads none of its
+ * inputs: zeroing the histograms and counters that its workspace must hold
+ * zero on entry (shapes with at most 64 query rows and more than 16384
+ * entries; for other shapes there is nothing to zero and the call enqueues
+ * nothing).  indexer_topk with dtype | LAC_TOPK_PREPARED on the same
+ * workspace and the same B, Tq, N and k then skips that zeroing.  A prepared
+ * workspace serves one indexer_topk call: the caller guarantees that nothing
+ * else writes the workspace in between.
+ * Inside a launch group (lac_group_begin) the zeroing joins the group's
+ * compress launch as extra workgroups: it reads nothing the other calls write,
+ * so it may share a group with the compress calls whose output the indexer
+ * call then reads.  Outside a group it is one small kernel launch.
+ *   workspace  >= indexer_topk_workspace_size(B, Tq, N, k) bytes, 256-byte aligned
+ * Errors as indexer_topk; LAC_TOPK_PREPARED on indexer_topk_noalloc is
+ * LAC_ERR_INVALID.
+ */
+int32_t indexer_topk_prepare(int32_t B, int32_t Tq, int32_t N, int32_t k, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * indexer_topk_noalloc -- indexer_topk for callers that cannot allocate
@@ -407,6 +433,8 @@ int32_t grouped_output_projection(const void* attn, const void* w1, const void* 
  * workspaces are detected and refused).  Memory named by a recorded call must
  * stay valid until the enqueued work completes, as for any call.
  *
+ * indexer_topk_prepare may be recorded too: its zeroing joins the compress
+ * launch (see there).
  * Inside a group, every call must pass the group's stream (else
  * LAC_ERR_INVALID, nothing recorded), and indexer_topk, indexer_topk_noalloc
  * and grouped_output_projection return LAC_ERR_INVALID.  lac_group_begin on a

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "LacError", "csa_compress", "hca_compress", "indexer_topk", "indexer_topk_workspace_size",
-    "indexer_topk_noalloc",
+    "indexer_topk_noalloc", "indexer_topk_prepare", "LAC_TOPK_PREPARED",
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
     "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "LAC_MXFP4", "LAC_SCORE_BF16",
@@ -30,6 +30,7 @@ __all__ = [
 
 LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3, LAC_MXFP4 = 0, 1, 2, 3, 4
 LAC_SCORE_BF16 = 0x100      # dtype flag of indexer_topk: scores rounded to bf16
+LAC_TOPK_PREPARED = 0x200   # dtype flag of indexer_topk: workspace zeroed by indexer_topk_prepare
 KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4,
            "project": 5}
 STATUS = {0: "LAC_OK", 1: "LAC_ERR_INVALID", 2: "LAC_ERR_UNSUPPORTED", 3: "LAC_ERR_WORKSPACE",
@@ -62,6 +63,8 @@ lib.indexer_topk.argtypes = [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, 
 lib.indexer_topk.restype = _i32
 lib.indexer_topk_noalloc.argtypes = lib.indexer_topk.argtypes[:-3] + [_vp]
 lib.indexer_topk_noalloc.restype = _i32
+lib.indexer_topk_prepare.argtypes = [_i32, _i32, _i32, _i32, _vp, _sz, _vp]
+lib.indexer_topk_prepare.restype = _i32
 lib.attend_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]
 lib.attend_workspace_size.restype = _sz
 lib.csa_attend.argtypes = [_vp, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _i32, _vp, _f32,
@@ -325,16 +328,28 @@ def _indexer_dtype(q_idx, k_idx):
     return _fmt(q_idx)
 
 
+def indexer_topk_prepare(B, Tq, N, k, workspace, stream=None):
+    """Zero the counters of an indexer_topk workspace ahead of the call that
+    passes prepared=True (include/lac.h); inside a group() it joins the
+    group's compress launch."""
+    _call(lib.indexer_topk_prepare, (B, Tq, N, k, _ptr(workspace), workspace.numel(),
+                                     _stream(stream)))
+
+
 def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=None,
-                 workspace=None, stream=None, score_bf16=False):
+                 workspace=None, stream=None, score_bf16=False, prepared=False):
     """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I]
     (the dtype of q_idx; uint8 E4M3 codes with bf16 or uint8 E4M3 q_idx; or
     uint8 MXFP4 rows of d_I/2 + d_I/32 bytes with bf16 q_idx).
     score_bf16: select on scores rounded to bf16 (include/lac.h).
+    prepared: the workspace went through indexer_topk_prepare (LAC_TOPK_PREPARED).
     Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""
     B, Tq, HI, dI = q_idx.shape
     N = k_idx.shape[1]
-    dt = _indexer_dtype(q_idx, k_idx) | (LAC_SCORE_BF16 if score_bf16 else 0)
+    if prepared and workspace is None:
+        raise ValueError("prepared=True needs the prepared workspace")
+    dt = (_indexer_dtype(q_idx, k_idx) | (LAC_SCORE_BF16 if score_bf16 else 0)
+          | (LAC_TOPK_PREPARED if prepared else 0))
     for t, nm in ((q_idx, "q_idx"), (w, "w"), (k_idx, "k_idx")):
         _need_dense(t, nm)
     if topk_idx is None:

@@ -24,6 +24,7 @@ struct Group {
   bool open = false;
   void* stream = nullptr;
   std::vector<lac::CompressArgs> comp;
+  std::vector<lac::ClearJob> clears;
   std::vector<lac::AttendArgs> att;
   std::vector<void*> att_ws;
   std::vector<size_t> att_need;
@@ -31,6 +32,7 @@ struct Group {
     open = false;
     stream = nullptr;
     comp.clear();
+    clears.clear();
     att.clear();
     att_ws.clear();
     att_need.clear();
@@ -172,7 +174,10 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
                      float* topk_score, void* workspace, size_t workspace_bytes, bool fixed,
                      void* stream) {
   const int round_bf16 = (dtype & LAC_SCORE_BF16) != 0;
-  dtype &= ~LAC_SCORE_BF16;
+  const int prepared = (dtype & LAC_TOPK_PREPARED) != 0;
+  dtype &= ~(LAC_SCORE_BF16 | LAC_TOPK_PREPARED);
+  if (prepared && fixed)
+    return fail(LAC_ERR_INVALID, "%s: LAC_TOPK_PREPARED needs a caller's workspace", fn);
   if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16 && dtype != LAC_E4M3 &&
       dtype != LAC_MXFP4)
     return fail(LAC_ERR_UNSUPPORTED,
@@ -212,7 +217,7 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
     if (workspace_bytes < need)
       return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
   }
-  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype; a.round_bf16 = round_bf16;
+  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype; a.round_bf16 = round_bf16; a.prepared = prepared;
   a.B = B; a.Tq = Tq; a.HI = H_I; a.dI = d_I; a.N = N; a.m = m; a.k = k;
   a.topk_idx = topk_idx; a.topk_score = topk_score;
   return launch_status(fn, lac::launch_indexer_topk(a, workspace, static_cast<hipStream_t>(stream)));
@@ -441,6 +446,32 @@ int32_t indexer_topk_noalloc(const void* q_idx, const float* w, const void* k_id
   }
 }
 
+int32_t indexer_topk_prepare(int32_t B, int32_t Tq, int32_t N, int32_t k, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "indexer_topk_prepare";
+  try {
+    if (B < 0 || B > LAC_MAX_BATCH) return fail(LAC_ERR_INVALID, "%s: B = %d outside [0, %d]", fn, B, LAC_MAX_BATCH);
+    if (Tq < 0 || N < 0) return fail(LAC_ERR_INVALID, "%s: negative Tq or N", fn);
+    if (k < 1 || k > 8192) return fail(LAC_ERR_INVALID, "%s: k = %d outside [1, 8192]", fn, k);
+    const size_t need = lac::indexer_workspace_bytes(B, Tq, N, k);
+    if (!workspace || !aligned(workspace, 256))
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace must be non-null and 256-byte aligned", fn);
+    if (workspace_bytes < need)
+      return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
+    const lac::ClearJob c = lac::indexer_clear_job(B, Tq, N, k, workspace);
+    if (g_group.open) {
+      int32_t st = group_stream(fn, stream);
+      if (st) return st;
+      if (c.words) g_group.clears.push_back(c);
+      g_err[0] = 0;
+      return LAC_OK;
+    }
+    return launch_status(fn, lac::launch_clear(c, static_cast<hipStream_t>(stream)));
+  } catch (...) {
+    return fail(LAC_ERR_DEVICE, "%s: internal error", fn);
+  }
+}
+
 size_t attend_workspace_size(int32_t B, int32_t Tq, int32_t H, int32_t D, int32_t rope_dims,
                              int32_t kv_dtype, int32_t n_entries, int32_t window) {
   if (B < 0 || Tq < 0 || H < 1 || D < 8 || rope_dims < 0 || n_entries < 0 || window < 0) return 0;
@@ -587,8 +618,9 @@ int32_t lac_group_end(void* stream) {
     if (st) { g_group.close(); return st; }
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    if (!g_group.comp.empty())
-      e = lac::launch_compress_group(g_group.comp.data(), (int)g_group.comp.size(), hs);
+    if (!g_group.comp.empty() || !g_group.clears.empty())
+      e = lac::launch_compress_group(g_group.comp.data(), (int)g_group.comp.size(), hs,
+                                     g_group.clears.data(), (int)g_group.clears.size());
     if (e == hipSuccess && na)
       e = lac::launch_attend_group(g_group.att.data(), g_group.att_ws.data(), (int)na, hs);
     g_group.close();

@@ -125,6 +125,14 @@ struct CLaunch {
   CompressK c[kCompressGroup];
   uint32_t blk_end[kCompressGroup];   // workgroups of calls 0 .. i
   int n;
+  // clearing jobs after the calls' workgroups: job i zeroes clr_words[i]
+  // words at clr[i] with the workgroups up to clr_end[i] (cumulative, after
+  // the calls'); blk_total = all workgroups of the launch
+  int n_clr;
+  uint32_t* clr[kCompressGroup];
+  uint64_t clr_words[kCompressGroup];
+  uint32_t clr_end[kCompressGroup];
+  uint32_t blk_total;
   int32_t pos[kCompressPos];
   double freq[kCompressTables * kMaxRopePairs];
 };
@@ -147,7 +155,17 @@ __global__ void __launch_bounds__(512) compress_kernel(CLaunch L) {
   uint32_t lb = 0;
   if constexpr (MULTI) {
     const uint32_t wg = blockIdx.y * gridDim.x + blockIdx.x;
-    if (wg >= L.blk_end[L.n - 1]) return;     // the grid's rounding
+    if (wg >= L.blk_total) return;            // the grid's rounding
+    const uint32_t calls_end = L.n ? L.blk_end[L.n - 1] : 0u;
+    if (wg >= calls_end) {
+      // a clearing workgroup: 16 bytes per thread of its job's words
+      int q = 0;
+      while (q + 1 < L.n_clr && wg >= L.clr_end[q]) ++q;
+      const uint32_t first = q ? L.clr_end[q - 1] : calls_end;
+      const uint64_t v = ((uint64_t)(wg - first) * blockDim.x + threadIdx.x) * 4;
+      if (v < L.clr_words[q]) *reinterpret_cast<uint4*>(L.clr[q] + v) = make_uint4(0u, 0u, 0u, 0u);
+      return;
+    }
     while (ci + 1 < L.n && wg >= L.blk_end[ci]) ++ci;
     lb = wg - (ci ? L.blk_end[ci - 1] : 0u);
   }
@@ -412,7 +430,7 @@ hipError_t launch_one(const CLaunch& L, int threads, bool tree, int B, hipStream
   const size_t lds = tree ? (size_t)threads * 25 * sizeof(float) : 0;
   hipError_t e;
   TimedLaunch tl(kKernelCompress, st);
-  if (L.n == 1) {
+  if (L.n == 1 && L.n_clr == 0) {
     const CompressK& k = L.c[0];
     const dim3 grid(k.gx, k.gy, B), block(k.gb, k.s, k.epb);
     auto one = [&](auto out_c) {
@@ -431,7 +449,7 @@ hipError_t launch_one(const CLaunch& L, int threads, bool tree, int B, hipStream
   }
   if ((e = set_lds_limit<IN, TOKN, -1>()) != hipSuccess) return e;
   // (x, y) grid of at least the launch's workgroups, x fastest
-  const uint32_t total = L.blk_end[L.n - 1];
+  const uint32_t total = L.blk_total;
   const uint32_t gx = std::min<uint32_t>(total, 65536u);
   hipLaunchKernelGGL((compress_kernel<IN, TOKN, -1>), dim3(gx, (total + gx - 1) / gx),
                      dim3(threads), lds, st, L);
@@ -442,8 +460,27 @@ hipError_t launch_one(const CLaunch& L, int threads, bool tree, int B, hipStream
 
 // Calls of one input format and one loads-in-flight count go into launches
 // of up to kCompressGroup calls, in call order, as long as their positions
-// and rotation tables fit the launch's pools.
-hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t st) {
+// and rotation tables fit the launch's pools.  Clearing jobs ride on the
+// first launch (up to kCompressGroup of them; the rest, and jobs with no
+// compress call to join, take launches of their own).
+hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t st,
+                                 const ClearJob* clears, int n_clears) {
+  int clr_next = 0;
+  // append the pending clearing jobs (up to the launch's capacity) after the
+  // calls' workgroups of L, whose workgroups have `threads` threads
+  auto add_clears = [&](CLaunch& L, int threads) {
+    uint32_t end = L.n ? L.blk_end[L.n - 1] : 0u;
+    while (clr_next < n_clears && L.n_clr < kCompressGroup) {
+      const ClearJob& c = clears[clr_next++];
+      if (c.words == 0) continue;
+      L.clr[L.n_clr] = c.p;
+      L.clr_words[L.n_clr] = c.words;
+      end += (uint32_t)((c.words / 4 + threads - 1) / threads);
+      L.clr_end[L.n_clr] = end;
+      ++L.n_clr;
+    }
+    L.blk_total = end;
+  };
   for (int variant = 0; variant < 4; ++variant) {
     const int fmt = variant < 2 ? kF32 : kBF16, tokn = variant % 2 ? 8 : 4;
     CLaunch L{};
@@ -454,6 +491,7 @@ hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t s
     int tab_r[kCompressTables];
     auto flush = [&]() -> hipError_t {
       if (L.n == 0) return hipSuccess;
+      add_clears(L, threads);
       const hipError_t e = fmt == kF32 ? (tokn == 4 ? launch_one<kF32, 4>(L, threads, tree, B1, st)
                                                     : launch_one<kF32, 8>(L, threads, tree, B1, st))
                                        : (tokn == 4 ? launch_one<kBF16, 4>(L, threads, tree, B1, st)
@@ -477,7 +515,7 @@ hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t s
       const uint32_t nblk = (uint32_t)k.gx * (uint32_t)k.gy * (uint32_t)a.B;
       const bool fits = L.n < kCompressGroup && n_pos + a.B <= kCompressPos &&
                         (a.r == 0 || tab >= 0 || n_tab < kCompressTables) &&
-                        (L.n == 0 || (uint64_t)L.blk_end[L.n - 1] + nblk < (1u << 31));
+                        (L.n == 0 || (uint64_t)L.blk_end[L.n - 1] + nblk < (1u << 30));
       if (!fits) {
         const hipError_t e = flush();
         if (e != hipSuccess) return e;
@@ -503,6 +541,14 @@ hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t s
       tree = tree || k.s > 1;
     }
     const hipError_t e = flush();
+    if (e != hipSuccess) return e;
+  }
+  // clearing jobs left over: launches of 256-thread clearing workgroups
+  while (clr_next < n_clears) {
+    CLaunch L{};
+    add_clears(L, 256);
+    if (L.n_clr == 0) break;
+    const hipError_t e = launch_one<kBF16, 4>(L, 256, false, 0, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

@@ -791,6 +791,25 @@ Plan make_plan(int B, int Tq, int N, int k) {
 
 size_t indexer_workspace_bytes(int B, int Tq, int N, int k) { return make_plan(B, Tq, N, k).total; }
 
+// The words of the workspace that the split path needs zero on entry (the
+// histograms, the score kernel's tile counters and the chunk counts' lead-in),
+// or none when the shape takes one workgroup per row.
+ClearJob indexer_clear_job(int B, int Tq, int N, int k, void* ws) {
+  const Plan p = make_plan(B, Tq, N, k);
+  ClearJob c{};
+  if (!p.split || (int64_t)B * Tq == 0) return c;
+  c.p = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + p.off_hist);
+  c.words = (p.off_cnt - p.off_hist) / 4;
+  return c;
+}
+
+hipError_t launch_clear(const ClearJob& c, hipStream_t st) {
+  if (c.words == 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((c.words + 255) / 256)), dim3(256), 0, st,
+                     c.p, (int64_t)c.words);
+  return hipGetLastError();
+}
+
 hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
   const Plan p = make_plan(a.B, a.Tq, a.N, a.k);
   const int R = a.B * a.Tq;
@@ -810,11 +829,10 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
     ta.cand = reinterpret_cast<uint2*>(w8 + p.off_cand);
     // The score and filter kernels accumulate into the histograms and the
     // score kernel draws tiles from counters: clear them (and the adjacent
-    // chunk counts) first, with a kernel rather than a memset.
-    const int64_t n_clear = (int64_t)(p.off_cnt - p.off_hist) / 4;
-    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)((n_clear + 255) / 256)), dim3(256), 0, st,
-                       ta.hist, n_clear);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    // chunk counts) first, with a kernel rather than a memset -- unless the
+    // caller cleared them beforehand (indexer_topk_prepare).
+    if (!a.prepared && (err = launch_clear(indexer_clear_job(a.B, a.Tq, a.N, a.k, ws), st)) != hipSuccess)
+      return err;
   }
 
   // Largest visible count over all rows sizes the key sweep.

@@ -31,6 +31,13 @@ struct TimedLaunch {
 };
 void arm_timer(int kernel, hipEvent_t start, hipEvent_t stop);
 
+// Device words to zero: the indexer workspace's counters (indexer_clear_job),
+// done by a small fill launch (launch_clear) or inside a compress launch.
+struct ClearJob {
+  uint32_t* p;
+  uint64_t words;        // a multiple of 64
+};
+
 // ---------------------------------------------------------------- compress
 struct CompressArgs {
   const void* kv;
@@ -48,7 +55,8 @@ struct CompressArgs {
 hipError_t launch_compress(CompressArgs a, hipStream_t st);
 // n independent calls (none reads what another writes), in as few launches
 // as their input formats and the launch's argument pools allow.
-hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t st);
+hipError_t launch_compress_group(const CompressArgs* calls, int n, hipStream_t st,
+                                 const ClearJob* clears = nullptr, int n_clears = 0);
 // Launch limit: a call's workgroups, at most B * floor(T/m) * D/8, stay below 2^31.
 constexpr int64_t kCompressMaxGroups = (int64_t)1 << 31;
 
@@ -59,12 +67,15 @@ struct IndexerArgs {
   const void* K;         // [B, N, dI]
   int fmt;               // kF32 | kBF16 | kMixed (E4M3 keys) | kE4M3 (E4M3 queries and keys) | kMXFP4 (MXFP4 keys)
   int round_bf16;        // scores rounded to bf16 before selection
+  int prepared;          // the workspace's counters are already zero (indexer_topk_prepare)
   int B, Tq, HI, dI, N, m, k;
   int32_t* topk_idx;     // [B, Tq, k]
   float* topk_score;     // [B, Tq, k] or null
   Positions qpos;
 };
 size_t indexer_workspace_bytes(int B, int Tq, int N, int k);
+ClearJob indexer_clear_job(int B, int Tq, int N, int k, void* ws);
+hipError_t launch_clear(const ClearJob& c, hipStream_t st);
 // Lightning-Indexer scores (score.hip) into the top-k workspace: the score
 // rows, and on the split path the key histogram and the tile counters, both
 // cleared beforehand.  nv_max: largest visible count over the rows.

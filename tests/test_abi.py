@@ -195,3 +195,25 @@ def test_group_end_on_another_stream_closes_the_group(L):
     assert lib.csa_compress(*_csa_compress_args(fake)) == 0
     assert lib.lac_group_end(ctypes.c_void_p(0x20000)) == 1
     assert lib.lac_group_end(None) == 1
+
+
+def test_indexer_prepare_validation_and_grouping(L):
+    lib = L.lib
+    fake = ctypes.c_void_p(0x1000000)
+    need = L.indexer_topk_workspace_size(4, 1, 262144, 2048)
+    # bad sizes, workspace missing, misaligned or small
+    assert lib.indexer_topk_prepare(4, 1, 262144, 0, fake, need, None) == 1
+    assert lib.indexer_topk_prepare(-1, 1, 262144, 2048, fake, need, None) == 1
+    assert lib.indexer_topk_prepare(4, 1, 262144, 2048, None, need, None) == 3
+    assert lib.indexer_topk_prepare(4, 1, 262144, 2048, ctypes.c_void_p(0x1000010), need, None) == 3
+    assert lib.indexer_topk_prepare(4, 1, 262144, 2048, fake, need - 1, None) == 3
+    # inside a group it is recorded (nothing enqueued), on the group's stream only
+    assert lib.lac_group_begin(None) == 0
+    assert lib.indexer_topk_prepare(4, 1, 262144, 2048, fake, need, None) == 0
+    assert lib.indexer_topk_prepare(4, 1, 262144, 2048, fake, need, ctypes.c_void_p(0x20000)) == 1
+    assert lib.lac_group_cancel() == 0
+    # the flag needs a caller's workspace
+    q = ctypes.c_void_p(0x10000)
+    assert lib.indexer_topk_noalloc(q, q, q, 1 | L.LAC_TOPK_PREPARED, 1, 1, 64, 128, 64, None, 4,
+                                    16, q, None, None) == 1
+    assert "LAC_TOPK_PREPARED" in _err(L)

@@ -184,3 +184,57 @@ def test_group_refuses_shared_workspace_on_the_gpu():
         with lac.group():
             _attend(c, out, ws)
             _attend(c, out, ws)
+
+
+# ---------------------------------------------------------------- indexer workspace preparation
+def _indexer_inputs(seed, B, N, HI=64, dI=128):
+    q = synth.store(synth.normal(seed, "qI", (B, 1, HI, dI)), "bf16").to(DEV)
+    K = synth.store(synth.normal(seed, "KI", (B, N, dI)), "bf16").to(DEV)
+    w = synth.uniform(seed, "w", (B, 1, HI)).to(DEV)
+    return q, w, K
+
+
+@pytest.mark.parametrize("N", [40000, 3000])       # split path, one workgroup per row
+def test_prepared_indexer_matches_unprepared(N):
+    B, k = 2, 2048 if N > 16384 else 300
+    q, w, K = _indexer_inputs(21, B, N)
+    pos = [4 * N, 4 * (N - 7) + 1]
+    score_ref = torch.empty((B, 1, k), dtype=torch.float32, device=DEV)
+    ref = lac.indexer_topk(q, w, K, m=4, k=k, q_pos0=pos, topk_score=score_ref)
+    ws = torch.full((lac.indexer_topk_workspace_size(B, 1, N, k),), 0x7F, dtype=torch.uint8,
+                    device=DEV)                      # counters start dirty
+    for rep in range(2):                             # a prepared workspace serves one call
+        lac.indexer_topk_prepare(B, 1, N, k, ws)
+        score = torch.empty_like(score_ref)
+        idx = lac.indexer_topk(q, w, K, m=4, k=k, q_pos0=pos, topk_score=score, workspace=ws,
+                               prepared=True)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref) and torch.equal(score, score_ref), f"call {rep}"
+
+
+def test_indexer_prepare_joins_the_compress_group():
+    # the decode step's shape of work: the newest indexer key is compressed in
+    # a group with the workspace preparation, then the prepared call selects
+    # over the keys including it; the same as the ungrouped, unprepared calls
+    B, N, k, m, dI = 2, 20000, 700, 4, 128
+    q, w, K0 = _indexer_inputs(22, B, N, dI=dI)
+    x = synth.store(synth.normal(22, "x", (B, m, dI)), "bf16").to(DEV)
+    z = synth.store(synth.normal(22, "z", (B, m, dI)), "bf16").to(DEV)
+    pos = [4 * N, 4 * N]
+    ws = torch.full((lac.indexer_topk_workspace_size(B, 1, N, k),), 0x33, dtype=torch.uint8,
+                    device=DEV)
+    K1 = K0.clone()
+    with lac.group():
+        lac.csa_compress(x, z, K1[:, N - 1:], m=m, rope_dims=0, pos0=4 * (N - 1))
+        lac.indexer_topk_prepare(B, 1, N, k, ws)
+    idx = lac.indexer_topk(q, w, K1, m=m, k=k, q_pos0=pos, workspace=ws, prepared=True)
+    K2 = K0.clone()
+    lac.csa_compress(x, z, K2[:, N - 1:], m=m, rope_dims=0, pos0=4 * (N - 1))
+    ref = lac.indexer_topk(q, w, K2, m=m, k=k, q_pos0=pos)
+    torch.cuda.synchronize()
+    assert torch.equal(K1, K2)
+    assert torch.equal(idx, ref)
+    # and against the oracle's selection
+    s, nv = oracle.index_scores(host(q), host(w), host(K2), synth.BF16, B, 1, 64, dI, N, pos, m)
+    from parity import check_topk
+    check_topk(idx.cpu().numpy().reshape(B, k), oracle.topk(s, nv, k), s, nv, k)
