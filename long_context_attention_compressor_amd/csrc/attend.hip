@@ -254,6 +254,9 @@ struct KLaunch {
   double freq[kMaxRopePairs];
 };
 
+// A launch's whole argument is one kernel argument: keep it within 4 KB.
+static_assert(sizeof(KLaunch) <= 4096, "kernel argument above 4 KB");
+
 // The call that workgroup wg belongs to, and wg's index within that call.
 __device__ __forceinline__ int launch_call(const KLaunch& L, uint32_t wg, uint32_t* local) {
   int ci = 0;

@@ -137,6 +137,9 @@ struct CLaunch {
   double freq[kCompressTables * kMaxRopePairs];
 };
 
+// A launch's whole argument is one kernel argument: keep it within 4 KB.
+static_assert(sizeof(CLaunch) <= 4096, "kernel argument above 4 KB");
+
 // Thread (x, y, z) of a call's block (GB, S, epb) owns channel group
 // slice * GB + x of entry group * epb + z and token share y of its block; a
 // call's workgroups run (entry groups, channel slices, sequences), fastest

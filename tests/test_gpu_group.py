@@ -238,3 +238,80 @@ def test_indexer_prepare_joins_the_compress_group():
     s, nv = oracle.index_scores(host(q), host(w), host(K2), synth.BF16, B, 1, 64, dI, N, pos, m)
     from parity import check_topk
     check_topk(idx.cpu().numpy().reshape(B, k), oracle.topk(s, nv, k), s, nv, k)
+
+
+# ---------------------------------------------------------------- RMSNorm and overlapping windows in groups
+def test_rmsnorm_and_overlap_compress_in_one_group():
+    # the f3 and f2 forms of the decode step's compress calls, grouped: each
+    # output bit-identical to its ungrouped call and within the oracle's
+    # tolerance
+    B, D, r, eps, o = 3, 512, 64, 1e-6, 4
+    pos = [(1 << 20) - 128, 4096, 128 * 9]
+    gain = (synth.uniform(31, "gain", (D,)) + 0.5).to(DEV)
+    xh = synth.store(synth.normal(31, "x", (B, 128, D), std=3.0), "bf16").to(DEV)
+    zh = synth.store(synth.normal(31, "z", (B, 128, D)), "bf16").to(DEV)
+    # CSA with overlap o: rows start min(o, pos0) before the block
+    xc = synth.store(synth.normal(32, "x", (B, 4 + o, D)), "bf16").to(DEV)
+    zc = synth.store(synth.normal(32, "z", (B, 4 + o, D)), "bf16").to(DEV)
+    pc = [p + 124 for p in pos]
+
+    def calls(outs):
+        lac.hca_compress(xh, zh, outs[0], m=128, rope_dims=r, pos0=pos, norm_gain=gain, norm_eps=eps)
+        lac.csa_compress(xc, zc, outs[1], m=4, rope_dims=r, pos0=pc, T=4, overlap=o)
+        lac.csa_compress(xh, zh, outs[2], m=4, rope_dims=r, pos0=pos, norm_gain=gain, norm_eps=eps)
+
+    def new_outs():
+        return [torch.full((B, 1, D + r), 0x55, dtype=torch.uint8, device=DEV),
+                torch.full((B, 1, D + r), 0x55, dtype=torch.uint8, device=DEV),
+                torch.full((B, 32, D + r), 0x55, dtype=torch.uint8, device=DEV)]
+
+    single = new_outs()
+    calls(single)
+    grouped = new_outs()
+    with lac.group():
+        calls(grouped)
+    torch.cuda.synchronize()
+    for g, s1 in zip(grouped, single):
+        assert torch.equal(g, s1)
+    ref_h = oracle.compress(host(xh), host(zh), synth.BF16, B, 128, D, 128, r, 10000.0, pos,
+                            norm_gain=host(gain), norm_eps=eps)
+    check_compressed(grouped[0], ref_h, "mixed", D, r)
+    ref_c = oracle.compress_overlap(host(xc), host(zc), synth.BF16, B, 4, D, 4, o, r, 10000.0, pc)
+    check_compressed(grouped[1], ref_c, "mixed", D, r)
+    ref_n = oracle.compress(host(xh), host(zh), synth.BF16, B, 128, D, 4, r, 10000.0, pos,
+                            norm_gain=host(gain), norm_eps=eps)
+    check_compressed(grouped[2], ref_n, "mixed", D, r)
+
+
+def test_rmsnorm_attention_in_a_group():
+    # csa_attend_rmsnorm and hca_attend_rmsnorm grouped, against the oracle
+    eps = 1e-6
+    gain = (synth.uniform(33, "gain", (512,)) + 0.5)
+    pos = [300_001, 131_075]
+    cases = [_attend_case(0, 2, 1, 64, 512, 64, 20000, 256, 4, 128, pos, "mixed", 34),
+             _attend_case(1, 2, 1, 64, 512, 64, 2300, 0, 128, 128, pos, "mixed", 35)]
+    outs = [torch.empty_like(c["q"]) for c in cases]
+    wss = [torch.empty(max(c["need"], 256), dtype=torch.uint8, device=DEV) for c in cases]
+    g = gain.to(DEV)
+    with lac.group():
+        for c, out, ws in zip(cases, outs, wss):
+            if c["mode"] == 0:
+                lac.csa_attend(c["q"], c["kv"], c["idx"], c["raw"], c["W"], q_pos0=c["q_pos0"],
+                               raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=out, workspace=ws,
+                               q_norm_gain=g, norm_eps=eps)
+            else:
+                lac.hca_attend(c["q"], c["kv"], c["raw"], c["W"], m=c["m"], q_pos0=c["q_pos0"],
+                               raw_pos0=c["raw_pos0"], rope_dims=c["r"], out=out, workspace=ws,
+                               q_norm_gain=g, norm_eps=eps)
+    torch.cuda.synchronize()
+    for c, out in zip(cases, outs):
+        B, Tq, H, D = c["shape"]
+        N = c["kv"].shape[1]
+        k = 0 if c["idx"] is None else c["idx"].shape[-1]
+        idx = None if c["idx"] is None else c["idx"].cpu().numpy().reshape(B * Tq, k)
+        ref = oracle.attend(host(c["q"]), synth.BF16, host(c["kv"]), synth.MIXED, N, c["mode"],
+                            idx, k, c["m"], host(c["raw"]), c["raw"].shape[1], c["raw_pos0"],
+                            c["W"], None, 0.0, B, Tq, H, D, c["r"], 10000.0, c["q_pos0"],
+                            [(b, i) for b in range(B) for i in range(Tq)],
+                            q_norm_gain=host(gain), norm_eps=eps)
+        check_attention(as_f64(out).reshape(B * Tq, H, D), ref, "grouped rmsnorm " + c["tag"])
