@@ -18,6 +18,7 @@ the indexer keys stored as E4M3, one byte per dim), pair_decode_1m_fp8_indexer
 pair_decode_1m_mxfp4_indexer (MXFP4 indexer keys), csa_decode_128k (32
 sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
+csa_chunk_prefill_1m (the same chunk ending at 2^20 tokens),
 hca_prefill_8k (8192 tokens; TFLOP/s), bulk_compress_1m and
 bulk_compress_128k (building the compressed caches of whole contexts from raw
 activations; GB/s), and the grouped output projection.
@@ -355,10 +356,11 @@ class ChunkPrefill:
     name = "csa_chunk_prefill"
     unit = "TFLOP/s"
     timer_kernel = "indexer_score"
+    ctx = 262144
 
     def __init__(self, lac, synth, dev, sets, seed=3):
         self.lac = lac
-        c = self.c = synth.csa_chunk_prefill(seed=seed, device=dev)
+        c = self.c = synth.csa_chunk_prefill(seed=seed, ctx=self.ctx, device=dev)
         T = c["chunk"]
         self.idx = torch.empty((1, T, c["k"]), dtype=torch.int32, device=dev)
         self.out = torch.empty_like(c["q"])
@@ -422,6 +424,15 @@ class ChunkPrefill:
         return {"value": fl / el / 1e12, "unit": self.unit, "seconds": el,
                 "sample": "indexer + top-k + attention for 4 of the 4096 queries (the chunk's "
                           "compression excluded), FLOPs scaled by 4/4096"}
+
+
+class ChunkPrefill1M(ChunkPrefill):
+    """csa_chunk_prefill with the chunk of 4096 queries ending at 2^20 tokens:
+    262144 compressed entries per query row (4.3 GB of fp32 scores in the
+    indexer workspace), each row's top 2048 by the one-workgroup-per-row
+    selection."""
+    name = "csa_chunk_prefill_1m"
+    ctx = (1 << 20) - 4096
 
 
 class HcaPrefill(ChunkPrefill):
@@ -676,7 +687,8 @@ WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeUngrouped, PairDecodeE4M3
                                   PairDecodeFp8Indexer,
                                   PairDecodeMxfp4Indexer,
                                   PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
-                                  ChunkPrefill, HcaPrefill, ProjectionPrefill, ProjectionDecode,
+                                  ChunkPrefill, ChunkPrefill1M, HcaPrefill,
+                                  ProjectionPrefill, ProjectionDecode,
                                   BulkCompress1M, BulkCompress128K)}
 
 

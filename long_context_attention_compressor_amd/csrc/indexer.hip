@@ -753,6 +753,216 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
   }
 }
 
+// Rows of kPrefixMax to kLongMax visible entries (prefill chunks at up to 2M
+// tokens of context), one 512-thread workgroup per row: the steps of
+// topk_prefix_kernel with the row read from memory in each of three passes
+// instead of held in registers.  Pass 1 builds the histogram of key bits
+// 31..20 (four lane-interleaved copies) and fixes the threshold's 12-bit
+// bucket; pass 2 the histogram of bits 19..8 over the keys in it, fixing the
+// 24-bit prefix P; pass 3 writes the bitmap of the keys above P and collects
+// the keys carrying P, which are ranked by (key desc, index asc).  The set is
+// emitted in ascending index order from the LDS bitmap.  A pass's loads are
+// issued kLongU steps of the row at a time.
+constexpr int kLongMax = 1 << 19;             // LDS bitmap of 64 KB
+constexpr int kLongU = 8;
+
+__global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
+  __shared__ __align__(16) uint32_t hist4[kHistBins * 4];   // 4 copies, then bits 19..8 (one copy)
+  extern __shared__ __align__(16) uint32_t lbits[];        // [64 per 2048-entry step]
+  __shared__ int32_t cidx[kPrefCand];
+  __shared__ uint32_t ckey[kPrefCand];
+  __shared__ uint32_t wsum[kPT / 64];
+  __shared__ uint32_t bc[4];
+  __shared__ uint32_t t_d, t_above, n_cand;
+  const int row = blockIdx.x;
+  const int nv = (int)row_nvis(a, row);
+  const int keff = min(a.k, nv);
+  if (keff == nv) { write_all_visible(a, row, nv); return; }
+  const int tid = threadIdx.x, l = lane_id(), wv = tid >> 6;
+  const float* s = a.scores + (int64_t)row * a.Np;
+  const int n_steps = (nv + 4 * kPT - 1) / (4 * kPT);
+
+  // one pass over the row: f(step, c, e, key) for the 4 consecutive entries
+  // 4 tid .. 4 tid + 3 of every 2048-entry step (entries past the row are
+  // passed with e >= nv and key 0); kLongU steps' loads in flight at a time.
+  // The row's padding to a multiple of 64 keeps every float4 in bounds.
+  auto pass = [&](auto f) {
+    for (int u0 = 0; u0 < n_steps; u0 += kLongU) {
+      float4 v[kLongU];
+#pragma unroll
+      for (int j = 0; j < kLongU; ++j) {
+        const int e = 4 * (tid + kPT * (u0 + j));
+        v[j] = u0 + j < n_steps && e < nv ? *reinterpret_cast<const float4*>(s + e)
+                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < kLongU; ++j) {
+        if (u0 + j >= n_steps) break;
+        const int e = 4 * (tid + kPT * (u0 + j));
+        const float x[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        uint32_t key[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) key[c] = e + c < nv ? score_key(x[c]) : 0u;
+        f(u0 + j, e, key);
+      }
+    }
+  };
+
+  for (int e = tid; e < kHistBins * 4; e += kPT) hist4[e] = 0u;
+  if (tid == 0) n_cand = 0;
+  __syncthreads();
+
+  // ---- pass 1: histogram of key bits 31..20
+  pass([&](int, int e, const uint32_t* key) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (e + c < nv) atomicAdd(&hist4[4 * (key[c] >> 20) + (l & 3)], 1u);
+  });
+  __syncthreads();
+
+  // the bin holding the need-th largest key: thread t covers bins
+  // 4095 - kPBins t downwards, summed over `copies` interleaved copies
+  auto find_bucket = [&](uint32_t need, int copies) {
+    uint32_t c[kPBins], sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPBins; ++q) {
+      const int bin = kHistBins - 1 - kPBins * tid - q;
+      if (copies == 4) {
+        const uint4 h = *reinterpret_cast<const uint4*>(&hist4[4 * bin]);
+        c[q] = h.x + h.y + h.z + h.w;
+      } else {
+        c[q] = hist4[bin];
+      }
+      sum += c[q];
+    }
+    uint32_t incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t x = __shfl_up(incl, o);
+      if (l >= o) incl += x;
+    }
+    if (l == 63) wsum[wv] = incl;
+    __syncthreads();
+    for (int w = 0; w < wv; ++w) incl += wsum[w];
+    const uint32_t excl = incl - sum;
+    if (excl < need && incl >= need) {
+      uint32_t cum = excl;
+#pragma unroll
+      for (int q = 0; q < kPBins; ++q) {
+        if (cum + c[q] >= need) { t_d = kHistBins - 1 - kPBins * tid - q; t_above = cum; break; }
+        cum += c[q];
+      }
+    }
+    __syncthreads();
+  };
+  find_bucket((uint32_t)keff, 4);
+  const uint32_t d1 = t_d, above1 = t_above;
+  for (int e = tid; e < kHistBins; e += kPT) hist4[e] = 0u;
+  __syncthreads();
+
+  // ---- pass 2: bits 19..8 of the keys in bucket d1
+  pass([&](int, int e, const uint32_t* key) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (e + c < nv && (key[c] >> 20) == d1) atomicAdd(&hist4[(key[c] >> 8) & 4095u], 1u);
+  });
+  __syncthreads();
+  find_bucket((uint32_t)keff - above1, 1);
+  const uint32_t P = (d1 << 12) | t_d;                         // 24-bit threshold prefix
+  const uint32_t need_p = (uint32_t)keff - above1 - t_above;   // >= 1 keys carrying P
+
+  // ---- pass 3: bitmap of the keys above P; the keys carrying P (and their
+  // indices) collected on the way.  Lanes 8w .. 8w+7 hold the 32 entries of
+  // one bitmap word, merged with DPP moves.
+  pass([&](int step, int e, const uint32_t* key) {
+    uint32_t nib = 0, eq = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint32_t k24 = key[c] >> 8;
+      nib |= (uint32_t)(e + c < nv && k24 > P) << c;
+      eq |= (uint32_t)(e + c < nv && k24 == P) << c;
+    }
+    const uint32_t word = or8(nib << (4 * (l & 7)));
+    if ((l & 7) == 0) lbits[step * (kPT / 8) + (tid >> 3)] = word;
+    if (__ballot(eq != 0)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((eq >> c) & 1u) {
+          const uint32_t pos = atomicAdd(&n_cand, 1u);
+          if (pos < (uint32_t)kPrefCand) { cidx[pos] = e + c; ckey[pos] = key[c]; }
+        }
+      }
+    }
+  });
+  __syncthreads();
+  const int nc = (int)n_cand;
+  if (nc <= kPrefCand) {
+    // the need_p largest by (key desc, index asc), by rank among the candidates
+    for (int ci = tid; ci < nc; ci += kPT) {
+      const int me = cidx[ci];
+      const uint32_t mk = ckey[ci];
+      uint32_t rank = 0;
+      for (int j = 0; j < nc; ++j) {
+        const uint32_t ok = ckey[j];
+        rank += (ok > mk) || (ok == mk && cidx[j] < me);
+      }
+      if (rank < need_p) atomicOr(&lbits[me >> 5], 1u << (me & 31));
+    }
+  } else {
+    // many keys carry P: the (key, index) threshold of a radix select over them
+    uint32_t thr, need_eq, cnt_eq, thr2 = 0;
+    radix_select(nv, need_p,
+                 [&](int e, uint32_t* u) { *u = score_key(s[e]); return (*u >> 8) == P; }, hist4,
+                 bc, thr, need_eq, cnt_eq);
+    if (cnt_eq > need_eq) {
+      uint32_t ne2, ce2;
+      radix_select(nv, need_eq,
+                   [&](int e, uint32_t* u) { *u = ~(uint32_t)e; return score_key(s[e]) == thr; },
+                   hist4, bc, thr2, ne2, ce2);
+    }
+    for (int e = tid; e < nv; e += kPT) {
+      const uint32_t kk = score_key(s[e]);
+      if ((kk >> 8) == P && (kk > thr || (kk == thr && ~(uint32_t)e >= thr2)))
+        atomicOr(&lbits[e >> 5], 1u << (e & 31));
+    }
+  }
+  __syncthreads();
+
+  // ---- emit in ascending index order: thread t owns a run of words
+  const int nwords = (nv + 31) / 32;
+  const int per = (nwords + kPT - 1) / kPT;
+  const int w0 = min(nwords, tid * per), w1 = min(nwords, w0 + per);
+  uint32_t mine = 0;
+  for (int w = w0; w < w1; ++w) mine += __popc(lbits[w]);
+  uint32_t incl = mine;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t x = __shfl_up(incl, o);
+    if (l >= o) incl += x;
+  }
+  if (l == 63) wsum[wv] = incl;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) incl += wsum[w];
+  uint32_t pos = incl - mine;
+  int32_t* out = a.idx + (int64_t)row * a.k;
+  for (int w = w0; w < w1; ++w) {
+    uint32_t bits = lbits[w];
+    while (bits) {
+      const int e = 32 * w + __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < (uint32_t)keff) {
+        out[pos] = e;
+        if (a.score_out) a.score_out[(int64_t)row * a.k + pos] = s[e];
+      }
+      ++pos;
+    }
+  }
+  for (int e = keff + tid; e < a.k; e += kPT) {
+    out[e] = -1;
+    if (a.score_out) a.score_out[(int64_t)row * a.k + e] = -INFINITY;
+  }
+}
+
 struct Plan {
   int64_t Np;
   bool split;
@@ -852,6 +1062,13 @@ hipError_t launch_indexer_topk(const IndexerArgs& a, void* ws, hipStream_t st) {
     TimedLaunch tl(kKernelTopk, st);
     if (nv_max <= kPrefixMax) {
       hipLaunchKernelGGL(topk_prefix_kernel, dim3(R), dim3(kPT), 0, st, ta);
+    } else if (nv_max <= kLongMax) {
+      static const hipError_t attr = hipFuncSetAttribute(
+          reinterpret_cast<const void*>(&topk_long_kernel),
+          hipFuncAttributeMaxDynamicSharedMemorySize, kLongMax / 8);
+      if (attr != hipSuccess) return attr;
+      const int64_t n_steps = (nv_max + 4 * kPT - 1) / (4 * kPT);
+      hipLaunchKernelGGL(topk_long_kernel, dim3(R), dim3(kPT), (size_t)n_steps * (kPT / 8) * 4, st, ta);
     } else {
       hipLaunchKernelGGL(topk_rowwise_kernel, dim3(R), dim3(kTopkThreads), 0, st, ta);
     }

@@ -136,11 +136,14 @@ def test_e4m3_keys_head_and_dim_variants(HI, dI):
 
 
 # Rows longer than the register-resident kernel holds (67584 visible entries)
-# and too many of them for the split path (more than 64 rows): the 8-bit radix
-# select, one workgroup per row.  Drawn on the GPU; the oracle scores sampled
-# rows from a host copy of their sequences.
-def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zero=False):
-    print(f"indexer (row-wise radix path) B={B} Tq={Tq} N={N} k={k}", flush=True)
+# and too many of them for the split path (more than 64 rows): up to 2^19
+# visible entries the three-pass kernel (histograms and bitmap in LDS, the row
+# re-read per pass), beyond that the 8-bit radix select; one workgroup per
+# row.  Drawn on the GPU; the oracle scores sampled rows from a host copy of
+# their sequences.
+def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zero=False,
+                   min_nv=67584):
+    print(f"indexer (long rows) B={B} Tq={Tq} N={N} k={k}", flush=True)
     q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI), device=DEV), "bf16")
     K = synth.store(synth.normal(seed, "KI", (B, N, dI), device=DEV), "bf16")
     w = synth.uniform(seed, "w", (B, Tq, HI), device=DEV)
@@ -153,7 +156,7 @@ def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zer
     rows = [(j, i) for j in range(len(seqs)) for i in rows_per_seq]
     s, nv = oracle.index_scores(sub(q), sub(w), sub(K), synth.BF16, len(seqs), Tq, HI, dI, N,
                                 [qpos[b] for b in seqs], m, rows)
-    assert (nv > 67584).all() and B * Tq > 64
+    assert (nv > min_nv).all() and B * Tq > 64
     o_idx = oracle.topk(s, nv, k)
     g_idx = np.stack([idx[seqs[j], i].cpu().numpy() for j, i in rows])
     g_sc = np.stack([score[seqs[j], i].cpu().numpy() for j, i in rows])
@@ -166,17 +169,34 @@ def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zer
     return idx
 
 
-def test_bf16_rowwise_kernel_prefill_rows_past_67584():
+def test_bf16_long_kernel_prefill_rows_past_67584():
     # 80 queries at 280000..280079: n_vis 70000..70019 > 67584, 80 rows > 64
     _run_gpu_drawn(1, 80, 32, 64, 70080, 4, 2048, [280000], 41, [0], [0, 1, 39, 40, 78, 79])
 
 
-def test_bf16_rowwise_kernel_decode_72_sequences():
+def test_bf16_long_kernel_decode_72_sequences():
     qpos = [4 * 70080 - 8 * b for b in range(72)]
     _run_gpu_drawn(72, 1, 32, 64, 70080, 4, 2048, qpos, 42, [0, 35, 71], [0])
 
 
+def test_bf16_long_kernel_prefill_chunk_at_1m_tokens():
+    # a prefill chunk ending at 2^20 tokens: 262144 entries, ragged row lengths
+    _run_gpu_drawn(1, 72, 64, 128, 262144, 4, 2048, [(1 << 20) - 72], 44, [0], [0, 37, 71])
+
+
+def test_bf16_rowwise_kernel_rows_past_2_19():
+    # n_vis 530000.. > 2^19: the 8-bit radix select
+    _run_gpu_drawn(1, 80, 32, 64, 530080, 4, 2048, [4 * 530000], 45, [0], [0, 79],
+                   min_nv=1 << 19)
+
+
 def test_bf16_rowwise_kernel_all_tied_takes_lowest_indices():
+    idx = _run_gpu_drawn(1, 80, 32, 64, 530080, 4, 2048, [4 * 530000], 46, [0], [0, 79],
+                         w_zero=True, min_nv=1 << 19)
+    assert torch.equal(idx[0, 0].cpu(), torch.arange(2048, dtype=torch.int32))
+
+
+def test_bf16_long_kernel_all_tied_takes_lowest_indices():
     idx = _run_gpu_drawn(1, 80, 32, 64, 70080, 4, 2048, [280000], 43, [0], [0, 79], w_zero=True)
     assert torch.equal(idx[0].cpu(), torch.arange(2048, dtype=torch.int32).expand(80, 2048))
 
