@@ -765,9 +765,10 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
 // issued kLongU steps of the row at a time.
 constexpr int kLongMax = 1 << 19;             // LDS bitmap of 64 KB
 constexpr int kLongU = 8;
+constexpr int kLongCopies = 2;                // histogram copies: two workgroups fit a CU
 
 __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
-  __shared__ __align__(16) uint32_t hist4[kHistBins * 4];   // 4 copies, then bits 19..8 (one copy)
+  __shared__ __align__(16) uint32_t hist4[kHistBins * kLongCopies];   // copies, then bits 19..8 (one)
   extern __shared__ __align__(16) uint32_t lbits[];        // [64 per 2048-entry step]
   __shared__ int32_t cidx[kPrefCand];
   __shared__ uint32_t ckey[kPrefCand];
@@ -808,7 +809,7 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
     }
   };
 
-  for (int e = tid; e < kHistBins * 4; e += kPT) hist4[e] = 0u;
+  for (int e = tid; e < kHistBins * kLongCopies; e += kPT) hist4[e] = 0u;
   if (tid == 0) n_cand = 0;
   __syncthreads();
 
@@ -816,7 +817,7 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
   pass([&](int, int e, const uint32_t* key) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      if (e + c < nv) atomicAdd(&hist4[4 * (key[c] >> 20) + (l & 3)], 1u);
+      if (e + c < nv) atomicAdd(&hist4[kLongCopies * (key[c] >> 20) + (l & (kLongCopies - 1))], 1u);
   });
   __syncthreads();
 
@@ -827,9 +828,9 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
 #pragma unroll
     for (int q = 0; q < kPBins; ++q) {
       const int bin = kHistBins - 1 - kPBins * tid - q;
-      if (copies == 4) {
-        const uint4 h = *reinterpret_cast<const uint4*>(&hist4[4 * bin]);
-        c[q] = h.x + h.y + h.z + h.w;
+      if (copies == 2) {
+        const uint2 h = *reinterpret_cast<const uint2*>(&hist4[2 * bin]);
+        c[q] = h.x + h.y;
       } else {
         c[q] = hist4[bin];
       }
@@ -855,7 +856,7 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
     }
     __syncthreads();
   };
-  find_bucket((uint32_t)keff, 4);
+  find_bucket((uint32_t)keff, kLongCopies);
   const uint32_t d1 = t_d, above1 = t_above;
   for (int e = tid; e < kHistBins; e += kPT) hist4[e] = 0u;
   __syncthreads();
