@@ -10,10 +10,13 @@
 // The scores come from score.hip (the same passage defines them).
 //
 // Top-k.  Keys are the order-preserving uint32 images of the fp32 scores.
-//  * Prefix path (many rows of up to 67584 entries, e.g. chunked prefill):
-//    one workgroup per row keeps the row's keys in registers, fixes the
-//    threshold's 24-bit prefix from two LDS histograms, and writes the set
-//    through an LDS bitmap, reading the scores from HBM once.
+//  * Prefix path (many rows of up to 16384 entries): one workgroup per row
+//    keeps the row's keys in registers, fixes the threshold's 24-bit prefix
+//    from two LDS histograms, and writes the set through an LDS bitmap,
+//    reading the scores from HBM once.
+//  * Long-row path (many rows of up to 2^19 entries, e.g. chunked prefill):
+//    the same steps with the row read in three passes, two workgroups per
+//    compute unit.
 //  * Row-wise path (many longer rows): one workgroup per row runs a 4-pass
 //    MSD radix select (8-bit digits, LDS histograms with wave-level
 //    aggregation of equal digits), then one ordered pass that keeps every key
@@ -208,7 +211,10 @@ __global__ void __launch_bounds__(kTopkThreads) topk_rowwise_kernel(TopkArgs a) 
 //    kPrefCand of them);
 //  * the set is emitted in ascending index order by one block-wide scan over
 //    per-thread runs of bitmap words.
-constexpr int kPrefixMax = 67584;
+// Rows up to 16384 entries: beyond that the three-pass kernel below, with
+// two workgroups per compute unit, is the faster one (the chunked prefill's
+// 66K-entry rows: 0.78 ms here with 67584-entry registers, 0.39 ms less there).
+constexpr int kPrefixMax = 16384;
 constexpr int kPrefCand = 1024;
 constexpr int kPT = 512;                           // threads per row
 constexpr int kPU = (kPrefixMax + 4 * kPT - 1) / (4 * kPT);   // float4 loads per thread
@@ -753,8 +759,8 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
   }
 }
 
-// Rows of kPrefixMax to kLongMax visible entries (prefill chunks at up to 2M
-// tokens of context), one 512-thread workgroup per row: the steps of
+// Rows of kPrefixMax to kLongMax visible entries (prefill chunks from about
+// 64K to 2M tokens of context), one 512-thread workgroup per row: the steps of
 // topk_prefix_kernel with the row read from memory in each of three passes
 // instead of held in registers.  Pass 1 builds the histogram of key bits
 // 31..20 (four lane-interleaved copies) and fixes the threshold's 12-bit

@@ -135,14 +135,14 @@ def test_e4m3_keys_head_and_dim_variants(HI, dI):
 
 
 
-# Rows longer than the register-resident kernel holds (67584 visible entries)
+# Rows longer than the register-resident kernel holds (16384 visible entries)
 # and too many of them for the split path (more than 64 rows): up to 2^19
 # visible entries the three-pass kernel (histograms and bitmap in LDS, the row
 # re-read per pass), beyond that the 8-bit radix select; one workgroup per
 # row.  Drawn on the GPU; the oracle scores sampled rows from a host copy of
 # their sequences.
 def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zero=False,
-                   min_nv=67584):
+                   min_nv=16384):
     print(f"indexer (long rows) B={B} Tq={Tq} N={N} k={k}", flush=True)
     q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI), device=DEV), "bf16")
     K = synth.store(synth.normal(seed, "KI", (B, N, dI), device=DEV), "bf16")
@@ -170,7 +170,7 @@ def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zer
 
 
 def test_bf16_long_kernel_prefill_rows_past_67584():
-    # 80 queries at 280000..280079: n_vis 70000..70019 > 67584, 80 rows > 64
+    # 80 queries at 280000..280079: n_vis 70000..70019, 80 rows > 64
     _run_gpu_drawn(1, 80, 32, 64, 70080, 4, 2048, [280000], 41, [0], [0, 1, 39, 40, 78, 79])
 
 
