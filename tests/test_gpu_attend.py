@@ -200,3 +200,17 @@ def test_d512_csa_mixed_prefill_single_split_with_sink():
 
 def test_d512_csa_bf16_decode_without_rotated_dims():
     _case(0, 2, 1, 64, 512, 0, 900, 100, 4, 16, [3600, 3000], "bf16", 64)
+
+
+# D = 512 with one or two heads: up to 64 tokens per block, whose query
+# angles (tokens x rope_dims/2 (cos, sin)) take the most LDS beside the tiles.
+def test_d512_csa_one_head_128_rope_dims():
+    _case(0, 1, 70, 1, 512, 128, 400, 32, 4, 16, [600], "bf16", 71)
+
+
+def test_d512_hca_two_heads_mixed_prefill():
+    _case(1, 1, 100, 2, 512, 64, 64, 0, 16, 32, [900], "mixed", 72, sink=True)
+
+
+def test_d512_hca_one_head_split_decode():
+    _case(1, 3, 1, 1, 512, 64, 3000, 0, 4, 64, [12000, 11000, 40], "bf16", 73)
