@@ -761,17 +761,23 @@ __global__ void __launch_bounds__(1024) topk_resolve_kernel(TopkArgs a) {
 
 // Rows of kPrefixMax to kLongMax visible entries (prefill chunks from about
 // 64K to 2M tokens of context), one 512-thread workgroup per row: the steps of
-// topk_prefix_kernel with the row read from memory in each of three passes
-// instead of held in registers.  Pass 1 builds the histogram of key bits
-// 31..20 (four lane-interleaved copies) and fixes the threshold's 12-bit
-// bucket; pass 2 the histogram of bits 19..8 over the keys in it, fixing the
-// 24-bit prefix P; pass 3 writes the bitmap of the keys above P and collects
-// the keys carrying P, which are ranked by (key desc, index asc).  The set is
-// emitted in ascending index order from the LDS bitmap.  A pass's loads are
-// issued kLongU steps of the row at a time.
+// topk_prefix_kernel with the row read from memory in passes instead of held
+// in registers.  Pass 1 builds the histogram of key bits 31..20 (two
+// lane-interleaved copies) and fixes the threshold's 12-bit bucket d1.  Pass 2
+// builds the histogram of bits 19..8 over the keys in d1, fixing the 24-bit
+// prefix P, writes the bitmap of the keys above d1 and keeps the indices of
+// the keys in d1 (a few thousand in a 64K-entry prefill row) in the LDS of
+// the second histogram copy; their keys are then gathered again, those above
+// P set in the bitmap and those carrying P collected.  When d1 holds more
+// keys than that LDS does, pass 3 reads the row once more for both.  The
+// keys carrying P are ranked by (key desc, index asc), and the set is emitted
+// in ascending index order from the LDS bitmap.  A pass's loads are issued
+// kLongU steps of the row at a time.
 constexpr int kLongMax = 1 << 19;             // LDS bitmap of 64 KB
 constexpr int kLongU = 8;
 constexpr int kLongCopies = 2;                // histogram copies: two workgroups fit a CU
+constexpr int kLongCand = kHistBins * (kLongCopies - 1);   // indices of the keys in d1
+static_assert(kLongCand >= 1024, "pass 2 keeps the keys of bucket d1 in the second copy");
 
 __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
   __shared__ __align__(16) uint32_t hist4[kHistBins * kLongCopies];   // copies, then bits 19..8 (one)
@@ -780,7 +786,7 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
   __shared__ uint32_t ckey[kPrefCand];
   __shared__ uint32_t wsum[kPT / 64];
   __shared__ uint32_t bc[4];
-  __shared__ uint32_t t_d, t_above, n_cand;
+  __shared__ uint32_t t_d, t_above, n_cand, n_c1;
   const int row = blockIdx.x;
   const int nv = (int)row_nvis(a, row);
   const int keff = min(a.k, nv);
@@ -816,7 +822,7 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
   };
 
   for (int e = tid; e < kHistBins * kLongCopies; e += kPT) hist4[e] = 0u;
-  if (tid == 0) n_cand = 0;
+  if (tid == 0) { n_cand = 0; n_c1 = 0; }
   __syncthreads();
 
   // ---- pass 1: histogram of key bits 31..20
@@ -867,40 +873,74 @@ __global__ void __launch_bounds__(kPT) topk_long_kernel(TopkArgs a) {
   for (int e = tid; e < kHistBins; e += kPT) hist4[e] = 0u;
   __syncthreads();
 
-  // ---- pass 2: bits 19..8 of the keys in bucket d1
-  pass([&](int, int e, const uint32_t* key) {
+  // ---- pass 2: bits 19..8 of the keys in bucket d1, the bitmap of the keys
+  // above d1, and the indices of the keys in d1 (while they fit).  Lanes
+  // 8w .. 8w+7 hold the 32 entries of one bitmap word, merged with DPP moves.
+  uint32_t* c1 = &hist4[kHistBins];
+  pass([&](int step, int e, const uint32_t* key) {
+    uint32_t nib = 0, in = 0;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      if (e + c < nv && (key[c] >> 20) == d1) atomicAdd(&hist4[(key[c] >> 8) & 4095u], 1u);
+    for (int c = 0; c < 4; ++c) {
+      const bool ok = e + c < nv;
+      nib |= (uint32_t)(ok && (key[c] >> 20) > d1) << c;
+      in |= (uint32_t)(ok && (key[c] >> 20) == d1) << c;
+    }
+    const uint32_t word = or8(nib << (4 * (l & 7)));
+    if ((l & 7) == 0) lbits[step * (kPT / 8) + (tid >> 3)] = word;
+    if (__ballot(in != 0)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((in >> c) & 1u) {
+          atomicAdd(&hist4[(key[c] >> 8) & 4095u], 1u);
+          const uint32_t pos = atomicAdd(&n_c1, 1u);
+          if (pos < (uint32_t)kLongCand) c1[pos] = (uint32_t)(e + c);
+        }
+      }
+    }
   });
   __syncthreads();
   find_bucket((uint32_t)keff - above1, 1);
   const uint32_t P = (d1 << 12) | t_d;                         // 24-bit threshold prefix
   const uint32_t need_p = (uint32_t)keff - above1 - t_above;   // >= 1 keys carrying P
 
-  // ---- pass 3: bitmap of the keys above P; the keys carrying P (and their
-  // indices) collected on the way.  Lanes 8w .. 8w+7 hold the 32 entries of
-  // one bitmap word, merged with DPP moves.
-  pass([&](int step, int e, const uint32_t* key) {
-    uint32_t nib = 0, eq = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t k24 = key[c] >> 8;
-      nib |= (uint32_t)(e + c < nv && k24 > P) << c;
-      eq |= (uint32_t)(e + c < nv && k24 == P) << c;
-    }
-    const uint32_t word = or8(nib << (4 * (l & 7)));
-    if ((l & 7) == 0) lbits[step * (kPT / 8) + (tid >> 3)] = word;
-    if (__ballot(eq != 0)) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if ((eq >> c) & 1u) {
-          const uint32_t pos = atomicAdd(&n_cand, 1u);
-          if (pos < (uint32_t)kPrefCand) { cidx[pos] = e + c; ckey[pos] = key[c]; }
-        }
+  const int nc1 = (int)n_c1;
+  if (nc1 <= kLongCand) {
+    // the keys of bucket d1 gathered again: above P into the bitmap, equal
+    // to P collected with their indices
+    for (int ci = tid; ci < nc1; ci += kPT) {
+      const int e = (int)c1[ci];
+      const uint32_t kk = score_key(s[e]);
+      if ((kk >> 8) > P) {
+        atomicOr(&lbits[e >> 5], 1u << (e & 31));
+      } else if ((kk >> 8) == P) {
+        const uint32_t pos = atomicAdd(&n_cand, 1u);
+        if (pos < (uint32_t)kPrefCand) { cidx[pos] = e; ckey[pos] = kk; }
       }
     }
-  });
+  } else {
+    // ---- pass 3 (bucket d1 did not fit): bitmap of the keys above P; the
+    // keys carrying P (and their indices) collected on the way.
+    pass([&](int step, int e, const uint32_t* key) {
+      uint32_t nib = 0, eq = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t k24 = key[c] >> 8;
+        nib |= (uint32_t)(e + c < nv && k24 > P) << c;
+        eq |= (uint32_t)(e + c < nv && k24 == P) << c;
+      }
+      const uint32_t word = or8(nib << (4 * (l & 7)));
+      if ((l & 7) == 0) lbits[step * (kPT / 8) + (tid >> 3)] = word;
+      if (__ballot(eq != 0)) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if ((eq >> c) & 1u) {
+            const uint32_t pos = atomicAdd(&n_cand, 1u);
+            if (pos < (uint32_t)kPrefCand) { cidx[pos] = e + c; ckey[pos] = key[c]; }
+          }
+        }
+      }
+    });
+  }
   __syncthreads();
   const int nc = (int)n_cand;
   if (nc <= kPrefCand) {

@@ -158,6 +158,14 @@ def _run_gpu_drawn(B, Tq, HI, dI, N, m, k, qpos, seed, seqs, rows_per_seq, w_zer
                                 [qpos[b] for b in seqs], m, rows)
     assert (nv > min_nv).all() and B * Tq > 64
     o_idx = oracle.topk(s, nv, k)
+    # keys sharing the k-th key's top 12 bits (the long kernel keeps up to
+    # 4096 of them in LDS, else reads the row a third time)
+    for rr in range(len(rows)):
+        u = s[rr, :int(nv[rr])].astype(np.float32).view(np.uint32)
+        key = np.where(u >> 31 != 0, ~u, u | np.uint32(0x80000000))
+        kth = np.sort(key)[::-1][min(k, int(nv[rr])) - 1]
+        print(f"  row {rows[rr]}: {int((key >> 20 == kth >> 20).sum())} keys in the threshold's "
+              f"12-bit bucket", flush=True)
     g_idx = np.stack([idx[seqs[j], i].cpu().numpy() for j, i in rows])
     g_sc = np.stack([score[seqs[j], i].cpu().numpy() for j, i in rows])
     check_topk(g_idx, o_idx, s, nv, k)
@@ -182,6 +190,29 @@ def test_bf16_long_kernel_decode_72_sequences():
 def test_bf16_long_kernel_prefill_chunk_at_1m_tokens():
     # a prefill chunk ending at 2^20 tokens: 262144 entries, ragged row lengths
     _run_gpu_drawn(1, 72, 64, 128, 262144, 4, 2048, [(1 << 20) - 72], 44, [0], [0, 37, 71])
+
+
+def test_long_kernel_threshold_bucket_past_its_lds_list():
+    # Scores spread evenly over [1, 1.1): the f32 queries pick the keys' first
+    # dim, so every key lands in the threshold's 12-bit bucket (more keys than
+    # the kernel keeps in LDS: the row is read a third time) and about 20
+    # share each 24-bit prefix (ranked by key, then index).
+    B, Tq, HI, dI, N, m, k, qpos = 1, 80, 4, 32, 70080, 4, 2048, [280000]
+    print(f"indexer (long rows, narrow band) B={B} Tq={Tq} N={N} k={k}", flush=True)
+    q = torch.zeros((B, Tq, HI, dI))
+    q[..., 0] = 1.0
+    w = torch.full((B, Tq, HI), 0.25)
+    K = torch.zeros((B, N, dI))
+    K[..., 0] = 1.0 + 0.1 * synth.uniform(47, "KI", (B, N))
+    idx = lac.indexer_topk(q.to(DEV), w.to(DEV), K.to(DEV), m=m, k=k, q_pos0=qpos)
+    torch.cuda.synchronize()
+    rows = [(0, i) for i in (0, 41, 79)]
+    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.F32, B, Tq, HI, dI, N, qpos, m,
+                                rows)
+    key = s.astype(np.float32).view(np.uint32)
+    assert ((key[:, :int(nv.min())] >> 23) == (key[0, 0] >> 23)).all()   # one exponent
+    g_idx = np.stack([idx[b, i].cpu().numpy() for b, i in rows])
+    check_topk(g_idx, oracle.topk(s, nv, k), s, nv, k)
 
 
 def test_bf16_rowwise_kernel_rows_past_2_19():
