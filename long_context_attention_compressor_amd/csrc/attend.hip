@@ -103,20 +103,29 @@ AttnPlan make_plan(int B, int Tq, int H, int D, int r, int kv_fmt, int n_entries
   p.chunk = (int)round_up((p.max_entries + ns - 1) / ns, 32);
   if (p.chunk > kIdxLds) p.chunk = kIdxLds;    // a split's CSA indices fit in LDS
   p.nsplit = (p.max_entries + p.chunk - 1) / p.chunk;
+  int ns_alloc = p.nsplit;
   if (p.nsplit > 1 && W > 0) {
     // Split-K with a window: the window rows (rotated in the kernel, with
     // low parts) get splits of one tile each after the compressed entries'
-    // splits, so that their extra work does not lengthen the longest split.
+    // splits, so that their extra work does not lengthen the longest split
+    // -- while the launch stays within one wave of blocks over the chip;
+    // beyond that the extra splits would start a second wave, and the
+    // window rows stay in the last splits of the entry list.  The partials
+    // are sized for the window splits, the most any target plans.
     const int n_comp_max = p.max_entries - (W + p.G - 1);
     const int n_win_max = W + p.G - 1;
-    p.wchunk = kTile;
-    p.nsplit = (n_comp_max + p.chunk - 1) / p.chunk + (n_win_max + kTile - 1) / kTile;
+    const int ns_w = (n_comp_max + p.chunk - 1) / p.chunk + (n_win_max + kTile - 1) / kTile;
+    ns_alloc = std::max(ns_alloc, ns_w);
+    if ((int64_t)p.n_work * ns_w <= kGridTarget) {
+      p.wchunk = kTile;
+      p.nsplit = ns_w;
+    }
   }
-  if (p.nsplit > 1) {
+  if (ns_alloc > 1) {
     p.off_po = off;
-    off += round_up((int64_t)p.n_work * p.nsplit * 64 * D * 2, 256);
+    off += round_up((int64_t)p.n_work * ns_alloc * 64 * D * 2, 256);
     p.off_pml = off;
-    off += round_up((int64_t)p.n_work * p.nsplit * 64 * 2 * 4, 256);
+    off += round_up((int64_t)p.n_work * ns_alloc * 64 * 2 * 4, 256);
   }
   p.total = off;
   return p;

@@ -214,3 +214,10 @@ def test_d512_hca_two_heads_mixed_prefill():
 
 def test_d512_hca_one_head_split_decode():
     _case(1, 3, 1, 1, 512, 64, 3000, 0, 4, 64, [12000, 11000, 40], "bf16", 73)
+
+
+def test_d512_csa_mixed_decode_many_sequences_window_in_entry_splits():
+    # 40 work items: one-tile window splits would take the launch past 256
+    # workgroups, so the window rows ride in the last entry splits
+    _case(0, 40, 1, 64, 512, 64, 3000, 512, 4, 64, [12000 - 97 * b for b in range(40)], "mixed",
+          74)
