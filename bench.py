@@ -15,7 +15,9 @@ pair_decode_1m_ungrouped makes the same calls one launch each.
 Other workloads (--workload): pair_decode_1m_e4m3_indexer (the same step with
 the indexer keys stored as E4M3, one byte per dim), pair_decode_1m_fp8_indexer
 (E4M3 indexer queries and keys on the FP8 matrix cores),
-pair_decode_1m_mxfp4_indexer (MXFP4 indexer keys), csa_decode_128k (32
+pair_decode_1m_mxfp4_indexer (MXFP4 indexer keys, widened for bf16 queries),
+pair_decode_1m_fp4_indexer (E4M3 queries against MXFP4 keys on the
+block-scaled FP4 matrix cores), csa_decode_128k (32
 sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
 csa_chunk_prefill_1m (the same chunk ending at 2^20 tokens),
@@ -193,6 +195,8 @@ class PairDecode:
                 "window": c["W"], "heads": c["H"], "kv_dim": c["D"], "rope_dims": c["r"],
                 "indexer": (f"{c['HI']}x{c['dI']} bf16" if self.ki_fmt == "bf16" else
                             f"{c['HI']}x{c['dI']}, bf16 queries, mxfp4 keys (e2m1 + e8m0 per 32)"
+                            if self.ki_fmt == "mxfp4" and self.qi_fmt == "bf16" else
+                            f"{c['HI']}x{c['dI']}, e4m3 queries, mxfp4 keys (scaled fp4 mfma)"
                             if self.ki_fmt == "mxfp4" else
                             f"{c['HI']}x{c['dI']}, bf16 queries, e4m3 keys" if self.qi_fmt == "bf16"
                             else f"{c['HI']}x{c['dI']}, e4m3 queries and keys (fp8 mfma)"),
@@ -284,6 +288,14 @@ class PairDecodeMxfp4Indexer(PairDecode):
     per 32 dims, 68 bytes per key); the step quantises the newest key."""
     name = "pair_decode_1m_mxfp4_indexer"
     ki_fmt = "mxfp4"
+
+
+class PairDecodeFp4Indexer(PairDecode):
+    """pair_decode_1m with E4M3 indexer queries against MXFP4 keys: codes
+    and block scales go to the scaled FP4 matrix cores as stored."""
+    name = "pair_decode_1m_fp4_indexer"
+    ki_fmt = "mxfp4"
+    qi_fmt = "mixed"
 
 
 class PairDecodeRmsNorm(PairDecode):
@@ -685,7 +697,7 @@ class BulkCompress128K(BulkCompress1M):
 
 WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeUngrouped, PairDecodeE4M3Indexer,
                                   PairDecodeFp8Indexer,
-                                  PairDecodeMxfp4Indexer,
+                                  PairDecodeMxfp4Indexer, PairDecodeFp4Indexer,
                                   PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, ChunkPrefill1M, HcaPrefill,
                                   ProjectionPrefill, ProjectionDecode,

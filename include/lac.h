@@ -94,6 +94,9 @@ typedef enum {
 /* Flag for the dtype of indexer_topk: the workspace was prepared by
  * indexer_topk_prepare (see there). */
 #define LAC_TOPK_PREPARED 0x200
+/* Flag for the dtype of indexer_topk, with LAC_MXFP4 keys only: q_idx holds
+ * E4M3 codes (see indexer_topk). */
+#define LAC_Q_E4M3 0x400
 
 /* Largest batch the position arrays may describe. */
 #define LAC_MAX_BATCH 128
@@ -223,6 +226,11 @@ int32_t hca_compress_rmsnorm(const void* raw_kv, const void* logits, int32_t in_
  *               Training": FP4 block scales fold losslessly into FP8).
  *               Each key value E2M1 x 2^(b - 127) is formed exactly in bf16
  *               (which holds every such FP8 value) and scored as above.
+ *               With LAC_MXFP4 | LAC_Q_E4M3 (d_I = 128 only), q_idx holds
+ *               E4M3 codes of d_I bytes per head and each product of an
+ *               E4M3 query value with a key's E2M1 code and block scale runs
+ *               on the block-scaled FP4 matrix cores as stored (no widening:
+ *               every product exact, sums in fp32).
  *   topk_idx    [B, Tq, k] int32, output
  *   topk_score  [B, Tq, k] float32, output (score of each chosen index,
  *               -inf in padded slots); may be NULL

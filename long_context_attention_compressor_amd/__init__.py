@@ -24,13 +24,14 @@ __all__ = [
     "csa_attend", "hca_attend", "attend_workspace_size", "time_next_launch", "lib",
     "grouped_output_projection", "grouped_projection_workspace_size",
     "LAC_F32", "LAC_BF16", "LAC_KV_E4M3_ROPE_BF16", "LAC_E4M3", "LAC_MXFP4", "LAC_SCORE_BF16",
-    "KERNELS",
+    "LAC_Q_E4M3", "KERNELS",
     "CallList", "group",
 ]
 
 LAC_F32, LAC_BF16, LAC_KV_E4M3_ROPE_BF16, LAC_E4M3, LAC_MXFP4 = 0, 1, 2, 3, 4
 LAC_SCORE_BF16 = 0x100      # dtype flag of indexer_topk: scores rounded to bf16
 LAC_TOPK_PREPARED = 0x200   # dtype flag of indexer_topk: workspace zeroed by indexer_topk_prepare
+LAC_Q_E4M3 = 0x400          # dtype flag of indexer_topk: E4M3 q_idx with MXFP4 keys
 KERNELS = {"compress": 0, "indexer_score": 1, "topk": 2, "attend": 3, "combine": 4,
            "project": 5}
 STATUS = {0: "LAC_OK", 1: "LAC_ERR_INVALID", 2: "LAC_ERR_UNSUPPORTED", 3: "LAC_ERR_WORKSPACE",
@@ -316,9 +317,11 @@ def indexer_topk_workspace_size(B, Tq, N, k) -> int:
 
 def _indexer_dtype(q_idx, k_idx):
     dI = q_idx.shape[-1]
-    if k_idx.dtype == torch.uint8 and q_idx.dtype == torch.bfloat16 and \
-            k_idx.shape[-1] == dI // 2 + dI // 32 and dI % 32 == 0:
-        return LAC_MXFP4                       # MXFP4 key rows (include/lac.h)
+    if k_idx.dtype == torch.uint8 and k_idx.shape[-1] == dI // 2 + dI // 32 and dI % 32 == 0:
+        if q_idx.dtype == torch.bfloat16:
+            return LAC_MXFP4                   # MXFP4 key rows (include/lac.h)
+        if q_idx.dtype == torch.uint8:
+            return LAC_MXFP4 | LAC_Q_E4M3      # E4M3 queries, scaled FP4 products
     if q_idx.dtype == torch.uint8:
         if k_idx.dtype != torch.uint8:
             raise TypeError("E4M3 (uint8) q_idx needs E4M3 (uint8) k_idx")
@@ -340,7 +343,8 @@ def indexer_topk(q_idx, w, k_idx, m, k, q_pos0=None, topk_idx=None, topk_score=N
                  workspace=None, stream=None, score_bf16=False, prepared=False):
     """Scores + top-k.  q_idx [B,Tq,H_I,d_I], w [B,Tq,H_I] f32, k_idx [B,N,d_I]
     (the dtype of q_idx; uint8 E4M3 codes with bf16 or uint8 E4M3 q_idx; or
-    uint8 MXFP4 rows of d_I/2 + d_I/32 bytes with bf16 q_idx).
+    uint8 MXFP4 rows of d_I/2 + d_I/32 bytes with bf16 q_idx, or with uint8
+    E4M3 q_idx at d_I = 128: the scaled FP4 matrix-core path, LAC_Q_E4M3).
     score_bf16: select on scores rounded to bf16 (include/lac.h).
     prepared: the workspace went through indexer_topk_prepare (LAC_TOPK_PREPARED).
     Returns topk_idx [B,Tq,k] int32 (ascending, -1 padded)."""

@@ -175,7 +175,10 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
                      void* stream) {
   const int round_bf16 = (dtype & LAC_SCORE_BF16) != 0;
   const int prepared = (dtype & LAC_TOPK_PREPARED) != 0;
-  dtype &= ~(LAC_SCORE_BF16 | LAC_TOPK_PREPARED);
+  const bool q_e4m3 = (dtype & LAC_Q_E4M3) != 0;
+  dtype &= ~(LAC_SCORE_BF16 | LAC_TOPK_PREPARED | LAC_Q_E4M3);
+  if (q_e4m3 && dtype != LAC_MXFP4)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: LAC_Q_E4M3 applies to LAC_MXFP4 keys only", fn);
   if (prepared && fixed)
     return fail(LAC_ERR_INVALID, "%s: LAC_TOPK_PREPARED needs a caller's workspace", fn);
   if (dtype != LAC_F32 && dtype != LAC_BF16 && dtype != LAC_KV_E4M3_ROPE_BF16 && dtype != LAC_E4M3 &&
@@ -193,6 +196,8 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
   } else if ((int64_t)H_I * d_I > 8192) {
     return fail(LAC_ERR_UNSUPPORTED, "%s: float32 path needs H_I * d_I <= 8192", fn);
   }
+  if (q_e4m3 && d_I != 128)
+    return fail(LAC_ERR_UNSUPPORTED, "%s: E4M3 queries with MXFP4 keys need d_I = 128", fn);
   lac::IndexerArgs a{};
   int32_t st = take_positions(fn, "q_pos0", q_pos0, B, Tq, 1, &a.qpos);
   if (st) return st;
@@ -217,7 +222,8 @@ int32_t indexer_impl(const char* fn, const void* q_idx, const float* w, const vo
     if (workspace_bytes < need)
       return fail(LAC_ERR_WORKSPACE, "%s: workspace of %zu bytes is below the %zu needed", fn, workspace_bytes, need);
   }
-  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = dtype; a.round_bf16 = round_bf16; a.prepared = prepared;
+  a.q = q_idx; a.w = w; a.K = k_idx; a.fmt = q_e4m3 ? lac::kMX4E4 : dtype;
+  a.round_bf16 = round_bf16; a.prepared = prepared;
   a.B = B; a.Tq = Tq; a.HI = H_I; a.dI = d_I; a.N = N; a.m = m; a.k = k;
   a.topk_idx = topk_idx; a.topk_score = topk_score;
   return launch_status(fn, lac::launch_indexer_topk(a, workspace, static_cast<hipStream_t>(stream)));

@@ -16,6 +16,31 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// gfx950's block-scaled FP8/FP4 matrix product, 32 x 32 outputs over 64
+// products per step: acc[32 x 32] += (A x 2^(sa - 127)) (B x 2^(sb - 127)).
+// Operand layout (pinned on the device against exact products): lane l holds
+// row (A) or column (B) l % 32; with h = l / 32,
+//   FP8 (format 0, E4M3): byte p of the 32 is step index
+//       32 (p / 16) + 16 h + p % 16,
+//   FP4 (format 4, E2M1; only the first 16 bytes are read): nibble q (value
+//       2i in the low nibble of byte i) is step index 32 h + q,
+// and the scale of row/column l % 32 over step indices [32c, 32c + 32) comes
+// from lane l % 32 + 32 c (byte 0 of its scale word).  The result is laid out
+// as for v_mfma_f32_32x32x16_bf16.
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma_scaled_32x32x64(const i32x8& a, const i32x8& b, const f32x16& acc,
+                                                       int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc, FA, FB, 0, sa, 0, sb);
+}
+// Four 8-byte fragments (consecutive step indices of one lane) as one operand.
+__device__ __forceinline__ i32x8 cat4(long a, long b, long c, long d) {
+  i32x8 r;
+  r[0] = (int)a; r[1] = (int)(a >> 32); r[2] = (int)b; r[3] = (int)(b >> 32);
+  r[4] = (int)c; r[5] = (int)(c >> 32); r[6] = (int)d; r[7] = (int)(d >> 32);
+  return r;
+}
 
 // Streaming loads (read-once data): non-temporal hint, 16 or 8 bytes.
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
@@ -27,7 +52,8 @@ __device__ __forceinline__ uint2 ld_stream8(const void* p) {
   return make_uint2(v.x, v.y);
 }
 
-enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2, kE4M3 = 3, kMXFP4 = 4 };
+// kMX4E4: MXFP4 indexer keys scored against E4M3 queries on the scaled FP4 MFMA.
+enum Fmt { kF32 = 0, kBF16 = 1, kMixed = 2, kE4M3 = 3, kMXFP4 = 4, kMX4E4 = 5 };
 
 // Per-batch positions passed by value (the library keeps nothing on the device).
 struct Positions {

@@ -66,6 +66,7 @@ struct IndexerArgs {
   const float* w;        // [B, Tq, HI]
   const void* K;         // [B, N, dI]
   int fmt;               // kF32 | kBF16 | kMixed (E4M3 keys) | kE4M3 (E4M3 queries and keys) | kMXFP4 (MXFP4 keys)
+                         // | kMX4E4 (MXFP4 keys, E4M3 queries)
   int round_bf16;        // scores rounded to bf16 before selection
   int prepared;          // the workspace's counters are already zero (indexer_topk_prepare)
   int B, Tq, HI, dI, N, m, k;

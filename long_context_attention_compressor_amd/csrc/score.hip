@@ -27,8 +27,8 @@ namespace {
 constexpr int kHistBins = kScoreHistBins;
 // Decode score launches: tile stages in flight per wave (bf16 keys, E4M3
 // keys) and the blocks the grid spreads over (bf16, E4M3 queries).
-constexpr int kStagesBF16 = 2, kStagesF8 = 2;
-constexpr int kDecodeBlocksBF16 = 512, kDecodeBlocksF8 = 768;
+constexpr int kStagesBF16 = 2, kStagesF8 = 2, kStagesFP4 = 4;
+constexpr int kDecodeBlocksBF16 = 512, kDecodeBlocksF8 = 768, kDecodeBlocksFP4 = 512;
 
 // E4M3 key tiles in LDS (E4M3 queries): a row is d_I bytes, its 8-byte
 // chunks XOR-swizzled by f8_swz(row), chosen so that the MFMA-layout reads
@@ -123,14 +123,21 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   // bytes; a tile is copied as bytes to a per-wave LDS area and widened from
   // there to the bf16 layout.
   constexpr bool FP4 = KF == kMXFP4;
-  constexpr int KROWB = FP4 ? dI / 2 + dI / 32 : KF == kMixed || F8 ? dI : ROWB;
+  // MXFP4 keys against E4M3 queries (kMX4E4): no LDS at all.  Each lane loads
+  // its MFMA operands straight from the key rows: the 16 code bytes of the
+  // 32-dim blocks hf and 2 + hf of key ln (one per 64-dim product step) and
+  // the row's scale word, and the scaled FP4 product consumes the codes and
+  // scales as stored.
+  constexpr bool FP4D = KF == kMX4E4;
+  static_assert(!FP4D || dI == 128, "direct MXFP4 keys take d_I = 128");
+  constexpr int KROWB = FP4 || FP4D ? dI / 2 + dI / 32 : KF == kMixed || F8 ? dI : ROWB;
   constexpr int CH8 = dI / 8;                // 8-byte chunks per E4M3 key row
   constexpr int KTILEB = 32 * KROWB;
-  constexpr int NLD = (KTILEB + 1023) / 1024;   // 16-byte registers per lane per tile
+  constexpr int NLD = FP4D ? 3 : (KTILEB + 1023) / 1024;   // 16-byte registers per lane per tile
   constexpr int kLPR = dI / 8;               // E4M3: lanes per key (8 codes each)
   constexpr int kRPI = 64 / kLPR;            // E4M3: keys per 8-byte load
   __shared__ float sw[kRowsPerBlock][HI];
-  __shared__ __align__(16) uint8_t ktile[4][F8 ? KTILEB : TILEB];
+  __shared__ __align__(16) uint8_t ktile[4][FP4D ? 16 : F8 ? KTILEB : TILEB];
   __shared__ __align__(16) uint8_t kraw[4][FP4 ? NLD * 1024 : 16];
   __shared__ uint32_t lhist[kHistBins];
   const int wave = threadIdx.x >> 6;
@@ -196,6 +203,14 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
           const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsrc, (kRPI * j + l / kLPR) * dI + (l % kLPR) * 8, 0, 2);
           if (h == 0) { st[u].x = v[0]; st[u].y = v[1]; } else { st[u].z = v[0]; st[u].w = v[1]; }
         }
+      } else if constexpr (FP4D) {
+        // u = 0, 1: code bytes of block 2u + hf of key ln; u = 2: its scale word
+        if (u < 2) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, ln * KROWB + 16 * (2 * u + hf), 0, 2);
+          st[u] = make_uint4(v.x, v.y, v.z, v.w);
+        } else {
+          st[u].x = __builtin_amdgcn_raw_buffer_load_b32(rsrc, ln * KROWB + dI / 2, 0, 2);
+        }
       } else if constexpr (FP4) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, u * 1024 + l * 16, 0, 2);
         st[u] = make_uint4(v.x, v.y, v.z, v.w);
@@ -212,7 +227,13 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
       }
     }
   };
+  uint4 cur[FP4D ? NLD : 1];
   auto store_tile = [&](const uint4* st) {
+    if constexpr (FP4D) {
+#pragma unroll
+      for (int u = 0; u < NLD; ++u) cur[u] = st[u];
+      return;
+    }
     if constexpr (FP4) {
       // bytes of the tile to the wave's raw area, then lane l widens chunks
       // l, l + 64, ... (key kk = o / CH, 8 dims c = o % CH): 4 code bytes and
@@ -255,24 +276,35 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   // else, so their latency overlaps the set-up below.  PF tiles are in
   // flight per wave (two for the one-query decode shape, whose registers
   // allow it); the stages alternate.
-  constexpr int PF = QPW == 1 ? (F8 ? kStagesF8 : kStagesBF16) : 1;
+  constexpr int PF = QPW == 1 ? (FP4D ? kStagesFP4 : F8 ? kStagesF8 : kStagesBF16) : 1;
   uint4 stage[PF][NLD];
   // Query fragments first: lane (ln, hf) holds head ht*32+ln, dims
   // hf*dI/2 + s*8 .. +8.  (They come from L2 for all but the first waves of
   // a row, so the first tile's compute need not wait for the second tile.)
-  typedef typename std::conditional<F8, long, bf16x8>::type QFrag;
+  typedef typename std::conditional<F8 || FP4D, long, bf16x8>::type QFrag;
   QFrag qf[QPW][HT][KS];
   int64_t nv_row[QPW];
+  __amdgpu_buffer_rsrc_t srow[QPW];
   {
 #pragma unroll
     for (int qi = 0; qi < QPW; ++qi) {
       const int rr = wr * QPW + qi;
       const int i = min(i0 + rr, a.Tq - 1);
       nv_row[qi] = (i0 + rr < a.Tq) ? n_visible((int64_t)a.qpos.v[b] + i, a.N, a.m) : 0;
+      srow[qi] = __builtin_amdgcn_make_buffer_rsrc(a.scores + ((int64_t)b * a.Tq + i) * a.Np, 0,
+                                                   (int)(nv_row[qi] * 4), 0x00020000);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         const int64_t qrow = (((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln;
-        if constexpr (F8) {
+        if constexpr (FP4D) {
+          // step u, fragment r: the query bytes that meet the key dims
+          // 64u + 32(r/2) + 16hf + 8(r%2) .. +8 in the scaled FP4 product
+          const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * dI;
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
+            qf[qi][ht][s] = *reinterpret_cast<const long*>(
+                qp + 64 * (s >> 2) + 32 * ((s >> 1) & 1) + 16 * hf + 8 * (s & 1));
+        } else if constexpr (F8) {
           const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * dI + hf * (dI / 2);
 #pragma unroll
           for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const long*>(qp + s * 8);
@@ -303,7 +335,9 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     QFrag kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if constexpr (F8) {
+      if constexpr (FP4D) {
+        kf[s] = 0;                           // unused: the operands are in cur
+      } else if constexpr (F8) {
         const int c = hf * (CH8 / 2) + s;
         kf[s] = *reinterpret_cast<const long*>(kt + ln * dI + ((c ^ f8_swz<dI>(ln)) * 8));
       } else {
@@ -319,11 +353,30 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc = {};
+        if constexpr (FP4D) {
+          // E4M3 queries (unit scales) x MXFP4 keys with their own block
+          // scales: step u covers dims 64u .. 64u + 63; this lane's key
+          // block is 2u + hf, whose scale is byte 2u + hf of the scale word.
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          if constexpr (F8)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
-          else
+          for (int u = 0; u < 2; ++u) {
+            i32x8 kb = {};
+            kb[0] = (int)cur[u].x; kb[1] = (int)cur[u].y; kb[2] = (int)cur[u].z; kb[3] = (int)cur[u].w;
+            acc = mfma_scaled_32x32x64<0, 4>(
+                cat4(qf[qi][ht][4 * u], qf[qi][ht][4 * u + 1], qf[qi][ht][4 * u + 2], qf[qi][ht][4 * u + 3]),
+                kb, acc, 127, (int)(cur[2].x >> (8 * (2 * u + hf))));
+          }
+        } else if constexpr (F8) {
+          // E4M3 x E4M3 on the 64-deep scaled FP8 product (unit scales):
+          // fragments 4u .. 4u+3 of a lane are 32 bytes of its row, in the
+          // same order for queries and keys, so every dim meets its partner.
+#pragma unroll
+          for (int u = 0; u < KS / 4; ++u)
+            acc = mfma_scaled_32x32x64<0, 0>(
+                cat4(qf[qi][ht][4 * u], qf[qi][ht][4 * u + 1], qf[qi][ht][4 * u + 2], qf[qi][ht][4 * u + 3]),
+                cat4(kf[4 * u], kf[4 * u + 1], kf[4 * u + 2], kf[4 * u + 3]), acc, 127, 127);
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
         }
         // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
@@ -335,7 +388,10 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
       const float pr = round_bf16(part);
       part = a.round_bf16 ? pr : part;
       const bool live = hf == 0 && j < nv_row[qi];
-      if (live) a.scores[((int64_t)b * a.Tq + i0 + rr) * a.Np + j] = part;
+      // through the row's buffer resource: a lane that is not live stores out
+      // of range and its store is dropped, so the store is issued on every path
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(part), srow[qi], live ? (int)j * 4 : 0x7fffffff,
+                                            0, 0);
       if (do_hist) hist_add(lhist, live, score_key(part) >> 20);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);      // LDS reads of this tile done
@@ -391,15 +447,27 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
     }
   done:;
   } else if (n_mine > 0) {
-    for (int64_t it = 0; it < n_mine; it += PF) {
+    // Whole rounds of PF tiles first.  Every load and store in them is issued
+    // on every path (a refill past the wave's share loads a tile with no rows,
+    // which reads nothing), so the compiler's memory-counter waits are exact
+    // and only the oldest stage is waited for: a refill issued under a branch
+    // would make it wait for every load in flight at each stage.
+    const int64_t none = (a.N + 31) / 32;      // a tile with no rows
+    int64_t it = 0;
+    for (; it + PF <= n_mine; it += PF) {
 #pragma unroll
       for (int f = 0; f < PF; ++f) {
-        if (it + f < n_mine) {
-          const int64_t tile = gw + (it + f) * nw;
-          stage_in(stage[f]);
-          if (it + f + PF < n_mine) load_tile(tile + PF * nw, stage[f]);
-          compute(tile);
-        }
+        const int64_t k = it + f;
+        stage_in(stage[f]);
+        load_tile(k + PF < n_mine ? gw + (k + PF) * nw : none, stage[f]);
+        compute(gw + k * nw);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < PF; ++f) {
+      if (it + f < n_mine) {
+        stage_in(stage[f]);
+        compute(gw + (it + f) * nw);
       }
     }
   }
@@ -560,11 +628,18 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc = {};
+        if constexpr (F8) {
+          // E4M3 x E4M3 on the 64-deep scaled FP8 product (unit scales):
+          // fragments 4u .. 4u+3 of a lane are 32 bytes of its row, in the
+          // same order for queries and keys, so every dim meets its partner.
 #pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          if constexpr (F8)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
-          else
+          for (int u = 0; u < KS / 4; ++u)
+            acc = mfma_scaled_32x32x64<0, 0>(
+                cat4(qf[qi][ht][4 * u], qf[qi][ht][4 * u + 1], qf[qi][ht][4 * u + 2], qf[qi][ht][4 * u + 3]),
+                cat4(kf[4 * u], kf[4 * u + 1], kf[4 * u + 2], kf[4 * u + 3]), acc, 127, 127);
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s)
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[qi][ht][s], kf[s], acc, 0, 0, 0);
         }
         // acc[v] is head ht*32 + 8*(v/4) + 4*hf + v%4 against key j.
@@ -623,7 +698,7 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
       // kE4M3: E4M3 queries and keys (FP8 MFMA); kMXFP4: bf16 queries, MXFP4
       // keys (the decode kernel for every shape)
       const int kf = a.fmt;
-      if (a.Tq >= 8 && !sb.split && kf != kMXFP4) {
+      if (a.Tq >= 8 && !sb.split && kf != kMXFP4 && kf != kMX4E4) {
         // Prefill: a block of eight waves shares each key tile among 8 * QPW
         // queries and sweeps all the keys they see.
 #define LAC_SCORE_CASE(ht, ks, qpw)                                                        \
@@ -645,12 +720,18 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
         // one round of the 512 resident blocks (two blocks of 4 waves per
         // compute unit at this kernel's register use), so no partial second
         // round trails the sweep.
-        const int64_t per_row = std::max<int64_t>(1, (kf == kE4M3 ? kDecodeBlocksF8 : kDecodeBlocksBF16) / R);
+        const int64_t per_row = std::max<int64_t>(
+            1, (kf == kE4M3 ? kDecodeBlocksF8 : kf == kMX4E4 ? kDecodeBlocksFP4 : kDecodeBlocksBF16) / R);
         sa.tiles_per_wave = (int)std::max<int64_t>(2, (n_tiles + 4 * per_row - 1) / (4 * per_row));
         const int64_t chunks = (n_tiles + 4 * sa.tiles_per_wave - 1) / (4 * sa.tiles_per_wave);
         // dynamic schedule: about the last quarter of the sweep
         sa.n_static = std::max(2, sa.tiles_per_wave * 3 / 4);
         sa.n_groups = (int)std::min<int64_t>(16, std::max<int64_t>(1, chunks / 8));
+        // E4M3 and MXFP4 keys: the sweep is bound by each tile's MFMA and
+        // ReLU-weighting work rather than by HBM, so every wave takes its
+        // strided share (its rounds of tiles keep exact prefetch waits); the
+        // counters only pay for bf16 keys, whose waves stream at different rates.
+        if (kf == kE4M3 || kf == kMX4E4) sa.tile_ctr = nullptr;
         const int groups = a.B * a.Tq;
 #define LAC_SCORE_CASE(ht, ks)                                                      \
   if (HT == ht && KS == ks)                                                         \
@@ -658,8 +739,16 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
           : kf == kMixed ? launch_score<ht, ks, 1, 1, kMixed>(sa, chunks, groups, st) \
           : kf == kMXFP4 ? launch_score<ht, ks, 1, 1, kMXFP4>(sa, chunks, groups, st) \
                          : launch_score<ht, ks, 1, 1, kBF16>(sa, chunks, groups, st);
+        if (kf == kMX4E4) {
+          // d_I = 128 only (the ABI refuses other widths for this format)
+          if (KS == 8)
+            err = HT == 1   ? launch_score<1, 8, 1, 1, kMX4E4>(sa, chunks, groups, st)
+                  : HT == 2 ? launch_score<2, 8, 1, 1, kMX4E4>(sa, chunks, groups, st)
+                            : launch_score<4, 8, 1, 1, kMX4E4>(sa, chunks, groups, st);
+        } else {
         LAC_SCORE_CASE(1, 4) LAC_SCORE_CASE(1, 8) LAC_SCORE_CASE(2, 4) LAC_SCORE_CASE(2, 8)
         LAC_SCORE_CASE(4, 4) LAC_SCORE_CASE(4, 8)
+        }
 #undef LAC_SCORE_CASE
       }
     }

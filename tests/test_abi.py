@@ -99,6 +99,10 @@ def test_indexer_rejects_bad_arguments(L):
     neg = (ctypes.c_int64 * 2)(5, -1)
     assert call(pos=neg) == 1
     assert call(dtype=0, HI=64, dI=256) == 2
+    # E4M3 queries (LAC_Q_E4M3) go with MXFP4 keys only, at d_I = 128
+    assert call(dtype=L.LAC_BF16 | L.LAC_Q_E4M3) == 2 and "LAC_Q_E4M3" in _err(L)
+    assert call(dtype=L.LAC_E4M3 | L.LAC_Q_E4M3) == 2
+    assert call(dtype=L.LAC_MXFP4 | L.LAC_Q_E4M3, dI=64) == 2 and "d_I = 128" in _err(L)
 
 
 def test_attend_rejects_bad_arguments(L):

@@ -311,16 +311,19 @@ def test_bf16_scores_all_tied_take_the_lowest_indices():
 
 # MXFP4 keys (E2M1 codes with E8M0 block scales) and bf16 queries: the keys
 # are widened exactly to bf16 in LDS.  Random code bytes; scales 2^-3..2^3.
-def _run_fp4(B, Tq, HI, dI, N, m, k, qpos, seed):
-    print(f"indexer mxfp4 keys B={B} Tq={Tq} HI={HI} dI={dI} N={N} k={k}", flush=True)
-    q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI)), "bf16")
+# With E4M3 queries (qfmt "mixed": E4M3 codes) the codes and scales go to the
+# block-scaled FP4 matrix cores as stored (LAC_Q_E4M3).
+def _run_fp4(B, Tq, HI, dI, N, m, k, qpos, seed, qfmt="bf16"):
+    print(f"indexer mxfp4 keys, {qfmt} queries B={B} Tq={Tq} HI={HI} dI={dI} N={N} k={k}",
+          flush=True)
+    q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI)), qfmt)
     K = synth.mxfp4_rows(seed, "KI", (B, N), dI)
     w = synth.uniform(seed, "w", (B, Tq, HI))
     score = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
     idx = lac.indexer_topk(q.to(DEV), w.to(DEV), K.to(DEV), m=m, k=k, q_pos0=qpos,
                            topk_score=score)
     torch.cuda.synchronize()
-    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.DTYPE_CODES["bf16"], B, Tq, HI,
+    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.DTYPE_CODES[qfmt], B, Tq, HI,
                                 dI, N, qpos, m, k_dtype=synth.DTYPE_CODES["mxfp4"])
     o_idx = oracle.topk(s, nv, k)
     g_idx = idx.cpu().numpy().reshape(B * Tq, k)
@@ -349,3 +352,44 @@ def test_mxfp4_keys_prefill_rows():
 @pytest.mark.parametrize("HI,dI", [(32, 64), (128, 128)])
 def test_mxfp4_keys_head_and_dim_variants(HI, dI):
     _run_fp4(2, 1, HI, dI, 2100, 4, 256, [8400, 9000], 54 + HI + dI)
+
+
+# E4M3 queries against MXFP4 keys on the scaled FP4 matrix cores (d_I = 128).
+def test_mxfp4_keys_e4m3_queries_decode_split_path():
+    _run_fp4(2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], 61, qfmt="mixed")
+
+
+def test_mxfp4_keys_e4m3_queries_decode_prefix_path_ragged():
+    _run_fp4(4, 1, 64, 128, 5003, 4, 512, [4 * 5003 + 1, 4 * 5003, 4 * 3000 + 3, 40000], 62,
+             qfmt="mixed")
+
+
+def test_mxfp4_keys_e4m3_queries_prefill_rows():
+    _run_fp4(1, 20, 64, 128, 2010, 4, 300, [8000], 63, qfmt="mixed")
+
+
+def test_mxfp4_keys_e4m3_queries_rows_that_see_nothing():
+    _run_fp4(2, 9, 64, 128, 40, 4, 8, [0, 100], 64, qfmt="mixed")
+
+
+@pytest.mark.parametrize("HI", [32, 128])
+def test_mxfp4_keys_e4m3_queries_head_variants(HI):
+    _run_fp4(2, 1, HI, 128, 2100, 4, 256, [8400, 9000], 65 + HI, qfmt="mixed")
+
+
+def test_mxfp4_keys_e4m3_queries_bf16_scores():
+    print("indexer mxfp4 keys, e4m3 queries, bf16 scores", flush=True)
+    B, Tq, HI, dI, N, m, k, qpos, seed = 2, 1, 64, 128, 40000, 4, 2048, [4 * 40000, 4 * 39001 + 2], 66
+    q = synth.store(synth.normal(seed, "qI", (B, Tq, HI, dI)), "mixed")
+    K = synth.mxfp4_rows(seed, "KI", (B, N), dI)
+    w = synth.uniform(seed, "w", (B, Tq, HI))
+    score = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    idx = lac.indexer_topk(q.to(DEV), w.to(DEV), K.to(DEV), m=m, k=k, q_pos0=qpos,
+                           topk_score=score, score_bf16=True)
+    torch.cuda.synchronize()
+    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.DTYPE_CODES["mixed"], B, Tq, HI,
+                                dI, N, qpos, m, k_dtype=synth.DTYPE_CODES["mxfp4"], score_bf16=True)
+    o_idx = oracle.topk(s, nv, k)
+    g_idx = idx.cpu().numpy().reshape(B * Tq, k)
+    g_sc = score.cpu().numpy().reshape(B * Tq, k).astype(np.float64)
+    check_topk_bf16(g_idx, g_sc, o_idx, s, nv, k)
