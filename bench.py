@@ -55,11 +55,12 @@ BF16_PEAK_TFLOPS = 2500.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273731584, "pair_decode_1m_ungrouped": 273731584,
-                       "csa_decode_128k": 277464064, "csa_chunk_prefill": 1330352128,
-                       "pair_decode_1m_fp8_indexer": 139360256,
-                       "pair_decode_1m_mxfp4_indexer": 76702720}
-SCORE_TRAFFIC_SOURCE_SHA256 = "b4f7338e6bf5913564328b601bac09fc91ed627f9e88e56676fd6106312d4420"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273741824, "pair_decode_1m_ungrouped": 273741824,
+                       "csa_decode_128k": 277474304, "csa_chunk_prefill": 1330361344,
+                       "pair_decode_1m_fp8_indexer": 138920960,
+                       "pair_decode_1m_mxfp4_indexer": 76721152,
+                       "pair_decode_1m_fp4_indexer": 76256256}
+SCORE_TRAFFIC_SOURCE_SHA256 = "48a782ebd82885c798079da1d6e113984d5bd4dc98093d5496db6d27f36b3d76"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
