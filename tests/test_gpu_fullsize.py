@@ -41,12 +41,15 @@ def _check_select(g_idx, qI, w, KI_h, fmt, B, Tq, HI, dI, N, qpos, m, k, rows, k
     return o_idx, same
 
 
-@pytest.mark.parametrize("ki_fmt", ["bf16", "mixed", "mxfp4"])
-def test_pair_decode_1m(ki_fmt):
+@pytest.mark.parametrize("ki_fmt,qi_fmt", [("bf16", "bf16"), ("mixed", "bf16"), ("mxfp4", "bf16"),
+                                           ("mxfp4", "mixed")])
+def test_pair_decode_1m(ki_fmt, qi_fmt):
     # ki_fmt "mixed": the indexer keys are E4M3 (the mixed format, no rotated
-    # dims); "mxfp4": E2M1 codes with a scale per 32 dims
-    print(f"full size: pair decode, B=4 at 2^20, indexer keys {ki_fmt}", flush=True)
-    c = synth.pair_decode(ki_fmt=ki_fmt, device=DEV)
+    # dims); "mxfp4": E2M1 codes with a scale per 32 dims.  qi_fmt "mixed":
+    # E4M3 indexer queries (with MXFP4 keys: the scaled FP4 matrix-core path)
+    print(f"full size: pair decode, B=4 at 2^20, indexer keys {ki_fmt}, queries {qi_fmt}",
+          flush=True)
+    c = synth.pair_decode(ki_fmt=ki_fmt, qi_fmt=qi_fmt, device=DEV)
     B, N, Nh, m, mh, D, r, k, W = (c[x] for x in ("B", "N", "Nh", "m", "m_hca", "D", "r", "k", "W"))
     HI, dI, H, ctx = c["HI"], c["dI"], c["H"], c["q_pos0"]
     # the benchmarked step
@@ -85,7 +88,7 @@ def test_pair_decode_1m(ki_fmt):
 
     rows = [(b, 0) for b in range(B)]
     g_idx = idx.cpu().numpy()
-    o_idx, _ = _check_select(g_idx, _h(c["qI"]), _h(c["w"]), KI_h, "bf16", B, 1, HI, dI, N,
+    o_idx, _ = _check_select(g_idx, _h(c["qI"]), _h(c["w"]), KI_h, qi_fmt, B, 1, HI, dI, N,
                              ctx, m, k, rows, k_fmt=ki_fmt)
 
     # CSA attention on the oracle's selection, same launch configuration
