@@ -21,6 +21,8 @@ block-scaled FP4 matrix cores), csa_decode_128k (32
 sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
 csa_chunk_prefill_1m (the same chunk ending at 2^20 tokens),
+csa_chunk_prefill_fp8_indexer (the 262144-token chunk with E4M3 indexer
+queries and keys),
 hca_prefill_8k (8192 tokens; TFLOP/s), bulk_compress_1m and
 bulk_compress_128k (building the compressed caches of whole contexts from raw
 activations; GB/s), and the grouped output projection.
@@ -48,6 +50,7 @@ import torch  # noqa: E402
 METRIC = "CSA+HCA decode tokens/s and HBM GB/s at 128K-1M ctx; prefill TFLOP/s"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
 
 # HBM bytes per launch of the indexer score kernel, from rocprofv3 FETCH_SIZE and
 # WRITE_SIZE (one pass each), scaled by what the same counters read for a 1 GiB
@@ -370,10 +373,12 @@ class ChunkPrefill:
     unit = "TFLOP/s"
     timer_kernel = "indexer_score"
     ctx = 262144
+    idx_fmt = "bf16"        # indexer queries and keys; "mixed": E4M3 codes
 
     def __init__(self, lac, synth, dev, sets, seed=3):
         self.lac = lac
-        c = self.c = synth.csa_chunk_prefill(seed=seed, ctx=self.ctx, device=dev)
+        c = self.c = synth.csa_chunk_prefill(seed=seed, ctx=self.ctx, idx_fmt=self.idx_fmt,
+                                             device=dev)
         T = c["chunk"]
         self.idx = torch.empty((1, T, c["k"]), dtype=torch.int32, device=dev)
         self.out = torch.empty_like(c["q"])
@@ -416,7 +421,9 @@ class ChunkPrefill:
         c = self.c
         return {"workload": self.name, "batch": 1, "ctx": c["q_pos0"], "chunk": c["chunk"],
                 "topk": c["k"], "window": c["W"], "heads": c["H"], "kv_dim": c["D"],
-                "indexer": f"{c['HI']}x{c['dI']} bf16", "csa_entries": c["N"], "kv_format": "bf16"}
+                "indexer": (f"{c['HI']}x{c['dI']} bf16" if self.idx_fmt == "bf16" else
+                            f"{c['HI']}x{c['dI']}, e4m3 queries and keys (scaled fp8 mfma)"),
+                "csa_entries": c["N"], "kv_format": "bf16"}
 
     def cpu_sample(self):
         import oracle
@@ -427,8 +434,8 @@ class ChunkPrefill:
         h = {k_: synth.host_bytes(v) for k_, v in c.items() if isinstance(v, torch.Tensor)}
         rows = [(0, i) for i in range(0, c["chunk"], 1024)]       # 4 of 4096 queries
         t0 = time.perf_counter()
-        idx, _, _ = chain.csa_select(h["qI"], h["w"], h["KI"], "bf16", 1, c["chunk"], c["HI"],
-                                     c["dI"], c["N"], c["q_pos0"], c["m"], c["k"], rows)
+        idx, _, _ = chain.csa_select(h["qI"], h["w"], h["KI"], self.idx_fmt, 1, c["chunk"],
+                                     c["HI"], c["dI"], c["N"], c["q_pos0"], c["m"], c["k"], rows)
         oracle.attend(h["q"], oracle.BF16, h["ckv"], oracle.BF16, c["N"], 0, idx, c["k"], c["m"],
                       h["raw"], c["T_raw"], c["raw_pos0"], c["W"], None, 0.0, 1, c["chunk"],
                       c["H"], c["D"], c["r"], 1e4, c["q_pos0"], rows)
@@ -446,6 +453,14 @@ class ChunkPrefill1M(ChunkPrefill):
     selection."""
     name = "csa_chunk_prefill_1m"
     ctx = (1 << 20) - 4096
+
+
+class ChunkPrefillFp8Indexer(ChunkPrefill):
+    """csa_chunk_prefill with E4M3 indexer queries and keys: the score matrix
+    on gfx950's block-scaled FP8 product (unit scales), the rest as in the
+    bf16 workload; the score kernel is priced against the FP8 dense peak."""
+    name = "csa_chunk_prefill_fp8_indexer"
+    idx_fmt = "mixed"
 
 
 class HcaPrefill(ChunkPrefill):
@@ -698,7 +713,7 @@ class BulkCompress128K(BulkCompress1M):
 
 WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeUngrouped, PairDecodeE4M3Indexer,
                                   PairDecodeFp8Indexer,
-                                  PairDecodeMxfp4Indexer, PairDecodeFp4Indexer,
+                                  PairDecodeMxfp4Indexer, PairDecodeFp4Indexer, ChunkPrefillFp8Indexer,
                                   PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, ChunkPrefill1M, HcaPrefill,
                                   ProjectionPrefill, ProjectionDecode,
@@ -820,10 +835,12 @@ def main():
         else:
             kfl, kname = wl.indexer_flops(), "score_prefill_kernel (indexer scores)"
             traffic = _score_traffic(wl.name)
+        # the score kernel's own dtype sets its peak (E4M3 indexer: FP8 dense)
+        kpeak = FP8_PEAK_TFLOPS if getattr(wl, "idx_fmt", "bf16") == "mixed" else BF16_PEAK_TFLOPS
         ach = kfl / (kern_ms / 1e3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
-                           "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": traffic,
+                           "peak": kpeak, "unit": "TFLOP/s",
+                           "frac": round(ach / kpeak, 4), "traffic": traffic,
                            "traffic_unit": "B/launch",
                            "launch_ms": round(kern_ms / launches, 5),
                            "step_frac": round(res["value"] / BF16_PEAK_TFLOPS, 4)}

@@ -143,18 +143,20 @@ def csa_decode(seed=2, B=32, ctx=131072, D=512, m=4, r=64, HI=64, dI=128, H=64, 
 
 
 def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, dI=128, H=64,
-                      k=2048, W=128, device="cpu"):
+                      k=2048, W=128, idx_fmt="bf16", device="cpu"):
     """CSA chunked prefill: a chunk of queries appended to a long context.  The
     cache rows of the context are drawn directly; the chunk's raw KV and
-    indexer keys are compressed into the rows that follow."""
+    indexer keys are compressed into the rows that follow.  Indexer queries
+    and keys are bf16, or E4M3 codes with idx_fmt = "mixed"."""
     B = 1
     N_ctx = ctx // m
     N = (ctx + chunk) // m
     T_raw = chunk + W - 1
     ckv = torch.zeros((B, N, D), dtype=torch.bfloat16, device=device)
     ckv[:, :N_ctx] = store(normal(seed, "ckv", (B, N_ctx, D), device=device), "bf16")
-    KI = torch.zeros((B, N, dI), dtype=torch.bfloat16, device=device)
-    KI[:, :N_ctx] = store(normal(seed, "KI", (B, N_ctx, dI), device=device), "bf16")
+    KI = torch.zeros((B, N, dI), dtype=torch.bfloat16 if idx_fmt == "bf16" else torch.uint8,
+                     device=device)
+    KI[:, :N_ctx] = store(normal(seed, "KI", (B, N_ctx, dI), device=device), idx_fmt)
     return dict(
         kind="csa_chunk_prefill", fmt="bf16", B=B, D=D, m=m, r=r, HI=HI, dI=dI, H=H, k=k, W=W,
         N=N, N_ctx=N_ctx, chunk=chunk, theta=10000.0, q_pos0=ctx, raw_pos0=ctx - W + 1,
@@ -164,9 +166,10 @@ def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, d
         z=store(normal(seed, "z", (B, chunk, D), device=device), "bf16"),
         kI_raw=store(normal(seed, "kI_raw", (B, chunk, dI), device=device), "bf16"),
         zI=store(normal(seed, "zI", (B, chunk, dI), device=device), "bf16"),
-        qI=store(normal(seed, "qI", (B, chunk, HI, dI), device=device), "bf16"),
+        qI=store(normal(seed, "qI", (B, chunk, HI, dI), device=device), idx_fmt),
         w=uniform(seed, "w", (B, chunk, HI), device=device),
         q=store(normal(seed, "q", (B, chunk, H, D), device=device), "bf16"),
+        idx_fmt=idx_fmt,
     )
 
 

@@ -55,6 +55,15 @@ def test_block_sizes_and_no_rope(m):
     _run(2, m * 5 + (m // 2), 256, m, 0, "bf16", "bf16", [0, 4096 * m], 4 + m)
 
 
+# Long blocks split over S threads per channel group: with a power-of-two
+# group count the shares merge by lane shuffles inside a wave, with 3 or 25
+# groups (D = 96 in a decode step, D = 200) by the LDS tree alone.
+@pytest.mark.parametrize("B,T,D,r", [(1, 128, 96, 16), (2, 128 * 3 + 5, 200, 8), (1, 128, 512, 64),
+                                     (3, 256 + 9, 64, 0)])
+def test_long_blocks_token_split_merges(B, T, D, r):
+    _run(B, T, D, 128, r, "bf16", "bf16", [1 << 19] * B, 80 + D, hca=True)
+
+
 def test_indexer_keys_f32_no_rope():
     _run(3, 64, 32, 4, 0, "f32", "f32", None, 5)
 
