@@ -215,6 +215,34 @@ def test_long_kernel_threshold_bucket_past_its_lds_list():
     check_topk(g_idx, oracle.topk(s, nv, k), s, nv, k)
 
 
+def test_bf16_long_kernel_threshold_bucket_past_its_lds_list():
+    # The same narrow band from bf16 queries and keys, scored by the prefill
+    # score kernel: s = k0 + k1 / 64 with k0 in [1, 1.1) and k1 in [0, 1), all
+    # in one 12-bit bucket, several dozen keys per distinct score.
+    B, Tq, HI, dI, N, m, k, qpos = 1, 80, 32, 64, 70080, 4, 2048, [280000]
+    print(f"indexer (long rows, narrow band, bf16) B={B} Tq={Tq} N={N} k={k}", flush=True)
+    q = torch.zeros((B, Tq, HI, dI))
+    q[..., 0] = 1.0
+    q[..., 1] = 1.0 / 64
+    w = torch.full((B, Tq, HI), 1.0 / HI)
+    K = torch.zeros((B, N, dI))
+    K[..., 0] = 1.0 + 0.1 * synth.uniform(48, "KI", (B, N))
+    K[..., 1] = synth.uniform(49, "KI", (B, N))
+    q, K = q.to(torch.bfloat16), K.to(torch.bfloat16)
+    score = torch.empty((B, Tq, k), dtype=torch.float32, device=DEV)
+    idx = lac.indexer_topk(q.to(DEV), w.to(DEV), K.to(DEV), m=m, k=k, q_pos0=qpos,
+                           topk_score=score)
+    torch.cuda.synchronize()
+    rows = [(0, i) for i in (0, 41, 79)]
+    s, nv = oracle.index_scores(host(q), host(w), host(K), synth.DTYPE_CODES["bf16"], B, Tq, HI,
+                                dI, N, qpos, m, rows)
+    g_idx = np.stack([idx[b, i].cpu().numpy() for b, i in rows])
+    check_topk(g_idx, oracle.topk(s, nv, k), s, nv, k)
+    g_sc = np.stack([score[b, i].cpu().numpy() for b, i in rows]).astype(np.float64)
+    for rr in range(len(rows)):
+        assert np.allclose(g_sc[rr], s[rr, g_idx[rr]], rtol=1e-6, atol=0)
+
+
 def test_bf16_rowwise_kernel_rows_past_2_19():
     # n_vis 530000.. > 2^19: the 8-bit radix select
     _run_gpu_drawn(1, 80, 32, 64, 530080, 4, 2048, [4 * 530000], 45, [0], [0, 79],
