@@ -94,6 +94,32 @@ def test_scores_with_mxfp4_keys_use_the_decoded_key_values():
         assert np.allclose(s[i, : nv[i]], ref[0, i, : nv[i]], rtol=1e-13, atol=1e-12)
 
 
+def test_scores_with_e4m3_queries_and_mxfp4_keys_use_the_decoded_values():
+    # The FP4 QK path with FP8 queries: queries are E4M3 codes from PyTorch's
+    # float8 conversion, decoded here by PyTorch; keys are MXFP4 rows decoded
+    # by the generic minifloat formula and the E8M0 rule.
+    B, Tq, HI, dI, N, m = 2, 3, 8, 64, 25, 4
+    qpos0 = np.array([4 * N + 1, 70])
+    rng = np.random.default_rng(23)
+    keys = rng.integers(0, 256, (B, N, dI // 2 + dI // 32), dtype=np.uint8)
+    keys[..., dI // 2:] = rng.integers(121, 134, (B, N, dI // 32))
+    qv = torch.from_numpy(rng.standard_normal((B, Tq, HI, dI)) * 2.0).to(torch.float8_e4m3fn)
+    q8 = qv.view(torch.uint8).numpy().copy()
+    w = rng.uniform(-0.3, 1, (B, Tq, HI)).astype(np.float32)
+    s, nv = oracle.index_scores(q8, w, keys, oracle.MIXED, B, Tq, HI, dI, N, qpos0, m,
+                                k_dtype=oracle.MXFP4)
+    kd = np.stack([_decode_rows(keys[b], dI) for b in range(B)])
+    qd = qv.to(torch.float64).numpy()
+    dots = np.einsum("bthc,bjc->btjh", qd, kd)
+    ref = (np.maximum(dots, 0.0) * w.astype(np.float64)[:, :, None, :]).sum(-1)
+    for b in range(B):
+        for i in range(Tq):
+            rr = b * Tq + i
+            assert nv[rr] == min(N, (qpos0[b] + i) // m)
+            assert np.allclose(s[rr, : nv[rr]], ref[b, i, : nv[rr]], rtol=1e-13, atol=1e-12)
+            assert np.isneginf(s[rr, nv[rr]:]).all()
+
+
 def test_mxfp4_encode_round_trips_rows_whose_blocks_reach_four():
     # a block whose largest code is 4 or 6 times 2^k has shared exponent k,
     # so encoding its decoded values gives the same bytes back
