@@ -22,7 +22,8 @@ sequences at 131072),
 csa_chunk_prefill (4096 queries appended to 262144 tokens; TFLOP/s),
 csa_chunk_prefill_1m (the same chunk ending at 2^20 tokens),
 csa_chunk_prefill_fp8_indexer (the 262144-token chunk with E4M3 indexer
-queries and keys),
+queries and keys), csa_chunk_prefill_fp4_indexer (E4M3 queries against MXFP4
+keys),
 hca_prefill_8k (8192 tokens; TFLOP/s), bulk_compress_1m and
 bulk_compress_128k (building the compressed caches of whole contexts from raw
 activations; GB/s), and the grouped output projection.
@@ -422,7 +423,9 @@ class ChunkPrefill:
         return {"workload": self.name, "batch": 1, "ctx": c["q_pos0"], "chunk": c["chunk"],
                 "topk": c["k"], "window": c["W"], "heads": c["H"], "kv_dim": c["D"],
                 "indexer": (f"{c['HI']}x{c['dI']} bf16" if self.idx_fmt == "bf16" else
-                            f"{c['HI']}x{c['dI']}, e4m3 queries and keys (scaled fp8 mfma)"),
+                            f"{c['HI']}x{c['dI']}, e4m3 queries and keys (scaled fp8 mfma)"
+                            if self.idx_fmt == "mixed" else
+                            f"{c['HI']}x{c['dI']}, e4m3 queries, mxfp4 keys (scaled fp4 mfma)"),
                 "csa_entries": c["N"], "kv_format": "bf16"}
 
     def cpu_sample(self):
@@ -434,8 +437,9 @@ class ChunkPrefill:
         h = {k_: synth.host_bytes(v) for k_, v in c.items() if isinstance(v, torch.Tensor)}
         rows = [(0, i) for i in range(0, c["chunk"], 1024)]       # 4 of 4096 queries
         t0 = time.perf_counter()
-        idx, _, _ = chain.csa_select(h["qI"], h["w"], h["KI"], self.idx_fmt, 1, c["chunk"],
-                                     c["HI"], c["dI"], c["N"], c["q_pos0"], c["m"], c["k"], rows)
+        qf, kf = ("mixed", "mxfp4") if self.idx_fmt == "fp4" else (self.idx_fmt, self.idx_fmt)
+        idx, _, _ = chain.csa_select(h["qI"], h["w"], h["KI"], qf, 1, c["chunk"], c["HI"],
+                                     c["dI"], c["N"], c["q_pos0"], c["m"], c["k"], rows, k_fmt=kf)
         oracle.attend(h["q"], oracle.BF16, h["ckv"], oracle.BF16, c["N"], 0, idx, c["k"], c["m"],
                       h["raw"], c["T_raw"], c["raw_pos0"], c["W"], None, 0.0, 1, c["chunk"],
                       c["H"], c["D"], c["r"], 1e4, c["q_pos0"], rows)
@@ -461,6 +465,15 @@ class ChunkPrefillFp8Indexer(ChunkPrefill):
     bf16 workload; the score kernel is priced against the FP8 dense peak."""
     name = "csa_chunk_prefill_fp8_indexer"
     idx_fmt = "mixed"
+
+
+class ChunkPrefillFp4Indexer(ChunkPrefill):
+    """csa_chunk_prefill with E4M3 indexer queries against MXFP4 keys: the
+    score matrix on gfx950's block-scaled FP4 product; the chunk's new keys
+    are quantised by the compress call.  Priced against the FP8 dense peak
+    (the products' E4M3 side)."""
+    name = "csa_chunk_prefill_fp4_indexer"
+    idx_fmt = "fp4"
 
 
 class HcaPrefill(ChunkPrefill):
@@ -714,6 +727,7 @@ class BulkCompress128K(BulkCompress1M):
 WORKLOADS = {w.name: w for w in (PairDecode, PairDecodeUngrouped, PairDecodeE4M3Indexer,
                                   PairDecodeFp8Indexer,
                                   PairDecodeMxfp4Indexer, PairDecodeFp4Indexer, ChunkPrefillFp8Indexer,
+                                  ChunkPrefillFp4Indexer,
                                   PairDecodeRmsNorm, PairDecodeOverlap, CsaDecode,
                                   ChunkPrefill, ChunkPrefill1M, HcaPrefill,
                                   ProjectionPrefill, ProjectionDecode,
@@ -836,7 +850,7 @@ def main():
             kfl, kname = wl.indexer_flops(), "score_prefill_kernel (indexer scores)"
             traffic = _score_traffic(wl.name)
         # the score kernel's own dtype sets its peak (E4M3 indexer: FP8 dense)
-        kpeak = FP8_PEAK_TFLOPS if getattr(wl, "idx_fmt", "bf16") == "mixed" else BF16_PEAK_TFLOPS
+        kpeak = FP8_PEAK_TFLOPS if getattr(wl, "idx_fmt", "bf16") != "bf16" else BF16_PEAK_TFLOPS
         ach = kfl / (kern_ms / 1e3) / 1e12
         res["roofline"] = {"bound": "mfma", "kernel": kname, "achieved": round(ach, 2),
                            "peak": kpeak, "unit": "TFLOP/s",

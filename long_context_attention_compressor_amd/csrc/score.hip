@@ -499,12 +499,20 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   // Keys in HBM: bf16 rows or E4M3 rows (widened to bf16 in LDS for bf16
   // queries, kept E4M3 in LDS for E4M3 queries).
   constexpr bool F8 = KF == kE4M3;
-  constexpr int KROWB = KF == kMixed || F8 ? dI : ROWB;
+  // MXFP4 keys against E4M3 queries (kMX4E4, d_I = 128): a tile is 32 rows
+  // of 64 code bytes and a 4-byte scale word; every thread loads one of its
+  // 544 words (the first 32 threads a second) and puts it in LDS as 32 rows
+  // of 64 code bytes followed by the 32 scale words, so that the operand
+  // reads are aligned 16-byte reads.
+  constexpr bool FP4D = KF == kMX4E4;
+  static_assert(!FP4D || dI == 128, "MXFP4 keys against E4M3 queries take d_I = 128");
+  constexpr int KROWB = FP4D ? dI / 2 + dI / 32 : KF == kMixed || F8 ? dI : ROWB;
   constexpr int CH8 = dI / 8;
-  constexpr int LBYTES = KF == kMixed ? 8 : 16;    // bytes each loader reads
-  constexpr int LOADERS = 32 * KROWB / LBYTES;
+  constexpr int LBYTES = FP4D ? 4 : KF == kMixed ? 8 : 16;    // bytes each loader reads
+  constexpr int LOADERS = FP4D ? 512 : 32 * KROWB / LBYTES;
+  constexpr int FP4W = 32 * KROWB / 4;       // words per MXFP4 tile (544)
   __shared__ float sw[QB][HI];
-  __shared__ __align__(16) uint8_t ktile[2][F8 ? 32 * dI : TILEB];
+  __shared__ __align__(16) uint8_t ktile[2][FP4D ? 32 * KROWB : F8 ? 32 * dI : TILEB];
   const int wave = threadIdx.x >> 6;
   const int l = lane_id();
   const int hf = l >> 5, ln = l & 31;
@@ -540,6 +548,21 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   bool lo_swap = false;
   const int lo_src8 = F8 ? f8_src<dI>(lo_off, lo_swap) % dI : 0;   // byte in its row
   auto load_tile = [&](int64_t tile) {
+    if constexpr (FP4D) {
+      // words t and 512 + t of the tile (rows past N read row N - 1)
+      uint4 r = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int wd = (int)threadIdx.x + 512 * h;
+        if (wd < FP4W) {
+          int64_t j = tile * 32 + wd / 17;
+          if (j > a.N - 1) j = a.N - 1;
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(Kb + j * KROWB + 4 * (wd % 17));
+          if (h == 0) r.x = v; else r.y = v;
+        }
+      }
+      return r;
+    }
     int64_t j = tile * 32 + lo_kk;
     if (j > a.N - 1) j = a.N - 1;
     if constexpr (KF == kMixed) {
@@ -552,6 +575,18 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
     }
   };
   auto put_tile = [&](uint8_t* kt, const uint4& st) {
+    if constexpr (FP4D) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int wd = (int)threadIdx.x + 512 * h;
+        if (wd < FP4W) {
+          const int kk = wd / 17, c = wd % 17;
+          *reinterpret_cast<uint32_t*>(kt + (c < 16 ? kk * 64 + 4 * c : 32 * 64 + 4 * kk)) =
+              h == 0 ? st.x : st.y;
+        }
+      }
+      return;
+    }
     if constexpr (KF == kMixed)
       *reinterpret_cast<uint4*>(kt + lo_kk * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16)) =
           e4m3x8_to_bf16x8(st.x, st.y);
@@ -569,7 +604,7 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   // lane (hidden key, second half-wave, row past Tq) stores out of range and
   // the store is dropped, so every store instruction is issued unconditionally
   // and the memory counter stays exact for the prefetch waits.
-  typedef typename std::conditional<F8, long, bf16x8>::type QFrag;
+  typedef typename std::conditional<F8 || FP4D, long, bf16x8>::type QFrag;
   QFrag qf[QPW][HT][KS];
   int64_t nv_row[QPW];
   __amdgpu_buffer_rsrc_t srow[QPW];
@@ -583,7 +618,15 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
       const int64_t qrow = (((int64_t)b * a.Tq + i) * HI) + ht * 32 + ln;
-      if constexpr (F8) {
+      if constexpr (FP4D) {
+        // step u, fragment r: the query bytes that meet the key dims
+        // 64u + 32(r/2) + 16hf + 8(r%2) .. +8 in the scaled FP4 product
+        const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * dI;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          qf[qi][ht][s] = *reinterpret_cast<const long*>(
+              qp + 64 * (s >> 2) + 32 * ((s >> 1) & 1) + 16 * hf + 8 * (s & 1));
+      } else if constexpr (F8) {
         const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qrow * dI + hf * (dI / 2);
 #pragma unroll
         for (int s = 0; s < KS; ++s) qf[qi][ht][s] = *reinterpret_cast<const long*>(qp + s * 8);
@@ -610,9 +653,19 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
     }
     __syncthreads();             // tile visible; every wave is done with tile - 1
     QFrag kf[KS];
+    // MXFP4: this lane's code blocks 2u + hf of key ln, and its scale word
+    uint4 kc[2];
+    uint32_t ksc = 0;
+    if constexpr (FP4D) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) kc[u] = *reinterpret_cast<const uint4*>(kt + ln * 64 + 16 * (2 * u + hf));
+      ksc = *reinterpret_cast<const uint32_t*>(kt + 32 * 64 + 4 * ln);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      if constexpr (F8) {
+      if constexpr (FP4D) {
+        kf[s] = 0;                           // unused: the operands are in kc
+      } else if constexpr (F8) {
         const int c = hf * (CH8 / 2) + s;
         kf[s] = *reinterpret_cast<const long*>(kt + ln * dI + ((c ^ f8_swz<dI>(ln)) * 8));
       } else {
@@ -628,7 +681,18 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         f32x16 acc = {};
-        if constexpr (F8) {
+        if constexpr (FP4D) {
+          // E4M3 queries (unit scales) x MXFP4 keys with their block scales,
+          // as in the decode kernel
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            i32x8 kb = {};
+            kb[0] = (int)kc[u].x; kb[1] = (int)kc[u].y; kb[2] = (int)kc[u].z; kb[3] = (int)kc[u].w;
+            acc = mfma_scaled_32x32x64<0, 4>(
+                cat4(qf[qi][ht][4 * u], qf[qi][ht][4 * u + 1], qf[qi][ht][4 * u + 2], qf[qi][ht][4 * u + 3]),
+                kb, acc, 127, (int)(ksc >> (8 * (2 * u + hf))));
+          }
+        } else if constexpr (F8) {
           // E4M3 x E4M3 on the 64-deep scaled FP8 product (unit scales):
           // fragments 4u .. 4u+3 of a lane are 32 bytes of its row, in the
           // same order for queries and keys, so every dim meets its partner.
@@ -696,9 +760,21 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
       const int HT = a.HI / 32, KS = a.dI / 16;
       // kBF16: bf16 queries and keys; kMixed: bf16 queries, E4M3 keys;
       // kE4M3: E4M3 queries and keys (FP8 MFMA); kMXFP4: bf16 queries, MXFP4
-      // keys (the decode kernel for every shape)
+      // keys (the decode kernel for every shape); kMX4E4: E4M3 queries, MXFP4
+      // keys (scaled FP4 MFMA)
       const int kf = a.fmt;
-      if (a.Tq >= 8 && !sb.split && kf != kMXFP4 && kf != kMX4E4) {
+      if (a.Tq >= 8 && !sb.split && kf == kMX4E4 && KS == 8) {
+        // MXFP4 keys against E4M3 queries: d_I = 128 (the ABI refuses others)
+        const int qpw = HT == 4 ? 1 : 2;
+        const int blocks = a.B * ((a.Tq + 8 * qpw - 1) / (8 * qpw));
+        if (HT == 1)
+          hipLaunchKernelGGL((score_prefill_kernel<1, 8, 2, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
+        else if (HT == 2)
+          hipLaunchKernelGGL((score_prefill_kernel<2, 8, 2, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
+        else
+          hipLaunchKernelGGL((score_prefill_kernel<4, 8, 1, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
+        err = hipGetLastError();
+      } else if (a.Tq >= 8 && !sb.split && kf != kMXFP4 && kf != kMX4E4) {
         // Prefill: a block of eight waves shares each key tile among 8 * QPW
         // queries and sweeps all the keys they see.
 #define LAC_SCORE_CASE(ht, ks, qpw)                                                        \

@@ -147,16 +147,22 @@ def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, d
     """CSA chunked prefill: a chunk of queries appended to a long context.  The
     cache rows of the context are drawn directly; the chunk's raw KV and
     indexer keys are compressed into the rows that follow.  Indexer queries
-    and keys are bf16, or E4M3 codes with idx_fmt = "mixed"."""
+    and keys are bf16, or E4M3 codes with idx_fmt = "mixed"; with idx_fmt =
+    "fp4" the queries are E4M3 codes and the keys MXFP4 rows (random codes,
+    scales 2^-3..2^3)."""
     B = 1
     N_ctx = ctx // m
     N = (ctx + chunk) // m
     T_raw = chunk + W - 1
     ckv = torch.zeros((B, N, D), dtype=torch.bfloat16, device=device)
     ckv[:, :N_ctx] = store(normal(seed, "ckv", (B, N_ctx, D), device=device), "bf16")
-    KI = torch.zeros((B, N, dI), dtype=torch.bfloat16 if idx_fmt == "bf16" else torch.uint8,
-                     device=device)
-    KI[:, :N_ctx] = store(normal(seed, "KI", (B, N_ctx, dI), device=device), idx_fmt)
+    if idx_fmt == "fp4":
+        KI = torch.zeros((B, N, dI // 2 + dI // 32), dtype=torch.uint8, device=device)
+        KI[:, :N_ctx] = mxfp4_rows(seed, "KI", (B, N_ctx), dI, device=device)
+    else:
+        KI = torch.zeros((B, N, dI), dtype=torch.bfloat16 if idx_fmt == "bf16" else torch.uint8,
+                         device=device)
+        KI[:, :N_ctx] = store(normal(seed, "KI", (B, N_ctx, dI), device=device), idx_fmt)
     return dict(
         kind="csa_chunk_prefill", fmt="bf16", B=B, D=D, m=m, r=r, HI=HI, dI=dI, H=H, k=k, W=W,
         N=N, N_ctx=N_ctx, chunk=chunk, theta=10000.0, q_pos0=ctx, raw_pos0=ctx - W + 1,
@@ -166,7 +172,8 @@ def csa_chunk_prefill(seed=3, ctx=262144, chunk=4096, D=512, m=4, r=64, HI=64, d
         z=store(normal(seed, "z", (B, chunk, D), device=device), "bf16"),
         kI_raw=store(normal(seed, "kI_raw", (B, chunk, dI), device=device), "bf16"),
         zI=store(normal(seed, "zI", (B, chunk, dI), device=device), "bf16"),
-        qI=store(normal(seed, "qI", (B, chunk, HI, dI), device=device), idx_fmt),
+        qI=store(normal(seed, "qI", (B, chunk, HI, dI), device=device),
+                 "mixed" if idx_fmt == "fp4" else idx_fmt),
         w=uniform(seed, "w", (B, chunk, HI), device=device),
         q=store(normal(seed, "q", (B, chunk, H, D), device=device), "bf16"),
         idx_fmt=idx_fmt,

@@ -400,6 +400,17 @@ def test_mxfp4_keys_e4m3_queries_rows_that_see_nothing():
     _run_fp4(2, 9, 64, 128, 40, 4, 8, [0, 100], 64, qfmt="mixed")
 
 
+def test_mxfp4_keys_e4m3_queries_chunked_prefill_causal_rows():
+    # 40 queries: the prefill score kernel (8 queries per wave group share
+    # each key tile in LDS), ragged key count
+    _run_fp4(1, 40, 64, 128, 5010, 4, 300, [20000], 67, qfmt="mixed")
+
+
+@pytest.mark.parametrize("HI", [32, 128])
+def test_mxfp4_keys_e4m3_queries_prefill_head_variants(HI):
+    _run_fp4(1, 17, HI, 128, 700, 4, 64, [2790], 68 + HI, qfmt="mixed")
+
+
 @pytest.mark.parametrize("HI", [32, 128])
 def test_mxfp4_keys_e4m3_queries_head_variants(HI):
     _run_fp4(2, 1, HI, 128, 2100, 4, 256, [8400, 9000], 65 + HI, qfmt="mixed")
