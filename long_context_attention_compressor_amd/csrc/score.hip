@@ -30,28 +30,30 @@ constexpr int kHistBins = kScoreHistBins;
 constexpr int kStagesBF16 = 2, kStagesF8 = 2, kStagesFP4 = 4;
 constexpr int kDecodeBlocksBF16 = 512, kDecodeBlocksF8 = 768, kDecodeBlocksFP4 = 512;
 
-// E4M3 key tiles in LDS (E4M3 queries): a row is d_I bytes, its 8-byte
+// E4M3 key tiles in LDS (E4M3 queries): a row is d_I bytes, its 16-byte
 // chunks XOR-swizzled by f8_swz(row), chosen so that the MFMA-layout reads
-// (chunk c of 32 consecutive rows, 16 lanes per LDS cycle) hit distinct
-// banks: with d_I = 64 two rows share a 128-byte line, so the swizzle
+// (one 16-byte chunk of each of 8 consecutive rows per LDS pass) hit distinct
+// bank groups: with d_I = 64 two rows share a 128-byte line, so the swizzle
 // follows the line index.
 template <int dI>
 __device__ __forceinline__ int f8_swz(int row) {
   static_assert(dI == 64 || dI == 128, "E4M3 score tiles take d_I of 64 or 128");
-  return (row / (128 / dI)) % (dI / 8);
+  return (row / (128 / dI)) % (dI / 16);
 }
-// The 16 bytes at LDS offset o of a swizzled E4M3 tile: physical chunks 2p,
-// 2p + 1 of row kk hold its chunks 2p ^ x and 2p ^ x ^ 1 (x = f8_swz(kk)),
-// i.e. its 16-byte chunk p ^ (x / 2), with the halves swapped when x is odd.
-// Returns the byte offset of that chunk in the HBM tile and the swap flag.
+// The byte offset in the HBM tile of the 16 bytes at LDS offset o of a
+// swizzled E4M3 tile: physical chunk p of row kk holds its chunk p ^ f8_swz(kk).
 template <int dI>
-__device__ __forceinline__ int f8_src(int o, bool& swap) {
-  const int kk = o / dI, p = (o % dI) / 16, x = f8_swz<dI>(kk);
-  swap = x & 1;
-  return kk * dI + ((p ^ (x >> 1)) * 16);
+__device__ __forceinline__ int f8_src(int o) {
+  const int kk = o / dI, p = (o % dI) / 16;
+  return kk * dI + ((p ^ f8_swz<dI>(kk)) * 16);
 }
-__device__ __forceinline__ uint4 swap_halves(const uint4& v, bool swap) {
-  return swap ? make_uint4(v.z, v.w, v.x, v.y) : v;
+// Fragments 2c and 2c + 1 of a lane (8 codes each) from its row's logical
+// 16-byte chunk c of a swizzled E4M3 tile.
+template <int dI>
+__device__ __forceinline__ void f8_pair(const uint8_t* kt, int row, int c, long* f) {
+  const uint4 v = *reinterpret_cast<const uint4*>(kt + row * dI + ((c ^ f8_swz<dI>(row)) * 16));
+  f[0] = (long)((uint64_t)v.x | ((uint64_t)v.y << 32));
+  f[1] = (long)((uint64_t)v.z | ((uint64_t)v.w << 32));
 }
 
 struct ScoreArgs {
@@ -131,7 +133,6 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   constexpr bool FP4D = KF == kMX4E4;
   static_assert(!FP4D || dI == 128, "direct MXFP4 keys take d_I = 128");
   constexpr int KROWB = FP4 || FP4D ? dI / 2 + dI / 32 : KF == kMixed || F8 ? dI : ROWB;
-  constexpr int CH8 = dI / 8;                // 8-byte chunks per E4M3 key row
   constexpr int KTILEB = 32 * KROWB;
   constexpr int NLD = FP4D ? 3 : (KTILEB + 1023) / 1024;   // 16-byte registers per lane per tile
   constexpr int kLPR = dI / 8;               // E4M3: lanes per key (8 codes each)
@@ -215,10 +216,9 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, u * 1024 + l * 16, 0, 2);
         st[u] = make_uint4(v.x, v.y, v.z, v.w);
       } else if constexpr (F8) {
-        bool sw8;
-        const int src = f8_src<dI>(u * 1024 + l * 16, sw8);
+        const int src = f8_src<dI>(u * 1024 + l * 16);
         const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsrc, src, 0, 2);
-        st[u] = swap_halves(make_uint4(v.x, v.y, v.z, v.w), sw8);
+        st[u] = make_uint4(v.x, v.y, v.z, v.w);
       } else {
         const int o = u * 1024 + l * 16;
         const int kk = o / ROWB, cs = (o % ROWB) / 16;
@@ -333,13 +333,17 @@ __global__ void __launch_bounds__(256) score_bf16_kernel(ScoreArgs a) {
   // Work on one tile held in LDS: scores of the wave's query rows.
   auto compute = [&](int64_t tile) {
     QFrag kf[KS];
+    if constexpr (F8) {
+      // fragments s, s + 1 hold dims hf * d_I / 2 + 8 s .. + 16: one 16-byte read
+#pragma unroll
+      for (int s = 0; s < KS; s += 2) f8_pair<dI>(kt, ln, hf * (dI / 32) + s / 2, &kf[s]);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if constexpr (FP4D) {
         kf[s] = 0;                           // unused: the operands are in cur
       } else if constexpr (F8) {
-        const int c = hf * (CH8 / 2) + s;
-        kf[s] = *reinterpret_cast<const long*>(kt + ln * dI + ((c ^ f8_swz<dI>(ln)) * 8));
+        // read above
       } else {
         const int c = hf * (CH / 2) + s;
         kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
@@ -507,7 +511,6 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   constexpr bool FP4D = KF == kMX4E4;
   static_assert(!FP4D || dI == 128, "MXFP4 keys against E4M3 queries take d_I = 128");
   constexpr int KROWB = FP4D ? dI / 2 + dI / 32 : KF == kMixed || F8 ? dI : ROWB;
-  constexpr int CH8 = dI / 8;
   constexpr int LBYTES = FP4D ? 4 : KF == kMixed ? 8 : 16;    // bytes each loader reads
   constexpr int LOADERS = FP4D ? 512 : 32 * KROWB / LBYTES;
   constexpr int FP4W = 32 * KROWB / 4;       // words per MXFP4 tile (544)
@@ -545,8 +548,7 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
   const bool loader = (int)threadIdx.x < LOADERS;
   const int lo_off = threadIdx.x * LBYTES;
   const int lo_kk = lo_off / KROWB, lo_cs = (lo_off % KROWB) / LBYTES;
-  bool lo_swap = false;
-  const int lo_src8 = F8 ? f8_src<dI>(lo_off, lo_swap) % dI : 0;   // byte in its row
+  const int lo_src8 = F8 ? f8_src<dI>(lo_off) % dI : 0;   // byte in its row
   auto load_tile = [&](int64_t tile) {
     if constexpr (FP4D) {
       // words t and 512 + t of the tile (rows past N read row N - 1)
@@ -569,7 +571,7 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
       const uint2 v = ld_stream8(Kb + j * KROWB + lo_cs * 8);
       return make_uint4(v.x, v.y, 0u, 0u);
     } else if constexpr (F8) {
-      return swap_halves(ld_stream16(Kb + j * dI + lo_src8), lo_swap);
+      return ld_stream16(Kb + j * dI + lo_src8);
     } else {
       return ld_stream16(Kb + j * ROWB + ((lo_cs ^ (lo_kk % CH)) * 16));
     }
@@ -661,13 +663,17 @@ __global__ void __launch_bounds__(512) score_prefill_kernel(ScoreArgs a) {
       for (int u = 0; u < 2; ++u) kc[u] = *reinterpret_cast<const uint4*>(kt + ln * 64 + 16 * (2 * u + hf));
       ksc = *reinterpret_cast<const uint32_t*>(kt + 32 * 64 + 4 * ln);
     }
+    if constexpr (F8) {
+      // fragments s, s + 1 hold dims hf * d_I / 2 + 8 s .. + 16: one 16-byte read
+#pragma unroll
+      for (int s = 0; s < KS; s += 2) f8_pair<dI>(kt, ln, hf * (dI / 32) + s / 2, &kf[s]);
+    }
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       if constexpr (FP4D) {
         kf[s] = 0;                           // unused: the operands are in kc
       } else if constexpr (F8) {
-        const int c = hf * (CH8 / 2) + s;
-        kf[s] = *reinterpret_cast<const long*>(kt + ln * dI + ((c ^ f8_swz<dI>(ln)) * 8));
+        // read above
       } else {
         const int c = hf * (CH / 2) + s;
         kf[s] = *reinterpret_cast<const bf16x8*>(kt + ln * ROWB + ((c ^ (ln % CH)) * 16));
