@@ -59,14 +59,14 @@ FP8_PEAK_TFLOPS = 5000.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273745920, "pair_decode_1m_ungrouped": 273745920,
-                       "csa_decode_128k": 277476352, "csa_chunk_prefill": 1323486208,
-                       "pair_decode_1m_fp8_indexer": 138918912,
-                       "pair_decode_1m_mxfp4_indexer": 76721152,
-                       "pair_decode_1m_fp4_indexer": 76233728,
-                       "csa_chunk_prefill_fp8_indexer": 1185114112,
-                       "csa_chunk_prefill_fp4_indexer": 1153319936}
-SCORE_TRAFFIC_SOURCE_SHA256 = "2c7ff41844b9f46b65d1f93a779f32baebf8d1c699f5a195c9c29f8a0b8becad"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273741824, "pair_decode_1m_ungrouped": 273741824,
+                       "csa_decode_128k": 277470208, "csa_chunk_prefill": 1335117824,
+                       "pair_decode_1m_fp8_indexer": 138912768,
+                       "pair_decode_1m_mxfp4_indexer": 76717056,
+                       "pair_decode_1m_fp4_indexer": 76272640,
+                       "csa_chunk_prefill_fp8_indexer": 1199477760,
+                       "csa_chunk_prefill_fp4_indexer": 1153289216}
+SCORE_TRAFFIC_SOURCE_SHA256 = "18356592f5262a6f95effd5c98fc77b37ef039263f14284cc0d8b681188ab0f9"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
