@@ -771,14 +771,21 @@ hipError_t launch_indexer_scores(const IndexerArgs& a, const ScoreBuffers& sb, i
       const int kf = a.fmt;
       if (a.Tq >= 8 && !sb.split && kf == kMX4E4 && KS == 8) {
         // MXFP4 keys against E4M3 queries: d_I = 128 (the ABI refuses others)
-        const int qpw = HT == 4 ? 1 : 2;
+        // one query per wave (HT > 1): 109 VGPRs, two blocks per compute unit
+        const int qpw = HT == 1 ? 2 : 1;
         const int blocks = a.B * ((a.Tq + 8 * qpw - 1) / (8 * qpw));
         if (HT == 1)
           hipLaunchKernelGGL((score_prefill_kernel<1, 8, 2, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
         else if (HT == 2)
-          hipLaunchKernelGGL((score_prefill_kernel<2, 8, 2, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
+          hipLaunchKernelGGL((score_prefill_kernel<2, 8, 1, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
         else
           hipLaunchKernelGGL((score_prefill_kernel<4, 8, 1, kMX4E4>), dim3(blocks), dim3(512), 0, st, sa);
+        err = hipGetLastError();
+      } else if (a.Tq >= 8 && !sb.split && kf == kE4M3 && HT == 2 && KS == 8) {
+        // E4M3 queries and keys, 64 heads x 128: one query per wave as well
+        // (low register use, two blocks per compute unit)
+        const int blocks = a.B * ((a.Tq + 7) / 8);
+        hipLaunchKernelGGL((score_prefill_kernel<2, 8, 1, kE4M3>), dim3(blocks), dim3(512), 0, st, sa);
         err = hipGetLastError();
       } else if (a.Tq >= 8 && !sb.split && kf != kMXFP4 && kf != kMX4E4) {
         // Prefill: a block of eight waves shares each key tile among 8 * QPW
