@@ -59,14 +59,14 @@ FP8_PEAK_TFLOPS = 5000.0
 # sources they were taken on (score.hip and the device helpers it includes),
 # identified by their SHA-256; after any change to them the roofline reports
 # traffic as null until the counters are taken again.
-SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273741824, "pair_decode_1m_ungrouped": 273741824,
-                       "csa_decode_128k": 277470208, "csa_chunk_prefill": 1335117824,
-                       "pair_decode_1m_fp8_indexer": 138912768,
-                       "pair_decode_1m_mxfp4_indexer": 76717056,
-                       "pair_decode_1m_fp4_indexer": 76272640,
-                       "csa_chunk_prefill_fp8_indexer": 1199477760,
-                       "csa_chunk_prefill_fp4_indexer": 1153289216}
-SCORE_TRAFFIC_SOURCE_SHA256 = "18356592f5262a6f95effd5c98fc77b37ef039263f14284cc0d8b681188ab0f9"
+SCORE_TRAFFIC_BYTES = {"pair_decode_1m": 273737728, "pair_decode_1m_ungrouped": 273737728,
+                       "csa_decode_128k": 277470208, "csa_chunk_prefill": 1328329728,
+                       "pair_decode_1m_fp8_indexer": 138900480,
+                       "pair_decode_1m_mxfp4_indexer": 76721152,
+                       "pair_decode_1m_fp4_indexer": 76252160,
+                       "csa_chunk_prefill_fp8_indexer": 1278718976,
+                       "csa_chunk_prefill_fp4_indexer": 1158550528}
+SCORE_TRAFFIC_SOURCE_SHA256 = "f2fbdff8ead546bfc2485b2304e89ecc502bd8f3f22f65c2c57a140e80a3e770"
 SCORE_SOURCES = ("score.hip", "lac_device.h")
 
 
